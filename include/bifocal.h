@@ -1,0 +1,164 @@
+/*
+ * libbifocal -- Dynamic Bifocal RoPE attention for AMD MI355X (gfx950).
+ *
+ * What is computed (Jet-Long, arXiv 2607.07740, as described on the pages):
+ *   - s(L) = max(1, ceil(L / w_pre)), one factor per sequence of length L
+ *     [Jet-Long promo script (papers.ananclaw.com), section 4 storyboard,
+ *      scene-2 formula; ai-feeds.com summary, "方法 / 关键模块" item 2].
+ *   - For a query at position i and a key at position j <= i of the same
+ *     sequence, the pair is LOCAL when i - j < w0 and is scored with the
+ *     model's original RoPE; otherwise it is FAR and is scored with RoPE at
+ *     the scaled positions phi(p): p / s (frequency interpolation) or
+ *     floor(p / s) (position aliasing) [ai-feeds.com summary, "关键模块"
+ *     item 1 and "关键发现", ablation bullet].
+ *   - Softmax over j <= i with every pair counted once: the inclusion-
+ *     exclusion merge of the full scaled branch, minus its local band, plus
+ *     the band under original RoPE [seventnews.com (FR), fusion paragraph].
+ *   - Inputs q, k are the cache form: they already carry original RoPE at
+ *     their absolute positions. The far branch is reached by a correction
+ *     rotation R(theta_m * (phi(p) - p)) applied on the fly to cached keys
+ *     and to the query [ai-feeds.com summary, "关键模块" item 3].
+ * Rotary pairs are half-split (m, m + D/2), theta_m = rope_theta^(-2m/D).
+ *
+ * Conventions for every entry point:
+ *   - Tensors are caller-owned DEVICE memory and must stay valid until the
+ *     work enqueued on `stream` completes. Host arrays (cu_seqlens_host,
+ *     seqlens_host) are read before the call returns.
+ *   - All work is enqueued on `stream` (a hipStream_t, NULL = default
+ *     stream). The library never synchronises and keeps no state between
+ *     calls except a thread-local error string.
+ *   - Scratch memory lives only in the caller's `workspace` (device memory,
+ *     256-byte aligned, at least bifocal_workspace_bytes(...) bytes); its
+ *     contents on entry do not matter. Calls that run concurrently need
+ *     distinct workspaces.
+ *   - Every argument is validated before the first HIP call: on any error
+ *     nothing is launched and outputs are untouched.
+ *   - Returns BF_OK (0) or a negative code; bifocal_last_error() explains.
+ *   - Output is bitwise reproducible for the same inputs and device.
+ */
+#ifndef BIFOCAL_H
+#define BIFOCAL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* return codes */
+#define BF_OK 0
+#define BF_ERR_INVALID_ARG (-1) /* null pointer, non-positive size, Hq % Hkv != 0,
+                                   w0 < 0, w_pre < 1, bad lengths, theta <= 1, bad enum */
+#define BF_ERR_UNSUPPORTED (-2) /* head_dim != 128, fp32 decode */
+#define BF_ERR_WORKSPACE (-3)   /* workspace NULL, too small or misaligned */
+#define BF_ERR_HIP (-4)         /* a HIP launch failed; see bifocal_last_error() */
+
+/* element types of q, k, v, o (and the caches) */
+#define BF_DTYPE_BF16 0
+#define BF_DTYPE_FP32 1
+
+/* long-branch position map phi(p) */
+#define BF_LONG_FI 0 /* frequency interpolation: phi(p) = p / s */
+#define BF_LONG_PA 1 /* position aliasing:       phi(p) = floor(p / s) */
+
+/* phases for the workspace query and the plain reference */
+#define BF_PHASE_PREFILL 0
+#define BF_PHASE_DECODE 1
+
+/*
+ * s(L) = max(1, ceil(L / w_pre)) in 64-bit integers; -1 if L < 1 or
+ * w_pre < 1. Host only. [promo script, storyboard scene-2 formula]
+ */
+int64_t bifocal_s_of_L(int64_t L, int64_t w_pre);
+
+/*
+ * Workspace bytes needed by bifocal_prefill / bifocal_decode /
+ * plain_attention_ref_gpu for the given phase and sizes.
+ *   PREFILL: `tokens` = total packed tokens T = cu_seqlens[batch].
+ *   DECODE:  `tokens` = the largest seqlens[b] of the call.
+ * The same figure covers both the bifocal and the plain call of a phase.
+ * Returns 0 for invalid arguments.
+ */
+size_t bifocal_workspace_bytes(int32_t phase, int32_t batch, int64_t tokens, int32_t n_heads_q,
+                               int32_t n_heads_kv, int32_t head_dim, int32_t dtype);
+
+/*
+ * Causal bifocal prefill over a packed ragged batch.
+ *   q, o : [n_heads_q,  T, head_dim]   dtype (bf16 or fp32), head-major,
+ *                                      head_dim contiguous
+ *   k, v : [n_heads_kv, T, head_dim]   same dtype
+ *   lse  : [n_heads_q, T] fp32 natural-log row log-sum-exp, or NULL
+ *   cu_seqlens_host : host int32 [batch + 1], cu[0] = 0, strictly
+ *          increasing; sequence b is tokens cu[b] .. cu[b+1]-1, its
+ *          positions restart at 0 and it gets its own s(L_b).
+ *   w0 >= 0 local window (w0 = 0: every pair far; w0 >= L: plain RoPE),
+ *   w_pre >= 1 pretrained window, rope_theta > 1 RoPE base,
+ *   long_mode BF_LONG_FI or BF_LONG_PA, softmax_scale > 0 (both branches).
+ * Query head h reads KV head h / (n_heads_q / n_heads_kv).
+ * [ai-feeds.com summary, "方法": inputs are L and the pretrained RoPE
+ *  configuration, the output is the attention output of the sequence;
+ *  "关键发现": the two long-branch strategies]
+ */
+int bifocal_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
+                    const int32_t* cu_seqlens_host, int32_t batch, int32_t n_heads_q,
+                    int32_t n_heads_kv, int32_t head_dim, int32_t dtype, int64_t w0,
+                    int64_t w_pre, double rope_theta, int32_t long_mode, float softmax_scale,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Single-token bifocal decode over a KV cache (bf16 only).
+ *   q, o             : [batch, n_heads_q, head_dim] bf16
+ *   k_cache, v_cache : [batch, n_heads_kv, cache_capacity, head_dim] bf16,
+ *                      keys stored with ORIGINAL RoPE at their positions
+ *   lse              : [batch, n_heads_q] fp32 or NULL
+ *   seqlens_host     : host int32 [batch], 1 <= N_b <= cache_capacity,
+ *                      the number of valid keys INCLUDING the new token's
+ *                      own (already appended); the query sits at position
+ *                      N_b - 1 and s = s(N_b).
+ * Result equals the last row of bifocal_prefill over the same N_b tokens.
+ * [promo script, voice-over: single-batch generation; ai-feeds.com summary,
+ *  "关键模块" item 3: the correction rotation applied to cached keys]
+ */
+int bifocal_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                   const int32_t* seqlens_host, int32_t batch, int32_t cache_capacity,
+                   int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim, int32_t dtype,
+                   int64_t w0, int64_t w_pre, double rope_theta, int32_t long_mode,
+                   float softmax_scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Plain causal softmax attention on the same (original-RoPE) q and k, run by
+ * the same engine with the bifocal features compiled out: the reference for
+ * the bifocal overhead and for the s = 1 identity.
+ *   phase BF_PHASE_PREFILL: layouts and lens_host as bifocal_prefill
+ *          (lens_host = cu_seqlens [batch + 1]; cache_capacity ignored);
+ *   phase BF_PHASE_DECODE: layouts and lens_host as bifocal_decode
+ *          (lens_host = seqlens [batch]).
+ */
+int plain_attention_ref_gpu(int32_t phase, const void* q, const void* k, const void* v, void* o,
+                            float* lse, const int32_t* lens_host, int32_t batch,
+                            int32_t cache_capacity, int32_t n_heads_q, int32_t n_heads_kv,
+                            int32_t head_dim, int32_t dtype, float softmax_scale,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Test hook: runs the kernels' own device-side pair classification and
+ * position map for one sequence of length L (L <= 4096).
+ *   branch_out : device int8 [L * L], row-major (i, j): 0 masked (j > i),
+ *                1 local, 2 far;
+ *   phi_num_out: device int64 [L], phi(p) * s for FI (= p) and
+ *                floor(p / s) * s for PA, so both are exact integers;
+ *   s_out      : device int64 [1], s(L) as the device computes it.
+ */
+int bifocal_test_pair_map(int64_t L, int64_t w0, int64_t w_pre, int32_t long_mode,
+                          int8_t* branch_out, int64_t* phi_num_out, int64_t* s_out,
+                          void* stream);
+
+/* Thread-local description of the last error (empty string after success). */
+const char* bifocal_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BIFOCAL_H */

@@ -1,0 +1,194 @@
+"""Python binding of libbifocal (ctypes). Argument marshalling only.
+
+Every step of the computation runs in the HIP kernels of libbifocal.so; this
+module allocates outputs and workspaces through PyTorch (device memory and
+streams are the only things PyTorch provides) and passes raw pointers to the
+C-ABI entry points declared in include/bifocal.h. There is no fallback: if
+the library is missing or a call fails, an exception is raised.
+"""
+import ctypes
+import math
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libbifocal.so")
+
+BF_OK, BF_ERR_INVALID_ARG, BF_ERR_UNSUPPORTED, BF_ERR_WORKSPACE, BF_ERR_HIP = 0, -1, -2, -3, -4
+BF_DTYPE_BF16, BF_DTYPE_FP32 = 0, 1
+BF_LONG_FI, BF_LONG_PA = 0, 1
+BF_PHASE_PREFILL, BF_PHASE_DECODE = 0, 1
+LONG_MODES = {"fi": BF_LONG_FI, "pa": BF_LONG_PA}
+_DTYPES = {torch.bfloat16: BF_DTYPE_BF16, torch.float32: BF_DTYPE_FP32}
+
+EXPORTED = ("bifocal_s_of_L", "bifocal_workspace_bytes", "bifocal_prefill", "bifocal_decode",
+            "plain_attention_ref_gpu", "bifocal_test_pair_map", "bifocal_last_error")
+
+_lib = None
+
+
+class BifocalError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"libbifocal error {code}: {msg}")
+        self.code = code
+
+
+def lib():
+    """Load libbifocal.so (built in-tree); raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() or "
+                               "python -m rope_context_extension_bifocal_amd.csrc.build")
+        L = ctypes.CDLL(LIB_PATH)
+        p, i32, i64, f32, f64, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                                     ctypes.c_float, ctypes.c_double, ctypes.c_size_t)
+        L.bifocal_s_of_L.restype = i64
+        L.bifocal_s_of_L.argtypes = [i64, i64]
+        L.bifocal_workspace_bytes.restype = sz
+        L.bifocal_workspace_bytes.argtypes = [i32, i32, i64, i32, i32, i32, i32]
+        L.bifocal_prefill.restype = ctypes.c_int
+        L.bifocal_prefill.argtypes = [p, p, p, p, p, p, i32, i32, i32, i32, i32, i64, i64, f64,
+                                      i32, f32, p, sz, p]
+        L.bifocal_decode.restype = ctypes.c_int
+        L.bifocal_decode.argtypes = [p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, i64, i64,
+                                     f64, i32, f32, p, sz, p]
+        L.plain_attention_ref_gpu.restype = ctypes.c_int
+        L.plain_attention_ref_gpu.argtypes = [i32, p, p, p, p, p, p, i32, i32, i32, i32, i32,
+                                              i32, f32, p, sz, p]
+        L.bifocal_test_pair_map.restype = ctypes.c_int
+        L.bifocal_test_pair_map.argtypes = [i64, i64, i64, i32, p, p, p, p]
+        L.bifocal_last_error.restype = ctypes.c_char_p
+        L.bifocal_last_error.argtypes = []
+        _lib = L
+    return _lib
+
+
+def _check(rc):
+    if rc != BF_OK:
+        raise BifocalError(rc, lib().bifocal_last_error().decode())
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _i32_array(vals):
+    arr = (ctypes.c_int32 * len(vals))(*[int(x) for x in vals])
+    return arr
+
+
+def s_of_L(L, w_pre):
+    return int(lib().bifocal_s_of_L(int(L), int(w_pre)))
+
+
+def workspace_bytes(phase, batch, tokens, n_heads_q, n_heads_kv, head_dim=128,
+                    dtype=torch.bfloat16):
+    return int(lib().bifocal_workspace_bytes(int(phase), int(batch), int(tokens), int(n_heads_q),
+                                             int(n_heads_kv), int(head_dim), _DTYPES[dtype]))
+
+
+def alloc_workspace(nbytes, device):
+    """Device workspace (256-byte aligned: the caching allocator aligns to 512)."""
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def _scale(softmax_scale, D):
+    return float(softmax_scale) if softmax_scale is not None else 1.0 / math.sqrt(D)
+
+
+def prefill(q, k, v, cu_seqlens, w0, w_pre, rope_theta, long_mode="fi", softmax_scale=None,
+            return_lse=False, out=None, lse=None, workspace=None, stream=None):
+    """Bifocal causal prefill. q [Hq,T,D], k/v [Hkv,T,D] on the GPU (bf16 or fp32),
+    cu_seqlens a host list [B+1]. Returns o (and lse [Hq,T] fp32)."""
+    Hq, T, D = q.shape
+    Hkv = k.shape[0]
+    B = len(cu_seqlens) - 1
+    o = out if out is not None else torch.empty_like(q)
+    if return_lse and lse is None:
+        lse = torch.empty((Hq, T), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = alloc_workspace(workspace_bytes(BF_PHASE_PREFILL, B, T, Hq, Hkv, D, q.dtype),
+                                    q.device)
+    cu = _i32_array(cu_seqlens)
+    _check(lib().bifocal_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), cu, B, Hq, Hkv,
+                                 D, _DTYPES[q.dtype], int(w0), int(w_pre), float(rope_theta),
+                                 LONG_MODES[long_mode], _scale(softmax_scale, D), _ptr(workspace),
+                                 workspace.numel(), _stream(stream)))
+    return (o, lse) if return_lse else o
+
+
+def plain_prefill(q, k, v, cu_seqlens, softmax_scale=None, return_lse=False, out=None, lse=None,
+                  workspace=None, stream=None):
+    """Plain causal attention on the same engine (bifocal features compiled out)."""
+    Hq, T, D = q.shape
+    Hkv = k.shape[0]
+    B = len(cu_seqlens) - 1
+    o = out if out is not None else torch.empty_like(q)
+    if return_lse and lse is None:
+        lse = torch.empty((Hq, T), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = alloc_workspace(workspace_bytes(BF_PHASE_PREFILL, B, T, Hq, Hkv, D, q.dtype),
+                                    q.device)
+    cu = _i32_array(cu_seqlens)
+    _check(lib().plain_attention_ref_gpu(BF_PHASE_PREFILL, _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                         _ptr(lse), cu, B, 0, Hq, Hkv, D, _DTYPES[q.dtype],
+                                         _scale(softmax_scale, D), _ptr(workspace),
+                                         workspace.numel(), _stream(stream)))
+    return (o, lse) if return_lse else o
+
+
+def decode(q, k_cache, v_cache, seqlens, w0, w_pre, rope_theta, long_mode="fi",
+           softmax_scale=None, return_lse=False, out=None, lse=None, workspace=None, stream=None):
+    """Bifocal single-token decode. q [B,Hq,D], caches [B,Hkv,cap,D] bf16 on the GPU,
+    seqlens a host list [B] (valid keys including the new token's)."""
+    B, Hq, D = q.shape
+    Hkv, cap = k_cache.shape[1], k_cache.shape[2]
+    o = out if out is not None else torch.empty_like(q)
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = alloc_workspace(workspace_bytes(BF_PHASE_DECODE, B, max(seqlens), Hq, Hkv, D,
+                                                    q.dtype), q.device)
+    sl = _i32_array(seqlens)
+    _check(lib().bifocal_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(lse), sl, B,
+                                cap, Hq, Hkv, D, _DTYPES[q.dtype], int(w0), int(w_pre),
+                                float(rope_theta), LONG_MODES[long_mode],
+                                _scale(softmax_scale, D), _ptr(workspace), workspace.numel(),
+                                _stream(stream)))
+    return (o, lse) if return_lse else o
+
+
+def plain_decode(q, k_cache, v_cache, seqlens, softmax_scale=None, return_lse=False, out=None,
+                 lse=None, workspace=None, stream=None):
+    B, Hq, D = q.shape
+    Hkv, cap = k_cache.shape[1], k_cache.shape[2]
+    o = out if out is not None else torch.empty_like(q)
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = alloc_workspace(workspace_bytes(BF_PHASE_DECODE, B, max(seqlens), Hq, Hkv, D,
+                                                    q.dtype), q.device)
+    sl = _i32_array(seqlens)
+    _check(lib().plain_attention_ref_gpu(BF_PHASE_DECODE, _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                         _ptr(o), _ptr(lse), sl, B, cap, Hq, Hkv, D,
+                                         _DTYPES[q.dtype], _scale(softmax_scale, D),
+                                         _ptr(workspace), workspace.numel(), _stream(stream)))
+    return (o, lse) if return_lse else o
+
+
+def test_pair_map(L, w0, w_pre, long_mode="fi", device="cuda"):
+    """Device pair classification and correction offsets (test hook)."""
+    br = torch.empty((L, L), dtype=torch.int8, device=device)
+    num = torch.empty((L,), dtype=torch.int64, device=device)
+    s = torch.empty((1,), dtype=torch.int64, device=device)
+    _check(lib().bifocal_test_pair_map(int(L), int(w0), int(w_pre), LONG_MODES[long_mode],
+                                       _ptr(br), _ptr(num), _ptr(s), _stream(None)))
+    return br, num, int(s.item())

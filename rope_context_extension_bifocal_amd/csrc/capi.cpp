@@ -1,0 +1,318 @@
+// libbifocal C-ABI: argument validation, the s(L) schedule, per-launch
+// sequence tables, workspace carving and kernel launches. Host code only; the
+// kernels live in prefill.hip and decode.hip.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <numeric>
+#include <string>
+#include <vector>
+
+#include "bifocal.h"
+#include "bf_common.h"
+
+namespace bf {
+hipError_t launch_correction_prep(int dtype, const PrepParams& pp, const SeqTable& st,
+                                  const ThetaTable& tt, hipStream_t stream);
+hipError_t launch_vt_transpose(int dtype, const VtParams& vp, const SeqTable& st,
+                               hipStream_t stream);
+hipError_t launch_prefill_main(int dtype, bool bifocal, const PrefillParams& pp,
+                               const SeqTable& st, int grid, hipStream_t stream);
+hipError_t launch_pair_map(long long L, long long w0, long long s, int mode, int8_t* br,
+                           long long* dphi_num, long long* s_out, hipStream_t stream);
+int decode_splits(long long N);
+size_t decode_workspace_bytes(int batch, long long max_len, int Hq);
+int run_decode(bool bifocal, const void* q, const void* kc, const void* vc, void* o, float* lse,
+               const int32_t* seqlens, int batch, int cap, int Hq, int Hkv, long long w0,
+               long long w_pre, double theta, int mode, float scale, void* ws, size_t ws_bytes,
+               hipStream_t stream, std::string& err);
+}  // namespace bf
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+bool trace_on() {
+  const char* e = getenv("BIFOCAL_TRACE");
+  return e && e[0] == '1';
+}
+
+bool forced_launch_failure() {
+  const char* e = getenv("BIFOCAL_TEST_FAIL_LAUNCH");
+  return e && e[0] == '1';
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t elem_size(int dtype) { return dtype == BF_DTYPE_BF16 ? 2 : 4; }
+
+bf::ThetaTable theta_table(double rope_theta) {
+  bf::ThetaTable tt;
+  for (int m = 0; m < bf::kPairs; ++m)
+    tt.th[m] = std::pow(rope_theta, -2.0 * (double)m / (double)bf::kHeadDim);
+  return tt;
+}
+
+// Geometry of the prefill launch for a given element type and GQA group size.
+struct PrefillGeom {
+  int hpw, n_hsub, P_wg;
+};
+
+PrefillGeom prefill_geom(int dtype, int G) {
+  PrefillGeom g;
+  g.hpw = std::gcd(G, bf::kWavesPerGroup);
+  g.n_hsub = G / g.hpw;
+  const int rows = dtype == BF_DTYPE_BF16 ? bf::kWaveRowsBf16 : bf::kWaveRowsF32;
+  g.P_wg = rows * bf::kWavesPerGroup / g.hpw;
+  return g;
+}
+
+struct PrefillWs {
+  size_t vt_off, q2_off, k2_off, total;
+};
+
+PrefillWs prefill_ws_layout(int batch, long long T, int Hq, int Hkv, int dtype) {
+  const size_t es = elem_size(dtype);
+  const size_t tpad_bound = (size_t)T + 63u * (size_t)batch;
+  PrefillWs w;
+  w.vt_off = 0;
+  w.q2_off = align256((size_t)Hkv * bf::kHeadDim * tpad_bound * es);
+  w.k2_off = w.q2_off + align256((size_t)Hq * (size_t)T * bf::kHeadDim * es);
+  w.total = w.k2_off + align256((size_t)Hkv * (size_t)T * bf::kHeadDim * es);
+  return w;
+}
+
+int check_common(int Hq, int Hkv, int head_dim, int dtype) {
+  if (Hq < 1 || Hkv < 1) return fail(BF_ERR_INVALID_ARG, "head counts must be >= 1 (Hq=%d, Hkv=%d)", Hq, Hkv);
+  if (Hq % Hkv != 0) return fail(BF_ERR_INVALID_ARG, "n_heads_q %% n_heads_kv != 0 (%d, %d)", Hq, Hkv);
+  if (dtype != BF_DTYPE_BF16 && dtype != BF_DTYPE_FP32)
+    return fail(BF_ERR_INVALID_ARG, "dtype must be BF_DTYPE_BF16 or BF_DTYPE_FP32 (got %d)", dtype);
+  if (head_dim != bf::kHeadDim) return fail(BF_ERR_UNSUPPORTED, "head_dim must be 128 (got %d)", head_dim);
+  return BF_OK;
+}
+
+int check_bifocal_knobs(long long w0, long long w_pre, double theta, int mode) {
+  if (w0 < 0) return fail(BF_ERR_INVALID_ARG, "w0 must be >= 0 (got %lld)", w0);
+  if (w_pre < 1) return fail(BF_ERR_INVALID_ARG, "w_pre must be >= 1 (got %lld)", w_pre);
+  if (!(theta > 1.0) || !std::isfinite(theta))
+    return fail(BF_ERR_INVALID_ARG, "rope_theta must be finite and > 1");
+  if (mode != BF_LONG_FI && mode != BF_LONG_PA)
+    return fail(BF_ERR_INVALID_ARG, "long_mode must be BF_LONG_FI or BF_LONG_PA (got %d)", mode);
+  return BF_OK;
+}
+
+int check_scale(float scale) {
+  if (!(scale > 0.f) || !std::isfinite(scale))
+    return fail(BF_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
+  return BF_OK;
+}
+
+// Shared prefill path of bifocal_prefill and the plain reference.
+int run_prefill(bool bifocal, const void* q, const void* k, const void* v, void* o, float* lse,
+                const int32_t* cu, int batch, int Hq, int Hkv, int head_dim, int dtype,
+                long long w0, long long w_pre, double theta, int mode, float scale, void* ws,
+                size_t ws_bytes, hipStream_t stream) {
+  if (!q || !k || !v || !o || !cu) return fail(BF_ERR_INVALID_ARG, "null tensor or cu_seqlens pointer");
+  if (batch < 1) return fail(BF_ERR_INVALID_ARG, "batch must be >= 1 (got %d)", batch);
+  int rc = check_common(Hq, Hkv, head_dim, dtype);
+  if (rc) return rc;
+  if (bifocal && (rc = check_bifocal_knobs(w0, w_pre, theta, mode))) return rc;
+  if ((rc = check_scale(scale))) return rc;
+  if (cu[0] != 0) return fail(BF_ERR_INVALID_ARG, "cu_seqlens[0] must be 0 (got %d)", cu[0]);
+  for (int b = 0; b < batch; ++b)
+    if (cu[b + 1] <= cu[b])
+      return fail(BF_ERR_INVALID_ARG, "cu_seqlens must be strictly increasing (b=%d: %d -> %d)", b, cu[b], cu[b + 1]);
+  const long long T = cu[batch];
+  if (T + 63LL * batch > (1LL << 31) - 1) return fail(BF_ERR_INVALID_ARG, "too many tokens (%lld)", T);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(BF_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned");
+  if (lse && ((uintptr_t)lse & 3u)) return fail(BF_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  const PrefillWs wl = prefill_ws_layout(batch, T, Hq, Hkv, dtype);
+  if (!ws) return fail(BF_ERR_WORKSPACE, "workspace is null");
+  if ((uintptr_t)ws & 255u) return fail(BF_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  const size_t need = bifocal ? wl.total : wl.q2_off;
+  if (ws_bytes < need)
+    return fail(BF_ERR_WORKSPACE, "workspace too small: %zu bytes given, %zu needed", ws_bytes, need);
+
+  const int G = Hq / Hkv;
+  const PrefillGeom geo = prefill_geom(dtype, G);
+  // padded V^T offsets over the whole batch
+  std::vector<int> vt_off(batch + 1, 0);
+  for (int b = 0; b < batch; ++b) {
+    const int L = cu[b + 1] - cu[b];
+    vt_off[b + 1] = vt_off[b] + ((L + bf::kKeyTile - 1) / bf::kKeyTile) * bf::kKeyTile;
+  }
+  const int Tpad = vt_off[batch];
+  const bf::ThetaTable tt = theta_table(bifocal ? theta : 10000.0);
+  char* wsb = (char*)ws;
+  if (forced_launch_failure()) return fail(BF_ERR_HIP, "launch failure forced by BIFOCAL_TEST_FAIL_LAUNCH");
+
+  for (int b0 = 0; b0 < batch; b0 += bf::kMaxSeqPerLaunch) {
+    const int nb = std::min(bf::kMaxSeqPerLaunch, batch - b0);
+    bf::SeqTable st;
+    std::memset(&st, 0, sizeof st);
+    st.n = nb;
+    bool any_far = false;
+    int total_items = 0, max_nrb = 0;
+    for (int i = 0; i <= nb; ++i) {
+      st.cu[i] = cu[b0 + i];
+      st.vt_off[i] = vt_off[b0 + i];
+    }
+    for (int i = 0; i < nb; ++i) {
+      const long long L = cu[b0 + i + 1] - cu[b0 + i];
+      const long long s = bifocal ? bifocal_s_of_L(L, w_pre) : 1;
+      if (s > (1LL << 30)) return fail(BF_ERR_INVALID_ARG, "s(L) too large");
+      st.s[i] = (int)s;
+      if (s > 1 && w0 < L) any_far = true;
+      st.nrb[i] = (int)((L + geo.P_wg - 1) / geo.P_wg);
+      total_items += st.nrb[i];
+      max_nrb = std::max(max_nrb, st.nrb[i]);
+    }
+    hipError_t e = hipSuccess;
+    bf::VtParams vp{v, wsb + wl.vt_off, (int)T, Tpad, Hkv};
+    e = bf::launch_vt_transpose(dtype, vp, st, stream);
+    if (e != hipSuccess) return fail(BF_ERR_HIP, "vt_transpose launch: %s", hipGetErrorString(e));
+    if (bifocal && any_far) {
+      bf::PrepParams pp{q, k, wsb + wl.q2_off, wsb + wl.k2_off, (int)T, Hq, Hkv, mode};
+      e = bf::launch_correction_prep(dtype, pp, st, tt, stream);
+      if (e != hipSuccess) return fail(BF_ERR_HIP, "correction_prep launch: %s", hipGetErrorString(e));
+    }
+    bf::PrefillParams pp;
+    pp.q = q;
+    pp.k = k;
+    pp.q2 = wsb + wl.q2_off;
+    pp.k2 = wsb + wl.k2_off;
+    pp.vt = wsb + wl.vt_off;
+    pp.o = o;
+    pp.lse = lse;
+    pp.w0 = w0;
+    pp.scale_log2 = scale * 1.4426950408889634f;
+    pp.T = (int)T;
+    pp.Tpad = Tpad;
+    pp.Hq = Hq;
+    pp.Hkv = Hkv;
+    pp.G = G;
+    pp.hpw = geo.hpw;
+    pp.n_hsub = geo.n_hsub;
+    pp.P_wg = geo.P_wg;
+    pp.total_items = total_items;
+    pp.max_nrb = max_nrb;
+    const long long grid = (long long)Hkv * geo.n_hsub * total_items;
+    if (grid > 0x7fffffffLL) return fail(BF_ERR_INVALID_ARG, "launch grid too large");
+    if (trace_on())
+      fprintf(stderr, "[bifocal] prefill %s dtype=%d seqs=%d..%d grid=%lld P_wg=%d hpw=%d n_hsub=%d s0=%d w0=%lld\n",
+              bifocal ? "bifocal" : "plain", dtype, b0, b0 + nb - 1, grid, geo.P_wg, geo.hpw,
+              geo.n_hsub, st.s[0], w0);
+    e = bf::launch_prefill_main(dtype, bifocal && any_far, pp, st, (int)grid, stream);
+    if (e != hipSuccess) return fail(BF_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
+  }
+  g_err.clear();
+  return BF_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t bifocal_s_of_L(int64_t L, int64_t w_pre) {
+  if (L < 1 || w_pre < 1) return -1;
+  const int64_t q = L / w_pre + (L % w_pre != 0 ? 1 : 0);  // ceil(L / w_pre), no overflow
+  return q < 1 ? 1 : q;
+}
+
+size_t bifocal_workspace_bytes(int32_t phase, int32_t batch, int64_t tokens, int32_t n_heads_q,
+                               int32_t n_heads_kv, int32_t head_dim, int32_t dtype) {
+  if (batch < 1 || tokens < 1 || n_heads_q < 1 || n_heads_kv < 1 || head_dim != bf::kHeadDim)
+    return 0;
+  if (dtype != BF_DTYPE_BF16 && dtype != BF_DTYPE_FP32) return 0;
+  if (phase == BF_PHASE_PREFILL) return prefill_ws_layout(batch, tokens, n_heads_q, n_heads_kv, dtype).total;
+  if (phase == BF_PHASE_DECODE) return bf::decode_workspace_bytes(batch, tokens, n_heads_q);
+  return 0;
+}
+
+int bifocal_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
+                    const int32_t* cu_seqlens_host, int32_t batch, int32_t n_heads_q,
+                    int32_t n_heads_kv, int32_t head_dim, int32_t dtype, int64_t w0, int64_t w_pre,
+                    double rope_theta, int32_t long_mode, float softmax_scale, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  return run_prefill(true, q, k, v, o, lse, cu_seqlens_host, batch, n_heads_q, n_heads_kv,
+                     head_dim, dtype, w0, w_pre, rope_theta, long_mode, softmax_scale, workspace,
+                     workspace_bytes, (hipStream_t)stream);
+}
+
+int bifocal_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                   const int32_t* seqlens_host, int32_t batch, int32_t cache_capacity,
+                   int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim, int32_t dtype,
+                   int64_t w0, int64_t w_pre, double rope_theta, int32_t long_mode,
+                   float softmax_scale, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_common(n_heads_q, n_heads_kv, head_dim, dtype);
+  if (rc) return rc;
+  if ((rc = check_bifocal_knobs(w0, w_pre, rope_theta, long_mode))) return rc;
+  if (dtype != BF_DTYPE_BF16) return fail(BF_ERR_UNSUPPORTED, "decode supports bf16 only");
+  std::string err;
+  rc = bf::run_decode(true, q, k_cache, v_cache, o, lse, seqlens_host, batch, cache_capacity,
+                      n_heads_q, n_heads_kv, w0, w_pre, rope_theta, long_mode, softmax_scale,
+                      workspace, workspace_bytes, (hipStream_t)stream, err);
+  if (rc) return fail(rc, "%s", err.c_str());
+  g_err.clear();
+  return BF_OK;
+}
+
+int plain_attention_ref_gpu(int32_t phase, const void* q, const void* k, const void* v, void* o,
+                            float* lse, const int32_t* lens_host, int32_t batch,
+                            int32_t cache_capacity, int32_t n_heads_q, int32_t n_heads_kv,
+                            int32_t head_dim, int32_t dtype, float softmax_scale, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  if (phase == BF_PHASE_PREFILL)
+    return run_prefill(false, q, k, v, o, lse, lens_host, batch, n_heads_q, n_heads_kv, head_dim,
+                       dtype, 0, 1, 10000.0, 0, softmax_scale, workspace, workspace_bytes,
+                       (hipStream_t)stream);
+  if (phase != BF_PHASE_DECODE) return fail(BF_ERR_INVALID_ARG, "phase must be PREFILL or DECODE (got %d)", phase);
+  int rc = check_common(n_heads_q, n_heads_kv, head_dim, dtype);
+  if (rc) return rc;
+  if (dtype != BF_DTYPE_BF16) return fail(BF_ERR_UNSUPPORTED, "decode supports bf16 only");
+  std::string err;
+  rc = bf::run_decode(false, q, k, v, o, lse, lens_host, batch, cache_capacity, n_heads_q,
+                      n_heads_kv, 0, 1, 10000.0, 0, softmax_scale, workspace, workspace_bytes,
+                      (hipStream_t)stream, err);
+  if (rc) return fail(rc, "%s", err.c_str());
+  g_err.clear();
+  return BF_OK;
+}
+
+int bifocal_test_pair_map(int64_t L, int64_t w0, int64_t w_pre, int32_t long_mode,
+                          int8_t* branch_out, int64_t* phi_num_out, int64_t* s_out,
+                          void* stream) {
+  if (L < 1 || L > 4096) return fail(BF_ERR_INVALID_ARG, "test_pair_map needs 1 <= L <= 4096");
+  int rc = check_bifocal_knobs(w0, w_pre, 10000.0, long_mode);
+  if (rc) return rc;
+  if (!branch_out || !phi_num_out || !s_out) return fail(BF_ERR_INVALID_ARG, "null output pointer");
+  if (forced_launch_failure()) return fail(BF_ERR_HIP, "launch failure forced by BIFOCAL_TEST_FAIL_LAUNCH");
+  const long long s = bifocal_s_of_L(L, w_pre);
+  hipError_t e = bf::launch_pair_map(L, w0, s, long_mode, branch_out, (long long*)phi_num_out,
+                                     (long long*)s_out, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(BF_ERR_HIP, "pair_map launch: %s", hipGetErrorString(e));
+  g_err.clear();
+  return BF_OK;
+}
+
+const char* bifocal_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

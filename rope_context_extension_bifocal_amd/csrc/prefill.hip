@@ -1,0 +1,669 @@
+// Bifocal RoPE attention, causal prefill on gfx950 (CDNA4).
+//
+// Kernels:
+//   correction_prep_kernel  far-branch copies q'' = R(Delta(i)) q', k'' = R(Delta(j)) k'
+//                           with Delta_m(p) = theta_m * (phi(p) - p), angles in fp64
+//                           [ai-feeds.com summary, "关键模块" item 3: correction
+//                            rotation of cached keys so that long-range keys meet
+//                            the query at the scaled positions]
+//   vt_transpose_kernel     V -> V^T, each sequence padded to a multiple of 64 keys
+//   prefill_bf16_kernel     MFMA 32x32x16 bf16 tile loop, one online softmax
+//   prefill_f32_kernel      the same loop on MFMA 32x32x2 f32 for fp32 inputs
+//   pair_map_kernel         test hook: the device pair rule and position map
+//
+// Tile loop [ai-feeds.com summary, "关键模块" items 1 and 3; seventnews.com (FR),
+// fusion paragraph]: for a query row block and a 64-key tile, every causal pair
+// is either local (i - j < w0: original RoPE, q' . k') or far (q'' . k''). Keys
+// are visited in ascending order, which is the order far -> mixed -> band ->
+// diagonal. A far tile only reads K'', a band tile only K', and a mixed tile
+// computes both score blocks and picks per element, so each pair enters the
+// softmax exactly once and the scaled-branch work over the band that the
+// inclusion-exclusion merge would subtract again is never done.
+#include <hip/hip_runtime.h>
+
+#include "bf_common.h"
+
+namespace bf {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+
+// ----------------------------------------------------------------- helpers
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float((uint32_t)h << 16);
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {  // round to nearest even
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+// Local-window rule for one causal pair [ai-feeds.com summary, "关键模块" item 1].
+__device__ __forceinline__ bool pair_is_local(long long i, long long j, long long w0) {
+  return i - j < w0;
+}
+
+// (phi(p) - p) * s as an exact integer: FI phi = p / s gives -p (s - 1);
+// PA phi = floor(p / s) gives (floor(p / s) - p) * s.
+__device__ __forceinline__ long long corr_num(long long p, long long s, int mode) {
+  return mode == 1 ? (p / s - p) * s : -p * (s - 1);
+}
+
+// MFMA row r of a 32-row key block -> key index inside the block. Chosen so
+// that the 32x32 accumulator register r of lane half h holds key
+// 16 * (r / 8) + 8 * h + r % 8, i.e. 8 consecutive keys per lane half for
+// every 8 consecutive registers: the P operand of the PV product then lines
+// up with 16-byte reads of a V^T row.
+__device__ __forceinline__ int key_of_mfma_row(int r) {
+  const int a = r >> 3, h = (r >> 2) & 1, b = r & 3;
+  return ((a >> 1) << 4) | (h << 3) | ((a & 1) << 2) | b;
+}
+
+__device__ __forceinline__ int key_of_acc(int r, int hl) {  // key of acc register r
+  return ((r >> 3) << 4) | (hl << 3) | (r & 7);
+}
+
+// Work item of a workgroup: rank counts row blocks heaviest first (largest
+// row-block index first, ties by sequence order), across all sequences.
+__device__ __forceinline__ int items_at_or_above(const SeqTable& st, int x) {
+  int n = 0;
+  for (int b = 0; b < st.n; ++b) n += max(0, st.nrb[b] - x);
+  return n;
+}
+
+__device__ __forceinline__ void decode_item(const SeqTable& st, int rank, int max_nrb, int& b,
+                                            int& rb) {
+  int lo = 0, hi = max_nrb;  // items_at_or_above(lo) > rank >= items_at_or_above(hi)
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (items_at_or_above(st, mid) > rank) lo = mid;
+    else hi = mid;
+  }
+  rb = lo;
+  int e = rank - items_at_or_above(st, rb + 1);
+  for (b = 0; b < st.n; ++b) {
+    if (st.nrb[b] > rb) {
+      if (e == 0) break;
+      --e;
+    }
+  }
+}
+
+// ----------------------------------------------------------------- prep
+// One thread per (token, rotary pair m); 4 tokens per 256-lane group. The
+// angle is formed in fp64 from an exact integer numerator, so it stays
+// accurate at 128K positions (theta_0 * p ~ 1e5 rad), and is applied in fp32.
+template <typename T>
+__device__ __forceinline__ float ld_elem(const T* p) {
+  if constexpr (sizeof(T) == 2) return bf16_to_f32(*p);
+  else return *p;
+}
+template <typename T>
+__device__ __forceinline__ void st_elem(T* p, float f) {
+  if constexpr (sizeof(T) == 2) *p = f32_to_bf16(f);
+  else *p = f;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void correction_prep_kernel(PrepParams p, SeqTable st,
+                                                              ThetaTable tt) {
+  const int tok = st.cu[0] + blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int m = threadIdx.x & 63;
+  if (tok >= st.cu[st.n]) return;
+  int b = 0;
+  while (b + 1 < st.n && tok >= st.cu[b + 1]) ++b;
+  const int s = st.s[b];
+  if (s == 1) return;  // no far branch for this sequence
+  const long long pos = tok - st.cu[b];
+  const double dphi = (double)corr_num(pos, s, p.long_mode) / (double)s;
+  double sd, cd;
+  sincos(tt.th[m] * dphi, &sd, &cd);
+  const float c = (float)cd, sn = (float)sd;
+  const T* q = (const T*)p.q;
+  const T* k = (const T*)p.k;
+  T* q2 = (T*)p.q2;
+  T* k2 = (T*)p.k2;
+  for (int h = 0; h < p.Hq; ++h) {
+    const size_t base = ((size_t)h * p.T + tok) * kHeadDim;
+    const float x0 = ld_elem(q + base + m), x1 = ld_elem(q + base + m + kPairs);
+    st_elem(q2 + base + m, x0 * c - x1 * sn);
+    st_elem(q2 + base + m + kPairs, x1 * c + x0 * sn);
+  }
+  for (int h = 0; h < p.Hkv; ++h) {
+    const size_t base = ((size_t)h * p.T + tok) * kHeadDim;
+    const float x0 = ld_elem(k + base + m), x1 = ld_elem(k + base + m + kPairs);
+    st_elem(k2 + base + m, x0 * c - x1 * sn);
+    st_elem(k2 + base + m + kPairs, x1 * c + x0 * sn);
+  }
+}
+
+// V [Hkv][T][D] -> V^T [Hkv][D][Tpad]; sequence b occupies padded columns
+// vt_off[b] .. vt_off[b+1]-1, columns past its length are zero.
+template <typename T>
+__global__ __launch_bounds__(256) void vt_transpose_kernel(VtParams p, SeqTable st) {
+  __shared__ T tile[kKeyTile][kHeadDim + 2];
+  const int c = st.vt_off[0] + blockIdx.x * kKeyTile;
+  const int h = blockIdx.y;
+  int b = 0;
+  while (b + 1 < st.n && c >= st.vt_off[b + 1]) ++b;
+  const int p0 = c - st.vt_off[b];
+  const int L = st.cu[b + 1] - st.cu[b];
+  const T* v = (const T*)p.v + ((size_t)h * p.T + st.cu[b]) * kHeadDim;
+  for (int e = threadIdx.x; e < kKeyTile * kHeadDim; e += 256) {
+    const int r = e / kHeadDim, d = e % kHeadDim;
+    tile[r][d] = (p0 + r < L) ? v[(size_t)(p0 + r) * kHeadDim + d] : T(0);
+  }
+  __syncthreads();
+  T* vt = (T*)p.vt + (size_t)h * kHeadDim * p.Tpad;
+  for (int e = threadIdx.x; e < kKeyTile * kHeadDim; e += 256) {
+    const int d = e / kKeyTile, r = e % kKeyTile;
+    vt[(size_t)d * p.Tpad + c + r] = tile[r][d];
+  }
+}
+
+// ----------------------------------------------------------------- main
+// Shared work-item geometry of both element types.
+struct Item {
+  int kvh, hq, b, tok0, L, R0, r0, nkt;
+  long long w0;
+};
+
+template <bool BIFOCAL>
+__device__ __forceinline__ Item make_item(const PrefillParams& p, const SeqTable& st, int wave,
+                                          int wave_rows) {
+  Item it;
+  const int id = blockIdx.x;
+  it.kvh = id % p.Hkv;
+  const int r1 = id / p.Hkv;
+  const int hsub = r1 % p.n_hsub;
+  const int rank = r1 / p.n_hsub;
+  int rb;
+  decode_item(st, rank, p.max_nrb, it.b, rb);
+  it.tok0 = st.cu[it.b];
+  it.L = st.cu[it.b + 1] - it.tok0;
+  // s = 1 means the far branch equals the local one: treat every pair as local
+  it.w0 = (BIFOCAL && st.s[it.b] > 1) ? p.w0 : (1LL << 62);
+  const int hw = wave % p.hpw, pw = wave / p.hpw;
+  it.hq = it.kvh * p.G + hsub * p.hpw + hw;
+  it.R0 = rb * p.P_wg;
+  it.r0 = it.R0 + pw * wave_rows;
+  const int wg_end = min(it.R0 + p.P_wg, it.L);
+  it.nkt = (wg_end + kKeyTile - 1) / kKeyTile;
+  return it;
+}
+
+// Tile needs, for the whole workgroup (rows R0 .. R0 + P_wg - 1) and keys
+// c0 .. c0 + 63: any far pair / any local pair.
+template <bool BIFOCAL>
+__device__ __forceinline__ void tile_needs(long long R0, long long P_wg, long long c0,
+                                           long long w0, bool& need_far, bool& need_loc) {
+  need_far = BIFOCAL && (R0 + P_wg - 1 - c0 >= w0);
+  need_loc = !BIFOCAL || (w0 > 0 && R0 - (c0 + kKeyTile - 1) < w0);
+}
+
+__device__ __forceinline__ void online_softmax_rescale(float& m_run, float& l_run, float mx,
+                                                       float scale_log2, float& mbase,
+                                                       float& alpha) {
+  const float mnew = fmaxf(m_run, mx * scale_log2);
+  mbase = (mnew == -INFINITY) ? 0.f : mnew;
+  alpha = __builtin_amdgcn_exp2f(m_run - mbase);
+  m_run = mnew;
+}
+
+// --------------------------------------------------------------- bf16
+// Workgroup: 4 waves; wave = (query head, 64 query positions). G query heads
+// of one KV group share every staged K/V tile. Per wave and 64-key tile:
+// S^T = K Q^T as 2x2 MFMA 32x32x16 blocks (keys x queries), then O^T += V^T P^T
+// as 4x2 blocks (head dim x queries). A lane owns one query column of each
+// block, so row max / sum need one exchange with the other lane half.
+template <bool BIFOCAL>
+__device__ __forceinline__ void qk_bf16(const uint4* __restrict__ sk, const bf16x8 (&q)[2][8],
+                                        int li, int hl, f32x16 (&S)[2][2]) {
+#pragma unroll
+  for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib) S[jb][ib] = f32x16{};
+  const int row0 = key_of_mfma_row(li), row1 = 32 + row0;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const int ch = 2 * t + hl;
+    const bf16x8 a0 = __builtin_bit_cast(bf16x8, sk[row0 * 16 + (ch ^ (row0 & 15))]);
+    const bf16x8 a1 = __builtin_bit_cast(bf16x8, sk[row1 * 16 + (ch ^ (row1 & 15))]);
+    S[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, q[0][t], S[0][0], 0, 0, 0);
+    S[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, q[1][t], S[0][1], 0, 0, 0);
+    S[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, q[0][t], S[1][0], 0, 0, 0);
+    S[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, q[1][t], S[1][1], 0, 0, 0);
+  }
+}
+
+template <bool BIFOCAL>
+__global__ __launch_bounds__(256, 1) void prefill_bf16_kernel(PrefillParams p, SeqTable st) {
+  extern __shared__ uint4 smem[];
+  uint4* sK = smem;                         // K' tile   [64][16 x 16 B], swizzled
+  uint4* sK2 = smem + 1024;                 // K'' tile
+  uint4* sV = smem + (BIFOCAL ? 2048 : 1024);  // V^T tile [128][8 x 16 B], swizzled
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 31, hl = lane >> 5;
+  const Item it = make_item<BIFOCAL>(p, st, wave, kWaveRowsBf16);
+  const long long w0 = it.w0;
+
+  const uint16_t* qg = (const uint16_t*)p.q + ((size_t)it.hq * p.T + it.tok0) * kHeadDim;
+  const uint16_t* kg = (const uint16_t*)p.k + ((size_t)it.kvh * p.T + it.tok0) * kHeadDim;
+  const uint16_t* q2g = BIFOCAL ? (const uint16_t*)p.q2 + ((size_t)it.hq * p.T + it.tok0) * kHeadDim : nullptr;
+  const uint16_t* k2g = BIFOCAL ? (const uint16_t*)p.k2 + ((size_t)it.kvh * p.T + it.tok0) * kHeadDim : nullptr;
+  const uint16_t* vtg = (const uint16_t*)p.vt + (size_t)it.kvh * kHeadDim * p.Tpad + st.vt_off[it.b];
+
+  // Q fragments (B operand): lane (li, hl) holds query r0 + 32 ib + li,
+  // head dims 16 t + 8 hl .. +7 for k-step t.
+  bf16x8 qf[2][8], qf2[2][8];
+  const uint4 zero4 = make_uint4(0, 0, 0, 0);
+#pragma unroll
+  for (int ib = 0; ib < 2; ++ib) {
+    const int row = it.r0 + 32 * ib + li;
+    const bool ok = row < it.L;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const size_t off = (size_t)row * kHeadDim + (2 * t + hl) * 8;
+      qf[ib][t] = __builtin_bit_cast(bf16x8, ok ? *(const uint4*)(qg + off) : zero4);
+      if constexpr (BIFOCAL)
+        qf2[ib][t] = __builtin_bit_cast(bf16x8, (ok && w0 < it.L) ? *(const uint4*)(q2g + off) : zero4);
+    }
+  }
+
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  f32x16 oacc[4][2];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib) oacc[db][ib] = f32x16{};
+
+  // register prefetch of the next tile: K' / K'' rows (4 x 16 B each) and V^T (4 x 16 B)
+  uint4 pk[4], pk2[4], pv[4];
+  bool nf = false, nl = true;
+  auto load_tile = [&](int c0, bool need_far, bool need_loc) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + 256 * i;
+      const int row = c >> 4, col = c & 15;
+      const bool ok = c0 + row < it.L;
+      const size_t off = (size_t)(c0 + row) * kHeadDim + col * 8;
+      if (need_loc) pk[i] = ok ? *(const uint4*)(kg + off) : zero4;
+      if constexpr (BIFOCAL)
+        if (need_far) pk2[i] = ok ? *(const uint4*)(k2g + off) : zero4;
+      const int d = c >> 3, vc = c & 7;
+      pv[i] = *(const uint4*)(vtg + (size_t)d * p.Tpad + c0 + vc * 8);
+    }
+  };
+  tile_needs<BIFOCAL>(it.R0, p.P_wg, 0, w0, nf, nl);
+  load_tile(0, nf, nl);
+
+  for (int kt = 0; kt < it.nkt; ++kt) {
+    const int c0 = kt * kKeyTile;
+    const bool cf = nf, cl = nl;
+    __syncthreads();  // previous tile's LDS reads are done
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + 256 * i;
+      const int row = c >> 4, col = c & 15;
+      if (cl) sK[row * 16 + (col ^ (row & 15))] = pk[i];
+      if constexpr (BIFOCAL)
+        if (cf) sK2[row * 16 + (col ^ (row & 15))] = pk2[i];
+      const int d = c >> 3, vc = c & 7;
+      sV[d * 8 + (vc ^ (d & 7))] = pv[i];
+    }
+    __syncthreads();
+    if (kt + 1 < it.nkt) {
+      tile_needs<BIFOCAL>(it.R0, p.P_wg, c0 + kKeyTile, w0, nf, nl);
+      load_tile(c0 + kKeyTile, nf, nl);
+    }
+
+    const bool wave_skip = (it.r0 >= it.L) || (c0 > it.r0 + kWaveRowsBf16 - 1);
+    if (wave_skip) continue;
+    const long long dmax = (long long)it.r0 + kWaveRowsBf16 - 1 - c0;
+    const long long dmin = (long long)it.r0 - (c0 + kKeyTile - 1);
+    const bool has_far = BIFOCAL && dmax >= w0;
+    const bool has_loc = !BIFOCAL || (w0 > 0 && dmin < w0);
+
+    f32x16 S[2][2];
+    if (BIFOCAL && has_far) qk_bf16<BIFOCAL>(sK2, qf2, li, hl, S);
+    else qk_bf16<BIFOCAL>(sK, qf, li, hl, S);
+    if (BIFOCAL && has_far && has_loc) {  // mixed tile: choose per pair
+      f32x16 Sl[2][2];
+      qk_bf16<BIFOCAL>(sK, qf, li, hl, Sl);
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+        for (int ib = 0; ib < 2; ++ib) {
+          const long long i = it.r0 + 32 * ib + li;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const long long j = c0 + 32 * jb + key_of_acc(r, hl);
+            if (pair_is_local(i, j, w0)) S[jb][ib][r] = Sl[jb][ib][r];
+          }
+        }
+    }
+    if (dmin < 0) {  // causal mask on the diagonal tile
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+        for (int ib = 0; ib < 2; ++ib) {
+          const int i = it.r0 + 32 * ib + li;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int j = c0 + 32 * jb + key_of_acc(r, hl);
+            if (j > i) S[jb][ib][r] = -INFINITY;
+          }
+        }
+    }
+
+    // online softmax, one state per query row
+    bf16x8 pb[2][2][2];  // [ib][jb][u]
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[jb][ib][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      float mbase, alpha;
+      online_softmax_rescale(m_run[ib], l_run[ib], mx, p.scale_log2, mbase, alpha);
+      float rs = 0.f;
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float e = __builtin_amdgcn_exp2f(fmaf(S[jb][ib][r], p.scale_log2, -mbase));
+          S[jb][ib][r] = e;
+          rs += e;
+        }
+      rs += __shfl_xor(rs, 32);
+      l_run[ib] = l_run[ib] * alpha + rs;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) oacc[db][ib] *= alpha;
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          bf16x8 v;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = (__bf16)S[jb][ib][8 * u + e];
+          pb[ib][jb][u] = v;
+        }
+    }
+    // O^T += V^T P^T
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const int d = 32 * db + li;
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int ch = 4 * jb + 2 * u + hl;
+          const bf16x8 a = __builtin_bit_cast(bf16x8, sV[d * 8 + (ch ^ (d & 7))]);
+          oacc[db][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[0][jb][u], oacc[db][0], 0, 0, 0);
+          oacc[db][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[1][jb][u], oacc[db][1], 0, 0, 0);
+        }
+    }
+  }
+
+  // epilogue: normalise, store O (bf16) and lse
+  if (it.r0 >= it.L) return;
+  uint16_t* og = (uint16_t*)p.o + ((size_t)it.hq * p.T + it.tok0) * kHeadDim;
+#pragma unroll
+  for (int ib = 0; ib < 2; ++ib) {
+    const int row = it.r0 + 32 * ib + li;
+    if (row >= it.L) continue;
+    const float inv = 1.f / l_run[ib];
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = 32 * db + 8 * g + 4 * hl;
+        uint2 w;
+        w.x = (uint32_t)f32_to_bf16(oacc[db][ib][4 * g + 0] * inv) |
+              ((uint32_t)f32_to_bf16(oacc[db][ib][4 * g + 1] * inv) << 16);
+        w.y = (uint32_t)f32_to_bf16(oacc[db][ib][4 * g + 2] * inv) |
+              ((uint32_t)f32_to_bf16(oacc[db][ib][4 * g + 3] * inv) << 16);
+        *(uint2*)(og + (size_t)row * kHeadDim + d) = w;
+      }
+    if (p.lse && hl == 0)
+      p.lse[(size_t)it.hq * p.T + it.tok0 + row] = (m_run[ib] + __log2f(l_run[ib])) * 0.69314718055994530942f;
+  }
+}
+
+// --------------------------------------------------------------- fp32
+// Same loop with fp32 operands on MFMA 32x32x2 f32: one 32-row query block per
+// wave; k-step t contracts head dims t (lanes 0-31) and 64 + t (lanes 32-63).
+__device__ __forceinline__ void qk_f32(const uint4* __restrict__ sk, const float (&q)[64], int li,
+                                       int hl, f32x16 (&S)[2]) {
+  S[0] = f32x16{};
+  S[1] = f32x16{};
+  const int row0 = key_of_mfma_row(li), row1 = 32 + row0;
+#pragma unroll
+  for (int tc = 0; tc < 16; ++tc) {
+    const int ch = 16 * hl + tc;
+    const float4 a0 = __builtin_bit_cast(float4, sk[row0 * 32 + (ch ^ (row0 & 31))]);
+    const float4 a1 = __builtin_bit_cast(float4, sk[row1 * 32 + (ch ^ (row1 & 31))]);
+    S[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.x, q[4 * tc + 0], S[0], 0, 0, 0);
+    S[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1.x, q[4 * tc + 0], S[1], 0, 0, 0);
+    S[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.y, q[4 * tc + 1], S[0], 0, 0, 0);
+    S[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1.y, q[4 * tc + 1], S[1], 0, 0, 0);
+    S[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.z, q[4 * tc + 2], S[0], 0, 0, 0);
+    S[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1.z, q[4 * tc + 2], S[1], 0, 0, 0);
+    S[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.w, q[4 * tc + 3], S[0], 0, 0, 0);
+    S[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1.w, q[4 * tc + 3], S[1], 0, 0, 0);
+  }
+}
+
+template <bool BIFOCAL>
+__global__ __launch_bounds__(256, 1) void prefill_f32_kernel(PrefillParams p, SeqTable st) {
+  extern __shared__ uint4 smem[];
+  uint4* sK = smem;                            // [64][32 x 16 B]
+  uint4* sK2 = smem + 2048;
+  uint4* sV = smem + (BIFOCAL ? 4096 : 2048);  // [128][16 x 16 B]
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 31, hl = lane >> 5;
+  const Item it = make_item<BIFOCAL>(p, st, wave, kWaveRowsF32);
+  const long long w0 = it.w0;
+
+  const float* qg = (const float*)p.q + ((size_t)it.hq * p.T + it.tok0) * kHeadDim;
+  const float* kg = (const float*)p.k + ((size_t)it.kvh * p.T + it.tok0) * kHeadDim;
+  const float* q2g = BIFOCAL ? (const float*)p.q2 + ((size_t)it.hq * p.T + it.tok0) * kHeadDim : nullptr;
+  const float* k2g = BIFOCAL ? (const float*)p.k2 + ((size_t)it.kvh * p.T + it.tok0) * kHeadDim : nullptr;
+  const float* vtg = (const float*)p.vt + (size_t)it.kvh * kHeadDim * p.Tpad + st.vt_off[it.b];
+
+  float qf[64], qf2[64];
+  {
+    const int row = it.r0 + li;
+    const bool ok = row < it.L;
+#pragma unroll
+    for (int tc = 0; tc < 16; ++tc) {
+      const size_t off = (size_t)row * kHeadDim + 64 * hl + 4 * tc;
+      const float4 a = ok ? *(const float4*)(qg + off) : make_float4(0, 0, 0, 0);
+      qf[4 * tc] = a.x; qf[4 * tc + 1] = a.y; qf[4 * tc + 2] = a.z; qf[4 * tc + 3] = a.w;
+      if constexpr (BIFOCAL) {
+        const float4 c = (ok && w0 < it.L) ? *(const float4*)(q2g + off) : make_float4(0, 0, 0, 0);
+        qf2[4 * tc] = c.x; qf2[4 * tc + 1] = c.y; qf2[4 * tc + 2] = c.z; qf2[4 * tc + 3] = c.w;
+      }
+    }
+  }
+
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x16 oacc[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) oacc[db] = f32x16{};
+  const uint4 zero4 = make_uint4(0, 0, 0, 0);
+
+  for (int kt = 0; kt < it.nkt; ++kt) {
+    const int c0 = kt * kKeyTile;
+    bool cf, cl;
+    tile_needs<BIFOCAL>(it.R0, p.P_wg, c0, w0, cf, cl);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int c = tid + 256 * i;
+      const int row = c >> 5, col = c & 31;
+      const bool ok = c0 + row < it.L;
+      const size_t off = (size_t)(c0 + row) * kHeadDim + col * 4;
+      if (cl) sK[row * 32 + (col ^ (row & 31))] = ok ? *(const uint4*)(kg + off) : zero4;
+      if constexpr (BIFOCAL)
+        if (cf) sK2[row * 32 + (col ^ (row & 31))] = ok ? *(const uint4*)(k2g + off) : zero4;
+      const int d = c >> 4, vc = c & 15;
+      sV[d * 16 + (vc ^ (d & 15))] = *(const uint4*)(vtg + (size_t)d * p.Tpad + c0 + vc * 4);
+    }
+    __syncthreads();
+
+    const bool wave_skip = (it.r0 >= it.L) || (c0 > it.r0 + kWaveRowsF32 - 1);
+    if (wave_skip) continue;
+    const long long dmax = (long long)it.r0 + kWaveRowsF32 - 1 - c0;
+    const long long dmin = (long long)it.r0 - (c0 + kKeyTile - 1);
+    const bool has_far = BIFOCAL && dmax >= w0;
+    const bool has_loc = !BIFOCAL || (w0 > 0 && dmin < w0);
+
+    f32x16 S[2];
+    if (BIFOCAL && has_far) qk_f32(sK2, qf2, li, hl, S);
+    else qk_f32(sK, qf, li, hl, S);
+    const long long i = it.r0 + li;
+    if (BIFOCAL && has_far && has_loc) {
+      f32x16 Sl[2];
+      qk_f32(sK, qf, li, hl, Sl);
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const long long j = c0 + 32 * jb + key_of_acc(r, hl);
+          if (pair_is_local(i, j, w0)) S[jb][r] = Sl[jb][r];
+        }
+    }
+    if (dmin < 0) {
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const long long j = c0 + 32 * jb + key_of_acc(r, hl);
+          if (j > i) S[jb][r] = -INFINITY;
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[jb][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    float mbase, alpha;
+    online_softmax_rescale(m_run, l_run, mx, p.scale_log2, mbase, alpha);
+    float rs = 0.f;
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float e = __builtin_amdgcn_exp2f(fmaf(S[jb][r], p.scale_log2, -mbase));
+        S[jb][r] = e;
+        rs += e;
+      }
+    rs += __shfl_xor(rs, 32);
+    l_run = l_run * alpha + rs;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
+    // O^T += V^T P^T; register r of lane half hl is key 32 jb + key_of_acc(r, hl)
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const int d = 32 * db + li;
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {  // registers 4g .. 4g+3
+          const int key = 32 * jb + key_of_acc(4 * g, hl);
+          const int ch = key >> 2;
+          const float4 a = __builtin_bit_cast(float4, sV[d * 16 + (ch ^ (d & 15))]);
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, S[jb][4 * g + 0], oacc[db], 0, 0, 0);
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, S[jb][4 * g + 1], oacc[db], 0, 0, 0);
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, S[jb][4 * g + 2], oacc[db], 0, 0, 0);
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, S[jb][4 * g + 3], oacc[db], 0, 0, 0);
+        }
+    }
+  }
+
+  const int row = it.r0 + li;
+  if (row >= it.L) return;
+  float* og = (float*)p.o + ((size_t)it.hq * p.T + it.tok0) * kHeadDim;
+  const float inv = 1.f / l_run;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d = 32 * db + 8 * g + 4 * hl;
+      *(float4*)(og + (size_t)row * kHeadDim + d) =
+          make_float4(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv, oacc[db][4 * g + 2] * inv,
+                      oacc[db][4 * g + 3] * inv);
+    }
+  if (p.lse && hl == 0)
+    p.lse[(size_t)it.hq * p.T + it.tok0 + row] = (m_run + __log2f(l_run)) * 0.69314718055994530942f;
+}
+
+// --------------------------------------------------------------- test hook
+__global__ void pair_map_kernel(long long L, long long w0, long long s, int mode, int8_t* br,
+                                long long* dphi_num, long long* s_out) {
+  const long long n = L * L;
+  for (long long e = blockIdx.x * (long long)blockDim.x + threadIdx.x; e < n;
+       e += (long long)gridDim.x * blockDim.x) {
+    const long long i = e / L, j = e % L;
+    br[e] = (j > i) ? 0 : (pair_is_local(i, j, w0) ? 1 : 2);
+  }
+  for (long long pidx = blockIdx.x * (long long)blockDim.x + threadIdx.x; pidx < L;
+       pidx += (long long)gridDim.x * blockDim.x)
+    dphi_num[pidx] = corr_num(pidx, s, mode);
+  if (blockIdx.x == 0 && threadIdx.x == 0) *s_out = s;
+}
+
+// --------------------------------------------------------------- launchers
+hipError_t launch_correction_prep(int dtype, const PrepParams& pp, const SeqTable& st,
+                                  const ThetaTable& tt, hipStream_t stream) {
+  const int grid = (st.cu[st.n] - st.cu[0] + 3) / 4;
+  if (dtype == 0)
+    hipLaunchKernelGGL(correction_prep_kernel<uint16_t>, dim3(grid), dim3(256), 0, stream, pp, st, tt);
+  else
+    hipLaunchKernelGGL(correction_prep_kernel<float>, dim3(grid), dim3(256), 0, stream, pp, st, tt);
+  return hipGetLastError();
+}
+
+hipError_t launch_vt_transpose(int dtype, const VtParams& vp, const SeqTable& st,
+                               hipStream_t stream) {
+  dim3 grid((st.vt_off[st.n] - st.vt_off[0]) / kKeyTile, vp.Hkv);
+  if (dtype == 0)
+    hipLaunchKernelGGL(vt_transpose_kernel<uint16_t>, grid, dim3(256), 0, stream, vp, st);
+  else
+    hipLaunchKernelGGL(vt_transpose_kernel<float>, grid, dim3(256), 0, stream, vp, st);
+  return hipGetLastError();
+}
+
+template <typename K>
+static hipError_t launch_with_lds(K kernel, int grid, size_t lds, hipStream_t stream,
+                                  const PrefillParams& pp, const SeqTable& st) {
+  hipError_t e = hipFuncSetAttribute((const void*)kernel,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), lds, stream, pp, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_main(int dtype, bool bifocal, const PrefillParams& pp,
+                               const SeqTable& st, int grid, hipStream_t stream) {
+  if (dtype == 0) {
+    if (bifocal) return launch_with_lds(prefill_bf16_kernel<true>, grid, 3 * 16384, stream, pp, st);
+    return launch_with_lds(prefill_bf16_kernel<false>, grid, 2 * 16384, stream, pp, st);
+  }
+  if (bifocal) return launch_with_lds(prefill_f32_kernel<true>, grid, 3 * 32768, stream, pp, st);
+  return launch_with_lds(prefill_f32_kernel<false>, grid, 2 * 32768, stream, pp, st);
+}
+
+hipError_t launch_pair_map(long long L, long long w0, long long s, int mode, int8_t* br,
+                           long long* dphi_num, long long* s_out, hipStream_t stream) {
+  hipLaunchKernelGGL(pair_map_kernel, dim3(64), dim3(256), 0, stream, L, w0, s, mode, br,
+                     dphi_num, s_out);
+  return hipGetLastError();
+}
+
+}  // namespace bf

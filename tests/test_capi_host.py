@@ -1,0 +1,134 @@
+"""Host-side checks of libbifocal that need no GPU: the library loads, exports
+every entry point include/bifocal.h declares, computes s(L) bit-exactly, sizes
+workspaces, and rejects every invalid argument before any HIP call."""
+import ctypes
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from rope_context_extension_bifocal_amd import bifocal as bfl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bifocal.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(bfl.LIB_PATH):
+        from rope_context_extension_bifocal_amd.csrc.build import build
+        build()
+    return bfl.lib()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_symbols_exported(L):
+    names = declared_functions()
+    assert set(names) == set(bfl.EXPORTED)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_s_of_L_bit_exact_against_oracle(L):
+    with open(os.path.join(ROOT, "tests", "golden", "s_of_L.json")) as f:
+        for c in json.load(f)["cases"]:
+            assert bfl.s_of_L(c["L"], c["w_pre"]) == c["s"]
+    rng = np.random.default_rng(3)
+    for w_pre in [1, 3, 1024, 32768]:
+        Ls = list(range(1, 4 * w_pre + 2)) if w_pre <= 1024 else []
+        Ls += [int(x) for x in rng.integers(1, 1 << 40, size=200)]
+        for Lx in Ls:
+            assert bfl.s_of_L(Lx, w_pre) == oracle.s_of_L(Lx, w_pre)
+    assert bfl.s_of_L(0, 5) == -1 and bfl.s_of_L(5, 0) == -1
+    assert bfl.s_of_L(2**62, 1) == 2**62
+
+
+def test_workspace_bytes(L):
+    pre = bfl.workspace_bytes(bfl.BF_PHASE_PREFILL, 1, 131072, 32, 8)
+    # V^T (8 x 128 x (T + 63) bf16) + corrected Q (32 x T x 128) + corrected K (8 x T x 128)
+    assert pre >= 2 * 128 * (32 + 8 + 8) * 131072
+    dec = bfl.workspace_bytes(bfl.BF_PHASE_DECODE, 1, 131073, 32, 8)
+    assert dec >= 4 * 32 * 130 * 129
+    assert L.bifocal_workspace_bytes(0, 1, 10, 2, 1, 64, 0) == 0     # head_dim 64 unsupported
+    assert L.bifocal_workspace_bytes(5, 1, 10, 2, 1, 128, 0) == 0    # bad phase
+
+
+# Fake device pointers: validation reads only their values, never the memory.
+P = ctypes.c_void_p(0x100000)
+
+
+def _prefill(L, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=None, cu=[0, 100], Hq=2, Hkv=1, D=128, dtype=0, w0=16,
+             w_pre=64, theta=1e4, mode=0, scale=0.088, ws=P, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    cu = (ctypes.c_int32 * len(a["cu"]))(*a["cu"])
+    return L.bifocal_prefill(a["q"], a["k"], a["v"], a["o"], a["lse"], cu, len(a["cu"]) - 1,
+                             a["Hq"], a["Hkv"], a["D"], a["dtype"], a["w0"], a["w_pre"],
+                             a["theta"], a["mode"], a["scale"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+def _decode(L, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=None, sl=[100], cap=128, Hq=4, Hkv=2, D=128, dtype=0, w0=16,
+             w_pre=64, theta=1e4, mode=1, scale=0.088, ws=P, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    sl = (ctypes.c_int32 * len(a["sl"]))(*a["sl"])
+    return L.bifocal_decode(a["q"], a["k"], a["v"], a["o"], a["lse"], sl, len(a["sl"]), a["cap"],
+                            a["Hq"], a["Hkv"], a["D"], a["dtype"], a["w0"], a["w_pre"], a["theta"],
+                            a["mode"], a["scale"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(o=None), -1), (dict(Hq=3, Hkv=2), -1), (dict(Hkv=0), -1),
+    (dict(D=64), -2), (dict(dtype=7), -1), (dict(w0=-1), -1), (dict(w_pre=0), -1),
+    (dict(theta=1.0), -1), (dict(theta=float("nan")), -1), (dict(mode=2), -1),
+    (dict(scale=0.0), -1), (dict(scale=float("inf")), -1), (dict(cu=[1, 100]), -1),
+    (dict(cu=[0, 50, 50]), -1), (dict(cu=[0, 60, 40]), -1), (dict(ws=None), -3),
+    (dict(ws=ctypes.c_void_p(0x100010)), -3), (dict(ws_bytes=1000), -3),
+    (dict(q=ctypes.c_void_p(0x100002)), -1),
+])
+def test_prefill_validation(L, kw, code):
+    assert _prefill(L, **kw) == code
+    assert len(L.bifocal_last_error()) > 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(sl=[0]), -1), (dict(sl=[129]), -1), (dict(dtype=1), -2),
+    (dict(D=96), -2), (dict(Hq=5, Hkv=2), -1), (dict(w0=-3), -1), (dict(mode=9), -1),
+    (dict(ws_bytes=10), -3), (dict(Hq=34, Hkv=2), -2),
+])
+def test_decode_validation(L, kw, code):
+    assert _decode(L, **kw) == code
+
+
+def test_valid_arguments_reach_the_launch(L, monkeypatch):
+    # with every argument valid the call gets as far as the launch; the hook
+    # makes that launch fail without touching a GPU
+    monkeypatch.setenv("BIFOCAL_TEST_FAIL_LAUNCH", "1")
+    assert _prefill(L) == bfl.BF_ERR_HIP
+    assert _prefill(L, dtype=1, mode=1, cu=[0, 5, 300, 301]) == bfl.BF_ERR_HIP
+    assert _decode(L) == bfl.BF_ERR_HIP
+    assert b"forced" in L.bifocal_last_error()
+
+
+def test_plain_validation(L):
+    cu = (ctypes.c_int32 * 2)(0, 100)
+    assert L.plain_attention_ref_gpu(7, P, P, P, P, None, cu, 1, 0, 2, 1, 128, 0, 0.1, P, 1 << 30,
+                                     None) == -1
+    assert L.plain_attention_ref_gpu(0, P, P, P, P, None, cu, 1, 0, 2, 1, 128, 0, -0.1, P,
+                                     1 << 30, None) == -1
+    assert L.plain_attention_ref_gpu(1, P, P, P, P, None, cu, 1, 50, 2, 1, 128, 1, 0.1, P,
+                                     1 << 30, None) == -2
+
+
+def test_pair_map_validation(L):
+    assert L.bifocal_test_pair_map(5000, 4, 8, 0, P, P, P, None) == -1
+    assert L.bifocal_test_pair_map(64, -1, 8, 0, P, P, P, None) == -1
+    assert L.bifocal_test_pair_map(64, 4, 8, 0, None, P, P, None) == -1

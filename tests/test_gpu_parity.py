@@ -1,0 +1,293 @@
+"""GPU parity of libbifocal against the fp64 CPU oracle (needs an MI355X).
+
+All calls go through the C-ABI (via the ctypes binding). Tolerances are the
+ones the workloads are specified with: bf16 max-abs 2e-2 and mean-abs 2e-3,
+fp32 max-abs 1e-4; integer work (s(L), pair classification, correction
+offsets) is bit-exact. Full-size workloads are compared on seeded sampled
+rows the oracle evaluates one by one, always including the edge rows.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from rope_context_extension_bifocal_amd import bifocal as bfl
+from rope_context_extension_bifocal_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+BF16_MAX, BF16_MEAN, F32_MAX = 2e-2, 2e-3, 1e-4
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm GPU"
+    bfl.lib()
+    yield
+
+
+def _f32(t):
+    return t.detach().float().cpu().numpy()
+
+
+def _err(gpu, ref):
+    d = np.abs(np.asarray(gpu, np.float64) - ref)
+    return float(d.max()), float(d.mean())
+
+
+def _check_bf16(gpu, ref, what):
+    mx, mean = _err(gpu, ref)
+    print(f"[{what}] max-abs {mx:.3e} mean-abs {mean:.3e}", flush=True)
+    assert mx <= BF16_MAX and mean <= BF16_MEAN, what
+
+
+def _prefill_case(lens, Hq, Hkv, dtype, w0, w_pre, theta, mode, seed, rows_per_seq=None,
+                  edges=True, check_plain=False):
+    """Run GPU prefill on seeded inputs and compare with the oracle on all rows
+    (rows_per_seq None) or on sampled rows."""
+    cu = wl.cu_seqlens(lens)
+    T = cu[-1]
+    q, k, v = wl.prefill_inputs(Hq, Hkv, T, 128, dtype, seed)
+    scale = 1 / math.sqrt(128)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    o, lse = bfl.prefill(qd, kd, vd, cu, w0, w_pre, theta, mode, scale, return_lse=True)
+    torch.cuda.synchronize()
+    if rows_per_seq is None:
+        rows = np.arange(T)
+    else:
+        rows = []
+        for b, L in enumerate(lens):
+            e = [0, 1, w0 - 1, w0, w0 + 1, w_pre - 1, w_pre, L - 2, L - 1, 63, 64, 65] if edges else []
+            rows += list(cu[b] + wl.sample_rows(L, rows_per_seq, e, seed + 17 * b))
+        rows = np.array(rows, dtype=np.int64)
+    o_ref, lse_ref = oracle.prefill(_f32(q), _f32(k), _f32(v), cu, w0, w_pre, theta, mode, scale,
+                                    rows=rows)
+    og = _f32(o)[:, rows]
+    lg = _f32(lse)[:, rows]
+    return og, lg, o_ref, lse_ref, (q, k, v, cu, rows, qd, kd, vd)
+
+
+# ---------------------------------------------------------------- integer work
+@pytest.mark.parametrize("L,w0,w_pre,mode", [
+    (1, 0, 1, "fi"), (200, 17, 64, "fi"), (200, 17, 64, "pa"), (300, 0, 7, "pa"),
+    (129, 200, 16, "fi"), (1000, 64, 333, "pa"), (4096, 256, 1024, "pa")])
+def test_pair_map_bit_exact(L, w0, w_pre, mode):
+    br, num, s = bfl.test_pair_map(L, w0, w_pre, mode)
+    assert s == oracle.s_of_L(L, w_pre)
+    br = br.cpu().numpy()
+    i, j = np.meshgrid(np.arange(L), np.arange(L), indexing="ij")
+    sub = [(a, b) for a, b in zip(np.random.default_rng(L).integers(0, L, 2000),
+                                  np.random.default_rng(L + 1).integers(0, L, 2000))]
+    sub += [(a, b) for a in range(min(L, 40)) for b in range(min(L, 40))]
+    for a, b in sub:
+        assert br[a, b] == oracle.pair_branch(a, b, w0)
+    # closed form counts of the band
+    assert int((br == 1).sum()) == sum(min(x + 1, w0) for x in range(L))
+    assert int((br == 0).sum()) == L * (L - 1) // 2
+    num = num.cpu().numpy()
+    for p in list(range(min(L, 300))) + [L - 1]:
+        assert num[p] == round((oracle.phi(p, s, mode) - p) * s)
+
+
+# ---------------------------------------------------------------- prefill, fp32
+@pytest.mark.parametrize("mode", ["fi", "pa"])
+def test_tiny_fp32_s2_full(mode):
+    c = wl.CONFIGS["tiny_fp32_s2"]
+    og, lg, o_ref, lse_ref, _ = _prefill_case(c["lens"], c["Hq"], c["Hkv"], "fp32", c["w0"],
+                                              c["w_pre"], c["theta"], mode, c["seed"])
+    mx, mean = _err(og, o_ref)
+    print(f"[tiny fp32 {mode}] max-abs {mx:.3e} mean-abs {mean:.3e}", flush=True)
+    assert mx <= F32_MAX
+    assert _err(lg, lse_ref)[0] <= F32_MAX
+
+
+def test_tiny_fp32_discriminates():
+    # fp32 tolerance alone separates the method from plain attention and from
+    # the other long mode on this workload
+    c = wl.CONFIGS["tiny_fp32_s2"]
+    og, _, o_ref, _, (q, k, v, cu, rows, *_r) = _prefill_case(
+        c["lens"], c["Hq"], c["Hkv"], "fp32", c["w0"], c["w_pre"], c["theta"], "fi", c["seed"])
+    plain, _ = oracle.prefill(_f32(q), _f32(k), _f32(v), cu, 10**9, c["w_pre"], c["theta"], "fi",
+                              1 / math.sqrt(128), rows=rows)
+    pa, _ = oracle.prefill(_f32(q), _f32(k), _f32(v), cu, c["w0"], c["w_pre"], c["theta"], "pa",
+                           1 / math.sqrt(128), rows=rows)
+    assert _err(plain, o_ref)[0] > 100 * F32_MAX
+    assert _err(pa, o_ref)[0] > 100 * F32_MAX
+    assert _err(og, o_ref)[0] <= F32_MAX
+
+
+# ---------------------------------------------------------------- prefill, bf16 edges
+@pytest.mark.parametrize("lens,Hq,Hkv,w0,w_pre,mode", [
+    ([1], 4, 2, 0, 1, "fi"),
+    ([7], 2, 1, 3, 2, "pa"),
+    ([63], 4, 1, 17, 16, "fi"),
+    ([64], 4, 4, 64, 16, "pa"),
+    ([65], 8, 2, 1, 16, "fi"),
+    ([129], 3, 1, 0, 40, "pa"),
+    ([1000], 8, 1, 64, 333, "fi"),
+    ([4097], 4, 2, 256, 1024, "pa"),
+    ([33, 1, 200, 64, 700], 4, 2, 17, 50, "fi"),
+    ([300, 129, 65], 16, 2, 1000, 64, "pa"),
+])
+def test_prefill_bf16_edges(lens, Hq, Hkv, w0, w_pre, mode):
+    og, lg, o_ref, lse_ref, _ = _prefill_case(lens, Hq, Hkv, "bf16", w0, w_pre, 1e6, mode,
+                                              seed=sum(lens) + Hq)
+    _check_bf16(og, o_ref, f"bf16 edges {lens} G={Hq // Hkv} w0={w0} {mode}")
+    assert _err(lg, lse_ref)[0] <= BF16_MAX
+
+
+@pytest.mark.parametrize("mode", ["fi", "pa"])
+def test_prefill_bf16_shrunk_128k_geometry(mode):
+    # the 128K workload's geometry shrunk 16x: s = 4, GQA 4, several row blocks
+    og, lg, o_ref, lse_ref, (q, k, v, cu, rows, *_r) = _prefill_case(
+        [8192], 8, 2, "bf16", 256, 2048, 1e6, mode, seed=11, rows_per_seq=96)
+    _check_bf16(og, o_ref, f"shrunk s=4 {mode}")
+    plain, _ = oracle.prefill(_f32(q), _f32(k), _f32(v), cu, 10**9, 2048, 1e6, mode,
+                              1 / math.sqrt(128), rows=rows)
+    far_rows = rows >= 256
+    gap = np.linalg.norm(o_ref[:, far_rows] - plain[:, far_rows])
+    err = np.linalg.norm(og[:, far_rows] - o_ref[:, far_rows])
+    print(f"[discrimination {mode}] |gpu-ref| {err:.3e}  |ref-plain| {gap:.3e}", flush=True)
+    assert err <= 0.05 * gap
+
+
+def test_prefill_values_constant_one():
+    T, Hq, Hkv = 777, 4, 2
+    q, k, _ = wl.prefill_inputs(Hq, Hkv, T, 128, "bf16", 5)
+    v = torch.ones((Hkv, T, 128), dtype=torch.bfloat16)
+    o = bfl.prefill(q.cuda(), k.cuda(), v.cuda(), [0, T], 31, 100, 1e6, "pa")
+    assert torch.all(o.float() == 1.0)
+
+
+def test_prefill_deterministic_and_s1_equals_plain():
+    T, Hq, Hkv = 3000, 8, 4
+    q, k, v = (x.cuda() for x in wl.prefill_inputs(Hq, Hkv, T, 128, "bf16", 9))
+    a = bfl.prefill(q, k, v, [0, T], 128, 4096, 1e6, "fi")
+    b = bfl.prefill(q, k, v, [0, T], 128, 4096, 1e6, "fi")
+    assert torch.equal(a, b)
+    c = bfl.plain_prefill(q, k, v, [0, T])
+    assert torch.equal(a, c)          # s(3000) = 1 with w_pre = 4096
+    d = bfl.prefill(q, k, v, [0, T], 128, 1000, 1e6, "pa")
+    e = bfl.prefill(q, k, v, [0, T], 128, 1000, 1e6, "pa")
+    assert torch.equal(d, e) and not torch.equal(d, c)
+
+
+def test_plain_prefill_matches_oracle():
+    lens = [500, 77]
+    cu = wl.cu_seqlens(lens)
+    q, k, v = wl.prefill_inputs(4, 2, cu[-1], 128, "bf16", 21)
+    o = bfl.plain_prefill(q.cuda(), k.cuda(), v.cuda(), cu)
+    o_ref, _ = oracle.prefill(_f32(q), _f32(k), _f32(v), cu, 10**9, 1, 1e6, "fi",
+                              1 / math.sqrt(128))
+    _check_bf16(_f32(o), o_ref, "plain prefill")
+
+
+# ---------------------------------------------------------------- full-size workloads
+def test_qwen3_1p7b_32k_s1_equals_plain_and_oracle():
+    c = wl.CONFIGS["qwen3_1p7b_prefill_32k_s1"]
+    og, lg, o_ref, lse_ref, (q, k, v, cu, rows, qd, kd, vd) = _prefill_case(
+        c["lens"], c["Hq"], c["Hkv"], "bf16", c["w0"], c["w_pre"], c["theta"], "fi", c["seed"],
+        rows_per_seq=48)
+    _check_bf16(og, o_ref, "32k s=1")
+    o_b = bfl.prefill(qd, kd, vd, cu, c["w0"], c["w_pre"], c["theta"], "fi")
+    o_p = bfl.plain_prefill(qd, kd, vd, cu)
+    assert torch.equal(o_b, o_p)
+
+
+@pytest.mark.parametrize("mode", ["fi", "pa"])
+def test_qwen3_8b_128k_sampled(mode):
+    c = wl.CONFIGS["qwen3_8b_prefill_128k"]
+    og, lg, o_ref, lse_ref, (q, k, v, cu, rows, *_r) = _prefill_case(
+        c["lens"], c["Hq"], c["Hkv"], "bf16", c["w0"], c["w_pre"], c["theta"], mode, c["seed"],
+        rows_per_seq=24)
+    _check_bf16(og, o_ref, f"128k {mode}")
+    assert _err(lg, lse_ref)[0] <= BF16_MAX
+    other, _ = oracle.prefill(_f32(q), _f32(k), _f32(v), cu, c["w0"], c["w_pre"], c["theta"],
+                              "pa" if mode == "fi" else "fi", 1 / math.sqrt(128), rows=rows)
+    far_rows = rows >= c["w0"]
+    gap = np.linalg.norm(o_ref[:, far_rows] - other[:, far_rows])
+    err = np.linalg.norm(og[:, far_rows] - o_ref[:, far_rows])
+    print(f"[128k discrimination vs other mode] err {err:.3e} gap {gap:.3e}", flush=True)
+    assert err <= 0.05 * gap
+
+
+def test_qwen3_4b_ragged_sampled():
+    c = wl.CONFIGS["qwen3_4b_ragged_prefill"]
+    lens = wl.ragged_lengths(c["n_seqs"], c["len_lo"], c["len_hi"], c["seed"])
+    print(f"[ragged] lengths {lens} s {[oracle.s_of_L(L, c['w_pre']) for L in lens]}", flush=True)
+    og, lg, o_ref, lse_ref, _ = _prefill_case(lens, c["Hq"], c["Hkv"], "bf16", c["w0"],
+                                              c["w_pre"], c["theta"], "fi", c["seed"],
+                                              rows_per_seq=6)
+    _check_bf16(og, o_ref, "ragged")
+
+
+# ---------------------------------------------------------------- decode
+def _decode_case(N, cap, Hq, Hkv, w0, w_pre, theta, mode, seed, B=1):
+    q, kc, vc = wl.decode_inputs(B, Hq, Hkv, cap, 128, "bf16", seed)
+    scale = 1 / math.sqrt(128)
+    Ns = [N] * B if isinstance(N, int) else N
+    o, lse = bfl.decode(q.cuda(), kc.cuda(), vc.cuda(), Ns, w0, w_pre, theta, mode, scale,
+                        return_lse=True)
+    o_ref, lse_ref = oracle.decode(_f32(q), _f32(kc), _f32(vc), Ns, w0, w_pre, theta, mode, scale)
+    return _f32(o), _f32(lse), o_ref, lse_ref, (q, kc, vc, Ns)
+
+
+@pytest.mark.parametrize("mode", ["fi", "pa"])
+@pytest.mark.parametrize("Lc", [4096, 32768, 131072])
+def test_qwen3_8b_decode(Lc, mode):
+    c = wl.CONFIGS["qwen3_8b_decode"]
+    N = Lc + 1
+    og, lg, o_ref, lse_ref, (q, kc, vc, Ns) = _decode_case(
+        N, N, c["Hq"], c["Hkv"], c["w0"], c["w_pre"], c["theta"], mode,
+        c["seed"] + c["cache_lens"].index(Lc))
+    _check_bf16(og, o_ref, f"decode N={N} s={oracle.s_of_L(N, c['w_pre'])} {mode}")
+    assert _err(lg, lse_ref)[0] <= BF16_MAX
+    if oracle.s_of_L(N, c["w_pre"]) > 1:
+        plain, _ = oracle.decode(_f32(q), _f32(kc), _f32(vc), Ns, 10**9, c["w_pre"], c["theta"],
+                                 mode, 1 / math.sqrt(128))
+        gap = np.linalg.norm(o_ref - plain)
+        err = np.linalg.norm(og - o_ref)
+        print(f"[decode discrimination] err {err:.3e} gap {gap:.3e}", flush=True)
+        assert err <= 0.05 * gap
+
+
+@pytest.mark.parametrize("N,cap,B,G,w0,w_pre,mode", [
+    (1, 8, 1, 4, 0, 1, "fi"), (63, 70, 2, 2, 5, 16, "pa"), (64, 64, 1, 16, 64, 20, "fi"),
+    (65, 100, 3, 1, 1, 10, "pa"), (1000, 1024, 2, 8, 200, 300, "fi"),
+    ([5, 900, 4097], 4100, 3, 4, 256, 1024, "pa")])
+def test_decode_edges(N, cap, B, G, w0, w_pre, mode):
+    Hkv = 2
+    og, lg, o_ref, lse_ref, _ = _decode_case(N, cap, G * Hkv, Hkv, w0, w_pre, 1e6, mode, 77, B)
+    _check_bf16(og, o_ref, f"decode edges N={N} G={G}")
+    assert _err(lg, lse_ref)[0] <= BF16_MAX
+
+
+def test_plain_decode_matches_oracle():
+    q, kc, vc = wl.decode_inputs(2, 8, 2, 3000, 128, "bf16", 31)
+    Ns = [2999, 1234]
+    o = bfl.plain_decode(q.cuda(), kc.cuda(), vc.cuda(), Ns)
+    o_ref, _ = oracle.decode(_f32(q), _f32(kc), _f32(vc), Ns, 10**9, 1, 1e6, "fi",
+                             1 / math.sqrt(128))
+    _check_bf16(_f32(o), o_ref, "plain decode")
+
+
+@pytest.mark.parametrize("mode", ["fi", "pa"])
+def test_decode_equals_last_prefill_row(mode):
+    N, Hq, Hkv = 5000, 8, 2
+    q, k, v = wl.prefill_inputs(Hq, Hkv, N, 128, "bf16", 44)
+    o_pre = bfl.prefill(q.cuda(), k.cuda(), v.cuda(), [0, N], 300, 1024, 1e6, mode)
+    qd = q[:, N - 1].unsqueeze(0).contiguous().cuda()
+    o_dec = bfl.decode(qd, k.unsqueeze(0).cuda(), v.unsqueeze(0).cuda(), [N], 300, 1024, 1e6,
+                       mode)
+    d = (o_dec[0].float() - o_pre[:, N - 1].float()).abs().max().item()
+    print(f"[decode vs prefill last row] max-abs {d:.3e}", flush=True)
+    assert d <= BF16_MAX
+
+
+def test_decode_deterministic():
+    q, kc, vc = (x.cuda() for x in wl.decode_inputs(1, 32, 8, 40000, 128, "bf16", 3))
+    a = bfl.decode(q, kc, vc, [40000], 4096, 32768, 1e6, "pa")
+    b = bfl.decode(q, kc, vc, [40000], 4096, 32768, 1e6, "pa")
+    assert torch.equal(a, b)
