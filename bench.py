@@ -1,0 +1,261 @@
+"""Benchmark: bifocal prefill TFLOP/s on a 128K Qwen3-8B attention layer and
+bifocal decode GB/s over a 128K KV cache, on one MI355X.
+
+One step = one bifocal prefill (32 query / 8 KV heads, head_dim 128,
+L = 131072, w_pre = 32768 so s = 4, w0 = 4096, rope_theta 1e6, frequency
+interpolation, bf16) plus one bifocal decode of one query per head over the
+same layer's cache of N = 131073 keys (the new token's own key included, so
+s = 5). Inputs are seeded N(0,1) bf16 (synthetic), resident in HBM before the
+timed region.
+
+Prints one JSON line. `value` is the prefill effective TFLOP/s: algorithmic
+flops 4 * D * Hq * L (L + 1) / 2 (one score and one PV product per causal
+pair) over the measured prefill time. Extra fields report the decode
+bandwidth, position aliasing, the library's plain causal attention on the
+same shapes (overhead reference), roofline fractions against MI355X peaks
+(bf16 dense MFMA 2.5 PFLOP/s, HBM 8 TB/s) and the fp64 CPU oracle timed on a
+bounded row sample of the prefill workload.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from rope_context_extension_bifocal_amd import bifocal as bfl  # noqa: E402
+from rope_context_extension_bifocal_amd import workloads as wl  # noqa: E402
+
+METRIC = "bifocal prefill TFLOP/s + % MFMA peak @128K Qwen3-8B layer; decode GB/s"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCES = ["rope_context_extension_bifocal_amd/csrc/prefill.hip",
+                  "rope_context_extension_bifocal_amd/csrc/decode.hip",
+                  "rope_context_extension_bifocal_amd/csrc/capi.cpp",
+                  "rope_context_extension_bifocal_amd/csrc/bf_common.h"]
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_hash(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel_key):
+    """HBM traffic per launch from the committed rocprofv3 counter summary,
+    only if it was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    ent = data.get(kernel_key)
+    if not ent or ent.get("source_hash") != source_hash(KERNEL_SOURCES):
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def time_calls(fn, n, stream):
+    """Average ms of fn() over n calls, hipEvents on the stream the library
+    launches on (torch's current stream)."""
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(n):
+        fn()
+    end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end) / n
+
+
+def cpu_baseline(q, k, v, L, cfg, budget_s=15.0):
+    """The fp64 oracle as it stands, on a seeded sample of query rows of the
+    same prefill workload (all heads), timed on the host cores. The sample
+    grows until one run takes at least a third of the budget."""
+    import oracle
+
+    kf, vf = k.float().numpy(), v.float().numpy()
+    rng = np.random.default_rng(7)
+    n_rows = 4
+    while True:
+        rows = np.sort(rng.choice(L, size=n_rows, replace=False)).astype(np.int64)
+        q_rows = q[:, torch.from_numpy(rows)].float().numpy()
+        t0 = time.perf_counter()
+        oracle.prefill(q_rows, kf, vf, [0, L], cfg["w0"], cfg["w_pre"], cfg["theta"], "fi",
+                       1 / math.sqrt(q.shape[-1]), rows=rows, gathered=True)
+        dt = time.perf_counter() - t0
+        if dt >= budget_s / 3 or n_rows >= 4096:
+            break
+        n_rows = int(min(4096, n_rows * max(2.0, budget_s / max(dt, 1e-3))))
+    pairs = int(q.shape[0] * (rows + 1).sum())
+    return {"value": round(4.0 * q.shape[-1] * pairs / dt / 1e12, 6), "unit": "TFLOP/s",
+            "cores": oracle.threads(), "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"{len(rows)} seeded query rows x {q.shape[0]} heads of the 128K FI "
+                      f"prefill workload ({pairs} causal pairs; key/value setup included)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the per-GPU shard is the single-GPU workload). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    bfl.lib()
+    stream = torch.cuda.current_stream()
+
+    cfg = wl.CONFIGS["qwen3_8b_prefill_128k"]
+    dcfg = wl.CONFIGS["qwen3_8b_decode"]
+    L = cfg["lens"][0]
+    Hq, Hkv, D = cfg["Hq"], cfg["Hkv"], cfg["D"]
+    scale = 1 / math.sqrt(D)
+    log("generating 128K prefill inputs")
+    q, k, v = wl.prefill_inputs(Hq, Hkv, L, D, "bf16", cfg["seed"])
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    cu = [0, L]
+    o = torch.empty_like(qd)
+    ws_p = bfl.alloc_workspace(bfl.workspace_bytes(bfl.BF_PHASE_PREFILL, 1, L, Hq, Hkv), "cuda")
+    N = dcfg["cache_lens"][2] + 1
+    log("generating 128K decode inputs")
+    qdc, kc, vc = wl.decode_inputs(1, Hq, Hkv, N, D, "bf16", dcfg["seed"] + 2)
+    qdc, kc, vc = qdc.cuda(), kc.cuda(), vc.cuda()
+    od = torch.empty_like(qdc)
+    ws_d = bfl.alloc_workspace(bfl.workspace_bytes(bfl.BF_PHASE_DECODE, 1, N, Hq, Hkv), "cuda")
+
+    def prefill(mode="fi"):
+        bfl.prefill(qd, kd, vd, cu, cfg["w0"], cfg["w_pre"], cfg["theta"], mode, scale, out=o,
+                    workspace=ws_p)
+
+    def plain_prefill():
+        bfl.plain_prefill(qd, kd, vd, cu, scale, out=o, workspace=ws_p)
+
+    def decode(mode="fi"):
+        bfl.decode(qdc, kc, vc, [N], dcfg["w0"], dcfg["w_pre"], dcfg["theta"], mode, scale,
+                   out=od, workspace=ws_d)
+
+    def plain_decode():
+        bfl.plain_decode(qdc, kc, vc, [N], scale, out=od, workspace=ws_d)
+
+    flops = 4.0 * D * Hq * L * (L + 1) / 2
+    kv_bytes = 2.0 * N * Hkv * D * 2
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        prefill()
+        decode()
+    torch.cuda.synchronize()
+
+    # timed region: K steps, each one prefill and one decode, events per part
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1, e2 in ev:
+        e0.record(stream)
+        prefill()
+        e1.record(stream)
+        decode()
+        e2.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pre_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
+    dec_ms = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
+    log(f"timed: prefill {pre_ms:.3f} ms, decode {dec_ms * 1e3:.1f} us, wall {wall:.3f} s")
+
+    # references outside the timed region
+    prefill("pa")
+    pa_ms = time_calls(lambda: prefill("pa"), 3, stream)
+    plain_prefill()
+    plain_ms = time_calls(plain_prefill, 3, stream)
+    for _ in range(10):
+        decode()
+    dec_many_ms = time_calls(decode, 50, stream)
+    for _ in range(10):
+        plain_decode()
+    plain_dec_ms = time_calls(plain_decode, 50, stream)
+    small = {}
+    for Lc in dcfg["cache_lens"][:2]:
+        n = Lc + 1
+        qs, ks, vs = (x.cuda() for x in wl.decode_inputs(1, Hq, Hkv, n, D, "bf16", dcfg["seed"]))
+        ws_s = bfl.alloc_workspace(bfl.workspace_bytes(bfl.BF_PHASE_DECODE, 1, n, Hq, Hkv), "cuda")
+        fn = lambda: bfl.decode(qs, ks, vs, [n], dcfg["w0"], dcfg["w_pre"], dcfg["theta"], "fi",
+                                scale, workspace=ws_s)
+        pfn = lambda: bfl.plain_decode(qs, ks, vs, [n], scale, workspace=ws_s)
+        for _ in range(10):
+            fn()
+            pfn()
+        t_b = time_calls(fn, 100, stream)
+        t_p = time_calls(pfn, 100, stream)
+        small[str(n)] = {"bifocal_us": round(t_b * 1e3, 2), "plain_us": round(t_p * 1e3, 2),
+                         "bifocal_gbs": round(2.0 * n * Hkv * D * 2 / (t_b * 1e-3) / 1e9, 1)}
+
+    tflops = flops / (pre_ms * 1e-3) / 1e12
+    gbs = kv_bytes / (dec_ms * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(pre_ms + dec_ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "qwen3_8b_prefill_128k (FI) + qwen3_8b_decode_128k",
+                   "batch": 1, "seq_len": L, "n_heads_q": Hq, "n_heads_kv": Hkv, "head_dim": D,
+                   "w_pre": cfg["w_pre"], "w0": cfg["w0"], "rope_theta": cfg["theta"],
+                   "s_prefill": bfl.s_of_L(L, cfg["w_pre"]), "decode_keys": N,
+                   "s_decode": bfl.s_of_L(N, dcfg["w_pre"]), "long_mode": "fi"},
+        "prefill_ms": round(pre_ms, 3),
+        "prefill_frac_mfma_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "prefill_pa_tflops": round(flops / (pa_ms * 1e-3) / 1e12, 2),
+        "plain_prefill_tflops": round(flops / (plain_ms * 1e-3) / 1e12, 2),
+        "prefill_overhead_vs_plain": round(pre_ms / plain_ms - 1, 4),
+        "prefill_pa_overhead_vs_plain": round(pa_ms / plain_ms - 1, 4),
+        "decode_us": round(dec_ms * 1e3, 2),
+        "decode_gbs": round(gbs, 1),
+        "decode_frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+        "decode_us_50_calls": round(dec_many_ms * 1e3, 2),
+        "plain_decode_us": round(plain_dec_ms * 1e3, 2),
+        "decode_overhead_vs_plain": round(dec_many_ms / plain_dec_ms - 1, 4),
+        "decode_small": small,
+        "roofline": {"kernel": "bifocal_prefill call (correction prep + V^T + MFMA tile loop)",
+                     "bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic_for("prefill_bf16_kernel_bifocal")},
+        "roofline_decode": {"kernel": "bifocal_decode call (split-K + combine)", "bound": "hbm",
+                            "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                            "frac": round(gbs / PEAK_HBM_GBS, 4),
+                            "traffic": traffic_for("decode_split_kernel_bifocal")},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a row sample")
+        result["cpu_baseline"] = cpu_baseline(q, k, v, L, cfg)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -73,21 +73,24 @@ def rope_rotate(x, pos, theta):
     return y
 
 
-def prefill(q, k, v, cu_seqlens, w0, w_pre, theta, mode, scale, rows=None, variant=0):
+def prefill(q, k, v, cu_seqlens, w0, w_pre, theta, mode, scale, rows=None, variant=0,
+            gathered=False):
     """Bifocal prefill at query rows `rows` (global packed token indices; all
-    rows when None).  q [Hq,T,D], k/v [Hkv,T,D].  Returns fp64 (o [Hq,R,D],
-    lse [Hq,R]).  variant 1 evaluates the inclusion-exclusion partials."""
+    rows when None).  q [Hq,T,D] (or [Hq,R,D] already gathered at `rows` when
+    gathered=True), k/v [Hkv,T,D].  Returns fp64 (o [Hq,R,D], lse [Hq,R]).
+    variant 1 evaluates the inclusion-exclusion partials."""
     k = _f32(k)
     v = _f32(v)
     q = np.asarray(q)
-    Hq, T, D = q.shape
+    Hq, _, D = q.shape
+    T = k.shape[1]
     Hkv = k.shape[0]
     cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
     B = cu.shape[0] - 1
     if rows is None:
         rows = np.arange(T, dtype=np.int64)
     rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
-    q_rows = _f32(q[:, rows, :])
+    q_rows = _f32(q) if gathered else _f32(q[:, rows, :])
     R = rows.shape[0]
     o = np.empty((Hq, R, D), dtype=np.float64)
     lse = np.empty((Hq, R), dtype=np.float64)
