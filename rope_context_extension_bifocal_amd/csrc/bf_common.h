@@ -10,7 +10,7 @@ constexpr int kHeadDim = 128;     // the only head_dim the kernels are built for
 constexpr int kPairs = kHeadDim / 2;
 constexpr int kMaxSeqPerLaunch = 64;
 constexpr int kKeyTile = 64;      // keys per K/V tile (prefill) and V^T padding unit
-constexpr int kWaveRowsBf16 = 64; // query positions per wave, bf16 prefill
+constexpr int kWaveRowsBf16 = 32; // query positions per wave, bf16 prefill
 constexpr int kWaveRowsF32 = 32;  // query positions per wave, fp32 prefill
 constexpr int kWavesPerGroup = 4; // waves per prefill workgroup (256 lanes)
 

@@ -210,226 +210,253 @@ __device__ __forceinline__ void online_softmax_rescale(float& m_run, float& l_ru
 }
 
 // --------------------------------------------------------------- bf16
-// Workgroup: 4 waves; wave = (query head, 64 query positions). G query heads
-// of one KV group share every staged K/V tile. Per wave and 64-key tile:
-// S^T = K Q^T as 2x2 MFMA 32x32x16 blocks (keys x queries), then O^T += V^T P^T
-// as 4x2 blocks (head dim x queries). A lane owns one query column of each
-// block, so row max / sum need one exchange with the other lane half.
-template <bool BIFOCAL>
-__device__ __forceinline__ void qk_bf16(const uint4* __restrict__ sk, const bf16x8 (&q)[2][8],
-                                        int li, int hl, f32x16 (&S)[2][2]) {
-#pragma unroll
-  for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-    for (int ib = 0; ib < 2; ++ib) S[jb][ib] = f32x16{};
+// Workgroup: 4 waves; wave = (query head, 32 query positions); two workgroups
+// share a CU, so each SIMD runs two independent waves whose softmax (VALU) and
+// matrix (MFMA) phases overlap. The G query heads of one KV group share every
+// staged K/V tile. Scores are formed as S^T = K Q^T on MFMA 32x32x16 blocks
+// (keys x queries) and the output as O^T += V^T P^T (head dims x queries); a
+// lane owns one query column, so a row max needs one exchange with the other
+// lane half and the row sum none until the end.
+//
+// The far branch and the local branch run as two passes over their own tile
+// ranges with one online-softmax state: the far pass (q'' . k'' on every tile
+// that holds a far pair, local pairs masked out) leaves its partial
+// (m, l, O) in place, and the local pass (q' . k' on every tile that holds a
+// band pair, far pairs masked out) continues from it. Carrying the state over
+// is the log-sum-exp merge of the two branch partials, so every causal pair is
+// counted once and the scaled-branch work over the band is never done. Only
+// the one or two tiles at the window edge are visited by both passes.
+//
+// K and V^T tiles (64 keys) are staged by direct global->LDS loads one tile
+// ahead (two slots each). The O accumulator is rescaled only when a row max
+// grows by more than 2^8: numerator and denominator share the same stale max,
+// so the result is unchanged, and probabilities stay below 2^8.
+constexpr float kRescaleLog2 = 8.f;
+constexpr int kSlot = 1024;  // 16-byte chunks per staged 64 x 128 bf16 tile
+
+struct WaveRows {
+  int r0;  // first query position of the wave (sequence-relative)
+  int L;   // sequence length
+  int w0;  // local window, clamped to 2^30 (s = 1 or the plain engine: all local)
+};
+
+struct RowState {
+  float m_used;  // stale row max in scaled log2 units (-inf: no key yet)
+  float l_part;  // this lane half's share of the row sum
+};
+
+__device__ __forceinline__ void qk_tile(const uint4* __restrict__ sk, const bf16x8 (&q)[8], int li,
+                                        int hl, f32x16 (&S)[2]) {
+  S[0] = f32x16{};
+  S[1] = f32x16{};
   const int row0 = key_of_mfma_row(li), row1 = 32 + row0;
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
     const int ch = 2 * t + hl;
     const bf16x8 a0 = __builtin_bit_cast(bf16x8, sk[row0 * 16 + (ch ^ (row0 & 15))]);
     const bf16x8 a1 = __builtin_bit_cast(bf16x8, sk[row1 * 16 + (ch ^ (row1 & 15))]);
-    S[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, q[0][t], S[0][0], 0, 0, 0);
-    S[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, q[1][t], S[0][1], 0, 0, 0);
-    S[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, q[0][t], S[1][0], 0, 0, 0);
-    S[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, q[1][t], S[1][1], 0, 0, 0);
+    S[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, q[t], S[0], 0, 0, 0);
+    S[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, q[t], S[1], 0, 0, 0);
+  }
+}
+
+// Mask a tile (keys c0 .. c0 + 63) for a pass: the far pass keeps pairs with
+// i - j >= w0, the local pass keeps 0 <= i - j < w0.
+template <bool FAR>
+__device__ __forceinline__ void mask_tile(f32x16 (&S)[2], const WaveRows& wr, int c0, int li,
+                                          int hl) {
+  const int dmax = wr.r0 + 31 - c0;
+  const int dmin = wr.r0 - (c0 + 63);
+  const bool full = FAR ? (dmin >= wr.w0) : (dmin >= 0 && dmax < wr.w0);
+  if (full) return;
+  const int base = wr.r0 + li - c0 - 8 * hl;  // i - j = base - 32 jb - 16 (r / 8) - r % 8
+#pragma unroll
+  for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int d = base - 32 * jb - 16 * (r >> 3) - (r & 7);
+      const bool keep = FAR ? (d >= wr.w0) : (d >= 0 && d < wr.w0);
+      if (!keep) S[jb][r] = -INFINITY;
+    }
+}
+
+__device__ __forceinline__ void pv_tile(const uint4* __restrict__ sv, const bf16x8 (&P)[2][2],
+                                        int li, int hl, f32x16 (&oacc)[4]) {
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    const int d = 32 * db + li;
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int ch = 4 * jb + 2 * u + hl;
+        const bf16x8 a = __builtin_bit_cast(bf16x8, sv[d * 8 + (ch ^ (d & 7))]);
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, P[jb][u], oacc[db], 0, 0, 0);
+      }
+  }
+}
+
+__device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Direct global -> LDS staging (16 bytes per lane, 1 KiB per wave instruction).
+// LDS chunk p of a K tile holds row p / 16, swizzled column (p % 16) ^ (row % 16);
+// keys past the sequence end read the last key (finite data, masked later).
+__device__ __forceinline__ void stage_k(uint4* slot, const uint16_t* kptr, int c0, int L,
+                                        int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int p = (4 * i + wave) * 64 + lane;
+    const int row = p >> 4, col = (p & 15) ^ (row & 15);
+    const int key = min(c0 + row, L - 1);
+    __builtin_amdgcn_global_load_lds(
+        (const __attribute__((address_space(1))) void*)(kptr + (size_t)key * kHeadDim + col * 8),
+        (__attribute__((address_space(3))) void*)(slot + (4 * i + wave) * 64), 16, 0, 0);
+  }
+}
+
+// V^T tile: LDS chunk p holds head dim p / 8, swizzled key chunk (p % 8) ^ (d % 8).
+__device__ __forceinline__ void stage_v(uint4* slot, const uint16_t* vtg, int Tpad, int c0,
+                                        int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int p = (4 * i + wave) * 64 + lane;
+    const int d = p >> 3, col = (p & 7) ^ (d & 7);
+    __builtin_amdgcn_global_load_lds(
+        (const __attribute__((address_space(1))) void*)(vtg + (size_t)d * Tpad + c0 + col * 8),
+        (__attribute__((address_space(3))) void*)(slot + (4 * i + wave) * 64), 16, 0, 0);
+  }
+}
+
+// One pass (far or local) of a wave over tiles [ktb, kte).
+template <bool FAR>
+__device__ __forceinline__ void run_pass(const uint16_t* qsrc, const uint16_t* ksrc,
+                                         const uint16_t* vtg, int Tpad, int ktb, int kte,
+                                         const WaveRows& wr, float sc, int wave, int lane,
+                                         uint4* sK, uint4* sV, RowState& rs,
+                                         f32x16 (&oacc)[4]) {
+  const int li = lane & 31, hl = lane >> 5;
+  bf16x8 qf[8];
+  {
+    const int row = wr.r0 + li;
+    const bool ok = row < wr.L;
+    const int rowc = ok ? row : wr.L - 1;  // in-bounds address, value zeroed below
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      uint4 v = *(const uint4*)(qsrc + (size_t)rowc * kHeadDim + (2 * t + hl) * 8);
+      if (!ok) v = make_uint4(0, 0, 0, 0);
+      qf[t] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+  __syncthreads();  // LDS of a previous pass is no longer read
+  stage_k(sK + (ktb & 1) * kSlot, ksrc, ktb * kKeyTile, wr.L, wave, lane);
+  stage_v(sV + (ktb & 1) * kSlot, vtg, Tpad, ktb * kKeyTile, wave, lane);
+  for (int t = ktb; t < kte; ++t) {
+    const int c0 = t * kKeyTile;
+    wait_vmem_all();
+    __syncthreads();  // tile t landed for every wave; slot (t + 1) & 1 is free
+    if (t + 1 < kte) {
+      stage_k(sK + ((t + 1) & 1) * kSlot, ksrc, c0 + kKeyTile, wr.L, wave, lane);
+      stage_v(sV + ((t + 1) & 1) * kSlot, vtg, Tpad, c0 + kKeyTile, wave, lane);
+    }
+    if (wr.r0 >= wr.L || c0 > wr.r0 + 31) continue;  // no causal pair of this wave here
+    f32x16 S[2];
+    qk_tile(sK + (t & 1) * kSlot, qf, li, hl, S);
+    mask_tile<FAR>(S, wr, c0, li, hl);
+    // row max (the lane's query), lazily applied
+    float m = -INFINITY;
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) m = fmaxf(m, fmaxf(S[jb][r], S[jb][r + 1]));
+    m = fmaxf(m, __shfl_xor(m, 32)) * sc;
+    if (__any(m > rs.m_used + kRescaleLog2)) {
+      const float mn = fmaxf(rs.m_used, m);
+      const float alpha = (rs.m_used == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(rs.m_used - mn);
+      rs.l_part *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
+      rs.m_used = mn;
+    }
+    const float mb = (rs.m_used == -INFINITY) ? 0.f : rs.m_used;
+    bf16x8 P[2][2];
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        bf16x8 v;
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const float x0 = __builtin_amdgcn_exp2f(fmaf(S[jb][8 * u + e], sc, -mb));
+          const float x1 = __builtin_amdgcn_exp2f(fmaf(S[jb][8 * u + e + 1], sc, -mb));
+          s0 += x0;
+          s1 += x1;
+          v[e] = (__bf16)x0;
+          v[e + 1] = (__bf16)x1;
+        }
+        P[jb][u] = v;
+      }
+    rs.l_part += s0 + s1;
+    pv_tile(sV + (t & 1) * kSlot, P, li, hl, oacc);
   }
 }
 
 template <bool BIFOCAL>
-__global__ __launch_bounds__(256, 1) void prefill_bf16_kernel(PrefillParams p, SeqTable st) {
+__global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillParams p, SeqTable st) {
   extern __shared__ uint4 smem[];
-  uint4* sK = smem;                         // K' tile   [64][16 x 16 B], swizzled
-  uint4* sK2 = smem + 1024;                 // K'' tile
-  uint4* sV = smem + (BIFOCAL ? 2048 : 1024);  // V^T tile [128][8 x 16 B], swizzled
-
+  uint4* sK = smem;             // 2 slots
+  uint4* sV = smem + 2 * kSlot;  // 2 slots
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 31, hl = lane >> 5;
   const Item it = make_item<BIFOCAL>(p, st, wave, kWaveRowsBf16);
-  const long long w0 = it.w0;
+  const WaveRows wr{it.r0, it.L, (int)min(it.w0, (long long)(1 << 30))};
 
   const uint16_t* qg = (const uint16_t*)p.q + ((size_t)it.hq * p.T + it.tok0) * kHeadDim;
   const uint16_t* kg = (const uint16_t*)p.k + ((size_t)it.kvh * p.T + it.tok0) * kHeadDim;
-  const uint16_t* q2g = BIFOCAL ? (const uint16_t*)p.q2 + ((size_t)it.hq * p.T + it.tok0) * kHeadDim : nullptr;
-  const uint16_t* k2g = BIFOCAL ? (const uint16_t*)p.k2 + ((size_t)it.kvh * p.T + it.tok0) * kHeadDim : nullptr;
   const uint16_t* vtg = (const uint16_t*)p.vt + (size_t)it.kvh * kHeadDim * p.Tpad + st.vt_off[it.b];
 
-  // Q fragments (B operand): lane (li, hl) holds query r0 + 32 ib + li,
-  // head dims 16 t + 8 hl .. +7 for k-step t.
-  bf16x8 qf[2][8], qf2[2][8];
-  const uint4 zero4 = make_uint4(0, 0, 0, 0);
+  RowState rs{-INFINITY, 0.f};
+  f32x16 oacc[4];
 #pragma unroll
-  for (int ib = 0; ib < 2; ++ib) {
-    const int row = it.r0 + 32 * ib + li;
-    const bool ok = row < it.L;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const size_t off = (size_t)row * kHeadDim + (2 * t + hl) * 8;
-      qf[ib][t] = __builtin_bit_cast(bf16x8, ok ? *(const uint4*)(qg + off) : zero4);
-      if constexpr (BIFOCAL)
-        qf2[ib][t] = __builtin_bit_cast(bf16x8, (ok && w0 < it.L) ? *(const uint4*)(q2g + off) : zero4);
-    }
+  for (int db = 0; db < 4; ++db) oacc[db] = f32x16{};
+
+  // tile ranges of the two passes for the workgroup's rows R0 .. R0 + P_wg - 1
+  const long long R0 = it.R0, Rl = (long long)it.R0 + p.P_wg - 1;
+  const long long w0 = it.w0;
+  if (BIFOCAL && Rl - w0 >= 0) {  // far pairs exist: keys j <= Rl - w0
+    const int kte = min(it.nkt, (int)((Rl - w0) / kKeyTile) + 1);
+    run_pass<true>((const uint16_t*)p.q2 + ((size_t)it.hq * p.T + it.tok0) * kHeadDim,
+                   (const uint16_t*)p.k2 + ((size_t)it.kvh * p.T + it.tok0) * kHeadDim, vtg,
+                   p.Tpad, 0, kte, wr, p.scale_log2, wave, lane, sK, sV, rs, oacc);
   }
-
-  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
-  f32x16 oacc[4][2];
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int ib = 0; ib < 2; ++ib) oacc[db][ib] = f32x16{};
-
-  // register prefetch of the next tile: K' / K'' rows (4 x 16 B each) and V^T (4 x 16 B)
-  uint4 pk[4], pk2[4], pv[4];
-  bool nf = false, nl = true;
-  auto load_tile = [&](int c0, bool need_far, bool need_loc) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i;
-      const int row = c >> 4, col = c & 15;
-      const bool ok = c0 + row < it.L;
-      const size_t off = (size_t)(c0 + row) * kHeadDim + col * 8;
-      if (need_loc) pk[i] = ok ? *(const uint4*)(kg + off) : zero4;
-      if constexpr (BIFOCAL)
-        if (need_far) pk2[i] = ok ? *(const uint4*)(k2g + off) : zero4;
-      const int d = c >> 3, vc = c & 7;
-      pv[i] = *(const uint4*)(vtg + (size_t)d * p.Tpad + c0 + vc * 8);
-    }
-  };
-  tile_needs<BIFOCAL>(it.R0, p.P_wg, 0, w0, nf, nl);
-  load_tile(0, nf, nl);
-
-  for (int kt = 0; kt < it.nkt; ++kt) {
-    const int c0 = kt * kKeyTile;
-    const bool cf = nf, cl = nl;
-    __syncthreads();  // previous tile's LDS reads are done
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i;
-      const int row = c >> 4, col = c & 15;
-      if (cl) sK[row * 16 + (col ^ (row & 15))] = pk[i];
-      if constexpr (BIFOCAL)
-        if (cf) sK2[row * 16 + (col ^ (row & 15))] = pk2[i];
-      const int d = c >> 3, vc = c & 7;
-      sV[d * 8 + (vc ^ (d & 7))] = pv[i];
-    }
-    __syncthreads();
-    if (kt + 1 < it.nkt) {
-      tile_needs<BIFOCAL>(it.R0, p.P_wg, c0 + kKeyTile, w0, nf, nl);
-      load_tile(c0 + kKeyTile, nf, nl);
-    }
-
-    const bool wave_skip = (it.r0 >= it.L) || (c0 > it.r0 + kWaveRowsBf16 - 1);
-    if (wave_skip) continue;
-    const long long dmax = (long long)it.r0 + kWaveRowsBf16 - 1 - c0;
-    const long long dmin = (long long)it.r0 - (c0 + kKeyTile - 1);
-    const bool has_far = BIFOCAL && dmax >= w0;
-    const bool has_loc = !BIFOCAL || (w0 > 0 && dmin < w0);
-
-    f32x16 S[2][2];
-    if (BIFOCAL && has_far) qk_bf16<BIFOCAL>(sK2, qf2, li, hl, S);
-    else qk_bf16<BIFOCAL>(sK, qf, li, hl, S);
-    if (BIFOCAL && has_far && has_loc) {  // mixed tile: choose per pair
-      f32x16 Sl[2][2];
-      qk_bf16<BIFOCAL>(sK, qf, li, hl, Sl);
-#pragma unroll
-      for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-        for (int ib = 0; ib < 2; ++ib) {
-          const long long i = it.r0 + 32 * ib + li;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const long long j = c0 + 32 * jb + key_of_acc(r, hl);
-            if (pair_is_local(i, j, w0)) S[jb][ib][r] = Sl[jb][ib][r];
-          }
-        }
-    }
-    if (dmin < 0) {  // causal mask on the diagonal tile
-#pragma unroll
-      for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-        for (int ib = 0; ib < 2; ++ib) {
-          const int i = it.r0 + 32 * ib + li;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int j = c0 + 32 * jb + key_of_acc(r, hl);
-            if (j > i) S[jb][ib][r] = -INFINITY;
-          }
-        }
-    }
-
-    // online softmax, one state per query row
-    bf16x8 pb[2][2][2];  // [ib][jb][u]
-#pragma unroll
-    for (int ib = 0; ib < 2; ++ib) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[jb][ib][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      float mbase, alpha;
-      online_softmax_rescale(m_run[ib], l_run[ib], mx, p.scale_log2, mbase, alpha);
-      float rs = 0.f;
-#pragma unroll
-      for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float e = __builtin_amdgcn_exp2f(fmaf(S[jb][ib][r], p.scale_log2, -mbase));
-          S[jb][ib][r] = e;
-          rs += e;
-        }
-      rs += __shfl_xor(rs, 32);
-      l_run[ib] = l_run[ib] * alpha + rs;
-#pragma unroll
-      for (int db = 0; db < 4; ++db) oacc[db][ib] *= alpha;
-#pragma unroll
-      for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          bf16x8 v;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = (__bf16)S[jb][ib][8 * u + e];
-          pb[ib][jb][u] = v;
-        }
-    }
-    // O^T += V^T P^T
-#pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      const int d = 32 * db + li;
-#pragma unroll
-      for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int ch = 4 * jb + 2 * u + hl;
-          const bf16x8 a = __builtin_bit_cast(bf16x8, sV[d * 8 + (ch ^ (d & 7))]);
-          oacc[db][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[0][jb][u], oacc[db][0], 0, 0, 0);
-          oacc[db][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[1][jb][u], oacc[db][1], 0, 0, 0);
-        }
-    }
+  if (w0 > 0) {  // local pairs exist: keys j > R0 - w0 (and j <= Rl)
+    const long long first = R0 - w0 + 1;  // smallest key with a local pair
+    const int ktb = first <= 0 ? 0 : (int)(first / kKeyTile);
+    if (ktb < it.nkt)
+      run_pass<false>(qg, kg, vtg, p.Tpad, ktb, it.nkt, wr, p.scale_log2, wave, lane, sK, sV, rs,
+                      oacc);
   }
 
   // epilogue: normalise, store O (bf16) and lse
-  if (it.r0 >= it.L) return;
+  const int row = it.r0 + li;
+  const float l = rs.l_part + __shfl_xor(rs.l_part, 32);
+  if (row >= it.L) return;
   uint16_t* og = (uint16_t*)p.o + ((size_t)it.hq * p.T + it.tok0) * kHeadDim;
+  const float inv = 1.f / l;
 #pragma unroll
-  for (int ib = 0; ib < 2; ++ib) {
-    const int row = it.r0 + 32 * ib + li;
-    if (row >= it.L) continue;
-    const float inv = 1.f / l_run[ib];
+  for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d = 32 * db + 8 * g + 4 * hl;
-        uint2 w;
-        w.x = (uint32_t)f32_to_bf16(oacc[db][ib][4 * g + 0] * inv) |
-              ((uint32_t)f32_to_bf16(oacc[db][ib][4 * g + 1] * inv) << 16);
-        w.y = (uint32_t)f32_to_bf16(oacc[db][ib][4 * g + 2] * inv) |
-              ((uint32_t)f32_to_bf16(oacc[db][ib][4 * g + 3] * inv) << 16);
-        *(uint2*)(og + (size_t)row * kHeadDim + d) = w;
-      }
-    if (p.lse && hl == 0)
-      p.lse[(size_t)it.hq * p.T + it.tok0 + row] = (m_run[ib] + __log2f(l_run[ib])) * 0.69314718055994530942f;
-  }
+    for (int g = 0; g < 4; ++g) {
+      const int d = 32 * db + 8 * g + 4 * hl;
+      uint2 w;
+      w.x = (uint32_t)f32_to_bf16(oacc[db][4 * g + 0] * inv) |
+            ((uint32_t)f32_to_bf16(oacc[db][4 * g + 1] * inv) << 16);
+      w.y = (uint32_t)f32_to_bf16(oacc[db][4 * g + 2] * inv) |
+            ((uint32_t)f32_to_bf16(oacc[db][4 * g + 3] * inv) << 16);
+      *(uint2*)(og + (size_t)row * kHeadDim + d) = w;
+    }
+  if (p.lse && hl == 0)
+    p.lse[(size_t)it.hq * p.T + it.tok0 + row] = (rs.m_used + __log2f(l)) * 0.69314718055994530942f;
 }
 
 // --------------------------------------------------------------- fp32
@@ -478,13 +505,17 @@ __global__ __launch_bounds__(256, 1) void prefill_f32_kernel(PrefillParams p, Se
   {
     const int row = it.r0 + li;
     const bool ok = row < it.L;
+    const bool ok2 = ok && w0 < it.L;  // corrected queries exist only with far pairs
+    const int rowc = ok ? row : it.L - 1;
 #pragma unroll
     for (int tc = 0; tc < 16; ++tc) {
-      const size_t off = (size_t)row * kHeadDim + 64 * hl + 4 * tc;
-      const float4 a = ok ? *(const float4*)(qg + off) : make_float4(0, 0, 0, 0);
+      const size_t off = (size_t)rowc * kHeadDim + 64 * hl + 4 * tc;
+      float4 a = *(const float4*)(qg + off);
+      if (!ok) a = make_float4(0, 0, 0, 0);
       qf[4 * tc] = a.x; qf[4 * tc + 1] = a.y; qf[4 * tc + 2] = a.z; qf[4 * tc + 3] = a.w;
       if constexpr (BIFOCAL) {
-        const float4 c = (ok && w0 < it.L) ? *(const float4*)(q2g + off) : make_float4(0, 0, 0, 0);
+        float4 c = make_float4(0, 0, 0, 0);
+        if (ok2) c = *(const float4*)(q2g + off);
         qf2[4 * tc] = c.x; qf2[4 * tc + 1] = c.y; qf2[4 * tc + 2] = c.z; qf2[4 * tc + 3] = c.w;
       }
     }
@@ -506,10 +537,18 @@ __global__ __launch_bounds__(256, 1) void prefill_f32_kernel(PrefillParams p, Se
       const int c = tid + 256 * i;
       const int row = c >> 5, col = c & 31;
       const bool ok = c0 + row < it.L;
-      const size_t off = (size_t)(c0 + row) * kHeadDim + col * 4;
-      if (cl) sK[row * 32 + (col ^ (row & 31))] = ok ? *(const uint4*)(kg + off) : zero4;
+      const size_t off = (size_t)min(c0 + row, it.L - 1) * kHeadDim + col * 4;
+      if (cl) {
+        uint4 kv = *(const uint4*)(kg + off);
+        if (!ok) kv = zero4;
+        sK[row * 32 + (col ^ (row & 31))] = kv;
+      }
       if constexpr (BIFOCAL)
-        if (cf) sK2[row * 32 + (col ^ (row & 31))] = ok ? *(const uint4*)(k2g + off) : zero4;
+        if (cf) {
+          uint4 kv = *(const uint4*)(k2g + off);
+          if (!ok) kv = zero4;
+          sK2[row * 32 + (col ^ (row & 31))] = kv;
+        }
       const int d = c >> 4, vc = c & 15;
       sV[d * 16 + (vc ^ (d & 15))] = *(const uint4*)(vtg + (size_t)d * p.Tpad + c0 + vc * 4);
     }
@@ -652,8 +691,8 @@ static hipError_t launch_with_lds(K kernel, int grid, size_t lds, hipStream_t st
 hipError_t launch_prefill_main(int dtype, bool bifocal, const PrefillParams& pp,
                                const SeqTable& st, int grid, hipStream_t stream) {
   if (dtype == 0) {
-    if (bifocal) return launch_with_lds(prefill_bf16_kernel<true>, grid, 3 * 16384, stream, pp, st);
-    return launch_with_lds(prefill_bf16_kernel<false>, grid, 2 * 16384, stream, pp, st);
+    if (bifocal) return launch_with_lds(prefill_bf16_kernel<true>, grid, 4 * 16384, stream, pp, st);
+    return launch_with_lds(prefill_bf16_kernel<false>, grid, 4 * 16384, stream, pp, st);
   }
   if (bifocal) return launch_with_lds(prefill_f32_kernel<true>, grid, 3 * 32768, stream, pp, st);
   return launch_with_lds(prefill_f32_kernel<false>, grid, 2 * 32768, stream, pp, st);
