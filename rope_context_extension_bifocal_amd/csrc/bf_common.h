@@ -12,7 +12,8 @@ constexpr int kMaxSeqPerLaunch = 64;
 constexpr int kKeyTile = 64;      // keys per K/V tile (prefill) and V^T padding unit
 constexpr int kWaveRowsBf16 = 32; // query positions per wave, bf16 prefill
 constexpr int kWaveRowsF32 = 32;  // query positions per wave, fp32 prefill
-constexpr int kWavesPerGroup = 4; // waves per prefill workgroup (256 lanes)
+constexpr int kWavesPerGroupBf16 = 4;  // waves per bf16 prefill workgroup (256 lanes)
+constexpr int kWavesPerGroupF32 = 4;   // waves per fp32 prefill workgroup (256 lanes)
 
 // Per-launch description of up to kMaxSeqPerLaunch packed sequences.
 struct SeqTable {

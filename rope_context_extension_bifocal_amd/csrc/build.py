@@ -3,7 +3,9 @@
     python -m rope_context_extension_bifocal_amd.csrc.build
 
 Every HIP source is compiled with packed fp32 arithmetic disabled (the host
-pass warns that it does not know the feature; that is harmless).
+pass warns that it does not know the feature; that is harmless) and without
+IEEE NaN quieting in min/max (no kernel relies on NaN propagation; masked
+scores use -inf, which is still honoured).
 """
 import os
 import subprocess
@@ -19,6 +21,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 def build(verbose=False):
     cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+           "-mno-amdgpu-ieee", "-fno-honor-nans",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
            "-I", os.path.join(ROOT, "include"), "-I", HERE,
            "-o", LIB + ".tmp"] + [os.path.join(HERE, s) for s in SOURCES]

@@ -77,10 +77,11 @@ struct PrefillGeom {
 
 PrefillGeom prefill_geom(int dtype, int G) {
   PrefillGeom g;
-  g.hpw = std::gcd(G, bf::kWavesPerGroup);
+  g.hpw = std::gcd(G, 4);
   g.n_hsub = G / g.hpw;
   const int rows = dtype == BF_DTYPE_BF16 ? bf::kWaveRowsBf16 : bf::kWaveRowsF32;
-  g.P_wg = rows * bf::kWavesPerGroup / g.hpw;
+  const int waves = dtype == BF_DTYPE_BF16 ? bf::kWavesPerGroupBf16 : bf::kWavesPerGroupF32;
+  g.P_wg = rows * waves / g.hpw;
   return g;
 }
 

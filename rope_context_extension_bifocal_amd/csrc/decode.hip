@@ -1,16 +1,15 @@
 // Bifocal RoPE attention, single-token decode over a KV cache on gfx950.
 //
 // decode_split_kernel: workgroup = (batch b, KV head, split of C keys). The
-//   split's keys and values are streamed from HBM once, 64 keys at a time.
-//   Keys farther than w0 from the query (position N - 1) get the correction
-//   rotation R(theta_m * (phi(j) - j)) in registers before they are staged in
-//   LDS, keys inside the window are used as cached [ai-feeds.com summary,
-//   "关键模块" item 3: rotation of cached keys; item 1: the w0 window keeps
-//   original RoPE]. The query gets the same correction at its own position.
-//   Each of the 4 waves scores 16 keys of a block for all G query heads of
-//   the KV group (MFMA 16x16x32, queries as columns), keeps one online
-//   softmax state per query, and accumulates O^T with MFMA 16x16x16. At the
-//   end the waves are merged and the split writes (m, l, acc) partials.
+//   split's keys and values are streamed from HBM once. Keys farther than w0
+//   from the query (position N - 1) get the correction rotation
+//   R(theta_m * (phi(j) - j)) in registers right after they are loaded, keys
+//   inside the window are used as cached [ai-feeds.com summary, "关键模块"
+//   item 3: rotation of cached keys; item 1: the w0 window keeps original
+//   RoPE]. The query gets the same correction at its own position. Scores use
+//   MFMA 16x16x32 (queries as columns), P V uses MFMA 16x16x16, with one
+//   online softmax state per query and wave; at the end the waves are merged
+//   and the split writes its (m, l, acc) partial.
 // decode_combine_kernel: log-sum-exp merge of the splits of each query head.
 #include <hip/hip_runtime.h>
 
@@ -71,29 +70,59 @@ __device__ __forceinline__ void corr_cos_sin(double th, long long num, long long
   c = __builtin_amdgcn_cosf(fr);
 }
 
+// ------------------------------------------------------------------ kernels
+// Split kernel: workgroup = (batch b, KV head, split of `chunk` keys). Each of
+// the 4 waves streams its own contiguous quarter of the split in 16-key steps,
+// independently of the other waves:
+//   - the 16 keys' K rows go straight into registers, laid out as the A
+//     operand of MFMA 16x16x32 (lane = key n16, head-dim chunks 4 t + g4), so
+//     both halves (m, m + 64) of every rotary pair sit in the same lane and the
+//     correction rotation of far keys is done in place;
+//   - the 16 keys' V rows go by direct global->LDS loads into a wave-private
+//     ring; P V uses the head-dim order d = 8 row + block so that one 16-byte
+//     LDS read per key feeds all 8 output blocks;
+//   - loads run two steps ahead of compute.
+// The G query heads of the KV group are the MFMA columns (columns >= G are
+// zero queries whose results are dropped).
+constexpr int kDecWaves = 4;
+constexpr int kDecStep = 16;  // keys per wave step
+constexpr int kDecRing = 3;   // V ring slots per wave (two steps in flight)
+constexpr float kDecRescaleLog2 = 8.f;
+
+__device__ __forceinline__ void dec_wait_vm(int outstanding_steps) {
+  // loads complete in issue order; each step issues 8 vector-memory operations
+  if (outstanding_steps >= 2) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  else if (outstanding_steps == 1) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 template <bool BIFOCAL>
-__global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p, DecodeSeqs ds,
-                                                           ThetaTable tt) {
-  // LDS: K block [64][16 x 16 B] swizzled | V block [64][136] bf16 | Q' and Q'' [2][16][16 x 16 B]
-  __shared__ uint4 smem[1024 + (kDecBlock * kDecVRow * 2) / 16 + 2 * kDecMaxG * 16];
-  uint4* sK = smem;
-  uint16_t* sV = (uint16_t*)(smem + 1024);
-  uint4* sQ = smem + 1024 + (kDecBlock * kDecVRow * 2) / 16;
+__global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p, DecodeSeqs ds,
+                                                              ThetaTable tt) {
+  // LDS: V rings [4 waves][3 slots][16 keys x 16 chunks] | Q' and Q'' [2][16][16 chunks]
+  __shared__ uint4 smem[kDecWaves * kDecRing * 256 + 2 * kDecMaxG * 16];
+  uint4* sQ = smem + kDecWaves * kDecRing * 256;
 
   const int b = blockIdx.z, kvh = blockIdx.y, sp = blockIdx.x;
   if (sp >= ds.nsplit[b]) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n16 = lane & 15, g4 = lane >> 4;
   const long long N = ds.N[b];
   const long long s = ds.s[b];
   const long long w0 = (BIFOCAL && s > 1) ? p.w0 : (1LL << 62);
   const long long far_lim = N - w0;  // keys j < far_lim are far
-  const long long k_begin = (long long)sp * ds.chunk[b];
-  const long long k_end = min(N, k_begin + ds.chunk[b]);
+  const int chunk = ds.chunk[b];
+  const long long k_begin = (long long)sp * chunk;
+  const long long k_end = min(N, k_begin + chunk);
+  const int per = chunk / kDecWaves;  // multiple of 16
+  const long long kw0 = k_begin + (long long)wave * per;
+  const long long kw1 = min(k_end, kw0 + per);
+  const int ns = kw1 > kw0 ? (int)((kw1 - kw0 + kDecStep - 1) / kDecStep) : 0;
 
   // ---- queries: Q' as given, Q'' = R(Delta(N - 1)) Q'; rows >= G are zero
   {
-    const int qi = tid >> 4, c = tid & 15;  // 16 rows x 16 chunks
+    const int qi = tid >> 4, c = tid & 15;
     uint4 v0 = make_uint4(0, 0, 0, 0);
     if (qi < p.G) v0 = *(const uint4*)(p.q + ((size_t)b * p.Hq + kvh * p.G + qi) * kHeadDim + c * 8);
     sQ[qi * 16 + c] = v0;
@@ -101,7 +130,6 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p, Decod
   }
   __syncthreads();
   if (BIFOCAL && far_lim > 0) {
-    // thread (qi, m): 256 threads cover 4 queries x 64 pairs per pass
     for (int e = tid; e < p.G * kPairs; e += 256) {
       const int qi = e >> 6, m = e & 63;
       double sd, cd;
@@ -122,140 +150,163 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p, Decod
     qf2[t] = __builtin_bit_cast(dbf16x8, sQ[kDecMaxG * 16 + n16 * 16 + 4 * t + g4]);
   }
 
-  float m_run = -INFINITY, l_run = 0.f;
+  const uint16_t* kbase = p.kc + ((size_t)b * p.Hkv + kvh) * (size_t)p.cap * kHeadDim;
+  const uint16_t* vbase = p.vc + ((size_t)b * p.Hkv + kvh) * (size_t)p.cap * kHeadDim;
+  uint4* vring = smem + wave * (kDecRing * 256);
+  const double inv_s = 1.0 / (double)s;
+
+  float m_used = -INFINITY, l_part = 0.f;
   df32x4 oacc[8];
 #pragma unroll
   for (int db = 0; db < 8; ++db) oacc[db] = df32x4{};
 
-  const uint16_t* kbase = p.kc + ((size_t)b * p.Hkv + kvh) * (size_t)p.cap * kHeadDim;
-  const uint16_t* vbase = p.vc + ((size_t)b * p.Hkv + kvh) * (size_t)p.cap * kHeadDim;
-  const int kk = tid >> 2, q4 = tid & 3;  // staging: key row kk, chunks q4 + 4i
-
-  for (long long kb = k_begin; kb < k_end; kb += kDecBlock) {
-    // ---- stage: load this thread's 4 key chunks and 4 value chunks
-    const long long j = kb + kk;
-    const bool valid = j < k_end;
-    uint4 kv[4], vv[4];
+  uint4 kreg[kDecRing][4];
+  // issue the loads of step st into ring slot r: V rows first, then this lane's K row
+  auto issue = [&](int st, int r) {
+    const long long j0 = kw0 + (long long)st * kDecStep;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int c = q4 + 4 * i;
-      kv[i] = valid ? *(const uint4*)(kbase + (size_t)j * kHeadDim + c * 8) : make_uint4(0, 0, 0, 0);
-      vv[i] = valid ? *(const uint4*)(vbase + (size_t)j * kHeadDim + c * 8) : make_uint4(0, 0, 0, 0);
+      const long long key = min(j0 + 4 * i + (lane >> 4), kw1 - 1);
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(vbase + (size_t)key * kHeadDim + (lane & 15) * 8),
+          (__attribute__((address_space(3))) void*)(vring + r * 256 + i * 64), 16, 0, 0);
     }
-    if (BIFOCAL && valid && j < far_lim) {
-      // chunk pairs (q4, q4 + 8) and (q4 + 4, q4 + 12) hold rotary pairs (m, m + 64)
-      const long long num = dcorr_num(j, s, p.mode);
+    const long long key = min(j0 + n16, kw1 - 1);
 #pragma unroll
-      for (int hp = 0; hp < 2; ++hp) {
-        uint32_t* lo = (uint32_t*)&kv[hp];
-        uint32_t* hi = (uint32_t*)&kv[hp + 2];
+    for (int t = 0; t < 4; ++t)
+      kreg[r][t] = *(const uint4*)(kbase + (size_t)key * kHeadDim + (4 * t + g4) * 8);
+  };
+
+  auto process = [&](int st, int r) {
+    const long long jb = kw0 + (long long)st * kDecStep;
+    const bool any_far = BIFOCAL && jb < far_lim;
+    const bool any_loc = !BIFOCAL || jb + kDecStep - 1 >= far_lim;
+    uint4 kr[4] = {kreg[r][0], kreg[r][1], kreg[r][2], kreg[r][3]};
+    const long long j = jb + n16;  // this lane's A-operand key
+    if (any_far && j < far_lim) {
+      // rotary pairs (m, m + 64) = (element e of chunk 4 t + g4, same element of chunk 4 (t + 2) + g4)
+      const double qn = (double)dcorr_num(j, s, p.mode) * inv_s;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        uint32_t* lo = (uint32_t*)&kr[t];
+        uint32_t* hi = (uint32_t*)&kr[t + 2];
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          const int m0 = 8 * (q4 + 4 * hp) + 2 * w;
-          float c0, s0, c1, s1;
-          corr_cos_sin(tt.th[m0], num, s, c0, s0);
-          corr_cos_sin(tt.th[m0 + 1], num, s, c1, s1);
+          const int m0 = 32 * t + 8 * g4 + 2 * w;
+          const double tu0 = tt.th[m0] * qn * 0.15915494309189533577;
+          const double tu1 = tt.th[m0 + 1] * qn * 0.15915494309189533577;
+          const float f0 = (float)(tu0 - rint(tu0)), f1 = (float)(tu1 - rint(tu1));
+          const float c0 = __builtin_amdgcn_cosf(f0), s0 = __builtin_amdgcn_sinf(f0);
+          const float c1 = __builtin_amdgcn_cosf(f1), s1 = __builtin_amdgcn_sinf(f1);
           const float a0 = __uint_as_float(lo[w] << 16), a1 = __uint_as_float(lo[w] & 0xffff0000u);
           const float b0 = __uint_as_float(hi[w] << 16), b1 = __uint_as_float(hi[w] & 0xffff0000u);
-          const float ra0 = a0 * c0 - b0 * s0, rb0 = b0 * c0 + a0 * s0;
-          const float ra1 = a1 * c1 - b1 * s1, rb1 = b1 * c1 + a1 * s1;
-          lo[w] = (uint32_t)df2bf(ra0) | ((uint32_t)df2bf(ra1) << 16);
-          hi[w] = (uint32_t)df2bf(rb0) | ((uint32_t)df2bf(rb1) << 16);
+          lo[w] = (uint32_t)df2bf(a0 * c0 - b0 * s0) | ((uint32_t)df2bf(a1 * c1 - b1 * s1) << 16);
+          hi[w] = (uint32_t)df2bf(b0 * c0 + a0 * s0) | ((uint32_t)df2bf(b1 * c1 + a1 * s1) << 16);
         }
       }
     }
-    __syncthreads();  // previous block's LDS reads are done
+    df32x4 S = df32x4{};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = q4 + 4 * i;
-      sK[kk * 16 + (c ^ (kk & 15))] = kv[i];
-      *(uint4*)(sV + kk * kDecVRow + c * 8) = vv[i];
+    for (int t = 0; t < 4; ++t)
+      S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(dbf16x8, kr[t]),
+                                                  any_far ? qf2[t] : qf[t], S, 0, 0, 0);
+    if (any_far && any_loc) {  // step straddles the window edge: local keys score with Q'
+      df32x4 Sl = df32x4{};
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        Sl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(dbf16x8, kreg[r][t]), qf[t],
+                                                     Sl, 0, 0, 0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (jb + 4 * g4 + q >= far_lim) S[q] = Sl[q];
     }
-    __syncthreads();
+    // C layout: lane (query n16, g4) holds keys jb + 4 g4 + q
+    if (jb + kDecStep > kw1) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (jb + 4 * g4 + q >= kw1) S[q] = -INFINITY;
+    }
+    float mx = fmaxf(fmaxf(S[0], S[1]), fmaxf(S[2], S[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx *= p.scale_log2;
+    if (__any(mx > m_used + kDecRescaleLog2)) {
+      const float mn = fmaxf(m_used, mx);
+      const float alpha = (m_used == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_used - mn);
+      l_part *= alpha;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) oacc[db] *= alpha;
+      m_used = mn;
+    }
+    const float mb = (m_used == -INFINITY) ? 0.f : m_used;
+    ds16x4 pb;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float e = __builtin_amdgcn_exp2f(fmaf(S[q], p.scale_log2, -mb));
+      l_part += e;
+      pb[q] = (short)df2bf(e);
+    }
+    // V rows of keys 4 g4 + q, chunk n16 (head dims 8 n16 .. 8 n16 + 7)
+    uint4 vr[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) vr[q] = vring[r * 256 + (4 * g4 + q) * 16 + n16];
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const uint32_t w0q = ((const uint32_t*)&vr[0])[db >> 1], w1q = ((const uint32_t*)&vr[1])[db >> 1];
+      const uint32_t w2q = ((const uint32_t*)&vr[2])[db >> 1], w3q = ((const uint32_t*)&vr[3])[db >> 1];
+      const uint32_t sel = (db & 1) ? 0x07060302u : 0x05040100u;
+      const uint32_t x01 = __builtin_amdgcn_perm(w1q, w0q, sel), x23 = __builtin_amdgcn_perm(w3q, w2q, sel);
+      ds16x4 a;
+      a[0] = (short)(x01 & 0xffff);
+      a[1] = (short)(x01 >> 16);
+      a[2] = (short)(x23 & 0xffff);
+      a[3] = (short)(x23 >> 16);
+      oacc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pb, oacc[db], 0, 0, 0);
+    }
+  };
 
-    // ---- wave: 16 keys kb + 16 wave .. +15
-    const long long jw = kb + 16 * wave;
-    if (jw < k_end) {
-      const int krow = 16 * wave + n16;  // A operand row of this lane
-      df32x4 S = df32x4{};
-      const bool any_far = BIFOCAL && jw < far_lim;
-      const bool any_loc = !BIFOCAL || jw + 15 >= far_lim;
+  if (ns > 0) issue(0, 0);
+  if (ns > 1) issue(1, 1);
+  for (int st = 0; st < ns; st += kDecRing) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const dbf16x8 a = __builtin_bit_cast(dbf16x8, sK[krow * 16 + ((4 * t + g4) ^ (krow & 15))]);
-        S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, any_far ? qf2[t] : qf[t], S, 0, 0, 0);
-      }
-      if (any_far && any_loc) {  // block straddles the window edge: local keys use Q'
-        df32x4 Sl = df32x4{};
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const dbf16x8 a = __builtin_bit_cast(dbf16x8, sK[krow * 16 + ((4 * t + g4) ^ (krow & 15))]);
-          Sl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[t], Sl, 0, 0, 0);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (jw + 4 * g4 + r >= far_lim) S[r] = Sl[r];
-      }
-      // C layout: lane (query n16, g4) holds keys jw + 4 g4 + r
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (jw + 4 * g4 + r >= k_end) S[r] = -INFINITY;
-      float mx = fmaxf(fmaxf(S[0], S[1]), fmaxf(S[2], S[3]));
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(m_run, mx * p.scale_log2);
-      const float mbase = (mnew == -INFINITY) ? 0.f : mnew;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - mbase);
-      m_run = mnew;
-      float rs = 0.f;
-      ds16x4 pb;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float e = __builtin_amdgcn_exp2f(fmaf(S[r], p.scale_log2, -mbase));
-        rs += e;
-        pb[r] = (short)df2bf(e);
-      }
-      rs += __shfl_xor(rs, 16);
-      rs += __shfl_xor(rs, 32);
-      l_run = l_run * alpha + rs;
-      // O^T += V^T P^T: A = V^T rows d = 16 db + n16, keys 16 wave + 4 g4 + r
-#pragma unroll
-      for (int db = 0; db < 8; ++db) {
-        const int d = 16 * db + n16;
-        ds16x4 a;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) a[r] = (short)sV[(16 * wave + 4 * g4 + r) * kDecVRow + d];
-        oacc[db] *= alpha;
-        oacc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pb, oacc[db], 0, 0, 0);
+    for (int u = 0; u < kDecRing; ++u) {
+      const int cur = st + u;
+      if (cur < ns) {
+        if (cur + 2 < ns) issue(cur + 2, (u + 2) % kDecRing);
+        dec_wait_vm(min(2, ns - 1 - cur));
+        process(cur, u);
       }
     }
   }
 
-  // ---- merge the 4 waves (LDS reused), write the split's partial
+  // ---- merge the 4 waves (V rings reused), write the split's partial
+  const float lsum = l_part + __shfl_xor(l_part, 16);
+  const float ltot = lsum + __shfl_xor(lsum, 32);  // column total over the wave's keys
   __syncthreads();
   float* mw = (float*)smem;                 // [4][16]
-  float* lw = mw + 4 * kDecMaxG;            // [4][16]
-  float* ow = lw + 4 * kDecMaxG;            // [4][16][128]
+  float* lw = mw + kDecWaves * kDecMaxG;    // [4][16]
+  float* ow = lw + kDecWaves * kDecMaxG;    // [4][16][128]
   if (g4 == 0) {
-    mw[wave * kDecMaxG + n16] = m_run;
-    lw[wave * kDecMaxG + n16] = l_run;
+    mw[wave * kDecMaxG + n16] = m_used;
+    lw[wave * kDecMaxG + n16] = ltot;
   }
+  // oacc[db][q] is O^T row (4 g4 + q) of block db = head dim 8 (4 g4 + q) + db, query n16
 #pragma unroll
   for (int db = 0; db < 8; ++db)
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      ow[(wave * kDecMaxG + n16) * kHeadDim + 16 * db + 4 * g4 + r] = oacc[db][r];
+    for (int q = 0; q < 4; ++q)
+      ow[(wave * kDecMaxG + n16) * kHeadDim + 8 * (4 * g4 + q) + db] = oacc[db][q];
   __syncthreads();
   for (int e = tid; e < p.G * kHeadDim; e += 256) {
     const int qi = e >> 7, d = e & 127;
     float mt = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) mt = fmaxf(mt, mw[w * kDecMaxG + qi]);
-    const float mb = (mt == -INFINITY) ? 0.f : mt;
+    for (int w = 0; w < kDecWaves; ++w) mt = fmaxf(mt, mw[w * kDecMaxG + qi]);
+    const float mbt = (mt == -INFINITY) ? 0.f : mt;
     float acc = 0.f, lt = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float f = __builtin_amdgcn_exp2f(mw[w * kDecMaxG + qi] - mb);
+    for (int w = 0; w < kDecWaves; ++w) {
+      const float f = __builtin_amdgcn_exp2f(mw[w * kDecMaxG + qi] - mbt);
       acc += f * ow[(w * kDecMaxG + qi) * kHeadDim + d];
       lt += f * lw[w * kDecMaxG + qi];
     }
@@ -268,22 +319,70 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p, Decod
   }
 }
 
-// One workgroup per (query head, batch): LSE merge of the splits.
-__global__ __launch_bounds__(128) void decode_combine_kernel(DecodeParams p, DecodeSeqs ds) {
-  const int b = blockIdx.y, h = blockIdx.x, d = threadIdx.x;
+// One workgroup per (query head, batch): log-sum-exp merge of the splits.
+// Split weights are computed once into LDS; each thread then sums a strided
+// subset of splits for one float4 of head dims and the subsets are added.
+__global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p, DecodeSeqs ds) {
+  __shared__ float wgt[1088];
+  __shared__ float red[256];
+  __shared__ float4 part4[8][32];
+  const int b = blockIdx.y, h = blockIdx.x, t = threadIdx.x;
   const int ns = ds.nsplit[b];
   const size_t row0 = ((size_t)b * p.Hq + h) * p.S;
-  float mt = -INFINITY;
-  for (int i = 0; i < ns; ++i) mt = fmaxf(mt, p.part_m[row0 + i]);
-  const float mb = (mt == -INFINITY) ? 0.f : mt;
-  float acc = 0.f, lt = 0.f;
-  for (int i = 0; i < ns; ++i) {
-    const float f = __builtin_amdgcn_exp2f(p.part_m[row0 + i] - mb);
-    acc += f * p.part_acc[(row0 + i) * kHeadDim + d];
-    lt += f * p.part_l[row0 + i];
+  float mloc = -INFINITY;
+  for (int i = t; i < ns; i += 256) mloc = fmaxf(mloc, p.part_m[row0 + i]);
+  red[t] = mloc;
+  __syncthreads();
+  for (int k = 128; k > 0; k >>= 1) {
+    if (t < k) red[t] = fmaxf(red[t], red[t + k]);
+    __syncthreads();
   }
-  p.o[((size_t)b * p.Hq + h) * kHeadDim + d] = df2bf(acc / lt);
-  if (p.lse && d == 0) p.lse[(size_t)b * p.Hq + h] = (mt + __log2f(lt)) * 0.69314718055994530942f;
+  const float mt = red[0];
+  const float mbt = (mt == -INFINITY) ? 0.f : mt;
+  __syncthreads();
+  float lloc = 0.f;
+  for (int i = t; i < ns; i += 256) {
+    const float w = __builtin_amdgcn_exp2f(p.part_m[row0 + i] - mbt);
+    wgt[i] = w;
+    lloc += w * p.part_l[row0 + i];
+  }
+  red[t] = lloc;
+  __syncthreads();
+  for (int k = 128; k > 0; k >>= 1) {
+    if (t < k) red[t] += red[t + k];
+    __syncthreads();
+  }
+  const float lt = red[0];
+  const int d4 = t & 31, grp = t >> 5;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
+  for (int i = grp; i < ns; i += 8) {
+    const float4 v = *(const float4*)(p.part_acc + (row0 + i) * kHeadDim + 4 * d4);
+    const float w = wgt[i];
+    acc.x += w * v.x;
+    acc.y += w * v.y;
+    acc.z += w * v.z;
+    acc.w += w * v.w;
+  }
+  part4[grp][d4] = acc;
+  __syncthreads();
+  if (t < 32) {
+    float4 a = part4[0][t];
+#pragma unroll
+    for (int g = 1; g < 8; ++g) {
+      a.x += part4[g][t].x;
+      a.y += part4[g][t].y;
+      a.z += part4[g][t].z;
+      a.w += part4[g][t].w;
+    }
+    const float inv = 1.f / lt;
+    uint16_t* o = p.o + ((size_t)b * p.Hq + h) * kHeadDim + 4 * t;
+    uint2 w;
+    w.x = (uint32_t)df2bf(a.x * inv) | ((uint32_t)df2bf(a.y * inv) << 16);
+    w.y = (uint32_t)df2bf(a.z * inv) | ((uint32_t)df2bf(a.w * inv) << 16);
+    *(uint2*)o = w;
+    if (p.lse && t == 0) p.lse[(size_t)b * p.Hq + h] = (mt + __log2f(lt)) * 0.69314718055994530942f;
+  }
 }
 
 // ------------------------------------------------------------------ host side
@@ -342,6 +441,8 @@ int run_decode(bool bifocal, const void* q, const void* kc, const void* vc, void
       return bad(BF_ERR_INVALID_ARG, "seqlens[" + std::to_string(b) + "] out of [1, cache_capacity]");
     if (seqlens[b] > max_len) max_len = seqlens[b];
   }
+  if (decode_split_bound(max_len) > 1088)
+    return bad(BF_ERR_UNSUPPORTED, "decode supports caches of at most 1088 x 1024 keys");
   const DecodeWs wl = decode_ws_layout(batch, max_len, Hq);
   if (!ws) return bad(BF_ERR_WORKSPACE, "workspace is null");
   if ((uintptr_t)ws & 255u) return bad(BF_ERR_WORKSPACE, "workspace must be 256-byte aligned");
@@ -396,7 +497,7 @@ int run_decode(bool bifocal, const void* q, const void* kc, const void* vc, void
       hipLaunchKernelGGL(decode_split_kernel<false>, grid, dim3(256), 0, stream, dp, ds, tt);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return bad(BF_ERR_HIP, std::string("decode split launch: ") + hipGetErrorString(e));
-    hipLaunchKernelGGL(decode_combine_kernel, dim3(Hq, nb), dim3(128), 0, stream, dp, ds);
+    hipLaunchKernelGGL(decode_combine_kernel, dim3(Hq, nb), dim3(256), 0, stream, dp, ds);
     e = hipGetLastError();
     if (e != hipSuccess) return bad(BF_ERR_HIP, std::string("decode combine launch: ") + hipGetErrorString(e));
   }

@@ -27,6 +27,7 @@ namespace bf {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 
 // ----------------------------------------------------------------- helpers
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
@@ -136,8 +137,10 @@ __global__ __launch_bounds__(256) void correction_prep_kernel(PrepParams p, SeqT
   }
 }
 
-// V [Hkv][T][D] -> V^T [Hkv][D][Tpad]; sequence b occupies padded columns
-// vt_off[b] .. vt_off[b+1]-1, columns past its length are zero.
+// V [Hkv][T][D] -> V^T in 64-key tiles: tile t (global over the padded key
+// axis, sequence b owns tiles vt_off[b] / 64 ..) of KV head h is the contiguous
+// block vt[(h * Tpad / 64 + t) * D * 64 ..], laid out [head dim][64 keys].
+// Keys past a sequence's length are zero.
 template <typename T>
 __global__ __launch_bounds__(256) void vt_transpose_kernel(VtParams p, SeqTable st) {
   __shared__ T tile[kKeyTile][kHeadDim + 2];
@@ -153,10 +156,10 @@ __global__ __launch_bounds__(256) void vt_transpose_kernel(VtParams p, SeqTable 
     tile[r][d] = (p0 + r < L) ? v[(size_t)(p0 + r) * kHeadDim + d] : T(0);
   }
   __syncthreads();
-  T* vt = (T*)p.vt + (size_t)h * kHeadDim * p.Tpad;
+  T* vt = (T*)p.vt + ((size_t)h * (p.Tpad / kKeyTile) + c / kKeyTile) * (kHeadDim * kKeyTile);
   for (int e = threadIdx.x; e < kKeyTile * kHeadDim; e += 256) {
     const int d = e / kKeyTile, r = e % kKeyTile;
-    vt[(size_t)d * p.Tpad + c + r] = tile[r][d];
+    vt[d * kKeyTile + r] = tile[r][d];
   }
 }
 
@@ -210,13 +213,12 @@ __device__ __forceinline__ void online_softmax_rescale(float& m_run, float& l_ru
 }
 
 // --------------------------------------------------------------- bf16
-// Workgroup: 4 waves; wave = (query head, 32 query positions); two workgroups
-// share a CU, so each SIMD runs two independent waves whose softmax (VALU) and
-// matrix (MFMA) phases overlap. The G query heads of one KV group share every
-// staged K/V tile. Scores are formed as S^T = K Q^T on MFMA 32x32x16 blocks
-// (keys x queries) and the output as O^T += V^T P^T (head dims x queries); a
-// lane owns one query column, so a row max needs one exchange with the other
-// lane half and the row sum none until the end.
+// Workgroup: 4 waves; wave = (query head, 32 query positions). The G query
+// heads of one KV group share every staged K/V tile. Scores are formed as
+// S^T = K Q^T on MFMA 32x32x16 blocks (keys x queries) and the output as
+// O^T += V^T P^T (head dims x queries); a lane owns one query column, so a row
+// max needs one exchange with the other lane half and the row sum none until
+// the end.
 //
 // The far branch and the local branch run as two passes over their own tile
 // ranges with one online-softmax state: the far pass (q'' . k'' on every tile
@@ -227,12 +229,17 @@ __device__ __forceinline__ void online_softmax_rescale(float& m_run, float& l_ru
 // counted once and the scaled-branch work over the band is never done. Only
 // the one or two tiles at the window edge are visited by both passes.
 //
-// K and V^T tiles (64 keys) are staged by direct global->LDS loads one tile
-// ahead (two slots each). The O accumulator is rescaled only when a row max
-// grows by more than 2^8: numerator and denominator share the same stale max,
-// so the result is unchanged, and probabilities stay below 2^8.
+// Two 4-wave workgroups share a CU, so each SIMD runs two independent waves
+// whose softmax (VALU) and matrix (MFMA) phases overlap. K and V^T tiles (64
+// keys) are staged by direct global->LDS loads one tile ahead (two-slot
+// rings); within a tile the MFMA operands are read from LDS two MFMA steps
+// ahead of their use. The O accumulator is rescaled only when a row max grows
+// by more than 2^8: numerator and denominator share the same stale max, so
+// the result is unchanged, and probabilities stay below 2^8.
 constexpr float kRescaleLog2 = 8.f;
 constexpr int kSlot = 1024;  // 16-byte chunks per staged 64 x 128 bf16 tile
+constexpr int kBf16Waves = 4;
+constexpr int kStageIters = kSlot / (64 * kBf16Waves);  // 1 KiB loads per wave per tile
 
 struct WaveRows {
   int r0;  // first query position of the wave (sequence-relative)
@@ -243,21 +250,45 @@ struct WaveRows {
 struct RowState {
   float m_used;  // stale row max in scaled log2 units (-inf: no key yet)
   float l_part;  // this lane half's share of the row sum
+  float alpha;   // pending factor for the O accumulator
+  bool rescale;  // (wave-uniform) alpha differs from 1
 };
+
+// apply a pending rescale of the O accumulator
+__device__ __forceinline__ void apply_rescale(RowState& rs, f32x16 (&oacc)[4]) {
+  if (rs.rescale) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db) oacc[db] *= rs.alpha;
+    rs.alpha = 1.f;
+    rs.rescale = false;
+  }
+}
 
 __device__ __forceinline__ void qk_tile(const uint4* __restrict__ sk, const bf16x8 (&q)[8], int li,
                                         int hl, f32x16 (&S)[2]) {
-  S[0] = f32x16{};
-  S[1] = f32x16{};
   const int row0 = key_of_mfma_row(li), row1 = 32 + row0;
+  bf16x8 a0[8], a1[8];
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
     const int ch = 2 * t + hl;
-    const bf16x8 a0 = __builtin_bit_cast(bf16x8, sk[row0 * 16 + (ch ^ (row0 & 15))]);
-    const bf16x8 a1 = __builtin_bit_cast(bf16x8, sk[row1 * 16 + (ch ^ (row1 & 15))]);
-    S[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, q[t], S[0], 0, 0, 0);
-    S[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, q[t], S[1], 0, 0, 0);
+    a0[t] = __builtin_bit_cast(bf16x8, sk[row0 * 16 + (ch ^ (row0 & 15))]);
+    a1[t] = __builtin_bit_cast(bf16x8, sk[row1 * 16 + (ch ^ (row1 & 15))]);
   }
+  S[0] = f32x16{};
+  S[1] = f32x16{};
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    S[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[t], q[t], S[0], 0, 0, 0);
+    S[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[t], q[t], S[1], 0, 0, 0);
+  }
+  // operands two k-steps ahead of their MFMAs
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+  for (int t = 0; t < 6; ++t) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 }
 
 // Mask a tile (keys c0 .. c0 + 63) for a pass: the far pass keeps pairs with
@@ -282,6 +313,7 @@ __device__ __forceinline__ void mask_tile(f32x16 (&S)[2], const WaveRows& wr, in
 
 __device__ __forceinline__ void pv_tile(const uint4* __restrict__ sv, const bf16x8 (&P)[2][2],
                                         int li, int hl, f32x16 (&oacc)[4]) {
+  bf16x8 a[4][2][2];
 #pragma unroll
   for (int db = 0; db < 4; ++db) {
     const int d = 32 * db + li;
@@ -290,47 +322,149 @@ __device__ __forceinline__ void pv_tile(const uint4* __restrict__ sv, const bf16
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int ch = 4 * jb + 2 * u + hl;
-        const bf16x8 a = __builtin_bit_cast(bf16x8, sv[d * 8 + (ch ^ (d & 7))]);
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, P[jb][u], oacc[db], 0, 0, 0);
+        a[db][jb][u] = __builtin_bit_cast(bf16x8, sv[d * 8 + (ch ^ ((d >> 1) & 7))]);
       }
   }
+#pragma unroll
+  for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[db][jb][u], P[jb][u], oacc[db], 0, 0, 0);
+  // operands two MFMAs ahead
+  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+  for (int i = 0; i < 14; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
 }
 
 __device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Direct global -> LDS staging (16 bytes per lane, 1 KiB per wave instruction).
-// LDS chunk p of a K tile holds row p / 16, swizzled column (p % 16) ^ (row % 16);
-// keys past the sequence end read the last key (finite data, masked later).
-__device__ __forceinline__ void stage_k(uint4* slot, const uint16_t* kptr, int c0, int L,
-                                        int wave, int lane) {
+// Workgroup barrier that waits for this wave's LDS reads but not for its
+// outstanding global->LDS loads (those are waited for explicitly).
+__device__ __forceinline__ void slot_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+}
+
+// Per-lane byte offsets of the direct global -> LDS staging, fixed for a pass
+// (16 bytes per lane, 1 KiB per wave instruction, kStageIters instructions per
+// wave, tile and operand). LDS chunk p of a K tile holds key row p / 16 and
+// swizzled column (p % 16) ^ (row % 16); chunk p of a V^T tile holds head dim
+// d = p / 8 and key chunk (p % 8) ^ ((d / 2) % 8). Both swizzles keep the 16
+// lanes of one LDS read cycle on distinct banks.
+struct StageOffsets {
+  uint32_t k[kStageIters];  // byte offset inside a 64-key K tile (key row = offset / 256)
+  uint32_t v[kStageIters];  // byte offset inside a V^T tile
+};
+
+__device__ __forceinline__ StageOffsets stage_offsets(int wave, int lane) {
+  StageOffsets so;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int p = (4 * i + wave) * 64 + lane;
+  for (int i = 0; i < kStageIters; ++i) {
+    const int p = (kBf16Waves * i + wave) * 64 + lane;
     const int row = p >> 4, col = (p & 15) ^ (row & 15);
-    const int key = min(c0 + row, L - 1);
-    __builtin_amdgcn_global_load_lds(
-        (const __attribute__((address_space(1))) void*)(kptr + (size_t)key * kHeadDim + col * 8),
-        (__attribute__((address_space(3))) void*)(slot + (4 * i + wave) * 64), 16, 0, 0);
+    so.k[i] = (uint32_t)(row * kHeadDim + col * 8) * 2u;
+    const int d = p >> 3, vc = (p & 7) ^ ((d >> 1) & 7);
+    so.v[i] = (uint32_t)(d * kKeyTile + vc * 8) * 2u;
   }
+  return so;
 }
 
-// V^T tile: LDS chunk p holds head dim p / 8, swizzled key chunk (p % 8) ^ (d % 8).
-__device__ __forceinline__ void stage_v(uint4* slot, const uint16_t* vtg, int Tpad, int c0,
-                                        int wave, int lane) {
+// A wave-uniform pointer, held in scalar registers (the loads below then use
+// a scalar base plus a 32-bit per-lane offset).
+__device__ __forceinline__ const char* scalar_ptr(const void* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const char*)(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ void g2lds(const char* gbase, uint32_t off, uint4* lds) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(gbase + off),
+                                   (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+
+// ktile: first key of the tile; keys_left (>= 1, wave-uniform): keys of the
+// sequence from that key on. Rows past the sequence end read its last key
+// (finite data; those scores are masked).
+__device__ __forceinline__ void stage_k(uint4* slot, const uint16_t* ktile, int keys_left,
+                                        const StageOffsets& so, int wave) {
+  const char* kb = scalar_ptr(ktile);
+  if (keys_left >= kKeyTile) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int p = (4 * i + wave) * 64 + lane;
-    const int d = p >> 3, col = (p & 7) ^ (d & 7);
-    __builtin_amdgcn_global_load_lds(
-        (const __attribute__((address_space(1))) void*)(vtg + (size_t)d * Tpad + c0 + col * 8),
-        (__attribute__((address_space(3))) void*)(slot + (4 * i + wave) * 64), 16, 0, 0);
+    for (int i = 0; i < kStageIters; ++i) g2lds(kb, so.k[i], slot + (kBf16Waves * i + wave) * 64);
+  } else {
+#pragma unroll
+    for (int i = 0; i < kStageIters; ++i) {
+      const int row = (int)(so.k[i] >> 8);
+      const int shift = row < keys_left ? 0 : (keys_left - 1 - row) * kHeadDim * 2;
+      g2lds(kb, (uint32_t)((int)so.k[i] + shift), slot + (kBf16Waves * i + wave) * 64);
+    }
   }
 }
 
-// One pass (far or local) of a wave over tiles [ktb, kte).
+__device__ __forceinline__ void stage_v(uint4* slot, const uint16_t* vtile, const StageOffsets& so,
+                                        int wave) {
+  const char* vb = scalar_ptr(vtile);
+#pragma unroll
+  for (int i = 0; i < kStageIters; ++i) g2lds(vb, so.v[i], slot + (kBf16Waves * i + wave) * 64);
+}
+
+// Softmax step of a tile: mask, row max, lazy rescale, probabilities (bf16)
+// and row sum.
+template <bool FAR>
+__device__ __forceinline__ void vector_slot(f32x16 (&S)[2], const WaveRows& wr, int c0, float sc,
+                                            int li, int hl, RowState& rs, f32x16 (&oacc)[4],
+                                            bf16x8 (&P)[2][2]) {
+  mask_tile<FAR>(S, wr, c0, li, hl);
+  float m = -INFINITY;
+#pragma unroll
+  for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) m = fmaxf(m, fmaxf(S[jb][r], S[jb][r + 1]));
+  m = fmaxf(m, __shfl_xor(m, 32)) * sc;
+  // A new row max more than 2^8 above the stale one: move the stale max and
+  // leave the factor for the O accumulator to the next matrix slot.
+  if (__any(m > rs.m_used + kRescaleLog2)) {
+    const float mn = fmaxf(rs.m_used, m);
+    const float alpha = (rs.m_used == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(rs.m_used - mn);
+    rs.l_part *= alpha;
+    rs.alpha *= alpha;
+    rs.rescale = true;
+    rs.m_used = mn;
+  }
+  const float mb = (rs.m_used == -INFINITY) ? 0.f : rs.m_used;
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  float sum = rs.l_part;
+#pragma unroll
+  for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      bf16x8 v;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        v[e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(S[jb][8 * u + e], sc, -mb));
+      P[jb][u] = v;
+      // the row sum adds the same bf16-rounded probabilities the P V product uses
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const bf16x2 pr = {v[e], v[e + 1]};
+        sum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, sum, false);
+      }
+    }
+  rs.l_part = sum;
+}
+
+// One pass (far or local) of a wave over tiles [ktb, kte). vt0 points at the
+// sequence's first V^T tile of this KV head.
 template <bool FAR>
 __device__ __forceinline__ void run_pass(const uint16_t* qsrc, const uint16_t* ksrc,
-                                         const uint16_t* vtg, int Tpad, int ktb, int kte,
+                                         const uint16_t* vt0, int ktb, int kte,
                                          const WaveRows& wr, float sc, int wave, int lane,
                                          uint4* sK, uint4* sV, RowState& rs,
                                          f32x16 (&oacc)[4]) {
@@ -347,56 +481,26 @@ __device__ __forceinline__ void run_pass(const uint16_t* qsrc, const uint16_t* k
       qf[t] = __builtin_bit_cast(bf16x8, v);
     }
   }
-  __syncthreads();  // LDS of a previous pass is no longer read
-  stage_k(sK + (ktb & 1) * kSlot, ksrc, ktb * kKeyTile, wr.L, wave, lane);
-  stage_v(sV + (ktb & 1) * kSlot, vtg, Tpad, ktb * kKeyTile, wave, lane);
+  const StageOffsets so = stage_offsets(wave, lane);
+  constexpr int kTileElems = kHeadDim * kKeyTile;
+  slot_barrier();  // LDS of a previous pass is no longer read
+  stage_k(sK + (ktb & 1) * kSlot, ksrc + (size_t)ktb * kTileElems, wr.L - ktb * kKeyTile, so, wave);
+  stage_v(sV + (ktb & 1) * kSlot, vt0 + (size_t)ktb * kTileElems, so, wave);
   for (int t = ktb; t < kte; ++t) {
     const int c0 = t * kKeyTile;
     wait_vmem_all();
-    __syncthreads();  // tile t landed for every wave; slot (t + 1) & 1 is free
+    slot_barrier();  // tile t landed for every wave; slot (t + 1) & 1 is free
     if (t + 1 < kte) {
-      stage_k(sK + ((t + 1) & 1) * kSlot, ksrc, c0 + kKeyTile, wr.L, wave, lane);
-      stage_v(sV + ((t + 1) & 1) * kSlot, vtg, Tpad, c0 + kKeyTile, wave, lane);
+      stage_k(sK + ((t + 1) & 1) * kSlot, ksrc + (size_t)(t + 1) * kTileElems,
+              wr.L - c0 - kKeyTile, so, wave);
+      stage_v(sV + ((t + 1) & 1) * kSlot, vt0 + (size_t)(t + 1) * kTileElems, so, wave);
     }
     if (wr.r0 >= wr.L || c0 > wr.r0 + 31) continue;  // no causal pair of this wave here
     f32x16 S[2];
-    qk_tile(sK + (t & 1) * kSlot, qf, li, hl, S);
-    mask_tile<FAR>(S, wr, c0, li, hl);
-    // row max (the lane's query), lazily applied
-    float m = -INFINITY;
-#pragma unroll
-    for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) m = fmaxf(m, fmaxf(S[jb][r], S[jb][r + 1]));
-    m = fmaxf(m, __shfl_xor(m, 32)) * sc;
-    if (__any(m > rs.m_used + kRescaleLog2)) {
-      const float mn = fmaxf(rs.m_used, m);
-      const float alpha = (rs.m_used == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(rs.m_used - mn);
-      rs.l_part *= alpha;
-#pragma unroll
-      for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
-      rs.m_used = mn;
-    }
-    const float mb = (rs.m_used == -INFINITY) ? 0.f : rs.m_used;
     bf16x8 P[2][2];
-    float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-    for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        bf16x8 v;
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const float x0 = __builtin_amdgcn_exp2f(fmaf(S[jb][8 * u + e], sc, -mb));
-          const float x1 = __builtin_amdgcn_exp2f(fmaf(S[jb][8 * u + e + 1], sc, -mb));
-          s0 += x0;
-          s1 += x1;
-          v[e] = (__bf16)x0;
-          v[e + 1] = (__bf16)x1;
-        }
-        P[jb][u] = v;
-      }
-    rs.l_part += s0 + s1;
+    qk_tile(sK + (t & 1) * kSlot, qf, li, hl, S);
+    vector_slot<FAR>(S, wr, c0, sc, li, hl, rs, oacc, P);
+    apply_rescale(rs, oacc);
     pv_tile(sV + (t & 1) * kSlot, P, li, hl, oacc);
   }
 }
@@ -404,18 +508,21 @@ __device__ __forceinline__ void run_pass(const uint16_t* qsrc, const uint16_t* k
 template <bool BIFOCAL>
 __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillParams p, SeqTable st) {
   extern __shared__ uint4 smem[];
-  uint4* sK = smem;             // 2 slots
+  uint4* sK = smem;              // 2 slots
   uint4* sV = smem + 2 * kSlot;  // 2 slots
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar) index
   const int li = lane & 31, hl = lane >> 5;
   const Item it = make_item<BIFOCAL>(p, st, wave, kWaveRowsBf16);
   const WaveRows wr{it.r0, it.L, (int)min(it.w0, (long long)(1 << 30))};
 
   const uint16_t* qg = (const uint16_t*)p.q + ((size_t)it.hq * p.T + it.tok0) * kHeadDim;
   const uint16_t* kg = (const uint16_t*)p.k + ((size_t)it.kvh * p.T + it.tok0) * kHeadDim;
-  const uint16_t* vtg = (const uint16_t*)p.vt + (size_t)it.kvh * kHeadDim * p.Tpad + st.vt_off[it.b];
+  const uint16_t* vt0 = (const uint16_t*)p.vt +
+                        ((size_t)it.kvh * (p.Tpad / kKeyTile) + st.vt_off[it.b] / kKeyTile) *
+                            (kHeadDim * kKeyTile);
 
-  RowState rs{-INFINITY, 0.f};
+  RowState rs{-INFINITY, 0.f, 1.f, false};
   f32x16 oacc[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) oacc[db] = f32x16{};
@@ -426,15 +533,14 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillParams p, S
   if (BIFOCAL && Rl - w0 >= 0) {  // far pairs exist: keys j <= Rl - w0
     const int kte = min(it.nkt, (int)((Rl - w0) / kKeyTile) + 1);
     run_pass<true>((const uint16_t*)p.q2 + ((size_t)it.hq * p.T + it.tok0) * kHeadDim,
-                   (const uint16_t*)p.k2 + ((size_t)it.kvh * p.T + it.tok0) * kHeadDim, vtg,
-                   p.Tpad, 0, kte, wr, p.scale_log2, wave, lane, sK, sV, rs, oacc);
+                   (const uint16_t*)p.k2 + ((size_t)it.kvh * p.T + it.tok0) * kHeadDim, vt0,
+                   0, kte, wr, p.scale_log2, wave, lane, sK, sV, rs, oacc);
   }
   if (w0 > 0) {  // local pairs exist: keys j > R0 - w0 (and j <= Rl)
     const long long first = R0 - w0 + 1;  // smallest key with a local pair
     const int ktb = first <= 0 ? 0 : (int)(first / kKeyTile);
     if (ktb < it.nkt)
-      run_pass<false>(qg, kg, vtg, p.Tpad, ktb, it.nkt, wr, p.scale_log2, wave, lane, sK, sV, rs,
-                      oacc);
+      run_pass<false>(qg, kg, vt0, ktb, it.nkt, wr, p.scale_log2, wave, lane, sK, sV, rs, oacc);
   }
 
   // epilogue: normalise, store O (bf16) and lse
@@ -499,7 +605,9 @@ __global__ __launch_bounds__(256, 1) void prefill_f32_kernel(PrefillParams p, Se
   const float* kg = (const float*)p.k + ((size_t)it.kvh * p.T + it.tok0) * kHeadDim;
   const float* q2g = BIFOCAL ? (const float*)p.q2 + ((size_t)it.hq * p.T + it.tok0) * kHeadDim : nullptr;
   const float* k2g = BIFOCAL ? (const float*)p.k2 + ((size_t)it.kvh * p.T + it.tok0) * kHeadDim : nullptr;
-  const float* vtg = (const float*)p.vt + (size_t)it.kvh * kHeadDim * p.Tpad + st.vt_off[it.b];
+  const float* vt0 = (const float*)p.vt +
+                     ((size_t)it.kvh * (p.Tpad / kKeyTile) + st.vt_off[it.b] / kKeyTile) *
+                         (kHeadDim * kKeyTile);
 
   float qf[64], qf2[64];
   {
@@ -550,7 +658,8 @@ __global__ __launch_bounds__(256, 1) void prefill_f32_kernel(PrefillParams p, Se
           sK2[row * 32 + (col ^ (row & 31))] = kv;
         }
       const int d = c >> 4, vc = c & 15;
-      sV[d * 16 + (vc ^ (d & 15))] = *(const uint4*)(vtg + (size_t)d * p.Tpad + c0 + vc * 4);
+      sV[d * 16 + (vc ^ (d & 15))] =
+          *(const uint4*)(vt0 + (size_t)kt * (kHeadDim * kKeyTile) + d * kKeyTile + vc * 4);
     }
     __syncthreads();
 
@@ -679,23 +788,24 @@ hipError_t launch_vt_transpose(int dtype, const VtParams& vp, const SeqTable& st
 }
 
 template <typename K>
-static hipError_t launch_with_lds(K kernel, int grid, size_t lds, hipStream_t stream,
+static hipError_t launch_with_lds(K kernel, int grid, int threads, size_t lds, hipStream_t stream,
                                   const PrefillParams& pp, const SeqTable& st) {
   hipError_t e = hipFuncSetAttribute((const void*)kernel,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), lds, stream, pp, st);
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(threads), lds, stream, pp, st);
   return hipGetLastError();
 }
 
 hipError_t launch_prefill_main(int dtype, bool bifocal, const PrefillParams& pp,
                                const SeqTable& st, int grid, hipStream_t stream) {
   if (dtype == 0) {
-    if (bifocal) return launch_with_lds(prefill_bf16_kernel<true>, grid, 4 * 16384, stream, pp, st);
-    return launch_with_lds(prefill_bf16_kernel<false>, grid, 4 * 16384, stream, pp, st);
+    const int th = 64 * kBf16Waves;
+    if (bifocal) return launch_with_lds(prefill_bf16_kernel<true>, grid, th, 4 * 16384, stream, pp, st);
+    return launch_with_lds(prefill_bf16_kernel<false>, grid, th, 4 * 16384, stream, pp, st);
   }
-  if (bifocal) return launch_with_lds(prefill_f32_kernel<true>, grid, 3 * 32768, stream, pp, st);
-  return launch_with_lds(prefill_f32_kernel<false>, grid, 2 * 32768, stream, pp, st);
+  if (bifocal) return launch_with_lds(prefill_f32_kernel<true>, grid, 256, 3 * 32768, stream, pp, st);
+  return launch_with_lds(prefill_f32_kernel<false>, grid, 256, 2 * 32768, stream, pp, st);
 }
 
 hipError_t launch_pair_map(long long L, long long w0, long long s, int mode, int8_t* br,
