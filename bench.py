@@ -113,6 +113,8 @@ def main():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
+                    help="run only this leg (W warmup + K calls, no JSON line); for profilers")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -158,6 +160,14 @@ def main():
 
     flops = 4.0 * D * Hq * L * (L + 1) / 2
     kv_bytes = 2.0 * N * Hkv * D * 2
+
+    if args.only is not None:  # profiling mode: one leg only
+        fn = prefill if args.only == "prefill" else decode
+        for _ in range(args.warmup + args.steps):
+            fn()
+        torch.cuda.synchronize()
+        log(f"only {args.only}: {args.warmup} + {args.steps} calls done")
+        return
 
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
