@@ -23,10 +23,11 @@ namespace bf {
 typedef __attribute__((ext_vector_type(8))) __bf16 dbf16x8;
 typedef __attribute__((ext_vector_type(4))) short ds16x4;
 typedef __attribute__((ext_vector_type(4))) float df32x4;
+typedef __attribute__((ext_vector_type(2))) float df32x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 dbf16x2;
 
 constexpr int kDecBlock = 64;    // keys per streamed block
 constexpr int kDecMaxG = 16;     // query heads per KV head the kernel supports
-constexpr int kDecVRow = 136;    // padded LDS row of V (elements)
 
 struct DecodeParams {
   const uint16_t* q;    // [B][Hq][D]
@@ -59,49 +60,103 @@ __device__ __forceinline__ long long dcorr_num(long long p, long long s, int mod
   return mode == 1 ? (p / s - p) * s : -p * (s - 1);
 }
 
-// cos / sin of theta_m * (phi(p) - p): the angle and its reduction to one
-// turn are done in fp64 (exact integer numerator, ~1e5 rad at 128K), the
-// reduced turn fraction goes through the hardware sin / cos (input in turns).
-__device__ __forceinline__ void corr_cos_sin(double th, long long num, long long s, float& c,
-                                             float& sn) {
-  const double turns = th * ((double)num / (double)s) * 0.15915494309189533577;
+constexpr double kInv2Pi = 0.15915494309189533577;
+
+// cos / sin of an angle given in turns (fp64): the reduction to one turn is
+// done in fp64 (angles reach ~1e5 rad at 128K keys), the reduced fraction goes
+// through the hardware sin / cos, which take their input in turns.
+__device__ __forceinline__ void turn_cos_sin(double turns, float& c, float& sn) {
   const float fr = (float)(turns - rint(turns));
   sn = __builtin_amdgcn_sinf(fr);
   c = __builtin_amdgcn_cosf(fr);
 }
 
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((df32x2){lo, hi}, dbf16x2));
+}
+
+// a wave-uniform pointer forced into scalar registers, so that loads use the
+// scalar-base + 32-bit vector-offset addressing form
+__device__ __forceinline__ const char* dscalar_ptr(const void* ptr) {
+  const uint64_t v = (uint64_t)ptr;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const char*)(((uint64_t)hi << 32) | lo);
+}
+
+// 16-byte global load at a base plus a 32-bit offset (loaded as a native
+// vector: copying the uint4 struct through a reference would go back to a
+// generic pointer and a flat load)
+typedef __attribute__((ext_vector_type(4))) unsigned int du32x4;
+__device__ __forceinline__ uint4 gload16(const char* base, uint32_t off) {
+  const du32x4 v = *(const __attribute__((address_space(1))) du32x4*)(base + off);
+  return __builtin_bit_cast(uint4, v);
+}
+
+// x holds elements (m, m + 1), y holds (m + 64, m + 65): rotate both pairs,
+// returning the new x and writing the new y.
+__device__ __forceinline__ uint32_t rot_word(uint32_t x, uint32_t y, float c0, float s0, float c1,
+                                             float s1, uint32_t& y_out) {
+  const float a0 = __uint_as_float(x << 16), a1 = __uint_as_float(x & 0xffff0000u);
+  const float b0 = __uint_as_float(y << 16), b1 = __uint_as_float(y & 0xffff0000u);
+  y_out = pack_bf16x2(b0 * c0 + a0 * s0, b1 * c1 + a1 * s1);
+  return pack_bf16x2(a0 * c0 - b0 * s0, a1 * c1 - b1 * s1);
+}
+
 // ------------------------------------------------------------------ kernels
 // Split kernel: workgroup = (batch b, KV head, split of `chunk` keys). Each of
 // the 4 waves streams its own contiguous quarter of the split in 16-key steps,
-// independently of the other waves:
-//   - the 16 keys' K rows go straight into registers, laid out as the A
-//     operand of MFMA 16x16x32 (lane = key n16, head-dim chunks 4 t + g4), so
-//     both halves (m, m + 64) of every rotary pair sit in the same lane and the
-//     correction rotation of far keys is done in place;
-//   - the 16 keys' V rows go by direct global->LDS loads into a wave-private
-//     ring; P V uses the head-dim order d = 8 row + block so that one 16-byte
-//     LDS read per key feeds all 8 output blocks;
-//   - loads run two steps ahead of compute.
+// independently of the other waves. Both K and V go straight from HBM into
+// registers, already in the MFMA operand layouts (no LDS staging):
+//   - K: lane (key n16, group g4) holds head-dim chunks 4 t + g4 (t = 0..3) of
+//     its key, the A operand of MFMA 16x16x32 for S^T = K Q^T. Both halves
+//     (m, m + 64) of every rotary pair sit in the same lane, so the correction
+//     rotation of far keys is done in place;
+//   - V: lane (n16, g4) holds chunk n16 (head dims 8 n16 .. 8 n16 + 7) of keys
+//     4 g4 + q (q = 0..3); each quarter-wave reads whole 256-byte rows. P V
+//     uses the head-dim order d = 8 row + block, so these four registers feed
+//     the 8 MFMA 16x16x16 of the step after byte permutes only;
+//   - loads run two steps ahead of compute (three register slots).
 // The G query heads of the KV group are the MFMA columns (columns >= G are
 // zero queries whose results are dropped).
+//
+// Correction angles of far keys by angle addition. For a step starting at key
+// jb, key jb + n has phi(jb + n) - (jb + n) = [phi(jb) - jb] + e, where
+//   FI: e = -n (s - 1) / s                         (idx = n)
+//   PA: e = floor((r + n) / s) - n, r = jb mod s   (idx = n - floor((r + n) / s))
+// so e = -idx * kappa with idx in [0, 16) and kappa = (s - 1) / s (FI) or 1 (PA).
+// Per step each lane m computes the base rotation of theta_m [phi(jb) - jb]
+// (one fp64 reduction per pair for the whole wave), the 16 x 64 rotations by
+// theta_m e are a per-workgroup table, and a key's rotation is the product of
+// the two (cos / sin addition formulas).
 constexpr int kDecWaves = 4;
 constexpr int kDecStep = 16;  // keys per wave step
-constexpr int kDecRing = 3;   // V ring slots per wave (two steps in flight)
+constexpr int kDecRing = 3;   // register slots per wave (two steps in flight)
+constexpr int kDecTRow = 66;  // padded float2 row of the offset table (conflict-free reads)
 constexpr float kDecRescaleLog2 = 8.f;
 
-__device__ __forceinline__ void dec_wait_vm(int outstanding_steps) {
-  // loads complete in issue order; each step issues 8 vector-memory operations
-  if (outstanding_steps >= 2) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-  else if (outstanding_steps == 1) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+// LDS layout (bytes). Prologue / loop: Q' and Q'' [2][16][128] bf16, offset
+// table [16][66] float2, per-wave base rows [4][64] float2. After the loop the
+// same memory holds the 4-wave merge: m [4][16], l [4][16], acc [4][16][128].
+constexpr int kDecLdsQ = 0;
+constexpr int kDecLdsT = kDecLdsQ + 2 * kDecMaxG * kHeadDim * 2;
+constexpr int kDecLdsB = kDecLdsT + kDecStep * kDecTRow * 8;
+constexpr int kDecLdsLoop = kDecLdsB + kDecWaves * kPairs * 8;
+constexpr int kDecLdsMerge = (2 * kDecWaves * kDecMaxG + kDecWaves * kDecMaxG * kHeadDim) * 4;
+constexpr int kDecLds = kDecLdsLoop > kDecLdsMerge ? kDecLdsLoop : kDecLdsMerge;
+
+// Workgroup barrier after ds_write-only LDS traffic, with a compiler memory
+// barrier; unlike __syncthreads it does not wait for the K / V prefetches
+// already in flight.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 template <bool BIFOCAL>
 __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p, DecodeSeqs ds,
                                                               ThetaTable tt) {
-  // LDS: V rings [4 waves][3 slots][16 keys x 16 chunks] | Q' and Q'' [2][16][16 chunks]
-  __shared__ uint4 smem[kDecWaves * kDecRing * 256 + 2 * kDecMaxG * 16];
-  uint4* sQ = smem + kDecWaves * kDecRing * 256;
+  __shared__ uint4 smem[kDecLds / 16];
+  uint4* sQ = smem + kDecLdsQ / 16;
 
   const int b = blockIdx.z, kvh = blockIdx.y, sp = blockIdx.x;
   if (sp >= ds.nsplit[b]) return;
@@ -109,7 +164,8 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p, De
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n16 = lane & 15, g4 = lane >> 4;
   const long long N = ds.N[b];
-  const long long s = ds.s[b];
+  const int s_i = ds.s[b];
+  const long long s = s_i;
   const long long w0 = (BIFOCAL && s > 1) ? p.w0 : (1LL << 62);
   const long long far_lim = N - w0;  // keys j < far_lim are far
   const int chunk = ds.chunk[b];
@@ -119,22 +175,72 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p, De
   const long long kw0 = k_begin + (long long)wave * per;
   const long long kw1 = min(k_end, kw0 + per);
   const int ns = kw1 > kw0 ? (int)((kw1 - kw0 + kDecStep - 1) / kDecStep) : 0;
+  const bool split_far = BIFOCAL && k_begin < far_lim;
 
-  // ---- queries: Q' as given, Q'' = R(Delta(N - 1)) Q'; rows >= G are zero
+  const uint16_t* kbase = p.kc + ((size_t)b * p.Hkv + kvh) * (size_t)p.cap * kHeadDim;
+  const uint16_t* vbase = p.vc + ((size_t)b * p.Hkv + kvh) * (size_t)p.cap * kHeadDim;
+  // wave-local key indexing: key kw0 + jl, jl in [0, nl); byte offsets fit 32 bits
+  const int nl = ns > 0 ? (int)(kw1 - kw0) : 0;
+  const int far_l = (int)max(-1LL, min(far_lim - kw0, (long long)(per + kDecStep)));
+  const char* kwb = dscalar_ptr(kbase + (size_t)(ns > 0 ? kw0 : 0) * kHeadDim);
+  const char* vwb = dscalar_ptr(vbase + (size_t)(ns > 0 ? kw0 : 0) * kHeadDim);
+  const uint32_t v_lane = (uint32_t)(g4 * 4 * 256 + n16 * 16);  // key 4 g4, chunk n16
+  const uint32_t k_lane = (uint32_t)(n16 * 256 + g4 * 16);      // key n16, chunk g4
+  uint4 kreg[kDecRing][4], vreg[kDecRing][4];
+  // issue the loads of step st into register slot r, K first (needed first);
+  // rows past the wave's last key re-read that key (their scores are masked)
+  auto issue = [&](int st, int r) {
+    const int j0 = st * kDecStep;
+    if (j0 + kDecStep <= nl) {
+      const uint32_t base = (uint32_t)j0 * (kHeadDim * 2);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) kreg[r][t] = gload16(kwb, base + k_lane + t * 64);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) vreg[r][q] = gload16(vwb, base + v_lane + q * 256);
+    } else {
+      const uint32_t kk = (uint32_t)min(j0 + n16, nl - 1);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) kreg[r][t] = gload16(kwb, kk * (kHeadDim * 2) + (4 * t + g4) * 16);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t kv = (uint32_t)min(j0 + 4 * g4 + q, nl - 1);
+        vreg[r][q] = gload16(vwb, kv * (kHeadDim * 2) + n16 * 16);
+      }
+    }
+  };
+
+  // the query row and this lane's theta (every loop below over pairs has
+  // m = lane) are loaded first, then the first two steps' K / V loads go out
+  // before the prologue that needs them
+  const double th_lane = BIFOCAL ? tt.th[lane] : 0.0;
   {
     const int qi = tid >> 4, c = tid & 15;
     uint4 v0 = make_uint4(0, 0, 0, 0);
-    if (qi < p.G) v0 = *(const uint4*)(p.q + ((size_t)b * p.Hq + kvh * p.G + qi) * kHeadDim + c * 8);
+    if (qi < p.G) v0 = gload16((const char*)p.q, (uint32_t)((((size_t)b * p.Hq + kvh * p.G + qi) * kHeadDim + c * 8) * 2));
+    if (ns > 0) issue(0, 0);
+    if (ns > 1) issue(1, 1);
     sQ[qi * 16 + c] = v0;
     sQ[kDecMaxG * 16 + qi * 16 + c] = v0;
   }
-  __syncthreads();
-  if (BIFOCAL && far_lim > 0) {
-    for (int e = tid; e < p.G * kPairs; e += 256) {
-      const int qi = e >> 6, m = e & 63;
-      double sd, cd;
-      sincos(tt.th[m] * ((double)dcorr_num(N - 1, s, p.mode) / (double)s), &sd, &cd);
-      const float c = (float)cd, sn = (float)sd;
+  float2* sT = (float2*)((char*)smem + kDecLdsT);
+  float2* sBw = (float2*)((char*)smem + kDecLdsB) + wave * kPairs;
+  if (split_far) {
+    // offset table: row idx, pair m = rotation by -theta_m * idx * kappa
+    const double kappa = p.mode == 1 ? 1.0 : (double)(s - 1) / (double)s;
+    for (int e = tid; e < kDecStep * kPairs; e += 256) {  // pair m = e % 64 = lane
+      const int idx = e >> 6;
+      float c, sn;
+      turn_cos_sin(-th_lane * kInv2Pi * (double)idx * kappa, c, sn);
+      sT[idx * kDecTRow + lane] = make_float2(c, sn);
+    }
+  }
+  lds_barrier();
+  if (split_far) {
+    const double qn = (double)dcorr_num(N - 1, s, p.mode) / (double)s;
+    float c, sn;
+    turn_cos_sin(th_lane * kInv2Pi * qn, c, sn);
+    for (int e = tid; e < p.G * kPairs; e += 256) {  // pair m = e % 64 = lane
+      const int qi = e >> 6, m = lane;
       const uint16_t* row = (const uint16_t*)(sQ + qi * 16);
       const float x0 = dbf2f(row[m]), x1 = dbf2f(row[m + kPairs]);
       uint16_t* r2 = (uint16_t*)(sQ + kDecMaxG * 16 + qi * 16);
@@ -142,95 +248,113 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p, De
       r2[m + kPairs] = df2bf(x1 * c + x0 * sn);
     }
   }
-  __syncthreads();
-  dbf16x8 qf[4], qf2[4];  // B operand: lane (query n16, group g4), head dims 32 t + 8 g4 .. +7
+  lds_barrier();
+  // B operand of a step, read from LDS per step (Q' or Q''): lane (query n16,
+  // group g4) holds head dims 32 t + 8 g4 .. +7
+  auto q_operand = [&](bool corrected, dbf16x8 (&qo)[4]) {
+    const uint4* src = sQ + (corrected ? kDecMaxG * 16 : 0) + n16 * 16 + g4;
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    qf[t] = __builtin_bit_cast(dbf16x8, sQ[n16 * 16 + 4 * t + g4]);
-    qf2[t] = __builtin_bit_cast(dbf16x8, sQ[kDecMaxG * 16 + n16 * 16 + 4 * t + g4]);
-  }
+    for (int t = 0; t < 4; ++t) qo[t] = __builtin_bit_cast(dbf16x8, src[4 * t]);
+  };
 
-  const uint16_t* kbase = p.kc + ((size_t)b * p.Hkv + kvh) * (size_t)p.cap * kHeadDim;
-  const uint16_t* vbase = p.vc + ((size_t)b * p.Hkv + kvh) * (size_t)p.cap * kHeadDim;
-  uint4* vring = smem + wave * (kDecRing * 256);
   const double inv_s = 1.0 / (double)s;
+  const float inv_s_f = 1.f / (float)s_i;
+  const double th_turn = th_lane * kInv2Pi;  // this lane's pair m = lane
+  // (q_pa, r_pa) = divmod(step start, s), advanced by 16 keys per step
+  long long q_pa = 0;
+  int r_pa = 0;
+  if (BIFOCAL) {
+    q_pa = kw0 / s;
+    r_pa = (int)(kw0 - q_pa * s);
+  }
+  const int add16_q = 16 / s_i, add16_r = 16 % s_i;
 
   float m_used = -INFINITY, l_part = 0.f;
   df32x4 oacc[8];
 #pragma unroll
   for (int db = 0; db < 8; ++db) oacc[db] = df32x4{};
 
-  uint4 kreg[kDecRing][4];
-  // issue the loads of step st into ring slot r: V rows first, then this lane's K row
-  auto issue = [&](int st, int r) {
-    const long long j0 = kw0 + (long long)st * kDecStep;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const long long key = min(j0 + 4 * i + (lane >> 4), kw1 - 1);
-      __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(vbase + (size_t)key * kHeadDim + (lane & 15) * 8),
-          (__attribute__((address_space(3))) void*)(vring + r * 256 + i * 64), 16, 0, 0);
-    }
-    const long long key = min(j0 + n16, kw1 - 1);
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-      kreg[r][t] = *(const uint4*)(kbase + (size_t)key * kHeadDim + (4 * t + g4) * 8);
-  };
-
   auto process = [&](int st, int r) {
-    const long long jb = kw0 + (long long)st * kDecStep;
-    const bool any_far = BIFOCAL && jb < far_lim;
-    const bool any_loc = !BIFOCAL || jb + kDecStep - 1 >= far_lim;
-    uint4 kr[4] = {kreg[r][0], kreg[r][1], kreg[r][2], kreg[r][3]};
-    const long long j = jb + n16;  // this lane's A-operand key
-    if (any_far && j < far_lim) {
-      // rotary pairs (m, m + 64) = (element e of chunk 4 t + g4, same element of chunk 4 (t + 2) + g4)
-      const double qn = (double)dcorr_num(j, s, p.mode) * inv_s;
+    const int jbl = st * kDecStep;  // wave-local first key of the step
+    const bool any_far = BIFOCAL && jbl < far_l;
+    const bool any_loc = !BIFOCAL || jbl + kDecStep - 1 >= far_l;
+    uint4* kr = kreg[r];  // rotated in place
+    df32x4 Sl = df32x4{};
+    if (any_far && any_loc) {  // step straddles the window edge: local keys score with Q'
+      dbf16x8 ql[4];
+      q_operand(false, ql);
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        uint32_t* lo = (uint32_t*)&kr[t];
-        uint32_t* hi = (uint32_t*)&kr[t + 2];
+      for (int t = 0; t < 4; ++t)
+        Sl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(dbf16x8, kr[t]), ql[t], Sl, 0, 0, 0);
+    }
+    if (any_far) {
+      // base rotation of the step, pair m = lane
+      const long long jb = kw0 + jbl;
+      const double qb = p.mode == 1 ? (double)(q_pa - jb) : (double)(-jb * (s - 1)) * inv_s;
+      float cb, sb;
+      turn_cos_sin(th_turn * qb, cb, sb);
+      sBw[lane] = make_float2(cb, sb);
+      int idx = n16;
+      if (p.mode == 1) {
+        const int x = r_pa + n16;
+        int qd = (int)((float)x * inv_s_f);
+        if ((qd + 1) * s_i <= x) ++qd;
+        if (qd * s_i > x) --qd;
+        idx = n16 - qd;
+      }
+      if (jbl + n16 < far_l) {
+        const float4* bq4 = (const float4*)sBw;
+        const float4* tq4 = (const float4*)(sT + idx * kDecTRow);
+        // rotary pairs (m, m + 64) = (element e of chunk 4 t + g4, same element of chunk 4 (t + 2) + g4)
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const int m0 = 32 * t + 8 * g4 + 2 * w;
-          const double tu0 = tt.th[m0] * qn * 0.15915494309189533577;
-          const double tu1 = tt.th[m0 + 1] * qn * 0.15915494309189533577;
-          const float f0 = (float)(tu0 - rint(tu0)), f1 = (float)(tu1 - rint(tu1));
-          const float c0 = __builtin_amdgcn_cosf(f0), s0 = __builtin_amdgcn_sinf(f0);
-          const float c1 = __builtin_amdgcn_cosf(f1), s1 = __builtin_amdgcn_sinf(f1);
-          const float a0 = __uint_as_float(lo[w] << 16), a1 = __uint_as_float(lo[w] & 0xffff0000u);
-          const float b0 = __uint_as_float(hi[w] << 16), b1 = __uint_as_float(hi[w] & 0xffff0000u);
-          lo[w] = (uint32_t)df2bf(a0 * c0 - b0 * s0) | ((uint32_t)df2bf(a1 * c1 - b1 * s1) << 16);
-          hi[w] = (uint32_t)df2bf(b0 * c0 + a0 * s0) | ((uint32_t)df2bf(b1 * c1 + a1 * s1) << 16);
+        for (int t = 0; t < 2; ++t) {
+          uint32_t* lo = (uint32_t*)&kr[t];
+          uint32_t* hi = (uint32_t*)&kr[t + 2];
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            // pairs m = 32 t + 8 g4 + 2 w and m + 1
+            const float4 bq = bq4[16 * t + 4 * g4 + w];
+            const float4 tq = tq4[16 * t + 4 * g4 + w];
+            const float c0 = bq.x * tq.x - bq.y * tq.y, s0 = bq.y * tq.x + bq.x * tq.y;
+            const float c1 = bq.z * tq.z - bq.w * tq.w, s1 = bq.w * tq.z + bq.z * tq.w;
+            uint32_t yo;
+            lo[w] = rot_word(lo[w], hi[w], c0, s0, c1, s1, yo);
+            hi[w] = yo;
+          }
         }
       }
     }
+    if (BIFOCAL) {
+      q_pa += add16_q;
+      r_pa += add16_r;
+      if (r_pa >= s_i) {
+        r_pa -= s_i;
+        ++q_pa;
+      }
+    }
+    dbf16x8 qs[4];
+    q_operand(any_far, qs);
     df32x4 S = df32x4{};
 #pragma unroll
     for (int t = 0; t < 4; ++t)
-      S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(dbf16x8, kr[t]),
-                                                  any_far ? qf2[t] : qf[t], S, 0, 0, 0);
-    if (any_far && any_loc) {  // step straddles the window edge: local keys score with Q'
-      df32x4 Sl = df32x4{};
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-        Sl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(dbf16x8, kreg[r][t]), qf[t],
-                                                     Sl, 0, 0, 0);
+      S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(dbf16x8, kr[t]), qs[t], S, 0, 0, 0);
+    if (any_far && any_loc) {
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        if (jb + 4 * g4 + q >= far_lim) S[q] = Sl[q];
+        if (jbl + 4 * g4 + q >= far_l) S[q] = Sl[q];
     }
-    // C layout: lane (query n16, g4) holds keys jb + 4 g4 + q
-    if (jb + kDecStep > kw1) {
+    // C layout: lane (query n16, g4) holds keys jbl + 4 g4 + q
+    if (jbl + kDecStep > nl) {
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        if (jb + 4 * g4 + q >= kw1) S[q] = -INFINITY;
+        if (jbl + 4 * g4 + q >= nl) S[q] = -INFINITY;
     }
-    float mx = fmaxf(fmaxf(S[0], S[1]), fmaxf(S[2], S[3]));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    mx *= p.scale_log2;
+    // lazy rescale: the reference max of a query moves only when one of its
+    // scores exceeds it by more than 2^8; the column max is needed only then
+    float mx = fmaxf(fmaxf(S[0], S[1]), fmaxf(S[2], S[3])) * p.scale_log2;
     if (__any(mx > m_used + kDecRescaleLog2)) {
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
       const float mn = fmaxf(m_used, mx);
       const float alpha = (m_used == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_used - mn);
       l_part *= alpha;
@@ -239,47 +363,48 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p, De
       m_used = mn;
     }
     const float mb = (m_used == -INFINITY) ? 0.f : m_used;
-    ds16x4 pb;
+    float e[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const float e = __builtin_amdgcn_exp2f(fmaf(S[q], p.scale_log2, -mb));
-      l_part += e;
-      pb[q] = (short)df2bf(e);
+      e[q] = __builtin_amdgcn_exp2f(fmaf(S[q], p.scale_log2, -mb));
+      l_part += e[q];
     }
-    // V rows of keys 4 g4 + q, chunk n16 (head dims 8 n16 .. 8 n16 + 7)
-    uint4 vr[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) vr[q] = vring[r * 256 + (4 * g4 + q) * 16 + n16];
+    const ds16x4 pb =
+        __builtin_bit_cast(ds16x4, make_uint2(pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3])));
+    // vreg[r][q]: key 4 g4 + q, head dims 8 n16 .. 8 n16 + 7
+    const uint4* vr = vreg[r];
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
       const uint32_t w0q = ((const uint32_t*)&vr[0])[db >> 1], w1q = ((const uint32_t*)&vr[1])[db >> 1];
       const uint32_t w2q = ((const uint32_t*)&vr[2])[db >> 1], w3q = ((const uint32_t*)&vr[3])[db >> 1];
       const uint32_t sel = (db & 1) ? 0x07060302u : 0x05040100u;
       const uint32_t x01 = __builtin_amdgcn_perm(w1q, w0q, sel), x23 = __builtin_amdgcn_perm(w3q, w2q, sel);
-      ds16x4 a;
-      a[0] = (short)(x01 & 0xffff);
-      a[1] = (short)(x01 >> 16);
-      a[2] = (short)(x23 & 0xffff);
-      a[3] = (short)(x23 >> 16);
-      oacc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pb, oacc[db], 0, 0, 0);
+      oacc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+          __builtin_bit_cast(ds16x4, make_uint2(x01, x23)), pb, oacc[db], 0, 0, 0);
     }
   };
 
-  if (ns > 0) issue(0, 0);
-  if (ns > 1) issue(1, 1);
-  for (int st = 0; st < ns; st += kDecRing) {
+  // steady state: every step issues the step two ahead (no branches, so the
+  // compiler's load-counter waits stay exact); the last steps drain
+  int st = 0;
+  for (; st + 5 <= ns; st += kDecRing) {
+    issue(st + 2, 2);
+    process(st, 0);
+    issue(st + 3, 0);
+    process(st + 1, 1);
+    issue(st + 4, 1);
+    process(st + 2, 2);
+  }
 #pragma unroll
-    for (int u = 0; u < kDecRing; ++u) {
-      const int cur = st + u;
-      if (cur < ns) {
-        if (cur + 2 < ns) issue(cur + 2, (u + 2) % kDecRing);
-        dec_wait_vm(min(2, ns - 1 - cur));
-        process(cur, u);
-      }
+  for (int u = 0; u < 4; ++u) {
+    const int cur = st + u;
+    if (cur < ns) {
+      if (cur + 2 < ns) issue(cur + 2, (u + 2) % kDecRing);
+      process(cur, u % kDecRing);
     }
   }
 
-  // ---- merge the 4 waves (V rings reused), write the split's partial
+  // ---- merge the 4 waves, write the split's partial
   const float lsum = l_part + __shfl_xor(l_part, 16);
   const float ltot = lsum + __shfl_xor(lsum, 32);  // column total over the wave's keys
   __syncthreads();
@@ -320,43 +445,57 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p, De
 }
 
 // One workgroup per (query head, batch): log-sum-exp merge of the splits.
-// Split weights are computed once into LDS; each thread then sums a strided
-// subset of splits for one float4 of head dims and the subsets are added.
+// Thread t owns float4 d4 = t % 32 of the head dims for splits t / 32 + 8 k.
+// The partial rows of the first kHold rounds are loaded into registers before
+// the max / weight reductions so that their latency overlaps them.
+constexpr int kDecMaxSplits = 1088;
+constexpr int kCombHold = 17;  // 8 x 17 = 136 splits held in registers
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p, DecodeSeqs ds) {
-  __shared__ float wgt[1088];
-  __shared__ float red[256];
+  __shared__ float wgt[kDecMaxSplits];
+  __shared__ float red[8];
   __shared__ float4 part4[8][32];
   const int b = blockIdx.y, h = blockIdx.x, t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
   const int ns = ds.nsplit[b];
   const size_t row0 = ((size_t)b * p.Hq + h) * p.S;
+  const int d4 = t & 31, grp = t >> 5;
+  float4 hold[kCombHold];
+#pragma unroll
+  for (int k = 0; k < kCombHold; ++k) {
+    const int i = grp + 8 * k;
+    const float4 v = *(const float4*)(p.part_acc + (row0 + min(i, ns - 1)) * kHeadDim + 4 * d4);
+    hold[k] = i < ns ? v : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
   float mloc = -INFINITY;
   for (int i = t; i < ns; i += 256) mloc = fmaxf(mloc, p.part_m[row0 + i]);
-  red[t] = mloc;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, o));
+  if (lane == 0) red[wave] = mloc;
   __syncthreads();
-  for (int k = 128; k > 0; k >>= 1) {
-    if (t < k) red[t] = fmaxf(red[t], red[t + k]);
-    __syncthreads();
-  }
-  const float mt = red[0];
+  const float mt = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const float mbt = (mt == -INFINITY) ? 0.f : mt;
-  __syncthreads();
   float lloc = 0.f;
   for (int i = t; i < ns; i += 256) {
     const float w = __builtin_amdgcn_exp2f(p.part_m[row0 + i] - mbt);
     wgt[i] = w;
     lloc += w * p.part_l[row0 + i];
   }
-  red[t] = lloc;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) lloc += __shfl_xor(lloc, o);
+  if (lane == 0) red[4 + wave] = lloc;
   __syncthreads();
-  for (int k = 128; k > 0; k >>= 1) {
-    if (t < k) red[t] += red[t + k];
-    __syncthreads();
-  }
-  const float lt = red[0];
-  const int d4 = t & 31, grp = t >> 5;
+  const float lt = (red[4] + red[5]) + (red[6] + red[7]);
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 4
-  for (int i = grp; i < ns; i += 8) {
+#pragma unroll
+  for (int k = 0; k < kCombHold; ++k) {
+    const int i = grp + 8 * k;
+    const float w = i < ns ? wgt[min(i, ns - 1)] : 0.f;
+    acc.x += w * hold[k].x;
+    acc.y += w * hold[k].y;
+    acc.z += w * hold[k].z;
+    acc.w += w * hold[k].w;
+  }
+  for (int i = grp + 8 * kCombHold; i < ns; i += 8) {
     const float4 v = *(const float4*)(p.part_acc + (row0 + i) * kHeadDim + 4 * d4);
     const float w = wgt[i];
     acc.x += w * v.x;
@@ -386,20 +525,32 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p, Dec
 }
 
 // ------------------------------------------------------------------ host side
-// Keys per split: about 128 splits per sequence, 64..1024 keys each.
+// Keys per split: about kDecTargetSplits splits per sequence, 64 to
+// kDecMaxChunk keys each (both overridable at build time for tuning sweeps).
+#ifndef BF_DEC_TARGET_SPLITS
+#define BF_DEC_TARGET_SPLITS 128
+#endif
+#ifndef BF_DEC_MAX_CHUNK
+#define BF_DEC_MAX_CHUNK 1024
+#endif
+constexpr long long kDecTargetSplits = BF_DEC_TARGET_SPLITS;
+constexpr long long kDecMaxChunk = BF_DEC_MAX_CHUNK;
+static_assert(kDecMaxChunk % kDecBlock == 0, "chunk must be a multiple of 64 keys");
+
 static int decode_chunk(long long N) {
-  long long c = (N + 127) / 128;
+  long long c = (N + kDecTargetSplits - 1) / kDecTargetSplits;
   c = ((c + kDecBlock - 1) / kDecBlock) * kDecBlock;
   if (c < kDecBlock) c = kDecBlock;
-  if (c > 1024) c = 1024;
+  if (c > kDecMaxChunk) c = kDecMaxChunk;
   return (int)c;
 }
 
 int decode_splits(long long N) { return (int)((N + decode_chunk(N) - 1) / decode_chunk(N)); }
 
+// Upper bound of decode_splits over all lengths <= max_len (it is monotone).
 static int decode_split_bound(long long max_len) {
-  const long long a = (max_len + 1023) / 1024 + 1;
-  return (int)(a > 129 ? a : 129);
+  const long long a = (max_len + kDecMaxChunk - 1) / kDecMaxChunk + 1;
+  return (int)(a > kDecTargetSplits + 1 ? a : kDecTargetSplits + 1);
 }
 
 struct DecodeWs {
@@ -441,8 +592,9 @@ int run_decode(bool bifocal, const void* q, const void* kc, const void* vc, void
       return bad(BF_ERR_INVALID_ARG, "seqlens[" + std::to_string(b) + "] out of [1, cache_capacity]");
     if (seqlens[b] > max_len) max_len = seqlens[b];
   }
-  if (decode_split_bound(max_len) > 1088)
-    return bad(BF_ERR_UNSUPPORTED, "decode supports caches of at most 1088 x 1024 keys");
+  if (decode_split_bound(max_len) > kDecMaxSplits)
+    return bad(BF_ERR_UNSUPPORTED, "decode supports at most " + std::to_string(kDecMaxSplits - 1) +
+                                       " x " + std::to_string(kDecMaxChunk) + " keys per sequence");
   const DecodeWs wl = decode_ws_layout(batch, max_len, Hq);
   if (!ws) return bad(BF_ERR_WORKSPACE, "workspace is null");
   if ((uintptr_t)ws & 255u) return bad(BF_ERR_WORKSPACE, "workspace must be 256-byte aligned");

@@ -268,7 +268,8 @@ def test_qwen3_8b_decode(Lc, mode):
 @pytest.mark.parametrize("N,cap,B,G,w0,w_pre,mode", [
     (1, 8, 1, 4, 0, 1, "fi"), (63, 70, 2, 2, 5, 16, "pa"), (64, 64, 1, 16, 64, 20, "fi"),
     (65, 100, 3, 1, 1, 10, "pa"), (1000, 1024, 2, 8, 200, 300, "fi"),
-    ([5, 900, 4097], 4100, 3, 4, 256, 1024, "pa")])
+    ([5, 900, 4097], 4100, 3, 4, 256, 1024, "pa"), (3000, 3000, 1, 4, 100, 7, "pa"),
+    (3000, 3000, 1, 4, 100, 7, "fi"), (2049, 2100, 2, 8, 64, 1000, "pa")])
 def test_decode_edges(N, cap, B, G, w0, w_pre, mode):
     Hkv = 2
     og, lg, o_ref, lse_ref, _ = _decode_case(N, cap, G * Hkv, Hkv, w0, w_pre, 1e6, mode, 77, B)
