@@ -12,13 +12,14 @@
 //   pair_map_kernel         test hook: the device pair rule and position map
 //
 // Tile loop [ai-feeds.com summary, "关键模块" items 1 and 3; seventnews.com (FR),
-// fusion paragraph]: for a query row block and a 64-key tile, every causal pair
-// is either local (i - j < w0: original RoPE, q' . k') or far (q'' . k''). Keys
-// are visited in ascending order, which is the order far -> mixed -> band ->
-// diagonal. A far tile only reads K'', a band tile only K', and a mixed tile
-// computes both score blocks and picks per element, so each pair enters the
-// softmax exactly once and the scaled-branch work over the band that the
-// inclusion-exclusion merge would subtract again is never done.
+// fusion paragraph]: every causal pair is either local (i - j < w0: original
+// RoPE, q' . k') or far (q'' . k''). In the bf16 kernel the far branch and the
+// local branch run as two passes over their own key-tile ranges, sharing one
+// online-softmax state; the fp32 kernel visits the tiles once in ascending
+// order and, on a tile holding both kinds, computes both score blocks and
+// picks per element. Either way each pair enters the softmax exactly once and
+// the scaled-branch work over the band that the inclusion-exclusion merge
+// would subtract again is never done.
 #include <hip/hip_runtime.h>
 
 #include "bf_common.h"
