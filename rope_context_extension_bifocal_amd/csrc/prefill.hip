@@ -29,6 +29,7 @@ namespace bf {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;  // 8 packed bf16
 
 // ----------------------------------------------------------------- helpers
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
@@ -265,31 +266,70 @@ __device__ __forceinline__ void apply_rescale(RowState& rs, f32x16 (&oacc)[4]) {
   }
 }
 
-__device__ __forceinline__ void qk_tile(const uint4* __restrict__ sk, const bf16x8 (&q)[8], int li,
-                                        int hl, f32x16 (&S)[2]) {
-  const int row0 = key_of_mfma_row(li), row1 = 32 + row0;
-  bf16x8 a0[8], a1[8];
-#pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    const int ch = 2 * t + hl;
-    a0[t] = __builtin_bit_cast(bf16x8, sk[row0 * 16 + (ch ^ (row0 & 15))]);
-    a1[t] = __builtin_bit_cast(bf16x8, sk[row1 * 16 + (ch ^ (row1 & 15))]);
-  }
+// LDS byte addresses of MFMA operand fragments. Both swizzles XOR the chunk
+// index with lane bits only, so the address of k-step t is one v_xad of a
+// lane base: base + ((step bits) ^ lane swizzle). The lane swizzle is made
+// opaque at each use so that the compiler recomputes the per-step addresses
+// (one instruction each) instead of holding all of them in registers.
+struct FragAddr {
+  uint32_t k_base, k_sw;  // K tile: row key_of_mfma_row(li), chunk (2 t + hl) ^ (row % 16)
+  uint32_t v_base, v_sw;  // V^T tile: head dim li (+ 32 db), chunk (4 jb + 2 u + hl) ^ ((li / 2) % 8)
+};
+
+__device__ __forceinline__ FragAddr frag_addr(int li, int hl) {
+  FragAddr fa;
+  const int row0 = key_of_mfma_row(li), sk = row0 & 15;
+  fa.k_base = (uint32_t)(row0 * 256 + ((hl ^ sk) & 1) * 16);
+  fa.k_sw = (uint32_t)((sk & 14) * 16);
+  const int sv = (li >> 1) & 7;
+  fa.v_base = (uint32_t)(li * 128 + ((hl ^ sv) & 1) * 16);
+  fa.v_sw = (uint32_t)((sv & 6) * 16);
+  return fa;
+}
+
+__device__ __forceinline__ bf16x8 lds_frag(const uint4* tile, uint32_t byte_off) {
+  return __builtin_bit_cast(bf16x8, *(const uint4*)((const char*)tile + byte_off));
+}
+
+// Waits for all outstanding LDS reads. Written with the builtin (not inline
+// asm) so that the compiler's wait insertion knows the reads are complete.
+// Explicit waits are used in the tile loops because after a direct
+// global->LDS load the compiler only emits full LDS waits anyway (those do not
+// wait for the direct loads themselves); placing them before the next operand
+// batch is issued keeps that batch in flight.
+__device__ __forceinline__ void lds_reads_done() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// QK^T of one tile: S[blk] (keys 32 blk .. 32 blk + 31 x the wave's 32
+// queries). K operands are read in batches of four, one batch ahead of their
+// MFMAs, with one full LDS wait per batch (see lds_reads_done).
+__device__ __forceinline__ void qk_tile(const uint4* __restrict__ sk, const bf16x8 (&q)[8],
+                                        FragAddr fa, f32x16 (&S)[2]) {
+  asm volatile("" : "+v"(fa.k_sw));
+  bf16x8 fr[16];
+  auto load = [&](int i) {  // MFMA i: k-step t = i / 2, key block blk = i % 2
+    const int t = i >> 1, blk = i & 1;
+    fr[i] = lds_frag(sk, (((uint32_t)(32 * t) ^ fa.k_sw) + fa.k_base) + blk * (32 * 256));
+  };
   S[0] = f32x16{};
   S[1] = f32x16{};
 #pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    S[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[t], q[t], S[0], 0, 0, 0);
-    S[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[t], q[t], S[1], 0, 0, 0);
-  }
-  // operands two k-steps ahead of their MFMAs
-  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+  for (int i = 0; i < 4; ++i) load(i);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int t = 0; t < 6; ++t) {
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+  for (int b = 0; b < 4; ++b) {
+    lds_reads_done();
+    if (b < 3) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) load(4 * b + 4 + j);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = 4 * b + j;
+      S[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i], q[i >> 1], S[i & 1], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
-  __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 }
 
 // Mask a tile (keys c0 .. c0 + 63) for a pass: the far pass keeps pairs with
@@ -312,27 +352,26 @@ __device__ __forceinline__ void mask_tile(f32x16 (&S)[2], const WaveRows& wr, in
     }
 }
 
-__device__ __forceinline__ void pv_tile(const uint4* __restrict__ sv, const bf16x8 (&P)[2][2],
-                                        int li, int hl, f32x16 (&oacc)[4]) {
+__device__ __forceinline__ void pv_tile(const uint4* __restrict__ sv, const u32x4 (&P)[2][2],
+                                        FragAddr fa, f32x16 (&oacc)[4]) {
+  asm volatile("" : "+v"(fa.v_sw));
   bf16x8 a[4][2][2];
 #pragma unroll
-  for (int db = 0; db < 4; ++db) {
-    const int d = 32 * db + li;
+  for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
-    for (int jb = 0; jb < 2; ++jb)
+    for (int u = 0; u < 2; ++u) {
+      const uint32_t off = ((uint32_t)(64 * jb + 32 * u) ^ fa.v_sw) + fa.v_base;
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int ch = 4 * jb + 2 * u + hl;
-        a[db][jb][u] = __builtin_bit_cast(bf16x8, sv[d * 8 + (ch ^ ((d >> 1) & 7))]);
-      }
-  }
+      for (int db = 0; db < 4; ++db) a[db][jb][u] = lds_frag(sv, off + db * 32 * 128);
+    }
 #pragma unroll
   for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int db = 0; db < 4; ++db)
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[db][jb][u], P[jb][u], oacc[db], 0, 0, 0);
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[db][jb][u], __builtin_bit_cast(bf16x8, P[jb][u]),
+                                                           oacc[db], 0, 0, 0);
   // operands two MFMAs ahead
   __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
@@ -359,20 +398,21 @@ __device__ __forceinline__ void slot_barrier() {
 // d = p / 8 and key chunk (p % 8) ^ ((d / 2) % 8). Both swizzles keep the 16
 // lanes of one LDS read cycle on distinct banks.
 struct StageOffsets {
-  uint32_t k[kStageIters];  // byte offset inside a 64-key K tile (key row = offset / 256)
-  uint32_t v[kStageIters];  // byte offset inside a V^T tile
+  uint32_t k;  // byte offset inside a 64-key K tile of instruction 0 (key row = offset / 256)
+  uint32_t v;  // byte offset inside a V^T tile of instruction 0
 };
+// Instruction i of a wave covers chunks p + 256 i: the swizzled column does
+// not depend on i (row % 16 and (d / 2) % 8 only see the wave and lane bits),
+// so instruction i is instruction 0 moved by 4 KiB.
+constexpr uint32_t kStageStride = 4096;
 
 __device__ __forceinline__ StageOffsets stage_offsets(int wave, int lane) {
   StageOffsets so;
-#pragma unroll
-  for (int i = 0; i < kStageIters; ++i) {
-    const int p = (kBf16Waves * i + wave) * 64 + lane;
-    const int row = p >> 4, col = (p & 15) ^ (row & 15);
-    so.k[i] = (uint32_t)(row * kHeadDim + col * 8) * 2u;
-    const int d = p >> 3, vc = (p & 7) ^ ((d >> 1) & 7);
-    so.v[i] = (uint32_t)(d * kKeyTile + vc * 8) * 2u;
-  }
+  const int p = wave * 64 + lane;
+  const int row = p >> 4, col = (p & 15) ^ (row & 15);
+  so.k = (uint32_t)(row * kHeadDim + col * 8) * 2u;
+  const int d = p >> 3, vc = (p & 7) ^ ((d >> 1) & 7);
+  so.v = (uint32_t)(d * kKeyTile + vc * 8) * 2u;
   return so;
 }
 
@@ -398,13 +438,15 @@ __device__ __forceinline__ void stage_k(uint4* slot, const uint16_t* ktile, int 
   const char* kb = scalar_ptr(ktile);
   if (keys_left >= kKeyTile) {
 #pragma unroll
-    for (int i = 0; i < kStageIters; ++i) g2lds(kb, so.k[i], slot + (kBf16Waves * i + wave) * 64);
+    for (int i = 0; i < kStageIters; ++i)
+      g2lds(kb + i * kStageStride, so.k, slot + (kBf16Waves * i + wave) * 64);
   } else {
 #pragma unroll
     for (int i = 0; i < kStageIters; ++i) {
-      const int row = (int)(so.k[i] >> 8);
+      const uint32_t off = so.k + i * kStageStride;
+      const int row = (int)(off >> 8);
       const int shift = row < keys_left ? 0 : (keys_left - 1 - row) * kHeadDim * 2;
-      g2lds(kb, (uint32_t)((int)so.k[i] + shift), slot + (kBf16Waves * i + wave) * 64);
+      g2lds(kb, (uint32_t)((int)off + shift), slot + (kBf16Waves * i + wave) * 64);
     }
   }
 }
@@ -413,33 +455,41 @@ __device__ __forceinline__ void stage_v(uint4* slot, const uint16_t* vtile, cons
                                         int wave) {
   const char* vb = scalar_ptr(vtile);
 #pragma unroll
-  for (int i = 0; i < kStageIters; ++i) g2lds(vb, so.v[i], slot + (kBf16Waves * i + wave) * 64);
+  for (int i = 0; i < kStageIters; ++i)
+    g2lds(vb + i * kStageStride, so.v, slot + (kBf16Waves * i + wave) * 64);
 }
 
-// Softmax step of a tile: mask, row max, lazy rescale, probabilities (bf16)
-// and row sum.
-template <bool FAR>
-__device__ __forceinline__ void vector_slot(f32x16 (&S)[2], const WaveRows& wr, int c0, float sc,
-                                            int li, int hl, RowState& rs, f32x16 (&oacc)[4],
-                                            bf16x8 (&P)[2][2]) {
-  mask_tile<FAR>(S, wr, c0, li, hl);
+// Row max over the two lane halves that hold one query row: one cross-half
+// lane swap (no LDS round trip). max3 of the value and both swap results is
+// the row max whichever half each result comes from.
+__device__ __forceinline__ float row_max_halves(float m) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  return fmaxf(m, fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
+}
+
+// Softmax of one tile's (already masked) scores: row max, lazy rescale
+// decision, probabilities (bf16) and row sum. Branch-free, so that it can
+// share a scheduling region with the next tile's QK MFMAs: the decision to
+// move the stale max is a wave-wide ballot applied with selects (when nothing
+// moves, alpha = exp2(0) = 1 exactly).
+__device__ __forceinline__ void softmax_tile(f32x16 (&S)[2], float sc, RowState& rs,
+                                             u32x4 (&P)[2][2]) {
   float m = -INFINITY;
 #pragma unroll
   for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
     for (int r = 0; r < 16; r += 2) m = fmaxf(m, fmaxf(S[jb][r], S[jb][r + 1]));
-  m = fmaxf(m, __shfl_xor(m, 32)) * sc;
-  // A new row max more than 2^8 above the stale one: move the stale max and
-  // leave the factor for the O accumulator to the next matrix slot.
-  if (__any(m > rs.m_used + kRescaleLog2)) {
-    const float mn = fmaxf(rs.m_used, m);
-    const float alpha = (rs.m_used == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(rs.m_used - mn);
-    rs.l_part *= alpha;
-    rs.alpha *= alpha;
-    rs.rescale = true;
-    rs.m_used = mn;
-  }
-  const float mb = (rs.m_used == -INFINITY) ? 0.f : rs.m_used;
+  m = row_max_halves(m) * sc;
+  // a new row max more than 2^8 above the stale one moves the stale max; the
+  // factor for the O accumulator is left to the next matrix slot
+  const bool grow = __any(m > rs.m_used + kRescaleLog2);
+  const float mn = grow ? fmaxf(rs.m_used, m) : rs.m_used;
+  const float alpha = (rs.m_used == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(rs.m_used - mn);
+  rs.l_part *= alpha;
+  rs.alpha *= alpha;
+  rs.rescale = rs.rescale || grow;
+  rs.m_used = mn;
+  const float mb = (mn == -INFINITY) ? 0.f : mn;
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   float sum = rs.l_part;
 #pragma unroll
@@ -450,7 +500,7 @@ __device__ __forceinline__ void vector_slot(f32x16 (&S)[2], const WaveRows& wr, 
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         v[e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(S[jb][8 * u + e], sc, -mb));
-      P[jb][u] = v;
+      P[jb][u] = __builtin_bit_cast(u32x4, v);
       // the row sum adds the same bf16-rounded probabilities the P V product uses
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
@@ -461,8 +511,90 @@ __device__ __forceinline__ void vector_slot(f32x16 (&S)[2], const WaveRows& wr, 
   rs.l_part = sum;
 }
 
-// One pass (far or local) of a wave over tiles [ktb, kte). vt0 points at the
-// sequence's first V^T tile of this KV head.
+constexpr int kRing = 2;  // K and V^T ring slots per workgroup
+
+// P V of tile t - 1 (probabilities Pp) and the softmax of tile t (scores S ->
+// Pn) in an instruction order fixed by sched_barrier: each of the 16 MFMA
+// slots carries a piece of the softmax (row max over slots 0-3, the rescale
+// decision in slot 4, then two or four probabilities per slot). V^T operands
+// are read in batches of four, one batch ahead. O picks up P V of tile t - 1
+// here; a rescale the softmax decides is applied by the caller afterwards,
+// before P V of tile t.
+__device__ __forceinline__ void pv_softmax(const uint4* __restrict__ sv, const u32x4 (&Pp)[2][2],
+                                           FragAddr fa, f32x16 (&oacc)[4], const f32x16 (&S)[2],
+                                           float sc, RowState& rs, u32x4 (&Pn)[2][2]) {
+  asm volatile("" : "+v"(fa.v_sw));
+  bf16x8 fr[16];
+  auto load = [&](int pi) {  // MFMA slot pi: key half jb, step u, head-dim block db
+    const int jb = pi >> 3, u = (pi >> 2) & 1, db = pi & 3;
+    fr[pi] = lds_frag(sv, (((uint32_t)(64 * jb + 32 * u) ^ fa.v_sw) + fa.v_base) + db * (32 * 128));
+  };
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  float m = -INFINITY, mb = 0.f, sum = 0.f;
+  // probabilities of score pair q (0..15): S[jb][r], S[jb][r + 1], r = 2 q % 16
+  auto prob_pair = [&](int qp) {
+    const int idx = 2 * qp, jb = idx >> 4, r = idx & 15, u = r >> 3, w = (r & 7) >> 1;
+    const float x0 = __builtin_amdgcn_exp2f(fmaf(S[jb][r], sc, -mb));
+    const float x1 = __builtin_amdgcn_exp2f(fmaf(S[jb][r + 1], sc, -mb));
+    const bf16x2 pr = {(__bf16)x0, (__bf16)x1};
+    Pn[jb][u][w] = __builtin_bit_cast(unsigned int, pr);
+    sum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, sum, false);  // row sum of the bf16 P V uses
+  };
+#pragma unroll
+  for (int i = 0; i < 4; ++i) load(i);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    if ((i & 3) == 0) {  // batch i / 4 has landed; send the next batch
+      lds_reads_done();
+      if (i + 4 < 16) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) load(i + 4 + j);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    {
+      const int jb = i >> 3, u = (i >> 2) & 1, db = i & 3;
+      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i], __builtin_bit_cast(bf16x8, Pp[jb][u]),
+                                                         oacc[db], 0, 0, 0);
+    }
+    if (i < 4) {  // row max, 8 scores per slot
+      const int jb = i >> 1, r = (i & 1) * 8;
+      m = fmaxf(m, fmaxf(fmaxf(fmaxf(S[jb][r], S[jb][r + 1]), fmaxf(S[jb][r + 2], S[jb][r + 3])),
+                         fmaxf(fmaxf(S[jb][r + 4], S[jb][r + 5]), fmaxf(S[jb][r + 6], S[jb][r + 7]))));
+    } else {
+      if (i == 4) {  // row max over both lane halves, lazy rescale decision
+        m = row_max_halves(m) * sc;
+        const bool grow = __any(m > rs.m_used + kRescaleLog2);
+        const float mn = grow ? fmaxf(rs.m_used, m) : rs.m_used;
+        const float alpha = (rs.m_used == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(rs.m_used - mn);
+        rs.l_part *= alpha;
+        rs.alpha *= alpha;
+        rs.rescale = rs.rescale || grow;
+        rs.m_used = mn;
+        mb = (mn == -INFINITY) ? 0.f : mn;
+        sum = rs.l_part;
+      }
+      // pairs 0..7 two per slot in slots 4..7, pairs 8..15 one per slot in slots 8..15
+      if (i < 8) {
+        prob_pair(2 * (i - 4));
+        prob_pair(2 * (i - 4) + 1);
+      } else {
+        prob_pair(i);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  rs.l_part = sum;
+}
+
+// One pass (far or local) of a wave over tiles [ktb, kte), software-pipelined:
+// iteration t runs P V of tile t - 1 together with the softmax of tile t
+// (pv_softmax), then QK^T of tile t + 1. K tiles are staged two tiles ahead of
+// their QK^T and V^T tiles one tile ahead of their P V, in two-slot rings
+// (slot = (t - ktb) % 2). Tiles from kte_w on hold no causal pair of this
+// wave's rows: there it only stages and takes part in the barriers. vt0
+// points at the sequence's first V^T tile of this KV head.
 template <bool FAR>
 __device__ __forceinline__ void run_pass(const uint16_t* qsrc, const uint16_t* ksrc,
                                          const uint16_t* vt0, int ktb, int kte,
@@ -482,35 +614,62 @@ __device__ __forceinline__ void run_pass(const uint16_t* qsrc, const uint16_t* k
       qf[t] = __builtin_bit_cast(bf16x8, v);
     }
   }
+  // tiles with a causal pair of this wave: c0 <= r0 + 31, none if r0 >= L
+  const int kte_w = wr.r0 >= wr.L ? ktb : min(kte, (wr.r0 + 31) / kKeyTile + 1);
   const StageOffsets so = stage_offsets(wave, lane);
+  const FragAddr fa = frag_addr(li, hl);
   constexpr int kTileElems = kHeadDim * kKeyTile;
+  auto k_tile = [&](int t) { return ksrc + (size_t)t * kTileElems; };
+  auto v_tile = [&](int t) { return vt0 + (size_t)t * kTileElems; };
+  auto kslot = [&](int t) { return sK + ((t - ktb) & 1) * kSlot; };
+  auto vslot = [&](int t) { return sV + ((t - ktb) & 1) * kSlot; };
+
   slot_barrier();  // LDS of a previous pass is no longer read
-  stage_k(sK + (ktb & 1) * kSlot, ksrc + (size_t)ktb * kTileElems, wr.L - ktb * kKeyTile, so, wave);
-  stage_v(sV + (ktb & 1) * kSlot, vt0 + (size_t)ktb * kTileElems, so, wave);
-  for (int t = ktb; t < kte; ++t) {
-    const int c0 = t * kKeyTile;
+  stage_k(kslot(ktb), k_tile(ktb), wr.L - ktb * kKeyTile, so, wave);
+  if (ktb + 1 < kte) stage_k(kslot(ktb + 1), k_tile(ktb + 1), wr.L - (ktb + 1) * kKeyTile, so, wave);
+  wait_vmem_all();
+  slot_barrier();
+  f32x16 S[2];
+  if (ktb < kte_w) qk_tile(kslot(ktb), qf, fa, S);
+
+  // iteration t: S holds the scores of tile t (then receives tile t + 1); Pp
+  // the probabilities of tile t - 1, Pn receives those of tile t
+  auto step = [&](int t, u32x4 (&Pp)[2][2], u32x4 (&Pn)[2][2]) {
     wait_vmem_all();
-    slot_barrier();  // tile t landed for every wave; slot (t + 1) & 1 is free
-    if (t + 1 < kte) {
-      stage_k(sK + ((t + 1) & 1) * kSlot, ksrc + (size_t)(t + 1) * kTileElems,
-              wr.L - c0 - kKeyTile, so, wave);
-      stage_v(sV + ((t + 1) & 1) * kSlot, vt0 + (size_t)(t + 1) * kTileElems, so, wave);
+    slot_barrier();  // K(t + 1), V(t - 1) landed for every wave; K(t) and V(t - 2) are no longer read
+    if (t + 2 < kte) stage_k(kslot(t + 2), k_tile(t + 2), wr.L - (t + 2) * kKeyTile, so, wave);
+    stage_v(vslot(t), v_tile(t), so, wave);
+    const bool sm = t < kte_w, pv = t > ktb && t - 1 < kte_w, qk = t + 1 < kte_w;
+    if (sm) {
+      mask_tile<FAR>(S, wr, t * kKeyTile, li, hl);
+      if (pv) pv_softmax(vslot(t - 1), Pp, fa, oacc, S, sc, rs, Pn);
+      else softmax_tile(S, sc, rs, Pn);
+    } else if (pv) {
+      pv_tile(vslot(t - 1), Pp, fa, oacc);
     }
-    if (wr.r0 >= wr.L || c0 > wr.r0 + 31) continue;  // no causal pair of this wave here
-    f32x16 S[2];
-    bf16x8 P[2][2];
-    qk_tile(sK + (t & 1) * kSlot, qf, li, hl, S);
-    vector_slot<FAR>(S, wr, c0, sc, li, hl, rs, oacc, P);
     apply_rescale(rs, oacc);
-    pv_tile(sV + (t & 1) * kSlot, P, li, hl, oacc);
+    if (qk) qk_tile(kslot(t + 1), qf, fa, S);
+  };
+  u32x4 Pa[2][2], Pb[2][2];
+  for (int t = ktb; t < kte; t += 2) {
+    step(t, Pa, Pb);
+    if (t + 1 < kte) step(t + 1, Pb, Pa);
+  }
+  // P V of the last tile: P(t) sits in Pb when t - ktb is even
+  wait_vmem_all();
+  slot_barrier();
+  const int tl = kte - 1;
+  if (tl < kte_w) {
+    if (((tl - ktb) & 1) == 0) pv_tile(vslot(tl), Pb, fa, oacc);
+    else pv_tile(vslot(tl), Pa, fa, oacc);
   }
 }
 
 template <bool BIFOCAL>
 __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillParams p, SeqTable st) {
   extern __shared__ uint4 smem[];
-  uint4* sK = smem;              // 2 slots
-  uint4* sV = smem + 2 * kSlot;  // 2 slots
+  uint4* sK = smem;                  // kRing slots
+  uint4* sV = smem + kRing * kSlot;  // kRing slots
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar) index
   const int li = lane & 31, hl = lane >> 5;
@@ -802,8 +961,9 @@ hipError_t launch_prefill_main(int dtype, bool bifocal, const PrefillParams& pp,
                                const SeqTable& st, int grid, hipStream_t stream) {
   if (dtype == 0) {
     const int th = 64 * kBf16Waves;
-    if (bifocal) return launch_with_lds(prefill_bf16_kernel<true>, grid, th, 4 * 16384, stream, pp, st);
-    return launch_with_lds(prefill_bf16_kernel<false>, grid, th, 4 * 16384, stream, pp, st);
+    const size_t lds = 2 * kRing * kSlot * sizeof(uint4);
+    if (bifocal) return launch_with_lds(prefill_bf16_kernel<true>, grid, th, lds, stream, pp, st);
+    return launch_with_lds(prefill_bf16_kernel<false>, grid, th, lds, stream, pp, st);
   }
   if (bifocal) return launch_with_lds(prefill_f32_kernel<true>, grid, 256, 3 * 32768, stream, pp, st);
   return launch_with_lds(prefill_f32_kernel<false>, grid, 256, 2 * 32768, stream, pp, st);
