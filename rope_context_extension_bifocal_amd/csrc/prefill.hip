@@ -22,6 +22,8 @@
 // would subtract again is never done.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "bf_common.h"
 
 namespace bf {
@@ -30,6 +32,7 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;  // 8 packed bf16
+typedef __attribute__((ext_vector_type(4))) unsigned int du32x4;
 
 // ----------------------------------------------------------------- helpers
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
@@ -276,19 +279,22 @@ struct FragAddr {
   uint32_t v_base, v_sw;  // V^T tile: head dim li (+ 32 db), chunk (4 jb + 2 u + hl) ^ ((li / 2) % 8)
 };
 
-__device__ __forceinline__ FragAddr frag_addr(int li, int hl) {
+// k_base / v_base are absolute LDS byte addresses of slot 0 of the K / V^T
+// rings; other slots and the second 32-key block are immediate offsets.
+__device__ __forceinline__ FragAddr frag_addr(int li, int hl, const uint4* sK, const uint4* sV) {
   FragAddr fa;
   const int row0 = key_of_mfma_row(li), sk = row0 & 15;
-  fa.k_base = (uint32_t)(row0 * 256 + ((hl ^ sk) & 1) * 16);
+  fa.k_base = (uint32_t)(uintptr_t)sK + (uint32_t)(row0 * 256 + ((hl ^ sk) & 1) * 16);
   fa.k_sw = (uint32_t)((sk & 14) * 16);
   const int sv = (li >> 1) & 7;
-  fa.v_base = (uint32_t)(li * 128 + ((hl ^ sv) & 1) * 16);
+  fa.v_base = (uint32_t)(uintptr_t)sV + (uint32_t)(li * 128 + ((hl ^ sv) & 1) * 16);
   fa.v_sw = (uint32_t)((sv & 6) * 16);
   return fa;
 }
 
-__device__ __forceinline__ bf16x8 lds_frag(const uint4* tile, uint32_t byte_off) {
-  return __builtin_bit_cast(bf16x8, *(const uint4*)((const char*)tile + byte_off));
+__device__ __forceinline__ bf16x8 lds_at(uint32_t addr) {
+  const du32x4 v = *(const __attribute__((address_space(3))) du32x4*)addr;
+  return __builtin_bit_cast(bf16x8, v);
 }
 
 // Waits for all outstanding LDS reads. Written with the builtin (not inline
@@ -302,13 +308,13 @@ __device__ __forceinline__ void lds_reads_done() { __builtin_amdgcn_s_waitcnt(0x
 // QK^T of one tile: S[blk] (keys 32 blk .. 32 blk + 31 x the wave's 32
 // queries). K operands are read in batches of four, one batch ahead of their
 // MFMAs, with one full LDS wait per batch (see lds_reads_done).
-__device__ __forceinline__ void qk_tile(const uint4* __restrict__ sk, const bf16x8 (&q)[8],
-                                        FragAddr fa, f32x16 (&S)[2]) {
+__device__ __forceinline__ void qk_tile(uint32_t slot_off, const bf16x8 (&q)[8], FragAddr fa,
+                                        f32x16 (&S)[2]) {
   asm volatile("" : "+v"(fa.k_sw));
   bf16x8 fr[16];
   auto load = [&](int i) {  // MFMA i: k-step t = i / 2, key block blk = i % 2
     const int t = i >> 1, blk = i & 1;
-    fr[i] = lds_frag(sk, (((uint32_t)(32 * t) ^ fa.k_sw) + fa.k_base) + blk * (32 * 256));
+    fr[i] = lds_at((((uint32_t)(32 * t) ^ fa.k_sw) + fa.k_base) + slot_off + blk * (32 * 256));
   };
   S[0] = f32x16{};
   S[1] = f32x16{};
@@ -352,8 +358,8 @@ __device__ __forceinline__ void mask_tile(f32x16 (&S)[2], const WaveRows& wr, in
     }
 }
 
-__device__ __forceinline__ void pv_tile(const uint4* __restrict__ sv, const u32x4 (&P)[2][2],
-                                        FragAddr fa, f32x16 (&oacc)[4]) {
+__device__ __forceinline__ void pv_tile(uint32_t slot_off, const u32x4 (&P)[2][2], FragAddr fa,
+                                        f32x16 (&oacc)[4]) {
   asm volatile("" : "+v"(fa.v_sw));
   bf16x8 a[4][2][2];
 #pragma unroll
@@ -362,7 +368,7 @@ __device__ __forceinline__ void pv_tile(const uint4* __restrict__ sv, const u32x
     for (int u = 0; u < 2; ++u) {
       const uint32_t off = ((uint32_t)(64 * jb + 32 * u) ^ fa.v_sw) + fa.v_base;
 #pragma unroll
-      for (int db = 0; db < 4; ++db) a[db][jb][u] = lds_frag(sv, off + db * 32 * 128);
+      for (int db = 0; db < 4; ++db) a[db][jb][u] = lds_at(off + slot_off + db * 32 * 128);
     }
 #pragma unroll
   for (int jb = 0; jb < 2; ++jb)
@@ -433,30 +439,46 @@ __device__ __forceinline__ void g2lds(const char* gbase, uint32_t off, uint4* ld
 // ktile: first key of the tile; keys_left (>= 1, wave-uniform): keys of the
 // sequence from that key on. Rows past the sequence end read its last key
 // (finite data; those scores are masked).
-__device__ __forceinline__ void stage_k(uint4* slot, const uint16_t* ktile, int keys_left,
-                                        const StageOffsets& so, int wave) {
-  const char* kb = scalar_ptr(ktile);
-  if (keys_left >= kKeyTile) {
-#pragma unroll
-    for (int i = 0; i < kStageIters; ++i)
-      g2lds(kb + i * kStageStride, so.k, slot + (kBf16Waves * i + wave) * 64);
-  } else {
-#pragma unroll
-    for (int i = 0; i < kStageIters; ++i) {
-      const uint32_t off = so.k + i * kStageStride;
-      const int row = (int)(off >> 8);
-      const int shift = row < keys_left ? 0 : (keys_left - 1 - row) * kHeadDim * 2;
-      g2lds(kb, (uint32_t)((int)off + shift), slot + (kBf16Waves * i + wave) * 64);
-    }
-  }
+// Direct global -> LDS staging of one 64-key tile through a buffer resource
+// whose base is the tile start and whose size runs to the end of the tensor:
+// instruction i of a wave reads 1 KiB at lane offset (fixed per pass) + 4 KiB
+// i. Base and size sit in scalar registers, so a load costs no vector
+// arithmetic. K rows past a sequence end read the next tokens of the packed
+// tensor (finite data; those scores are masked) and reads past the tensor end
+// return zeros (buffer range check). V^T tiles are zero-padded per sequence.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char* tile, const char* end) {
+  const long long left = (long long)(end - tile);
+  const int n = (int)(left < 0x7fffffffLL ? left : 0x7fffffffLL);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)tile, (short)0, n, 0x00020000);
 }
 
-__device__ __forceinline__ void stage_v(uint4* slot, const uint16_t* vtile, const StageOffsets& so,
+__device__ __forceinline__ void b2lds(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                      uint4* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff,
+                                           soff, 0, 0);
+}
+
+struct KStage {
+  uint32_t off[kStageIters];  // lane byte offsets of the K loads inside a tile (range-checked)
+};
+
+__device__ __forceinline__ KStage k_stage_offsets(const StageOffsets& so) {
+  KStage ks;
+#pragma unroll
+  for (int i = 0; i < kStageIters; ++i) ks.off[i] = so.k + i * kStageStride;
+  return ks;
+}
+
+__device__ __forceinline__ void stage_k(uint4* slot, __amdgpu_buffer_rsrc_t r, const KStage& ks,
                                         int wave) {
-  const char* vb = scalar_ptr(vtile);
+#pragma unroll
+  for (int i = 0; i < kStageIters; ++i) b2lds(r, ks.off[i], 0, slot + (kBf16Waves * i + wave) * 64);
+}
+
+__device__ __forceinline__ void stage_v(uint4* slot, __amdgpu_buffer_rsrc_t r, uint32_t so_v, int wave) {
 #pragma unroll
   for (int i = 0; i < kStageIters; ++i)
-    g2lds(vb + i * kStageStride, so.v, slot + (kBf16Waves * i + wave) * 64);
+    b2lds(r, so_v, i * kStageStride, slot + (kBf16Waves * i + wave) * 64);
 }
 
 // Row max over the two lane halves that hold one query row: one cross-half
@@ -478,7 +500,7 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&S)[2], float sc, RowState&
 #pragma unroll
   for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
-    for (int r = 0; r < 16; r += 2) m = fmaxf(m, fmaxf(S[jb][r], S[jb][r + 1]));
+    for (int r = 0; r < 16; r += 2) m = fmaxf(fmaxf(m, S[jb][r]), S[jb][r + 1]);
   m = row_max_halves(m) * sc;
   // a new row max more than 2^8 above the stale one moves the stale max; the
   // factor for the O accumulator is left to the next matrix slot
@@ -520,14 +542,14 @@ constexpr int kRing = 2;  // K and V^T ring slots per workgroup
 // are read in batches of four, one batch ahead. O picks up P V of tile t - 1
 // here; a rescale the softmax decides is applied by the caller afterwards,
 // before P V of tile t.
-__device__ __forceinline__ void pv_softmax(const uint4* __restrict__ sv, const u32x4 (&Pp)[2][2],
+__device__ __forceinline__ void pv_softmax(uint32_t slot_off, const u32x4 (&Pp)[2][2],
                                            FragAddr fa, f32x16 (&oacc)[4], const f32x16 (&S)[2],
                                            float sc, RowState& rs, u32x4 (&Pn)[2][2]) {
   asm volatile("" : "+v"(fa.v_sw));
   bf16x8 fr[16];
   auto load = [&](int pi) {  // MFMA slot pi: key half jb, step u, head-dim block db
     const int jb = pi >> 3, u = (pi >> 2) & 1, db = pi & 3;
-    fr[pi] = lds_frag(sv, (((uint32_t)(64 * jb + 32 * u) ^ fa.v_sw) + fa.v_base) + db * (32 * 128));
+    fr[pi] = lds_at((((uint32_t)(64 * jb + 32 * u) ^ fa.v_sw) + fa.v_base) + slot_off + db * (32 * 128));
   };
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   float m = -INFINITY, mb = 0.f, sum = 0.f;
@@ -558,10 +580,10 @@ __device__ __forceinline__ void pv_softmax(const uint4* __restrict__ sv, const u
       oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i], __builtin_bit_cast(bf16x8, Pp[jb][u]),
                                                          oacc[db], 0, 0, 0);
     }
-    if (i < 4) {  // row max, 8 scores per slot
+    if (i < 4) {  // row max, 8 scores per slot (a chain of 3-input maxima)
       const int jb = i >> 1, r = (i & 1) * 8;
-      m = fmaxf(m, fmaxf(fmaxf(fmaxf(S[jb][r], S[jb][r + 1]), fmaxf(S[jb][r + 2], S[jb][r + 3])),
-                         fmaxf(fmaxf(S[jb][r + 4], S[jb][r + 5]), fmaxf(S[jb][r + 6], S[jb][r + 7]))));
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) m = fmaxf(fmaxf(m, S[jb][r + e]), S[jb][r + e + 1]);
     } else {
       if (i == 4) {  // row max over both lane halves, lazy rescale decision
         m = row_max_halves(m) * sc;
@@ -597,7 +619,8 @@ __device__ __forceinline__ void pv_softmax(const uint4* __restrict__ sv, const u
 // points at the sequence's first V^T tile of this KV head.
 template <bool FAR>
 __device__ __forceinline__ void run_pass(const uint16_t* qsrc, const uint16_t* ksrc,
-                                         const uint16_t* vt0, int ktb, int kte,
+                                         const uint16_t* vt0, const char* kend, const char* vend,
+                                         int ktb, int kte,
                                          const WaveRows& wr, float sc, int wave, int lane,
                                          uint4* sK, uint4* sV, RowState& rs,
                                          f32x16 (&oacc)[4]) {
@@ -617,51 +640,71 @@ __device__ __forceinline__ void run_pass(const uint16_t* qsrc, const uint16_t* k
   // tiles with a causal pair of this wave: c0 <= r0 + 31, none if r0 >= L
   const int kte_w = wr.r0 >= wr.L ? ktb : min(kte, (wr.r0 + 31) / kKeyTile + 1);
   const StageOffsets so = stage_offsets(wave, lane);
-  const FragAddr fa = frag_addr(li, hl);
-  constexpr int kTileElems = kHeadDim * kKeyTile;
-  auto k_tile = [&](int t) { return ksrc + (size_t)t * kTileElems; };
-  auto v_tile = [&](int t) { return vt0 + (size_t)t * kTileElems; };
-  auto kslot = [&](int t) { return sK + ((t - ktb) & 1) * kSlot; };
-  auto vslot = [&](int t) { return sV + ((t - ktb) & 1) * kSlot; };
+  const KStage ks = k_stage_offsets(so);
+  const FragAddr fa = frag_addr(li, hl, sK, sV);
+  constexpr int kTileBytes = kHeadDim * kKeyTile * 2;
+  const char* kb0 = scalar_ptr(ksrc);
+  const char* vb0 = scalar_ptr(vt0);
+  auto stage_k_t = [&](uint4* slot, int t) {
+    const char* tile = kb0 + (size_t)t * kTileBytes;
+    stage_k(slot, tile_rsrc(tile, kend), ks, wave);
+  };
+  auto stage_v_t = [&](uint4* slot, int t) {
+    const char* tile = vb0 + (size_t)t * kTileBytes;
+    stage_v(slot, tile_rsrc(tile, vend), so.v, wave);
+  };
+  uint4* const sK0 = sK;
+  uint4* const sK1 = sK + kSlot;
+  uint4* const sV0 = sV;
+  uint4* const sV1 = sV + kSlot;
 
   slot_barrier();  // LDS of a previous pass is no longer read
-  stage_k(kslot(ktb), k_tile(ktb), wr.L - ktb * kKeyTile, so, wave);
-  if (ktb + 1 < kte) stage_k(kslot(ktb + 1), k_tile(ktb + 1), wr.L - (ktb + 1) * kKeyTile, so, wave);
+  stage_k_t(sK0, ktb);
+  if (ktb + 1 < kte) stage_k_t(sK1, ktb + 1);
   wait_vmem_all();
   slot_barrier();
   f32x16 S[2];
-  if (ktb < kte_w) qk_tile(kslot(ktb), qf, fa, S);
+  constexpr uint32_t kSlotBytes = kSlot * 16;
+  if (ktb < kte_w) qk_tile(0, qf, fa, S);
 
-  // iteration t: S holds the scores of tile t (then receives tile t + 1); Pp
-  // the probabilities of tile t - 1, Pn receives those of tile t
-  auto step = [&](int t, u32x4 (&Pp)[2][2], u32x4 (&Pn)[2][2]) {
+  // iteration t (ring slot parity E = (t - ktb) & 1): S holds the scores of
+  // tile t (then receives tile t + 1); Pp the probabilities of tile t - 1, Pn
+  // receives those of tile t
+  auto step = [&](int t, auto parity, u32x4 (&Pp)[2][2], u32x4 (&Pn)[2][2]) {
+    constexpr int E = decltype(parity)::value;
+    uint4* const k_this = E ? sK1 : sK0;  // K(t), refilled with K(t + 2)
+    uint4* const v_this = E ? sV1 : sV0;  // V(t), staged now
+    constexpr uint32_t k_next = E ? 0 : kSlotBytes;  // K(t + 1), ring offset
+    constexpr uint32_t v_prev = E ? 0 : kSlotBytes;  // V(t - 1), ring offset
     wait_vmem_all();
     slot_barrier();  // K(t + 1), V(t - 1) landed for every wave; K(t) and V(t - 2) are no longer read
-    if (t + 2 < kte) stage_k(kslot(t + 2), k_tile(t + 2), wr.L - (t + 2) * kKeyTile, so, wave);
-    stage_v(vslot(t), v_tile(t), so, wave);
+    if (t + 2 < kte) stage_k_t(k_this, t + 2);
+    stage_v_t(v_this, t);
     const bool sm = t < kte_w, pv = t > ktb && t - 1 < kte_w, qk = t + 1 < kte_w;
     if (sm) {
       mask_tile<FAR>(S, wr, t * kKeyTile, li, hl);
-      if (pv) pv_softmax(vslot(t - 1), Pp, fa, oacc, S, sc, rs, Pn);
+      if (pv) pv_softmax(v_prev, Pp, fa, oacc, S, sc, rs, Pn);
       else softmax_tile(S, sc, rs, Pn);
     } else if (pv) {
-      pv_tile(vslot(t - 1), Pp, fa, oacc);
+      pv_tile(v_prev, Pp, fa, oacc);
     }
     apply_rescale(rs, oacc);
-    if (qk) qk_tile(kslot(t + 1), qf, fa, S);
+    if (qk) qk_tile(k_next, qf, fa, S);
   };
+  using Even = std::integral_constant<int, 0>;
+  using Odd = std::integral_constant<int, 1>;
   u32x4 Pa[2][2], Pb[2][2];
   for (int t = ktb; t < kte; t += 2) {
-    step(t, Pa, Pb);
-    if (t + 1 < kte) step(t + 1, Pb, Pa);
+    step(t, Even{}, Pa, Pb);
+    if (t + 1 < kte) step(t + 1, Odd{}, Pb, Pa);
   }
   // P V of the last tile: P(t) sits in Pb when t - ktb is even
   wait_vmem_all();
   slot_barrier();
   const int tl = kte - 1;
   if (tl < kte_w) {
-    if (((tl - ktb) & 1) == 0) pv_tile(vslot(tl), Pb, fa, oacc);
-    else pv_tile(vslot(tl), Pa, fa, oacc);
+    if (((tl - ktb) & 1) == 0) pv_tile(0, Pb, fa, oacc);
+    else pv_tile(kSlotBytes, Pa, fa, oacc);
   }
 }
 
@@ -682,6 +725,12 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillParams p, S
                         ((size_t)it.kvh * (p.Tpad / kKeyTile) + st.vt_off[it.b] / kKeyTile) *
                             (kHeadDim * kKeyTile);
 
+  // ends of the K, K'' and V^T tensors (range limit of the staging loads)
+  const size_t kv_bytes = (size_t)p.Hkv * p.T * kHeadDim * 2;
+  const char* k_end = (const char*)p.k + kv_bytes;
+  const char* k2_end = (const char*)p.k2 + kv_bytes;
+  const char* vt_end = (const char*)p.vt + (size_t)p.Hkv * p.Tpad * kHeadDim * 2;
+
   RowState rs{-INFINITY, 0.f, 1.f, false};
   f32x16 oacc[4];
 #pragma unroll
@@ -694,13 +743,14 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillParams p, S
     const int kte = min(it.nkt, (int)((Rl - w0) / kKeyTile) + 1);
     run_pass<true>((const uint16_t*)p.q2 + ((size_t)it.hq * p.T + it.tok0) * kHeadDim,
                    (const uint16_t*)p.k2 + ((size_t)it.kvh * p.T + it.tok0) * kHeadDim, vt0,
-                   0, kte, wr, p.scale_log2, wave, lane, sK, sV, rs, oacc);
+                   k2_end, vt_end, 0, kte, wr, p.scale_log2, wave, lane, sK, sV, rs, oacc);
   }
   if (w0 > 0) {  // local pairs exist: keys j > R0 - w0 (and j <= Rl)
     const long long first = R0 - w0 + 1;  // smallest key with a local pair
     const int ktb = first <= 0 ? 0 : (int)(first / kKeyTile);
     if (ktb < it.nkt)
-      run_pass<false>(qg, kg, vt0, ktb, it.nkt, wr, p.scale_log2, wave, lane, sK, sV, rs, oacc);
+      run_pass<false>(qg, kg, vt0, k_end, vt_end, ktb, it.nkt, wr, p.scale_log2, wave, lane, sK, sV,
+                      rs, oacc);
   }
 
   // epilogue: normalise, store O (bf16) and lse
