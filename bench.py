@@ -68,6 +68,55 @@ def traffic_for(kernel_key):
     return ent.get("bytes_per_launch")
 
 
+COPY_BYTES = 256 * 1024 * 1024
+# kernels whose HBM traffic is reported: key -> substring of the kernel name
+TRAFFIC_KERNELS = {"prefill_bf16_kernel_bifocal": "prefill_bf16_kernel<true>",
+                   "decode_split_kernel_bifocal": "decode_split_kernel<true>",
+                   "copy": "copyBuffer"}
+
+
+def _pmc_kib_per_dispatch(run_dir, counter, name_part):
+    """Average value of one counter per dispatch of the kernels whose name
+    contains name_part, over every counter_collection.csv under run_dir."""
+    import csv
+    import glob
+    vals = {}
+    for path in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row.get("Counter_Name") != counter or name_part not in row.get("Kernel_Name", ""):
+                    continue
+                key = row.get("Dispatch_Id") or row.get("Correlation_Id")
+                vals[key] = vals.get(key, 0.0) + float(row["Counter_Value"])
+    if not vals:
+        raise SystemExit(f"no {counter} rows for '{name_part}' under {run_dir}")
+    return sum(vals.values()) / len(vals), len(vals)
+
+
+def write_traffic(root):
+    """profiles/traffic.json from six rocprofv3 --pmc runs under root:
+    {prefill,decode,copy}_{fetch,write}. FETCH_SIZE and WRITE_SIZE are KiB per
+    dispatch; each is scaled by the factor that makes the 256 MiB copy read and
+    write 256 MiB."""
+    kib = COPY_BYTES / 1024.0
+    cf, _ = _pmc_kib_per_dispatch(os.path.join(root, "copy_fetch"), "FETCH_SIZE", TRAFFIC_KERNELS["copy"])
+    cw, _ = _pmc_kib_per_dispatch(os.path.join(root, "copy_write"), "WRITE_SIZE", TRAFFIC_KERNELS["copy"])
+    f_fetch, f_write = kib / cf, kib / cw
+    out = {"source_hash": source_hash(KERNEL_SOURCES), "fetch_factor": round(f_fetch, 4),
+           "write_factor": round(f_write, 4),
+           "copy_calibration_kib": {"fetch": round(cf, 1), "write": round(cw, 1), "true": kib}}
+    for key, leg in (("prefill_bf16_kernel_bifocal", "prefill"), ("decode_split_kernel_bifocal", "decode")):
+        fk, nf = _pmc_kib_per_dispatch(os.path.join(root, f"{leg}_fetch"), "FETCH_SIZE", TRAFFIC_KERNELS[key])
+        wk, nw = _pmc_kib_per_dispatch(os.path.join(root, f"{leg}_write"), "WRITE_SIZE", TRAFFIC_KERNELS[key])
+        out[key] = {"source_hash": out["source_hash"], "fetch_kib": round(fk, 1), "write_kib": round(wk, 1),
+                    "dispatches": [nf, nw],
+                    "bytes_per_launch": round((fk * f_fetch + wk * f_write) * 1024.0)}
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
 def time_calls(fn, n, stream):
     """Average ms of fn() over n calls, hipEvents on the stream the library
     launches on (torch's current stream)."""
@@ -113,9 +162,16 @@ def main():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
-                    help="run only this leg (W warmup + K calls, no JSON line); for profilers")
+    ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
+                    help="run only this leg (W warmup + K calls, no JSON line); for profilers. "
+                         "'copy' is a plain 256 MiB device copy that calibrates the HBM counters")
+    ap.add_argument("--write-traffic", metavar="DIR", default=None,
+                    help="read the rocprofv3 --pmc runs under DIR (see profiles/hbm_traffic.txt) "
+                         "and write profiles/traffic.json; needs no GPU")
     args = ap.parse_args()
+    if args.write_traffic:
+        write_traffic(args.write_traffic)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the per-GPU shard is the single-GPU workload). Run with --gpus 1.",
@@ -123,6 +179,14 @@ def main():
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.only == "copy":  # counter calibration: read 256 MiB, write 256 MiB per call
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup + args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"only copy: {args.warmup} + {args.steps} copies of {COPY_BYTES} bytes done")
+        return
     bfl.lib()
     stream = torch.cuda.current_stream()
 
