@@ -25,7 +25,6 @@ hipError_t launch_prefill_main(int dtype, bool bifocal, const PrefillParams& pp,
                                const SeqTable& st, int grid, hipStream_t stream);
 hipError_t launch_pair_map(long long L, long long w0, long long s, int mode, int8_t* br,
                            long long* dphi_num, long long* s_out, hipStream_t stream);
-int decode_splits(long long N);
 size_t decode_workspace_bytes(int batch, long long max_len, int Hq);
 int run_decode(bool bifocal, const void* q, const void* kc, const void* vc, void* o, float* lse,
                const int32_t* seqlens, int batch, int cap, int Hq, int Hkv, long long w0,

@@ -525,32 +525,47 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p, Dec
 }
 
 // ------------------------------------------------------------------ host side
-// Keys per split: about kDecTargetSplits splits per sequence, 64 to
-// kDecMaxChunk keys each (both overridable at build time for tuning sweeps).
-#ifndef BF_DEC_TARGET_SPLITS
-#define BF_DEC_TARGET_SPLITS 128
+// Split geometry. A launch should hold about kDecTargetWgs split workgroups
+// (two per CU of the 256 CUs: one full round), so a sequence gets
+// kDecTargetWgs / (Hkv x batch) splits, between 8 and 128, of 64 to
+// kDecMaxChunk keys each (the bounds are build-time overridable for tuning).
+#ifndef BF_DEC_TARGET_WGS
+#define BF_DEC_TARGET_WGS 512
 #endif
 #ifndef BF_DEC_MAX_CHUNK
-#define BF_DEC_MAX_CHUNK 1024
+#define BF_DEC_MAX_CHUNK 2048
 #endif
-constexpr long long kDecTargetSplits = BF_DEC_TARGET_SPLITS;
+constexpr long long kDecTargetWgs = BF_DEC_TARGET_WGS;
 constexpr long long kDecMaxChunk = BF_DEC_MAX_CHUNK;
+constexpr long long kDecMinTargetSplits = 8, kDecMaxTargetSplits = 128;
 static_assert(kDecMaxChunk % kDecBlock == 0, "chunk must be a multiple of 64 keys");
 
-static int decode_chunk(long long N) {
-  long long c = (N + kDecTargetSplits - 1) / kDecTargetSplits;
+static long long decode_target_splits(int batch, int Hkv) {
+  const long long per = (long long)batch * Hkv;
+  long long t = (kDecTargetWgs + per - 1) / per;
+  if (t < kDecMinTargetSplits) t = kDecMinTargetSplits;
+  if (t > kDecMaxTargetSplits) t = kDecMaxTargetSplits;
+  return t;
+}
+
+static int decode_chunk(long long N, long long target) {
+  long long c = (N + target - 1) / target;
   c = ((c + kDecBlock - 1) / kDecBlock) * kDecBlock;
   if (c < kDecBlock) c = kDecBlock;
   if (c > kDecMaxChunk) c = kDecMaxChunk;
   return (int)c;
 }
 
-int decode_splits(long long N) { return (int)((N + decode_chunk(N) - 1) / decode_chunk(N)); }
+static int decode_splits(long long N, long long target) {
+  const long long c = decode_chunk(N, target);
+  return (int)((N + c - 1) / c);
+}
 
-// Upper bound of decode_splits over all lengths <= max_len (it is monotone).
+// Upper bound of decode_splits over all lengths <= max_len and every target
+// (splits <= target unless the chunk is capped at kDecMaxChunk).
 static int decode_split_bound(long long max_len) {
   const long long a = (max_len + kDecMaxChunk - 1) / kDecMaxChunk + 1;
-  return (int)(a > kDecTargetSplits + 1 ? a : kDecTargetSplits + 1);
+  return (int)(a > kDecMaxTargetSplits + 1 ? a : kDecMaxTargetSplits + 1);
 }
 
 struct DecodeWs {
@@ -618,6 +633,7 @@ int run_decode(bool bifocal, const void* q, const void* kc, const void* vc, void
   dp.mode = mode;
   for (int b0 = 0; b0 < batch; b0 += kMaxSeqPerLaunch) {
     const int nb = batch - b0 < kMaxSeqPerLaunch ? batch - b0 : kMaxSeqPerLaunch;
+    const long long target = decode_target_splits(nb, Hkv);
     DecodeSeqs ds;
     ds.n = nb;
     int max_split = 0;
@@ -627,8 +643,8 @@ int run_decode(bool bifocal, const void* q, const void* kc, const void* vc, void
       long long s = 1;
       if (bifocal) s = N / w_pre + (N % w_pre != 0 ? 1 : 0);
       ds.s[i] = (int)(s < 1 ? 1 : s);
-      ds.chunk[i] = decode_chunk(N);
-      ds.nsplit[i] = decode_splits(N);
+      ds.chunk[i] = decode_chunk(N, target);
+      ds.nsplit[i] = decode_splits(N, target);
       if (ds.nsplit[i] > max_split) max_split = ds.nsplit[i];
     }
     dp.q = (const uint16_t*)q + (size_t)b0 * Hq * kHeadDim;
