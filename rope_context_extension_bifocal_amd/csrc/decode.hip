@@ -444,30 +444,43 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p, De
   }
 }
 
-// One workgroup per (query head, batch): log-sum-exp merge of the splits.
-// Thread t owns float4 d4 = t % 32 of the head dims for splits t / 32 + 8 k.
-// The partial rows of the first kHold rounds are loaded into registers before
-// the max / weight reductions so that their latency overlaps them.
+// Log-sum-exp merge of the splits. Workgroup = (query head, batch, quarter
+// of the head dims). Every load (the split maxima, row sums and partial rows)
+// is issued up front, so the merge costs one memory round trip: thread t
+// owns float4 d4 = t % 8 of the quarter for splits t / 8 + 32 k, and the
+// split maxima / sums of splits t + 256 k.
 constexpr int kDecMaxSplits = 1088;
-constexpr int kCombHold = 17;  // 8 x 17 = 136 splits held in registers
+constexpr int kCombGroups = 32;  // split groups per workgroup
+constexpr int kCombHold = 5;     // 32 x 5 = 160 splits held in registers
+static_assert(5 * 256 >= kDecMaxSplits, "split maxima are read five per thread");
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p, DecodeSeqs ds) {
   __shared__ float wgt[kDecMaxSplits];
   __shared__ float red[8];
-  __shared__ float4 part4[8][32];
-  const int b = blockIdx.y, h = blockIdx.x, t = threadIdx.x;
+  __shared__ float4 part4[kCombGroups][8];
+  const int b = blockIdx.y, h = blockIdx.x, dq = blockIdx.z, t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
   const int ns = ds.nsplit[b];
   const size_t row0 = ((size_t)b * p.Hq + h) * p.S;
-  const int d4 = t & 31, grp = t >> 5;
+  const int d4 = t & 7, grp = t >> 3;
+  const int dcol = 32 * dq + 4 * d4;  // first head dim of this thread's float4
   float4 hold[kCombHold];
 #pragma unroll
   for (int k = 0; k < kCombHold; ++k) {
-    const int i = grp + 8 * k;
-    const float4 v = *(const float4*)(p.part_acc + (row0 + min(i, ns - 1)) * kHeadDim + 4 * d4);
+    const int i = grp + kCombGroups * k;
+    const float4 v = *(const float4*)(p.part_acc + (row0 + min(i, ns - 1)) * kHeadDim + dcol);
     hold[k] = i < ns ? v : make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  float mloc = -INFINITY;
-  for (int i = t; i < ns; i += 256) mloc = fmaxf(mloc, p.part_m[row0 + i]);
+  // split maxima and row sums of splits t, t + 256, ... (at most kDecMaxSplits)
+  float mi[5], li[5];
+#pragma unroll
+  for (int k = 0; k < 5; ++k) {
+    const int i = t + 256 * k;
+    const int ic = min(i, ns - 1);
+    const float m = p.part_m[row0 + ic], l = p.part_l[row0 + ic];
+    mi[k] = i < ns ? m : -INFINITY;
+    li[k] = i < ns ? l : 0.f;
+  }
+  float mloc = fmaxf(fmaxf(fmaxf(mi[0], mi[1]), fmaxf(mi[2], mi[3])), mi[4]);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, o));
   if (lane == 0) red[wave] = mloc;
@@ -475,10 +488,12 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p, Dec
   const float mt = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const float mbt = (mt == -INFINITY) ? 0.f : mt;
   float lloc = 0.f;
-  for (int i = t; i < ns; i += 256) {
-    const float w = __builtin_amdgcn_exp2f(p.part_m[row0 + i] - mbt);
-    wgt[i] = w;
-    lloc += w * p.part_l[row0 + i];
+#pragma unroll
+  for (int k = 0; k < 5; ++k) {
+    const int i = t + 256 * k;
+    const float w = __builtin_amdgcn_exp2f(mi[k] - mbt);  // 0 for absent splits
+    if (i < ns) wgt[i] = w;
+    lloc += w * li[k];
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) lloc += __shfl_xor(lloc, o);
@@ -488,15 +503,15 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p, Dec
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
   for (int k = 0; k < kCombHold; ++k) {
-    const int i = grp + 8 * k;
+    const int i = grp + kCombGroups * k;
     const float w = i < ns ? wgt[min(i, ns - 1)] : 0.f;
     acc.x += w * hold[k].x;
     acc.y += w * hold[k].y;
     acc.z += w * hold[k].z;
     acc.w += w * hold[k].w;
   }
-  for (int i = grp + 8 * kCombHold; i < ns; i += 8) {
-    const float4 v = *(const float4*)(p.part_acc + (row0 + i) * kHeadDim + 4 * d4);
+  for (int i = grp + kCombGroups * kCombHold; i < ns; i += kCombGroups) {
+    const float4 v = *(const float4*)(p.part_acc + (row0 + i) * kHeadDim + dcol);
     const float w = wgt[i];
     acc.x += w * v.x;
     acc.y += w * v.y;
@@ -505,22 +520,22 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p, Dec
   }
   part4[grp][d4] = acc;
   __syncthreads();
-  if (t < 32) {
+  if (t < 8) {
     float4 a = part4[0][t];
-#pragma unroll
-    for (int g = 1; g < 8; ++g) {
+    for (int g = 1; g < kCombGroups; ++g) {
       a.x += part4[g][t].x;
       a.y += part4[g][t].y;
       a.z += part4[g][t].z;
       a.w += part4[g][t].w;
     }
     const float inv = 1.f / lt;
-    uint16_t* o = p.o + ((size_t)b * p.Hq + h) * kHeadDim + 4 * t;
+    uint16_t* o = p.o + ((size_t)b * p.Hq + h) * kHeadDim + 32 * dq + 4 * t;
     uint2 w;
     w.x = (uint32_t)df2bf(a.x * inv) | ((uint32_t)df2bf(a.y * inv) << 16);
     w.y = (uint32_t)df2bf(a.z * inv) | ((uint32_t)df2bf(a.w * inv) << 16);
     *(uint2*)o = w;
-    if (p.lse && t == 0) p.lse[(size_t)b * p.Hq + h] = (mt + __log2f(lt)) * 0.69314718055994530942f;
+    if (p.lse && t == 0 && dq == 0)
+      p.lse[(size_t)b * p.Hq + h] = (mt + __log2f(lt)) * 0.69314718055994530942f;
   }
 }
 
@@ -665,7 +680,7 @@ int run_decode(bool bifocal, const void* q, const void* kc, const void* vc, void
       hipLaunchKernelGGL(decode_split_kernel<false>, grid, dim3(256), 0, stream, dp, ds, tt);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return bad(BF_ERR_HIP, std::string("decode split launch: ") + hipGetErrorString(e));
-    hipLaunchKernelGGL(decode_combine_kernel, dim3(Hq, nb), dim3(256), 0, stream, dp, ds);
+    hipLaunchKernelGGL(decode_combine_kernel, dim3(Hq, nb, kHeadDim / 32), dim3(256), 0, stream, dp, ds);
     e = hipGetLastError();
     if (e != hipSuccess) return bad(BF_ERR_HIP, std::string("decode combine launch: ") + hipGetErrorString(e));
   }
