@@ -36,10 +36,10 @@ from rope_context_extension_bifocal_amd import workloads as wl  # noqa: E402
 METRIC = "bifocal prefill TFLOP/s + % MFMA peak @128K Qwen3-8B layer; decode GB/s"
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
-KERNEL_SOURCES = ["rope_context_extension_bifocal_amd/csrc/prefill.hip",
-                  "rope_context_extension_bifocal_amd/csrc/decode.hip",
-                  "rope_context_extension_bifocal_amd/csrc/capi.cpp",
-                  "rope_context_extension_bifocal_amd/csrc/bf_common.h"]
+_CSRC = "rope_context_extension_bifocal_amd/csrc/"
+# sources each measured kernel is built from: its counters go stale when one changes
+KERNEL_SOURCES = {"prefill_bf16_kernel_bifocal": [_CSRC + "prefill.hip", _CSRC + "capi.cpp", _CSRC + "bf_common.h"],
+                  "decode_split_kernel_bifocal": [_CSRC + "decode.hip", _CSRC + "capi.cpp", _CSRC + "bf_common.h"]}
 
 
 def log(msg):
@@ -63,7 +63,7 @@ def traffic_for(kernel_key):
     with open(path) as f:
         data = json.load(f)
     ent = data.get(kernel_key)
-    if not ent or ent.get("source_hash") != source_hash(KERNEL_SOURCES):
+    if not ent or ent.get("source_hash") != source_hash(KERNEL_SOURCES[kernel_key]):
         return None
     return ent.get("bytes_per_launch")
 
@@ -102,13 +102,13 @@ def write_traffic(root):
     cf, _ = _pmc_kib_per_dispatch(os.path.join(root, "copy_fetch"), "FETCH_SIZE", TRAFFIC_KERNELS["copy"])
     cw, _ = _pmc_kib_per_dispatch(os.path.join(root, "copy_write"), "WRITE_SIZE", TRAFFIC_KERNELS["copy"])
     f_fetch, f_write = kib / cf, kib / cw
-    out = {"source_hash": source_hash(KERNEL_SOURCES), "fetch_factor": round(f_fetch, 4),
+    out = {"fetch_factor": round(f_fetch, 4),
            "write_factor": round(f_write, 4),
            "copy_calibration_kib": {"fetch": round(cf, 1), "write": round(cw, 1), "true": kib}}
     for key, leg in (("prefill_bf16_kernel_bifocal", "prefill"), ("decode_split_kernel_bifocal", "decode")):
         fk, nf = _pmc_kib_per_dispatch(os.path.join(root, f"{leg}_fetch"), "FETCH_SIZE", TRAFFIC_KERNELS[key])
         wk, nw = _pmc_kib_per_dispatch(os.path.join(root, f"{leg}_write"), "WRITE_SIZE", TRAFFIC_KERNELS[key])
-        out[key] = {"source_hash": out["source_hash"], "fetch_kib": round(fk, 1), "write_kib": round(wk, 1),
+        out[key] = {"source_hash": source_hash(KERNEL_SOURCES[key]), "fetch_kib": round(fk, 1), "write_kib": round(wk, 1),
                     "dispatches": [nf, nw],
                     "bytes_per_launch": round((fk * f_fetch + wk * f_write) * 1024.0)}
     path = os.path.join(ROOT, "profiles", "traffic.json")
