@@ -39,7 +39,8 @@ PEAK_HBM_GBS = 8000.0
 _CSRC = "rope_context_extension_bifocal_amd/csrc/"
 # sources each measured kernel is built from: its counters go stale when one changes
 KERNEL_SOURCES = {"prefill_bf16_kernel_bifocal": [_CSRC + "prefill.hip", _CSRC + "capi.cpp", _CSRC + "bf_common.h"],
-                  "decode_split_kernel_bifocal": [_CSRC + "decode.hip", _CSRC + "capi.cpp", _CSRC + "bf_common.h"]}
+                  "decode_split_kernel_bifocal": [_CSRC + "decode.hip", _CSRC + "capi.cpp", _CSRC + "bf_common.h"],
+                  "rope_kernel": [_CSRC + "rope.hip", _CSRC + "capi.cpp", _CSRC + "bf_common.h"]}
 
 
 def log(msg):
@@ -72,6 +73,7 @@ COPY_BYTES = 256 * 1024 * 1024
 # kernels whose HBM traffic is reported: key -> substring of the kernel name
 TRAFFIC_KERNELS = {"prefill_bf16_kernel_bifocal": "prefill_bf16_kernel<true>",
                    "decode_split_kernel_bifocal": "decode_split_kernel<true>",
+                   "rope_kernel": "rope_kernel",
                    "copy": "copyBuffer"}
 
 
@@ -94,8 +96,8 @@ def _pmc_kib_per_dispatch(run_dir, counter, name_part):
 
 
 def write_traffic(root):
-    """profiles/traffic.json from six rocprofv3 --pmc runs under root:
-    {prefill,decode,copy}_{fetch,write}. FETCH_SIZE and WRITE_SIZE are KiB per
+    """profiles/traffic.json from the rocprofv3 --pmc runs under root:
+    {copy,prefill,decode,rope}_{fetch,write}. FETCH_SIZE and WRITE_SIZE are KiB per
     dispatch; each is scaled by the factor that makes the 256 MiB copy read and
     write 256 MiB."""
     kib = COPY_BYTES / 1024.0
@@ -105,7 +107,11 @@ def write_traffic(root):
     out = {"fetch_factor": round(f_fetch, 4),
            "write_factor": round(f_write, 4),
            "copy_calibration_kib": {"fetch": round(cf, 1), "write": round(cw, 1), "true": kib}}
-    for key, leg in (("prefill_bf16_kernel_bifocal", "prefill"), ("decode_split_kernel_bifocal", "decode")):
+    for key, leg in (("prefill_bf16_kernel_bifocal", "prefill"), ("decode_split_kernel_bifocal", "decode"),
+                     ("rope_kernel", "rope")):
+        if not os.path.isdir(os.path.join(root, f"{leg}_fetch")):
+            log(f"no {leg}_fetch run under {root}: {key} left out")
+            continue
         fk, nf = _pmc_kib_per_dispatch(os.path.join(root, f"{leg}_fetch"), "FETCH_SIZE", TRAFFIC_KERNELS[key])
         wk, nw = _pmc_kib_per_dispatch(os.path.join(root, f"{leg}_write"), "WRITE_SIZE", TRAFFIC_KERNELS[key])
         out[key] = {"source_hash": source_hash(KERNEL_SOURCES[key]), "fetch_kib": round(fk, 1), "write_kib": round(wk, 1),
@@ -162,7 +168,7 @@ def main():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "copy", "rope"], default=None,
                     help="run only this leg (W warmup + K calls, no JSON line); for profilers. "
                          "'copy' is a plain 256 MiB device copy that calibrates the HBM counters")
     ap.add_argument("--write-traffic", metavar="DIR", default=None,
@@ -225,6 +231,21 @@ def main():
     flops = 4.0 * D * Hq * L * (L + 1) / 2
     kv_bytes = 2.0 * N * Hkv * D * 2
 
+    # raw-input pre-step at the prefill shape: original RoPE of raw q, k in
+    # place (on copies), and the same with the cache fill of k' and v
+    qr, kr = None, None
+
+    def rope_pre(cache=None):
+        bfl.rope_prefill(qr, kr, cu, cfg["theta"], q_out=qr, k_out=kr,
+                         **({} if cache is None else dict(v=vd, k_cache=cache[0], v_cache=cache[1])))
+
+    if args.only == "rope":
+        qr, kr = qd.clone(), kd.clone()
+        for _ in range(args.warmup + args.steps):
+            rope_pre()
+        torch.cuda.synchronize()
+        log(f"only rope: {args.warmup} + {args.steps} calls done")
+        return
     if args.only is not None:  # profiling mode: one leg only
         fn = prefill if args.only == "prefill" else decode
         for _ in range(args.warmup + args.steps):
@@ -283,6 +304,35 @@ def main():
         small[str(n)] = {"bifocal_us": round(t_b * 1e3, 2), "plain_us": round(t_p * 1e3, 2),
                          "bifocal_gbs": round(2.0 * n * Hkv * D * 2 / (t_b * 1e-3) / 1e9, 1)}
 
+    log("raw-input pre-step")
+    qr, kr = qd.clone(), kd.clone()
+    rope_pre()
+    rope_ms = time_calls(rope_pre, 10, stream)
+    kcache = torch.empty((1, Hkv, L, D), dtype=torch.bfloat16, device="cuda")
+    vcache = torch.empty_like(kcache)
+    rope_pre((kcache, vcache))
+    rope_c_ms = time_calls(lambda: rope_pre((kcache, vcache)), 10, stream)
+    del kcache, vcache
+    q1, k1, v1 = qdc.clone(), torch.randn(1, Hkv, D, device="cuda").to(torch.bfloat16), \
+        torch.randn(1, Hkv, D, device="cuda").to(torch.bfloat16)
+    kc_app, vc_app = kc.clone(), vc.clone()
+    app = lambda: bfl.rope_append(q1, k1, v1, kc_app, vc_app, [N], dcfg["theta"], q_out=q1)
+    for _ in range(10):
+        app()
+    app_ms = time_calls(app, 100, stream)
+    # the same bytes moved by a plain device copy (read q, k; write copies):
+    # the ceiling of a read-plus-write stream on this part
+    qcp, kcp = torch.empty_like(qr), torch.empty_like(kr)
+    cp = lambda: (qcp.copy_(qr), kcp.copy_(kr))
+    cp()
+    copy_ms = time_calls(cp, 10, stream)
+    del q1, kc_app, vc_app, qr, kr, qcp, kcp
+    # algorithmic bytes: read raw q, k and write q', k'; the cache fill adds
+    # k' to the cache and the copy of v (read + write)
+    rope_bytes = 2.0 * (Hq + Hkv) * L * D * 2
+    rope_c_bytes = rope_bytes + 3.0 * Hkv * L * D * 2
+    rope_gbs = rope_bytes / (rope_ms * 1e-3) / 1e9
+
     tflops = flops / (pre_ms * 1e-3) / 1e12
     gbs = kv_bytes / (dec_ms * 1e-3) / 1e9
     result = {
@@ -316,6 +366,12 @@ def main():
         "plain_decode_us": round(plain_dec_ms * 1e3, 2),
         "decode_overhead_vs_plain": round(dec_many_ms / plain_dec_ms - 1, 4),
         "decode_small": small,
+        "rope_prefill_ms": round(rope_ms, 4),
+        "rope_prefill_gbs": round(rope_gbs, 1),
+        "rope_prefill_cache_ms": round(rope_c_ms, 4),
+        "rope_prefill_cache_gbs": round(rope_c_bytes / (rope_c_ms * 1e-3) / 1e9, 1),
+        "rope_append_us": round(app_ms * 1e3, 2),
+        "copy_same_bytes_gbs": round(rope_bytes / (copy_ms * 1e-3) / 1e9, 1),
         "roofline": {"kernel": "bifocal_prefill call (correction prep + V^T + MFMA tile loop)",
                      "bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
@@ -324,6 +380,10 @@ def main():
                             "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                             "frac": round(gbs / PEAK_HBM_GBS, 4),
                             "traffic": traffic_for("decode_split_kernel_bifocal")},
+        "roofline_rope": {"kernel": "bifocal_rope_prefill (raw-input pre-step, in place)",
+                          "bound": "hbm", "achieved": round(rope_gbs, 1), "peak": PEAK_HBM_GBS,
+                          "unit": "GB/s", "frac": round(rope_gbs / PEAK_HBM_GBS, 4),
+                          "traffic": traffic_for("rope_kernel")},
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a row sample")

@@ -142,6 +142,49 @@ int plain_attention_ref_gpu(int32_t phase, const void* q, const void* k, const v
                             void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Raw-input pre-step for prefill: the model's ORIGINAL RoPE applied to raw
+ * (position-free) q and k, giving the q', k' that bifocal_prefill takes, and
+ * optionally the KV-cache fill for a following bifocal_decode.
+ *   q_raw, q_out : [n_heads_q,  T, head_dim]  dtype (bf16 or fp32)
+ *   k_raw, k_out : [n_heads_kv, T, head_dim]  same dtype; k_out may be NULL
+ *                  when k_cache is given
+ *   cu_seqlens_host : as bifocal_prefill; token t of sequence b is rotated
+ *                  at position t - cu[b]
+ *   k_cache, v_cache, v : if k_cache is not NULL, k' and v of sequence b are
+ *                  also written to k_cache / v_cache [batch, n_heads_kv,
+ *                  cache_capacity, head_dim] at positions 0 .. L_b - 1
+ *                  (L_b <= cache_capacity); v is [n_heads_kv, T, head_dim].
+ * q_out may be q_raw and k_out may be k_raw (in place); no other buffers may
+ * overlap. theta_m = rope_theta^(-2m/D), half-split pairs (m, m + D/2); the
+ * angle is formed in fp64, the rotation in fp32. No workspace.
+ * [mufans.github.io wiki, Jet-Long Dynamic RoPE, "关键实现 / 推理流程": the
+ *  flow starts by computing RoPE for the input tokens; ai-feeds.com summary,
+ *  "关键模块" item 3: cached keys carry original RoPE]
+ */
+int bifocal_rope_prefill(const void* q_raw, const void* k_raw, const void* v, void* q_out,
+                         void* k_out, void* k_cache, void* v_cache, int32_t cache_capacity,
+                         const int32_t* cu_seqlens_host, int32_t batch, int32_t n_heads_q,
+                         int32_t n_heads_kv, int32_t head_dim, int32_t dtype, double rope_theta,
+                         void* stream);
+
+/*
+ * Raw-input pre-step for one decode step: the new token of sequence b sits at
+ * position p_b = seqlens_host[b] - 1.
+ *   q_raw, q_out : [batch, n_heads_q, head_dim]; q_out = R(p_b theta) q_raw
+ *                  (may be q_raw: in place)
+ *   k_raw, v_new : [batch, n_heads_kv, head_dim]; R(p_b theta) k_raw and
+ *                  v_new are written to k_cache / v_cache [batch, n_heads_kv,
+ *                  cache_capacity, head_dim] at position p_b
+ *   1 <= seqlens_host[b] <= cache_capacity.
+ * bifocal_decode with the same seqlens then runs the step. Same rotation and
+ * references as bifocal_rope_prefill. No workspace.
+ */
+int bifocal_rope_append(const void* q_raw, const void* k_raw, const void* v_new, void* q_out,
+                        void* k_cache, void* v_cache, const int32_t* seqlens_host, int32_t batch,
+                        int32_t cache_capacity, int32_t n_heads_q, int32_t n_heads_kv,
+                        int32_t head_dim, int32_t dtype, double rope_theta, void* stream);
+
+/*
  * Test hook: runs the kernels' own device-side pair classification and
  * position map for one sequence of length L (L <= 4096).
  *   branch_out : device int8 [L * L], row-major (i, j): 0 masked (j > i),

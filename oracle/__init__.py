@@ -30,6 +30,8 @@ def _load():
         lib.oracle_phi.argtypes = [i64, i64, i32]
         lib.oracle_rope_rotate.restype = None
         lib.oracle_rope_rotate.argtypes = [p, p, i64, f64, f64]
+        lib.oracle_rope_rows.restype = ctypes.c_int
+        lib.oracle_rope_rows.argtypes = [p, p, i64, i64, i64, p, f64]
         lib.oracle_pair_branch.restype = i32
         lib.oracle_pair_branch.argtypes = [i64, i64, i64]
         lib.oracle_prefill_rows.restype = ctypes.c_int
@@ -71,6 +73,26 @@ def rope_rotate(x, pos, theta):
     y = np.empty_like(x)
     _load().oracle_rope_rotate(_ptr(x), _ptr(y), x.shape[-1], float(pos), float(theta))
     return y
+
+
+def rope_rows(x, positions, theta):
+    """Original RoPE of raw rows: x [H,T,D] (row (h, t) a token at
+    positions[t]) -> fp64 [H,T,D] rotated by positions[t] * theta_m."""
+    x = _f32(x)
+    H, T, D = x.shape
+    pos = np.ascontiguousarray(np.asarray(positions, dtype=np.int64))
+    assert pos.shape == (T,)
+    y = np.empty((H, T, D), dtype=np.float64)
+    rc = _load().oracle_rope_rows(_ptr(x), _ptr(y), H, T, D, _ptr(pos), float(theta))
+    if rc != 0:
+        raise ValueError(f"oracle_rope_rows failed: {rc}")
+    return y
+
+
+def packed_positions(cu_seqlens):
+    """Sequence-relative position of every packed token (restarts per sequence)."""
+    cu = [int(c) for c in cu_seqlens]
+    return np.concatenate([np.arange(cu[b + 1] - cu[b], dtype=np.int64) for b in range(len(cu) - 1)])
 
 
 def prefill(q, k, v, cu_seqlens, w0, w_pre, theta, mode, scale, rows=None, variant=0,

@@ -369,3 +369,24 @@ int32_t oracle_pair_branch(int64_t i, int64_t j, int64_t w0)
     if (j > i) return 0;
     return (i - j < w0) ? 1 : 2;
 }
+
+/* Original RoPE of packed rows (the raw-input pre-step): row (h, t) of
+ * x [H][T][D] is the raw vector of a token at position pos[t], and y gets
+ * the model's own rotation of it, R(pos[t] * theta) x, in fp64.
+ * [mufans.github.io wiki, Jet-Long Dynamic RoPE, "关键实现 / 推理流程":
+ *  the flow starts by computing RoPE for the input tokens]               */
+int oracle_rope_rows(const float* x, double* y, int64_t H, int64_t T, int64_t D,
+                     const int64_t* pos, double theta_base)
+{
+    if (H < 1 || T < 1 || D < 2 || (D & 1)) return ORC_BAD;
+    double* row = (double*)malloc(sizeof(double) * (size_t)D);
+    if (!row) return ORC_NOMEM;
+    for (int64_t h = 0; h < H; ++h)
+        for (int64_t t = 0; t < T; ++t) {
+            const float* xr = x + (h * T + t) * D;
+            for (int64_t d = 0; d < D; ++d) row[d] = (double)xr[d];
+            oracle_rope_rotate(row, y + (h * T + t) * D, D, (double)pos[t], theta_base);
+        }
+    free(row);
+    return ORC_OK;
+}

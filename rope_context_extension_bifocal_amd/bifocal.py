@@ -23,7 +23,8 @@ LONG_MODES = {"fi": BF_LONG_FI, "pa": BF_LONG_PA}
 _DTYPES = {torch.bfloat16: BF_DTYPE_BF16, torch.float32: BF_DTYPE_FP32}
 
 EXPORTED = ("bifocal_s_of_L", "bifocal_workspace_bytes", "bifocal_prefill", "bifocal_decode",
-            "plain_attention_ref_gpu", "bifocal_test_pair_map", "bifocal_last_error")
+            "plain_attention_ref_gpu", "bifocal_rope_prefill", "bifocal_rope_append",
+            "bifocal_test_pair_map", "bifocal_last_error")
 
 _lib = None
 
@@ -57,6 +58,12 @@ def lib():
         L.plain_attention_ref_gpu.restype = ctypes.c_int
         L.plain_attention_ref_gpu.argtypes = [i32, p, p, p, p, p, p, i32, i32, i32, i32, i32,
                                               i32, f32, p, sz, p]
+        L.bifocal_rope_prefill.restype = ctypes.c_int
+        L.bifocal_rope_prefill.argtypes = [p, p, p, p, p, p, p, i32, p, i32, i32, i32, i32, i32,
+                                           f64, p]
+        L.bifocal_rope_append.restype = ctypes.c_int
+        L.bifocal_rope_append.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, f64,
+                                          p]
         L.bifocal_test_pair_map.restype = ctypes.c_int
         L.bifocal_test_pair_map.argtypes = [i64, i64, i64, i32, p, p, p, p]
         L.bifocal_last_error.restype = ctypes.c_char_p
@@ -182,6 +189,40 @@ def plain_decode(q, k_cache, v_cache, seqlens, softmax_scale=None, return_lse=Fa
                                          _DTYPES[q.dtype], _scale(softmax_scale, D),
                                          _ptr(workspace), workspace.numel(), _stream(stream)))
     return (o, lse) if return_lse else o
+
+
+def rope_prefill(q_raw, k_raw, cu_seqlens, rope_theta, v=None, k_cache=None, v_cache=None,
+                 q_out=None, k_out=None, write_k=True, stream=None):
+    """Original RoPE on raw packed q [Hq,T,D] and k [Hkv,T,D] at sequence-relative
+    positions. With k_cache / v_cache [B,Hkv,cap,D] (and v [Hkv,T,D]) the rotated
+    keys and the values are also written to the cache. Returns (q', k') (k' is
+    None when write_k is False and a cache is given)."""
+    Hq, T, D = q_raw.shape
+    Hkv = k_raw.shape[0]
+    B = len(cu_seqlens) - 1
+    qo = q_out if q_out is not None else torch.empty_like(q_raw)
+    ko = k_out if k_out is not None else (torch.empty_like(k_raw) if write_k or k_cache is None
+                                          else None)
+    cap = k_cache.shape[2] if k_cache is not None else 0
+    cu = _i32_array(cu_seqlens)
+    _check(lib().bifocal_rope_prefill(_ptr(q_raw), _ptr(k_raw), _ptr(v), _ptr(qo), _ptr(ko),
+                                      _ptr(k_cache), _ptr(v_cache), cap, cu, B, Hq, Hkv, D,
+                                      _DTYPES[q_raw.dtype], float(rope_theta), _stream(stream)))
+    return qo, ko
+
+
+def rope_append(q_raw, k_raw, v_new, k_cache, v_cache, seqlens, rope_theta, q_out=None,
+                stream=None):
+    """One decode step's raw q [B,Hq,D] and new k, v [B,Hkv,D]: q' at position
+    seqlens[b] - 1 is returned, k' and v go to the caches at that position."""
+    B, Hq, D = q_raw.shape
+    Hkv, cap = k_cache.shape[1], k_cache.shape[2]
+    qo = q_out if q_out is not None else torch.empty_like(q_raw)
+    sl = _i32_array(seqlens)
+    _check(lib().bifocal_rope_append(_ptr(q_raw), _ptr(k_raw), _ptr(v_new), _ptr(qo),
+                                     _ptr(k_cache), _ptr(v_cache), sl, B, cap, Hq, Hkv, D,
+                                     _DTYPES[q_raw.dtype], float(rope_theta), _stream(stream)))
+    return qo
 
 
 def test_pair_map(L, w0, w_pre, long_mode="fi", device="cuda"):

@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 PKG = os.path.dirname(HERE)
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libbifocal.so")
-SOURCES = ["capi.cpp", "prefill.hip", "decode.hip"]
+SOURCES = ["capi.cpp", "prefill.hip", "decode.hip", "rope.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 

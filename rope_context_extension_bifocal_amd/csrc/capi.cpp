@@ -1,6 +1,6 @@
 // libbifocal C-ABI: argument validation, the s(L) schedule, per-launch
 // sequence tables, workspace carving and kernel launches. Host code only; the
-// kernels live in prefill.hip and decode.hip.
+// kernels live in prefill.hip, decode.hip and rope.hip.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -30,6 +30,12 @@ int run_decode(bool bifocal, const void* q, const void* kc, const void* vc, void
                const int32_t* seqlens, int batch, int cap, int Hq, int Hkv, long long w0,
                long long w_pre, double theta, int mode, float scale, void* ws, size_t ws_bytes,
                hipStream_t stream, std::string& err);
+int run_rope_prefill(const void* q, const void* k, const void* v, void* q_out, void* k_out,
+                     void* k_cache, void* v_cache, int cap, const int32_t* cu, int batch, int Hq,
+                     int Hkv, int dtype, double theta, hipStream_t stream, std::string& err);
+int run_rope_append(const void* q, const void* k, const void* v, void* q_out, void* k_cache,
+                    void* v_cache, int cap, const int32_t* seqlens, int batch, int Hq, int Hkv,
+                    int dtype, double theta, hipStream_t stream, std::string& err);
 }  // namespace bf
 
 namespace {
@@ -309,6 +315,65 @@ int bifocal_test_pair_map(int64_t L, int64_t w0, int64_t w_pre, int32_t long_mod
   hipError_t e = bf::launch_pair_map(L, w0, s, long_mode, branch_out, (long long*)phi_num_out,
                                      (long long*)s_out, (hipStream_t)stream);
   if (e != hipSuccess) return fail(BF_ERR_HIP, "pair_map launch: %s", hipGetErrorString(e));
+  g_err.clear();
+  return BF_OK;
+}
+
+int bifocal_rope_prefill(const void* q_raw, const void* k_raw, const void* v, void* q_out,
+                         void* k_out, void* k_cache, void* v_cache, int32_t cache_capacity,
+                         const int32_t* cu, int32_t batch, int32_t n_heads_q, int32_t n_heads_kv,
+                         int32_t head_dim, int32_t dtype, double rope_theta, void* stream) {
+  int rc = check_common(n_heads_q, n_heads_kv, head_dim, dtype);
+  if (rc) return rc;
+  if (!q_raw || !k_raw || !q_out || !cu) return fail(BF_ERR_INVALID_ARG, "null tensor or cu_seqlens pointer");
+  if (!k_out && !k_cache) return fail(BF_ERR_INVALID_ARG, "k_out and k_cache are both NULL");
+  if (k_cache && (!v_cache || !v)) return fail(BF_ERR_INVALID_ARG, "k_cache given without v_cache and v");
+  if (!(rope_theta > 1.0) || !std::isfinite(rope_theta))
+    return fail(BF_ERR_INVALID_ARG, "rope_theta must be finite and > 1");
+  if (batch < 1) return fail(BF_ERR_INVALID_ARG, "batch must be >= 1 (got %d)", batch);
+  if (cu[0] != 0) return fail(BF_ERR_INVALID_ARG, "cu_seqlens[0] must be 0 (got %d)", cu[0]);
+  int max_len = 0;
+  for (int b = 0; b < batch; ++b) {
+    if (cu[b + 1] <= cu[b])
+      return fail(BF_ERR_INVALID_ARG, "cu_seqlens must be strictly increasing (b=%d: %d -> %d)", b, cu[b], cu[b + 1]);
+    max_len = std::max(max_len, cu[b + 1] - cu[b]);
+  }
+  if (k_cache && max_len > cache_capacity)
+    return fail(BF_ERR_INVALID_ARG, "a sequence (%d tokens) exceeds cache_capacity %d", max_len, cache_capacity);
+  if (!aligned16(q_raw) || !aligned16(k_raw) || !aligned16(q_out) || (k_out && !aligned16(k_out)) ||
+      (k_cache && (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(v))))
+    return fail(BF_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+  if (forced_launch_failure()) return fail(BF_ERR_HIP, "launch failure forced by BIFOCAL_TEST_FAIL_LAUNCH");
+  std::string err;
+  rc = bf::run_rope_prefill(q_raw, k_raw, v, q_out, k_out, k_cache, v_cache, cache_capacity, cu, batch,
+                            n_heads_q, n_heads_kv, dtype, rope_theta, (hipStream_t)stream, err);
+  if (rc) return fail(rc, "%s", err.c_str());
+  g_err.clear();
+  return BF_OK;
+}
+
+int bifocal_rope_append(const void* q_raw, const void* k_raw, const void* v_new, void* q_out,
+                        void* k_cache, void* v_cache, const int32_t* seqlens, int32_t batch,
+                        int32_t cache_capacity, int32_t n_heads_q, int32_t n_heads_kv,
+                        int32_t head_dim, int32_t dtype, double rope_theta, void* stream) {
+  int rc = check_common(n_heads_q, n_heads_kv, head_dim, dtype);
+  if (rc) return rc;
+  if (!q_raw || !k_raw || !v_new || !q_out || !k_cache || !v_cache || !seqlens)
+    return fail(BF_ERR_INVALID_ARG, "null tensor or seqlens pointer");
+  if (!(rope_theta > 1.0) || !std::isfinite(rope_theta))
+    return fail(BF_ERR_INVALID_ARG, "rope_theta must be finite and > 1");
+  if (batch < 1 || cache_capacity < 1) return fail(BF_ERR_INVALID_ARG, "batch and cache_capacity must be >= 1");
+  for (int b = 0; b < batch; ++b)
+    if (seqlens[b] < 1 || seqlens[b] > cache_capacity)
+      return fail(BF_ERR_INVALID_ARG, "seqlens[%d] = %d out of [1, cache_capacity]", b, seqlens[b]);
+  if (!aligned16(q_raw) || !aligned16(k_raw) || !aligned16(v_new) || !aligned16(q_out) ||
+      !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(BF_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+  if (forced_launch_failure()) return fail(BF_ERR_HIP, "launch failure forced by BIFOCAL_TEST_FAIL_LAUNCH");
+  std::string err;
+  rc = bf::run_rope_append(q_raw, k_raw, v_new, q_out, k_cache, v_cache, cache_capacity, seqlens, batch,
+                           n_heads_q, n_heads_kv, dtype, rope_theta, (hipStream_t)stream, err);
+  if (rc) return fail(rc, "%s", err.c_str());
   g_err.clear();
   return BF_OK;
 }

@@ -132,3 +132,51 @@ def test_pair_map_validation(L):
     assert L.bifocal_test_pair_map(5000, 4, 8, 0, P, P, P, None) == -1
     assert L.bifocal_test_pair_map(64, -1, 8, 0, P, P, P, None) == -1
     assert L.bifocal_test_pair_map(64, 4, 8, 0, None, P, P, None) == -1
+
+
+def _rope_prefill(L, **kw):
+    a = dict(q=P, k=P, v=None, qo=P, ko=P, kc=None, vc=None, cap=0, cu=[0, 100, 150], Hq=4, Hkv=2,
+             D=128, dtype=0, theta=1e6, stream=None)
+    a.update(kw)
+    cu = (ctypes.c_int32 * len(a["cu"]))(*a["cu"])
+    return L.bifocal_rope_prefill(a["q"], a["k"], a["v"], a["qo"], a["ko"], a["kc"], a["vc"],
+                                  a["cap"], cu, len(a["cu"]) - 1, a["Hq"], a["Hkv"], a["D"],
+                                  a["dtype"], a["theta"], a["stream"])
+
+
+def _rope_append(L, **kw):
+    a = dict(q=P, k=P, v=P, qo=P, kc=P, vc=P, sl=[100, 7], cap=128, Hq=4, Hkv=2, D=128, dtype=0,
+             theta=1e6, stream=None)
+    a.update(kw)
+    sl = (ctypes.c_int32 * len(a["sl"]))(*a["sl"])
+    return L.bifocal_rope_append(a["q"], a["k"], a["v"], a["qo"], a["kc"], a["vc"], sl,
+                                 len(a["sl"]), a["cap"], a["Hq"], a["Hkv"], a["D"], a["dtype"],
+                                 a["theta"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(qo=None), -1), (dict(ko=None), -1),            # no k output at all
+    (dict(ko=None, kc=P), -1),                                              # cache without v_cache / v
+    (dict(kc=P, vc=P, v=P, cap=60), -1),                                    # sequence longer than the cache
+    (dict(theta=0.5), -1), (dict(theta=float("inf")), -1), (dict(cu=[0, 100, 100]), -1),
+    (dict(cu=[2, 100]), -1), (dict(D=64), -2), (dict(dtype=3), -1), (dict(Hq=3), -1),
+    (dict(k=ctypes.c_void_p(0x100008)), -1),
+])
+def test_rope_prefill_validation(L, kw, code):
+    assert _rope_prefill(L, **kw) == code
+    assert len(L.bifocal_last_error()) > 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kc=None), -1), (dict(v=None), -1), (dict(sl=[0, 5]), -1), (dict(sl=[129]), -1),
+    (dict(cap=0), -1), (dict(theta=1.0), -1), (dict(D=256), -2), (dict(Hq=5), -1),
+])
+def test_rope_append_validation(L, kw, code):
+    assert _rope_append(L, **kw) == code
+
+
+def test_rope_valid_arguments_reach_the_launch(L, monkeypatch):
+    monkeypatch.setenv("BIFOCAL_TEST_FAIL_LAUNCH", "1")
+    assert _rope_prefill(L) == bfl.BF_ERR_HIP
+    assert _rope_prefill(L, ko=None, kc=P, vc=P, v=P, cap=100, dtype=1) == bfl.BF_ERR_HIP
+    assert _rope_append(L) == bfl.BF_ERR_HIP

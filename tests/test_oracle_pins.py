@@ -13,6 +13,7 @@ import pytest
 import torch
 
 import oracle
+from oracle import brute
 from oracle.brute import brute_prefill
 from rope_context_extension_bifocal_amd import workloads
 
@@ -304,3 +305,62 @@ def test_decode_is_last_prefill_row(mode):
                             rows=[N - 1])
     np.testing.assert_array_equal(od[0], op[:, 0])
     np.testing.assert_array_equal(ld[0], lp[:, 0])
+
+
+# ---------------------------------------------------------------- raw-input RoPE (pre-step)
+def test_rope_rows_match_library_llama_rope():
+    # the library's half-split RoPE (transformers' Llama rotary embedding and
+    # apply_rotary_pos_emb, fp32 on the CPU) at moderate positions: a wrong
+    # pairing, sign or frequency exponent would differ by O(1)
+    torch_ = pytest.importorskip("torch")
+    tr = pytest.importorskip("transformers")
+    from transformers.models.llama import modeling_llama as ml
+
+    H, T, D = 3, 48, 128
+    x = np.random.default_rng(31).standard_normal((H, T, D)).astype(np.float32)
+    pos = np.arange(T, dtype=np.int64) * 41 + 7
+    cfg = tr.LlamaConfig(hidden_size=D * H, num_attention_heads=H, num_key_value_heads=H, head_dim=D,
+                         rope_theta=1e6, max_position_embeddings=4096)
+    rope = ml.LlamaRotaryEmbedding(config=cfg)
+    xt = torch_.from_numpy(x)[None]  # [1, H, T, D]
+    cos, sin = rope(xt, torch_.from_numpy(pos)[None])
+    lib_q, _ = ml.apply_rotary_pos_emb(xt, xt, cos, sin)
+    ref = lib_q[0].double().numpy()
+    got = oracle.rope_rows(x, pos, 1e6)
+    # fp32 angles at positions <= 2000 carry ~1e-4 rad of error
+    assert np.abs(got - ref).max() < 2e-3 * np.abs(x).max()
+
+
+def test_rope_rows_match_brute_2x2():
+    # the independent numpy route with explicit 2x2 matrices, at large positions
+    x = np.random.default_rng(32).standard_normal((2, 4, 128)).astype(np.float32)
+    pos = np.array([0, 4095, 98305, 131072], dtype=np.int64)
+    got = oracle.rope_rows(x, pos, 1e6)
+    for h in range(2):
+        for t in range(4):
+            ref = brute._rotate(x[h, t].astype(np.float64), float(pos[t]), 1e6)
+            np.testing.assert_allclose(got[h, t], ref, atol=1e-9)
+
+
+def test_rope_rows_relative_position():
+    # the defining RoPE property: <R(i) q, R(j) k> depends on i - j only
+    rng = np.random.default_rng(33)
+    q = rng.standard_normal((1, 1, 128)).astype(np.float32)
+    k = rng.standard_normal((1, 1, 128)).astype(np.float32)
+    dots = []
+    for i in [5, 1005, 131071]:
+        rq = oracle.rope_rows(q, [i], 1e6)[0, 0]
+        rk = oracle.rope_rows(k, [i - 3], 1e6)[0, 0]
+        dots.append(float(rq @ rk))
+    np.testing.assert_allclose(dots, dots[0], rtol=1e-9)
+
+
+def test_packed_positions_restart_per_sequence():
+    cu = [0, 5, 6, 9]
+    np.testing.assert_array_equal(oracle.packed_positions(cu), [0, 1, 2, 3, 4, 0, 0, 1, 2])
+    x = np.random.default_rng(34).standard_normal((2, 9, 128)).astype(np.float32)
+    packed = oracle.rope_rows(x, oracle.packed_positions(cu), 1e4)
+    for b in range(3):
+        sl = slice(cu[b], cu[b + 1])
+        alone = oracle.rope_rows(x[:, sl], np.arange(cu[b + 1] - cu[b]), 1e4)
+        np.testing.assert_array_equal(packed[:, sl], alone)
