@@ -273,7 +273,8 @@ def main():
         e2.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    pre_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
+    pre_list = [a.elapsed_time(b) for a, b, _ in ev]
+    pre_ms = float(np.mean(pre_list))
     dec_ms = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
     log(f"timed: prefill {pre_ms:.3f} ms, decode {dec_ms * 1e3:.1f} us, wall {wall:.3f} s")
 
@@ -288,6 +289,27 @@ def main():
     for _ in range(10):
         plain_decode()
     plain_dec_ms = time_calls(plain_decode, 50, stream)
+    def cold_us(qx, kx, vx, n, ws_x, copies, calls=200):
+        """Decode over `copies` distinct cache copies in turn (together more
+        than twice the 256 MB MALL), so no call finds its cache resident."""
+        kcs = [kx] + [kx.clone() for _ in range(copies - 1)]
+        vcs = [vx] + [vx.clone() for _ in range(copies - 1)]
+        it = [0]
+
+        def fn():
+            i = it[0] % copies
+            it[0] += 1
+            bfl.decode(qx, kcs[i], vcs[i], [n], dcfg["w0"], dcfg["w_pre"], dcfg["theta"], "fi",
+                       scale, workspace=ws_x)
+
+        for _ in range(20):
+            fn()
+        t = time_calls(fn, calls, stream)
+        del kcs, vcs
+        return t * 1e3
+
+    MALL = 256 * 1024 * 1024
+    dec_cold_us = cold_us(qdc, kc, vc, N, ws_d, max(2, math.ceil(2 * MALL / kv_bytes)))
     small = {}
     for Lc in dcfg["cache_lens"][:2]:
         n = Lc + 1
@@ -301,8 +323,29 @@ def main():
             pfn()
         t_b = time_calls(fn, 100, stream)
         t_p = time_calls(pfn, 100, stream)
+        nbytes = 2.0 * n * Hkv * D * 2
+        t_c = cold_us(qs, ks, vs, n, ws_s, max(2, math.ceil(2 * MALL / nbytes))) * 1e-3
         small[str(n)] = {"bifocal_us": round(t_b * 1e3, 2), "plain_us": round(t_p * 1e3, 2),
-                         "bifocal_gbs": round(2.0 * n * Hkv * D * 2 / (t_b * 1e-3) / 1e9, 1)}
+                         "bifocal_gbs": round(nbytes / (t_b * 1e-3) / 1e9, 1),
+                         "bifocal_cold_us": round(t_c * 1e3, 2),
+                         "bifocal_cold_gbs": round(nbytes / (t_c * 1e-3) / 1e9, 1)}
+        del qs, ks, vs
+
+    log("ragged 8-sequence prefill")
+    rcfg = wl.CONFIGS["qwen3_4b_ragged_prefill"]
+    rlens = wl.ragged_lengths(rcfg["n_seqs"], rcfg["len_lo"], rcfg["len_hi"], rcfg["seed"])
+    rcu = wl.cu_seqlens(rlens)
+    rq, rk, rv = (x.cuda() for x in wl.prefill_inputs(rcfg["Hq"], rcfg["Hkv"], rcu[-1], D, "bf16",
+                                                      rcfg["seed"]))
+    ro = torch.empty_like(rq)
+    rws = bfl.alloc_workspace(bfl.workspace_bytes(bfl.BF_PHASE_PREFILL, len(rlens), rcu[-1],
+                                                  rcfg["Hq"], rcfg["Hkv"]), "cuda")
+    rfn = lambda: bfl.prefill(rq, rk, rv, rcu, rcfg["w0"], rcfg["w_pre"], rcfg["theta"], "fi",
+                              scale, out=ro, workspace=rws)
+    rfn()
+    ragged_ms = time_calls(rfn, 3, stream)
+    ragged_flops = 4.0 * D * rcfg["Hq"] * sum(x * (x + 1) / 2 for x in rlens)
+    del rq, rk, rv, ro, rws
 
     log("raw-input pre-step")
     qr, kr = qd.clone(), kd.clone()
@@ -354,6 +397,8 @@ def main():
                    "s_prefill": bfl.s_of_L(L, cfg["w_pre"]), "decode_keys": N,
                    "s_decode": bfl.s_of_L(N, dcfg["w_pre"]), "long_mode": "fi"},
         "prefill_ms": round(pre_ms, 3),
+        "prefill_ms_median": round(float(np.median(pre_list)), 3),
+        "prefill_ms_min": round(float(np.min(pre_list)), 3),
         "prefill_frac_mfma_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
         "prefill_pa_tflops": round(flops / (pa_ms * 1e-3) / 1e12, 2),
         "plain_prefill_tflops": round(flops / (plain_ms * 1e-3) / 1e12, 2),
@@ -363,9 +408,13 @@ def main():
         "decode_gbs": round(gbs, 1),
         "decode_frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
         "decode_us_50_calls": round(dec_many_ms * 1e3, 2),
+        "decode_cold_us": round(dec_cold_us, 2),
+        "decode_cold_gbs": round(kv_bytes / (dec_cold_us * 1e-6) / 1e9, 1),
         "plain_decode_us": round(plain_dec_ms * 1e3, 2),
         "decode_overhead_vs_plain": round(dec_many_ms / plain_dec_ms - 1, 4),
         "decode_small": small,
+        "ragged_prefill": {"lengths": rlens, "ms": round(ragged_ms, 3),
+                           "tflops": round(ragged_flops / (ragged_ms * 1e-3) / 1e12, 2)},
         "rope_prefill_ms": round(rope_ms, 4),
         "rope_prefill_gbs": round(rope_gbs, 1),
         "rope_prefill_cache_ms": round(rope_c_ms, 4),
