@@ -331,6 +331,18 @@ def main():
                          "bifocal_cold_gbs": round(nbytes / (t_c * 1e-3) / 1e9, 1)}
         del qs, ks, vs
 
+    log("band-only (sliding-window) prefill and decode")
+    band_fn = lambda: prefill("band")
+    band_fn()
+    band_ms = time_calls(band_fn, 5, stream)
+    w0b = cfg["w0"]
+    band_flops = 4.0 * D * Hq * (w0b * (w0b + 1) / 2 + (L - w0b) * w0b)  # pairs with i - j < w0
+    band_dec = lambda: decode("band")
+    for _ in range(10):
+        band_dec()
+    band_dec_ms = time_calls(band_dec, 100, stream)
+    band_dec_bytes = 2.0 * min(N, dcfg["w0"]) * Hkv * D * 2
+
     log("ragged 8-sequence prefill")
     rcfg = wl.CONFIGS["qwen3_4b_ragged_prefill"]
     rlens = wl.ragged_lengths(rcfg["n_seqs"], rcfg["len_lo"], rcfg["len_hi"], rcfg["seed"])
@@ -413,6 +425,10 @@ def main():
         "plain_decode_us": round(plain_dec_ms * 1e3, 2),
         "decode_overhead_vs_plain": round(dec_many_ms / plain_dec_ms - 1, 4),
         "decode_small": small,
+        "band_only": {"prefill_ms": round(band_ms, 3),
+                      "prefill_tflops": round(band_flops / (band_ms * 1e-3) / 1e12, 2),
+                      "decode_us": round(band_dec_ms * 1e3, 2),
+                      "decode_gbs": round(band_dec_bytes / (band_dec_ms * 1e-3) / 1e9, 1)},
         "ragged_prefill": {"lengths": rlens, "ms": round(ragged_ms, 3),
                            "tflops": round(ragged_flops / (ragged_ms * 1e-3) / 1e12, 2)},
         "rope_prefill_ms": round(rope_ms, 4),

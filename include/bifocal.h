@@ -61,6 +61,9 @@ extern "C" {
 /* long-branch position map phi(p) */
 #define BF_LONG_FI 0 /* frequency interpolation: phi(p) = p / s */
 #define BF_LONG_PA 1 /* position aliasing:       phi(p) = floor(p / s) */
+#define BF_LONG_NONE 2 /* band only: far pairs are dropped, i.e. sliding-window attention
+                          over the w0 most recent keys with original RoPE (w0 >= 1; w_pre
+                          unused), the sliding-window layers of a hybrid model */
 
 /* phases for the workspace query and the plain reference */
 #define BF_PHASE_PREFILL 0
@@ -94,11 +97,15 @@ size_t bifocal_workspace_bytes(int32_t phase, int32_t batch, int64_t tokens, int
  *          positions restart at 0 and it gets its own s(L_b).
  *   w0 >= 0 local window (w0 = 0: every pair far; w0 >= L: plain RoPE),
  *   w_pre >= 1 pretrained window, rope_theta > 1 RoPE base,
- *   long_mode BF_LONG_FI or BF_LONG_PA, softmax_scale > 0 (both branches).
+ *   long_mode BF_LONG_FI or BF_LONG_PA, or BF_LONG_NONE for the band-only
+ *   special case (needs w0 >= 1), softmax_scale > 0 (both branches).
  * Query head h reads KV head h / (n_heads_q / n_heads_kv).
  * [ai-feeds.com summary, "方法": inputs are L and the pretrained RoPE
  *  configuration, the output is the attention output of the sequence;
- *  "关键发现": the two long-branch strategies]
+ *  "关键发现": the two long-branch strategies; band only: ai-feeds.com
+ *  summary, "核心洞察" third bullet, and seventnews.com (FR), "Généralisation
+ *  aux architectures d'attention hybrides": sliding-window and global
+ *  attention layers coexist in hybrid models]
  */
 int bifocal_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
                     const int32_t* cu_seqlens_host, int32_t batch, int32_t n_heads_q,
@@ -116,7 +123,8 @@ int bifocal_prefill(const void* q, const void* k, const void* v, void* o, float*
  *                      the number of valid keys INCLUDING the new token's
  *                      own (already appended); the query sits at position
  *                      N_b - 1 and s = s(N_b).
- * Result equals the last row of bifocal_prefill over the same N_b tokens.
+ * Result equals the last row of bifocal_prefill over the same N_b tokens;
+ * long_mode BF_LONG_NONE reads only the keys N_b - w0 .. N_b - 1.
  * [promo script, voice-over: single-batch generation; ai-feeds.com summary,
  *  "关键模块" item 3: the correction rotation applied to cached keys]
  */

@@ -52,7 +52,7 @@ def _ptr(a):
     return a.ctypes.data_as(ctypes.c_void_p)
 
 
-MODES = {"fi": 0, "pa": 1}
+MODES = {"fi": 0, "pa": 1, "band": 2}  # band: far pairs dropped (sliding window w0)
 
 
 def s_of_L(L, w_pre):

@@ -113,17 +113,25 @@ static int64_t seq_of_token(const int64_t* cu, int64_t B, int64_t t)
 /* ------------------------------------------------------------------ */
 /* One query row: the direct piecewise definition with an exact two-pass
  * softmax.  kv_orig / kv_far point at position 0 of this sequence for the
- * query's KV head; qo / qf are the original and far query vectors.       */
+ * query's KV head; qo / qf are the original and far query vectors.
+ * band_only drops the far pairs altogether (mode 2: the band-only special
+ * case, sliding-window attention over the w0 most recent keys with original
+ * RoPE, as in the sliding-window layers of a hybrid model) [ai-feeds.com
+ * summary, "关键模块" item 1: the w0 window keeps original RoPE; "核心洞察",
+ * third bullet, and seventnews.com (FR), "Généralisation aux architectures
+ * d'attention hybrides": hybrid designs where sliding-window and global
+ * attention layers coexist].                                             */
 static void one_row(const double* qo, const double* qf,
                     const double* k_orig, const double* k_far, const double* v,
-                    int64_t i, int64_t D, int64_t w0, double scale,
+                    int64_t i, int64_t D, int64_t w0, double scale, int band_only,
                     double* score_buf, double* o_out, double* lse_out)
 {
     double M = -INFINITY;
     for (int64_t j = 0; j <= i; ++j) {
         double sc;
-        if (i - j < w0) sc = scale * dot(qo, k_orig + j * D, D);   /* local */
-        else            sc = scale * dot(qf, k_far + j * D, D);    /* far   */
+        if (i - j < w0)     sc = scale * dot(qo, k_orig + j * D, D);   /* local   */
+        else if (band_only) sc = -INFINITY;                           /* dropped */
+        else                sc = scale * dot(qf, k_far + j * D, D);    /* far     */
         score_buf[j] = sc;
         if (sc > M) M = sc;
     }
@@ -190,6 +198,7 @@ static void one_row_inclexcl(const double* qo, const double* qf,
  *   k, v   [Hkv][T][D]      packed keys / values, T = cu[B]
  *   cu     [B+1]            sequence offsets; positions restart per sequence
  *   o      [Hq][n_rows][D], lse [Hq][n_rows]  (natural log)
+ *   mode 0 = FI, 1 = PA, 2 = band only (far pairs dropped).
  *   variant 0 = direct definition, 1 = inclusion-exclusion partials.
  * Returns 0, or a negative code for bad arguments / no memory.           */
 int oracle_prefill_rows(const float* q_rows, const float* k, const float* v,
@@ -199,7 +208,8 @@ int oracle_prefill_rows(const float* q_rows, const float* k, const float* v,
                         double* o, double* lse)
 {
     if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || D < 2 || D % 2 != 0 || D > 1024) return ORC_BAD;
-    if (w0 < 0 || w_pre < 1 || (mode != 0 && mode != 1)) return ORC_BAD;
+    if (w0 < 0 || w_pre < 1 || mode < 0 || mode > 2 || (mode == 2 && w0 < 1)) return ORC_BAD;
+    if (variant == 1 && mode == 2) return ORC_BAD;  /* no scaled branch to subtract */
     for (int64_t b = 0; b < B; ++b)
         if (cu[b + 1] <= cu[b]) return ORC_BAD;
     const int64_t T = cu[B];
@@ -283,7 +293,8 @@ int oracle_prefill_rows(const float* q_rows, const float* k, const float* v,
                         one_row_inclexcl(qo, qf, ko + kb, kf + kb, vv + kb, i, D, w0, scale,
                                          s1, s2, num, orow, lrow);
                     else
-                        one_row(qo, qf, ko + kb, kf + kb, vv + kb, i, D, w0, scale, s1, orow, lrow);
+                        one_row(qo, qf, ko + kb, kf + kb, vv + kb, i, D, w0, scale, mode == 2, s1,
+                                orow, lrow);
                 }
             free(buf);
         }
@@ -305,7 +316,7 @@ int oracle_decode(const float* q, const float* k_cache, const float* v_cache,
                   double scale, double* o, double* lse)
 {
     if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || D < 2 || D % 2 != 0 || D > 1024) return ORC_BAD;
-    if (w0 < 0 || w_pre < 1 || (mode != 0 && mode != 1)) return ORC_BAD;
+    if (w0 < 0 || w_pre < 1 || mode < 0 || mode > 2 || (mode == 2 && w0 < 1)) return ORC_BAD;
     int64_t maxN = 0;
     for (int64_t b = 0; b < B; ++b) {
         if (seqlens[b] < 1 || seqlens[b] > cap) return ORC_BAD;
@@ -348,7 +359,7 @@ int oracle_decode(const float* q, const float* k_cache, const float* v_cache,
                     for (int64_t d = 0; d < D; ++d) qo[d] = (double)qs[d];
                     far_vector(qo, qf, D, N - 1, s, mode, theta_base, tmp);
                     size_t kb = (size_t)hk * (size_t)N * (size_t)D;
-                    one_row(qo, qf, ko + kb, kf + kb, vv + kb, N - 1, D, w0, scale, sb,
+                    one_row(qo, qf, ko + kb, kf + kb, vv + kb, N - 1, D, w0, scale, mode == 2, sb,
                             o + ((size_t)b * (size_t)Hq + (size_t)h) * (size_t)D,
                             lse + (size_t)b * (size_t)Hq + (size_t)h);
                 }

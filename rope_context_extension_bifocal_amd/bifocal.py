@@ -17,9 +17,9 @@ LIB_PATH = os.path.join(_PKG, "libbifocal.so")
 
 BF_OK, BF_ERR_INVALID_ARG, BF_ERR_UNSUPPORTED, BF_ERR_WORKSPACE, BF_ERR_HIP = 0, -1, -2, -3, -4
 BF_DTYPE_BF16, BF_DTYPE_FP32 = 0, 1
-BF_LONG_FI, BF_LONG_PA = 0, 1
+BF_LONG_FI, BF_LONG_PA, BF_LONG_NONE = 0, 1, 2
 BF_PHASE_PREFILL, BF_PHASE_DECODE = 0, 1
-LONG_MODES = {"fi": BF_LONG_FI, "pa": BF_LONG_PA}
+LONG_MODES = {"fi": BF_LONG_FI, "pa": BF_LONG_PA, "band": BF_LONG_NONE}  # band: far pairs dropped
 _DTYPES = {torch.bfloat16: BF_DTYPE_BF16, torch.float32: BF_DTYPE_FP32}
 
 EXPORTED = ("bifocal_s_of_L", "bifocal_workspace_bytes", "bifocal_prefill", "bifocal_decode",

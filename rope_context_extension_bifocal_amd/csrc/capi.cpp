@@ -29,7 +29,7 @@ size_t decode_workspace_bytes(int batch, long long max_len, int Hq);
 int run_decode(bool bifocal, const void* q, const void* kc, const void* vc, void* o, float* lse,
                const int32_t* seqlens, int batch, int cap, int Hq, int Hkv, long long w0,
                long long w_pre, double theta, int mode, float scale, void* ws, size_t ws_bytes,
-               hipStream_t stream, std::string& err);
+               hipStream_t stream, std::string& err, long long window = 0);
 int run_rope_prefill(const void* q, const void* k, const void* v, void* q_out, void* k_out,
                      void* k_cache, void* v_cache, int cap, const int32_t* cu, int batch, int Hq,
                      int Hkv, int dtype, double theta, hipStream_t stream, std::string& err);
@@ -119,8 +119,10 @@ int check_bifocal_knobs(long long w0, long long w_pre, double theta, int mode) {
   if (w_pre < 1) return fail(BF_ERR_INVALID_ARG, "w_pre must be >= 1 (got %lld)", w_pre);
   if (!(theta > 1.0) || !std::isfinite(theta))
     return fail(BF_ERR_INVALID_ARG, "rope_theta must be finite and > 1");
-  if (mode != BF_LONG_FI && mode != BF_LONG_PA)
-    return fail(BF_ERR_INVALID_ARG, "long_mode must be BF_LONG_FI or BF_LONG_PA (got %d)", mode);
+  if (mode != BF_LONG_FI && mode != BF_LONG_PA && mode != BF_LONG_NONE)
+    return fail(BF_ERR_INVALID_ARG, "long_mode must be BF_LONG_FI, BF_LONG_PA or BF_LONG_NONE (got %d)", mode);
+  if (mode == BF_LONG_NONE && w0 < 1)
+    return fail(BF_ERR_INVALID_ARG, "band-only attention (BF_LONG_NONE) needs w0 >= 1");
   return BF_OK;
 }
 
@@ -153,7 +155,8 @@ int run_prefill(bool bifocal, const void* q, const void* k, const void* v, void*
   const PrefillWs wl = prefill_ws_layout(batch, T, Hq, Hkv, dtype);
   if (!ws) return fail(BF_ERR_WORKSPACE, "workspace is null");
   if ((uintptr_t)ws & 255u) return fail(BF_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-  const size_t need = bifocal ? wl.total : wl.q2_off;
+  const bool band_only = bifocal && mode == BF_LONG_NONE;
+  const size_t need = bifocal && !band_only ? wl.total : wl.q2_off;
   if (ws_bytes < need)
     return fail(BF_ERR_WORKSPACE, "workspace too small: %zu bytes given, %zu needed", ws_bytes, need);
 
@@ -183,10 +186,11 @@ int run_prefill(bool bifocal, const void* q, const void* k, const void* v, void*
     }
     for (int i = 0; i < nb; ++i) {
       const long long L = cu[b0 + i + 1] - cu[b0 + i];
-      const long long s = bifocal ? bifocal_s_of_L(L, w_pre) : 1;
+      const long long s = bifocal && !band_only ? bifocal_s_of_L(L, w_pre) : 1;
       if (s > (1LL << 30)) return fail(BF_ERR_INVALID_ARG, "s(L) too large");
       st.s[i] = (int)s;
-      if (s > 1 && w0 < L) any_far = true;
+      // far pairs to score (bifocal) or to drop (band only)
+      if ((s > 1 || band_only) && w0 < L) any_far = true;
       st.nrb[i] = (int)((L + geo.P_wg - 1) / geo.P_wg);
       total_items += st.nrb[i];
       max_nrb = std::max(max_nrb, st.nrb[i]);
@@ -195,7 +199,7 @@ int run_prefill(bool bifocal, const void* q, const void* k, const void* v, void*
     bf::VtParams vp{v, wsb + wl.vt_off, (int)T, Tpad, Hkv};
     e = bf::launch_vt_transpose(dtype, vp, st, stream);
     if (e != hipSuccess) return fail(BF_ERR_HIP, "vt_transpose launch: %s", hipGetErrorString(e));
-    if (bifocal && any_far) {
+    if (bifocal && any_far && !band_only) {
       bf::PrepParams pp{q, k, wsb + wl.q2_off, wsb + wl.k2_off, (int)T, Hq, Hkv, mode};
       e = bf::launch_correction_prep(dtype, pp, st, tt, stream);
       if (e != hipSuccess) return fail(BF_ERR_HIP, "correction_prep launch: %s", hipGetErrorString(e));
@@ -209,6 +213,7 @@ int run_prefill(bool bifocal, const void* q, const void* k, const void* v, void*
     pp.o = o;
     pp.lse = lse;
     pp.w0 = w0;
+    pp.band_only = band_only ? 1 : 0;
     pp.scale_log2 = scale * 1.4426950408889634f;
     pp.T = (int)T;
     pp.Tpad = Tpad;
@@ -224,7 +229,7 @@ int run_prefill(bool bifocal, const void* q, const void* k, const void* v, void*
     if (grid > 0x7fffffffLL) return fail(BF_ERR_INVALID_ARG, "launch grid too large");
     if (trace_on())
       fprintf(stderr, "[bifocal] prefill %s dtype=%d seqs=%d..%d grid=%lld P_wg=%d hpw=%d n_hsub=%d s0=%d w0=%lld\n",
-              bifocal ? "bifocal" : "plain", dtype, b0, b0 + nb - 1, grid, geo.P_wg, geo.hpw,
+              band_only ? "band-only" : bifocal ? "bifocal" : "plain", dtype, b0, b0 + nb - 1, grid, geo.P_wg, geo.hpw,
               geo.n_hsub, st.s[0], w0);
     e = bf::launch_prefill_main(dtype, bifocal && any_far, pp, st, (int)grid, stream);
     if (e != hipSuccess) return fail(BF_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
@@ -273,9 +278,11 @@ int bifocal_decode(const void* q, const void* k_cache, const void* v_cache, void
   if ((rc = check_bifocal_knobs(w0, w_pre, rope_theta, long_mode))) return rc;
   if (dtype != BF_DTYPE_BF16) return fail(BF_ERR_UNSUPPORTED, "decode supports bf16 only");
   std::string err;
-  rc = bf::run_decode(true, q, k_cache, v_cache, o, lse, seqlens_host, batch, cache_capacity,
+  // band only: the plain engine over the keys N - w0 .. N - 1 of each sequence
+  const bool band_only = long_mode == BF_LONG_NONE;
+  rc = bf::run_decode(!band_only, q, k_cache, v_cache, o, lse, seqlens_host, batch, cache_capacity,
                       n_heads_q, n_heads_kv, w0, w_pre, rope_theta, long_mode, softmax_scale,
-                      workspace, workspace_bytes, (hipStream_t)stream, err);
+                      workspace, workspace_bytes, (hipStream_t)stream, err, band_only ? w0 : 0);
   if (rc) return fail(rc, "%s", err.c_str());
   g_err.clear();
   return BF_OK;

@@ -51,6 +51,7 @@ struct DecodeSeqs {
   int s[kMaxSeqPerLaunch];       // s(N)
   int nsplit[kMaxSeqPerLaunch];
   int chunk[kMaxSeqPerLaunch];   // keys per split (multiple of 64)
+  int kstart[kMaxSeqPerLaunch];  // first key read: 0, or N - w0 for band-only attention
 };
 
 __device__ __forceinline__ float dbf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
@@ -169,7 +170,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p, De
   const long long w0 = (BIFOCAL && s > 1) ? p.w0 : (1LL << 62);
   const long long far_lim = N - w0;  // keys j < far_lim are far
   const int chunk = ds.chunk[b];
-  const long long k_begin = (long long)sp * chunk;
+  const long long k_begin = ds.kstart[b] + (long long)sp * chunk;
   const long long k_end = min(N, k_begin + chunk);
   const int per = chunk / kDecWaves;  // multiple of 16
   const long long kw0 = k_begin + (long long)wave * per;
@@ -606,7 +607,7 @@ size_t decode_workspace_bytes(int batch, long long max_len, int Hq) {
 int run_decode(bool bifocal, const void* q, const void* kc, const void* vc, void* o, float* lse,
                const int32_t* seqlens, int batch, int cap, int Hq, int Hkv, long long w0,
                long long w_pre, double theta, int mode, float scale, void* ws, size_t ws_bytes,
-               hipStream_t stream, std::string& err) {
+               hipStream_t stream, std::string& err, long long window) {
   auto bad = [&](int code, const std::string& m) { err = m; return code; };
   if (!q || !kc || !vc || !o || !seqlens) return bad(BF_ERR_INVALID_ARG, "null tensor or seqlens pointer");
   if (batch < 1 || cap < 1) return bad(BF_ERR_INVALID_ARG, "batch and cache_capacity must be >= 1");
@@ -658,8 +659,11 @@ int run_decode(bool bifocal, const void* q, const void* kc, const void* vc, void
       long long s = 1;
       if (bifocal) s = N / w_pre + (N % w_pre != 0 ? 1 : 0);
       ds.s[i] = (int)(s < 1 ? 1 : s);
-      ds.chunk[i] = decode_chunk(N, target);
-      ds.nsplit[i] = decode_splits(N, target);
+      // a window (band-only attention) reads keys N - window .. N - 1 only
+      const long long k0 = window > 0 && N > window ? N - window : 0;
+      ds.kstart[i] = (int)k0;
+      ds.chunk[i] = decode_chunk(N - k0, target);
+      ds.nsplit[i] = decode_splits(N - k0, target);
       if (ds.nsplit[i] > max_split) max_split = ds.nsplit[i];
     }
     dp.q = (const uint16_t*)q + (size_t)b0 * Hq * kHeadDim;

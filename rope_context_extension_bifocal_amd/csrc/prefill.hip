@@ -188,8 +188,9 @@ __device__ __forceinline__ Item make_item(const PrefillParams& p, const SeqTable
   decode_item(st, rank, p.max_nrb, it.b, rb);
   it.tok0 = st.cu[it.b];
   it.L = st.cu[it.b + 1] - it.tok0;
-  // s = 1 means the far branch equals the local one: treat every pair as local
-  it.w0 = (BIFOCAL && st.s[it.b] > 1) ? p.w0 : (1LL << 62);
+  // s = 1 means the far branch equals the local one: treat every pair as local;
+  // band-only attention keeps the window whatever s is
+  it.w0 = (BIFOCAL && (p.band_only || st.s[it.b] > 1)) ? p.w0 : (1LL << 62);
   const int hw = wave % p.hpw, pw = wave / p.hpw;
   it.hq = it.kvh * p.G + hsub * p.hpw + hw;
   it.R0 = rb * p.P_wg;
@@ -739,7 +740,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillParams p, S
   // tile ranges of the two passes for the workgroup's rows R0 .. R0 + P_wg - 1
   const long long R0 = it.R0, Rl = (long long)it.R0 + p.P_wg - 1;
   const long long w0 = it.w0;
-  if (BIFOCAL && Rl - w0 >= 0) {  // far pairs exist: keys j <= Rl - w0
+  if (BIFOCAL && !p.band_only && Rl - w0 >= 0) {  // far pairs exist: keys j <= Rl - w0
     const int kte = min(it.nkt, (int)((Rl - w0) / kKeyTile) + 1);
     run_pass<true>((const uint16_t*)p.q2 + ((size_t)it.hq * p.T + it.tok0) * kHeadDim,
                    (const uint16_t*)p.k2 + ((size_t)it.kvh * p.T + it.tok0) * kHeadDim, vt0,
@@ -823,7 +824,7 @@ __global__ __launch_bounds__(256, 1) void prefill_f32_kernel(PrefillParams p, Se
   {
     const int row = it.r0 + li;
     const bool ok = row < it.L;
-    const bool ok2 = ok && w0 < it.L;  // corrected queries exist only with far pairs
+    const bool ok2 = ok && w0 < it.L && !p.band_only;  // corrected queries exist only with far pairs
     const int rowc = ok ? row : it.L - 1;
 #pragma unroll
     for (int tc = 0; tc < 16; ++tc) {
@@ -849,6 +850,7 @@ __global__ __launch_bounds__(256, 1) void prefill_f32_kernel(PrefillParams p, Se
     const int c0 = kt * kKeyTile;
     bool cf, cl;
     tile_needs<BIFOCAL>(it.R0, p.P_wg, c0, w0, cf, cl);
+    if (p.band_only) cf = false;  // far pairs are dropped, never scored
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -879,12 +881,22 @@ __global__ __launch_bounds__(256, 1) void prefill_f32_kernel(PrefillParams p, Se
     const long long dmin = (long long)it.r0 - (c0 + kKeyTile - 1);
     const bool has_far = BIFOCAL && dmax >= w0;
     const bool has_loc = !BIFOCAL || (w0 > 0 && dmin < w0);
+    const bool band_only = BIFOCAL && p.band_only;
+    if (band_only && !has_loc) continue;  // every pair of the tile is dropped
 
     f32x16 S[2];
-    if (BIFOCAL && has_far) qk_f32(sK2, qf2, li, hl, S);
+    if (BIFOCAL && has_far && !band_only) qk_f32(sK2, qf2, li, hl, S);
     else qk_f32(sK, qf, li, hl, S);
     const long long i = it.r0 + li;
-    if (BIFOCAL && has_far && has_loc) {
+    if (band_only && has_far) {  // drop the far pairs of a mixed tile
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const long long j = c0 + 32 * jb + key_of_acc(r, hl);
+          if (!pair_is_local(i, j, w0)) S[jb][r] = -INFINITY;
+        }
+    } else if (BIFOCAL && has_far && has_loc) {
       f32x16 Sl[2];
       qk_f32(sK, qf, li, hl, Sl);
 #pragma unroll

@@ -88,11 +88,11 @@ def _decode(L, **kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(q=None), -1), (dict(o=None), -1), (dict(Hq=3, Hkv=2), -1), (dict(Hkv=0), -1),
     (dict(D=64), -2), (dict(dtype=7), -1), (dict(w0=-1), -1), (dict(w_pre=0), -1),
-    (dict(theta=1.0), -1), (dict(theta=float("nan")), -1), (dict(mode=2), -1),
+    (dict(theta=1.0), -1), (dict(theta=float("nan")), -1),
     (dict(scale=0.0), -1), (dict(scale=float("inf")), -1), (dict(cu=[1, 100]), -1),
     (dict(cu=[0, 50, 50]), -1), (dict(cu=[0, 60, 40]), -1), (dict(ws=None), -3),
     (dict(ws=ctypes.c_void_p(0x100010)), -3), (dict(ws_bytes=1000), -3),
-    (dict(q=ctypes.c_void_p(0x100002)), -1),
+    (dict(q=ctypes.c_void_p(0x100002)), -1), (dict(mode=2, w0=0), -1), (dict(mode=3), -1),
 ])
 def test_prefill_validation(L, kw, code):
     assert _prefill(L, **kw) == code
@@ -102,7 +102,7 @@ def test_prefill_validation(L, kw, code):
 @pytest.mark.parametrize("kw,code", [
     (dict(q=None), -1), (dict(sl=[0]), -1), (dict(sl=[129]), -1), (dict(dtype=1), -2),
     (dict(D=96), -2), (dict(Hq=5, Hkv=2), -1), (dict(w0=-3), -1), (dict(mode=9), -1),
-    (dict(ws_bytes=10), -3), (dict(Hq=34, Hkv=2), -2),
+    (dict(ws_bytes=10), -3), (dict(Hq=34, Hkv=2), -2), (dict(mode=2, w0=0), -1),
 ])
 def test_decode_validation(L, kw, code):
     assert _decode(L, **kw) == code
@@ -116,6 +116,8 @@ def test_valid_arguments_reach_the_launch(L, monkeypatch):
     assert _prefill(L, dtype=1, mode=1, cu=[0, 5, 300, 301]) == bfl.BF_ERR_HIP
     assert _decode(L) == bfl.BF_ERR_HIP
     assert b"forced" in L.bifocal_last_error()
+    assert _prefill(L, mode=2, w0=5) == bfl.BF_ERR_HIP  # band only: valid, reaches the launch
+    assert _decode(L, mode=2, w0=5) == bfl.BF_ERR_HIP
 
 
 def test_plain_validation(L):

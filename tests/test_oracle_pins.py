@@ -364,3 +364,44 @@ def test_packed_positions_restart_per_sequence():
         sl = slice(cu[b], cu[b + 1])
         alone = oracle.rope_rows(x[:, sl], np.arange(cu[b + 1] - cu[b]), 1e4)
         np.testing.assert_array_equal(packed[:, sl], alone)
+
+
+# ---------------------------------------------------------------- band-only (sliding window)
+def _sdpa_band(q, k, v, w0, scale):
+    """Library attention (torch SDPA, fp64) with the band mask j in (i - w0, i]."""
+    Hq, L, D = q.shape
+    G = Hq // k.shape[0]
+    i = torch.arange(L)[:, None]
+    j = torch.arange(L)[None, :]
+    mask = (j <= i) & (i - j < w0)
+    qt = torch.from_numpy(q.astype(np.float64))
+    kt = torch.from_numpy(np.repeat(k, G, axis=0).astype(np.float64))
+    vt = torch.from_numpy(np.repeat(v, G, axis=0).astype(np.float64))
+    return torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=scale).numpy()
+
+
+@pytest.mark.parametrize("w0", [1, 7, 64, 200])
+def test_band_only_matches_library_sliding_window(w0):
+    rng = np.random.default_rng(41 + w0)
+    Hq, Hkv, L, D = 4, 2, 150, 128
+    q = rng.standard_normal((Hq, L, D)).astype(np.float32)
+    k = rng.standard_normal((Hkv, L, D)).astype(np.float32)
+    v = rng.standard_normal((Hkv, L, D)).astype(np.float32)
+    scale = 1 / math.sqrt(D)
+    o, _ = oracle.prefill(q, k, v, [0, L], w0, 16, 1e4, "band", scale)
+    np.testing.assert_allclose(o, _sdpa_band(q, k, v, w0, scale), atol=1e-11)
+    if w0 == 1:  # every row sees only itself
+        np.testing.assert_allclose(o, np.repeat(v, Hq // Hkv, axis=0), atol=1e-12)
+
+
+def test_band_only_decode_is_last_row():
+    rng = np.random.default_rng(46)
+    Hq, Hkv, N, D, w0 = 4, 1, 90, 128, 20
+    q = rng.standard_normal((Hq, N, D)).astype(np.float32)
+    k = rng.standard_normal((Hkv, N, D)).astype(np.float32)
+    v = rng.standard_normal((Hkv, N, D)).astype(np.float32)
+    scale = 1 / math.sqrt(D)
+    o_pre, lse_pre = oracle.prefill(q, k, v, [0, N], w0, 32, 1e4, "band", scale, rows=[N - 1])
+    o_dec, lse_dec = oracle.decode(q[:, N - 1][None], k[None], v[None], [N], w0, 32, 1e4, "band", scale)
+    np.testing.assert_allclose(o_dec[0], o_pre[:, 0], atol=1e-12)
+    np.testing.assert_allclose(lse_dec[0], lse_pre[:, 0], atol=1e-12)
