@@ -283,6 +283,7 @@ def main():
     pa_ms = time_calls(lambda: prefill("pa"), 3, stream)
     plain_prefill()
     plain_ms = time_calls(plain_prefill, 3, stream)
+    shift_ms = time_calls(lambda: prefill("fi+shift"), 2, stream)
     for _ in range(10):
         decode()
     dec_many_ms = time_calls(decode, 50, stream)
@@ -416,6 +417,7 @@ def main():
         "plain_prefill_tflops": round(flops / (plain_ms * 1e-3) / 1e12, 2),
         "prefill_overhead_vs_plain": round(pre_ms / plain_ms - 1, 4),
         "prefill_pa_overhead_vs_plain": round(pa_ms / plain_ms - 1, 4),
+        "prefill_fi_shift_tflops": round(flops / (shift_ms * 1e-3) / 1e12, 2),
         "decode_us": round(dec_ms * 1e3, 2),
         "decode_gbs": round(gbs, 1),
         "decode_frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),

@@ -61,6 +61,11 @@ extern "C" {
 /* long-branch position map phi(p) */
 #define BF_LONG_FI 0 /* frequency interpolation: phi(p) = p / s */
 #define BF_LONG_PA 1 /* position aliasing:       phi(p) = floor(p / s) */
+#define BF_LONG_SHIFT 4 /* flag, OR-ed into BF_LONG_FI / BF_LONG_PA: band-edge continuity
+                           shift. The far query sits at phi(p) + w0 - phi(w0), so a far pair
+                           at distance exactly w0 sees relative position w0 as the band does
+                           [seventnews.com (FR), fusion paragraph: the correction re-aligns
+                           the phases of the two branches]. Off by default. */
 #define BF_LONG_NONE 2 /* band only: far pairs are dropped, i.e. sliding-window attention
                           over the w0 most recent keys with original RoPE (w0 >= 1; w_pre
                           unused), the sliding-window layers of a hybrid model */
@@ -97,8 +102,9 @@ size_t bifocal_workspace_bytes(int32_t phase, int32_t batch, int64_t tokens, int
  *          positions restart at 0 and it gets its own s(L_b).
  *   w0 >= 0 local window (w0 = 0: every pair far; w0 >= L: plain RoPE),
  *   w_pre >= 1 pretrained window, rope_theta > 1 RoPE base,
- *   long_mode BF_LONG_FI or BF_LONG_PA, or BF_LONG_NONE for the band-only
- *   special case (needs w0 >= 1), softmax_scale > 0 (both branches).
+ *   long_mode BF_LONG_FI or BF_LONG_PA (either with BF_LONG_SHIFT OR-ed
+ *   in), or BF_LONG_NONE for the band-only special case (needs w0 >= 1),
+ *   softmax_scale > 0 (both branches).
  * Query head h reads KV head h / (n_heads_q / n_heads_kv).
  * [ai-feeds.com summary, "方法": inputs are L and the pretrained RoPE
  *  configuration, the output is the attention output of the sequence;

@@ -52,7 +52,8 @@ def _ptr(a):
     return a.ctypes.data_as(ctypes.c_void_p)
 
 
-MODES = {"fi": 0, "pa": 1, "band": 2}  # band: far pairs dropped (sliding window w0)
+# band: far pairs dropped (sliding window w0); "+shift": band-edge continuity shift
+MODES = {"fi": 0, "pa": 1, "band": 2, "fi+shift": 4, "pa+shift": 5}
 
 
 def s_of_L(L, w_pre):

@@ -96,6 +96,27 @@ static void far_vector(const double* xp, double* out, int64_t D, int64_t p, int6
     oracle_rope_rotate(tmp, out, D, oracle_phi(p, s, mode), theta_base);
 }
 
+/* Band-edge continuity shift (long-mode flag 4, off by default): the far
+ * query is placed at phi(p) + delta with delta = w0 - phi(w0), so that a far
+ * pair at distance exactly w0 sees relative position w0, as the band does
+ * one step closer. FI: delta = w0 (s - 1) / s; PA: delta = w0 - floor(w0 / s)
+ * (the offset of Self-Extend's grouped attention). The pages say the
+ * correction rotation re-aligns the phases of the two branches without
+ * fixing a constant [seventnews.com (FR), fusion paragraph; promo script,
+ * "工程拐点" bullet: on-the-fly phase compensation]; the flag makes this
+ * reading available next to the default (no shift).                      */
+static double far_shift(int64_t w0, int64_t s, int32_t mode)
+{
+    return (double)w0 - oracle_phi(w0, s, mode);
+}
+
+static void far_query(const double* xp, double* out, int64_t D, int64_t p, int64_t s,
+                      int32_t mode, double shift, double theta_base, double* tmp)
+{
+    oracle_rope_rotate(xp, tmp, D, -(double)p, theta_base);          /* raw */
+    oracle_rope_rotate(tmp, out, D, oracle_phi(p, s, mode) + shift, theta_base);
+}
+
 static double dot(const double* a, const double* b, int64_t D)
 {
     double acc = 0.0;
@@ -198,7 +219,8 @@ static void one_row_inclexcl(const double* qo, const double* qf,
  *   k, v   [Hkv][T][D]      packed keys / values, T = cu[B]
  *   cu     [B+1]            sequence offsets; positions restart per sequence
  *   o      [Hq][n_rows][D], lse [Hq][n_rows]  (natural log)
- *   mode 0 = FI, 1 = PA, 2 = band only (far pairs dropped).
+ *   mode 0 = FI, 1 = PA, 2 = band only (far pairs dropped); 4 | 0 and
+ *   4 | 1 add the band-edge continuity shift to FI / PA.
  *   variant 0 = direct definition, 1 = inclusion-exclusion partials.
  * Returns 0, or a negative code for bad arguments / no memory.           */
 int oracle_prefill_rows(const float* q_rows, const float* k, const float* v,
@@ -208,7 +230,9 @@ int oracle_prefill_rows(const float* q_rows, const float* k, const float* v,
                         double* o, double* lse)
 {
     if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || D < 2 || D % 2 != 0 || D > 1024) return ORC_BAD;
-    if (w0 < 0 || w_pre < 1 || mode < 0 || mode > 2 || (mode == 2 && w0 < 1)) return ORC_BAD;
+    const int32_t shift_on = mode & 4;
+    mode &= ~4;
+    if (w0 < 0 || w_pre < 1 || mode < 0 || mode > 2 || (mode == 2 && (w0 < 1 || shift_on))) return ORC_BAD;
     if (variant == 1 && mode == 2) return ORC_BAD;  /* no scaled branch to subtract */
     for (int64_t b = 0; b < B; ++b)
         if (cu[b + 1] <= cu[b]) return ORC_BAD;
@@ -282,10 +306,11 @@ int oracle_prefill_rows(const float* q_rows, const float* k, const float* v,
                     int64_t i = t - cu[b];
                     int64_t L = cu[b + 1] - cu[b];
                     int64_t s = oracle_s_of_L(L, w_pre);
+                    const double shift = shift_on ? far_shift(w0, s, mode) : 0.0;
                     int64_t hk = h / G;
                     const float* qsrc = q_rows + ((size_t)h * (size_t)n_rows + (size_t)r) * (size_t)D;
                     for (int64_t d = 0; d < D; ++d) qo[d] = (double)qsrc[d];
-                    far_vector(qo, qf, D, i, s, mode, theta_base, tmp);
+                    far_query(qo, qf, D, i, s, mode, shift, theta_base, tmp);
                     size_t kb = ((size_t)hk * (size_t)total_need + (size_t)base[b]) * (size_t)D;
                     double* orow = o + ((size_t)h * (size_t)n_rows + (size_t)r) * (size_t)D;
                     double* lrow = lse + (size_t)h * (size_t)n_rows + (size_t)r;
@@ -316,7 +341,9 @@ int oracle_decode(const float* q, const float* k_cache, const float* v_cache,
                   double scale, double* o, double* lse)
 {
     if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || D < 2 || D % 2 != 0 || D > 1024) return ORC_BAD;
-    if (w0 < 0 || w_pre < 1 || mode < 0 || mode > 2 || (mode == 2 && w0 < 1)) return ORC_BAD;
+    const int32_t shift_on = mode & 4;
+    mode &= ~4;
+    if (w0 < 0 || w_pre < 1 || mode < 0 || mode > 2 || (mode == 2 && (w0 < 1 || shift_on))) return ORC_BAD;
     int64_t maxN = 0;
     for (int64_t b = 0; b < B; ++b) {
         if (seqlens[b] < 1 || seqlens[b] > cap) return ORC_BAD;
@@ -327,6 +354,7 @@ int oracle_decode(const float* q, const float* k_cache, const float* v_cache,
     for (int64_t b = 0; b < B; ++b) {
         const int64_t N = seqlens[b];
         const int64_t s = oracle_s_of_L(N, w_pre);
+        const double shift = shift_on ? far_shift(w0, s, mode) : 0.0;
         size_t nk = (size_t)Hkv * (size_t)N * (size_t)D;
         double* ko = (double*)malloc(nk * sizeof(double));
         double* kf = (double*)malloc(nk * sizeof(double));
@@ -357,7 +385,7 @@ int oracle_decode(const float* q, const float* k_cache, const float* v_cache,
                     int64_t hk = h / G;
                     const float* qs = q + ((size_t)b * (size_t)Hq + (size_t)h) * (size_t)D;
                     for (int64_t d = 0; d < D; ++d) qo[d] = (double)qs[d];
-                    far_vector(qo, qf, D, N - 1, s, mode, theta_base, tmp);
+                    far_query(qo, qf, D, N - 1, s, mode, shift, theta_base, tmp);
                     size_t kb = (size_t)hk * (size_t)N * (size_t)D;
                     one_row(qo, qf, ko + kb, kf + kb, vv + kb, N - 1, D, w0, scale, mode == 2, sb,
                             o + ((size_t)b * (size_t)Hq + (size_t)h) * (size_t)D,

@@ -17,9 +17,11 @@ LIB_PATH = os.path.join(_PKG, "libbifocal.so")
 
 BF_OK, BF_ERR_INVALID_ARG, BF_ERR_UNSUPPORTED, BF_ERR_WORKSPACE, BF_ERR_HIP = 0, -1, -2, -3, -4
 BF_DTYPE_BF16, BF_DTYPE_FP32 = 0, 1
-BF_LONG_FI, BF_LONG_PA, BF_LONG_NONE = 0, 1, 2
+BF_LONG_FI, BF_LONG_PA, BF_LONG_NONE, BF_LONG_SHIFT = 0, 1, 2, 4
 BF_PHASE_PREFILL, BF_PHASE_DECODE = 0, 1
-LONG_MODES = {"fi": BF_LONG_FI, "pa": BF_LONG_PA, "band": BF_LONG_NONE}  # band: far pairs dropped
+# band: far pairs dropped; "+shift": band-edge continuity shift of the far query
+LONG_MODES = {"fi": BF_LONG_FI, "pa": BF_LONG_PA, "band": BF_LONG_NONE,
+              "fi+shift": BF_LONG_FI | BF_LONG_SHIFT, "pa+shift": BF_LONG_PA | BF_LONG_SHIFT}
 _DTYPES = {torch.bfloat16: BF_DTYPE_BF16, torch.float32: BF_DTYPE_FP32}
 
 EXPORTED = ("bifocal_s_of_L", "bifocal_workspace_bytes", "bifocal_prefill", "bifocal_decode",

@@ -56,6 +56,8 @@ struct PrepParams {
   void* k2;       // [Hkv][T][D]
   int T, Hq, Hkv;
   int long_mode;  // 0 = FI, 1 = PA
+  int shift;      // 1: queries get the band-edge continuity shift w0 - phi(w0)
+  long long w0;
 };
 
 struct VtParams {

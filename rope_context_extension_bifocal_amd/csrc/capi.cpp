@@ -119,9 +119,13 @@ int check_bifocal_knobs(long long w0, long long w_pre, double theta, int mode) {
   if (w_pre < 1) return fail(BF_ERR_INVALID_ARG, "w_pre must be >= 1 (got %lld)", w_pre);
   if (!(theta > 1.0) || !std::isfinite(theta))
     return fail(BF_ERR_INVALID_ARG, "rope_theta must be finite and > 1");
-  if (mode != BF_LONG_FI && mode != BF_LONG_PA && mode != BF_LONG_NONE)
-    return fail(BF_ERR_INVALID_ARG, "long_mode must be BF_LONG_FI, BF_LONG_PA or BF_LONG_NONE (got %d)", mode);
-  if (mode == BF_LONG_NONE && w0 < 1)
+  const int base = mode & ~BF_LONG_SHIFT;
+  if (base != BF_LONG_FI && base != BF_LONG_PA && base != BF_LONG_NONE)
+    return fail(BF_ERR_INVALID_ARG, "long_mode must be BF_LONG_FI or BF_LONG_PA (optionally with "
+                "BF_LONG_SHIFT) or BF_LONG_NONE (got %d)", mode);
+  if (base == BF_LONG_NONE && (mode & BF_LONG_SHIFT))
+    return fail(BF_ERR_INVALID_ARG, "BF_LONG_SHIFT has no meaning for band-only attention");
+  if (base == BF_LONG_NONE && w0 < 1)
     return fail(BF_ERR_INVALID_ARG, "band-only attention (BF_LONG_NONE) needs w0 >= 1");
   return BF_OK;
 }
@@ -155,6 +159,8 @@ int run_prefill(bool bifocal, const void* q, const void* k, const void* v, void*
   const PrefillWs wl = prefill_ws_layout(batch, T, Hq, Hkv, dtype);
   if (!ws) return fail(BF_ERR_WORKSPACE, "workspace is null");
   if ((uintptr_t)ws & 255u) return fail(BF_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  const bool shift = bifocal && (mode & BF_LONG_SHIFT);
+  mode &= ~BF_LONG_SHIFT;
   const bool band_only = bifocal && mode == BF_LONG_NONE;
   const size_t need = bifocal && !band_only ? wl.total : wl.q2_off;
   if (ws_bytes < need)
@@ -200,7 +206,7 @@ int run_prefill(bool bifocal, const void* q, const void* k, const void* v, void*
     e = bf::launch_vt_transpose(dtype, vp, st, stream);
     if (e != hipSuccess) return fail(BF_ERR_HIP, "vt_transpose launch: %s", hipGetErrorString(e));
     if (bifocal && any_far && !band_only) {
-      bf::PrepParams pp{q, k, wsb + wl.q2_off, wsb + wl.k2_off, (int)T, Hq, Hkv, mode};
+      bf::PrepParams pp{q, k, wsb + wl.q2_off, wsb + wl.k2_off, (int)T, Hq, Hkv, mode, shift ? 1 : 0, w0};
       e = bf::launch_correction_prep(dtype, pp, st, tt, stream);
       if (e != hipSuccess) return fail(BF_ERR_HIP, "correction_prep launch: %s", hipGetErrorString(e));
     }

@@ -42,7 +42,8 @@ struct DecodeParams {
   long long w0;
   float scale_log2;
   int Hq, Hkv, G, S;
-  int mode;
+  int mode;   // 0 = FI, 1 = PA
+  int shift;  // 1: the query gets the band-edge continuity shift w0 - phi(w0)
 };
 
 struct DecodeSeqs {
@@ -237,7 +238,10 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p, De
   }
   lds_barrier();
   if (split_far) {
-    const double qn = (double)dcorr_num(N - 1, s, p.mode) / (double)s;
+    // query angle numerator (phi(N - 1) - (N - 1)) s, plus (w0 - phi(w0)) s
+    // with the band-edge continuity shift (w0 < N here, so no overflow)
+    const long long qsh = !p.shift ? 0 : p.mode == 1 ? (w0 - w0 / s) * s : w0 * (s - 1);
+    const double qn = (double)(dcorr_num(N - 1, s, p.mode) + qsh) / (double)s;
     float c, sn;
     turn_cos_sin(th_lane * kInv2Pi * qn, c, sn);
     for (int e = tid; e < p.G * kPairs; e += 256) {  // pair m = e % 64 = lane
@@ -646,7 +650,8 @@ int run_decode(bool bifocal, const void* q, const void* kc, const void* vc, void
   dp.Hkv = Hkv;
   dp.G = G;
   dp.S = decode_split_bound(max_len);
-  dp.mode = mode;
+  dp.shift = (mode & BF_LONG_SHIFT) ? 1 : 0;
+  dp.mode = mode & ~BF_LONG_SHIFT;
   for (int b0 = 0; b0 < batch; b0 += kMaxSeqPerLaunch) {
     const int nb = batch - b0 < kMaxSeqPerLaunch ? batch - b0 : kMaxSeqPerLaunch;
     const long long target = decode_target_splits(nb, Hkv);

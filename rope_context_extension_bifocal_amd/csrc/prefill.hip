@@ -120,10 +120,22 @@ __global__ __launch_bounds__(256) void correction_prep_kernel(PrepParams p, SeqT
   const int s = st.s[b];
   if (s == 1) return;  // no far branch for this sequence
   const long long pos = tok - st.cu[b];
-  const double dphi = (double)corr_num(pos, s, p.long_mode) / (double)s;
+  const long long num = corr_num(pos, s, p.long_mode);
+  const double dphi = (double)num / (double)s;
   double sd, cd;
   sincos(tt.th[m] * dphi, &sd, &cd);
   const float c = (float)cd, sn = (float)sd;
+  // queries: the same angle, plus the band-edge continuity shift if asked:
+  // (w0 - phi(w0)) * s is the exact integer w0 (s - 1) (FI) or
+  // (w0 - floor(w0 / s)) s (PA)
+  float cq = c, sq = sn;
+  if (p.shift) {
+    const long long sh = p.long_mode == 1 ? (p.w0 - p.w0 / s) * s : p.w0 * (s - 1);
+    double sdq, cdq;
+    sincos(tt.th[m] * ((double)(num + sh) / (double)s), &sdq, &cdq);
+    cq = (float)cdq;
+    sq = (float)sdq;
+  }
   const T* q = (const T*)p.q;
   const T* k = (const T*)p.k;
   T* q2 = (T*)p.q2;
@@ -131,8 +143,8 @@ __global__ __launch_bounds__(256) void correction_prep_kernel(PrepParams p, SeqT
   for (int h = 0; h < p.Hq; ++h) {
     const size_t base = ((size_t)h * p.T + tok) * kHeadDim;
     const float x0 = ld_elem(q + base + m), x1 = ld_elem(q + base + m + kPairs);
-    st_elem(q2 + base + m, x0 * c - x1 * sn);
-    st_elem(q2 + base + m + kPairs, x1 * c + x0 * sn);
+    st_elem(q2 + base + m, x0 * cq - x1 * sq);
+    st_elem(q2 + base + m + kPairs, x1 * cq + x0 * sq);
   }
   for (int h = 0; h < p.Hkv; ++h) {
     const size_t base = ((size_t)h * p.T + tok) * kHeadDim;

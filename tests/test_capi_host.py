@@ -93,6 +93,7 @@ def _decode(L, **kw):
     (dict(cu=[0, 50, 50]), -1), (dict(cu=[0, 60, 40]), -1), (dict(ws=None), -3),
     (dict(ws=ctypes.c_void_p(0x100010)), -3), (dict(ws_bytes=1000), -3),
     (dict(q=ctypes.c_void_p(0x100002)), -1), (dict(mode=2, w0=0), -1), (dict(mode=3), -1),
+    (dict(mode=6), -1), (dict(mode=8), -1), (dict(mode=7), -1),
 ])
 def test_prefill_validation(L, kw, code):
     assert _prefill(L, **kw) == code
@@ -117,6 +118,8 @@ def test_valid_arguments_reach_the_launch(L, monkeypatch):
     assert _decode(L) == bfl.BF_ERR_HIP
     assert b"forced" in L.bifocal_last_error()
     assert _prefill(L, mode=2, w0=5) == bfl.BF_ERR_HIP  # band only: valid, reaches the launch
+    assert _prefill(L, mode=4) == bfl.BF_ERR_HIP and _prefill(L, mode=5) == bfl.BF_ERR_HIP  # + shift
+    assert _decode(L, mode=5) == bfl.BF_ERR_HIP
     assert _decode(L, mode=2, w0=5) == bfl.BF_ERR_HIP
 
 

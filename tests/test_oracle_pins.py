@@ -405,3 +405,40 @@ def test_band_only_decode_is_last_row():
     o_dec, lse_dec = oracle.decode(q[:, N - 1][None], k[None], v[None], [N], w0, 32, 1e4, "band", scale)
     np.testing.assert_allclose(o_dec[0], o_pre[:, 0], atol=1e-12)
     np.testing.assert_allclose(lse_dec[0], lse_pre[:, 0], atol=1e-12)
+
+
+# ---------------------------------------------------------------- band-edge continuity shift
+@pytest.mark.parametrize("mode", ["fi", "pa"])
+def test_shift_makes_the_window_edge_continuous(mode):
+    # row i = w0 has exactly one far pair, j = 0, at distance w0. With the
+    # shift its relative position is w0 again (FI: w0/s + w0 - w0/s; PA:
+    # floor(w0/s) + w0 - floor(w0/s)), so the row equals plain causal
+    # attention on the original-RoPE inputs (library SDPA, fp64); without the
+    # shift it does not.
+    rng = np.random.default_rng(51)
+    Hq, Hkv, L, D, w0, w_pre = 2, 1, 60, 128, 24, 20  # s = 3
+    q = rng.standard_normal((Hq, L, D)).astype(np.float32)
+    k = rng.standard_normal((Hkv, L, D)).astype(np.float32)
+    v = rng.standard_normal((Hkv, L, D)).astype(np.float32)
+    scale = 1 / math.sqrt(D)
+    ref = _sdpa_band(q, k, v, L + 1, scale)[:, w0]  # plain causal
+    o_sh, _ = oracle.prefill(q, k, v, [0, L], w0, w_pre, 1e4, mode + "+shift", scale, rows=[w0])
+    o_no, _ = oracle.prefill(q, k, v, [0, L], w0, w_pre, 1e4, mode, scale, rows=[w0])
+    np.testing.assert_allclose(o_sh[:, 0], ref, atol=1e-11)
+    assert np.abs(o_no[:, 0] - ref).max() > 1e-4
+    # decode at N = w0 + 1 is the same row
+    od, _ = oracle.decode(q[:, w0][None], k[None, :, :w0 + 1], v[None, :, :w0 + 1], [w0 + 1], w0,
+                          w_pre, 1e4, mode + "+shift", scale)
+    o_pre, _ = oracle.prefill(q[:, :w0 + 1], k[:, :w0 + 1], v[:, :w0 + 1], [0, w0 + 1], w0, w_pre,
+                              1e4, mode + "+shift", scale, rows=[w0])
+    np.testing.assert_allclose(od[0], o_pre[:, 0], atol=1e-12)
+
+
+def test_shift_is_a_no_op_at_s1():
+    rng = np.random.default_rng(52)
+    q = rng.standard_normal((2, 50, 128)).astype(np.float32)
+    k = rng.standard_normal((1, 50, 128)).astype(np.float32)
+    v = rng.standard_normal((1, 50, 128)).astype(np.float32)
+    a, _ = oracle.prefill(q, k, v, [0, 50], 8, 64, 1e4, "fi+shift", 0.088)
+    b, _ = oracle.prefill(q, k, v, [0, 50], 8, 64, 1e4, "fi", 0.088)
+    np.testing.assert_array_equal(a, b)
