@@ -38,7 +38,6 @@ struct PrefillParams {
   void* o;          // [Hq][T][D]
   float* lse;       // [Hq][T] or null
   long long w0;     // local window (ignored by the plain engine)
-  int band_only;    // 1: far pairs are dropped (sliding window of w0 keys, original RoPE)
   float scale_log2; // softmax_scale * log2(e)
   int T, Tpad;
   int Hq, Hkv, G;

@@ -21,7 +21,7 @@ hipError_t launch_correction_prep(int dtype, const PrepParams& pp, const SeqTabl
                                   const ThetaTable& tt, hipStream_t stream);
 hipError_t launch_vt_transpose(int dtype, const VtParams& vp, const SeqTable& st,
                                hipStream_t stream);
-hipError_t launch_prefill_main(int dtype, bool bifocal, const PrefillParams& pp,
+hipError_t launch_prefill_main(int dtype, bool bifocal, bool band, const PrefillParams& pp,
                                const SeqTable& st, int grid, hipStream_t stream);
 hipError_t launch_pair_map(long long L, long long w0, long long s, int mode, int8_t* br,
                            long long* dphi_num, long long* s_out, hipStream_t stream);
@@ -219,7 +219,6 @@ int run_prefill(bool bifocal, const void* q, const void* k, const void* v, void*
     pp.o = o;
     pp.lse = lse;
     pp.w0 = w0;
-    pp.band_only = band_only ? 1 : 0;
     pp.scale_log2 = scale * 1.4426950408889634f;
     pp.T = (int)T;
     pp.Tpad = Tpad;
@@ -237,7 +236,7 @@ int run_prefill(bool bifocal, const void* q, const void* k, const void* v, void*
       fprintf(stderr, "[bifocal] prefill %s dtype=%d seqs=%d..%d grid=%lld P_wg=%d hpw=%d n_hsub=%d s0=%d w0=%lld\n",
               band_only ? "band-only" : bifocal ? "bifocal" : "plain", dtype, b0, b0 + nb - 1, grid, geo.P_wg, geo.hpw,
               geo.n_hsub, st.s[0], w0);
-    e = bf::launch_prefill_main(dtype, bifocal && any_far, pp, st, (int)grid, stream);
+    e = bf::launch_prefill_main(dtype, bifocal && any_far, band_only && any_far, pp, st, (int)grid, stream);
     if (e != hipSuccess) return fail(BF_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
   }
   g_err.clear();

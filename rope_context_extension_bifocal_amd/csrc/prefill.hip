@@ -187,7 +187,7 @@ struct Item {
   long long w0;
 };
 
-template <bool BIFOCAL>
+template <bool BIFOCAL, bool BAND>
 __device__ __forceinline__ Item make_item(const PrefillParams& p, const SeqTable& st, int wave,
                                           int wave_rows) {
   Item it;
@@ -202,7 +202,7 @@ __device__ __forceinline__ Item make_item(const PrefillParams& p, const SeqTable
   it.L = st.cu[it.b + 1] - it.tok0;
   // s = 1 means the far branch equals the local one: treat every pair as local;
   // band-only attention keeps the window whatever s is
-  it.w0 = (BIFOCAL && (p.band_only || st.s[it.b] > 1)) ? p.w0 : (1LL << 62);
+  it.w0 = (BIFOCAL && (BAND || st.s[it.b] > 1)) ? p.w0 : (1LL << 62);
   const int hw = wave % p.hpw, pw = wave / p.hpw;
   it.hq = it.kvh * p.G + hsub * p.hpw + hw;
   it.R0 = rb * p.P_wg;
@@ -721,7 +721,7 @@ __device__ __forceinline__ void run_pass(const uint16_t* qsrc, const uint16_t* k
   }
 }
 
-template <bool BIFOCAL>
+template <bool BIFOCAL, bool BAND>
 __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillParams p, SeqTable st) {
   extern __shared__ uint4 smem[];
   uint4* sK = smem;                  // kRing slots
@@ -729,7 +729,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillParams p, S
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar) index
   const int li = lane & 31, hl = lane >> 5;
-  const Item it = make_item<BIFOCAL>(p, st, wave, kWaveRowsBf16);
+  const Item it = make_item<BIFOCAL, BAND>(p, st, wave, kWaveRowsBf16);
   const WaveRows wr{it.r0, it.L, (int)min(it.w0, (long long)(1 << 30))};
 
   const uint16_t* qg = (const uint16_t*)p.q + ((size_t)it.hq * p.T + it.tok0) * kHeadDim;
@@ -752,7 +752,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillParams p, S
   // tile ranges of the two passes for the workgroup's rows R0 .. R0 + P_wg - 1
   const long long R0 = it.R0, Rl = (long long)it.R0 + p.P_wg - 1;
   const long long w0 = it.w0;
-  if (BIFOCAL && !p.band_only && Rl - w0 >= 0) {  // far pairs exist: keys j <= Rl - w0
+  if (BIFOCAL && !BAND && Rl - w0 >= 0) {  // far pairs exist: keys j <= Rl - w0
     const int kte = min(it.nkt, (int)((Rl - w0) / kKeyTile) + 1);
     run_pass<true>((const uint16_t*)p.q2 + ((size_t)it.hq * p.T + it.tok0) * kHeadDim,
                    (const uint16_t*)p.k2 + ((size_t)it.kvh * p.T + it.tok0) * kHeadDim, vt0,
@@ -812,16 +812,16 @@ __device__ __forceinline__ void qk_f32(const uint4* __restrict__ sk, const float
   }
 }
 
-template <bool BIFOCAL>
+template <bool BIFOCAL, bool BAND>
 __global__ __launch_bounds__(256, 1) void prefill_f32_kernel(PrefillParams p, SeqTable st) {
   extern __shared__ uint4 smem[];
   uint4* sK = smem;                            // [64][32 x 16 B]
   uint4* sK2 = smem + 2048;
-  uint4* sV = smem + (BIFOCAL ? 4096 : 2048);  // [128][16 x 16 B]
+  uint4* sV = smem + (BIFOCAL && !BAND ? 4096 : 2048);  // [128][16 x 16 B] (no K'' slot without a far branch)
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 31, hl = lane >> 5;
-  const Item it = make_item<BIFOCAL>(p, st, wave, kWaveRowsF32);
+  const Item it = make_item<BIFOCAL, BAND>(p, st, wave, kWaveRowsF32);
   const long long w0 = it.w0;
 
   const float* qg = (const float*)p.q + ((size_t)it.hq * p.T + it.tok0) * kHeadDim;
@@ -836,7 +836,7 @@ __global__ __launch_bounds__(256, 1) void prefill_f32_kernel(PrefillParams p, Se
   {
     const int row = it.r0 + li;
     const bool ok = row < it.L;
-    const bool ok2 = ok && w0 < it.L && !p.band_only;  // corrected queries exist only with far pairs
+    const bool ok2 = ok && w0 < it.L && !BAND;  // corrected queries exist only with far pairs
     const int rowc = ok ? row : it.L - 1;
 #pragma unroll
     for (int tc = 0; tc < 16; ++tc) {
@@ -862,7 +862,7 @@ __global__ __launch_bounds__(256, 1) void prefill_f32_kernel(PrefillParams p, Se
     const int c0 = kt * kKeyTile;
     bool cf, cl;
     tile_needs<BIFOCAL>(it.R0, p.P_wg, c0, w0, cf, cl);
-    if (p.band_only) cf = false;  // far pairs are dropped, never scored
+    if (BAND) cf = false;  // far pairs are dropped, never scored
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -893,7 +893,7 @@ __global__ __launch_bounds__(256, 1) void prefill_f32_kernel(PrefillParams p, Se
     const long long dmin = (long long)it.r0 - (c0 + kKeyTile - 1);
     const bool has_far = BIFOCAL && dmax >= w0;
     const bool has_loc = !BIFOCAL || (w0 > 0 && dmin < w0);
-    const bool band_only = BIFOCAL && p.band_only;
+    constexpr bool band_only = BIFOCAL && BAND;
     if (band_only && !has_loc) continue;  // every pair of the tile is dropped
 
     f32x16 S[2];
@@ -1031,16 +1031,18 @@ static hipError_t launch_with_lds(K kernel, int grid, int threads, size_t lds, h
   return hipGetLastError();
 }
 
-hipError_t launch_prefill_main(int dtype, bool bifocal, const PrefillParams& pp,
+hipError_t launch_prefill_main(int dtype, bool bifocal, bool band, const PrefillParams& pp,
                                const SeqTable& st, int grid, hipStream_t stream) {
   if (dtype == 0) {
     const int th = 64 * kBf16Waves;
     const size_t lds = 2 * kRing * kSlot * sizeof(uint4);
-    if (bifocal) return launch_with_lds(prefill_bf16_kernel<true>, grid, th, lds, stream, pp, st);
-    return launch_with_lds(prefill_bf16_kernel<false>, grid, th, lds, stream, pp, st);
+    if (band) return launch_with_lds(prefill_bf16_kernel<true, true>, grid, th, lds, stream, pp, st);
+    if (bifocal) return launch_with_lds(prefill_bf16_kernel<true, false>, grid, th, lds, stream, pp, st);
+    return launch_with_lds(prefill_bf16_kernel<false, false>, grid, th, lds, stream, pp, st);
   }
-  if (bifocal) return launch_with_lds(prefill_f32_kernel<true>, grid, 256, 3 * 32768, stream, pp, st);
-  return launch_with_lds(prefill_f32_kernel<false>, grid, 256, 2 * 32768, stream, pp, st);
+  if (band) return launch_with_lds(prefill_f32_kernel<true, true>, grid, 256, 2 * 32768, stream, pp, st);
+  if (bifocal) return launch_with_lds(prefill_f32_kernel<true, false>, grid, 256, 3 * 32768, stream, pp, st);
+  return launch_with_lds(prefill_f32_kernel<false, false>, grid, 256, 2 * 32768, stream, pp, st);
 }
 
 hipError_t launch_pair_map(long long L, long long w0, long long s, int mode, int8_t* br,
