@@ -309,6 +309,26 @@ def main():
         del kcs, vcs
         return t * 1e3
 
+    # the same 131073-key decode over a paged cache (16-key pages in shuffled
+    # order, as a serving engine's page pool would hold them)
+    PG = 16
+    n_pages = -(-N // PG)
+    def paged_pool(x):
+        xp = torch.zeros((Hkv, n_pages * PG, D), dtype=x.dtype, device=x.device)
+        xp[:, :N] = x[0, :, :N]
+        return xp.view(Hkv, n_pages, PG, D).transpose(0, 1).contiguous()  # [page, Hkv, PG, D]
+    perm = torch.randperm(n_pages, generator=torch.Generator().manual_seed(11))
+    kpg, vpg = paged_pool(kc)[perm.cuda()], paged_pool(vc)[perm.cuda()]
+    table = torch.empty(n_pages, dtype=torch.int32)
+    table[perm] = torch.arange(n_pages, dtype=torch.int32)
+    table = table[None].cuda()
+    pfn = lambda: bfl.decode_paged(qdc, kpg, vpg, table, [N], dcfg["w0"], dcfg["w_pre"],
+                                   dcfg["theta"], "fi", scale, out=od, workspace=ws_d)
+    for _ in range(10):
+        pfn()
+    paged_ms = time_calls(pfn, 50, stream)
+    del kpg, vpg
+
     MALL = 256 * 1024 * 1024
     dec_cold_us = cold_us(qdc, kc, vc, N, ws_d, max(2, math.ceil(2 * MALL / kv_bytes)))
     small = {}
@@ -423,6 +443,7 @@ def main():
         "decode_frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
         "decode_us_50_calls": round(dec_many_ms * 1e3, 2),
         "decode_cold_us": round(dec_cold_us, 2),
+        "decode_paged16_us": round(paged_ms * 1e3, 2),
         "decode_cold_gbs": round(kv_bytes / (dec_cold_us * 1e-6) / 1e9, 1),
         "plain_decode_us": round(plain_dec_ms * 1e3, 2),
         "decode_overhead_vs_plain": round(dec_many_ms / plain_dec_ms - 1, 4),

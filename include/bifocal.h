@@ -141,6 +141,30 @@ int bifocal_decode(const void* q, const void* k_cache, const void* v_cache, void
                    float softmax_scale, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * bifocal_decode over a PAGED KV cache: the same computation and arguments as
+ * bifocal_decode, with the cache split into fixed-size pages.
+ *   k_pages, v_pages : [num_pages, n_heads_kv, page_size, head_dim] bf16
+ *   block_table      : DEVICE int32 [batch, max_pages_per_seq]; keys
+ *                      p * page_size .. (p + 1) * page_size - 1 of sequence b
+ *                      are in page block_table[b][p] (entries are clamped to
+ *                      [0, num_pages - 1]; only the pages that hold keys the
+ *                      call reads need valid entries)
+ *   page_size        : a power of two, 16 <= page_size <= 2^20
+ *   seqlens_host     : as bifocal_decode, 1 <= N_b <= max_pages_per_seq *
+ *                      page_size
+ * The workspace is bifocal_workspace_bytes(BF_PHASE_DECODE, ...) as for the
+ * contiguous call, and the result is bitwise the same as bifocal_decode on a
+ * contiguous cache holding the same keys.
+ */
+int bifocal_decode_paged(const void* q, const void* k_pages, const void* v_pages, void* o,
+                         float* lse, const int32_t* block_table, const int32_t* seqlens_host,
+                         int32_t batch, int32_t page_size, int32_t max_pages_per_seq,
+                         int32_t num_pages, int32_t n_heads_q, int32_t n_heads_kv,
+                         int32_t head_dim, int32_t dtype, int64_t w0, int64_t w_pre,
+                         double rope_theta, int32_t long_mode, float softmax_scale,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Plain causal softmax attention on the same (original-RoPE) q and k, run by
  * the same engine with the bifocal features compiled out: the reference for
  * the bifocal overhead and for the s = 1 identity.

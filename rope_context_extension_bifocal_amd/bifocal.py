@@ -25,7 +25,7 @@ LONG_MODES = {"fi": BF_LONG_FI, "pa": BF_LONG_PA, "band": BF_LONG_NONE,
 _DTYPES = {torch.bfloat16: BF_DTYPE_BF16, torch.float32: BF_DTYPE_FP32}
 
 EXPORTED = ("bifocal_s_of_L", "bifocal_workspace_bytes", "bifocal_prefill", "bifocal_decode",
-            "plain_attention_ref_gpu", "bifocal_rope_prefill", "bifocal_rope_append",
+            "bifocal_decode_paged", "plain_attention_ref_gpu", "bifocal_rope_prefill", "bifocal_rope_append",
             "bifocal_test_pair_map", "bifocal_last_error")
 
 _lib = None
@@ -57,6 +57,9 @@ def lib():
         L.bifocal_decode.restype = ctypes.c_int
         L.bifocal_decode.argtypes = [p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, i64, i64,
                                      f64, i32, f32, p, sz, p]
+        L.bifocal_decode_paged.restype = ctypes.c_int
+        L.bifocal_decode_paged.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, i32,
+                                           i32, i64, i64, f64, i32, f32, p, sz, p]
         L.plain_attention_ref_gpu.restype = ctypes.c_int
         L.plain_attention_ref_gpu.argtypes = [i32, p, p, p, p, p, p, i32, i32, i32, i32, i32,
                                               i32, f32, p, sz, p]
@@ -172,6 +175,30 @@ def decode(q, k_cache, v_cache, seqlens, w0, w_pre, rope_theta, long_mode="fi",
                                 float(rope_theta), LONG_MODES[long_mode],
                                 _scale(softmax_scale, D), _ptr(workspace), workspace.numel(),
                                 _stream(stream)))
+    return (o, lse) if return_lse else o
+
+
+def decode_paged(q, k_pages, v_pages, block_table, seqlens, w0, w_pre, rope_theta, long_mode="fi",
+                 softmax_scale=None, return_lse=False, out=None, lse=None, workspace=None,
+                 stream=None):
+    """Bifocal decode over a paged cache: pages [num_pages,Hkv,page,D] bf16,
+    block_table a device int32 tensor [B,max_pages]."""
+    B, Hq, D = q.shape
+    num_pages, Hkv, page = k_pages.shape[0], k_pages.shape[1], k_pages.shape[2]
+    o = out if out is not None else torch.empty_like(q)
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = alloc_workspace(workspace_bytes(BF_PHASE_DECODE, B, max(seqlens), Hq, Hkv, D,
+                                                    q.dtype), q.device)
+    assert block_table.dtype == torch.int32 and block_table.is_contiguous()
+    sl = _i32_array(seqlens)
+    _check(lib().bifocal_decode_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(o), _ptr(lse),
+                                      _ptr(block_table), sl, B, page, block_table.shape[1],
+                                      num_pages, Hq, Hkv, D, _DTYPES[q.dtype], int(w0), int(w_pre),
+                                      float(rope_theta), LONG_MODES[long_mode],
+                                      _scale(softmax_scale, D), _ptr(workspace), workspace.numel(),
+                                      _stream(stream)))
     return (o, lse) if return_lse else o
 
 

@@ -26,10 +26,16 @@ hipError_t launch_prefill_main(int dtype, bool bifocal, bool band, const Prefill
 hipError_t launch_pair_map(long long L, long long w0, long long s, int mode, int8_t* br,
                            long long* dphi_num, long long* s_out, hipStream_t stream);
 size_t decode_workspace_bytes(int batch, long long max_len, int Hq);
+struct PagedCache {
+  const int* block_table;
+  int page_size;
+  int max_pages;
+  int num_pages;
+};
 int run_decode(bool bifocal, const void* q, const void* kc, const void* vc, void* o, float* lse,
                const int32_t* seqlens, int batch, int cap, int Hq, int Hkv, long long w0,
                long long w_pre, double theta, int mode, float scale, void* ws, size_t ws_bytes,
-               hipStream_t stream, std::string& err, long long window = 0);
+               hipStream_t stream, std::string& err, long long window, const PagedCache* paged);
 int run_rope_prefill(const void* q, const void* k, const void* v, void* q_out, void* k_out,
                      void* k_cache, void* v_cache, int cap, const int32_t* cu, int batch, int Hq,
                      int Hkv, int dtype, double theta, hipStream_t stream, std::string& err);
@@ -287,7 +293,29 @@ int bifocal_decode(const void* q, const void* k_cache, const void* v_cache, void
   const bool band_only = long_mode == BF_LONG_NONE;
   rc = bf::run_decode(!band_only, q, k_cache, v_cache, o, lse, seqlens_host, batch, cache_capacity,
                       n_heads_q, n_heads_kv, w0, w_pre, rope_theta, long_mode, softmax_scale,
-                      workspace, workspace_bytes, (hipStream_t)stream, err, band_only ? w0 : 0);
+                      workspace, workspace_bytes, (hipStream_t)stream, err, band_only ? w0 : 0, nullptr);
+  if (rc) return fail(rc, "%s", err.c_str());
+  g_err.clear();
+  return BF_OK;
+}
+
+int bifocal_decode_paged(const void* q, const void* k_pages, const void* v_pages, void* o,
+                         float* lse, const int32_t* block_table, const int32_t* seqlens_host,
+                         int32_t batch, int32_t page_size, int32_t max_pages_per_seq,
+                         int32_t num_pages, int32_t n_heads_q, int32_t n_heads_kv,
+                         int32_t head_dim, int32_t dtype, int64_t w0, int64_t w_pre,
+                         double rope_theta, int32_t long_mode, float softmax_scale,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_common(n_heads_q, n_heads_kv, head_dim, dtype);
+  if (rc) return rc;
+  if ((rc = check_bifocal_knobs(w0, w_pre, rope_theta, long_mode))) return rc;
+  if (dtype != BF_DTYPE_BF16) return fail(BF_ERR_UNSUPPORTED, "decode supports bf16 only");
+  const bf::PagedCache pc{block_table, page_size, max_pages_per_seq, num_pages};
+  std::string err;
+  const bool band_only = long_mode == BF_LONG_NONE;
+  rc = bf::run_decode(!band_only, q, k_pages, v_pages, o, lse, seqlens_host, batch, 1, n_heads_q,
+                      n_heads_kv, w0, w_pre, rope_theta, long_mode, softmax_scale, workspace,
+                      workspace_bytes, (hipStream_t)stream, err, band_only ? w0 : 0, &pc);
   if (rc) return fail(rc, "%s", err.c_str());
   g_err.clear();
   return BF_OK;
@@ -309,7 +337,7 @@ int plain_attention_ref_gpu(int32_t phase, const void* q, const void* k, const v
   std::string err;
   rc = bf::run_decode(false, q, k, v, o, lse, lens_host, batch, cache_capacity, n_heads_q,
                       n_heads_kv, 0, 1, 10000.0, 0, softmax_scale, workspace, workspace_bytes,
-                      (hipStream_t)stream, err);
+                      (hipStream_t)stream, err, 0, nullptr);
   if (rc) return fail(rc, "%s", err.c_str());
   g_err.clear();
   return BF_OK;

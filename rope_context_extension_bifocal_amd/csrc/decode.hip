@@ -31,8 +31,9 @@ constexpr int kDecMaxG = 16;     // query heads per KV head the kernel supports
 
 struct DecodeParams {
   const uint16_t* q;    // [B][Hq][D]
-  const uint16_t* kc;   // [B][Hkv][cap][D]
-  const uint16_t* vc;   // [B][Hkv][cap][D]
+  const uint16_t* kc;   // [B][Hkv][cap][D], or pages [num_pages][Hkv][page][D]
+  const uint16_t* vc;   // same layout as kc
+  const int* block_table;  // paged cache: [B][max_pages] page of each page-sized key block
   float* part_m;        // [B][Hq][S]  running max (log2 domain, scaled)
   float* part_l;        // [B][Hq][S]
   float* part_acc;      // [B][Hq][S][D]
@@ -44,6 +45,9 @@ struct DecodeParams {
   int Hq, Hkv, G, S;
   int mode;   // 0 = FI, 1 = PA
   int shift;  // 1: the query gets the band-edge continuity shift w0 - phi(w0)
+  int max_pages;  // paged cache: row length of block_table
+  int num_pages;  // paged cache: pages in the pool (page numbers are clamped below it)
+  int page_log2;  // paged cache: log2 of the page size (keys per page, >= 16)
 };
 
 struct DecodeSeqs {
@@ -52,7 +56,8 @@ struct DecodeSeqs {
   int s[kMaxSeqPerLaunch];       // s(N)
   int nsplit[kMaxSeqPerLaunch];
   int chunk[kMaxSeqPerLaunch];   // keys per split (multiple of 64)
-  int kstart[kMaxSeqPerLaunch];  // first key read: 0, or N - w0 for band-only attention
+  int kstart[kMaxSeqPerLaunch];  // first key read, a multiple of 16 (steps never cross a page)
+  int kmin[kMaxSeqPerLaunch];    // first key that counts: 0, or N - w0 for band-only attention
 };
 
 __device__ __forceinline__ float dbf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
@@ -154,7 +159,7 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <bool BIFOCAL>
+template <bool BIFOCAL, bool PAGED>
 __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p, DecodeSeqs ds,
                                                               ThetaTable tt) {
   __shared__ uint4 smem[kDecLds / 16];
@@ -179,34 +184,66 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p, De
   const int ns = kw1 > kw0 ? (int)((kw1 - kw0 + kDecStep - 1) / kDecStep) : 0;
   const bool split_far = BIFOCAL && k_begin < far_lim;
 
-  const uint16_t* kbase = p.kc + ((size_t)b * p.Hkv + kvh) * (size_t)p.cap * kHeadDim;
-  const uint16_t* vbase = p.vc + ((size_t)b * p.Hkv + kvh) * (size_t)p.cap * kHeadDim;
   // wave-local key indexing: key kw0 + jl, jl in [0, nl); byte offsets fit 32 bits
   const int nl = ns > 0 ? (int)(kw1 - kw0) : 0;
   const int far_l = (int)max(-1LL, min(far_lim - kw0, (long long)(per + kDecStep)));
-  const char* kwb = dscalar_ptr(kbase + (size_t)(ns > 0 ? kw0 : 0) * kHeadDim);
-  const char* vwb = dscalar_ptr(vbase + (size_t)(ns > 0 ? kw0 : 0) * kHeadDim);
+  // keys below kmin (the band-only window start, rounded down to kstart) are masked
+  const int lo_l = (int)max(0LL, min((long long)ds.kmin[b] - kw0, (long long)(per + kDecStep)));
+  const char* kwb;
+  const char* vwb;
+  int first_page = 0, pg = 0;
+  if constexpr (!PAGED) {
+    const uint16_t* kbase = p.kc + ((size_t)b * p.Hkv + kvh) * (size_t)p.cap * kHeadDim;
+    const uint16_t* vbase = p.vc + ((size_t)b * p.Hkv + kvh) * (size_t)p.cap * kHeadDim;
+    kwb = dscalar_ptr(kbase + (size_t)(ns > 0 ? kw0 : 0) * kHeadDim);
+    vwb = dscalar_ptr(vbase + (size_t)(ns > 0 ? kw0 : 0) * kHeadDim);
+  } else {
+    // the pages this wave's keys live in, one per lane (a wave spans at most
+    // per / 16 + 1 <= 33 pages), read once; each step picks its page by lane
+    kwb = dscalar_ptr(p.kc);
+    vwb = dscalar_ptr(p.vc);
+    if (ns > 0) {
+      first_page = (int)(kw0 >> p.page_log2);
+      const int last_page = (int)((kw1 - 1) >> p.page_log2);
+      if (first_page + lane <= last_page)
+        pg = min(max(p.block_table[(size_t)b * p.max_pages + first_page + lane], 0), p.num_pages - 1);
+    }
+  }
   const uint32_t v_lane = (uint32_t)(g4 * 4 * 256 + n16 * 16);  // key 4 g4, chunk n16
   const uint32_t k_lane = (uint32_t)(n16 * 256 + g4 * 16);      // key n16, chunk g4
   uint4 kreg[kDecRing][4], vreg[kDecRing][4];
   // issue the loads of step st into register slot r, K first (needed first);
-  // rows past the wave's last key re-read that key (their scores are masked)
+  // rows past the wave's last key re-read that key (their scores are masked).
+  // Keys are addressed from kb / vb: the wave's first key (contiguous cache)
+  // or the first key of the step's page block (paged cache, rel0 = 0).
   auto issue = [&](int st, int r) {
     const int j0 = st * kDecStep;
+    const char* kb = kwb;
+    const char* vb = vwb;
+    int rel0 = j0;
+    if constexpr (PAGED) {
+      const long long key = kw0 + j0;  // a step never crosses a page (16 | page size)
+      const int page = __builtin_amdgcn_readlane(pg, (int)(key >> p.page_log2) - first_page);
+      const size_t row = (((size_t)page * p.Hkv + kvh) << p.page_log2) +
+                         (size_t)(key & ((1LL << p.page_log2) - 1));
+      kb = dscalar_ptr((const char*)p.kc + row * (kHeadDim * 2));
+      vb = dscalar_ptr((const char*)p.vc + row * (kHeadDim * 2));
+      rel0 = 0;
+    }
     if (j0 + kDecStep <= nl) {
-      const uint32_t base = (uint32_t)j0 * (kHeadDim * 2);
+      const uint32_t base = (uint32_t)rel0 * (kHeadDim * 2);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) kreg[r][t] = gload16(kwb, base + k_lane + t * 64);
+      for (int t = 0; t < 4; ++t) kreg[r][t] = gload16(kb, base + k_lane + t * 64);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) vreg[r][q] = gload16(vwb, base + v_lane + q * 256);
+      for (int q = 0; q < 4; ++q) vreg[r][q] = gload16(vb, base + v_lane + q * 256);
     } else {
-      const uint32_t kk = (uint32_t)min(j0 + n16, nl - 1);
+      const uint32_t kk = (uint32_t)(min(j0 + n16, nl - 1) - j0 + rel0);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) kreg[r][t] = gload16(kwb, kk * (kHeadDim * 2) + (4 * t + g4) * 16);
+      for (int t = 0; t < 4; ++t) kreg[r][t] = gload16(kb, kk * (kHeadDim * 2) + (4 * t + g4) * 16);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const uint32_t kv = (uint32_t)min(j0 + 4 * g4 + q, nl - 1);
-        vreg[r][q] = gload16(vwb, kv * (kHeadDim * 2) + n16 * 16);
+        const uint32_t kv = (uint32_t)(min(j0 + 4 * g4 + q, nl - 1) - j0 + rel0);
+        vreg[r][q] = gload16(vb, kv * (kHeadDim * 2) + n16 * 16);
       }
     }
   };
@@ -353,6 +390,11 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p, De
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         if (jbl + 4 * g4 + q >= nl) S[q] = -INFINITY;
+    }
+    if (jbl < lo_l) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (jbl + 4 * g4 + q < lo_l) S[q] = -INFINITY;
     }
     // lazy rescale: the reference max of a query moves only when one of its
     // scores exceeds it by more than 2^8; the column max is needed only then
@@ -608,12 +650,37 @@ size_t decode_workspace_bytes(int batch, long long max_len, int Hq) {
   return decode_ws_layout(batch, max_len, Hq).total;
 }
 
+// A paged cache: pages [num_pages][Hkv][page_size][D]; sequence b's keys
+// p * page_size .. (p + 1) * page_size - 1 live in page block_table[b][p].
+struct PagedCache {
+  const int* block_table;  // device [batch][max_pages], or null: contiguous cache
+  int page_size;           // keys per page: a power of two >= 16
+  int max_pages;           // row length of block_table
+  int num_pages;           // pages in the pool
+};
+static_assert(BF_DEC_MAX_CHUNK / kDecWaves / kDecStep + 1 <= 64,
+              "a wave's keys must span at most 64 pages of 16 keys");
+
 int run_decode(bool bifocal, const void* q, const void* kc, const void* vc, void* o, float* lse,
                const int32_t* seqlens, int batch, int cap, int Hq, int Hkv, long long w0,
                long long w_pre, double theta, int mode, float scale, void* ws, size_t ws_bytes,
-               hipStream_t stream, std::string& err, long long window) {
+               hipStream_t stream, std::string& err, long long window, const PagedCache* paged) {
   auto bad = [&](int code, const std::string& m) { err = m; return code; };
   if (!q || !kc || !vc || !o || !seqlens) return bad(BF_ERR_INVALID_ARG, "null tensor or seqlens pointer");
+  int page_log2 = 0;
+  if (paged) {
+    if (!paged->block_table || ((uintptr_t)paged->block_table & 3u))
+      return bad(BF_ERR_INVALID_ARG, "block_table must be a non-null 4-byte aligned device pointer");
+    const int ps = paged->page_size;
+    if (ps < kDecStep || (ps & (ps - 1)) != 0 || ps > (1 << 20))
+      return bad(BF_ERR_INVALID_ARG, "page_size must be a power of two in [16, 2^20] (got " + std::to_string(ps) + ")");
+    while ((1 << page_log2) < ps) ++page_log2;
+    if (paged->max_pages < 1 || paged->num_pages < 1)
+      return bad(BF_ERR_INVALID_ARG, "max_pages_per_seq and num_pages must be >= 1");
+    if ((long long)paged->max_pages * ps > 0x7fffffffLL)
+      return bad(BF_ERR_INVALID_ARG, "max_pages_per_seq x page_size exceeds 2^31 - 1 keys");
+    cap = paged->max_pages * ps;  // keys a sequence can hold
+  }
   if (batch < 1 || cap < 1) return bad(BF_ERR_INVALID_ARG, "batch and cache_capacity must be >= 1");
   if (!(scale > 0.f) || !(scale < 1e30f)) return bad(BF_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
   const int G = Hq / Hkv;
@@ -650,6 +717,10 @@ int run_decode(bool bifocal, const void* q, const void* kc, const void* vc, void
   dp.Hkv = Hkv;
   dp.G = G;
   dp.S = decode_split_bound(max_len);
+  dp.block_table = paged ? paged->block_table : nullptr;
+  dp.max_pages = paged ? paged->max_pages : 0;
+  dp.num_pages = paged ? paged->num_pages : 0;
+  dp.page_log2 = page_log2;
   dp.shift = (mode & BF_LONG_SHIFT) ? 1 : 0;
   dp.mode = mode & ~BF_LONG_SHIFT;
   for (int b0 = 0; b0 < batch; b0 += kMaxSeqPerLaunch) {
@@ -664,16 +735,22 @@ int run_decode(bool bifocal, const void* q, const void* kc, const void* vc, void
       long long s = 1;
       if (bifocal) s = N / w_pre + (N % w_pre != 0 ? 1 : 0);
       ds.s[i] = (int)(s < 1 ? 1 : s);
-      // a window (band-only attention) reads keys N - window .. N - 1 only
-      const long long k0 = window > 0 && N > window ? N - window : 0;
+      // a window (band-only attention) reads keys N - window .. N - 1 only,
+      // from the multiple of 16 at or below N - window on (the rest masked)
+      const long long kmin = window > 0 && N > window ? N - window : 0;
+      const long long k0 = kmin & ~15LL;
+      ds.kmin[i] = (int)kmin;
       ds.kstart[i] = (int)k0;
       ds.chunk[i] = decode_chunk(N - k0, target);
       ds.nsplit[i] = decode_splits(N - k0, target);
       if (ds.nsplit[i] > max_split) max_split = ds.nsplit[i];
     }
     dp.q = (const uint16_t*)q + (size_t)b0 * Hq * kHeadDim;
-    dp.kc = (const uint16_t*)kc + (size_t)b0 * Hkv * cap * kHeadDim;
-    dp.vc = (const uint16_t*)vc + (size_t)b0 * Hkv * cap * kHeadDim;
+    // contiguous: the launch's first sequence; paged: the page pool, rows of
+    // the block table from the launch's first sequence on
+    dp.kc = (const uint16_t*)kc + (paged ? 0 : (size_t)b0 * Hkv * cap * kHeadDim);
+    dp.vc = (const uint16_t*)vc + (paged ? 0 : (size_t)b0 * Hkv * cap * kHeadDim);
+    if (paged) dp.block_table = paged->block_table + (size_t)b0 * paged->max_pages;
     dp.o = (uint16_t*)o + (size_t)b0 * Hq * kHeadDim;
     dp.lse = lse ? lse + (size_t)b0 * Hq : nullptr;
     dp.part_m = (float*)(wsb + wl.m_off) + (size_t)b0 * Hq * dp.S;
@@ -683,10 +760,14 @@ int run_decode(bool bifocal, const void* q, const void* kc, const void* vc, void
       fprintf(stderr, "[bifocal] decode %s seqs=%d..%d N0=%d s0=%d splits=%d chunk=%d\n",
               bifocal ? "bifocal" : "plain", b0, b0 + nb - 1, ds.N[0], ds.s[0], ds.nsplit[0], ds.chunk[0]);
     dim3 grid(max_split, Hkv, nb);
-    if (bifocal)
-      hipLaunchKernelGGL(decode_split_kernel<true>, grid, dim3(256), 0, stream, dp, ds, tt);
+    if (bifocal && paged)
+      hipLaunchKernelGGL((decode_split_kernel<true, true>), grid, dim3(256), 0, stream, dp, ds, tt);
+    else if (bifocal)
+      hipLaunchKernelGGL((decode_split_kernel<true, false>), grid, dim3(256), 0, stream, dp, ds, tt);
+    else if (paged)
+      hipLaunchKernelGGL((decode_split_kernel<false, true>), grid, dim3(256), 0, stream, dp, ds, tt);
     else
-      hipLaunchKernelGGL(decode_split_kernel<false>, grid, dim3(256), 0, stream, dp, ds, tt);
+      hipLaunchKernelGGL((decode_split_kernel<false, false>), grid, dim3(256), 0, stream, dp, ds, tt);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return bad(BF_ERR_HIP, std::string("decode split launch: ") + hipGetErrorString(e));
     hipLaunchKernelGGL(decode_combine_kernel, dim3(Hq, nb, kHeadDim / 32), dim3(256), 0, stream, dp, ds);

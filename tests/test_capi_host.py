@@ -185,3 +185,30 @@ def test_rope_valid_arguments_reach_the_launch(L, monkeypatch):
     assert _rope_prefill(L) == bfl.BF_ERR_HIP
     assert _rope_prefill(L, ko=None, kc=P, vc=P, v=P, cap=100, dtype=1) == bfl.BF_ERR_HIP
     assert _rope_append(L) == bfl.BF_ERR_HIP
+
+
+def _decode_paged(L, **kw):
+    a = dict(q=P, kp=P, vp=P, o=P, lse=None, bt=P, sl=[100, 7], page=16, maxp=8, npages=20, Hq=4,
+             Hkv=2, D=128, dtype=0, w0=16, w_pre=64, theta=1e4, mode=0, scale=0.088, ws=P,
+             ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    sl = (ctypes.c_int32 * len(a["sl"]))(*a["sl"])
+    return L.bifocal_decode_paged(a["q"], a["kp"], a["vp"], a["o"], a["lse"], a["bt"], sl,
+                                  len(a["sl"]), a["page"], a["maxp"], a["npages"], a["Hq"],
+                                  a["Hkv"], a["D"], a["dtype"], a["w0"], a["w_pre"], a["theta"],
+                                  a["mode"], a["scale"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(bt=None), -1), (dict(bt=ctypes.c_void_p(0x100002)), -1), (dict(page=24), -1),
+    (dict(page=8), -1), (dict(maxp=0), -1), (dict(npages=0), -1), (dict(sl=[129]), -1),
+    (dict(sl=[0]), -1), (dict(dtype=1), -2), (dict(mode=9), -1), (dict(ws_bytes=10), -3),
+])
+def test_decode_paged_validation(L, kw, code):
+    assert _decode_paged(L, **kw) == code
+
+
+def test_decode_paged_valid_arguments_reach_the_launch(L, monkeypatch):
+    monkeypatch.setenv("BIFOCAL_TEST_FAIL_LAUNCH", "1")
+    assert _decode_paged(L) == bfl.BF_ERR_HIP
+    assert _decode_paged(L, mode=2, page=64, maxp=2) == bfl.BF_ERR_HIP
