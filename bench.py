@@ -12,7 +12,8 @@ Prints one JSON line. `value` is the prefill effective TFLOP/s: algorithmic
 flops 4 * D * Hq * L (L + 1) / 2 (one score and one PV product per causal
 pair) over the measured prefill time. Extra fields report the decode
 bandwidth, position aliasing, the library's plain causal attention on the
-same shapes (overhead reference), roofline fractions against MI355X peaks
+same shapes (overhead reference), chunks of the last 4096 / 16384 queries
+against the 128K cache, roofline fractions against MI355X peaks
 (bf16 dense MFMA 2.5 PFLOP/s, HBM 8 TB/s) and the fp64 CPU oracle timed on a
 bounded row sample of the prefill workload.
 """
@@ -380,6 +381,21 @@ def main():
     ragged_flops = 4.0 * D * rcfg["Hq"] * sum(x * (x + 1) / 2 for x in rlens)
     del rq, rk, rv, ro, rws
 
+    log("chunked prefill: the last 4096 / 16384 queries against the 128K cache")
+    kcc, vcc = kd.unsqueeze(0), vd.unsqueeze(0)  # [1, Hkv, L, D]: the cache layout, cap = L
+    chunk = {}
+    for lq in (4096, 16384):
+        qch = qd[:, L - lq:].contiguous()
+        och = torch.empty_like(qch)
+        wsc = bfl.alloc_workspace(bfl.chunk_workspace_bytes(1, lq, L, Hq, Hkv), "cuda")
+        cfn = lambda: bfl.prefill_chunk(qch, kcc, vcc, [0, lq], [L], cfg["w0"], cfg["w_pre"],
+                                        cfg["theta"], "fi", scale, out=och, workspace=wsc)
+        cfn()
+        c_ms = time_calls(cfn, 5, stream)
+        c_flops = 4.0 * D * Hq * (lq * L - lq * (lq - 1) / 2)  # positions L - lq .. L - 1
+        chunk[str(lq)] = {"ms": round(c_ms, 3), "tflops": round(c_flops / (c_ms * 1e-3) / 1e12, 2)}
+        del qch, och, wsc
+
     log("raw-input pre-step")
     qr, kr = qd.clone(), kd.clone()
     rope_pre()
@@ -454,6 +470,7 @@ def main():
                       "decode_gbs": round(band_dec_bytes / (band_dec_ms * 1e-3) / 1e9, 1)},
         "ragged_prefill": {"lengths": rlens, "ms": round(ragged_ms, 3),
                            "tflops": round(ragged_flops / (ragged_ms * 1e-3) / 1e12, 2)},
+        "chunk_prefill_at_128k": chunk,
         "rope_prefill_ms": round(rope_ms, 4),
         "rope_prefill_gbs": round(rope_gbs, 1),
         "rope_prefill_cache_ms": round(rope_c_ms, 4),

@@ -120,6 +120,51 @@ int bifocal_prefill(const void* q, const void* k, const void* v, void* o, float*
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Workspace bytes of bifocal_prefill_chunk: q_tokens = cu_q[batch] (the
+ * packed queries), kv_tokens = the sum of seqlens[b] (the keys the call
+ * reads). Returns 0 for invalid arguments (also kv_tokens < q_tokens).
+ */
+size_t bifocal_chunk_workspace_bytes(int32_t batch, int64_t q_tokens, int64_t kv_tokens,
+                                     int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim,
+                                     int32_t dtype);
+
+/*
+ * Multi-token queries against a KV cache (chunked prefill, a prompt suffix
+ * after a cached prefix, speculative verification): the queries of sequence b
+ * are its LAST Lq_b positions, N_b - Lq_b .. N_b - 1, and attend causally
+ * (bottom-right aligned) to the N_b keys in the cache, the chunk's own keys
+ * included (append them first, e.g. with bifocal_rope_prefill). Each row is
+ * the bifocal_prefill row at its position, with s = s(s_len_host[b]) (or
+ * s(N_b) when s_len_host is NULL: the length seen so far, as decode does).
+ *   q, o             : [n_heads_q, Tq, head_dim] dtype, packed as in
+ *                      bifocal_prefill, Tq = cu_q_host[batch]
+ *   k_cache, v_cache : [batch, n_heads_kv, cache_capacity, head_dim] dtype,
+ *                      ORIGINAL RoPE at their positions; entries past N_b
+ *                      are never used
+ *   lse              : [n_heads_q, Tq] fp32 or NULL
+ *   cu_q_host        : host int32 [batch + 1], cu_q[0] = 0, strictly
+ *                      increasing (Lq_b = cu_q[b+1] - cu_q[b] >= 1)
+ *   seqlens_host     : host int32 [batch], Lq_b <= N_b <= cache_capacity
+ *   s_len_host       : host int32 [batch] or NULL; s_len[b] >= N_b (pass
+ *                      the full prompt length to reproduce a one-shot
+ *                      bifocal_prefill of that prompt chunk by chunk)
+ *   workspace        : bifocal_chunk_workspace_bytes(batch, Tq, sum N_b, ...)
+ * Other arguments as bifocal_prefill (bf16 or fp32; every long_mode).
+ * With Lq_b = N_b and s_len = NULL this is bifocal_prefill of the cached
+ * sequences; with Lq_b = 1 it is bifocal_decode.
+ * [mufans.github.io wiki, Jet-Long Dynamic RoPE, "可执行建议": pairing the
+ *  method with prompt caching; ai-feeds.com summary, "关键模块" item 3: the
+ *  correction rotation applied to cached keys]
+ */
+int bifocal_prefill_chunk(const void* q, const void* k_cache, const void* v_cache, void* o,
+                          float* lse, const int32_t* cu_q_host, const int32_t* seqlens_host,
+                          const int32_t* s_len_host, int32_t batch, int32_t cache_capacity,
+                          int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim, int32_t dtype,
+                          int64_t w0, int64_t w_pre, double rope_theta, int32_t long_mode,
+                          float softmax_scale, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/*
  * Single-token bifocal decode over a KV cache (bf16 only).
  *   q, o             : [batch, n_heads_q, head_dim] bf16
  *   k_cache, v_cache : [batch, n_heads_kv, cache_capacity, head_dim] bf16,

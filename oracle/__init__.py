@@ -37,6 +37,9 @@ def _load():
         lib.oracle_prefill_rows.restype = ctypes.c_int
         lib.oracle_prefill_rows.argtypes = [p, p, p, p, i64, p, i64, i64, i64, i64, i64, i64,
                                             f64, i32, f64, i32, p, p]
+        lib.oracle_chunk_rows.restype = ctypes.c_int
+        lib.oracle_chunk_rows.argtypes = [p, p, p, p, p, p, i64, i64, p, i64, i64, i64, i64, i64,
+                                          i64, f64, i32, f64, p, p]
         lib.oracle_decode.restype = ctypes.c_int
         lib.oracle_decode.argtypes = [p, p, p, p, i64, i64, i64, i64, i64, i64, i64, f64, i32,
                                       f64, p, p]
@@ -142,6 +145,37 @@ def decode(q, k_cache, v_cache, seqlens, w0, w_pre, theta, mode, scale):
                                _ptr(o), _ptr(lse))
     if rc != 0:
         raise ValueError(f"oracle_decode failed: {rc}")
+    return o, lse
+
+
+def chunk(q, k_cache, v_cache, cu_q, seqlens, w0, w_pre, theta, mode, scale, s_len=None,
+          rows=None, gathered=False):
+    """Multi-token queries over a KV cache (chunked prefill).  q [Hq,Tq,D]
+    packed by cu_q (or [Hq,R,D] already gathered at `rows` when gathered=True),
+    caches [B,Hkv,cap,D] with seqlens[b] keys; the queries of b are its last
+    positions seqlens[b] - Lq_b .. seqlens[b] - 1, s = s(s_len[b]) (default
+    seqlens[b]).  Returns fp64 (o [Hq,R,D], lse [Hq,R])."""
+    k_cache = _f32(k_cache)
+    v_cache = _f32(v_cache)
+    q = np.asarray(q)
+    Hq, _, D = q.shape
+    B, Hkv, cap = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
+    cu = np.ascontiguousarray(np.asarray(cu_q, dtype=np.int64))
+    sl = np.ascontiguousarray(np.asarray(seqlens, dtype=np.int64))
+    sll = None if s_len is None else np.ascontiguousarray(np.asarray(s_len, dtype=np.int64))
+    if rows is None:
+        rows = np.arange(int(cu[-1]), dtype=np.int64)
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    q_rows = _f32(q) if gathered else _f32(q[:, rows, :])
+    R = rows.shape[0]
+    o = np.empty((Hq, R, D), dtype=np.float64)
+    lse = np.empty((Hq, R), dtype=np.float64)
+    rc = _load().oracle_chunk_rows(_ptr(q_rows), _ptr(k_cache), _ptr(v_cache), _ptr(cu), _ptr(sl),
+                                   _ptr(sll) if sll is not None else None, B, cap, _ptr(rows), R,
+                                   Hq, Hkv, D, int(w0), int(w_pre), float(theta), MODES[mode],
+                                   float(scale), _ptr(o), _ptr(lse))
+    if rc != 0:
+        raise ValueError(f"oracle_chunk_rows failed: {rc}")
     return o, lse
 
 

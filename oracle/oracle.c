@@ -400,6 +400,102 @@ int oracle_decode(const float* q, const float* k_cache, const float* v_cache,
     return err;
 }
 
+/* ------------------------------------------------------------------ */
+/* Multi-token queries over a KV cache (chunked prefill): sequence b holds
+ * N_b = seqlens[b] keys in the cache and its Lq_b = cu_q[b+1] - cu_q[b]
+ * queries are the last Lq_b positions N_b - Lq_b .. N_b - 1. A query at
+ * position i is the prefill row i of that sequence with L = s_len[b]
+ * (N_b when s_len is NULL), evaluated at the chosen packed query rows.
+ *   q_rows [Hq][n_rows][D]  query vectors of those rows (original RoPE)
+ *   k_cache, v_cache [B][Hkv][cap][D]
+ *   o [Hq][n_rows][D], lse [Hq][n_rows]
+ * [mufans.github.io wiki, Jet-Long Dynamic RoPE, "可执行建议": use with
+ *  prompt caching; ai-feeds.com summary, "关键模块" item 3: correction of
+ *  cached keys]                                                          */
+int oracle_chunk_rows(const float* q_rows, const float* k_cache, const float* v_cache,
+                      const int64_t* cu_q, const int64_t* seqlens, const int64_t* s_len,
+                      int64_t B, int64_t cap, const int64_t* rows, int64_t n_rows,
+                      int64_t Hq, int64_t Hkv, int64_t D, int64_t w0, int64_t w_pre,
+                      double theta_base, int32_t mode, double scale, double* o, double* lse)
+{
+    if (B < 1 || cap < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || D < 2 || D % 2 != 0 || D > 1024)
+        return ORC_BAD;
+    const int32_t shift_on = mode & 4;
+    mode &= ~4;
+    if (w0 < 0 || w_pre < 1 || mode < 0 || mode > 2 || (mode == 2 && (w0 < 1 || shift_on))) return ORC_BAD;
+    if (cu_q[0] != 0) return ORC_BAD;
+    for (int64_t b = 0; b < B; ++b) {
+        const int64_t Lq = cu_q[b + 1] - cu_q[b];
+        if (Lq < 1 || seqlens[b] < Lq || seqlens[b] > cap) return ORC_BAD;
+        if (s_len && s_len[b] < seqlens[b]) return ORC_BAD;
+    }
+    const int64_t G = Hq / Hkv;
+    /* keys each sequence needs: positions 0 .. largest requested position */
+    int64_t* need = (int64_t*)calloc((size_t)B, sizeof(int64_t));
+    int64_t* base = (int64_t*)calloc((size_t)B + 1, sizeof(int64_t));
+    if (!need || !base) { free(need); free(base); return ORC_NOMEM; }
+    for (int64_t r = 0; r < n_rows; ++r) {
+        const int64_t b = seq_of_token(cu_q, B, rows[r]);
+        if (b < 0) { free(need); free(base); return ORC_BAD; }
+        const int64_t i = seqlens[b] - (cu_q[b + 1] - cu_q[b]) + (rows[r] - cu_q[b]);
+        if (i + 1 > need[b]) need[b] = i + 1;
+    }
+    for (int64_t b = 0; b < B; ++b) base[b + 1] = base[b] + need[b];
+    const int64_t total = base[B];
+    const size_t nk = (size_t)Hkv * (size_t)total * (size_t)D;
+    double* ko = (double*)malloc((nk ? nk : 1) * sizeof(double));
+    double* kf = (double*)malloc((nk ? nk : 1) * sizeof(double));
+    double* vv = (double*)malloc((nk ? nk : 1) * sizeof(double));
+    if (!ko || !kf || !vv) { free(ko); free(kf); free(vv); free(need); free(base); return ORC_NOMEM; }
+    for (int64_t b = 0; b < B; ++b) {
+        if (!need[b]) continue;
+        const int64_t s = oracle_s_of_L(s_len ? s_len[b] : seqlens[b], w_pre);
+        #pragma omp parallel for collapse(2) schedule(static)
+        for (int64_t h = 0; h < Hkv; ++h)
+            for (int64_t p = 0; p < need[b]; ++p) {
+                double tmp[1024];
+                const size_t src = (((size_t)b * (size_t)Hkv + (size_t)h) * (size_t)cap + (size_t)p) * (size_t)D;
+                const size_t dst = ((size_t)h * (size_t)total + (size_t)(base[b] + p)) * (size_t)D;
+                for (int64_t d = 0; d < D; ++d) {
+                    ko[dst + d] = (double)k_cache[src + d];
+                    vv[dst + d] = (double)v_cache[src + d];
+                }
+                far_vector(ko + dst, kf + dst, D, p, s, mode, theta_base, tmp);
+            }
+    }
+    int64_t maxn = 0;
+    for (int64_t b = 0; b < B; ++b) if (need[b] > maxn) maxn = need[b];
+    int err = ORC_OK;
+    #pragma omp parallel
+    {
+        double* sb = (double*)malloc((size_t)(maxn + 1) * sizeof(double));
+        if (!sb) {
+            #pragma omp atomic write
+            err = ORC_NOMEM;
+        } else {
+            double qo[1024], qf[1024], tmp[1024];
+            #pragma omp for collapse(2) schedule(dynamic, 1)
+            for (int64_t h = 0; h < Hq; ++h)
+                for (int64_t r = 0; r < n_rows; ++r) {
+                    const int64_t b = seq_of_token(cu_q, B, rows[r]);
+                    const int64_t i = seqlens[b] - (cu_q[b + 1] - cu_q[b]) + (rows[r] - cu_q[b]);
+                    const int64_t s = oracle_s_of_L(s_len ? s_len[b] : seqlens[b], w_pre);
+                    const double shift = shift_on ? far_shift(w0, s, mode) : 0.0;
+                    const float* qs = q_rows + ((size_t)h * (size_t)n_rows + (size_t)r) * (size_t)D;
+                    for (int64_t d = 0; d < D; ++d) qo[d] = (double)qs[d];
+                    far_query(qo, qf, D, i, s, mode, shift, theta_base, tmp);
+                    const size_t kb = ((size_t)(h / G) * (size_t)total + (size_t)base[b]) * (size_t)D;
+                    one_row(qo, qf, ko + kb, kf + kb, vv + kb, i, D, w0, scale, mode == 2, sb,
+                            o + ((size_t)h * (size_t)n_rows + (size_t)r) * (size_t)D,
+                            lse + (size_t)h * (size_t)n_rows + (size_t)r);
+                }
+            free(sb);
+        }
+    }
+    free(ko); free(kf); free(vv); free(need); free(base);
+    return err;
+}
+
 /* Classification of one pair, for the integer pins: returns 1 for a local
  * pair (original RoPE), 2 for a far pair (scaled RoPE), 0 for a pair the
  * causal mask removes (j > i).                                           */

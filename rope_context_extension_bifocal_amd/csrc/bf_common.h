@@ -15,11 +15,21 @@ constexpr int kWaveRowsF32 = 32;  // query positions per wave, fp32 prefill
 constexpr int kWavesPerGroupBf16 = 4;  // waves per bf16 prefill workgroup (256 lanes)
 constexpr int kWavesPerGroupF32 = 4;   // waves per fp32 prefill workgroup (256 lanes)
 
-// Per-launch description of up to kMaxSeqPerLaunch packed sequences.
+// Per-launch description of up to kMaxSeqPerLaunch sequences. Queries are
+// packed along the T axis (q, o, lse, q''); keys are read from a K / V tensor
+// whose row of key j, KV head h, sequence b is h * k_hstride + kbase[b] + j
+// (a packed [Hkv][T][D] tensor: k_hstride = T, kbase = cu; a KV cache
+// [B][Hkv][cap][D]: k_hstride = cap, kbase = b * Hkv * cap). A one-shot
+// prefill has qpos = 0 and keys = queries; a chunk of queries against a cache
+// has its first query at position qpos = N - Lq.
 struct SeqTable {
   int n;                              // sequences in this launch
-  int cu[kMaxSeqPerLaunch + 1];       // token offsets into the packed T axis
+  int cu[kMaxSeqPerLaunch + 1];       // query token offsets into the packed T axis
+  int kcu[kMaxSeqPerLaunch + 1];      // key offsets into the packed k'' axis (Tk); keys of b: kcu[b+1]-kcu[b]
   int vt_off[kMaxSeqPerLaunch + 1];   // 64-aligned offsets into the padded V^T axis
+  int qpos[kMaxSeqPerLaunch];         // position of the sequence's first query row
+  int rboff[kMaxSeqPerLaunch];        // qpos / P_wg: heaviest-first rank offset of its row blocks
+  long long kbase[kMaxSeqPerLaunch];  // K / V row offset of the sequence's key 0
   int s[kMaxSeqPerLaunch];            // s(L_b) (1 = no far branch)
   int nrb[kMaxSeqPerLaunch];          // query row blocks of the sequence
 };
@@ -31,38 +41,42 @@ struct ThetaTable {
 
 struct PrefillParams {
   const void* q;    // [Hq][T][D]   original-RoPE queries
-  const void* k;    // [Hkv][T][D]  original-RoPE keys
+  const void* k;    // original-RoPE keys, rows h * k_hstride + kbase[b] + j
   const void* q2;   // [Hq][T][D]   corrected queries (far branch), workspace
-  const void* k2;   // [Hkv][T][D]  corrected keys (far branch), workspace
+  const void* k2;   // [Hkv][Tk][D] corrected keys (far branch), workspace
   const void* vt;   // [Hkv][D][Tpad] values, transposed and 64-padded per sequence
   void* o;          // [Hq][T][D]
   float* lse;       // [Hq][T] or null
   long long w0;     // local window (ignored by the plain engine)
   float scale_log2; // softmax_scale * log2(e)
-  int T, Tpad;
+  long long k_hstride;  // K rows between KV heads
+  long long k_rows;     // rows of the whole K tensor (range limit of the loads)
+  int T, Tk, Tpad;
   int Hq, Hkv, G;
   int hpw;          // query heads per workgroup
   int n_hsub;       // workgroups per (KV head, row block) = G / hpw
   int P_wg;         // query positions per workgroup
   int total_items;  // row blocks over all sequences of the launch
-  int max_nrb;
+  int max_nrb;      // 1 + the largest rank index rb + rboff[b]
 };
 
 struct PrepParams {
   const void* q;  // [Hq][T][D]
-  const void* k;  // [Hkv][T][D]
+  const void* k;  // rows h * k_hstride + kbase[b] + j
   void* q2;       // [Hq][T][D]
-  void* k2;       // [Hkv][T][D]
-  int T, Hq, Hkv;
+  void* k2;       // [Hkv][Tk][D]
+  long long k_hstride;
+  int T, Tk, Hq, Hkv;
   int long_mode;  // 0 = FI, 1 = PA
   int shift;      // 1: queries get the band-edge continuity shift w0 - phi(w0)
   long long w0;
 };
 
 struct VtParams {
-  const void* v;  // [Hkv][T][D]
+  const void* v;  // rows h * k_hstride + kbase[b] + j (the layout of K)
   void* vt;       // [Hkv][D][Tpad]
-  int T, Tpad, Hkv;
+  long long k_hstride;
+  int Tpad, Hkv;
 };
 
 }  // namespace bf

@@ -100,14 +100,16 @@ struct PrefillWs {
   size_t vt_off, q2_off, k2_off, total;
 };
 
-PrefillWs prefill_ws_layout(int batch, long long T, int Hq, int Hkv, int dtype) {
+// Workspace of Tq packed queries against Tk keys (a one-shot prefill has
+// Tq = Tk = T): V^T padded per sequence, q'' and k''.
+PrefillWs prefill_ws_layout(int batch, long long Tq, long long Tk, int Hq, int Hkv, int dtype) {
   const size_t es = elem_size(dtype);
-  const size_t tpad_bound = (size_t)T + 63u * (size_t)batch;
+  const size_t tpad_bound = (size_t)Tk + 63u * (size_t)batch;
   PrefillWs w;
   w.vt_off = 0;
   w.q2_off = align256((size_t)Hkv * bf::kHeadDim * tpad_bound * es);
-  w.k2_off = w.q2_off + align256((size_t)Hq * (size_t)T * bf::kHeadDim * es);
-  w.total = w.k2_off + align256((size_t)Hkv * (size_t)T * bf::kHeadDim * es);
+  w.k2_off = w.q2_off + align256((size_t)Hq * (size_t)Tq * bf::kHeadDim * es);
+  w.total = w.k2_off + align256((size_t)Hkv * (size_t)Tk * bf::kHeadDim * es);
   return w;
 }
 
@@ -142,47 +144,64 @@ int check_scale(float scale) {
   return BF_OK;
 }
 
-// Shared prefill path of bifocal_prefill and the plain reference.
-int run_prefill(bool bifocal, const void* q, const void* k, const void* v, void* o, float* lse,
-                const int32_t* cu, int batch, int Hq, int Hkv, int head_dim, int dtype,
-                long long w0, long long w_pre, double theta, int mode, float scale, void* ws,
-                size_t ws_bytes, hipStream_t stream) {
-  if (!q || !k || !v || !o || !cu) return fail(BF_ERR_INVALID_ARG, "null tensor or cu_seqlens pointer");
+// One launch description shared by the one-shot prefill and the chunk of
+// queries against a KV cache: sequence b has Lq_b = cu[b+1] - cu[b] packed
+// queries at positions qpos[b] .. qpos[b] + Lq_b - 1 and N_b = qpos[b] + Lq_b
+// keys at K / V rows h * k_hstride + kbase[b] + j; s comes from slen[b].
+struct RowsJob {
+  bool bifocal = false;
+  const void *q = nullptr, *k = nullptr, *v = nullptr;
+  void* o = nullptr;
+  float* lse = nullptr;
+  std::vector<int> cu, qpos;
+  std::vector<long long> kbase, slen;
+  long long k_hstride = 0, k_rows = 0;
+  int batch = 0, Hq = 0, Hkv = 0, dtype = 0;
+  long long w0 = 0, w_pre = 1;
+  double theta = 10000.0;
+  int mode = 0;
+  float scale = 1.f;
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  hipStream_t stream = nullptr;
+};
+
+// Validation of the arguments both paths share; tensors checked by the caller.
+int check_rows_common(bool bifocal, int batch, int Hq, int Hkv, int head_dim, int dtype,
+                      long long w0, long long w_pre, double theta, int mode, float scale) {
   if (batch < 1) return fail(BF_ERR_INVALID_ARG, "batch must be >= 1 (got %d)", batch);
   int rc = check_common(Hq, Hkv, head_dim, dtype);
   if (rc) return rc;
   if (bifocal && (rc = check_bifocal_knobs(w0, w_pre, theta, mode))) return rc;
-  if ((rc = check_scale(scale))) return rc;
-  if (cu[0] != 0) return fail(BF_ERR_INVALID_ARG, "cu_seqlens[0] must be 0 (got %d)", cu[0]);
-  for (int b = 0; b < batch; ++b)
-    if (cu[b + 1] <= cu[b])
-      return fail(BF_ERR_INVALID_ARG, "cu_seqlens must be strictly increasing (b=%d: %d -> %d)", b, cu[b], cu[b + 1]);
-  const long long T = cu[batch];
-  if (T + 63LL * batch > (1LL << 31) - 1) return fail(BF_ERR_INVALID_ARG, "too many tokens (%lld)", T);
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
-    return fail(BF_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned");
-  if (lse && ((uintptr_t)lse & 3u)) return fail(BF_ERR_INVALID_ARG, "lse must be 4-byte aligned");
-  const PrefillWs wl = prefill_ws_layout(batch, T, Hq, Hkv, dtype);
-  if (!ws) return fail(BF_ERR_WORKSPACE, "workspace is null");
-  if ((uintptr_t)ws & 255u) return fail(BF_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-  const bool shift = bifocal && (mode & BF_LONG_SHIFT);
-  mode &= ~BF_LONG_SHIFT;
+  return check_scale(scale);
+}
+
+int run_rows(RowsJob& j) {
+  const int batch = j.batch, Hq = j.Hq, Hkv = j.Hkv, dtype = j.dtype;
+  const bool bifocal = j.bifocal;
+  long long Tq = j.cu[batch], Tk = 0;
+  std::vector<int> kcu(batch + 1, 0), vt_off(batch + 1, 0);
+  for (int b = 0; b < batch; ++b) {
+    const long long N = (long long)j.qpos[b] + (j.cu[b + 1] - j.cu[b]);
+    kcu[b + 1] = (int)(kcu[b] + N);
+    vt_off[b + 1] = vt_off[b] + (int)((N + bf::kKeyTile - 1) / bf::kKeyTile) * bf::kKeyTile;
+  }
+  Tk = kcu[batch];
+  const PrefillWs wl = prefill_ws_layout(batch, Tq, Tk, Hq, Hkv, dtype);
+  if (!j.ws) return fail(BF_ERR_WORKSPACE, "workspace is null");
+  if ((uintptr_t)j.ws & 255u) return fail(BF_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  const bool shift = bifocal && (j.mode & BF_LONG_SHIFT);
+  const int mode = j.mode & ~BF_LONG_SHIFT;
   const bool band_only = bifocal && mode == BF_LONG_NONE;
   const size_t need = bifocal && !band_only ? wl.total : wl.q2_off;
-  if (ws_bytes < need)
-    return fail(BF_ERR_WORKSPACE, "workspace too small: %zu bytes given, %zu needed", ws_bytes, need);
+  if (j.ws_bytes < need)
+    return fail(BF_ERR_WORKSPACE, "workspace too small: %zu bytes given, %zu needed", j.ws_bytes, need);
 
   const int G = Hq / Hkv;
   const PrefillGeom geo = prefill_geom(dtype, G);
-  // padded V^T offsets over the whole batch
-  std::vector<int> vt_off(batch + 1, 0);
-  for (int b = 0; b < batch; ++b) {
-    const int L = cu[b + 1] - cu[b];
-    vt_off[b + 1] = vt_off[b] + ((L + bf::kKeyTile - 1) / bf::kKeyTile) * bf::kKeyTile;
-  }
   const int Tpad = vt_off[batch];
-  const bf::ThetaTable tt = theta_table(bifocal ? theta : 10000.0);
-  char* wsb = (char*)ws;
+  const bf::ThetaTable tt = theta_table(bifocal ? j.theta : 10000.0);
+  char* wsb = (char*)j.ws;
   if (forced_launch_failure()) return fail(BF_ERR_HIP, "launch failure forced by BIFOCAL_TEST_FAIL_LAUNCH");
 
   for (int b0 = 0; b0 < batch; b0 += bf::kMaxSeqPerLaunch) {
@@ -193,40 +212,50 @@ int run_prefill(bool bifocal, const void* q, const void* k, const void* v, void*
     bool any_far = false;
     int total_items = 0, max_nrb = 0;
     for (int i = 0; i <= nb; ++i) {
-      st.cu[i] = cu[b0 + i];
+      st.cu[i] = j.cu[b0 + i];
+      st.kcu[i] = kcu[b0 + i];
       st.vt_off[i] = vt_off[b0 + i];
     }
     for (int i = 0; i < nb; ++i) {
-      const long long L = cu[b0 + i + 1] - cu[b0 + i];
-      const long long s = bifocal && !band_only ? bifocal_s_of_L(L, w_pre) : 1;
-      if (s > (1LL << 30)) return fail(BF_ERR_INVALID_ARG, "s(L) too large");
+      const long long Lq = j.cu[b0 + i + 1] - j.cu[b0 + i];
+      const long long N = j.qpos[b0 + i] + Lq;
+      const long long s = bifocal && !band_only ? bifocal_s_of_L(j.slen[b0 + i], j.w_pre) : 1;
+      if (s < 1 || s > (1LL << 30)) return fail(BF_ERR_INVALID_ARG, "s(L) out of range");
       st.s[i] = (int)s;
-      // far pairs to score (bifocal) or to drop (band only)
-      if ((s > 1 || band_only) && w0 < L) any_far = true;
-      st.nrb[i] = (int)((L + geo.P_wg - 1) / geo.P_wg);
+      st.qpos[i] = j.qpos[b0 + i];
+      st.kbase[i] = j.kbase[b0 + i];
+      // far pairs to score (bifocal) or to drop (band only): the last query
+      // (position N - 1) reaches back past the window
+      if ((s > 1 || band_only) && j.w0 < N) any_far = true;
+      st.nrb[i] = (int)((Lq + geo.P_wg - 1) / geo.P_wg);
+      st.rboff[i] = st.qpos[i] / geo.P_wg;
       total_items += st.nrb[i];
-      max_nrb = std::max(max_nrb, st.nrb[i]);
+      max_nrb = std::max(max_nrb, st.nrb[i] + st.rboff[i]);
     }
     hipError_t e = hipSuccess;
-    bf::VtParams vp{v, wsb + wl.vt_off, (int)T, Tpad, Hkv};
-    e = bf::launch_vt_transpose(dtype, vp, st, stream);
+    bf::VtParams vp{j.v, wsb + wl.vt_off, j.k_hstride, Tpad, Hkv};
+    e = bf::launch_vt_transpose(dtype, vp, st, j.stream);
     if (e != hipSuccess) return fail(BF_ERR_HIP, "vt_transpose launch: %s", hipGetErrorString(e));
     if (bifocal && any_far && !band_only) {
-      bf::PrepParams pp{q, k, wsb + wl.q2_off, wsb + wl.k2_off, (int)T, Hq, Hkv, mode, shift ? 1 : 0, w0};
-      e = bf::launch_correction_prep(dtype, pp, st, tt, stream);
+      bf::PrepParams pp{j.q, j.k, wsb + wl.q2_off, wsb + wl.k2_off, j.k_hstride, (int)Tq, (int)Tk,
+                        Hq, Hkv, mode, shift ? 1 : 0, j.w0};
+      e = bf::launch_correction_prep(dtype, pp, st, tt, j.stream);
       if (e != hipSuccess) return fail(BF_ERR_HIP, "correction_prep launch: %s", hipGetErrorString(e));
     }
     bf::PrefillParams pp;
-    pp.q = q;
-    pp.k = k;
+    pp.q = j.q;
+    pp.k = j.k;
     pp.q2 = wsb + wl.q2_off;
     pp.k2 = wsb + wl.k2_off;
     pp.vt = wsb + wl.vt_off;
-    pp.o = o;
-    pp.lse = lse;
-    pp.w0 = w0;
-    pp.scale_log2 = scale * 1.4426950408889634f;
-    pp.T = (int)T;
+    pp.o = j.o;
+    pp.lse = j.lse;
+    pp.w0 = j.w0;
+    pp.scale_log2 = j.scale * 1.4426950408889634f;
+    pp.k_hstride = j.k_hstride;
+    pp.k_rows = j.k_rows;
+    pp.T = (int)Tq;
+    pp.Tk = (int)Tk;
     pp.Tpad = Tpad;
     pp.Hq = Hq;
     pp.Hkv = Hkv;
@@ -239,14 +268,99 @@ int run_prefill(bool bifocal, const void* q, const void* k, const void* v, void*
     const long long grid = (long long)Hkv * geo.n_hsub * total_items;
     if (grid > 0x7fffffffLL) return fail(BF_ERR_INVALID_ARG, "launch grid too large");
     if (trace_on())
-      fprintf(stderr, "[bifocal] prefill %s dtype=%d seqs=%d..%d grid=%lld P_wg=%d hpw=%d n_hsub=%d s0=%d w0=%lld\n",
+      fprintf(stderr, "[bifocal] prefill %s dtype=%d seqs=%d..%d grid=%lld P_wg=%d hpw=%d n_hsub=%d s0=%d qpos0=%d w0=%lld\n",
               band_only ? "band-only" : bifocal ? "bifocal" : "plain", dtype, b0, b0 + nb - 1, grid, geo.P_wg, geo.hpw,
-              geo.n_hsub, st.s[0], w0);
-    e = bf::launch_prefill_main(dtype, bifocal && any_far, band_only && any_far, pp, st, (int)grid, stream);
+              geo.n_hsub, st.s[0], st.qpos[0], j.w0);
+    e = bf::launch_prefill_main(dtype, bifocal && any_far, band_only && any_far, pp, st, (int)grid, j.stream);
     if (e != hipSuccess) return fail(BF_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
   }
   g_err.clear();
   return BF_OK;
+}
+
+// Shared prefill path of bifocal_prefill and the plain reference.
+int run_prefill(bool bifocal, const void* q, const void* k, const void* v, void* o, float* lse,
+                const int32_t* cu, int batch, int Hq, int Hkv, int head_dim, int dtype,
+                long long w0, long long w_pre, double theta, int mode, float scale, void* ws,
+                size_t ws_bytes, hipStream_t stream) {
+  if (!q || !k || !v || !o || !cu) return fail(BF_ERR_INVALID_ARG, "null tensor or cu_seqlens pointer");
+  int rc = check_rows_common(bifocal, batch, Hq, Hkv, head_dim, dtype, w0, w_pre, theta, mode, scale);
+  if (rc) return rc;
+  if (cu[0] != 0) return fail(BF_ERR_INVALID_ARG, "cu_seqlens[0] must be 0 (got %d)", cu[0]);
+  for (int b = 0; b < batch; ++b)
+    if (cu[b + 1] <= cu[b])
+      return fail(BF_ERR_INVALID_ARG, "cu_seqlens must be strictly increasing (b=%d: %d -> %d)", b, cu[b], cu[b + 1]);
+  const long long T = cu[batch];
+  if (T + 63LL * batch > (1LL << 31) - 1) return fail(BF_ERR_INVALID_ARG, "too many tokens (%lld)", T);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(BF_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned");
+  if (lse && ((uintptr_t)lse & 3u)) return fail(BF_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  RowsJob j;
+  j.bifocal = bifocal;
+  j.q = q; j.k = k; j.v = v; j.o = o; j.lse = lse;
+  j.cu.assign(cu, cu + batch + 1);
+  j.qpos.assign(batch, 0);
+  j.kbase.resize(batch);
+  j.slen.resize(batch);
+  for (int b = 0; b < batch; ++b) {
+    j.kbase[b] = cu[b];
+    j.slen[b] = cu[b + 1] - cu[b];
+  }
+  j.k_hstride = T;
+  j.k_rows = (long long)Hkv * T;
+  j.batch = batch; j.Hq = Hq; j.Hkv = Hkv; j.dtype = dtype;
+  j.w0 = w0; j.w_pre = w_pre; j.theta = theta; j.mode = mode; j.scale = scale;
+  j.ws = ws; j.ws_bytes = ws_bytes; j.stream = stream;
+  return run_rows(j);
+}
+
+// Chunk of queries against a KV cache [B][Hkv][cap][D] (bifocal_prefill_chunk).
+int run_chunk(const void* q, const void* kc, const void* vc, void* o, float* lse,
+              const int32_t* cu_q, const int32_t* seqlens, const int32_t* s_len, int batch,
+              int cap, int Hq, int Hkv, int head_dim, int dtype, long long w0, long long w_pre,
+              double theta, int mode, float scale, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!q || !kc || !vc || !o || !cu_q || !seqlens)
+    return fail(BF_ERR_INVALID_ARG, "null tensor, cu_q or seqlens pointer");
+  int rc = check_rows_common(true, batch, Hq, Hkv, head_dim, dtype, w0, w_pre, theta, mode, scale);
+  if (rc) return rc;
+  if (cap < 1) return fail(BF_ERR_INVALID_ARG, "cache_capacity must be >= 1 (got %d)", cap);
+  if (cu_q[0] != 0) return fail(BF_ERR_INVALID_ARG, "cu_q[0] must be 0 (got %d)", cu_q[0]);
+  long long Tk = 0;
+  for (int b = 0; b < batch; ++b) {
+    const int Lq = cu_q[b + 1] - cu_q[b];
+    if (Lq < 1) return fail(BF_ERR_INVALID_ARG, "cu_q must be strictly increasing (b=%d: %d -> %d)", b, cu_q[b], cu_q[b + 1]);
+    if (seqlens[b] < Lq || seqlens[b] > cap)
+      return fail(BF_ERR_INVALID_ARG, "seqlens[%d] = %d must lie in [chunk length %d, cache_capacity %d]",
+                  b, seqlens[b], Lq, cap);
+    if (s_len && s_len[b] < seqlens[b])
+      return fail(BF_ERR_INVALID_ARG, "s_len[%d] = %d is below seqlens[%d] = %d", b, s_len[b], b, seqlens[b]);
+    Tk += seqlens[b];
+  }
+  const long long Tq = cu_q[batch];
+  if (Tk + 63LL * batch > (1LL << 31) - 1) return fail(BF_ERR_INVALID_ARG, "too many keys (%lld)", Tk);
+  if ((long long)batch * Hkv * cap > (1LL << 40)) return fail(BF_ERR_INVALID_ARG, "cache too large");
+  if (!aligned16(q) || !aligned16(kc) || !aligned16(vc) || !aligned16(o))
+    return fail(BF_ERR_INVALID_ARG, "q, k_cache, v_cache and o must be 16-byte aligned");
+  if (lse && ((uintptr_t)lse & 3u)) return fail(BF_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  RowsJob j;
+  j.bifocal = true;
+  j.q = q; j.k = kc; j.v = vc; j.o = o; j.lse = lse;
+  j.cu.assign(cu_q, cu_q + batch + 1);
+  j.qpos.resize(batch);
+  j.kbase.resize(batch);
+  j.slen.resize(batch);
+  for (int b = 0; b < batch; ++b) {
+    j.qpos[b] = seqlens[b] - (cu_q[b + 1] - cu_q[b]);
+    j.kbase[b] = (long long)b * Hkv * cap;
+    j.slen[b] = s_len ? s_len[b] : seqlens[b];
+  }
+  (void)Tq;
+  j.k_hstride = cap;
+  j.k_rows = (long long)batch * Hkv * cap;
+  j.batch = batch; j.Hq = Hq; j.Hkv = Hkv; j.dtype = dtype;
+  j.w0 = w0; j.w_pre = w_pre; j.theta = theta; j.mode = mode; j.scale = scale;
+  j.ws = ws; j.ws_bytes = ws_bytes; j.stream = stream;
+  return run_rows(j);
 }
 
 }  // namespace
@@ -264,7 +378,8 @@ size_t bifocal_workspace_bytes(int32_t phase, int32_t batch, int64_t tokens, int
   if (batch < 1 || tokens < 1 || n_heads_q < 1 || n_heads_kv < 1 || head_dim != bf::kHeadDim)
     return 0;
   if (dtype != BF_DTYPE_BF16 && dtype != BF_DTYPE_FP32) return 0;
-  if (phase == BF_PHASE_PREFILL) return prefill_ws_layout(batch, tokens, n_heads_q, n_heads_kv, dtype).total;
+  if (phase == BF_PHASE_PREFILL)
+    return prefill_ws_layout(batch, tokens, tokens, n_heads_q, n_heads_kv, dtype).total;
   if (phase == BF_PHASE_DECODE) return bf::decode_workspace_bytes(batch, tokens, n_heads_q);
   return 0;
 }
@@ -277,6 +392,28 @@ int bifocal_prefill(const void* q, const void* k, const void* v, void* o, float*
   return run_prefill(true, q, k, v, o, lse, cu_seqlens_host, batch, n_heads_q, n_heads_kv,
                      head_dim, dtype, w0, w_pre, rope_theta, long_mode, softmax_scale, workspace,
                      workspace_bytes, (hipStream_t)stream);
+}
+
+size_t bifocal_chunk_workspace_bytes(int32_t batch, int64_t q_tokens, int64_t kv_tokens,
+                                     int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim,
+                                     int32_t dtype) {
+  if (batch < 1 || q_tokens < 1 || kv_tokens < q_tokens || n_heads_q < 1 || n_heads_kv < 1 ||
+      head_dim != bf::kHeadDim)
+    return 0;
+  if (dtype != BF_DTYPE_BF16 && dtype != BF_DTYPE_FP32) return 0;
+  return prefill_ws_layout(batch, q_tokens, kv_tokens, n_heads_q, n_heads_kv, dtype).total;
+}
+
+int bifocal_prefill_chunk(const void* q, const void* k_cache, const void* v_cache, void* o,
+                          float* lse, const int32_t* cu_q_host, const int32_t* seqlens_host,
+                          const int32_t* s_len_host, int32_t batch, int32_t cache_capacity,
+                          int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim, int32_t dtype,
+                          int64_t w0, int64_t w_pre, double rope_theta, int32_t long_mode,
+                          float softmax_scale, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  return run_chunk(q, k_cache, v_cache, o, lse, cu_q_host, seqlens_host, s_len_host, batch,
+                   cache_capacity, n_heads_q, n_heads_kv, head_dim, dtype, w0, w_pre, rope_theta,
+                   long_mode, softmax_scale, workspace, workspace_bytes, (hipStream_t)stream);
 }
 
 int bifocal_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,

@@ -68,11 +68,14 @@ __device__ __forceinline__ int key_of_acc(int r, int hl) {  // key of acc regist
   return ((r >> 3) << 4) | (hl << 3) | (r & 7);
 }
 
-// Work item of a workgroup: rank counts row blocks heaviest first (largest
-// row-block index first, ties by sequence order), across all sequences.
+// Work item of a workgroup: rank counts row blocks heaviest first, across all
+// sequences. Row block rb of sequence b ends near position
+// qpos[b] + (rb + 1) P_wg, so its weight index is x = rb + rboff[b]
+// (rboff = qpos / P_wg, zero for a one-shot prefill); ranks run over x
+// descending, ties by sequence order.
 __device__ __forceinline__ int items_at_or_above(const SeqTable& st, int x) {
   int n = 0;
-  for (int b = 0; b < st.n; ++b) n += max(0, st.nrb[b] - x);
+  for (int b = 0; b < st.n; ++b) n += min(st.nrb[b], max(0, st.nrb[b] + st.rboff[b] - x));
   return n;
 }
 
@@ -84,20 +87,22 @@ __device__ __forceinline__ void decode_item(const SeqTable& st, int rank, int ma
     if (items_at_or_above(st, mid) > rank) lo = mid;
     else hi = mid;
   }
-  rb = lo;
-  int e = rank - items_at_or_above(st, rb + 1);
+  int e = rank - items_at_or_above(st, lo + 1);
   for (b = 0; b < st.n; ++b) {
-    if (st.nrb[b] > rb) {
+    if (st.rboff[b] <= lo && lo < st.nrb[b] + st.rboff[b]) {
       if (e == 0) break;
       --e;
     }
   }
+  rb = lo - st.rboff[b];
 }
 
 // ----------------------------------------------------------------- prep
-// One thread per (token, rotary pair m); 4 tokens per 256-lane group. The
-// angle is formed in fp64 from an exact integer numerator, so it stays
-// accurate at 128K positions (theta_0 * p ~ 1e5 rad), and is applied in fp32.
+// One thread per (token, rotary pair m); 4 tokens per 256-lane group;
+// blockIdx.y = 0 rotates the queries (positions qpos[b] + row), 1 the keys
+// (positions 0 .. N_b - 1, read from the K layout, written packed). The angle
+// is formed in fp64 from an exact integer numerator, so it stays accurate at
+// 128K positions (theta_0 * p ~ 1e5 rad), and is applied in fp32.
 template <typename T>
 __device__ __forceinline__ float ld_elem(const T* p) {
   if constexpr (sizeof(T) == 2) return bf16_to_f32(*p);
@@ -112,52 +117,45 @@ __device__ __forceinline__ void st_elem(T* p, float f) {
 template <typename T>
 __global__ __launch_bounds__(256) void correction_prep_kernel(PrepParams p, SeqTable st,
                                                               ThetaTable tt) {
-  const int tok = st.cu[0] + blockIdx.x * 4 + (threadIdx.x >> 6);
+  const bool keys = blockIdx.y == 1;
+  auto cu = [&](int i) { return keys ? st.kcu[i] : st.cu[i]; };
+  const int tok = cu(0) + blockIdx.x * 4 + (threadIdx.x >> 6);
   const int m = threadIdx.x & 63;
-  if (tok >= st.cu[st.n]) return;
+  if (tok >= cu(st.n)) return;
   int b = 0;
-  while (b + 1 < st.n && tok >= st.cu[b + 1]) ++b;
+  while (b + 1 < st.n && tok >= cu(b + 1)) ++b;
   const int s = st.s[b];
   if (s == 1) return;  // no far branch for this sequence
-  const long long pos = tok - st.cu[b];
-  const long long num = corr_num(pos, s, p.long_mode);
-  const double dphi = (double)num / (double)s;
+  const long long row = tok - cu(b);
+  const long long pos = keys ? row : st.qpos[b] + row;
+  long long num = corr_num(pos, s, p.long_mode);
+  // queries with the band-edge continuity shift: (w0 - phi(w0)) * s is the
+  // exact integer w0 (s - 1) (FI) or (w0 - floor(w0 / s)) s (PA)
+  if (!keys && p.shift) num += p.long_mode == 1 ? (p.w0 - p.w0 / s) * s : p.w0 * (s - 1);
   double sd, cd;
-  sincos(tt.th[m] * dphi, &sd, &cd);
+  sincos(tt.th[m] * ((double)num / (double)s), &sd, &cd);
   const float c = (float)cd, sn = (float)sd;
-  // queries: the same angle, plus the band-edge continuity shift if asked:
-  // (w0 - phi(w0)) * s is the exact integer w0 (s - 1) (FI) or
-  // (w0 - floor(w0 / s)) s (PA)
-  float cq = c, sq = sn;
-  if (p.shift) {
-    const long long sh = p.long_mode == 1 ? (p.w0 - p.w0 / s) * s : p.w0 * (s - 1);
-    double sdq, cdq;
-    sincos(tt.th[m] * ((double)(num + sh) / (double)s), &sdq, &cdq);
-    cq = (float)cdq;
-    sq = (float)sdq;
-  }
-  const T* q = (const T*)p.q;
-  const T* k = (const T*)p.k;
-  T* q2 = (T*)p.q2;
-  T* k2 = (T*)p.k2;
-  for (int h = 0; h < p.Hq; ++h) {
-    const size_t base = ((size_t)h * p.T + tok) * kHeadDim;
-    const float x0 = ld_elem(q + base + m), x1 = ld_elem(q + base + m + kPairs);
-    st_elem(q2 + base + m, x0 * cq - x1 * sq);
-    st_elem(q2 + base + m + kPairs, x1 * cq + x0 * sq);
-  }
-  for (int h = 0; h < p.Hkv; ++h) {
-    const size_t base = ((size_t)h * p.T + tok) * kHeadDim;
-    const float x0 = ld_elem(k + base + m), x1 = ld_elem(k + base + m + kPairs);
-    st_elem(k2 + base + m, x0 * c - x1 * sn);
-    st_elem(k2 + base + m + kPairs, x1 * c + x0 * sn);
+  const int nh = keys ? p.Hkv : p.Hq;
+  for (int h = 0; h < nh; ++h) {
+    const T* src;
+    T* dst;
+    if (keys) {
+      src = (const T*)p.k + ((size_t)h * p.k_hstride + st.kbase[b] + row) * kHeadDim;
+      dst = (T*)p.k2 + ((size_t)h * p.Tk + tok) * kHeadDim;
+    } else {
+      src = (const T*)p.q + ((size_t)h * p.T + tok) * kHeadDim;
+      dst = (T*)p.q2 + ((size_t)h * p.T + tok) * kHeadDim;
+    }
+    const float x0 = ld_elem(src + m), x1 = ld_elem(src + m + kPairs);
+    st_elem(dst + m, x0 * c - x1 * sn);
+    st_elem(dst + m + kPairs, x1 * c + x0 * sn);
   }
 }
 
-// V [Hkv][T][D] -> V^T in 64-key tiles: tile t (global over the padded key
-// axis, sequence b owns tiles vt_off[b] / 64 ..) of KV head h is the contiguous
-// block vt[(h * Tpad / 64 + t) * D * 64 ..], laid out [head dim][64 keys].
-// Keys past a sequence's length are zero.
+// V (the layout of K) -> V^T in 64-key tiles: tile t (global over the padded
+// key axis, sequence b owns tiles vt_off[b] / 64 ..) of KV head h is the
+// contiguous block vt[(h * Tpad / 64 + t) * D * 64 ..], laid out
+// [head dim][64 keys]. Keys past a sequence's length are zero.
 template <typename T>
 __global__ __launch_bounds__(256) void vt_transpose_kernel(VtParams p, SeqTable st) {
   __shared__ T tile[kKeyTile][kHeadDim + 2];
@@ -166,8 +164,8 @@ __global__ __launch_bounds__(256) void vt_transpose_kernel(VtParams p, SeqTable 
   int b = 0;
   while (b + 1 < st.n && c >= st.vt_off[b + 1]) ++b;
   const int p0 = c - st.vt_off[b];
-  const int L = st.cu[b + 1] - st.cu[b];
-  const T* v = (const T*)p.v + ((size_t)h * p.T + st.cu[b]) * kHeadDim;
+  const int L = st.kcu[b + 1] - st.kcu[b];
+  const T* v = (const T*)p.v + ((size_t)h * p.k_hstride + st.kbase[b]) * kHeadDim;
   for (int e = threadIdx.x; e < kKeyTile * kHeadDim; e += 256) {
     const int r = e / kHeadDim, d = e % kHeadDim;
     tile[r][d] = (p0 + r < L) ? v[(size_t)(p0 + r) * kHeadDim + d] : T(0);
@@ -182,8 +180,10 @@ __global__ __launch_bounds__(256) void vt_transpose_kernel(VtParams p, SeqTable 
 
 // ----------------------------------------------------------------- main
 // Shared work-item geometry of both element types.
+// Rows index the packed queries of the sequence (0 .. L - 1); the query of
+// row r sits at position qp + r and sees keys 0 .. qp + r.
 struct Item {
-  int kvh, hq, b, tok0, L, R0, r0, nkt;
+  int kvh, hq, b, tok0, L, qp, R0, r0, nkt;
   long long w0;
 };
 
@@ -200,6 +200,7 @@ __device__ __forceinline__ Item make_item(const PrefillParams& p, const SeqTable
   decode_item(st, rank, p.max_nrb, it.b, rb);
   it.tok0 = st.cu[it.b];
   it.L = st.cu[it.b + 1] - it.tok0;
+  it.qp = st.qpos[it.b];
   // s = 1 means the far branch equals the local one: treat every pair as local;
   // band-only attention keeps the window whatever s is
   it.w0 = (BIFOCAL && (BAND || st.s[it.b] > 1)) ? p.w0 : (1LL << 62);
@@ -207,13 +208,13 @@ __device__ __forceinline__ Item make_item(const PrefillParams& p, const SeqTable
   it.hq = it.kvh * p.G + hsub * p.hpw + hw;
   it.R0 = rb * p.P_wg;
   it.r0 = it.R0 + pw * wave_rows;
-  const int wg_end = min(it.R0 + p.P_wg, it.L);
+  const int wg_end = it.qp + min(it.R0 + p.P_wg, it.L);  // keys < wg_end
   it.nkt = (wg_end + kKeyTile - 1) / kKeyTile;
   return it;
 }
 
-// Tile needs, for the whole workgroup (rows R0 .. R0 + P_wg - 1) and keys
-// c0 .. c0 + 63: any far pair / any local pair.
+// Tile needs, for the whole workgroup (query positions R0 .. R0 + P_wg - 1)
+// and keys c0 .. c0 + 63: any far pair / any local pair.
 template <bool BIFOCAL>
 __device__ __forceinline__ void tile_needs(long long R0, long long P_wg, long long c0,
                                            long long w0, bool& need_far, bool& need_loc) {
@@ -260,8 +261,9 @@ constexpr int kBf16Waves = 4;
 constexpr int kStageIters = kSlot / (64 * kBf16Waves);  // 1 KiB loads per wave per tile
 
 struct WaveRows {
-  int r0;  // first query position of the wave (sequence-relative)
-  int L;   // sequence length
+  int r0;  // first query row of the wave (sequence-relative)
+  int p0;  // its position (r0 + qpos)
+  int L;   // query rows of the sequence
   int w0;  // local window, clamped to 2^30 (s = 1 or the plain engine: all local)
 };
 
@@ -356,11 +358,11 @@ __device__ __forceinline__ void qk_tile(uint32_t slot_off, const bf16x8 (&q)[8],
 template <bool FAR>
 __device__ __forceinline__ void mask_tile(f32x16 (&S)[2], const WaveRows& wr, int c0, int li,
                                           int hl) {
-  const int dmax = wr.r0 + 31 - c0;
-  const int dmin = wr.r0 - (c0 + 63);
+  const int dmax = wr.p0 + 31 - c0;
+  const int dmin = wr.p0 - (c0 + 63);
   const bool full = FAR ? (dmin >= wr.w0) : (dmin >= 0 && dmax < wr.w0);
   if (full) return;
-  const int base = wr.r0 + li - c0 - 8 * hl;  // i - j = base - 32 jb - 16 (r / 8) - r % 8
+  const int base = wr.p0 + li - c0 - 8 * hl;  // i - j = base - 32 jb - 16 (r / 8) - r % 8
 #pragma unroll
   for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
@@ -650,8 +652,8 @@ __device__ __forceinline__ void run_pass(const uint16_t* qsrc, const uint16_t* k
       qf[t] = __builtin_bit_cast(bf16x8, v);
     }
   }
-  // tiles with a causal pair of this wave: c0 <= r0 + 31, none if r0 >= L
-  const int kte_w = wr.r0 >= wr.L ? ktb : min(kte, (wr.r0 + 31) / kKeyTile + 1);
+  // tiles with a causal pair of this wave: c0 <= p0 + 31, none if r0 >= L
+  const int kte_w = wr.r0 >= wr.L ? ktb : min(kte, (wr.p0 + 31) / kKeyTile + 1);
   const StageOffsets so = stage_offsets(wave, lane);
   const KStage ks = k_stage_offsets(so);
   const FragAddr fa = frag_addr(li, hl, sK, sV);
@@ -730,18 +732,18 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillParams p, S
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar) index
   const int li = lane & 31, hl = lane >> 5;
   const Item it = make_item<BIFOCAL, BAND>(p, st, wave, kWaveRowsBf16);
-  const WaveRows wr{it.r0, it.L, (int)min(it.w0, (long long)(1 << 30))};
+  const WaveRows wr{it.r0, it.qp + it.r0, it.L, (int)min(it.w0, (long long)(1 << 30))};
 
   const uint16_t* qg = (const uint16_t*)p.q + ((size_t)it.hq * p.T + it.tok0) * kHeadDim;
-  const uint16_t* kg = (const uint16_t*)p.k + ((size_t)it.kvh * p.T + it.tok0) * kHeadDim;
+  const uint16_t* kg =
+      (const uint16_t*)p.k + ((size_t)it.kvh * p.k_hstride + st.kbase[it.b]) * kHeadDim;
   const uint16_t* vt0 = (const uint16_t*)p.vt +
                         ((size_t)it.kvh * (p.Tpad / kKeyTile) + st.vt_off[it.b] / kKeyTile) *
                             (kHeadDim * kKeyTile);
 
   // ends of the K, K'' and V^T tensors (range limit of the staging loads)
-  const size_t kv_bytes = (size_t)p.Hkv * p.T * kHeadDim * 2;
-  const char* k_end = (const char*)p.k + kv_bytes;
-  const char* k2_end = (const char*)p.k2 + kv_bytes;
+  const char* k_end = (const char*)p.k + (size_t)p.k_rows * kHeadDim * 2;
+  const char* k2_end = (const char*)p.k2 + (size_t)p.Hkv * p.Tk * kHeadDim * 2;
   const char* vt_end = (const char*)p.vt + (size_t)p.Hkv * p.Tpad * kHeadDim * 2;
 
   RowState rs{-INFINITY, 0.f, 1.f, false};
@@ -749,13 +751,14 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillParams p, S
 #pragma unroll
   for (int db = 0; db < 4; ++db) oacc[db] = f32x16{};
 
-  // tile ranges of the two passes for the workgroup's rows R0 .. R0 + P_wg - 1
-  const long long R0 = it.R0, Rl = (long long)it.R0 + p.P_wg - 1;
+  // tile ranges of the two passes for the workgroup's query positions
+  // R0 .. R0 + P_wg - 1
+  const long long R0 = (long long)it.qp + it.R0, Rl = R0 + p.P_wg - 1;
   const long long w0 = it.w0;
   if (BIFOCAL && !BAND && Rl - w0 >= 0) {  // far pairs exist: keys j <= Rl - w0
     const int kte = min(it.nkt, (int)((Rl - w0) / kKeyTile) + 1);
     run_pass<true>((const uint16_t*)p.q2 + ((size_t)it.hq * p.T + it.tok0) * kHeadDim,
-                   (const uint16_t*)p.k2 + ((size_t)it.kvh * p.T + it.tok0) * kHeadDim, vt0,
+                   (const uint16_t*)p.k2 + ((size_t)it.kvh * p.Tk + st.kcu[it.b]) * kHeadDim, vt0,
                    k2_end, vt_end, 0, kte, wr, p.scale_log2, wave, lane, sK, sV, rs, oacc);
   }
   if (w0 > 0) {  // local pairs exist: keys j > R0 - w0 (and j <= Rl)
@@ -825,9 +828,12 @@ __global__ __launch_bounds__(256, 1) void prefill_f32_kernel(PrefillParams p, Se
   const long long w0 = it.w0;
 
   const float* qg = (const float*)p.q + ((size_t)it.hq * p.T + it.tok0) * kHeadDim;
-  const float* kg = (const float*)p.k + ((size_t)it.kvh * p.T + it.tok0) * kHeadDim;
+  const float* kg = (const float*)p.k + ((size_t)it.kvh * p.k_hstride + st.kbase[it.b]) * kHeadDim;
   const float* q2g = BIFOCAL ? (const float*)p.q2 + ((size_t)it.hq * p.T + it.tok0) * kHeadDim : nullptr;
-  const float* k2g = BIFOCAL ? (const float*)p.k2 + ((size_t)it.kvh * p.T + it.tok0) * kHeadDim : nullptr;
+  const float* k2g =
+      BIFOCAL ? (const float*)p.k2 + ((size_t)it.kvh * p.Tk + st.kcu[it.b]) * kHeadDim : nullptr;
+  const int nk = it.qp + it.L;   // keys of the sequence
+  const int p0 = it.qp + it.r0;  // position of the wave's first row
   const float* vt0 = (const float*)p.vt +
                      ((size_t)it.kvh * (p.Tpad / kKeyTile) + st.vt_off[it.b] / kKeyTile) *
                          (kHeadDim * kKeyTile);
@@ -836,7 +842,7 @@ __global__ __launch_bounds__(256, 1) void prefill_f32_kernel(PrefillParams p, Se
   {
     const int row = it.r0 + li;
     const bool ok = row < it.L;
-    const bool ok2 = ok && w0 < it.L && !BAND;  // corrected queries exist only with far pairs
+    const bool ok2 = ok && w0 < nk && !BAND;  // corrected queries exist only with far pairs
     const int rowc = ok ? row : it.L - 1;
 #pragma unroll
     for (int tc = 0; tc < 16; ++tc) {
@@ -861,15 +867,15 @@ __global__ __launch_bounds__(256, 1) void prefill_f32_kernel(PrefillParams p, Se
   for (int kt = 0; kt < it.nkt; ++kt) {
     const int c0 = kt * kKeyTile;
     bool cf, cl;
-    tile_needs<BIFOCAL>(it.R0, p.P_wg, c0, w0, cf, cl);
+    tile_needs<BIFOCAL>((long long)it.qp + it.R0, p.P_wg, c0, w0, cf, cl);
     if (BAND) cf = false;  // far pairs are dropped, never scored
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int c = tid + 256 * i;
       const int row = c >> 5, col = c & 31;
-      const bool ok = c0 + row < it.L;
-      const size_t off = (size_t)min(c0 + row, it.L - 1) * kHeadDim + col * 4;
+      const bool ok = c0 + row < nk;
+      const size_t off = (size_t)min(c0 + row, nk - 1) * kHeadDim + col * 4;
       if (cl) {
         uint4 kv = *(const uint4*)(kg + off);
         if (!ok) kv = zero4;
@@ -887,10 +893,10 @@ __global__ __launch_bounds__(256, 1) void prefill_f32_kernel(PrefillParams p, Se
     }
     __syncthreads();
 
-    const bool wave_skip = (it.r0 >= it.L) || (c0 > it.r0 + kWaveRowsF32 - 1);
+    const bool wave_skip = (it.r0 >= it.L) || (c0 > p0 + kWaveRowsF32 - 1);
     if (wave_skip) continue;
-    const long long dmax = (long long)it.r0 + kWaveRowsF32 - 1 - c0;
-    const long long dmin = (long long)it.r0 - (c0 + kKeyTile - 1);
+    const long long dmax = (long long)p0 + kWaveRowsF32 - 1 - c0;
+    const long long dmin = (long long)p0 - (c0 + kKeyTile - 1);
     const bool has_far = BIFOCAL && dmax >= w0;
     const bool has_loc = !BIFOCAL || (w0 > 0 && dmin < w0);
     constexpr bool band_only = BIFOCAL && BAND;
@@ -899,7 +905,7 @@ __global__ __launch_bounds__(256, 1) void prefill_f32_kernel(PrefillParams p, Se
     f32x16 S[2];
     if (BIFOCAL && has_far && !band_only) qk_f32(sK2, qf2, li, hl, S);
     else qk_f32(sK, qf, li, hl, S);
-    const long long i = it.r0 + li;
+    const long long i = p0 + li;
     if (band_only && has_far) {  // drop the far pairs of a mixed tile
 #pragma unroll
       for (int jb = 0; jb < 2; ++jb)
@@ -1003,11 +1009,12 @@ __global__ void pair_map_kernel(long long L, long long w0, long long s, int mode
 // --------------------------------------------------------------- launchers
 hipError_t launch_correction_prep(int dtype, const PrepParams& pp, const SeqTable& st,
                                   const ThetaTable& tt, hipStream_t stream) {
-  const int grid = (st.cu[st.n] - st.cu[0] + 3) / 4;
+  const int tq = st.cu[st.n] - st.cu[0], tk = st.kcu[st.n] - st.kcu[0];
+  const dim3 grid((max(tq, tk) + 3) / 4, 2);
   if (dtype == 0)
-    hipLaunchKernelGGL(correction_prep_kernel<uint16_t>, dim3(grid), dim3(256), 0, stream, pp, st, tt);
+    hipLaunchKernelGGL(correction_prep_kernel<uint16_t>, grid, dim3(256), 0, stream, pp, st, tt);
   else
-    hipLaunchKernelGGL(correction_prep_kernel<float>, dim3(grid), dim3(256), 0, stream, pp, st, tt);
+    hipLaunchKernelGGL(correction_prep_kernel<float>, grid, dim3(256), 0, stream, pp, st, tt);
   return hipGetLastError();
 }
 

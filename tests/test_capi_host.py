@@ -212,3 +212,49 @@ def test_decode_paged_valid_arguments_reach_the_launch(L, monkeypatch):
     monkeypatch.setenv("BIFOCAL_TEST_FAIL_LAUNCH", "1")
     assert _decode_paged(L) == bfl.BF_ERR_HIP
     assert _decode_paged(L, mode=2, page=64, maxp=2) == bfl.BF_ERR_HIP
+
+
+def _chunk(L, **kw):
+    a = dict(q=P, kc=P, vc=P, o=P, lse=None, cu=[0, 30, 31], sl=[100, 1], s_len=None, cap=128,
+             Hq=4, Hkv=2, D=128, dtype=0, w0=16, w_pre=64, theta=1e4, mode=0, scale=0.088, ws=P,
+             ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    cu = (ctypes.c_int32 * len(a["cu"]))(*a["cu"])
+    sl = (ctypes.c_int32 * len(a["sl"]))(*a["sl"])
+    sls = (ctypes.c_int32 * len(a["s_len"]))(*a["s_len"]) if a["s_len"] is not None else None
+    return L.bifocal_prefill_chunk(a["q"], a["kc"], a["vc"], a["o"], a["lse"], cu, sl, sls,
+                                   len(a["cu"]) - 1, a["cap"], a["Hq"], a["Hkv"], a["D"],
+                                   a["dtype"], a["w0"], a["w_pre"], a["theta"], a["mode"],
+                                   a["scale"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+def test_chunk_workspace_bytes(L):
+    ws = bfl.chunk_workspace_bytes(1, 4096, 131072, 32, 8)
+    # V^T over the keys + corrected Q over the queries + corrected K over the keys (bf16)
+    assert ws >= 2 * 128 * (8 * 131072 + 32 * 4096 + 8 * 131072)
+    assert ws < bfl.workspace_bytes(bfl.BF_PHASE_PREFILL, 1, 131072, 32, 8)
+    assert ws == bfl.chunk_workspace_bytes(1, 4096, 131072, 32, 8, dtype=bfl.torch.bfloat16)
+    assert bfl.chunk_workspace_bytes(1, 131072, 131072, 32, 8) == \
+        bfl.workspace_bytes(bfl.BF_PHASE_PREFILL, 1, 131072, 32, 8)
+    assert L.bifocal_chunk_workspace_bytes(1, 10, 5, 2, 1, 128, 0) == 0  # fewer keys than queries
+    assert L.bifocal_chunk_workspace_bytes(1, 10, 20, 2, 1, 64, 0) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(kc=None), -1), (dict(sl=[29, 1]), -1),   # chunk longer than N
+    (dict(sl=[129, 1]), -1), (dict(cu=[0, 30, 30]), -1), (dict(cu=[2, 30, 31]), -1),
+    (dict(s_len=[99, 1]), -1), (dict(cap=0), -1), (dict(D=64), -2), (dict(mode=9), -1),
+    (dict(mode=2, w0=0), -1), (dict(ws=None), -3), (dict(ws_bytes=1000), -3),
+    (dict(kc=ctypes.c_void_p(0x100004)), -1), (dict(Hq=3), -1), (dict(scale=-1.0), -1),
+])
+def test_chunk_validation(L, kw, code):
+    assert _chunk(L, **kw) == code
+    assert len(L.bifocal_last_error()) > 0
+
+
+def test_chunk_valid_arguments_reach_the_launch(L, monkeypatch):
+    monkeypatch.setenv("BIFOCAL_TEST_FAIL_LAUNCH", "1")
+    assert _chunk(L) == bfl.BF_ERR_HIP
+    assert _chunk(L, dtype=1, mode=5, s_len=[1000, 1]) == bfl.BF_ERR_HIP
+    assert _chunk(L, mode=2, w0=3) == bfl.BF_ERR_HIP
+    assert _chunk(L, cu=[0, 100, 101], sl=[100, 128]) == bfl.BF_ERR_HIP  # whole-sequence chunk

@@ -442,3 +442,104 @@ def test_shift_is_a_no_op_at_s1():
     a, _ = oracle.prefill(q, k, v, [0, 50], 8, 64, 1e4, "fi+shift", 0.088)
     b, _ = oracle.prefill(q, k, v, [0, 50], 8, 64, 1e4, "fi", 0.088)
     np.testing.assert_array_equal(a, b)
+
+
+# ---------------------------------------------------------------- chunk of queries over a cache
+def _as_cache(k, cap, fill):
+    """[Hkv, N, D] keys -> a one-sequence cache [1, Hkv, cap, D]; slots past N
+    hold `fill` (never read)."""
+    Hkv, N, D = k.shape
+    c = np.full((1, Hkv, cap, D), fill, np.float32)
+    c[0, :, :N] = k
+    return c
+
+
+@pytest.mark.parametrize("mode", ["fi", "pa"])
+@pytest.mark.parametrize("S", [None, 75])
+def test_chunk_matches_brute_force_tiny(mode, S):
+    # the last Lq queries of an N-token sequence against its N cached keys
+    # are rows N - Lq .. N - 1 of the per-pair definition; with s_len = S the
+    # factor is s(S): the brute force over an S-token sequence whose first N
+    # tokens are the cached ones (rows below N never see the later tokens)
+    N, Lq, Hq, Hkv, D, w0, w_pre = 40, 13, 2, 1, 16, 5, 12
+    Sl = S or N
+    q, k, v = _rand((Hq, Sl, D), 70), _rand((Hkv, Sl, D), 71), _rand((Hkv, Sl, D), 72)
+    o_b, lse_b = brute_prefill(q, k, v, w0, w_pre, 1e4, mode, 0.3)
+    kc, vc = _as_cache(k[:, :N], N + 9, np.nan), _as_cache(v[:, :N], N + 9, np.nan)
+    o, lse = oracle.chunk(q[:, N - Lq:N], kc, vc, [0, Lq], [N], w0, w_pre, 1e4, mode, 0.3,
+                          s_len=None if S is None else [S])
+    np.testing.assert_allclose(o, o_b[:, N - Lq:N], atol=1e-12, rtol=0)
+    np.testing.assert_allclose(lse, lse_b[:, N - Lq:N], atol=1e-12, rtol=0)
+
+
+def test_chunk_s_len_changes_the_result():
+    # a discriminating check of the s_len argument: s(40) = 4 and s(75) = 7
+    N, Lq = 40, 13
+    q, k, v = _rand((2, N, 16), 73), _rand((1, N, 16), 74), _rand((1, N, 16), 75)
+    kc, vc = _as_cache(k, N, 0.0), _as_cache(v, N, 0.0)
+    a, _ = oracle.chunk(q[:, N - Lq:], kc, vc, [0, Lq], [N], 5, 12, 1e4, "fi", 0.3)
+    b, _ = oracle.chunk(q[:, N - Lq:], kc, vc, [0, Lq], [N], 5, 12, 1e4, "fi", 0.3, s_len=[75])
+    assert np.abs(a - b).max() > 1e-3
+
+
+@pytest.mark.parametrize("mode", ["fi", "pa+shift", "band"])
+def test_chunk_of_whole_sequence_is_prefill_and_single_query_is_decode(mode):
+    Hq, Hkv, N, D = 4, 2, 70, 128
+    q, k, v = _rand((Hq, N, D), 76), _rand((Hkv, N, D), 77), _rand((Hkv, N, D), 78)
+    kc, vc = _as_cache(k, 80, np.inf), _as_cache(v, 80, np.inf)
+    o_c, l_c = oracle.chunk(q, kc, vc, [0, N], [N], 9, 16, 1e4, mode, 0.1)
+    o_p, l_p = oracle.prefill(q, k, v, [0, N], 9, 16, 1e4, mode, 0.1)
+    np.testing.assert_allclose(o_c, o_p, atol=1e-13, rtol=0)
+    np.testing.assert_allclose(l_c, l_p, atol=1e-13, rtol=0)
+    o_1, l_1 = oracle.chunk(q[:, N - 1:], kc, vc, [0, 1], [N], 9, 16, 1e4, mode, 0.1)
+    o_d, l_d = oracle.decode(q[:, N - 1][None], kc, vc, [N], 9, 16, 1e4, mode, 0.1)
+    np.testing.assert_allclose(o_1[:, 0], o_d[0], atol=1e-13, rtol=0)
+    np.testing.assert_allclose(l_1[:, 0], l_d[0], atol=1e-13, rtol=0)
+
+
+def test_chunk_band_matches_library_sliding_window():
+    rng = np.random.default_rng(79)
+    Hq, Hkv, N, D, w0, Lq = 4, 2, 150, 128, 33, 50
+    q = rng.standard_normal((Hq, N, D)).astype(np.float32)
+    k = rng.standard_normal((Hkv, N, D)).astype(np.float32)
+    v = rng.standard_normal((Hkv, N, D)).astype(np.float32)
+    scale = 1 / math.sqrt(D)
+    o, _ = oracle.chunk(q[:, N - Lq:], _as_cache(k, N, 0.0), _as_cache(v, N, 0.0), [0, Lq], [N],
+                        w0, 16, 1e4, "band", scale)
+    np.testing.assert_allclose(o, _sdpa_band(q, k, v, w0, scale)[:, N - Lq:], atol=1e-11)
+
+
+def test_chunk_batch_is_independent_per_sequence():
+    # packed chunks of three sequences (different N, Lq, a cache of capacity
+    # 64): each equals the chunk of that sequence alone; rows= picks a subset
+    Hq, Hkv, D, cap = 2, 1, 32, 64
+    Ns, Lqs = [64, 20, 33], [5, 20, 1]
+    cu = workloads.cu_seqlens(Lqs)
+    q = _rand((Hq, cu[-1], D), 80)
+    kc, vc = _rand((3, Hkv, cap, D), 81), _rand((3, Hkv, cap, D), 82)
+    o, lse = oracle.chunk(q, kc, vc, cu, Ns, 6, 10, 1e4, "pa", 0.2)
+    for b in range(3):
+        sl = slice(cu[b], cu[b + 1])
+        ob, lb = oracle.chunk(q[:, sl], kc[b:b + 1], vc[b:b + 1], [0, Lqs[b]], [Ns[b]], 6, 10, 1e4,
+                              "pa", 0.2)
+        np.testing.assert_array_equal(o[:, sl], ob)
+        np.testing.assert_array_equal(lse[:, sl], lb)
+    rows = [0, 4, 5, 25]
+    sub, _ = oracle.chunk(q, kc, vc, cu, Ns, 6, 10, 1e4, "pa", 0.2, rows=rows)
+    np.testing.assert_array_equal(sub, o[:, rows])
+
+
+def test_chunk_shift_makes_the_window_edge_continuous():
+    # the query at position w0 (the last of N = w0 + 1 keys) with the shift
+    # equals plain causal attention (library SDPA); cf. the prefill pin above
+    rng = np.random.default_rng(83)
+    Hq, Hkv, D, w0, w_pre = 2, 1, 128, 24, 20
+    N = w0 + 1
+    q = rng.standard_normal((Hq, N, D)).astype(np.float32)
+    k = rng.standard_normal((Hkv, N, D)).astype(np.float32)
+    v = rng.standard_normal((Hkv, N, D)).astype(np.float32)
+    scale = 1 / math.sqrt(D)
+    ref = _sdpa_band(q, k, v, N + 1, scale)[:, N - 3:]
+    o, _ = oracle.chunk(q[:, N - 3:], _as_cache(k, N, 0.0), _as_cache(v, N, 0.0), [0, 3], [N], w0,
+                        w_pre, 1e4, "fi+shift", scale, s_len=[60])
+    np.testing.assert_allclose(o, ref, atol=1e-11)
