@@ -100,6 +100,17 @@ __device__ __forceinline__ uint4 gload16(const char* base, uint32_t off) {
   return __builtin_bit_cast(uint4, v);
 }
 
+// The same load marked non-temporal: the line is streamed through the caches
+// instead of being kept. Every K / V byte of a call is read once, so keeping
+// the lines only evicts others; when the cache is larger than the MALL that
+// costs bandwidth (the lines could not have stayed resident anyway).
+template <bool NT>
+__device__ __forceinline__ uint4 kvload16(const char* base, uint32_t off) {
+  const auto* ptr = (const __attribute__((address_space(1))) du32x4*)(base + off);
+  if constexpr (NT) return __builtin_bit_cast(uint4, __builtin_nontemporal_load(ptr));
+  else return __builtin_bit_cast(uint4, *ptr);
+}
+
 // x holds elements (m, m + 1), y holds (m + 64, m + 65): rotate both pairs,
 // returning the new x and writing the new y.
 __device__ __forceinline__ uint32_t rot_word(uint32_t x, uint32_t y, float c0, float s0, float c1,
@@ -159,7 +170,7 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <bool BIFOCAL, bool PAGED>
+template <bool BIFOCAL, bool PAGED, bool NT>
 __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p, DecodeSeqs ds,
                                                               ThetaTable tt) {
   __shared__ uint4 smem[kDecLds / 16];
@@ -233,17 +244,17 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p, De
     if (j0 + kDecStep <= nl) {
       const uint32_t base = (uint32_t)rel0 * (kHeadDim * 2);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) kreg[r][t] = gload16(kb, base + k_lane + t * 64);
+      for (int t = 0; t < 4; ++t) kreg[r][t] = kvload16<NT>(kb, base + k_lane + t * 64);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) vreg[r][q] = gload16(vb, base + v_lane + q * 256);
+      for (int q = 0; q < 4; ++q) vreg[r][q] = kvload16<NT>(vb, base + v_lane + q * 256);
     } else {
       const uint32_t kk = (uint32_t)(min(j0 + n16, nl - 1) - j0 + rel0);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) kreg[r][t] = gload16(kb, kk * (kHeadDim * 2) + (4 * t + g4) * 16);
+      for (int t = 0; t < 4; ++t) kreg[r][t] = kvload16<NT>(kb, kk * (kHeadDim * 2) + (4 * t + g4) * 16);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const uint32_t kv = (uint32_t)(min(j0 + 4 * g4 + q, nl - 1) - j0 + rel0);
-        vreg[r][q] = gload16(vb, kv * (kHeadDim * 2) + n16 * 16);
+        vreg[r][q] = kvload16<NT>(vb, kv * (kHeadDim * 2) + n16 * 16);
       }
     }
   };
@@ -599,6 +610,9 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p, Dec
 #endif
 constexpr long long kDecTargetWgs = BF_DEC_TARGET_WGS;
 constexpr long long kDecMaxChunk = BF_DEC_MAX_CHUNK;
+// K + V bytes of a launch from which its loads are non-temporal (a quarter of
+// the 256 MB MALL: smaller caches can stay resident between calls)
+constexpr long long kDecStreamBytes = 64LL << 20;
 constexpr long long kDecMinTargetSplits = 8, kDecMaxTargetSplits = 128;
 static_assert(kDecMaxChunk % kDecBlock == 0, "chunk must be a multiple of 64 keys");
 
@@ -729,6 +743,7 @@ int run_decode(bool bifocal, const void* q, const void* kc, const void* vc, void
     DecodeSeqs ds;
     ds.n = nb;
     int max_split = 0;
+    long long kv_bytes = 0;  // K and V bytes the launch reads
     for (int i = 0; i < nb; ++i) {
       const long long N = seqlens[b0 + i];
       ds.N[i] = (int)N;
@@ -744,6 +759,7 @@ int run_decode(bool bifocal, const void* q, const void* kc, const void* vc, void
       ds.chunk[i] = decode_chunk(N - k0, target);
       ds.nsplit[i] = decode_splits(N - k0, target);
       if (ds.nsplit[i] > max_split) max_split = ds.nsplit[i];
+      kv_bytes += (N - k0) * Hkv * kHeadDim * 2 * 2;
     }
     dp.q = (const uint16_t*)q + (size_t)b0 * Hq * kHeadDim;
     // contiguous: the launch's first sequence; paged: the page pool, rows of
@@ -760,14 +776,14 @@ int run_decode(bool bifocal, const void* q, const void* kc, const void* vc, void
       fprintf(stderr, "[bifocal] decode %s seqs=%d..%d N0=%d s0=%d splits=%d chunk=%d\n",
               bifocal ? "bifocal" : "plain", b0, b0 + nb - 1, ds.N[0], ds.s[0], ds.nsplit[0], ds.chunk[0]);
     dim3 grid(max_split, Hkv, nb);
-    if (bifocal && paged)
-      hipLaunchKernelGGL((decode_split_kernel<true, true>), grid, dim3(256), 0, stream, dp, ds, tt);
-    else if (bifocal)
-      hipLaunchKernelGGL((decode_split_kernel<true, false>), grid, dim3(256), 0, stream, dp, ds, tt);
-    else if (paged)
-      hipLaunchKernelGGL((decode_split_kernel<false, true>), grid, dim3(256), 0, stream, dp, ds, tt);
-    else
-      hipLaunchKernelGGL((decode_split_kernel<false, false>), grid, dim3(256), 0, stream, dp, ds, tt);
+    // non-temporal K / V loads unless the launch reads little enough that
+    // its cache could stay resident in the 256 MB MALL between calls
+    const bool nt = kv_bytes >= kDecStreamBytes;
+    auto kern = bifocal ? (paged ? (nt ? decode_split_kernel<true, true, true> : decode_split_kernel<true, true, false>)
+                                 : (nt ? decode_split_kernel<true, false, true> : decode_split_kernel<true, false, false>))
+                        : (paged ? (nt ? decode_split_kernel<false, true, true> : decode_split_kernel<false, true, false>)
+                                 : (nt ? decode_split_kernel<false, false, true> : decode_split_kernel<false, false, false>));
+    hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, dp, ds, tt);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return bad(BF_ERR_HIP, std::string("decode split launch: ") + hipGetErrorString(e));
     hipLaunchKernelGGL(decode_combine_kernel, dim3(Hq, nb, kHeadDim / 32), dim3(256), 0, stream, dp, ds);

@@ -640,6 +640,12 @@ __device__ __forceinline__ void run_pass(const uint16_t* qsrc, const uint16_t* k
                                          uint4* sK, uint4* sV, RowState& rs,
                                          f32x16 (&oacc)[4]) {
   const int li = lane & 31, hl = lane >> 5;
+  // The tile range is wave-uniform but derives from sequence-table entries
+  // that the compiler sees as per-lane values; held in scalar registers, the
+  // tile addresses and buffer descriptors below are formed by scalar
+  // arithmetic instead of a per-load loop over the lanes' values.
+  ktb = __builtin_amdgcn_readfirstlane(ktb);
+  kte = __builtin_amdgcn_readfirstlane(kte);
   bf16x8 qf[8];
   {
     const int row = wr.r0 + li;

@@ -112,7 +112,42 @@ struct Oct<float> {
   }
 };
 
-template <typename T>
+// Loads and stores of one 8-element piece, optionally non-temporal: a large
+// pre-step streams every byte once (each input read once, each output written
+// once), and keeping those lines in the caches only evicts others.
+typedef __attribute__((ext_vector_type(4))) unsigned int ru32x4;
+typedef __attribute__((ext_vector_type(4))) float rf32x4;
+template <bool NT, typename E>
+__device__ __forceinline__ E ld_piece(const E* p) {
+  if constexpr (NT) return __builtin_nontemporal_load((const __attribute__((address_space(1))) E*)p);
+  else return *(const __attribute__((address_space(1))) E*)p;
+}
+template <bool NT, typename E>
+__device__ __forceinline__ void st_piece(E* p, E v) {
+  if constexpr (NT) __builtin_nontemporal_store(v, (__attribute__((address_space(1))) E*)p);
+  else *(__attribute__((address_space(1))) E*)p = v;
+}
+template <bool NT>
+__device__ __forceinline__ uint4 ld_oct(const uint4* p) {
+  return __builtin_bit_cast(uint4, ld_piece<NT>((const ru32x4*)p));
+}
+template <bool NT>
+__device__ __forceinline__ F8 ld_oct(const F8* p) {
+  const rf32x4* q = (const rf32x4*)p;
+  return F8{__builtin_bit_cast(float4, ld_piece<NT>(q)), __builtin_bit_cast(float4, ld_piece<NT>(q + 1))};
+}
+template <bool NT>
+__device__ __forceinline__ void st_oct(uint4* p, uint4 v) {
+  st_piece<NT>((ru32x4*)p, __builtin_bit_cast(ru32x4, v));
+}
+template <bool NT>
+__device__ __forceinline__ void st_oct(F8* p, F8 v) {
+  rf32x4* q = (rf32x4*)p;
+  st_piece<NT>(q, __builtin_bit_cast(rf32x4, v.a));
+  st_piece<NT>(q + 1, __builtin_bit_cast(rf32x4, v.b));
+}
+
+template <typename T, bool NT>
 __global__ __launch_bounds__(256) void rope_kernel(RopeParams p, RopeSeqs sq, ThetaTable tt) {
   typedef typename Oct<T>::V V;
   constexpr int kBatch = 4;  // rows loaded before the first store
@@ -162,12 +197,12 @@ __global__ __launch_bounds__(256) void rope_kernel(RopeParams p, RopeSeqs sq, Th
       const int j = j0 + i;
       if (j < r1) {
         const T* src = (const T*)(j < p.Hq ? p.q : p.k) + row_off(j);
-        lo[i] = *(const V*)(src + e_lo);
-        hi[i] = *(const V*)(src + e_hi);
+        lo[i] = ld_oct<NT>((const V*)(src + e_lo));
+        hi[i] = ld_oct<NT>((const V*)(src + e_hi));
         if (cache && j >= p.Hq) {
           const T* vs = (const T*)p.v + row_off(j);
-          vlo[i] = *(const V*)(vs + e_lo);
-          vhi[i] = *(const V*)(vs + e_hi);
+          vlo[i] = ld_oct<NT>((const V*)(vs + e_lo));
+          vhi[i] = ld_oct<NT>((const V*)(vs + e_hi));
         }
       }
     }
@@ -180,23 +215,23 @@ __global__ __launch_bounds__(256) void rope_kernel(RopeParams p, RopeSeqs sq, Th
       const long long r = row_off(j);
       if (j < p.Hq) {
         T* dst = (T*)p.q_out + r;
-        *(V*)(dst + e_lo) = lo_o;
-        *(V*)(dst + e_hi) = hi_o;
+        st_oct<NT>((V*)(dst + e_lo), lo_o);
+        st_oct<NT>((V*)(dst + e_hi), hi_o);
         continue;
       }
       if (p.k_out) {
         T* dst = (T*)p.k_out + r;
-        *(V*)(dst + e_lo) = lo_o;
-        *(V*)(dst + e_hi) = hi_o;
+        st_oct<NT>((V*)(dst + e_lo), lo_o);
+        st_oct<NT>((V*)(dst + e_hi), hi_o);
       }
       if (cache) {
         const long long cr = (((long long)b * p.Hkv + (j - p.Hq)) * p.cap + pos) * kHeadDim;
         T* kc = (T*)p.k_cache + cr;
         T* vc = (T*)p.v_cache + cr;
-        *(V*)(kc + e_lo) = lo_o;
-        *(V*)(kc + e_hi) = hi_o;
-        *(V*)(vc + e_lo) = vlo[i];
-        *(V*)(vc + e_hi) = vhi[i];
+        st_oct<NT>((V*)(kc + e_lo), lo_o);
+        st_oct<NT>((V*)(kc + e_hi), hi_o);
+        st_oct<NT>((V*)(vc + e_lo), vlo[i]);
+        st_oct<NT>((V*)(vc + e_hi), vhi[i]);
       }
     }
   }
@@ -212,10 +247,17 @@ static hipError_t launch_rope(int dtype, RopeParams p, const RopeSeqs& sq,
   p.groups_per_tok = (rows + p.rows_per_group - 1) / p.rows_per_group;
   const long long groups = (long long)p.n_tok * p.groups_per_tok;
   const int grid = (int)((groups + 31) / 32);
-  if (dtype == 0)
-    hipLaunchKernelGGL(rope_kernel<uint16_t>, dim3(grid), dim3(256), 0, stream, p, sq, tt);
-  else
-    hipLaunchKernelGGL(rope_kernel<float>, dim3(grid), dim3(256), 0, stream, p, sq, tt);
+  // non-temporal when the launch moves at least 64 MB (a quarter of the
+  // 256 MB MALL); a small step's outputs may still be cached for the next call
+  const long long moved = (long long)rows * p.n_tok * kHeadDim * (dtype == 0 ? 2 : 4) * 2;
+  const bool nt = moved >= (64LL << 20);
+  if (dtype == 0) {
+    if (nt) hipLaunchKernelGGL((rope_kernel<uint16_t, true>), dim3(grid), dim3(256), 0, stream, p, sq, tt);
+    else hipLaunchKernelGGL((rope_kernel<uint16_t, false>), dim3(grid), dim3(256), 0, stream, p, sq, tt);
+  } else {
+    if (nt) hipLaunchKernelGGL((rope_kernel<float, true>), dim3(grid), dim3(256), 0, stream, p, sq, tt);
+    else hipLaunchKernelGGL((rope_kernel<float, false>), dim3(grid), dim3(256), 0, stream, p, sq, tt);
+  }
   return hipGetLastError();
 }
 
