@@ -73,7 +73,7 @@ def traffic_for(kernel_key):
 COPY_BYTES = 256 * 1024 * 1024
 # kernels whose HBM traffic is reported: key -> substring of the kernel name
 TRAFFIC_KERNELS = {"prefill_bf16_kernel_bifocal": "prefill_bf16_kernel<true, false>",
-                   "decode_split_kernel_bifocal": "decode_split_kernel<true>",
+                   "decode_split_kernel_bifocal": "decode_split_kernel<true, false, true>",
                    "rope_kernel": "rope_kernel",
                    "copy": "copyBuffer"}
 
