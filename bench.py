@@ -13,7 +13,8 @@ flops 4 * D * Hq * L (L + 1) / 2 (one score and one PV product per causal
 pair) over the measured prefill time. Extra fields report the decode
 bandwidth, position aliasing, the library's plain causal attention on the
 same shapes (overhead reference), chunks of the last 4096 / 16384 queries
-against the 128K cache, roofline fractions against MI355X peaks
+against the 128K cache (contiguous, and 4096 over 16-key pages), roofline
+fractions against MI355X peaks
 (bf16 dense MFMA 2.5 PFLOP/s, HBM 8 TB/s) and the fp64 CPU oracle timed on a
 bounded row sample of the prefill workload.
 """
@@ -394,6 +395,23 @@ def main():
         c_ms = time_calls(cfn, 5, stream)
         c_flops = 4.0 * D * Hq * (lq * L - lq * (lq - 1) / 2)  # positions L - lq .. L - 1
         chunk[str(lq)] = {"ms": round(c_ms, 3), "tflops": round(c_flops / (c_ms * 1e-3) / 1e12, 2)}
+        if lq == 4096:  # the same chunk over a shuffled pool of 16-key pages
+            npg = L // 16
+            perm = torch.randperm(npg, generator=torch.Generator().manual_seed(17)).cuda()
+            kpg = torch.empty((npg, Hkv, 16, D), dtype=torch.bfloat16, device="cuda")
+            vpg = torch.empty_like(kpg)
+            kpg[perm] = kd.view(Hkv, npg, 16, D).permute(1, 0, 2, 3)
+            vpg[perm] = vd.view(Hkv, npg, 16, D).permute(1, 0, 2, 3)
+            tbl = perm.to(torch.int32).view(1, npg)
+            wsp = bfl.alloc_workspace(bfl.chunk_workspace_bytes(1, lq, L, Hq, Hkv, paged=True), "cuda")
+            pfn = lambda: bfl.prefill_chunk_paged(qch, kpg, vpg, tbl, [0, lq], [L], cfg["w0"],
+                                                  cfg["w_pre"], cfg["theta"], "fi", scale, out=och,
+                                                  workspace=wsp)
+            pfn()
+            p_ms = time_calls(pfn, 5, stream)
+            chunk["4096_paged16"] = {"ms": round(p_ms, 3),
+                                     "tflops": round(c_flops / (p_ms * 1e-3) / 1e12, 2)}
+            del kpg, vpg, tbl, wsp
         del qch, och, wsc
 
     log("raw-input pre-step")

@@ -120,13 +120,14 @@ int bifocal_prefill(const void* q, const void* k, const void* v, void* o, float*
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Workspace bytes of bifocal_prefill_chunk: q_tokens = cu_q[batch] (the
- * packed queries), kv_tokens = the sum of seqlens[b] (the keys the call
- * reads). Returns 0 for invalid arguments (also kv_tokens < q_tokens).
+ * Workspace bytes of bifocal_prefill_chunk (paged = 0) and
+ * bifocal_prefill_chunk_paged (paged = 1): q_tokens = cu_q[batch] (the packed
+ * queries), kv_tokens = the sum of seqlens[b] (the keys the call reads).
+ * Returns 0 for invalid arguments (also kv_tokens < q_tokens).
  */
 size_t bifocal_chunk_workspace_bytes(int32_t batch, int64_t q_tokens, int64_t kv_tokens,
                                      int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim,
-                                     int32_t dtype);
+                                     int32_t dtype, int32_t paged);
 
 /*
  * Multi-token queries against a KV cache (chunked prefill, a prompt suffix
@@ -148,7 +149,7 @@ size_t bifocal_chunk_workspace_bytes(int32_t batch, int64_t q_tokens, int64_t kv
  *   s_len_host       : host int32 [batch] or NULL; s_len[b] >= N_b (pass
  *                      the full prompt length to reproduce a one-shot
  *                      bifocal_prefill of that prompt chunk by chunk)
- *   workspace        : bifocal_chunk_workspace_bytes(batch, Tq, sum N_b, ...)
+ *   workspace        : bifocal_chunk_workspace_bytes(batch, Tq, sum N_b, ..., 0)
  * Other arguments as bifocal_prefill (bf16 or fp32; every long_mode).
  * With Lq_b = N_b and s_len = NULL this is bifocal_prefill of the cached
  * sequences; with Lq_b = 1 it is bifocal_decode.
@@ -163,6 +164,31 @@ int bifocal_prefill_chunk(const void* q, const void* k_cache, const void* v_cach
                           int64_t w0, int64_t w_pre, double rope_theta, int32_t long_mode,
                           float softmax_scale, void* workspace, size_t workspace_bytes,
                           void* stream);
+
+/*
+ * bifocal_prefill_chunk over a PAGED KV cache: the same computation and
+ * arguments, with the cache split into fixed-size pages.
+ *   k_pages, v_pages : [num_pages, n_heads_kv, page_size, head_dim] dtype
+ *   block_table      : DEVICE int32 [batch, max_pages_per_seq]; keys
+ *                      p * page_size .. (p + 1) * page_size - 1 of sequence b
+ *                      are in page block_table[b][p] (entries clamped to
+ *                      [0, num_pages - 1]; only pages holding keys below N_b
+ *                      are read)
+ *   page_size        : a power of two, 1 <= page_size <= 2^20
+ *   seqlens_host     : Lq_b <= N_b <= max_pages_per_seq * page_size
+ *   workspace        : bifocal_chunk_workspace_bytes(..., paged = 1)
+ * The keys are gathered once per call into a packed copy in the workspace,
+ * so the result is bitwise that of bifocal_prefill_chunk on a contiguous
+ * cache holding the same keys.
+ */
+int bifocal_prefill_chunk_paged(const void* q, const void* k_pages, const void* v_pages, void* o,
+                                float* lse, const int32_t* block_table, const int32_t* cu_q_host,
+                                const int32_t* seqlens_host, const int32_t* s_len_host,
+                                int32_t batch, int32_t page_size, int32_t max_pages_per_seq,
+                                int32_t num_pages, int32_t n_heads_q, int32_t n_heads_kv,
+                                int32_t head_dim, int32_t dtype, int64_t w0, int64_t w_pre,
+                                double rope_theta, int32_t long_mode, float softmax_scale,
+                                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Single-token bifocal decode over a KV cache (bf16 only).

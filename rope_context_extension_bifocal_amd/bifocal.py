@@ -25,7 +25,7 @@ LONG_MODES = {"fi": BF_LONG_FI, "pa": BF_LONG_PA, "band": BF_LONG_NONE,
 _DTYPES = {torch.bfloat16: BF_DTYPE_BF16, torch.float32: BF_DTYPE_FP32}
 
 EXPORTED = ("bifocal_s_of_L", "bifocal_workspace_bytes", "bifocal_prefill", "bifocal_decode",
-            "bifocal_chunk_workspace_bytes", "bifocal_prefill_chunk",
+            "bifocal_chunk_workspace_bytes", "bifocal_prefill_chunk", "bifocal_prefill_chunk_paged",
             "bifocal_decode_paged", "plain_attention_ref_gpu", "bifocal_rope_prefill", "bifocal_rope_append",
             "bifocal_test_pair_map", "bifocal_last_error")
 
@@ -56,7 +56,10 @@ def lib():
         L.bifocal_prefill.argtypes = [p, p, p, p, p, p, i32, i32, i32, i32, i32, i64, i64, f64,
                                       i32, f32, p, sz, p]
         L.bifocal_chunk_workspace_bytes.restype = sz
-        L.bifocal_chunk_workspace_bytes.argtypes = [i32, i64, i64, i32, i32, i32, i32]
+        L.bifocal_chunk_workspace_bytes.argtypes = [i32, i64, i64, i32, i32, i32, i32, i32]
+        L.bifocal_prefill_chunk_paged.restype = ctypes.c_int
+        L.bifocal_prefill_chunk_paged.argtypes = [p, p, p, p, p, p, p, p, p, i32, i32, i32, i32, i32,
+                                                  i32, i32, i32, i64, i64, f64, i32, f32, p, sz, p]
         L.bifocal_prefill_chunk.restype = ctypes.c_int
         L.bifocal_prefill_chunk.argtypes = [p, p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32,
                                             i64, i64, f64, i32, f32, p, sz, p]
@@ -144,10 +147,10 @@ def prefill(q, k, v, cu_seqlens, w0, w_pre, rope_theta, long_mode="fi", softmax_
 
 
 def chunk_workspace_bytes(batch, q_tokens, kv_tokens, n_heads_q, n_heads_kv, head_dim=128,
-                          dtype=torch.bfloat16):
+                          dtype=torch.bfloat16, paged=False):
     return int(lib().bifocal_chunk_workspace_bytes(int(batch), int(q_tokens), int(kv_tokens),
                                                    int(n_heads_q), int(n_heads_kv), int(head_dim),
-                                                   _DTYPES[dtype]))
+                                                   _DTYPES[dtype], int(bool(paged))))
 
 
 def prefill_chunk(q, k_cache, v_cache, cu_q, seqlens, w0, w_pre, rope_theta, long_mode="fi",
@@ -174,6 +177,33 @@ def prefill_chunk(q, k_cache, v_cache, cu_q, seqlens, w0, w_pre, rope_theta, lon
                                        int(w_pre), float(rope_theta), LONG_MODES[long_mode],
                                        _scale(softmax_scale, D), _ptr(workspace),
                                        workspace.numel(), _stream(stream)))
+    return (o, lse) if return_lse else o
+
+
+def prefill_chunk_paged(q, k_pages, v_pages, block_table, cu_q, seqlens, w0, w_pre, rope_theta,
+                        long_mode="fi", softmax_scale=None, s_len=None, return_lse=False, out=None,
+                        lse=None, workspace=None, stream=None):
+    """prefill_chunk over a paged cache: pages [num_pages,Hkv,page,D] and a
+    device int32 block table [B,max_pages]."""
+    Hq, Tq, D = q.shape
+    num_pages, Hkv, page = k_pages.shape[0], k_pages.shape[1], k_pages.shape[2]
+    B = len(cu_q) - 1
+    o = out if out is not None else torch.empty_like(q)
+    if return_lse and lse is None:
+        lse = torch.empty((Hq, Tq), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = alloc_workspace(chunk_workspace_bytes(B, Tq, sum(int(n) for n in seqlens), Hq,
+                                                          Hkv, D, q.dtype, paged=True), q.device)
+    cu = _i32_array(cu_q)
+    sl = _i32_array(seqlens)
+    sls = _i32_array(s_len) if s_len is not None else None
+    _check(lib().bifocal_prefill_chunk_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(o),
+                                             _ptr(lse), _ptr(block_table), cu, sl, sls, B, page,
+                                             block_table.shape[1], num_pages, Hq, Hkv, D,
+                                             _DTYPES[q.dtype], int(w0), int(w_pre),
+                                             float(rope_theta), LONG_MODES[long_mode],
+                                             _scale(softmax_scale, D), _ptr(workspace),
+                                             workspace.numel(), _stream(stream)))
     return (o, lse) if return_lse else o
 
 

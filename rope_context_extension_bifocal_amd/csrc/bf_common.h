@@ -60,11 +60,20 @@ struct PrefillParams {
   int max_nrb;      // 1 + the largest rank index rb + rboff[b]
 };
 
+// A paged K / V source: pages [num_pages][Hkv][page][D], key j of sequence
+// b in page block_table[b * max_pages + j / page] (entries clamped to the pool).
+struct PagedKV {
+  const int* block_table;  // null: the K / V layout of SeqTable (h * k_hstride + kbase[b] + j)
+  int page_log2, max_pages, num_pages;
+};
+
 struct PrepParams {
   const void* q;  // [Hq][T][D]
-  const void* k;  // rows h * k_hstride + kbase[b] + j
+  const void* k;  // rows h * k_hstride + kbase[b] + j, or pages (pk)
   void* q2;       // [Hq][T][D]
   void* k2;       // [Hkv][Tk][D]
+  void* kcopy;    // [Hkv][Tk][D] packed copy of the keys (paged source only), else null
+  PagedKV pk;
   long long k_hstride;
   int T, Tk, Hq, Hkv;
   int long_mode;  // 0 = FI, 1 = PA
@@ -73,8 +82,9 @@ struct PrepParams {
 };
 
 struct VtParams {
-  const void* v;  // rows h * k_hstride + kbase[b] + j (the layout of K)
+  const void* v;  // rows h * k_hstride + kbase[b] + j (the layout of K), or pages (pk)
   void* vt;       // [Hkv][D][Tpad]
+  PagedKV pk;
   long long k_hstride;
   int Tpad, Hkv;
 };

@@ -97,19 +97,22 @@ PrefillGeom prefill_geom(int dtype, int G) {
 }
 
 struct PrefillWs {
-  size_t vt_off, q2_off, k2_off, total;
+  size_t vt_off, q2_off, k2_off, kc_off, total;
 };
 
 // Workspace of Tq packed queries against Tk keys (a one-shot prefill has
-// Tq = Tk = T): V^T padded per sequence, q'' and k''.
-PrefillWs prefill_ws_layout(int batch, long long Tq, long long Tk, int Hq, int Hkv, int dtype) {
+// Tk = Tq = T): V^T padded per sequence, q'', k'', and for a paged key
+// source the packed copy of the keys.
+PrefillWs prefill_ws_layout(int batch, long long Tq, long long Tk, int Hq, int Hkv, int dtype,
+                            bool paged = false) {
   const size_t es = elem_size(dtype);
   const size_t tpad_bound = (size_t)Tk + 63u * (size_t)batch;
   PrefillWs w;
   w.vt_off = 0;
   w.q2_off = align256((size_t)Hkv * bf::kHeadDim * tpad_bound * es);
   w.k2_off = w.q2_off + align256((size_t)Hq * (size_t)Tq * bf::kHeadDim * es);
-  w.total = w.k2_off + align256((size_t)Hkv * (size_t)Tk * bf::kHeadDim * es);
+  w.kc_off = w.k2_off + align256((size_t)Hkv * (size_t)Tk * bf::kHeadDim * es);
+  w.total = w.kc_off + (paged ? align256((size_t)Hkv * (size_t)Tk * bf::kHeadDim * es) : 0);
   return w;
 }
 
@@ -156,6 +159,7 @@ struct RowsJob {
   std::vector<int> cu, qpos;
   std::vector<long long> kbase, slen;
   long long k_hstride = 0, k_rows = 0;
+  bf::PagedKV pk{nullptr, 0, 0, 0};  // paged K / V source (block table of the whole batch)
   int batch = 0, Hq = 0, Hkv = 0, dtype = 0;
   long long w0 = 0, w_pre = 1;
   double theta = 10000.0;
@@ -187,13 +191,14 @@ int run_rows(RowsJob& j) {
     vt_off[b + 1] = vt_off[b] + (int)((N + bf::kKeyTile - 1) / bf::kKeyTile) * bf::kKeyTile;
   }
   Tk = kcu[batch];
-  const PrefillWs wl = prefill_ws_layout(batch, Tq, Tk, Hq, Hkv, dtype);
+  const bool paged = j.pk.block_table != nullptr;
+  const PrefillWs wl = prefill_ws_layout(batch, Tq, Tk, Hq, Hkv, dtype, paged);
   if (!j.ws) return fail(BF_ERR_WORKSPACE, "workspace is null");
   if ((uintptr_t)j.ws & 255u) return fail(BF_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   const bool shift = bifocal && (j.mode & BF_LONG_SHIFT);
   const int mode = j.mode & ~BF_LONG_SHIFT;
   const bool band_only = bifocal && mode == BF_LONG_NONE;
-  const size_t need = bifocal && !band_only ? wl.total : wl.q2_off;
+  const size_t need = paged ? wl.total : bifocal && !band_only ? wl.kc_off : wl.q2_off;
   if (j.ws_bytes < need)
     return fail(BF_ERR_WORKSPACE, "workspace too small: %zu bytes given, %zu needed", j.ws_bytes, need);
 
@@ -223,7 +228,9 @@ int run_rows(RowsJob& j) {
       if (s < 1 || s > (1LL << 30)) return fail(BF_ERR_INVALID_ARG, "s(L) out of range");
       st.s[i] = (int)s;
       st.qpos[i] = j.qpos[b0 + i];
-      st.kbase[i] = j.kbase[b0 + i];
+      // a paged source is gathered into the packed copy, which the tile
+      // kernel then reads like packed keys
+      st.kbase[i] = paged ? kcu[b0 + i] : j.kbase[b0 + i];
       // far pairs to score (bifocal) or to drop (band only): the last query
       // (position N - 1) reaches back past the window
       if ((s > 1 || band_only) && j.w0 < N) any_far = true;
@@ -233,18 +240,21 @@ int run_rows(RowsJob& j) {
       max_nrb = std::max(max_nrb, st.nrb[i] + st.rboff[i]);
     }
     hipError_t e = hipSuccess;
-    bf::VtParams vp{j.v, wsb + wl.vt_off, j.k_hstride, Tpad, Hkv};
+    bf::PagedKV pk = j.pk;  // the block-table rows of this launch's sequences
+    if (paged) pk.block_table += (size_t)b0 * pk.max_pages;
+    bf::VtParams vp{j.v, wsb + wl.vt_off, pk, j.k_hstride, Tpad, Hkv};
     e = bf::launch_vt_transpose(dtype, vp, st, j.stream);
     if (e != hipSuccess) return fail(BF_ERR_HIP, "vt_transpose launch: %s", hipGetErrorString(e));
-    if (bifocal && any_far && !band_only) {
-      bf::PrepParams pp{j.q, j.k, wsb + wl.q2_off, wsb + wl.k2_off, j.k_hstride, (int)Tq, (int)Tk,
-                        Hq, Hkv, mode, shift ? 1 : 0, j.w0};
+    if ((bifocal && any_far && !band_only) || paged) {
+      // band-only or s = 1 sequences get no rotation: the prep only gathers
+      bf::PrepParams pp{j.q, j.k, wsb + wl.q2_off, wsb + wl.k2_off, paged ? wsb + wl.kc_off : nullptr, pk,
+                        j.k_hstride, (int)Tq, (int)Tk, Hq, Hkv, mode, shift ? 1 : 0, j.w0};
       e = bf::launch_correction_prep(dtype, pp, st, tt, j.stream);
       if (e != hipSuccess) return fail(BF_ERR_HIP, "correction_prep launch: %s", hipGetErrorString(e));
     }
     bf::PrefillParams pp;
     pp.q = j.q;
-    pp.k = j.k;
+    pp.k = paged ? (const void*)(wsb + wl.kc_off) : j.k;
     pp.q2 = wsb + wl.q2_off;
     pp.k2 = wsb + wl.k2_off;
     pp.vt = wsb + wl.vt_off;
@@ -252,8 +262,8 @@ int run_rows(RowsJob& j) {
     pp.lse = j.lse;
     pp.w0 = j.w0;
     pp.scale_log2 = j.scale * 1.4426950408889634f;
-    pp.k_hstride = j.k_hstride;
-    pp.k_rows = j.k_rows;
+    pp.k_hstride = paged ? Tk : j.k_hstride;
+    pp.k_rows = paged ? (long long)Hkv * Tk : j.k_rows;
     pp.T = (int)Tq;
     pp.Tk = (int)Tk;
     pp.Tpad = Tpad;
@@ -314,15 +324,37 @@ int run_prefill(bool bifocal, const void* q, const void* k, const void* v, void*
   return run_rows(j);
 }
 
-// Chunk of queries against a KV cache [B][Hkv][cap][D] (bifocal_prefill_chunk).
+// A paged cache of a chunk call: pages [num_pages][Hkv][page_size][D].
+struct ChunkPages {
+  const int32_t* block_table;  // device [batch][max_pages]
+  int page_size, max_pages, num_pages;
+};
+
+// Chunk of queries against a KV cache [B][Hkv][cap][D] (bifocal_prefill_chunk)
+// or a paged cache (bifocal_prefill_chunk_paged: pages != null, cap = the
+// most keys a sequence's pages hold).
 int run_chunk(const void* q, const void* kc, const void* vc, void* o, float* lse,
               const int32_t* cu_q, const int32_t* seqlens, const int32_t* s_len, int batch,
               int cap, int Hq, int Hkv, int head_dim, int dtype, long long w0, long long w_pre,
-              double theta, int mode, float scale, void* ws, size_t ws_bytes, hipStream_t stream) {
+              double theta, int mode, float scale, void* ws, size_t ws_bytes, hipStream_t stream,
+              const ChunkPages* pages = nullptr) {
   if (!q || !kc || !vc || !o || !cu_q || !seqlens)
     return fail(BF_ERR_INVALID_ARG, "null tensor, cu_q or seqlens pointer");
   int rc = check_rows_common(true, batch, Hq, Hkv, head_dim, dtype, w0, w_pre, theta, mode, scale);
   if (rc) return rc;
+  int page_log2 = 0;
+  if (pages) {
+    const int ps = pages->page_size;
+    if (ps < 1 || ps > (1 << 20) || (ps & (ps - 1)))
+      return fail(BF_ERR_INVALID_ARG, "page_size must be a power of two in [1, 2^20] (got %d)", ps);
+    if (pages->max_pages < 1 || pages->num_pages < 1)
+      return fail(BF_ERR_INVALID_ARG, "max_pages_per_seq and num_pages must be >= 1");
+    if (!pages->block_table || ((uintptr_t)pages->block_table & 3u))
+      return fail(BF_ERR_INVALID_ARG, "block_table must be a non-null 4-byte aligned device pointer");
+    while ((1 << page_log2) < ps) ++page_log2;
+    const long long hold = (long long)pages->max_pages * ps;
+    cap = (int)std::min<long long>(hold, 0x7fffffffLL);
+  }
   if (cap < 1) return fail(BF_ERR_INVALID_ARG, "cache_capacity must be >= 1 (got %d)", cap);
   if (cu_q[0] != 0) return fail(BF_ERR_INVALID_ARG, "cu_q[0] must be 0 (got %d)", cu_q[0]);
   long long Tk = 0;
@@ -330,15 +362,15 @@ int run_chunk(const void* q, const void* kc, const void* vc, void* o, float* lse
     const int Lq = cu_q[b + 1] - cu_q[b];
     if (Lq < 1) return fail(BF_ERR_INVALID_ARG, "cu_q must be strictly increasing (b=%d: %d -> %d)", b, cu_q[b], cu_q[b + 1]);
     if (seqlens[b] < Lq || seqlens[b] > cap)
-      return fail(BF_ERR_INVALID_ARG, "seqlens[%d] = %d must lie in [chunk length %d, cache_capacity %d]",
-                  b, seqlens[b], Lq, cap);
+      return fail(BF_ERR_INVALID_ARG, "seqlens[%d] = %d must lie in [chunk length %d, %s %d]", b, seqlens[b],
+                  Lq, pages ? "max_pages_per_seq * page_size" : "cache_capacity", cap);
     if (s_len && s_len[b] < seqlens[b])
       return fail(BF_ERR_INVALID_ARG, "s_len[%d] = %d is below seqlens[%d] = %d", b, s_len[b], b, seqlens[b]);
     Tk += seqlens[b];
   }
   const long long Tq = cu_q[batch];
   if (Tk + 63LL * batch > (1LL << 31) - 1) return fail(BF_ERR_INVALID_ARG, "too many keys (%lld)", Tk);
-  if ((long long)batch * Hkv * cap > (1LL << 40)) return fail(BF_ERR_INVALID_ARG, "cache too large");
+  if (!pages && (long long)batch * Hkv * cap > (1LL << 40)) return fail(BF_ERR_INVALID_ARG, "cache too large");
   if (!aligned16(q) || !aligned16(kc) || !aligned16(vc) || !aligned16(o))
     return fail(BF_ERR_INVALID_ARG, "q, k_cache, v_cache and o must be 16-byte aligned");
   if (lse && ((uintptr_t)lse & 3u)) return fail(BF_ERR_INVALID_ARG, "lse must be 4-byte aligned");
@@ -357,6 +389,7 @@ int run_chunk(const void* q, const void* kc, const void* vc, void* o, float* lse
   (void)Tq;
   j.k_hstride = cap;
   j.k_rows = (long long)batch * Hkv * cap;
+  if (pages) j.pk = bf::PagedKV{pages->block_table, page_log2, pages->max_pages, pages->num_pages};
   j.batch = batch; j.Hq = Hq; j.Hkv = Hkv; j.dtype = dtype;
   j.w0 = w0; j.w_pre = w_pre; j.theta = theta; j.mode = mode; j.scale = scale;
   j.ws = ws; j.ws_bytes = ws_bytes; j.stream = stream;
@@ -396,12 +429,12 @@ int bifocal_prefill(const void* q, const void* k, const void* v, void* o, float*
 
 size_t bifocal_chunk_workspace_bytes(int32_t batch, int64_t q_tokens, int64_t kv_tokens,
                                      int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim,
-                                     int32_t dtype) {
+                                     int32_t dtype, int32_t paged) {
   if (batch < 1 || q_tokens < 1 || kv_tokens < q_tokens || n_heads_q < 1 || n_heads_kv < 1 ||
       head_dim != bf::kHeadDim)
     return 0;
   if (dtype != BF_DTYPE_BF16 && dtype != BF_DTYPE_FP32) return 0;
-  return prefill_ws_layout(batch, q_tokens, kv_tokens, n_heads_q, n_heads_kv, dtype).total;
+  return prefill_ws_layout(batch, q_tokens, kv_tokens, n_heads_q, n_heads_kv, dtype, paged != 0).total;
 }
 
 int bifocal_prefill_chunk(const void* q, const void* k_cache, const void* v_cache, void* o,
@@ -414,6 +447,20 @@ int bifocal_prefill_chunk(const void* q, const void* k_cache, const void* v_cach
   return run_chunk(q, k_cache, v_cache, o, lse, cu_q_host, seqlens_host, s_len_host, batch,
                    cache_capacity, n_heads_q, n_heads_kv, head_dim, dtype, w0, w_pre, rope_theta,
                    long_mode, softmax_scale, workspace, workspace_bytes, (hipStream_t)stream);
+}
+
+int bifocal_prefill_chunk_paged(const void* q, const void* k_pages, const void* v_pages, void* o,
+                                float* lse, const int32_t* block_table, const int32_t* cu_q_host,
+                                const int32_t* seqlens_host, const int32_t* s_len_host,
+                                int32_t batch, int32_t page_size, int32_t max_pages_per_seq,
+                                int32_t num_pages, int32_t n_heads_q, int32_t n_heads_kv,
+                                int32_t head_dim, int32_t dtype, int64_t w0, int64_t w_pre,
+                                double rope_theta, int32_t long_mode, float softmax_scale,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  const ChunkPages pg{block_table, page_size, max_pages_per_seq, num_pages};
+  return run_chunk(q, k_pages, v_pages, o, lse, cu_q_host, seqlens_host, s_len_host, batch, 1,
+                   n_heads_q, n_heads_kv, head_dim, dtype, w0, w_pre, rope_theta, long_mode,
+                   softmax_scale, workspace, workspace_bytes, (hipStream_t)stream, &pg);
 }
 
 int bifocal_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,

@@ -114,6 +114,17 @@ __device__ __forceinline__ void st_elem(T* p, float f) {
   else *p = f;
 }
 
+// Row (in elements / kHeadDim) of key j of launch sequence b, KV head h, in a
+// K / V source: the SeqTable layout, or pages through the block table.
+__device__ __forceinline__ long long kv_row(const PagedKV& pk, const SeqTable& st,
+                                            long long k_hstride, int Hkv, int b, int h,
+                                            long long j) {
+  if (pk.block_table == nullptr) return (long long)h * k_hstride + st.kbase[b] + j;
+  int pg = pk.block_table[(size_t)b * pk.max_pages + (j >> pk.page_log2)];
+  pg = min(max(pg, 0), pk.num_pages - 1);
+  return (((long long)pg * Hkv + h) << pk.page_log2) + (j & ((1LL << pk.page_log2) - 1));
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void correction_prep_kernel(PrepParams p, SeqTable st,
                                                               ThetaTable tt) {
@@ -125,23 +136,35 @@ __global__ __launch_bounds__(256) void correction_prep_kernel(PrepParams p, SeqT
   int b = 0;
   while (b + 1 < st.n && tok >= cu(b + 1)) ++b;
   const int s = st.s[b];
-  if (s == 1) return;  // no far branch for this sequence
+  const bool rot = s > 1;         // s = 1: no far branch for this sequence
+  const bool copy = keys && p.kcopy != nullptr;  // paged keys: gather the packed copy
+  if (!rot && !copy) return;
   const long long row = tok - cu(b);
-  const long long pos = keys ? row : st.qpos[b] + row;
-  long long num = corr_num(pos, s, p.long_mode);
-  // queries with the band-edge continuity shift: (w0 - phi(w0)) * s is the
-  // exact integer w0 (s - 1) (FI) or (w0 - floor(w0 / s)) s (PA)
-  if (!keys && p.shift) num += p.long_mode == 1 ? (p.w0 - p.w0 / s) * s : p.w0 * (s - 1);
-  double sd, cd;
-  sincos(tt.th[m] * ((double)num / (double)s), &sd, &cd);
-  const float c = (float)cd, sn = (float)sd;
+  float c = 1.f, sn = 0.f;
+  if (rot) {
+    const long long pos = keys ? row : st.qpos[b] + row;
+    long long num = corr_num(pos, s, p.long_mode);
+    // queries with the band-edge continuity shift: (w0 - phi(w0)) * s is the
+    // exact integer w0 (s - 1) (FI) or (w0 - floor(w0 / s)) s (PA)
+    if (!keys && p.shift) num += p.long_mode == 1 ? (p.w0 - p.w0 / s) * s : p.w0 * (s - 1);
+    double sd, cd;
+    sincos(tt.th[m] * ((double)num / (double)s), &sd, &cd);
+    c = (float)cd;
+    sn = (float)sd;
+  }
   const int nh = keys ? p.Hkv : p.Hq;
   for (int h = 0; h < nh; ++h) {
     const T* src;
     T* dst;
     if (keys) {
-      src = (const T*)p.k + ((size_t)h * p.k_hstride + st.kbase[b] + row) * kHeadDim;
+      src = (const T*)p.k + kv_row(p.pk, st, p.k_hstride, p.Hkv, b, h, row) * kHeadDim;
       dst = (T*)p.k2 + ((size_t)h * p.Tk + tok) * kHeadDim;
+      if (copy) {
+        T* cp = (T*)p.kcopy + ((size_t)h * p.Tk + tok) * kHeadDim;
+        cp[m] = src[m];
+        cp[m + kPairs] = src[m + kPairs];
+      }
+      if (!rot) continue;
     } else {
       src = (const T*)p.q + ((size_t)h * p.T + tok) * kHeadDim;
       dst = (T*)p.q2 + ((size_t)h * p.T + tok) * kHeadDim;
@@ -165,10 +188,17 @@ __global__ __launch_bounds__(256) void vt_transpose_kernel(VtParams p, SeqTable 
   while (b + 1 < st.n && c >= st.vt_off[b + 1]) ++b;
   const int p0 = c - st.vt_off[b];
   const int L = st.kcu[b + 1] - st.kcu[b];
-  const T* v = (const T*)p.v + ((size_t)h * p.k_hstride + st.kbase[b]) * kHeadDim;
+  __shared__ long long rows[kKeyTile];  // V row of each key of the tile, -1 past the end
+  if (threadIdx.x < kKeyTile) {
+    const int j = p0 + threadIdx.x;
+    rows[threadIdx.x] = j < L ? kv_row(p.pk, st, p.k_hstride, p.Hkv, b, h, j) : -1;
+  }
+  __syncthreads();
+  const T* v = (const T*)p.v;
   for (int e = threadIdx.x; e < kKeyTile * kHeadDim; e += 256) {
     const int r = e / kHeadDim, d = e % kHeadDim;
-    tile[r][d] = (p0 + r < L) ? v[(size_t)(p0 + r) * kHeadDim + d] : T(0);
+    const long long vr = rows[r];
+    tile[r][d] = vr >= 0 ? v[(size_t)vr * kHeadDim + d] : T(0);
   }
   __syncthreads();
   T* vt = (T*)p.vt + ((size_t)h * (p.Tpad / kKeyTile) + c / kKeyTile) * (kHeadDim * kKeyTile);

@@ -236,8 +236,10 @@ def test_chunk_workspace_bytes(L):
     assert ws == bfl.chunk_workspace_bytes(1, 4096, 131072, 32, 8, dtype=bfl.torch.bfloat16)
     assert bfl.chunk_workspace_bytes(1, 131072, 131072, 32, 8) == \
         bfl.workspace_bytes(bfl.BF_PHASE_PREFILL, 1, 131072, 32, 8)
-    assert L.bifocal_chunk_workspace_bytes(1, 10, 5, 2, 1, 128, 0) == 0  # fewer keys than queries
-    assert L.bifocal_chunk_workspace_bytes(1, 10, 20, 2, 1, 64, 0) == 0
+    assert L.bifocal_chunk_workspace_bytes(1, 10, 5, 2, 1, 128, 0, 0) == 0  # fewer keys than queries
+    assert L.bifocal_chunk_workspace_bytes(1, 10, 20, 2, 1, 64, 0, 0) == 0
+    # the paged call adds the packed copy of the keys (8 heads x 131072 keys x 256 B)
+    assert bfl.chunk_workspace_bytes(1, 4096, 131072, 32, 8, paged=True) - ws == 8 * 131072 * 256
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -258,3 +260,36 @@ def test_chunk_valid_arguments_reach_the_launch(L, monkeypatch):
     assert _chunk(L, dtype=1, mode=5, s_len=[1000, 1]) == bfl.BF_ERR_HIP
     assert _chunk(L, mode=2, w0=3) == bfl.BF_ERR_HIP
     assert _chunk(L, cu=[0, 100, 101], sl=[100, 128]) == bfl.BF_ERR_HIP  # whole-sequence chunk
+
+
+def _chunk_paged(L, **kw):
+    a = dict(q=P, kp=P, vp=P, o=P, lse=None, bt=P, cu=[0, 30, 31], sl=[100, 1], s_len=None,
+             page=16, maxp=8, npages=20, Hq=4, Hkv=2, D=128, dtype=0, w0=16, w_pre=64, theta=1e4,
+             mode=0, scale=0.088, ws=P, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    cu = (ctypes.c_int32 * len(a["cu"]))(*a["cu"])
+    sl = (ctypes.c_int32 * len(a["sl"]))(*a["sl"])
+    sls = (ctypes.c_int32 * len(a["s_len"]))(*a["s_len"]) if a["s_len"] is not None else None
+    return L.bifocal_prefill_chunk_paged(a["q"], a["kp"], a["vp"], a["o"], a["lse"], a["bt"], cu, sl,
+                                         sls, len(a["cu"]) - 1, a["page"], a["maxp"], a["npages"],
+                                         a["Hq"], a["Hkv"], a["D"], a["dtype"], a["w0"], a["w_pre"],
+                                         a["theta"], a["mode"], a["scale"], a["ws"], a["ws_bytes"],
+                                         a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(bt=None), -1), (dict(bt=ctypes.c_void_p(0x100002)), -1), (dict(page=24), -1),
+    (dict(page=0), -1), (dict(maxp=0), -1), (dict(npages=0), -1), (dict(sl=[129, 1]), -1),
+    (dict(sl=[29, 1]), -1), (dict(kp=None), -1), (dict(D=64), -2), (dict(mode=9), -1),
+    (dict(ws_bytes=10), -3), (dict(cu=[0, 30, 30]), -1),
+])
+def test_chunk_paged_validation(L, kw, code):
+    assert _chunk_paged(L, **kw) == code
+    assert len(L.bifocal_last_error()) > 0
+
+
+def test_chunk_paged_valid_arguments_reach_the_launch(L, monkeypatch):
+    monkeypatch.setenv("BIFOCAL_TEST_FAIL_LAUNCH", "1")
+    assert _chunk_paged(L) == bfl.BF_ERR_HIP
+    assert _chunk_paged(L, page=1, maxp=128, dtype=1, mode=2, w0=4) == bfl.BF_ERR_HIP
+    assert _chunk_paged(L, sl=[128, 128], cu=[0, 128, 256]) == bfl.BF_ERR_HIP  # 8 pages of 16 hold 128

@@ -4,7 +4,9 @@ bf16 max-abs 2e-2 / mean-abs 2e-3 and fp32 max-abs 1e-4. Cache slots past N_b
 hold NaN, so a read of them would show. Identities: a chunk that is the whole
 sequence is bitwise the one-shot bifocal_prefill (same engine, same work
 split); chunk by chunk with s_len = the prompt length reproduces the one-shot
-prefill. Needs an MI355X.
+prefill. bifocal_prefill_chunk_paged (shuffled page pools of 1 to 256 keys per
+page, junk in unused table entries) must be bitwise the contiguous call.
+Needs an MI355X.
 """
 import math
 
@@ -176,3 +178,78 @@ def test_chunk_is_deterministic():
     b = bfl.prefill_chunk(*args)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+def paginate(kc, vc, seqlens, page, seed, spare=3):
+    """Scatter caches [B, Hkv, cap, D] (on the GPU) into a shuffled page pool
+    [pages, Hkv, page, D]; unused block-table entries hold junk."""
+    B, Hkv, cap, D = kc.shape
+    need = [math.ceil(n / page) for n in seqlens]
+    total = sum(need) + spare
+    perm = torch.from_numpy(np.random.default_rng(seed).permutation(total)).to(kc.device)
+    kp = torch.zeros((total, Hkv, page, D), dtype=kc.dtype, device=kc.device)
+    vp = torch.zeros_like(kp)
+    table = torch.full((B, max(need) + 2), -5, dtype=torch.int32, device=kc.device)
+    nxt = 0
+    for b in range(B):
+        n, pgs = seqlens[b], need[b]
+        phys = perm[nxt:nxt + pgs]
+        nxt += pgs
+        table[b, :pgs] = phys.to(torch.int32)
+        for src, dst in ((kc, kp), (vc, vp)):
+            x = torch.zeros((Hkv, pgs * page, D), dtype=kc.dtype, device=kc.device)
+            x[:, :n] = src[b, :, :n]
+            dst[phys] = x.view(Hkv, pgs, page, D).permute(1, 0, 2, 3)
+    return kp, vp, table
+
+
+@pytest.mark.parametrize("page", [1, 16, 64, 256])
+@pytest.mark.parametrize("mode", ["fi", "pa+shift", "band"])
+def test_paged_chunk_equals_contiguous(page, mode):
+    Ns = [1000, 4097, 700, 2500, 129, 64]
+    Lqs = [300, 1, 700, 37, 64, 33]
+    cu = wl.cu_seqlens(Lqs)
+    q, kc, vc = chunk_inputs(Ns, Lqs, 8, 2, 4200, "bf16", 99)
+    q, kc, vc = q.cuda(), kc.cuda(), vc.cuda()
+    scale = 1 / math.sqrt(128)
+    o_c, l_c = bfl.prefill_chunk(q, kc, vc, cu, Ns, 256, 512, THETA, mode, scale, return_lse=True)
+    kp, vp, table = paginate(kc, vc, Ns, page, seed=page)
+    del kc, vc
+    o_p, l_p = bfl.prefill_chunk_paged(q, kp, vp, table, cu, Ns, 256, 512, THETA, mode, scale,
+                                       return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o_p, o_c) and torch.equal(l_p, l_c), (page, mode)
+
+
+def test_paged_chunk_fp32_and_s_len():
+    Ns, Lqs = [900, 300], [200, 300]
+    cu = wl.cu_seqlens(Lqs)
+    q, kc, vc = chunk_inputs(Ns, Lqs, 4, 1, 1000, "fp32", 100)
+    q, kc, vc = q.cuda(), kc.cuda(), vc.cuda()
+    scale = 1 / math.sqrt(128)
+    o_c = bfl.prefill_chunk(q, kc, vc, cu, Ns, 100, 256, THETA, "pa", scale, s_len=[3000, 300])
+    kp, vp, table = paginate(kc, vc, Ns, 32, seed=5)
+    o_p = bfl.prefill_chunk_paged(q, kp, vp, table, cu, Ns, 100, 256, THETA, "pa", scale,
+                                  s_len=[3000, 300])
+    torch.cuda.synchronize()
+    assert torch.equal(o_p, o_c)
+    o_ref, _ = oracle.chunk(q.cpu().numpy(), kc.cpu().numpy(), vc.cpu().numpy(), cu, Ns, 100, 256,
+                            THETA, "pa", scale, s_len=[3000, 300])
+    d = np.abs(o_p.cpu().numpy().astype(np.float64) - o_ref)
+    print(f"[paged chunk fp32] max-abs {d.max():.3e}", flush=True)
+    assert d.max() <= 1e-4
+
+
+def test_paged_chunk_4k_at_128k():
+    c = wl.CONFIGS["qwen3_8b_prefill_128k"]
+    N, Lq = c["lens"][0], 4096
+    q, kc, vc = chunk_inputs([N], [Lq], c["Hq"], c["Hkv"], N, "bf16", 101)
+    q, kc, vc = q.cuda(), kc.cuda(), vc.cuda()
+    scale = 1 / math.sqrt(128)
+    o_c = bfl.prefill_chunk(q, kc, vc, [0, Lq], [N], c["w0"], c["w_pre"], c["theta"], "fi", scale)
+    kp, vp, table = paginate(kc, vc, [N], 16, seed=6)
+    del kc, vc
+    o_p = bfl.prefill_chunk_paged(q, kp, vp, table, [0, Lq], [N], c["w0"], c["w_pre"], c["theta"],
+                                  "fi", scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o_p, o_c)
