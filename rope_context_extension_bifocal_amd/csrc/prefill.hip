@@ -610,6 +610,10 @@ __device__ __forceinline__ void pv_softmax(uint32_t slot_off, const u32x4 (&Pp)[
 #pragma unroll
   for (int i = 0; i < 4; ++i) load(i);
   __builtin_amdgcn_sched_barrier(0);
+  // While a wave is in this region the SIMD's arbiter prefers it: its MFMAs
+  // and softmax slices then interleave tightly, and the other wave of the
+  // SIMD (in its QK^T or barrier phase) fills the gaps.
+  __builtin_amdgcn_s_setprio(1);
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     if ((i & 3) == 0) {  // batch i / 4 has landed; send the next batch
@@ -652,6 +656,7 @@ __device__ __forceinline__ void pv_softmax(uint32_t slot_off, const u32x4 (&Pp)[
     }
     __builtin_amdgcn_sched_barrier(0);
   }
+  __builtin_amdgcn_s_setprio(0);
   rs.l_part = sum;
 }
 
