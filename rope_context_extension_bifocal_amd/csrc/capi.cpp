@@ -368,7 +368,6 @@ int run_chunk(const void* q, const void* kc, const void* vc, void* o, float* lse
       return fail(BF_ERR_INVALID_ARG, "s_len[%d] = %d is below seqlens[%d] = %d", b, s_len[b], b, seqlens[b]);
     Tk += seqlens[b];
   }
-  const long long Tq = cu_q[batch];
   if (Tk + 63LL * batch > (1LL << 31) - 1) return fail(BF_ERR_INVALID_ARG, "too many keys (%lld)", Tk);
   if (!pages && (long long)batch * Hkv * cap > (1LL << 40)) return fail(BF_ERR_INVALID_ARG, "cache too large");
   if (!aligned16(q) || !aligned16(kc) || !aligned16(vc) || !aligned16(o))
@@ -386,7 +385,6 @@ int run_chunk(const void* q, const void* kc, const void* vc, void* o, float* lse
     j.kbase[b] = (long long)b * Hkv * cap;
     j.slen[b] = s_len ? s_len[b] : seqlens[b];
   }
-  (void)Tq;
   j.k_hstride = cap;
   j.k_rows = (long long)batch * Hkv * cap;
   if (pages) j.pk = bf::PagedKV{pages->block_table, page_log2, pages->max_pages, pages->num_pages};
