@@ -151,22 +151,36 @@ def test_single_query_chunk_matches_decode():
     _check(o_d.float().cpu().numpy(), o_ref, "decode")
 
 
-def test_chunk_4k_at_128k_sampled():
-    # the last 4096 queries of a 131072-token sequence (Qwen3-8B shape, FI, s = 4)
+@pytest.mark.parametrize("mode", ["fi", "pa"])
+def test_chunk_4k_at_128k_sampled(mode):
+    # the last 4096 queries of a 131072-token sequence (Qwen3-8B shape, s = 4)
     c = wl.CONFIGS["qwen3_8b_prefill_128k"]
     N, Lq = c["lens"][0], 4096
     Hq, Hkv = c["Hq"], c["Hkv"]
     q, kc, vc = chunk_inputs([N], [Lq], Hq, Hkv, N, "bf16", 96)
     scale = 1 / math.sqrt(128)
     o = bfl.prefill_chunk(q.cuda(), kc.cuda(), vc.cuda(), [0, Lq], [N], c["w0"], c["w_pre"],
-                          c["theta"], "fi", scale)
+                          c["theta"], mode, scale)
     torch.cuda.synchronize()
     rows = wl.sample_rows(Lq, 20, [0, 1, 31, 32, 4094, 4095], seed=97)
-    o_ref, _ = oracle.chunk(q[:, rows].float().numpy(), kc.float().numpy(), vc.float().numpy(),
-                            [0, Lq], [N], c["w0"], c["w_pre"], c["theta"], "fi", scale, rows=rows,
-                            gathered=True)
-    _check(o[:, torch.from_numpy(np.asarray(rows)).cuda()].float().cpu().numpy(), o_ref,
-           "chunk 4k at 128k")
+    qs, kf, vf = q[:, rows].float().numpy(), kc.float().numpy(), vc.float().numpy()
+    o_ref, _ = oracle.chunk(qs, kf, vf, [0, Lq], [N], c["w0"], c["w_pre"], c["theta"], mode, scale,
+                            rows=rows, gathered=True)
+    og = o[:, torch.from_numpy(np.asarray(rows)).cuda()].float().cpu().numpy()
+    _check(og, o_ref, f"chunk 4k at 128k {mode}")
+    # discrimination, as for the one-shot 128K prefill: every sampled row has
+    # far pairs; the error must be small next to the gap to plain attention
+    # (no correction) and to the other long mode
+    err = np.linalg.norm(og - o_ref)
+    plain, _ = oracle.chunk(qs, kf, vf, [0, Lq], [N], 10**9, c["w_pre"], c["theta"], mode, scale,
+                            rows=rows, gathered=True)
+    other, _ = oracle.chunk(qs, kf, vf, [0, Lq], [N], c["w0"], c["w_pre"], c["theta"],
+                            "pa" if mode == "fi" else "fi", scale, rows=rows, gathered=True)
+    gap_plain, gap_mode = np.linalg.norm(o_ref - plain), np.linalg.norm(o_ref - other)
+    print(f"[chunk 128k discrimination {mode}] err {err:.3e} gap-plain {gap_plain:.3e} "
+          f"gap-other-mode {gap_mode:.3e}", flush=True)
+    assert err <= 0.05 * gap_plain
+    assert err <= 0.25 * gap_mode
 
 
 def test_chunk_is_deterministic():
