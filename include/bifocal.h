@@ -252,17 +252,21 @@ int plain_attention_ref_gpu(int32_t phase, const void* q, const void* k, const v
 
 /*
  * Raw-input pre-step for prefill: the model's ORIGINAL RoPE applied to raw
- * (position-free) q and k, giving the q', k' that bifocal_prefill takes, and
- * optionally the KV-cache fill for a following bifocal_decode.
+ * (position-free) q and k, giving the q', k' that bifocal_prefill (or, with
+ * start positions, bifocal_prefill_chunk) takes, and optionally the KV-cache
+ * fill for a following bifocal_decode / bifocal_prefill_chunk.
  *   q_raw, q_out : [n_heads_q,  T, head_dim]  dtype (bf16 or fp32)
  *   k_raw, k_out : [n_heads_kv, T, head_dim]  same dtype; k_out may be NULL
  *                  when k_cache is given
  *   cu_seqlens_host : as bifocal_prefill; token t of sequence b is rotated
- *                  at position t - cu[b]
+ *                  at position P_b + t - cu[b]
+ *   pos0_host    : host int32 [batch] start positions P_b >= 0, or NULL for
+ *                  0 (a chunk that continues a cached prefix starts at the
+ *                  prefix length)
  *   k_cache, v_cache, v : if k_cache is not NULL, k' and v of sequence b are
  *                  also written to k_cache / v_cache [batch, n_heads_kv,
- *                  cache_capacity, head_dim] at positions 0 .. L_b - 1
- *                  (L_b <= cache_capacity); v is [n_heads_kv, T, head_dim].
+ *                  cache_capacity, head_dim] at positions P_b .. P_b + L_b - 1
+ *                  (P_b + L_b <= cache_capacity); v is [n_heads_kv, T, head_dim].
  * q_out may be q_raw and k_out may be k_raw (in place); no other buffers may
  * overlap. theta_m = rope_theta^(-2m/D), half-split pairs (m, m + D/2); the
  * angle is formed in fp64, the rotation in fp32. No workspace.
@@ -272,7 +276,8 @@ int plain_attention_ref_gpu(int32_t phase, const void* q, const void* k, const v
  */
 int bifocal_rope_prefill(const void* q_raw, const void* k_raw, const void* v, void* q_out,
                          void* k_out, void* k_cache, void* v_cache, int32_t cache_capacity,
-                         const int32_t* cu_seqlens_host, int32_t batch, int32_t n_heads_q,
+                         const int32_t* cu_seqlens_host, const int32_t* pos0_host, int32_t batch,
+                         int32_t n_heads_q,
                          int32_t n_heads_kv, int32_t head_dim, int32_t dtype, double rope_theta,
                          void* stream);
 

@@ -73,8 +73,8 @@ def lib():
         L.plain_attention_ref_gpu.argtypes = [i32, p, p, p, p, p, p, i32, i32, i32, i32, i32,
                                               i32, f32, p, sz, p]
         L.bifocal_rope_prefill.restype = ctypes.c_int
-        L.bifocal_rope_prefill.argtypes = [p, p, p, p, p, p, p, i32, p, i32, i32, i32, i32, i32,
-                                           f64, p]
+        L.bifocal_rope_prefill.argtypes = [p, p, p, p, p, p, p, i32, p, p, i32, i32, i32, i32,
+                                           i32, f64, p]
         L.bifocal_rope_append.restype = ctypes.c_int
         L.bifocal_rope_append.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, f64,
                                           p]
@@ -291,11 +291,13 @@ def plain_decode(q, k_cache, v_cache, seqlens, softmax_scale=None, return_lse=Fa
 
 
 def rope_prefill(q_raw, k_raw, cu_seqlens, rope_theta, v=None, k_cache=None, v_cache=None,
-                 q_out=None, k_out=None, write_k=True, stream=None):
+                 q_out=None, k_out=None, write_k=True, pos0=None, stream=None):
     """Original RoPE on raw packed q [Hq,T,D] and k [Hkv,T,D] at sequence-relative
-    positions. With k_cache / v_cache [B,Hkv,cap,D] (and v [Hkv,T,D]) the rotated
-    keys and the values are also written to the cache. Returns (q', k') (k' is
-    None when write_k is False and a cache is given)."""
+    positions, starting at pos0[b] (default 0; a chunk after a cached prefix
+    starts at the prefix length). With k_cache / v_cache [B,Hkv,cap,D] (and v
+    [Hkv,T,D]) the rotated keys and the values are also written to the cache at
+    those positions. Returns (q', k') (k' is None when write_k is False and a
+    cache is given)."""
     Hq, T, D = q_raw.shape
     Hkv = k_raw.shape[0]
     B = len(cu_seqlens) - 1
@@ -304,8 +306,9 @@ def rope_prefill(q_raw, k_raw, cu_seqlens, rope_theta, v=None, k_cache=None, v_c
                                           else None)
     cap = k_cache.shape[2] if k_cache is not None else 0
     cu = _i32_array(cu_seqlens)
+    p0 = _i32_array(pos0) if pos0 is not None else None
     _check(lib().bifocal_rope_prefill(_ptr(q_raw), _ptr(k_raw), _ptr(v), _ptr(qo), _ptr(ko),
-                                      _ptr(k_cache), _ptr(v_cache), cap, cu, B, Hq, Hkv, D,
+                                      _ptr(k_cache), _ptr(v_cache), cap, cu, p0, B, Hq, Hkv, D,
                                       _DTYPES[q_raw.dtype], float(rope_theta), _stream(stream)))
     return qo, ko
 

@@ -37,7 +37,8 @@ int run_decode(bool bifocal, const void* q, const void* kc, const void* vc, void
                long long w_pre, double theta, int mode, float scale, void* ws, size_t ws_bytes,
                hipStream_t stream, std::string& err, long long window, const PagedCache* paged);
 int run_rope_prefill(const void* q, const void* k, const void* v, void* q_out, void* k_out,
-                     void* k_cache, void* v_cache, int cap, const int32_t* cu, int batch, int Hq,
+                     void* k_cache, void* v_cache, int cap, const int32_t* cu, const int32_t* pos0,
+                     int batch, int Hq,
                      int Hkv, int dtype, double theta, hipStream_t stream, std::string& err);
 int run_rope_append(const void* q, const void* k, const void* v, void* q_out, void* k_cache,
                     void* v_cache, int cap, const int32_t* seqlens, int batch, int Hq, int Hkv,
@@ -543,7 +544,8 @@ int bifocal_test_pair_map(int64_t L, int64_t w0, int64_t w_pre, int32_t long_mod
 
 int bifocal_rope_prefill(const void* q_raw, const void* k_raw, const void* v, void* q_out,
                          void* k_out, void* k_cache, void* v_cache, int32_t cache_capacity,
-                         const int32_t* cu, int32_t batch, int32_t n_heads_q, int32_t n_heads_kv,
+                         const int32_t* cu, const int32_t* pos0, int32_t batch, int32_t n_heads_q,
+                         int32_t n_heads_kv,
                          int32_t head_dim, int32_t dtype, double rope_theta, void* stream) {
   int rc = check_common(n_heads_q, n_heads_kv, head_dim, dtype);
   if (rc) return rc;
@@ -554,20 +556,25 @@ int bifocal_rope_prefill(const void* q_raw, const void* k_raw, const void* v, vo
     return fail(BF_ERR_INVALID_ARG, "rope_theta must be finite and > 1");
   if (batch < 1) return fail(BF_ERR_INVALID_ARG, "batch must be >= 1 (got %d)", batch);
   if (cu[0] != 0) return fail(BF_ERR_INVALID_ARG, "cu_seqlens[0] must be 0 (got %d)", cu[0]);
-  int max_len = 0;
+  long long max_end = 0;  // largest P_b + L_b
   for (int b = 0; b < batch; ++b) {
     if (cu[b + 1] <= cu[b])
       return fail(BF_ERR_INVALID_ARG, "cu_seqlens must be strictly increasing (b=%d: %d -> %d)", b, cu[b], cu[b + 1]);
-    max_len = std::max(max_len, cu[b + 1] - cu[b]);
+    const long long p0 = pos0 ? pos0[b] : 0;
+    if (p0 < 0) return fail(BF_ERR_INVALID_ARG, "pos0[%d] = %lld must be >= 0", b, p0);
+    const long long end = p0 + (cu[b + 1] - cu[b]);
+    if (end > 0x7fffffffLL) return fail(BF_ERR_INVALID_ARG, "positions of sequence %d exceed 2^31 - 1", b);
+    max_end = std::max(max_end, end);
   }
-  if (k_cache && max_len > cache_capacity)
-    return fail(BF_ERR_INVALID_ARG, "a sequence (%d tokens) exceeds cache_capacity %d", max_len, cache_capacity);
+  if (k_cache && max_end > cache_capacity)
+    return fail(BF_ERR_INVALID_ARG, "a sequence reaches position %lld, beyond cache_capacity %d", max_end - 1,
+                cache_capacity);
   if (!aligned16(q_raw) || !aligned16(k_raw) || !aligned16(q_out) || (k_out && !aligned16(k_out)) ||
       (k_cache && (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(v))))
     return fail(BF_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
   if (forced_launch_failure()) return fail(BF_ERR_HIP, "launch failure forced by BIFOCAL_TEST_FAIL_LAUNCH");
   std::string err;
-  rc = bf::run_rope_prefill(q_raw, k_raw, v, q_out, k_out, k_cache, v_cache, cache_capacity, cu, batch,
+  rc = bf::run_rope_prefill(q_raw, k_raw, v, q_out, k_out, k_cache, v_cache, cache_capacity, cu, pos0, batch,
                             n_heads_q, n_heads_kv, dtype, rope_theta, (hipStream_t)stream, err);
   if (rc) return fail(rc, "%s", err.c_str());
   g_err.clear();

@@ -51,12 +51,12 @@ struct RopeParams {
 };
 
 // Token t of a launch: its sequence b and position; prefill tokens are packed
-// (SeqTable cu offsets, positions restart per sequence), decode tokens are one
+// (cu offsets; sequence b's positions run from pos0[b]), decode tokens are one
 // per sequence at position N_b - 1.
 struct RopeSeqs {
   int n;                          // sequences in the launch
   int cu[kMaxSeqPerLaunch + 1];   // prefill: token offsets; decode: unused
-  int pos0[kMaxSeqPerLaunch];     // decode: position of sequence b's token; prefill: 0
+  int pos0[kMaxSeqPerLaunch];     // decode: position of sequence b's token; prefill: its first token's
   int decode;                     // 1: token t is sequence t at pos0[t]
 };
 
@@ -164,7 +164,7 @@ __global__ __launch_bounds__(256) void rope_kernel(RopeParams p, RopeSeqs sq, Th
   } else {
     b = 0;
     while (b + 1 < sq.n && t >= sq.cu[b + 1]) ++b;
-    pos = t - sq.cu[b];
+    pos = sq.pos0[b] + t - sq.cu[b];
   }
   // cos / sin of pairs 8u .. 8u + 7 at this position
   float c[8], s[8];
@@ -262,10 +262,12 @@ static hipError_t launch_rope(int dtype, RopeParams p, const RopeSeqs& sq,
 }
 
 // Prefill layout [H][T][D]: one launch per group of kMaxSeqPerLaunch
-// sequences; the cache (if any) is [batch][Hkv][cap][D] with sequence b's
-// tokens at positions 0 .. L_b - 1.
+// sequences; sequence b's tokens sit at positions P_b .. P_b + L_b - 1
+// (P_b = pos0[b], 0 when pos0 is null), and the cache (if any) is
+// [batch][Hkv][cap][D] with those tokens at those positions.
 int run_rope_prefill(const void* q, const void* k, const void* v, void* q_out, void* k_out,
-                     void* k_cache, void* v_cache, int cap, const int32_t* cu, int batch, int Hq,
+                     void* k_cache, void* v_cache, int cap, const int32_t* cu, const int32_t* pos0,
+                     int batch, int Hq,
                      int Hkv, int dtype, double theta, hipStream_t stream, std::string& err) {
   ThetaTable tt;
   for (int m = 0; m < kPairs; ++m) tt.th[m] = pow(theta, -2.0 * (double)m / (double)kHeadDim);
@@ -277,7 +279,7 @@ int run_rope_prefill(const void* q, const void* k, const void* v, void* q_out, v
     sq.n = nb;
     sq.decode = 0;
     for (int i = 0; i <= nb; ++i) sq.cu[i] = cu[b0 + i] - cu[b0];
-    for (int i = 0; i < nb; ++i) sq.pos0[i] = 0;
+    for (int i = 0; i < nb; ++i) sq.pos0[i] = pos0 ? pos0[b0 + i] : 0;
     const long long t0 = cu[b0];
     RopeParams p;
     p.q = (const char*)q + t0 * kHeadDim * es;

@@ -140,12 +140,13 @@ def test_pair_map_validation(L):
 
 
 def _rope_prefill(L, **kw):
-    a = dict(q=P, k=P, v=None, qo=P, ko=P, kc=None, vc=None, cap=0, cu=[0, 100, 150], Hq=4, Hkv=2,
-             D=128, dtype=0, theta=1e6, stream=None)
+    a = dict(q=P, k=P, v=None, qo=P, ko=P, kc=None, vc=None, cap=0, cu=[0, 100, 150], pos0=None,
+             Hq=4, Hkv=2, D=128, dtype=0, theta=1e6, stream=None)
     a.update(kw)
     cu = (ctypes.c_int32 * len(a["cu"]))(*a["cu"])
+    p0 = (ctypes.c_int32 * len(a["pos0"]))(*a["pos0"]) if a["pos0"] is not None else None
     return L.bifocal_rope_prefill(a["q"], a["k"], a["v"], a["qo"], a["ko"], a["kc"], a["vc"],
-                                  a["cap"], cu, len(a["cu"]) - 1, a["Hq"], a["Hkv"], a["D"],
+                                  a["cap"], cu, p0, len(a["cu"]) - 1, a["Hq"], a["Hkv"], a["D"],
                                   a["dtype"], a["theta"], a["stream"])
 
 
@@ -166,6 +167,9 @@ def _rope_append(L, **kw):
     (dict(theta=0.5), -1), (dict(theta=float("inf")), -1), (dict(cu=[0, 100, 100]), -1),
     (dict(cu=[2, 100]), -1), (dict(D=64), -2), (dict(dtype=3), -1), (dict(Hq=3), -1),
     (dict(k=ctypes.c_void_p(0x100008)), -1),
+    (dict(pos0=[0, -1]), -1),                                               # negative start position
+    (dict(kc=P, vc=P, v=P, cap=150, pos0=[51, 0]), -1),                     # chunk runs past the cache
+    (dict(pos0=[2**31 - 50, 0]), -1),                                       # positions past 2^31 - 1
 ])
 def test_rope_prefill_validation(L, kw, code):
     assert _rope_prefill(L, **kw) == code
@@ -183,6 +187,7 @@ def test_rope_append_validation(L, kw, code):
 def test_rope_valid_arguments_reach_the_launch(L, monkeypatch):
     monkeypatch.setenv("BIFOCAL_TEST_FAIL_LAUNCH", "1")
     assert _rope_prefill(L) == bfl.BF_ERR_HIP
+    assert _rope_prefill(L, kc=P, vc=P, v=P, cap=150, pos0=[50, 100]) == bfl.BF_ERR_HIP
     assert _rope_prefill(L, ko=None, kc=P, vc=P, v=P, cap=100, dtype=1) == bfl.BF_ERR_HIP
     assert _rope_append(L) == bfl.BF_ERR_HIP
 

@@ -204,3 +204,59 @@ def test_raw_input_decode_flow(mode):
     d = np.abs(o.float().cpu().numpy() - o_ref)
     print(f"[raw decode {mode}] max-abs {d.max():.3e} mean-abs {d.mean():.3e}", flush=True)
     assert d.max() <= 2e-2 and d.mean() <= 2e-3
+
+
+def test_rope_prefill_start_positions_and_cache_rows():
+    # pos0 moves each sequence's positions (a chunk after a cached prefix);
+    # the cache rows written are pos0 .. pos0 + L - 1 and nothing else
+    lens, pos0 = [300, 1, 129], [0, 4096, 131000]
+    cu = wl.cu_seqlens(lens)
+    q, k, v = wl.prefill_inputs(4, 2, cu[-1], 128, "bf16", 77)
+    cap = 131129 + 3
+    sentinel = 5.0
+    kc = torch.full((3, 2, cap, 128), sentinel, dtype=torch.bfloat16, device="cuda")
+    vc = torch.full_like(kc, sentinel)
+    qo, ko = bfl.rope_prefill(q.cuda(), k.cuda(), cu, THETA, v=v.cuda(), k_cache=kc, v_cache=vc,
+                              pos0=pos0)
+    torch.cuda.synchronize()
+    pos = np.concatenate([np.arange(L) + p0 for L, p0 in zip(lens, pos0)])
+    _check_rot_bf16(qo.cpu(), oracle.rope_rows(q.float().numpy(), pos, THETA), q.float().numpy(),
+                    "rope q at start positions")
+    _check_rot_bf16(ko.cpu(), oracle.rope_rows(k.float().numpy(), pos, THETA), k.float().numpy(),
+                    "rope k at start positions")
+    for b, (L, p0) in enumerate(zip(lens, pos0)):
+        assert torch.equal(kc[b, :, p0:p0 + L], ko[:, cu[b]:cu[b + 1]]), b
+        assert torch.equal(vc[b, :, p0:p0 + L].cpu(), v[:, cu[b]:cu[b + 1]]), b
+        untouched = torch.ones(cap, dtype=torch.bool)
+        untouched[p0:p0 + L] = False
+        assert bool((kc[b][:, untouched] == sentinel).all()), b
+        assert bool((vc[b][:, untouched] == sentinel).all()), b
+
+
+@pytest.mark.parametrize("mode", ["fi", "pa"])
+def test_raw_input_chunked_prefill_flow(mode):
+    # a 3000-token raw prompt: the first 2000 tokens through the pre-step into
+    # the cache, then the last 1000 as a chunk (pre-step at position 2000,
+    # cache fill, bifocal_prefill_chunk); reference: the oracle's rows
+    # 2000 .. 2999 of a one-shot prefill on its own rotation of the raw inputs
+    N, P, Hq, Hkv, w0, w_pre = 3000, 2000, 8, 2, 128, 512
+    q, k, v = wl.prefill_inputs(Hq, Hkv, N, 128, "bf16", 78)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    kc = torch.zeros((1, Hkv, N, 128), dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    bfl.rope_prefill(qd[:, :P].contiguous(), kd[:, :P].contiguous(), [0, P], THETA,
+                     v=vd[:, :P].contiguous(), k_cache=kc, v_cache=vc, write_k=False)
+    q_chunk, _ = bfl.rope_prefill(qd[:, P:].contiguous(), kd[:, P:].contiguous(), [0, N - P], THETA,
+                                  v=vd[:, P:].contiguous(), k_cache=kc, v_cache=vc, write_k=False,
+                                  pos0=[P])
+    scale = 1 / math.sqrt(128)
+    o = bfl.prefill_chunk(q_chunk, kc, vc, [0, N - P], [N], w0, w_pre, THETA, mode, scale)
+    torch.cuda.synchronize()
+    pos = np.arange(N)
+    rq = _bf16_round(oracle.rope_rows(q.float().numpy(), pos, THETA)).float().numpy()
+    rk = _bf16_round(oracle.rope_rows(k.float().numpy(), pos, THETA)).float().numpy()
+    o_ref, _ = oracle.prefill(rq, rk, v.float().numpy(), [0, N], w0, w_pre, THETA, mode, scale,
+                              rows=np.arange(P, N))
+    d = np.abs(o.float().cpu().numpy() - o_ref)
+    print(f"[raw chunked prefill {mode}] max-abs {d.max():.3e} mean-abs {d.mean():.3e}", flush=True)
+    assert d.max() <= 2e-2 and d.mean() <= 2e-3
