@@ -299,6 +299,31 @@ int bifocal_rope_append(const void* q_raw, const void* k_raw, const void* v_new,
                         int32_t head_dim, int32_t dtype, double rope_theta, void* stream);
 
 /*
+ * The two pre-steps above with the cache PAGED, as bifocal_decode_paged and
+ * bifocal_prefill_chunk_paged read it:
+ *   k_pages, v_pages : [num_pages, n_heads_kv, page_size, head_dim] dtype;
+ *                      position p of sequence b goes to page
+ *                      block_table[b][p / page_size], row p % page_size
+ *   block_table      : DEVICE int32 [batch, max_pages_per_seq] (entries
+ *                      clamped to [0, num_pages - 1])
+ *   page_size        : a power of two, 1 <= page_size <= 2^20
+ * Positions must stay below max_pages_per_seq * page_size. Everything else
+ * (layouts, start positions, in-place use, rounding) as the contiguous calls.
+ */
+int bifocal_rope_prefill_paged(const void* q_raw, const void* k_raw, const void* v, void* q_out,
+                               void* k_out, void* k_pages, void* v_pages, const int32_t* block_table,
+                               int32_t page_size, int32_t max_pages_per_seq, int32_t num_pages,
+                               const int32_t* cu_seqlens_host, const int32_t* pos0_host,
+                               int32_t batch, int32_t n_heads_q, int32_t n_heads_kv,
+                               int32_t head_dim, int32_t dtype, double rope_theta, void* stream);
+int bifocal_rope_append_paged(const void* q_raw, const void* k_raw, const void* v_new, void* q_out,
+                              void* k_pages, void* v_pages, const int32_t* block_table,
+                              int32_t page_size, int32_t max_pages_per_seq, int32_t num_pages,
+                              const int32_t* seqlens_host, int32_t batch, int32_t n_heads_q,
+                              int32_t n_heads_kv, int32_t head_dim, int32_t dtype,
+                              double rope_theta, void* stream);
+
+/*
  * Test hook: runs the kernels' own device-side pair classification and
  * position map for one sequence of length L (L <= 4096).
  *   branch_out : device int8 [L * L], row-major (i, j): 0 masked (j > i),

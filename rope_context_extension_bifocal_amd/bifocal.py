@@ -27,6 +27,7 @@ _DTYPES = {torch.bfloat16: BF_DTYPE_BF16, torch.float32: BF_DTYPE_FP32}
 EXPORTED = ("bifocal_s_of_L", "bifocal_workspace_bytes", "bifocal_prefill", "bifocal_decode",
             "bifocal_chunk_workspace_bytes", "bifocal_prefill_chunk", "bifocal_prefill_chunk_paged",
             "bifocal_decode_paged", "plain_attention_ref_gpu", "bifocal_rope_prefill", "bifocal_rope_append",
+            "bifocal_rope_prefill_paged", "bifocal_rope_append_paged",
             "bifocal_test_pair_map", "bifocal_last_error")
 
 _lib = None
@@ -75,6 +76,12 @@ def lib():
         L.bifocal_rope_prefill.restype = ctypes.c_int
         L.bifocal_rope_prefill.argtypes = [p, p, p, p, p, p, p, i32, p, p, i32, i32, i32, i32,
                                            i32, f64, p]
+        L.bifocal_rope_prefill_paged.restype = ctypes.c_int
+        L.bifocal_rope_prefill_paged.argtypes = [p, p, p, p, p, p, p, p, i32, i32, i32, p, p, i32,
+                                                 i32, i32, i32, i32, f64, p]
+        L.bifocal_rope_append_paged.restype = ctypes.c_int
+        L.bifocal_rope_append_paged.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, p, i32, i32, i32,
+                                                i32, i32, f64, p]
         L.bifocal_rope_append.restype = ctypes.c_int
         L.bifocal_rope_append.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, f64,
                                           p]
@@ -324,6 +331,40 @@ def rope_append(q_raw, k_raw, v_new, k_cache, v_cache, seqlens, rope_theta, q_ou
     _check(lib().bifocal_rope_append(_ptr(q_raw), _ptr(k_raw), _ptr(v_new), _ptr(qo),
                                      _ptr(k_cache), _ptr(v_cache), sl, B, cap, Hq, Hkv, D,
                                      _DTYPES[q_raw.dtype], float(rope_theta), _stream(stream)))
+    return qo
+
+
+def rope_prefill_paged(q_raw, k_raw, v, cu_seqlens, rope_theta, k_pages, v_pages, block_table,
+                       q_out=None, k_out=None, write_k=False, pos0=None, stream=None):
+    """rope_prefill with the cache fill going to a paged cache (pages
+    [num_pages,Hkv,page,D], device int32 block table [B,max_pages])."""
+    Hq, T, D = q_raw.shape
+    Hkv = k_raw.shape[0]
+    B = len(cu_seqlens) - 1
+    qo = q_out if q_out is not None else torch.empty_like(q_raw)
+    ko = k_out if k_out is not None else (torch.empty_like(k_raw) if write_k else None)
+    cu = _i32_array(cu_seqlens)
+    p0 = _i32_array(pos0) if pos0 is not None else None
+    _check(lib().bifocal_rope_prefill_paged(_ptr(q_raw), _ptr(k_raw), _ptr(v), _ptr(qo), _ptr(ko),
+                                            _ptr(k_pages), _ptr(v_pages), _ptr(block_table),
+                                            k_pages.shape[2], block_table.shape[1], k_pages.shape[0],
+                                            cu, p0, B, Hq, Hkv, D, _DTYPES[q_raw.dtype],
+                                            float(rope_theta), _stream(stream)))
+    return qo, ko
+
+
+def rope_append_paged(q_raw, k_raw, v_new, k_pages, v_pages, block_table, seqlens, rope_theta,
+                      q_out=None, stream=None):
+    """rope_append into a paged cache."""
+    B, Hq, D = q_raw.shape
+    Hkv = k_raw.shape[1]
+    qo = q_out if q_out is not None else torch.empty_like(q_raw)
+    sl = _i32_array(seqlens)
+    _check(lib().bifocal_rope_append_paged(_ptr(q_raw), _ptr(k_raw), _ptr(v_new), _ptr(qo),
+                                           _ptr(k_pages), _ptr(v_pages), _ptr(block_table),
+                                           k_pages.shape[2], block_table.shape[1], k_pages.shape[0],
+                                           sl, B, Hq, Hkv, D, _DTYPES[q_raw.dtype],
+                                           float(rope_theta), _stream(stream)))
     return qo
 
 

@@ -38,11 +38,11 @@ int run_decode(bool bifocal, const void* q, const void* kc, const void* vc, void
                hipStream_t stream, std::string& err, long long window, const PagedCache* paged);
 int run_rope_prefill(const void* q, const void* k, const void* v, void* q_out, void* k_out,
                      void* k_cache, void* v_cache, int cap, const int32_t* cu, const int32_t* pos0,
-                     int batch, int Hq,
-                     int Hkv, int dtype, double theta, hipStream_t stream, std::string& err);
+                     const PagedKV& pk, int batch, int Hq, int Hkv, int dtype, double theta,
+                     hipStream_t stream, std::string& err);
 int run_rope_append(const void* q, const void* k, const void* v, void* q_out, void* k_cache,
-                    void* v_cache, int cap, const int32_t* seqlens, int batch, int Hq, int Hkv,
-                    int dtype, double theta, hipStream_t stream, std::string& err);
+                    void* v_cache, int cap, const int32_t* seqlens, const PagedKV& pk, int batch,
+                    int Hq, int Hkv, int dtype, double theta, hipStream_t stream, std::string& err);
 }  // namespace bf
 
 namespace {
@@ -289,6 +289,29 @@ int run_rows(RowsJob& j) {
   return BF_OK;
 }
 
+// A paged cache as the C-ABI passes it: pages [num_pages][Hkv][page_size][D].
+struct ChunkPages {
+  const int32_t* block_table;  // device [batch][max_pages]
+  int page_size, max_pages, num_pages;
+};
+
+// Validates a paged cache; sets the kernels' description and the most keys a
+// sequence's pages hold.
+int check_pages(const ChunkPages& pg, bf::PagedKV& pk, long long& hold) {
+  const int ps = pg.page_size;
+  if (ps < 1 || ps > (1 << 20) || (ps & (ps - 1)))
+    return fail(BF_ERR_INVALID_ARG, "page_size must be a power of two in [1, 2^20] (got %d)", ps);
+  if (pg.max_pages < 1 || pg.num_pages < 1)
+    return fail(BF_ERR_INVALID_ARG, "max_pages_per_seq and num_pages must be >= 1");
+  if (!pg.block_table || ((uintptr_t)pg.block_table & 3u))
+    return fail(BF_ERR_INVALID_ARG, "block_table must be a non-null 4-byte aligned device pointer");
+  int lg = 0;
+  while ((1 << lg) < ps) ++lg;
+  pk = bf::PagedKV{pg.block_table, lg, pg.max_pages, pg.num_pages};
+  hold = (long long)pg.max_pages * ps;
+  return BF_OK;
+}
+
 // Shared prefill path of bifocal_prefill and the plain reference.
 int run_prefill(bool bifocal, const void* q, const void* k, const void* v, void* o, float* lse,
                 const int32_t* cu, int batch, int Hq, int Hkv, int head_dim, int dtype,
@@ -325,11 +348,6 @@ int run_prefill(bool bifocal, const void* q, const void* k, const void* v, void*
   return run_rows(j);
 }
 
-// A paged cache of a chunk call: pages [num_pages][Hkv][page_size][D].
-struct ChunkPages {
-  const int32_t* block_table;  // device [batch][max_pages]
-  int page_size, max_pages, num_pages;
-};
 
 // Chunk of queries against a KV cache [B][Hkv][cap][D] (bifocal_prefill_chunk)
 // or a paged cache (bifocal_prefill_chunk_paged: pages != null, cap = the
@@ -343,17 +361,10 @@ int run_chunk(const void* q, const void* kc, const void* vc, void* o, float* lse
     return fail(BF_ERR_INVALID_ARG, "null tensor, cu_q or seqlens pointer");
   int rc = check_rows_common(true, batch, Hq, Hkv, head_dim, dtype, w0, w_pre, theta, mode, scale);
   if (rc) return rc;
-  int page_log2 = 0;
+  bf::PagedKV pk{nullptr, 0, 0, 0};
   if (pages) {
-    const int ps = pages->page_size;
-    if (ps < 1 || ps > (1 << 20) || (ps & (ps - 1)))
-      return fail(BF_ERR_INVALID_ARG, "page_size must be a power of two in [1, 2^20] (got %d)", ps);
-    if (pages->max_pages < 1 || pages->num_pages < 1)
-      return fail(BF_ERR_INVALID_ARG, "max_pages_per_seq and num_pages must be >= 1");
-    if (!pages->block_table || ((uintptr_t)pages->block_table & 3u))
-      return fail(BF_ERR_INVALID_ARG, "block_table must be a non-null 4-byte aligned device pointer");
-    while ((1 << page_log2) < ps) ++page_log2;
-    const long long hold = (long long)pages->max_pages * ps;
+    long long hold = 0;
+    if ((rc = check_pages(*pages, pk, hold))) return rc;
     cap = (int)std::min<long long>(hold, 0x7fffffffLL);
   }
   if (cap < 1) return fail(BF_ERR_INVALID_ARG, "cache_capacity must be >= 1 (got %d)", cap);
@@ -388,11 +399,89 @@ int run_chunk(const void* q, const void* kc, const void* vc, void* o, float* lse
   }
   j.k_hstride = cap;
   j.k_rows = (long long)batch * Hkv * cap;
-  if (pages) j.pk = bf::PagedKV{pages->block_table, page_log2, pages->max_pages, pages->num_pages};
+  j.pk = pk;
   j.batch = batch; j.Hq = Hq; j.Hkv = Hkv; j.dtype = dtype;
   j.w0 = w0; j.w_pre = w_pre; j.theta = theta; j.mode = mode; j.scale = scale;
   j.ws = ws; j.ws_bytes = ws_bytes; j.stream = stream;
   return run_rows(j);
+}
+
+int rope_prefill_impl(const void* q_raw, const void* k_raw, const void* v, void* q_out,
+                      void* k_out, void* k_cache, void* v_cache, int cache_capacity,
+                      const int32_t* cu, const int32_t* pos0, int batch, int n_heads_q,
+                      int n_heads_kv, int head_dim, int dtype, double rope_theta, void* stream,
+                      const ChunkPages* pages) {
+  int rc = check_common(n_heads_q, n_heads_kv, head_dim, dtype);
+  if (rc) return rc;
+  bf::PagedKV pk{nullptr, 0, 0, 0};
+  if (pages && k_cache) {
+    long long hold = 0;
+    if ((rc = check_pages(*pages, pk, hold))) return rc;
+    cache_capacity = (int)std::min<long long>(hold, 0x7fffffffLL);
+  }
+  if (!q_raw || !k_raw || !q_out || !cu) return fail(BF_ERR_INVALID_ARG, "null tensor or cu_seqlens pointer");
+  if (!k_out && !k_cache) return fail(BF_ERR_INVALID_ARG, "k_out and k_cache are both NULL");
+  if (k_cache && (!v_cache || !v)) return fail(BF_ERR_INVALID_ARG, "k_cache given without v_cache and v");
+  if (!(rope_theta > 1.0) || !std::isfinite(rope_theta))
+    return fail(BF_ERR_INVALID_ARG, "rope_theta must be finite and > 1");
+  if (batch < 1) return fail(BF_ERR_INVALID_ARG, "batch must be >= 1 (got %d)", batch);
+  if (cu[0] != 0) return fail(BF_ERR_INVALID_ARG, "cu_seqlens[0] must be 0 (got %d)", cu[0]);
+  long long max_end = 0;  // largest P_b + L_b
+  for (int b = 0; b < batch; ++b) {
+    if (cu[b + 1] <= cu[b])
+      return fail(BF_ERR_INVALID_ARG, "cu_seqlens must be strictly increasing (b=%d: %d -> %d)", b, cu[b], cu[b + 1]);
+    const long long p0 = pos0 ? pos0[b] : 0;
+    if (p0 < 0) return fail(BF_ERR_INVALID_ARG, "pos0[%d] = %lld must be >= 0", b, p0);
+    const long long end = p0 + (cu[b + 1] - cu[b]);
+    if (end > 0x7fffffffLL) return fail(BF_ERR_INVALID_ARG, "positions of sequence %d exceed 2^31 - 1", b);
+    max_end = std::max(max_end, end);
+  }
+  if (k_cache && max_end > cache_capacity)
+    return fail(BF_ERR_INVALID_ARG, "a sequence reaches position %lld, beyond %s %d", max_end - 1,
+                pages ? "max_pages_per_seq * page_size" : "cache_capacity", cache_capacity);
+  if (!aligned16(q_raw) || !aligned16(k_raw) || !aligned16(q_out) || (k_out && !aligned16(k_out)) ||
+      (k_cache && (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(v))))
+    return fail(BF_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+  if (forced_launch_failure()) return fail(BF_ERR_HIP, "launch failure forced by BIFOCAL_TEST_FAIL_LAUNCH");
+  std::string err;
+  rc = bf::run_rope_prefill(q_raw, k_raw, v, q_out, k_out, k_cache, v_cache, cache_capacity, cu, pos0, pk,
+                            batch, n_heads_q, n_heads_kv, dtype, rope_theta, (hipStream_t)stream, err);
+  if (rc) return fail(rc, "%s", err.c_str());
+  g_err.clear();
+  return BF_OK;
+}
+
+int rope_append_impl(const void* q_raw, const void* k_raw, const void* v_new, void* q_out,
+                     void* k_cache, void* v_cache, const int32_t* seqlens, int batch,
+                     int cache_capacity, int n_heads_q, int n_heads_kv, int head_dim, int dtype,
+                     double rope_theta, void* stream, const ChunkPages* pages) {
+  int rc = check_common(n_heads_q, n_heads_kv, head_dim, dtype);
+  if (rc) return rc;
+  bf::PagedKV pk{nullptr, 0, 0, 0};
+  if (pages) {
+    long long hold = 0;
+    if ((rc = check_pages(*pages, pk, hold))) return rc;
+    cache_capacity = (int)std::min<long long>(hold, 0x7fffffffLL);
+  }
+  if (!q_raw || !k_raw || !v_new || !q_out || !k_cache || !v_cache || !seqlens)
+    return fail(BF_ERR_INVALID_ARG, "null tensor or seqlens pointer");
+  if (!(rope_theta > 1.0) || !std::isfinite(rope_theta))
+    return fail(BF_ERR_INVALID_ARG, "rope_theta must be finite and > 1");
+  if (batch < 1 || cache_capacity < 1) return fail(BF_ERR_INVALID_ARG, "batch and cache_capacity must be >= 1");
+  for (int b = 0; b < batch; ++b)
+    if (seqlens[b] < 1 || seqlens[b] > cache_capacity)
+      return fail(BF_ERR_INVALID_ARG, "seqlens[%d] = %d out of [1, %s]", b, seqlens[b],
+                  pages ? "max_pages_per_seq * page_size" : "cache_capacity");
+  if (!aligned16(q_raw) || !aligned16(k_raw) || !aligned16(v_new) || !aligned16(q_out) ||
+      !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(BF_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+  if (forced_launch_failure()) return fail(BF_ERR_HIP, "launch failure forced by BIFOCAL_TEST_FAIL_LAUNCH");
+  std::string err;
+  rc = bf::run_rope_append(q_raw, k_raw, v_new, q_out, k_cache, v_cache, cache_capacity, seqlens, pk,
+                           batch, n_heads_q, n_heads_kv, dtype, rope_theta, (hipStream_t)stream, err);
+  if (rc) return fail(rc, "%s", err.c_str());
+  g_err.clear();
+  return BF_OK;
 }
 
 }  // namespace
@@ -545,66 +634,41 @@ int bifocal_test_pair_map(int64_t L, int64_t w0, int64_t w_pre, int32_t long_mod
 int bifocal_rope_prefill(const void* q_raw, const void* k_raw, const void* v, void* q_out,
                          void* k_out, void* k_cache, void* v_cache, int32_t cache_capacity,
                          const int32_t* cu, const int32_t* pos0, int32_t batch, int32_t n_heads_q,
-                         int32_t n_heads_kv,
-                         int32_t head_dim, int32_t dtype, double rope_theta, void* stream) {
-  int rc = check_common(n_heads_q, n_heads_kv, head_dim, dtype);
-  if (rc) return rc;
-  if (!q_raw || !k_raw || !q_out || !cu) return fail(BF_ERR_INVALID_ARG, "null tensor or cu_seqlens pointer");
-  if (!k_out && !k_cache) return fail(BF_ERR_INVALID_ARG, "k_out and k_cache are both NULL");
-  if (k_cache && (!v_cache || !v)) return fail(BF_ERR_INVALID_ARG, "k_cache given without v_cache and v");
-  if (!(rope_theta > 1.0) || !std::isfinite(rope_theta))
-    return fail(BF_ERR_INVALID_ARG, "rope_theta must be finite and > 1");
-  if (batch < 1) return fail(BF_ERR_INVALID_ARG, "batch must be >= 1 (got %d)", batch);
-  if (cu[0] != 0) return fail(BF_ERR_INVALID_ARG, "cu_seqlens[0] must be 0 (got %d)", cu[0]);
-  long long max_end = 0;  // largest P_b + L_b
-  for (int b = 0; b < batch; ++b) {
-    if (cu[b + 1] <= cu[b])
-      return fail(BF_ERR_INVALID_ARG, "cu_seqlens must be strictly increasing (b=%d: %d -> %d)", b, cu[b], cu[b + 1]);
-    const long long p0 = pos0 ? pos0[b] : 0;
-    if (p0 < 0) return fail(BF_ERR_INVALID_ARG, "pos0[%d] = %lld must be >= 0", b, p0);
-    const long long end = p0 + (cu[b + 1] - cu[b]);
-    if (end > 0x7fffffffLL) return fail(BF_ERR_INVALID_ARG, "positions of sequence %d exceed 2^31 - 1", b);
-    max_end = std::max(max_end, end);
-  }
-  if (k_cache && max_end > cache_capacity)
-    return fail(BF_ERR_INVALID_ARG, "a sequence reaches position %lld, beyond cache_capacity %d", max_end - 1,
-                cache_capacity);
-  if (!aligned16(q_raw) || !aligned16(k_raw) || !aligned16(q_out) || (k_out && !aligned16(k_out)) ||
-      (k_cache && (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(v))))
-    return fail(BF_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
-  if (forced_launch_failure()) return fail(BF_ERR_HIP, "launch failure forced by BIFOCAL_TEST_FAIL_LAUNCH");
-  std::string err;
-  rc = bf::run_rope_prefill(q_raw, k_raw, v, q_out, k_out, k_cache, v_cache, cache_capacity, cu, pos0, batch,
-                            n_heads_q, n_heads_kv, dtype, rope_theta, (hipStream_t)stream, err);
-  if (rc) return fail(rc, "%s", err.c_str());
-  g_err.clear();
-  return BF_OK;
+                         int32_t n_heads_kv, int32_t head_dim, int32_t dtype, double rope_theta,
+                         void* stream) {
+  return rope_prefill_impl(q_raw, k_raw, v, q_out, k_out, k_cache, v_cache, cache_capacity, cu, pos0,
+                           batch, n_heads_q, n_heads_kv, head_dim, dtype, rope_theta, stream, nullptr);
+}
+
+int bifocal_rope_prefill_paged(const void* q_raw, const void* k_raw, const void* v, void* q_out,
+                               void* k_out, void* k_pages, void* v_pages, const int32_t* block_table,
+                               int32_t page_size, int32_t max_pages_per_seq, int32_t num_pages,
+                               const int32_t* cu, const int32_t* pos0, int32_t batch,
+                               int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim,
+                               int32_t dtype, double rope_theta, void* stream) {
+  if (!k_pages) return fail(BF_ERR_INVALID_ARG, "k_pages is NULL");
+  const ChunkPages pg{block_table, page_size, max_pages_per_seq, num_pages};
+  return rope_prefill_impl(q_raw, k_raw, v, q_out, k_out, k_pages, v_pages, 0, cu, pos0, batch,
+                           n_heads_q, n_heads_kv, head_dim, dtype, rope_theta, stream, &pg);
 }
 
 int bifocal_rope_append(const void* q_raw, const void* k_raw, const void* v_new, void* q_out,
                         void* k_cache, void* v_cache, const int32_t* seqlens, int32_t batch,
                         int32_t cache_capacity, int32_t n_heads_q, int32_t n_heads_kv,
                         int32_t head_dim, int32_t dtype, double rope_theta, void* stream) {
-  int rc = check_common(n_heads_q, n_heads_kv, head_dim, dtype);
-  if (rc) return rc;
-  if (!q_raw || !k_raw || !v_new || !q_out || !k_cache || !v_cache || !seqlens)
-    return fail(BF_ERR_INVALID_ARG, "null tensor or seqlens pointer");
-  if (!(rope_theta > 1.0) || !std::isfinite(rope_theta))
-    return fail(BF_ERR_INVALID_ARG, "rope_theta must be finite and > 1");
-  if (batch < 1 || cache_capacity < 1) return fail(BF_ERR_INVALID_ARG, "batch and cache_capacity must be >= 1");
-  for (int b = 0; b < batch; ++b)
-    if (seqlens[b] < 1 || seqlens[b] > cache_capacity)
-      return fail(BF_ERR_INVALID_ARG, "seqlens[%d] = %d out of [1, cache_capacity]", b, seqlens[b]);
-  if (!aligned16(q_raw) || !aligned16(k_raw) || !aligned16(v_new) || !aligned16(q_out) ||
-      !aligned16(k_cache) || !aligned16(v_cache))
-    return fail(BF_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
-  if (forced_launch_failure()) return fail(BF_ERR_HIP, "launch failure forced by BIFOCAL_TEST_FAIL_LAUNCH");
-  std::string err;
-  rc = bf::run_rope_append(q_raw, k_raw, v_new, q_out, k_cache, v_cache, cache_capacity, seqlens, batch,
-                           n_heads_q, n_heads_kv, dtype, rope_theta, (hipStream_t)stream, err);
-  if (rc) return fail(rc, "%s", err.c_str());
-  g_err.clear();
-  return BF_OK;
+  return rope_append_impl(q_raw, k_raw, v_new, q_out, k_cache, v_cache, seqlens, batch, cache_capacity,
+                          n_heads_q, n_heads_kv, head_dim, dtype, rope_theta, stream, nullptr);
+}
+
+int bifocal_rope_append_paged(const void* q_raw, const void* k_raw, const void* v_new, void* q_out,
+                              void* k_pages, void* v_pages, const int32_t* block_table,
+                              int32_t page_size, int32_t max_pages_per_seq, int32_t num_pages,
+                              const int32_t* seqlens, int32_t batch, int32_t n_heads_q,
+                              int32_t n_heads_kv, int32_t head_dim, int32_t dtype,
+                              double rope_theta, void* stream) {
+  const ChunkPages pg{block_table, page_size, max_pages_per_seq, num_pages};
+  return rope_append_impl(q_raw, k_raw, v_new, q_out, k_pages, v_pages, seqlens, batch, 1, n_heads_q,
+                          n_heads_kv, head_dim, dtype, rope_theta, stream, &pg);
 }
 
 const char* bifocal_last_error(void) { return g_err.c_str(); }

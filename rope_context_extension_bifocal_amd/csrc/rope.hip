@@ -39,8 +39,9 @@ struct RopeParams {
   const void* v;     // values copied to the cache (may be null when no cache)
   void* q_out;       // rotated queries, same layout as q
   void* k_out;       // rotated keys, same layout as k (may be null: cache only)
-  void* k_cache;     // [B][Hkv][cap][D] or null
-  void* v_cache;     // [B][Hkv][cap][D] or null
+  void* k_cache;     // [B][Hkv][cap][D], pages [num_pages][Hkv][page][D], or null
+  void* v_cache;     // same layout as k_cache
+  PagedKV pk;        // block_table non-null: the caches are paged (rows of this launch)
   long long q_hs, q_ts;  // element strides of q / q_out: per head, per token
   long long k_hs, k_ts;  // element strides of k / k_out / v: per head, per token
   long long cap;         // cache capacity (tokens)
@@ -225,7 +226,16 @@ __global__ __launch_bounds__(256) void rope_kernel(RopeParams p, RopeSeqs sq, Th
         st_oct<NT>((V*)(dst + e_hi), hi_o);
       }
       if (cache) {
-        const long long cr = (((long long)b * p.Hkv + (j - p.Hq)) * p.cap + pos) * kHeadDim;
+        const int h = j - p.Hq;
+        long long crow;  // cache row of (sequence b, KV head h, position pos)
+        if (p.pk.block_table != nullptr) {
+          int pg = p.pk.block_table[(size_t)b * p.pk.max_pages + (pos >> p.pk.page_log2)];
+          pg = min(max(pg, 0), p.pk.num_pages - 1);
+          crow = (((long long)pg * p.Hkv + h) << p.pk.page_log2) + (pos & ((1 << p.pk.page_log2) - 1));
+        } else {
+          crow = ((long long)b * p.Hkv + h) * p.cap + pos;
+        }
+        const long long cr = crow * kHeadDim;
         T* kc = (T*)p.k_cache + cr;
         T* vc = (T*)p.v_cache + cr;
         st_oct<NT>((V*)(kc + e_lo), lo_o);
@@ -267,7 +277,7 @@ static hipError_t launch_rope(int dtype, RopeParams p, const RopeSeqs& sq,
 // [batch][Hkv][cap][D] with those tokens at those positions.
 int run_rope_prefill(const void* q, const void* k, const void* v, void* q_out, void* k_out,
                      void* k_cache, void* v_cache, int cap, const int32_t* cu, const int32_t* pos0,
-                     int batch, int Hq,
+                     const PagedKV& pk, int batch, int Hq,
                      int Hkv, int dtype, double theta, hipStream_t stream, std::string& err) {
   ThetaTable tt;
   for (int m = 0; m < kPairs; ++m) tt.th[m] = pow(theta, -2.0 * (double)m / (double)kHeadDim);
@@ -287,8 +297,11 @@ int run_rope_prefill(const void* q, const void* k, const void* v, void* q_out, v
     p.v = v ? (const char*)v + t0 * kHeadDim * es : nullptr;
     p.q_out = (char*)q_out + t0 * kHeadDim * es;
     p.k_out = k_out ? (char*)k_out + t0 * kHeadDim * es : nullptr;
-    p.k_cache = k_cache ? (char*)k_cache + (size_t)b0 * Hkv * cap * kHeadDim * es : nullptr;
-    p.v_cache = v_cache ? (char*)v_cache + (size_t)b0 * Hkv * cap * kHeadDim * es : nullptr;
+    const bool paged = pk.block_table != nullptr;
+    p.k_cache = !k_cache ? nullptr : paged ? k_cache : (char*)k_cache + (size_t)b0 * Hkv * cap * kHeadDim * es;
+    p.v_cache = !v_cache ? nullptr : paged ? v_cache : (char*)v_cache + (size_t)b0 * Hkv * cap * kHeadDim * es;
+    p.pk = pk;
+    if (paged) p.pk.block_table += (size_t)b0 * pk.max_pages;
     p.q_hs = T * kHeadDim;
     p.q_ts = kHeadDim;
     p.k_hs = T * kHeadDim;
@@ -309,7 +322,8 @@ int run_rope_prefill(const void* q, const void* k, const void* v, void* q_out, v
 // Decode layout: q [batch][Hq][D], k / v [batch][Hkv][D], one token per
 // sequence at position seqlens[b] - 1, appended to [batch][Hkv][cap][D].
 int run_rope_append(const void* q, const void* k, const void* v, void* q_out, void* k_cache,
-                    void* v_cache, int cap, const int32_t* seqlens, int batch, int Hq, int Hkv,
+                    void* v_cache, int cap, const int32_t* seqlens, const PagedKV& pk, int batch,
+                    int Hq, int Hkv,
                     int dtype, double theta, hipStream_t stream, std::string& err) {
   ThetaTable tt;
   for (int m = 0; m < kPairs; ++m) tt.th[m] = pow(theta, -2.0 * (double)m / (double)kHeadDim);
@@ -327,8 +341,11 @@ int run_rope_append(const void* q, const void* k, const void* v, void* q_out, vo
     p.v = (const char*)v + (size_t)b0 * Hkv * kHeadDim * es;
     p.q_out = (char*)q_out + (size_t)b0 * Hq * kHeadDim * es;
     p.k_out = nullptr;
-    p.k_cache = (char*)k_cache + (size_t)b0 * Hkv * cap * kHeadDim * es;
-    p.v_cache = (char*)v_cache + (size_t)b0 * Hkv * cap * kHeadDim * es;
+    const bool paged = pk.block_table != nullptr;
+    p.k_cache = paged ? k_cache : (char*)k_cache + (size_t)b0 * Hkv * cap * kHeadDim * es;
+    p.v_cache = paged ? v_cache : (char*)v_cache + (size_t)b0 * Hkv * cap * kHeadDim * es;
+    p.pk = pk;
+    if (paged) p.pk.block_table += (size_t)b0 * pk.max_pages;
     p.q_hs = kHeadDim;
     p.q_ts = (long long)Hq * kHeadDim;
     p.k_hs = kHeadDim;

@@ -298,3 +298,25 @@ def test_chunk_paged_valid_arguments_reach_the_launch(L, monkeypatch):
     assert _chunk_paged(L) == bfl.BF_ERR_HIP
     assert _chunk_paged(L, page=1, maxp=128, dtype=1, mode=2, w0=4) == bfl.BF_ERR_HIP
     assert _chunk_paged(L, sl=[128, 128], cu=[0, 128, 256]) == bfl.BF_ERR_HIP  # 8 pages of 16 hold 128
+
+
+def test_rope_paged_validation(L, monkeypatch):
+    cu = (ctypes.c_int32 * 3)(0, 100, 150)
+    p0 = (ctypes.c_int32 * 2)(0, 90)
+    sl = (ctypes.c_int32 * 2)(100, 7)
+
+    def pre(bt=P, page=16, maxp=8, npages=20, kp=P, pos=None):
+        return L.bifocal_rope_prefill_paged(P, P, P, P, None, kp, P, bt, page, maxp, npages, cu, pos, 2,
+                                            4, 2, 128, 0, 1e6, None)
+
+    def app(bt=P, page=16, maxp=8, npages=20, s=sl):
+        return L.bifocal_rope_append_paged(P, P, P, P, P, P, bt, page, maxp, npages, s, 2, 4, 2, 128,
+                                           0, 1e6, None)
+    for kw in [dict(bt=None), dict(page=12), dict(maxp=0), dict(npages=0), dict(kp=None),
+               dict(pos=p0)]:  # pos0 90 + 50 tokens > 8 pages of 16
+        assert pre(**kw) == bfl.BF_ERR_INVALID_ARG, kw
+    for kw in [dict(bt=ctypes.c_void_p(0x100001)), dict(page=0), dict(maxp=6)]:  # 100 keys > 6 x 16
+        assert app(**kw) == bfl.BF_ERR_INVALID_ARG, kw
+    monkeypatch.setenv("BIFOCAL_TEST_FAIL_LAUNCH", "1")
+    assert pre() == bfl.BF_ERR_HIP and pre(page=1, maxp=200) == bfl.BF_ERR_HIP
+    assert app() == bfl.BF_ERR_HIP
