@@ -412,6 +412,15 @@ def main():
             chunk["4096_paged16"] = {"ms": round(p_ms, 3),
                                      "tflops": round(c_flops / (p_ms * 1e-3) / 1e12, 2)}
             del kpg, vpg, tbl, wsp
+            # band-only (a sliding-window layer): the same chunk sees only its
+            # window; its work is the pairs with i - j < w0
+            bfn = lambda: bfl.prefill_chunk(qch, kcc, vcc, [0, lq], [L], cfg["w0"], cfg["w_pre"],
+                                            cfg["theta"], "band", scale, out=och, workspace=wsc)
+            bfn()
+            b_ms = time_calls(bfn, 5, stream)
+            b_flops = 4.0 * D * Hq * lq * cfg["w0"]  # every chunk row is past the first w0 keys
+            chunk["4096_band"] = {"ms": round(b_ms, 3),
+                                  "tflops": round(b_flops / (b_ms * 1e-3) / 1e12, 2)}
         del qch, och, wsc
 
     log("raw-input pre-step")

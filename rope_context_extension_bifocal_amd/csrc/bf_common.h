@@ -27,6 +27,8 @@ struct SeqTable {
   int cu[kMaxSeqPerLaunch + 1];       // query token offsets into the packed T axis
   int kcu[kMaxSeqPerLaunch + 1];      // key offsets into the packed k'' axis (Tk); keys of b: kcu[b+1]-kcu[b]
   int vt_off[kMaxSeqPerLaunch + 1];   // 64-aligned offsets into the padded V^T axis
+  int vt_t0[kMaxSeqPerLaunch];        // first key tile with a V^T copy: 0, or for band-only chunks
+                                      // the first tile any query's window reaches
   int qpos[kMaxSeqPerLaunch];         // position of the sequence's first query row
   int rboff[kMaxSeqPerLaunch];        // qpos / P_wg: heaviest-first rank offset of its row blocks
   long long kbase[kMaxSeqPerLaunch];  // K / V row offset of the sequence's key 0

@@ -185,11 +185,16 @@ int run_rows(RowsJob& j) {
   const int batch = j.batch, Hq = j.Hq, Hkv = j.Hkv, dtype = j.dtype;
   const bool bifocal = j.bifocal;
   long long Tq = j.cu[batch], Tk = 0;
-  std::vector<int> kcu(batch + 1, 0), vt_off(batch + 1, 0);
+  const bool band_mode = bifocal && (j.mode & ~BF_LONG_SHIFT) == BF_LONG_NONE;
+  std::vector<int> kcu(batch + 1, 0), vt_off(batch + 1, 0), vt_t0(batch, 0);
   for (int b = 0; b < batch; ++b) {
     const long long N = (long long)j.qpos[b] + (j.cu[b + 1] - j.cu[b]);
     kcu[b + 1] = (int)(kcu[b] + N);
-    vt_off[b + 1] = vt_off[b] + (int)((N + bf::kKeyTile - 1) / bf::kKeyTile) * bf::kKeyTile;
+    // band only: no query of the sequence reaches a key below qpos - w0 + 1,
+    // so V^T (and a paged gather) start at that key's tile
+    if (band_mode) vt_t0[b] = (int)(std::max(0LL, (long long)j.qpos[b] - j.w0 + 1) / bf::kKeyTile);
+    const long long tiles = (N + bf::kKeyTile - 1) / bf::kKeyTile - vt_t0[b];
+    vt_off[b + 1] = vt_off[b] + (int)tiles * bf::kKeyTile;
   }
   Tk = kcu[batch];
   const bool paged = j.pk.block_table != nullptr;
@@ -222,6 +227,7 @@ int run_rows(RowsJob& j) {
       st.kcu[i] = kcu[b0 + i];
       st.vt_off[i] = vt_off[b0 + i];
     }
+    for (int i = 0; i < nb; ++i) st.vt_t0[i] = vt_t0[b0 + i];
     for (int i = 0; i < nb; ++i) {
       const long long Lq = j.cu[b0 + i + 1] - j.cu[b0 + i];
       const long long N = j.qpos[b0 + i] + Lq;

@@ -140,6 +140,7 @@ __global__ __launch_bounds__(256) void correction_prep_kernel(PrepParams p, SeqT
   const bool copy = keys && p.kcopy != nullptr;  // paged keys: gather the packed copy
   if (!rot && !copy) return;
   const long long row = tok - cu(b);
+  if (keys && row < (long long)st.vt_t0[b] * kKeyTile) return;  // key no window reaches
   float c = 1.f, sn = 0.f;
   if (rot) {
     const long long pos = keys ? row : st.qpos[b] + row;
@@ -186,7 +187,7 @@ __global__ __launch_bounds__(256) void vt_transpose_kernel(VtParams p, SeqTable 
   const int h = blockIdx.y;
   int b = 0;
   while (b + 1 < st.n && c >= st.vt_off[b + 1]) ++b;
-  const int p0 = c - st.vt_off[b];
+  const int p0 = c - st.vt_off[b] + st.vt_t0[b] * kKeyTile;  // first key of the tile
   const int L = st.kcu[b + 1] - st.kcu[b];
   __shared__ long long rows[kKeyTile];  // V row of each key of the tile, -1 past the end
   if (threadIdx.x < kKeyTile) {
@@ -778,9 +779,11 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillParams p, S
   const uint16_t* qg = (const uint16_t*)p.q + ((size_t)it.hq * p.T + it.tok0) * kHeadDim;
   const uint16_t* kg =
       (const uint16_t*)p.k + ((size_t)it.kvh * p.k_hstride + st.kbase[it.b]) * kHeadDim;
+  // V^T tile t of the sequence sits at vt0 + t tiles, t >= vt_t0 (the first
+  // tile with a copy; the passes never go below it)
   const uint16_t* vt0 = (const uint16_t*)p.vt +
-                        ((size_t)it.kvh * (p.Tpad / kKeyTile) + st.vt_off[it.b] / kKeyTile) *
-                            (kHeadDim * kKeyTile);
+                        ((long long)it.kvh * (p.Tpad / kKeyTile) + st.vt_off[it.b] / kKeyTile -
+                         st.vt_t0[it.b]) * (kHeadDim * kKeyTile);
 
   // ends of the K, K'' and V^T tensors (range limit of the staging loads)
   const char* k_end = (const char*)p.k + (size_t)p.k_rows * kHeadDim * 2;
@@ -876,8 +879,8 @@ __global__ __launch_bounds__(256, 1) void prefill_f32_kernel(PrefillParams p, Se
   const int nk = it.qp + it.L;   // keys of the sequence
   const int p0 = it.qp + it.r0;  // position of the wave's first row
   const float* vt0 = (const float*)p.vt +
-                     ((size_t)it.kvh * (p.Tpad / kKeyTile) + st.vt_off[it.b] / kKeyTile) *
-                         (kHeadDim * kKeyTile);
+                     ((long long)it.kvh * (p.Tpad / kKeyTile) + st.vt_off[it.b] / kKeyTile -
+                      st.vt_t0[it.b]) * (kHeadDim * kKeyTile);
 
   float qf[64], qf2[64];
   {
@@ -905,7 +908,7 @@ __global__ __launch_bounds__(256, 1) void prefill_f32_kernel(PrefillParams p, Se
   for (int db = 0; db < 4; ++db) oacc[db] = f32x16{};
   const uint4 zero4 = make_uint4(0, 0, 0, 0);
 
-  for (int kt = 0; kt < it.nkt; ++kt) {
+  for (int kt = st.vt_t0[it.b]; kt < it.nkt; ++kt) {  // tiles below vt_t0 hold no pair of these rows
     const int c0 = kt * kKeyTile;
     bool cf, cl;
     tile_needs<BIFOCAL>((long long)it.qp + it.R0, p.P_wg, c0, w0, cf, cl);
