@@ -304,3 +304,53 @@ def test_decode_deterministic():
     a = bfl.decode(q, kc, vc, [40000], 4096, 32768, 1e6, "pa")
     b = bfl.decode(q, kc, vc, [40000], 4096, 32768, 1e6, "pa")
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("mode", ["fi", "pa"])
+def test_structured_input_8192_discriminates(mode):
+    # Structured input S1 at the size the scope table fixes (bf16, L = 8192,
+    # w_pre = 2048 so s = 4, w0 = 256): raw q and k of KV group g are
+    # amp * e_{m*_g}, given as q', k' under original RoPE, so every score is
+    # scale * a_q * amp * cos(theta_m* * dpos) and the far branch's dpos
+    # (phi(i) - phi(j) for FI or PA, i - j without the correction) moves the
+    # output at O(1). The kernel must match the oracle on the same bf16 inputs
+    # and sit far from plain attention (bar 0.05: the gap is ~27x the bf16
+    # error) and from the other long mode. FI and PA move this input's output
+    # far less (the Fourier-feature values average over many keys): that gap
+    # is only ~2.6x the bf16 error of q'', k'' and P, so its bar is 0.5 (a
+    # kernel computing the other mode would sit near 1).
+    L, D, theta, w0, w_pre = 8192, 128, 1e4, 256, 2048
+    scale = 1 / math.sqrt(D)
+    amp = math.sqrt(8 / scale)
+    mstars = [1, 9]
+    pos = np.arange(L)
+    q = np.zeros((4, L, D), np.float32)
+    k = np.zeros((2, L, D), np.float32)
+    v = np.zeros((2, L, D), np.float32)
+    for g, ms in enumerate(mstars):
+        th = theta ** (-2.0 * ms / D)
+        k[g, :, ms], k[g, :, ms + 64] = amp * np.cos(pos * th), amp * np.sin(pos * th)
+        for hh, a_q in enumerate((amp, 0.5 * amp)):
+            q[2 * g + hh, :, ms], q[2 * g + hh, :, ms + 64] = a_q * np.cos(pos * th), a_q * np.sin(pos * th)
+    for kk in range(64):
+        v[:, :, 2 * kk] = np.cos(2 * np.pi * pos * kk / L)
+        v[:, :, 2 * kk + 1] = np.sin(2 * np.pi * pos * kk / L)
+    qb, kb, vb = (torch.from_numpy(x).to(torch.bfloat16) for x in (q, k, v))
+    o = bfl.prefill(qb.cuda(), kb.cuda(), vb.cuda(), [0, L], w0, w_pre, theta, mode, scale)
+    torch.cuda.synchronize()
+    rows = np.array(sorted(set([0, 255, 256, 257, 2047, 2048, 4096, 8190, 8191] +
+                               list(np.random.default_rng(12).integers(0, L, 40)))))
+    qf, kf, vf = qb.float().numpy(), kb.float().numpy(), vb.float().numpy()
+    ref, _ = oracle.prefill(qf, kf, vf, [0, L], w0, w_pre, theta, mode, scale, rows=rows)
+    other, _ = oracle.prefill(qf, kf, vf, [0, L], w0, w_pre, theta, "pa" if mode == "fi" else "fi",
+                              scale, rows=rows)
+    plain, _ = oracle.prefill(qf, kf, vf, [0, L], 10**9, w_pre, theta, mode, scale, rows=rows)
+    og = o[:, torch.from_numpy(rows).cuda()].float().cpu().numpy()
+    _check_bf16(og, ref, f"S1 8192 {mode}")
+    far = rows >= w0
+    err = np.linalg.norm(og[:, far] - ref[:, far])
+    gap_mode = np.linalg.norm(ref[:, far] - other[:, far])
+    gap_plain = np.linalg.norm(ref[:, far] - plain[:, far])
+    print(f"[S1 8192 {mode}] err {err:.3e} gap-other-mode {gap_mode:.3e} gap-plain {gap_plain:.3e}",
+          flush=True)
+    assert err <= 0.05 * gap_plain and err <= 0.5 * gap_mode
