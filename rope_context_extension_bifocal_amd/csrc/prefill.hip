@@ -3,10 +3,16 @@
 // Kernels:
 //   correction_prep_kernel  far-branch copies q'' = R(Delta(i)) q', k'' = R(Delta(j)) k'
 //                           with Delta_m(p) = theta_m * (phi(p) - p), angles in fp64
+//                           (and, for a paged key source, the packed copy of k')
 //                           [ai-feeds.com summary, "关键模块" item 3: correction
 //                            rotation of cached keys so that long-range keys meet
 //                            the query at the scaled positions]
 //   vt_transpose_kernel     V -> V^T, each sequence padded to a multiple of 64 keys
+//
+// The queries of a launch are packed rows; row r of sequence b sits at
+// position qpos[b] + r (0 for a one-shot prefill, N - Lq for a chunk of
+// queries against a KV cache) and sees keys 0 .. qpos[b] + r. Keys come from a
+// packed tensor or a cache (SeqTable: k_hstride, kbase).
 //   prefill_bf16_kernel     MFMA 32x32x16 bf16 tile loop, one online softmax
 //   prefill_f32_kernel      the same loop on MFMA 32x32x2 f32 for fp32 inputs
 //   pair_map_kernel         test hook: the device pair rule and position map
@@ -477,24 +483,18 @@ __device__ __forceinline__ const char* scalar_ptr(const void* p) {
   return (const char*)(((uint64_t)hi << 32) | lo);
 }
 
-__device__ __forceinline__ void g2lds(const char* gbase, uint32_t off, uint4* lds) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(gbase + off),
-                                   (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
-}
-
-// ktile: first key of the tile; keys_left (>= 1, wave-uniform): keys of the
-// sequence from that key on. Rows past the sequence end read its last key
-// (finite data; those scores are masked).
 // Direct global -> LDS staging of one 64-key tile through a buffer resource
 // whose base is the tile start and whose size runs to the end of the tensor:
 // instruction i of a wave reads 1 KiB at lane offset (fixed per pass) + 4 KiB
 // i. Base and size sit in scalar registers, so a load costs no vector
-// arithmetic. K rows past a sequence end read the next tokens of the packed
-// tensor (finite data; those scores are masked) and reads past the tensor end
-// return zeros (buffer range check). V^T tiles are zero-padded per sequence.
+// arithmetic. K rows past a sequence's last key read whatever the next rows of
+// the K tensor hold (the next tokens of a packed tensor, or cache slots past
+// N): every score of such a key is replaced by -inf before use, and reads past
+// the tensor end return zeros (buffer range check). V^T tiles are zero-padded
+// per sequence, so P = 0 never meets a non-finite value.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char* tile, const char* end) {
   const long long left = (long long)(end - tile);
-  const int n = (int)(left < 0x7fffffffLL ? left : 0x7fffffffLL);
+  const int n = (int)(left < 0 ? 0 : left < 0x7fffffffLL ? left : 0x7fffffffLL);
   return __builtin_amdgcn_make_buffer_rsrc((void*)tile, (short)0, n, 0x00020000);
 }
 
@@ -666,8 +666,8 @@ __device__ __forceinline__ void pv_softmax(uint32_t slot_off, const u32x4 (&Pp)[
 // (pv_softmax), then QK^T of tile t + 1. K tiles are staged two tiles ahead of
 // their QK^T and V^T tiles one tile ahead of their P V, in two-slot rings
 // (slot = (t - ktb) % 2). Tiles from kte_w on hold no causal pair of this
-// wave's rows: there it only stages and takes part in the barriers. vt0
-// points at the sequence's first V^T tile of this KV head.
+// wave's rows: there it only stages and takes part in the barriers. vt0 + t
+// tiles is the sequence's V^T tile t of this KV head (for t >= ktb).
 template <bool FAR>
 __device__ __forceinline__ void run_pass(const uint16_t* qsrc, const uint16_t* ksrc,
                                          const uint16_t* vt0, const char* kend, const char* vend,
