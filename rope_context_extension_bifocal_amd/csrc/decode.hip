@@ -9,7 +9,9 @@
 //   RoPE]. The query gets the same correction at its own position. Scores use
 //   MFMA 16x16x32 (queries as columns), P V uses MFMA 16x16x16, with one
 //   online softmax state per query and wave; at the end the waves are merged
-//   and the split writes its (m, l, acc) partial.
+//   and the split writes its (m, l, acc) partial. Instantiated for a
+//   contiguous or a paged cache, and with non-temporal K / V loads for
+//   launches that stream more than the MALL could keep.
 // decode_combine_kernel: log-sum-exp merge of the splits of each query head.
 #include <hip/hip_runtime.h>
 
