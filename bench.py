@@ -354,6 +354,31 @@ def main():
                          "bifocal_cold_gbs": round(nbytes / (t_c * 1e-3) / 1e9, 1)}
         del qs, ks, vs
 
+    log("batched decode")
+    batched = {}
+    for Bb, Nb in ((32, 8193), (128, 2049)):
+        gq = torch.Generator(device="cuda").manual_seed(Bb)
+        qb = torch.randn(Bb, Hq, D, generator=gq, device="cuda").to(torch.bfloat16)
+        copies = max(2, math.ceil(2 * MALL / (2.0 * Bb * Hkv * Nb * D * 2)))
+        cb = [(torch.randn(Bb, Hkv, Nb, D, generator=gq, device="cuda").to(torch.bfloat16),
+               torch.randn(Bb, Hkv, Nb, D, generator=gq, device="cuda").to(torch.bfloat16))
+              for _ in range(copies)]
+        wsb = bfl.alloc_workspace(bfl.workspace_bytes(bfl.BF_PHASE_DECODE, Bb, Nb, Hq, Hkv), "cuda")
+        ob = torch.empty_like(qb)
+        itb = [0]
+
+        def bfn():  # rotate over cache copies: every call streams its cache from HBM
+            kx, vx = cb[itb[0] % copies]
+            itb[0] += 1
+            bfl.decode(qb, kx, vx, [Nb] * Bb, dcfg["w0"], dcfg["w_pre"], dcfg["theta"], "fi", scale,
+                       out=ob, workspace=wsb)
+        for _ in range(10):
+            bfn()
+        tb = time_calls(bfn, 50, stream)
+        nbytes = 2.0 * Bb * Hkv * Nb * D * 2
+        batched[f"{Bb}x{Nb}"] = {"us": round(tb * 1e3, 2), "gbs": round(nbytes / (tb * 1e-3) / 1e9, 1)}
+        del cb, qb, wsb, ob
+
     log("band-only (sliding-window) prefill and decode")
     band_fn = lambda: prefill("band")
     band_fn()
@@ -491,6 +516,7 @@ def main():
         "plain_decode_us": round(plain_dec_ms * 1e3, 2),
         "decode_overhead_vs_plain": round(dec_many_ms / plain_dec_ms - 1, 4),
         "decode_small": small,
+        "decode_batched_cold": batched,
         "band_only": {"prefill_ms": round(band_ms, 3),
                       "prefill_tflops": round(band_flops / (band_ms * 1e-3) / 1e12, 2),
                       "decode_us": round(band_dec_ms * 1e3, 2),

@@ -212,7 +212,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p, De
     vwb = dscalar_ptr(vbase + (size_t)(ns > 0 ? kw0 : 0) * kHeadDim);
   } else {
     // the pages this wave's keys live in, one per lane (a wave spans at most
-    // per / 16 + 1 <= 33 pages), read once; each step picks its page by lane
+    // per / 16 + 1 <= 64 pages), read once; each step picks its page by lane
     kwb = dscalar_ptr(p.kc);
     vwb = dscalar_ptr(p.vc);
     if (ns > 0) {
@@ -600,38 +600,55 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p, Dec
 }
 
 // ------------------------------------------------------------------ host side
-// Split geometry. A launch should hold about kDecTargetWgs split workgroups
-// (two per CU of the 256 CUs: one full round), so a sequence gets
-// kDecTargetWgs / (Hkv x batch) splits, between 8 and 128, of 64 to
-// kDecMaxChunk keys each (the bounds are build-time overridable for tuning).
+// Split geometry. The chip holds kDecTargetWgs split workgroups at once (two
+// per CU of the 256 CUs: one round). For N keys of a sequence in a launch of
+// `per` (sequence, KV head) groups the split count is the one that minimises
+// rounds x (chunk + a fixed per-workgroup cost), over splits of 256 to
+// kDecMaxChunk keys (at most kDecMaxTargetSplits splits unless the cap needs
+// more), with the keys spread evenly; a last split of under a quarter chunk
+// rides along without a round of its own. The bounds are build-time
+// overridable for tuning.
 #ifndef BF_DEC_TARGET_WGS
 #define BF_DEC_TARGET_WGS 512
 #endif
 #ifndef BF_DEC_MAX_CHUNK
-#define BF_DEC_MAX_CHUNK 2048
+#define BF_DEC_MAX_CHUNK 4032
 #endif
 constexpr long long kDecTargetWgs = BF_DEC_TARGET_WGS;
 constexpr long long kDecMaxChunk = BF_DEC_MAX_CHUNK;
 // K + V bytes of a launch from which its loads are non-temporal (a quarter of
 // the 256 MB MALL: smaller caches can stay resident between calls)
 constexpr long long kDecStreamBytes = 64LL << 20;
-constexpr long long kDecMinTargetSplits = 8, kDecMaxTargetSplits = 128;
+constexpr long long kDecMaxTargetSplits = 128;
+constexpr long long kDecMinChunk = 256;  // fewer keys per split cost more than they save
+constexpr long long kDecWgCost = 256;    // fixed cost of a split workgroup, in keys
 static_assert(kDecMaxChunk % kDecBlock == 0, "chunk must be a multiple of 64 keys");
 
 static long long decode_target_splits(int batch, int Hkv) {
-  const long long per = (long long)batch * Hkv;
-  long long t = (kDecTargetWgs + per - 1) / per;
-  if (t < kDecMinTargetSplits) t = kDecMinTargetSplits;
-  if (t > kDecMaxTargetSplits) t = kDecMaxTargetSplits;
-  return t;
+  return (long long)batch * Hkv;  // (sequence, KV head) groups sharing the launch
 }
 
-static int decode_chunk(long long N, long long target) {
-  long long c = (N + target - 1) / target;
-  c = ((c + kDecBlock - 1) / kDecBlock) * kDecBlock;
-  if (c < kDecBlock) c = kDecBlock;
-  if (c > kDecMaxChunk) c = kDecMaxChunk;
-  return (int)c;
+static int decode_chunk(long long N, long long per) {
+  const long long need = (N + kDecMaxChunk - 1) / kDecMaxChunk;  // splits the cap forces
+  long long most = (N + kDecMinChunk - 1) / kDecMinChunk;
+  if (most > kDecMaxTargetSplits) most = kDecMaxTargetSplits;
+  if (most < need) most = need;
+  long long best_c = kDecMaxChunk, best_cost = -1;
+  for (long long sp = need; sp <= most; ++sp) {
+    long long c = (N + sp - 1) / sp;
+    c = ((c + kDecBlock - 1) / kDecBlock) * kDecBlock;
+    if (c > kDecMaxChunk) continue;
+    const long long nsp = (N + c - 1) / c;
+    const long long rem = N - (nsp - 1) * c;              // keys of the last split
+    const long long heavy = nsp - (rem * 4 < c ? 1 : 0);  // a short last split rides along
+    const long long rounds = (per * heavy + kDecTargetWgs - 1) / kDecTargetWgs;
+    const long long cost = rounds * (c + kDecWgCost);
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best_c = c;
+    }
+  }
+  return (int)best_c;
 }
 
 static int decode_splits(long long N, long long target) {
