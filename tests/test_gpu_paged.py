@@ -94,3 +94,24 @@ def test_paged_validation():
     kp24 = torch.zeros((4, 2, 24, 128), dtype=torch.bfloat16, device="cuda")  # not a power of two
     with pytest.raises(bfl.BifocalError):
         bfl.decode_paged(q, kp24, kp24, table, [10], 16, 64, 1e4, "fi", 0.1)
+
+
+def test_paged_longest_wave_span():
+    # 64 sequences x 8 KV heads of 16128 keys make the split rule choose
+    # 4032-key chunks: each wave's 1008 keys span 63 pages of 16, close to the
+    # 64 page numbers a wave holds in its lanes
+    B, Hq, Hkv, N, page = 64, 8, 8, 16128, 16
+    q, kc, vc = wl.decode_inputs(B, Hq, Hkv, N, 128, "bf16", 103)
+    q, kc, vc = q.cuda(), kc.cuda(), vc.cuda()
+    o_c = bfl.decode(q, kc, vc, [N] * B, 4096, 8192, 1e6, "pa", 0.088)
+    per = N // page
+    perm = torch.randperm(B * per, generator=torch.Generator().manual_seed(104)).cuda()
+    kp = torch.empty((B * per, Hkv, page, 128), dtype=torch.bfloat16, device="cuda")
+    vp = torch.empty_like(kp)
+    kp[perm] = kc.view(B, Hkv, per, page, 128).permute(0, 2, 1, 3, 4).reshape(B * per, Hkv, page, 128)
+    vp[perm] = vc.view(B, Hkv, per, page, 128).permute(0, 2, 1, 3, 4).reshape(B * per, Hkv, page, 128)
+    del kc, vc
+    o_p = bfl.decode_paged(q, kp, vp, perm.to(torch.int32).view(B, per), [N] * B, 4096, 8192, 1e6,
+                           "pa", 0.088)
+    torch.cuda.synchronize()
+    assert torch.equal(o_p, o_c)
