@@ -407,6 +407,23 @@ def main():
     ragged_flops = 4.0 * D * rcfg["Hq"] * sum(x * (x + 1) / 2 for x in rlens)
     del rq, rk, rv, ro, rws
 
+    log("batched prefill: 64 x 2048 and 16 x 8192 prompts")
+    batched_pre = {}
+    for nb, lb in ((64, 2048), (16, 8192)):
+        bcu = wl.cu_seqlens([lb] * nb)
+        bq, bk, bv = (x.cuda() for x in wl.prefill_inputs(Hq, Hkv, bcu[-1], D, "bf16", 31 + nb))
+        bo = torch.empty_like(bq)
+        bws = bfl.alloc_workspace(bfl.workspace_bytes(bfl.BF_PHASE_PREFILL, nb, bcu[-1], Hq, Hkv),
+                                  "cuda")
+        bfn = lambda: bfl.prefill(bq, bk, bv, bcu, cfg["w0"], cfg["w_pre"], cfg["theta"], "fi",
+                                  scale, out=bo, workspace=bws)
+        bfn()
+        b_ms = time_calls(bfn, 5, stream)
+        b_flops = 4.0 * D * Hq * nb * lb * (lb + 1) / 2
+        batched_pre[f"{nb}x{lb}"] = {"ms": round(b_ms, 3),
+                                     "tflops": round(b_flops / (b_ms * 1e-3) / 1e12, 2)}
+        del bq, bk, bv, bo, bws
+
     log("chunked prefill: the last 4096 / 16384 queries against the 128K cache")
     kcc, vcc = kd.unsqueeze(0), vd.unsqueeze(0)  # [1, Hkv, L, D]: the cache layout, cap = L
     chunk = {}
@@ -523,6 +540,7 @@ def main():
                       "decode_gbs": round(band_dec_bytes / (band_dec_ms * 1e-3) / 1e9, 1)},
         "ragged_prefill": {"lengths": rlens, "ms": round(ragged_ms, 3),
                            "tflops": round(ragged_flops / (ragged_ms * 1e-3) / 1e12, 2)},
+        "batched_prefill": batched_pre,
         "chunk_prefill_at_128k": chunk,
         "rope_prefill_ms": round(rope_ms, 4),
         "rope_prefill_gbs": round(rope_gbs, 1),

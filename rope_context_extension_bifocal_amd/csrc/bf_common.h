@@ -30,7 +30,8 @@ struct SeqTable {
   int vt_t0[kMaxSeqPerLaunch];        // first key tile with a V^T copy: 0, or for band-only chunks
                                       // the first tile any query's window reaches
   int qpos[kMaxSeqPerLaunch];         // position of the sequence's first query row
-  int rboff[kMaxSeqPerLaunch];        // qpos / P_wg: heaviest-first rank offset of its row blocks
+  int order[kMaxSeqPerLaunch];        // sequences in work order (most scored pairs first)
+  int ioff[kMaxSeqPerLaunch + 1];     // first work-item rank of order[i]; ioff[n] = all row blocks
   long long kbase[kMaxSeqPerLaunch];  // K / V row offset of the sequence's key 0
   int s[kMaxSeqPerLaunch];            // s(L_b) (1 = no far branch)
   int nrb[kMaxSeqPerLaunch];          // query row blocks of the sequence
@@ -58,8 +59,6 @@ struct PrefillParams {
   int hpw;          // query heads per workgroup
   int n_hsub;       // workgroups per (KV head, row block) = G / hpw
   int P_wg;         // query positions per workgroup
-  int total_items;  // row blocks over all sequences of the launch
-  int max_nrb;      // 1 + the largest rank index rb + rboff[b]
 };
 
 // A paged K / V source: pages [num_pages][Hkv][page][D], key j of sequence

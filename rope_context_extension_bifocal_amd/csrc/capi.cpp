@@ -181,6 +181,15 @@ int check_rows_common(bool bifocal, int batch, int Hq, int Hkv, int head_dim, in
   return check_scale(scale);
 }
 
+// Query-key pairs a sequence scores: Lq queries at positions qpos .. qpos +
+// Lq - 1, each seeing every key up to its own position, or only the nearest
+// band of them when band >= 0 (band-only attention, band = w0).
+double scored_pairs(long long qpos, long long Lq, long long band) {
+  if (band < 0) return (double)Lq * qpos + 0.5 * (double)Lq * (Lq + 1);
+  const long long a = std::min(Lq, std::max(0LL, band - qpos - 1));  // rows seeing < band keys
+  return (double)a * (qpos + 1) + 0.5 * (double)a * (a - 1) + (double)(Lq - a) * band;
+}
+
 int run_rows(RowsJob& j) {
   const int batch = j.batch, Hq = j.Hq, Hkv = j.Hkv, dtype = j.dtype;
   const bool bifocal = j.bifocal;
@@ -221,7 +230,8 @@ int run_rows(RowsJob& j) {
     std::memset(&st, 0, sizeof st);
     st.n = nb;
     bool any_far = false;
-    int total_items = 0, max_nrb = 0;
+    int total_items = 0;
+    double work[bf::kMaxSeqPerLaunch];
     for (int i = 0; i <= nb; ++i) {
       st.cu[i] = j.cu[b0 + i];
       st.kcu[i] = kcu[b0 + i];
@@ -242,10 +252,15 @@ int run_rows(RowsJob& j) {
       // (position N - 1) reaches back past the window
       if ((s > 1 || band_only) && j.w0 < N) any_far = true;
       st.nrb[i] = (int)((Lq + geo.P_wg - 1) / geo.P_wg);
-      st.rboff[i] = st.qpos[i] / geo.P_wg;
       total_items += st.nrb[i];
-      max_nrb = std::max(max_nrb, st.nrb[i] + st.rboff[i]);
+      work[i] = scored_pairs(j.qpos[b0 + i], Lq, band_only ? j.w0 : -1);
     }
+    // work order: sequences with the most scored pairs first (ties in batch
+    // order), each one's row blocks as one run of ranks
+    std::iota(st.order, st.order + nb, 0);
+    std::stable_sort(st.order, st.order + nb, [&](int a, int b) { return work[a] > work[b]; });
+    st.ioff[0] = 0;
+    for (int i = 0; i < nb; ++i) st.ioff[i + 1] = st.ioff[i] + st.nrb[st.order[i]];
     hipError_t e = hipSuccess;
     bf::PagedKV pk = j.pk;  // the block-table rows of this launch's sequences
     if (paged) pk.block_table += (size_t)b0 * pk.max_pages;
@@ -280,8 +295,6 @@ int run_rows(RowsJob& j) {
     pp.hpw = geo.hpw;
     pp.n_hsub = geo.n_hsub;
     pp.P_wg = geo.P_wg;
-    pp.total_items = total_items;
-    pp.max_nrb = max_nrb;
     const long long grid = (long long)Hkv * geo.n_hsub * total_items;
     if (grid > 0x7fffffffLL) return fail(BF_ERR_INVALID_ARG, "launch grid too large");
     if (trace_on())

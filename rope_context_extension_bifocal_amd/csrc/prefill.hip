@@ -74,33 +74,20 @@ __device__ __forceinline__ int key_of_acc(int r, int hl) {  // key of acc regist
   return ((r >> 3) << 4) | (hl << 3) | (r & 7);
 }
 
-// Work item of a workgroup: rank counts row blocks heaviest first, across all
-// sequences. Row block rb of sequence b ends near position
-// qpos[b] + (rb + 1) P_wg, so its weight index is x = rb + rboff[b]
-// (rboff = qpos / P_wg, zero for a one-shot prefill); ranks run over x
-// descending, ties by sequence order.
-__device__ __forceinline__ int items_at_or_above(const SeqTable& st, int x) {
-  int n = 0;
-  for (int b = 0; b < st.n; ++b) n += min(st.nrb[b], max(0, st.nrb[b] + st.rboff[b] - x));
-  return n;
-}
-
-__device__ __forceinline__ void decode_item(const SeqTable& st, int rank, int max_nrb, int& b,
-                                            int& rb) {
-  int lo = 0, hi = max_nrb;  // items_at_or_above(lo) > rank >= items_at_or_above(hi)
+// Work item of a workgroup: ranks run over the sequences in the host's work
+// order (order[i] owns ranks ioff[i] .. ioff[i + 1] - 1) and, inside a
+// sequence, over its row blocks last (heaviest) first. The workgroups that
+// run at the same time then mostly share one sequence's keys, which the XCD's
+// L2 serves, and the lightest items come last.
+__device__ __forceinline__ void decode_item(const SeqTable& st, int rank, int& b, int& rb) {
+  int lo = 0, hi = st.n;  // the last i with ioff[i] <= rank (that sequence has items)
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (items_at_or_above(st, mid) > rank) lo = mid;
+    if (st.ioff[mid] <= rank) lo = mid;
     else hi = mid;
   }
-  int e = rank - items_at_or_above(st, lo + 1);
-  for (b = 0; b < st.n; ++b) {
-    if (st.rboff[b] <= lo && lo < st.nrb[b] + st.rboff[b]) {
-      if (e == 0) break;
-      --e;
-    }
-  }
-  rb = lo - st.rboff[b];
+  b = st.order[lo];
+  rb = st.nrb[b] - 1 - (rank - st.ioff[lo]);
 }
 
 // ----------------------------------------------------------------- prep
@@ -234,7 +221,7 @@ __device__ __forceinline__ Item make_item(const PrefillParams& p, const SeqTable
   const int hsub = r1 % p.n_hsub;
   const int rank = r1 / p.n_hsub;
   int rb;
-  decode_item(st, rank, p.max_nrb, it.b, rb);
+  decode_item(st, rank, it.b, rb);
   it.tok0 = st.cu[it.b];
   it.L = st.cu[it.b + 1] - it.tok0;
   it.qp = st.qpos[it.b];
