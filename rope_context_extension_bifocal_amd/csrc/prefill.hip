@@ -7,7 +7,7 @@
 //                           [ai-feeds.com summary, "关键模块" item 3: correction
 //                            rotation of cached keys so that long-range keys meet
 //                            the query at the scaled positions]
-//   vt_transpose_kernel     V -> V^T, each sequence padded to a multiple of 64 keys
+//   vt_transpose_*_kernel   V -> V^T, each sequence padded to a multiple of 64 keys
 //
 // The queries of a launch are packed rows; row r of sequence b sits at
 // position qpos[b] + r (0 for a one-shot prefill, N - Lq for a chunk of
@@ -173,32 +173,87 @@ __global__ __launch_bounds__(256) void correction_prep_kernel(PrepParams p, SeqT
 // key axis, sequence b owns tiles vt_off[b] / 64 ..) of KV head h is the
 // contiguous block vt[(h * Tpad / 64 + t) * D * 64 ..], laid out
 // [head dim][64 keys]. Keys past a sequence's length are zero.
-template <typename T>
-__global__ __launch_bounds__(256) void vt_transpose_kernel(VtParams p, SeqTable st) {
-  __shared__ T tile[kKeyTile][kHeadDim + 2];
+// Sequence of the padded V^T column c: the last b with vt_off[b] <= c.
+__device__ __forceinline__ int seq_of_vt(const SeqTable& st, int c) {
+  int lo = 0, hi = st.n;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (st.vt_off[mid] <= c) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
+
+// fp32 V^T: one 256-thread workgroup per (64-key tile, KV head), through LDS.
+__global__ __launch_bounds__(256) void vt_transpose_f32_kernel(VtParams p, SeqTable st) {
+  __shared__ float tile[kKeyTile][kHeadDim + 1];
+  __shared__ long long rows[kKeyTile];  // V row of each key of the tile, -1 past the end
   const int c = st.vt_off[0] + blockIdx.x * kKeyTile;
   const int h = blockIdx.y;
-  int b = 0;
-  while (b + 1 < st.n && c >= st.vt_off[b + 1]) ++b;
+  const int b = seq_of_vt(st, c);
   const int p0 = c - st.vt_off[b] + st.vt_t0[b] * kKeyTile;  // first key of the tile
   const int L = st.kcu[b + 1] - st.kcu[b];
-  __shared__ long long rows[kKeyTile];  // V row of each key of the tile, -1 past the end
   if (threadIdx.x < kKeyTile) {
     const int j = p0 + threadIdx.x;
     rows[threadIdx.x] = j < L ? kv_row(p.pk, st, p.k_hstride, p.Hkv, b, h, j) : -1;
   }
   __syncthreads();
-  const T* v = (const T*)p.v;
+  const float* v = (const float*)p.v;
   for (int e = threadIdx.x; e < kKeyTile * kHeadDim; e += 256) {
     const int r = e / kHeadDim, d = e % kHeadDim;
     const long long vr = rows[r];
-    tile[r][d] = vr >= 0 ? v[(size_t)vr * kHeadDim + d] : T(0);
+    tile[r][d] = vr >= 0 ? v[(size_t)vr * kHeadDim + d] : 0.f;
   }
   __syncthreads();
-  T* vt = (T*)p.vt + ((size_t)h * (p.Tpad / kKeyTile) + c / kKeyTile) * (kHeadDim * kKeyTile);
+  float* vt = (float*)p.vt + ((size_t)h * (p.Tpad / kKeyTile) + c / kKeyTile) * (kHeadDim * kKeyTile);
   for (int e = threadIdx.x; e < kKeyTile * kHeadDim; e += 256) {
     const int d = e / kKeyTile, r = e % kKeyTile;
     vt[d * kKeyTile + r] = tile[r][d];
+  }
+}
+
+// bf16 V^T: one 128-thread workgroup per (64-key tile, KV head), no LDS for
+// the data. Thread t moves the block of keys 8 kb .. 8 kb + 7 and head dims
+// 8 db .. 8 db + 7 (kb = t % 8, db = t / 8): eight 16-byte reads (one per
+// key), a transpose in registers, and eight 16-byte writes (one per head
+// dim, 8 keys each). Each read or write instruction of a wave then covers
+// whole 128-byte lines: 8 keys x 128 bytes of V, or 8 full V^T rows.
+__global__ __launch_bounds__(128) void vt_transpose_bf16_kernel(VtParams p, SeqTable st) {
+  __shared__ long long rows[kKeyTile];  // V row of each key of the tile, -1 past the end
+  const int c = st.vt_off[0] + blockIdx.x * kKeyTile;
+  const int h = blockIdx.y;
+  const int b = seq_of_vt(st, c);
+  const int p0 = c - st.vt_off[b] + st.vt_t0[b] * kKeyTile;  // first key of the tile
+  const int L = st.kcu[b + 1] - st.kcu[b];
+  if (threadIdx.x < kKeyTile) {
+    const int j = p0 + threadIdx.x;
+    rows[threadIdx.x] = j < L ? kv_row(p.pk, st, p.k_hstride, p.Hkv, b, h, j) : -1;
+  }
+  __syncthreads();
+  const int kb = threadIdx.x & 7, db = threadIdx.x >> 3;
+  const uint16_t* v = (const uint16_t*)p.v;
+  uint32_t in[8][4];  // key 8 kb + k: head dims 8 db + 2 w (low half) and + 1 (high half)
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const long long vr = rows[kb * 8 + k];
+    uint4 x = make_uint4(0, 0, 0, 0);
+    if (vr >= 0) x = *(const uint4*)(v + (size_t)vr * kHeadDim + db * 8);
+    in[k][0] = x.x;
+    in[k][1] = x.y;
+    in[k][2] = x.z;
+    in[k][3] = x.w;
+  }
+  uint16_t* vt = (uint16_t*)p.vt +
+                 ((size_t)h * (p.Tpad / kKeyTile) + c / kKeyTile) * (kHeadDim * kKeyTile);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {  // head dim 8 db + i: keys 8 kb .. 8 kb + 7, two per word
+    uint32_t w[4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const uint32_t x = in[2 * a][i >> 1], y = in[2 * a + 1][i >> 1];
+      w[a] = (i & 1) ? ((x >> 16) | (y & 0xFFFF0000u)) : ((x & 0xFFFFu) | (y << 16));
+    }
+    *(uint4*)(vt + (size_t)(db * 8 + i) * kKeyTile + kb * 8) = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
 
@@ -1053,9 +1108,9 @@ hipError_t launch_vt_transpose(int dtype, const VtParams& vp, const SeqTable& st
                                hipStream_t stream) {
   dim3 grid((st.vt_off[st.n] - st.vt_off[0]) / kKeyTile, vp.Hkv);
   if (dtype == 0)
-    hipLaunchKernelGGL(vt_transpose_kernel<uint16_t>, grid, dim3(256), 0, stream, vp, st);
+    hipLaunchKernelGGL(vt_transpose_bf16_kernel, grid, dim3(128), 0, stream, vp, st);
   else
-    hipLaunchKernelGGL(vt_transpose_kernel<float>, grid, dim3(256), 0, stream, vp, st);
+    hipLaunchKernelGGL(vt_transpose_f32_kernel, grid, dim3(256), 0, stream, vp, st);
   return hipGetLastError();
 }
 
