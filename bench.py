@@ -424,10 +424,10 @@ def main():
                                      "tflops": round(b_flops / (b_ms * 1e-3) / 1e12, 2)}
         del bq, bk, bv, bo, bws
 
-    log("chunked prefill: the last 4096 / 16384 queries against the 128K cache")
+    log("chunked prefill: the last 512 / 4096 / 16384 queries against the 128K cache")
     kcc, vcc = kd.unsqueeze(0), vd.unsqueeze(0)  # [1, Hkv, L, D]: the cache layout, cap = L
     chunk = {}
-    for lq in (4096, 16384):
+    for lq in (512, 4096, 16384):
         qch = qd[:, L - lq:].contiguous()
         och = torch.empty_like(qch)
         wsc = bfl.alloc_workspace(bfl.chunk_workspace_bytes(1, lq, L, Hq, Hkv), "cuda")

@@ -123,6 +123,10 @@ int bifocal_prefill(const void* q, const void* k, const void* v, void* o, float*
  * Workspace bytes of bifocal_prefill_chunk (paged = 0) and
  * bifocal_prefill_chunk_paged (paged = 1): q_tokens = cu_q[batch] (the packed
  * queries), kv_tokens = the sum of seqlens[b] (the keys the call reads).
+ * For bf16 chunks too short to fill the GPU with work items (fewer than
+ * about 1024 query rows per KV head group), the size includes room for up to
+ * 8 key splits per item: partial outputs (fp32) and their log-sum-exp,
+ * 516 bytes per (split, query head, query token).
  * Returns 0 for invalid arguments (also kv_tokens < q_tokens).
  */
 size_t bifocal_chunk_workspace_bytes(int32_t batch, int64_t q_tokens, int64_t kv_tokens,
@@ -153,6 +157,13 @@ size_t bifocal_chunk_workspace_bytes(int32_t batch, int64_t q_tokens, int64_t kv
  * Other arguments as bifocal_prefill (bf16 or fp32; every long_mode).
  * With Lq_b = N_b and s_len = NULL this is bifocal_prefill of the cached
  * sequences; with Lq_b = 1 it is bifocal_decode.
+ * Key splits (bf16): when a launch has too few work items (row blocks x KV
+ * heads) for the GPU, each item's key tiles are split into up to 8 parts,
+ * run as separate workgroups, and merged by their log-sum-exp (a second
+ * kernel) before O and lse are written. The split count follows from the
+ * shapes and from the workspace: a workspace that holds the base layout but
+ * not the partials runs unsplit. Split results are deterministic but not
+ * bitwise those of an unsplit call (the merge rounds differently).
  * [mufans.github.io wiki, Jet-Long Dynamic RoPE, "可执行建议": pairing the
  *  method with prompt caching; ai-feeds.com summary, "关键模块" item 3: the
  *  correction rotation applied to cached keys]

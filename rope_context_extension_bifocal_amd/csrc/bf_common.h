@@ -9,6 +9,7 @@ namespace bf {
 constexpr int kHeadDim = 128;     // the only head_dim the kernels are built for
 constexpr int kPairs = kHeadDim / 2;
 constexpr int kMaxSeqPerLaunch = 64;
+constexpr int kMaxKeySplits = 8;  // key splits of a chunk launch (prefill_bf16_kernel)
 constexpr int kKeyTile = 64;      // keys per K/V tile (prefill) and V^T padding unit
 constexpr int kWaveRowsBf16 = 32; // query positions per wave, bf16 prefill
 constexpr int kWaveRowsF32 = 32;  // query positions per wave, fp32 prefill
@@ -59,6 +60,13 @@ struct PrefillParams {
   int hpw;          // query heads per workgroup
   int n_hsub;       // workgroups per (KV head, row block) = G / hpw
   int P_wg;         // query positions per workgroup
+  int total_items;  // row blocks over the launch's sequences
+  // key splits (bf16 only): nks > 1 splits each work item's tile visits into
+  // nks parts; part s writes its normalised O and log2-sum-exp to
+  // part_o [nks][Hq][T][D] and part_lse [nks][Hq][T] instead of o / lse
+  int nks;
+  float* part_o;
+  float* part_lse;
 };
 
 // A paged K / V source: pages [num_pages][Hkv][page][D], key j of sequence

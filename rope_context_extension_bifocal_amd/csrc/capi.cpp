@@ -23,6 +23,8 @@ hipError_t launch_vt_transpose(int dtype, const VtParams& vp, const SeqTable& st
                                hipStream_t stream);
 hipError_t launch_prefill_main(int dtype, bool bifocal, bool band, const PrefillParams& pp,
                                const SeqTable& st, int grid, hipStream_t stream);
+hipError_t launch_chunk_combine(const PrefillParams& pp, int tok_begin, int n_tok,
+                                hipStream_t stream);
 hipError_t launch_pair_map(long long L, long long w0, long long s, int mode, int8_t* br,
                            long long* dphi_num, long long* s_out, hipStream_t stream);
 size_t decode_workspace_bytes(int batch, long long max_len, int Hq);
@@ -98,14 +100,15 @@ PrefillGeom prefill_geom(int dtype, int G) {
 }
 
 struct PrefillWs {
-  size_t vt_off, q2_off, k2_off, kc_off, total;
+  size_t vt_off, q2_off, k2_off, kc_off, base, po_off, pl_off, total;
 };
 
 // Workspace of Tq packed queries against Tk keys (a one-shot prefill has
-// Tk = Tq = T): V^T padded per sequence, q'', k'', and for a paged key
-// source the packed copy of the keys.
+// Tk = Tq = T): V^T padded per sequence, q'', k'', for a paged key source the
+// packed copy of the keys (base ends here), and for `splits` > 1 key splits
+// their partial O (fp32) and log2-sum-exp.
 PrefillWs prefill_ws_layout(int batch, long long Tq, long long Tk, int Hq, int Hkv, int dtype,
-                            bool paged = false) {
+                            bool paged = false, int splits = 1) {
   const size_t es = elem_size(dtype);
   const size_t tpad_bound = (size_t)Tk + 63u * (size_t)batch;
   PrefillWs w;
@@ -113,8 +116,46 @@ PrefillWs prefill_ws_layout(int batch, long long Tq, long long Tk, int Hq, int H
   w.q2_off = align256((size_t)Hkv * bf::kHeadDim * tpad_bound * es);
   w.k2_off = w.q2_off + align256((size_t)Hq * (size_t)Tq * bf::kHeadDim * es);
   w.kc_off = w.k2_off + align256((size_t)Hkv * (size_t)Tk * bf::kHeadDim * es);
-  w.total = w.kc_off + (paged ? align256((size_t)Hkv * (size_t)Tk * bf::kHeadDim * es) : 0);
+  w.base = w.kc_off + (paged ? align256((size_t)Hkv * (size_t)Tk * bf::kHeadDim * es) : 0);
+  const size_t rows = splits > 1 ? (size_t)splits * Hq * (size_t)Tq : 0;
+  w.po_off = w.base;
+  w.pl_off = w.po_off + align256(rows * bf::kHeadDim * sizeof(float));
+  w.total = w.pl_off + align256(rows * sizeof(float));
   return w;
+}
+
+// The 512 workgroup slots of the part: two prefill workgroups on each of 256 CUs.
+constexpr long long kPrefillSlots = 512;
+
+// Largest key-split count a chunk launch of Tq queries may use: a chunk is
+// split only while its work items fill at most two rounds of the slots, so
+// the count is bounded by the fewest items Tq queries can make (one
+// sequence). fp32 launches are not split.
+int chunk_split_cap(long long Tq, int Hq, int Hkv, int dtype) {
+  if (dtype != BF_DTYPE_BF16 || Hkv < 1 || Hq % Hkv) return 1;
+  const PrefillGeom geo = prefill_geom(dtype, Hq / Hkv);
+  const long long wmin = (long long)Hkv * geo.n_hsub * ((Tq + geo.P_wg - 1) / geo.P_wg);
+  return (int)std::max(1LL, std::min<long long>(bf::kMaxKeySplits, 2 * kPrefillSlots / std::max(1LL, wmin)));
+}
+
+// Key splits of one launch: W workgroups whose items visit about `visits`
+// key tiles each. k splits make ceil(W k / slots) rounds of visits / k tiles
+// plus a fixed cost of about 6 tile times per workgroup (prologue, the last
+// P V, the partial's store); the cheapest k up to `cap` wins, with at least
+// 32 tiles per split.
+int pick_key_splits(long long W, double visits, int cap) {
+  int best = 1;
+  double best_cost = -1.0;
+  for (int k = 1; k <= cap; ++k) {
+    if (k > 1 && visits / k < 32.0) break;
+    const double rounds = (double)((W * k + kPrefillSlots - 1) / kPrefillSlots);
+    const double cost = rounds * (visits / k + 6.0);
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best = k;
+    }
+  }
+  return best;
 }
 
 int check_common(int Hq, int Hkv, int head_dim, int dtype) {
@@ -169,6 +210,7 @@ struct RowsJob {
   void* ws = nullptr;
   size_t ws_bytes = 0;
   hipStream_t stream = nullptr;
+  int split_cap = 1;  // key splits allowed (chunk launches; the workspace may cap it further)
 };
 
 // Validation of the arguments both paths share; tensors checked by the caller.
@@ -213,9 +255,14 @@ int run_rows(RowsJob& j) {
   const bool shift = bifocal && (j.mode & BF_LONG_SHIFT);
   const int mode = j.mode & ~BF_LONG_SHIFT;
   const bool band_only = bifocal && mode == BF_LONG_NONE;
-  const size_t need = paged ? wl.total : bifocal && !band_only ? wl.kc_off : wl.q2_off;
+  const size_t need = paged ? wl.base : bifocal && !band_only ? wl.kc_off : wl.q2_off;
   if (j.ws_bytes < need)
     return fail(BF_ERR_WORKSPACE, "workspace too small: %zu bytes given, %zu needed", j.ws_bytes, need);
+  // key splits the workspace has room for (partials after the base layout)
+  int split_cap = dtype == BF_DTYPE_BF16 ? std::max(1, std::min(j.split_cap, bf::kMaxKeySplits)) : 1;
+  while (split_cap > 1 &&
+         prefill_ws_layout(batch, Tq, Tk, Hq, Hkv, dtype, paged, split_cap).total > j.ws_bytes)
+    --split_cap;
 
   const int G = Hq / Hkv;
   const PrefillGeom geo = prefill_geom(dtype, G);
@@ -231,7 +278,7 @@ int run_rows(RowsJob& j) {
     st.n = nb;
     bool any_far = false;
     int total_items = 0;
-    double work[bf::kMaxSeqPerLaunch];
+    double work[bf::kMaxSeqPerLaunch], visit_sum = 0.0;
     for (int i = 0; i <= nb; ++i) {
       st.cu[i] = j.cu[b0 + i];
       st.kcu[i] = kcu[b0 + i];
@@ -253,6 +300,9 @@ int run_rows(RowsJob& j) {
       if ((s > 1 || band_only) && j.w0 < N) any_far = true;
       st.nrb[i] = (int)((Lq + geo.P_wg - 1) / geo.P_wg);
       total_items += st.nrb[i];
+      // key tiles a row block visits: all N keys, or only its window (band only)
+      const long long span = band_only ? std::min(N, j.w0 + geo.P_wg + bf::kKeyTile) : N;
+      visit_sum += (double)st.nrb[i] * (double)((span + bf::kKeyTile - 1) / bf::kKeyTile);
       work[i] = scored_pairs(j.qpos[b0 + i], Lq, band_only ? j.w0 : -1);
     }
     // work order: sequences with the most scored pairs first (ties in batch
@@ -295,14 +345,24 @@ int run_rows(RowsJob& j) {
     pp.hpw = geo.hpw;
     pp.n_hsub = geo.n_hsub;
     pp.P_wg = geo.P_wg;
-    const long long grid = (long long)Hkv * geo.n_hsub * total_items;
+    pp.total_items = total_items;
+    const long long wgs = (long long)Hkv * geo.n_hsub * total_items;
+    pp.nks = split_cap > 1 ? pick_key_splits(wgs, visit_sum / total_items, split_cap) : 1;
+    pp.part_o = pp.nks > 1 ? (float*)(wsb + wl.po_off) : nullptr;
+    pp.part_lse = pp.nks > 1 ? (float*)(wsb + prefill_ws_layout(batch, Tq, Tk, Hq, Hkv, dtype, paged, pp.nks).pl_off)
+                             : nullptr;
+    const long long grid = wgs * pp.nks;
     if (grid > 0x7fffffffLL) return fail(BF_ERR_INVALID_ARG, "launch grid too large");
     if (trace_on())
-      fprintf(stderr, "[bifocal] prefill %s dtype=%d seqs=%d..%d grid=%lld P_wg=%d hpw=%d n_hsub=%d s0=%d qpos0=%d w0=%lld\n",
+      fprintf(stderr, "[bifocal] prefill %s dtype=%d seqs=%d..%d grid=%lld P_wg=%d hpw=%d n_hsub=%d s0=%d qpos0=%d w0=%lld key_splits=%d\n",
               band_only ? "band-only" : bifocal ? "bifocal" : "plain", dtype, b0, b0 + nb - 1, grid, geo.P_wg, geo.hpw,
-              geo.n_hsub, st.s[0], st.qpos[0], j.w0);
+              geo.n_hsub, st.s[0], st.qpos[0], j.w0, pp.nks);
     e = bf::launch_prefill_main(dtype, bifocal && any_far, band_only && any_far, pp, st, (int)grid, j.stream);
     if (e != hipSuccess) return fail(BF_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
+    if (pp.nks > 1) {
+      e = bf::launch_chunk_combine(pp, st.cu[0], st.cu[nb] - st.cu[0], j.stream);
+      if (e != hipSuccess) return fail(BF_ERR_HIP, "chunk combine launch: %s", hipGetErrorString(e));
+    }
   }
   g_err.clear();
   return BF_OK;
@@ -422,6 +482,7 @@ int run_chunk(const void* q, const void* kc, const void* vc, void* o, float* lse
   j.batch = batch; j.Hq = Hq; j.Hkv = Hkv; j.dtype = dtype;
   j.w0 = w0; j.w_pre = w_pre; j.theta = theta; j.mode = mode; j.scale = scale;
   j.ws = ws; j.ws_bytes = ws_bytes; j.stream = stream;
+  j.split_cap = chunk_split_cap(j.cu[batch], Hq, Hkv, dtype);
   return run_rows(j);
 }
 
@@ -541,7 +602,8 @@ size_t bifocal_chunk_workspace_bytes(int32_t batch, int64_t q_tokens, int64_t kv
       head_dim != bf::kHeadDim)
     return 0;
   if (dtype != BF_DTYPE_BF16 && dtype != BF_DTYPE_FP32) return 0;
-  return prefill_ws_layout(batch, q_tokens, kv_tokens, n_heads_q, n_heads_kv, dtype, paged != 0).total;
+  return prefill_ws_layout(batch, q_tokens, kv_tokens, n_heads_q, n_heads_kv, dtype, paged != 0,
+                           chunk_split_cap(q_tokens, n_heads_q, n_heads_kv, dtype)).total;
 }
 
 int bifocal_prefill_chunk(const void* q, const void* k_cache, const void* v_cache, void* o,

@@ -262,7 +262,7 @@ __global__ __launch_bounds__(128) void vt_transpose_bf16_kernel(VtParams p, SeqT
 // Rows index the packed queries of the sequence (0 .. L - 1); the query of
 // row r sits at position qp + r and sees keys 0 .. qp + r.
 struct Item {
-  int kvh, hq, b, tok0, L, qp, R0, r0, nkt;
+  int kvh, hq, b, tok0, L, qp, R0, r0, nkt, split;
   long long w0;
 };
 
@@ -274,7 +274,11 @@ __device__ __forceinline__ Item make_item(const PrefillParams& p, const SeqTable
   it.kvh = id % p.Hkv;
   const int r1 = id / p.Hkv;
   const int hsub = r1 % p.n_hsub;
-  const int rank = r1 / p.n_hsub;
+  const int r2 = r1 / p.n_hsub;
+  // key split in the high bits: the workgroups in flight together then share
+  // one key range
+  it.split = r2 / p.total_items;
+  const int rank = r2 - it.split * p.total_items;
   int rb;
   decode_item(st, rank, it.b, rb);
   it.tok0 = st.cu[it.b];
@@ -841,24 +845,57 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillParams p, S
   // R0 .. R0 + P_wg - 1
   const long long R0 = (long long)it.qp + it.R0, Rl = R0 + p.P_wg - 1;
   const long long w0 = it.w0;
-  if (BIFOCAL && !BAND && Rl - w0 >= 0) {  // far pairs exist: keys j <= Rl - w0
-    const int kte = min(it.nkt, (int)((Rl - w0) / kKeyTile) + 1);
+  // far pass over tiles [0, far_end) (far pairs exist: keys j <= Rl - w0),
+  // local pass over [loc_b, nkt) (local pairs: keys j > R0 - w0)
+  const int far_end = (BIFOCAL && !BAND && Rl - w0 >= 0)
+                          ? min(it.nkt, (int)((Rl - w0) / kKeyTile) + 1) : 0;
+  int loc_b = it.nkt;
+  if (w0 > 0) {
+    const long long first = R0 - w0 + 1;  // smallest key with a local pair
+    loc_b = first <= 0 ? 0 : (int)min((long long)it.nkt, first / kKeyTile);
+  }
+  // key split: part `split` of the nks takes visits [v0, v1) of the sequence
+  // far tiles, then local tiles
+  int far_b = 0, far_e = far_end, loc_e = it.nkt;
+  if (p.nks > 1) {
+    const int nv = far_end + (it.nkt - loc_b);
+    const int v0 = (int)((long long)nv * it.split / p.nks);
+    const int v1 = (int)((long long)nv * (it.split + 1) / p.nks);
+    far_b = min(v0, far_end);
+    far_e = min(v1, far_end);
+    const int lb = loc_b + max(v0 - far_end, 0);
+    loc_e = loc_b + max(v1 - far_end, 0);
+    loc_b = lb;
+  }
+  if (far_b < far_e)
     run_pass<true>((const uint16_t*)p.q2 + ((size_t)it.hq * p.T + it.tok0) * kHeadDim,
                    (const uint16_t*)p.k2 + ((size_t)it.kvh * p.Tk + st.kcu[it.b]) * kHeadDim, vt0,
-                   k2_end, vt_end, 0, kte, wr, p.scale_log2, wave, lane, sK, sV, rs, oacc);
-  }
-  if (w0 > 0) {  // local pairs exist: keys j > R0 - w0 (and j <= Rl)
-    const long long first = R0 - w0 + 1;  // smallest key with a local pair
-    const int ktb = first <= 0 ? 0 : (int)(first / kKeyTile);
-    if (ktb < it.nkt)
-      run_pass<false>(qg, kg, vt0, k_end, vt_end, ktb, it.nkt, wr, p.scale_log2, wave, lane, sK, sV,
-                      rs, oacc);
-  }
+                   k2_end, vt_end, far_b, far_e, wr, p.scale_log2, wave, lane, sK, sV, rs, oacc);
+  if (loc_b < loc_e)
+    run_pass<false>(qg, kg, vt0, k_end, vt_end, loc_b, loc_e, wr, p.scale_log2, wave, lane, sK, sV,
+                    rs, oacc);
 
-  // epilogue: normalise, store O (bf16) and lse
+  // epilogue: normalise, store O (bf16) and lse, or a key split's partial
   const int row = it.r0 + li;
   const float l = rs.l_part + __shfl_xor(rs.l_part, 32);
   if (row >= it.L) return;
+  if (p.nks > 1) {
+    // a split may hold no key of a row: O = 0 and lse = -inf then weigh
+    // nothing in the merge
+    const size_t prow = ((size_t)it.split * p.Hq + it.hq) * p.T + it.tok0 + row;
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    float* po = p.part_o + prow * kHeadDim;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = 32 * db + 8 * g + 4 * hl;
+        *(float4*)(po + d) = make_float4(oacc[db][4 * g + 0] * inv, oacc[db][4 * g + 1] * inv,
+                                         oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
+      }
+    if (hl == 0) p.part_lse[prow] = l > 0.f ? rs.m_used + __log2f(l) : -INFINITY;
+    return;
+  }
   uint16_t* og = (uint16_t*)p.o + ((size_t)it.hq * p.T + it.tok0) * kHeadDim;
   const float inv = 1.f / l;
 #pragma unroll
@@ -1111,6 +1148,57 @@ hipError_t launch_vt_transpose(int dtype, const VtParams& vp, const SeqTable& st
     hipLaunchKernelGGL(vt_transpose_bf16_kernel, grid, dim3(128), 0, stream, vp, st);
   else
     hipLaunchKernelGGL(vt_transpose_f32_kernel, grid, dim3(256), 0, stream, vp, st);
+  return hipGetLastError();
+}
+
+// Merge of the key splits of a chunk launch: one thread per (query head,
+// row, 8 head dims) weighs the parts' normalised O by 2^(lse_s - max lse) and
+// writes bf16 O (and lse, natural log) like the unsplit kernel.
+__global__ __launch_bounds__(256) void chunk_combine_kernel(PrefillParams p, int tok_begin,
+                                                            int n_tok) {
+  const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
+  const int g = (int)(gid & 15);  // head dims 8 g .. 8 g + 7
+  const long long hr = gid >> 4;
+  if (hr >= (long long)p.Hq * n_tok) return;
+  const int h = (int)(hr / n_tok);
+  const int tok = tok_begin + (int)(hr - (long long)h * n_tok);
+  const size_t plane = (size_t)p.Hq * p.T;  // rows per split
+  const size_t r = (size_t)h * p.T + tok;
+  float lse[kMaxKeySplits];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < kMaxKeySplits; ++s) {
+    lse[s] = s < p.nks ? p.part_lse[s * plane + r] : -INFINITY;
+    mx = fmaxf(mx, lse[s]);
+  }
+  const float mb = mx == -INFINITY ? 0.f : mx;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float wsum = 0.f;
+#pragma unroll
+  for (int s = 0; s < kMaxKeySplits; ++s) {
+    if (s < p.nks) {
+      const float w = __builtin_amdgcn_exp2f(lse[s] - mb);  // 0 for a split without keys
+      const float* po = p.part_o + (s * plane + r) * kHeadDim + 8 * g;
+      const float4 a = *(const float4*)po, b = *(const float4*)(po + 4);
+      acc[0] += w * a.x; acc[1] += w * a.y; acc[2] += w * a.z; acc[3] += w * a.w;
+      acc[4] += w * b.x; acc[5] += w * b.y; acc[6] += w * b.z; acc[7] += w * b.w;
+      wsum += w;
+    }
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  uint32_t wd[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    wd[e] = (uint32_t)f32_to_bf16(acc[2 * e] * inv) | ((uint32_t)f32_to_bf16(acc[2 * e + 1] * inv) << 16);
+  *(uint4*)((uint16_t*)p.o + r * kHeadDim + 8 * g) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+  if (p.lse && g == 0) p.lse[r] = (mb + __log2f(wsum)) * 0.69314718055994530942f;
+}
+
+hipError_t launch_chunk_combine(const PrefillParams& pp, int tok_begin, int n_tok,
+                                hipStream_t stream) {
+  const long long threads = (long long)pp.Hq * n_tok * 16;
+  const int grid = (int)((threads + 255) / 256);
+  hipLaunchKernelGGL(chunk_combine_kernel, dim3(grid), dim3(256), 0, stream, pp, tok_begin, n_tok);
   return hipGetLastError();
 }
 

@@ -6,9 +6,13 @@ sequence is bitwise the one-shot bifocal_prefill (same engine, same work
 split); chunk by chunk with s_len = the prompt length reproduces the one-shot
 prefill. bifocal_prefill_chunk_paged (shuffled page pools of 1 to 256 keys per
 page, junk in unused table entries) must be bitwise the contiguous call.
+Short chunks against long caches split each work item's key tiles into
+parts merged by their log-sum-exp; those launches are checked against the
+oracle too, and the trace confirms that they split.
 Needs an MI355X.
 """
 import math
+import re
 
 import numpy as np
 import pytest
@@ -267,3 +271,90 @@ def test_paged_chunk_4k_at_128k():
                                   "fi", scale)
     torch.cuda.synchronize()
     assert torch.equal(o_p, o_c)
+
+
+def _key_splits(capfd):
+    return [int(x) for x in re.findall(r"key_splits=(\d+)", capfd.readouterr().err)]
+
+
+@pytest.mark.parametrize("mode", ["fi", "pa", "pa+shift", "fi+shift", "band"])
+def test_short_chunks_split_keys_match_oracle(mode, capfd, monkeypatch):
+    # three short chunks against caches of 9K-20K keys: 16 work items, so the
+    # launch splits each item's key tiles and merges the parts
+    monkeypatch.setenv("BIFOCAL_TRACE", "1")
+    Ns, Lqs = [20000, 9000, 12345], [64, 33, 100]
+    Hq, Hkv, cap = 8, 2, 20000
+    w0, w_pre = (6000 if mode == "band" else 1024), 4096  # s = 5, 3, 4
+    cu = wl.cu_seqlens(Lqs)
+    q, kc, vc = chunk_inputs(Ns, Lqs, Hq, Hkv, cap, "bf16", 111)
+    scale = 1 / math.sqrt(128)
+    o, lse = bfl.prefill_chunk(q.cuda(), kc.cuda(), vc.cuda(), cu, Ns, w0, w_pre, THETA, mode,
+                               scale, return_lse=True)
+    torch.cuda.synchronize()
+    ks = _key_splits(capfd)
+    print(f"[split chunk {mode}] key splits {ks}", flush=True)
+    assert ks and max(ks) > 1
+    qf, kf, vf = q.float().numpy(), kc.float().numpy(), vc.float().numpy()
+    o_ref, lse_ref = oracle.chunk(qf, kf, vf, cu, Ns, w0, w_pre, THETA, mode, scale)
+    og = o.float().cpu().numpy()
+    _check(og, o_ref, f"split chunk {mode}")
+    _check(lse.cpu().numpy(), lse_ref, f"split chunk lse {mode}")
+    # the merge must not hide a wrong branch: the error is small next to the
+    # gap to plain causal attention over the same keys
+    plain, _ = oracle.chunk(qf, kf, vf, cu, Ns, 10**9, w_pre, THETA, "fi", scale)
+    err, gap = np.linalg.norm(og - o_ref), np.linalg.norm(o_ref - plain)
+    print(f"[split chunk {mode} discrimination] err {err:.3e} gap-plain {gap:.3e}", flush=True)
+    assert err <= 0.05 * gap
+
+
+def test_split_chunk_is_deterministic_and_paged_equal(capfd, monkeypatch):
+    monkeypatch.setenv("BIFOCAL_TRACE", "1")
+    Ns, Lqs = [30000, 17000], [128, 40]
+    Hq, Hkv, cap = 16, 4, 30000
+    cu = wl.cu_seqlens(Lqs)
+    q, kc, vc = chunk_inputs(Ns, Lqs, Hq, Hkv, cap, "bf16", 112)
+    q, kc, vc = q.cuda(), kc.cuda(), vc.cuda()
+    args = (cu, Ns, 2048, 8192, THETA, "pa+shift", 0.088)
+    a, la = bfl.prefill_chunk(q, kc, vc, *args, return_lse=True)
+    b, lb = bfl.prefill_chunk(q, kc, vc, *args, return_lse=True)
+    kp, vp, table = paginate(kc, vc, Ns, 16, seed=113)
+    c, lc = bfl.prefill_chunk_paged(q, kp, vp, table, *args, return_lse=True)
+    torch.cuda.synchronize()
+    ks = _key_splits(capfd)
+    assert ks and min(ks) > 1, ks
+    assert torch.equal(a, b) and torch.equal(la, lb)
+    assert torch.equal(c, a) and torch.equal(lc, la)
+
+
+@pytest.mark.parametrize("mode", ["fi", "pa"])
+def test_chunk_512_at_128k_split_sampled(mode, capfd, monkeypatch):
+    # the last 512 queries of a 131072-token sequence (Qwen3-8B shape, s = 4):
+    # 128 work items, split four ways
+    monkeypatch.setenv("BIFOCAL_TRACE", "1")
+    c = wl.CONFIGS["qwen3_8b_prefill_128k"]
+    N, Lq = c["lens"][0], 512
+    Hq, Hkv = c["Hq"], c["Hkv"]
+    q, kc, vc = chunk_inputs([N], [Lq], Hq, Hkv, N, "bf16", 114)
+    scale = 1 / math.sqrt(128)
+    o = bfl.prefill_chunk(q.cuda(), kc.cuda(), vc.cuda(), [0, Lq], [N], c["w0"], c["w_pre"],
+                          c["theta"], mode, scale)
+    torch.cuda.synchronize()
+    ks = _key_splits(capfd)
+    print(f"[chunk 512 at 128k {mode}] key splits {ks}", flush=True)
+    assert ks and max(ks) > 1
+    rows = wl.sample_rows(Lq, 16, [0, 1, 31, 32, 510, 511], seed=115)
+    qs, kf, vf = q[:, rows].float().numpy(), kc.float().numpy(), vc.float().numpy()
+    o_ref, _ = oracle.chunk(qs, kf, vf, [0, Lq], [N], c["w0"], c["w_pre"], c["theta"], mode, scale,
+                            rows=rows, gathered=True)
+    og = o[:, torch.from_numpy(np.asarray(rows)).cuda()].float().cpu().numpy()
+    _check(og, o_ref, f"chunk 512 at 128k {mode}")
+    err = np.linalg.norm(og - o_ref)
+    plain, _ = oracle.chunk(qs, kf, vf, [0, Lq], [N], 10**9, c["w_pre"], c["theta"], mode, scale,
+                            rows=rows, gathered=True)
+    other, _ = oracle.chunk(qs, kf, vf, [0, Lq], [N], c["w0"], c["w_pre"], c["theta"],
+                            "pa" if mode == "fi" else "fi", scale, rows=rows, gathered=True)
+    gap_plain, gap_mode = np.linalg.norm(o_ref - plain), np.linalg.norm(o_ref - other)
+    print(f"[chunk 512 discrimination {mode}] err {err:.3e} gap-plain {gap_plain:.3e} "
+          f"gap-other-mode {gap_mode:.3e}", flush=True)
+    assert err <= 0.05 * gap_plain
+    assert err <= 0.25 * gap_mode
