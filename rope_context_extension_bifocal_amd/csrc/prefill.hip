@@ -41,10 +41,6 @@ typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;  // 8 packed bf1
 typedef __attribute__((ext_vector_type(4))) unsigned int du32x4;
 
 // ----------------------------------------------------------------- helpers
-__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
-  return __uint_as_float((uint32_t)h << 16);
-}
-
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {  // round to nearest even
   return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
@@ -91,21 +87,49 @@ __device__ __forceinline__ void decode_item(const SeqTable& st, int rank, int& b
 }
 
 // ----------------------------------------------------------------- prep
-// One thread per (token, rotary pair m); 4 tokens per 256-lane group;
-// blockIdx.y = 0 rotates the queries (positions qpos[b] + row), 1 the keys
-// (positions 0 .. N_b - 1, read from the K layout, written packed). The angle
-// is formed in fp64 from an exact integer numerator, so it stays accurate at
-// 128K positions (theta_0 * p ~ 1e5 rad), and is applied in fp32.
+// One thread per (token, group of E = 16 / sizeof(T) rotary pairs): it forms
+// the E angles once and applies them to the token's row in every head,
+// reading and writing 16 bytes of each half of the row (pairs m0 .. m0 + E - 1
+// and m0 + 64 ..). blockIdx.y = 0 rotates the queries (positions qpos[b] +
+// row), 1 the keys (positions 0 .. N_b - 1, read from the K layout, written
+// packed). The angle is formed in fp64 from an exact integer numerator, so it
+// stays accurate at 128K positions (theta_0 * p ~ 1e5 rad), and is applied in
+// fp32.
 template <typename T>
-__device__ __forceinline__ float ld_elem(const T* p) {
-  if constexpr (sizeof(T) == 2) return bf16_to_f32(*p);
-  else return *p;
-}
-template <typename T>
-__device__ __forceinline__ void st_elem(T* p, float f) {
-  if constexpr (sizeof(T) == 2) *p = f32_to_bf16(f);
-  else *p = f;
-}
+struct Chunk16 {  // 16 bytes of T as floats
+  static constexpr int E = 16 / (int)sizeof(T);
+  float x[E];
+  __device__ __forceinline__ void load(const T* p) {
+    const uint4 u = *(const uint4*)p;
+    if constexpr (sizeof(T) == 2) {
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[2 * i] = __uint_as_float(w[i] << 16);
+        x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+      }
+    } else {
+      x[0] = __uint_as_float(u.x);
+      x[1] = __uint_as_float(u.y);
+      x[2] = __uint_as_float(u.z);
+      x[3] = __uint_as_float(u.w);
+    }
+  }
+  __device__ __forceinline__ void store(T* p) const {
+    uint4 u;
+    if constexpr (sizeof(T) == 2) {
+      uint32_t w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        w[i] = (uint32_t)f32_to_bf16(x[2 * i]) | ((uint32_t)f32_to_bf16(x[2 * i + 1]) << 16);
+      u = make_uint4(w[0], w[1], w[2], w[3]);
+    } else {
+      u = make_uint4(__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]),
+                     __float_as_uint(x[3]));
+    }
+    *(uint4*)p = u;
+  }
+};
 
 // Row (in elements / kHeadDim) of key j of launch sequence b, KV head h, in a
 // K / V source: the SeqTable layout, or pages through the block table.
@@ -118,33 +142,51 @@ __device__ __forceinline__ long long kv_row(const PagedKV& pk, const SeqTable& s
   return (((long long)pg * Hkv + h) << pk.page_log2) + (j & ((1LL << pk.page_log2) - 1));
 }
 
+// Sequence of packed token tok along offsets cu[0 .. n]: the last b with
+// cu[b] <= tok.
+__device__ __forceinline__ int seq_of_tok(const int* cu, int n, int tok) {
+  int lo = 0, hi = n;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (cu[mid] <= tok) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void correction_prep_kernel(PrepParams p, SeqTable st,
                                                               ThetaTable tt) {
+  constexpr int E = Chunk16<T>::E;   // pairs per thread
+  constexpr int TPR = kPairs / E;    // threads per token
+  constexpr int TOK = 256 / TPR;     // tokens per workgroup
   const bool keys = blockIdx.y == 1;
-  auto cu = [&](int i) { return keys ? st.kcu[i] : st.cu[i]; };
-  const int tok = cu(0) + blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int m = threadIdx.x & 63;
-  if (tok >= cu(st.n)) return;
-  int b = 0;
-  while (b + 1 < st.n && tok >= cu(b + 1)) ++b;
+  const int* cu = keys ? st.kcu : st.cu;
+  const int tok = cu[0] + blockIdx.x * TOK + (int)threadIdx.x / TPR;
+  const int m0 = ((int)threadIdx.x % TPR) * E;
+  if (tok >= cu[st.n]) return;
+  const int b = seq_of_tok(cu, st.n, tok);
   const int s = st.s[b];
   const bool rot = s > 1;         // s = 1: no far branch for this sequence
   const bool copy = keys && p.kcopy != nullptr;  // paged keys: gather the packed copy
   if (!rot && !copy) return;
-  const long long row = tok - cu(b);
+  const long long row = tok - cu[b];
   if (keys && row < (long long)st.vt_t0[b] * kKeyTile) return;  // key no window reaches
-  float c = 1.f, sn = 0.f;
+  float c[E], sn[E];
   if (rot) {
     const long long pos = keys ? row : st.qpos[b] + row;
     long long num = corr_num(pos, s, p.long_mode);
     // queries with the band-edge continuity shift: (w0 - phi(w0)) * s is the
     // exact integer w0 (s - 1) (FI) or (w0 - floor(w0 / s)) s (PA)
     if (!keys && p.shift) num += p.long_mode == 1 ? (p.w0 - p.w0 / s) * s : p.w0 * (s - 1);
-    double sd, cd;
-    sincos(tt.th[m] * ((double)num / (double)s), &sd, &cd);
-    c = (float)cd;
-    sn = (float)sd;
+    const double ratio = (double)num / (double)s;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      double sd, cd;
+      sincos(tt.th[m0 + e] * ratio, &sd, &cd);
+      c[e] = (float)cd;
+      sn[e] = (float)sd;
+    }
   }
   const int nh = keys ? p.Hkv : p.Hq;
   for (int h = 0; h < nh; ++h) {
@@ -153,19 +195,26 @@ __global__ __launch_bounds__(256) void correction_prep_kernel(PrepParams p, SeqT
     if (keys) {
       src = (const T*)p.k + kv_row(p.pk, st, p.k_hstride, p.Hkv, b, h, row) * kHeadDim;
       dst = (T*)p.k2 + ((size_t)h * p.Tk + tok) * kHeadDim;
-      if (copy) {
-        T* cp = (T*)p.kcopy + ((size_t)h * p.Tk + tok) * kHeadDim;
-        cp[m] = src[m];
-        cp[m + kPairs] = src[m + kPairs];
-      }
-      if (!rot) continue;
     } else {
       src = (const T*)p.q + ((size_t)h * p.T + tok) * kHeadDim;
       dst = (T*)p.q2 + ((size_t)h * p.T + tok) * kHeadDim;
     }
-    const float x0 = ld_elem(src + m), x1 = ld_elem(src + m + kPairs);
-    st_elem(dst + m, x0 * c - x1 * sn);
-    st_elem(dst + m + kPairs, x1 * c + x0 * sn);
+    if (copy) {  // 16-byte copies of both halves, unconverted
+      T* cp = (T*)p.kcopy + ((size_t)h * p.Tk + tok) * kHeadDim;
+      *(uint4*)(cp + m0) = *(const uint4*)(src + m0);
+      *(uint4*)(cp + kPairs + m0) = *(const uint4*)(src + kPairs + m0);
+    }
+    if (!rot) continue;
+    Chunk16<T> x0, x1, y0, y1;
+    x0.load(src + m0);
+    x1.load(src + kPairs + m0);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      y0.x[e] = x0.x[e] * c[e] - x1.x[e] * sn[e];
+      y1.x[e] = x1.x[e] * c[e] + x0.x[e] * sn[e];
+    }
+    y0.store(dst + m0);
+    y1.store(dst + kPairs + m0);
   }
 }
 
@@ -1133,7 +1182,8 @@ __global__ void pair_map_kernel(long long L, long long w0, long long s, int mode
 hipError_t launch_correction_prep(int dtype, const PrepParams& pp, const SeqTable& st,
                                   const ThetaTable& tt, hipStream_t stream) {
   const int tq = st.cu[st.n] - st.cu[0], tk = st.kcu[st.n] - st.kcu[0];
-  const dim3 grid((max(tq, tk) + 3) / 4, 2);
+  const int tok_per_wg = 256 / (kPairs / (dtype == 0 ? 8 : 4));
+  const dim3 grid((max(tq, tk) + tok_per_wg - 1) / tok_per_wg, 2);
   if (dtype == 0)
     hipLaunchKernelGGL(correction_prep_kernel<uint16_t>, grid, dim3(256), 0, stream, pp, st, tt);
   else
