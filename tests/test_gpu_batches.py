@@ -5,6 +5,7 @@ Each entry point is compared with the fp64 oracle at the usual bar (bf16
 max-abs 2e-2, mean-abs 2e-3) over the whole batch. Needs an MI355X.
 """
 import math
+import re
 
 import numpy as np
 import pytest
@@ -63,6 +64,28 @@ def test_chunk_100_sequences():
     o_ref, _ = oracle.chunk(q.float().numpy(), kc.float().numpy(), vc.float().numpy(), cu, Ns, 50,
                             64, THETA, "fi", SCALE)
     _check(o.float().cpu().numpy(), o_ref, "chunk 100 seqs")
+
+
+def test_split_chunk_70_sequences(capfd, monkeypatch):
+    # short chunks against 4K-8K-key caches: both launches (64 + 6 sequences)
+    # split their keys, each merging its own token range
+    monkeypatch.setenv("BIFOCAL_TRACE", "1")
+    Ns = _lens(70, 4000, 8000, 217)
+    Lqs = _lens(70, 1, 21, 218)
+    cu = wl.cu_seqlens(Lqs)
+    cap = max(Ns)
+    q, _, _ = wl.prefill_inputs(4, 1, cu[-1], 128, "bf16", 219)
+    _, kc, vc = wl.decode_inputs(len(Ns), 4, 1, cap, 128, "bf16", 220)
+    o, lse = bfl.prefill_chunk(q.cuda(), kc.cuda(), vc.cuda(), cu, Ns, 512, 2048, THETA, "pa",
+                               SCALE, return_lse=True)
+    torch.cuda.synchronize()
+    ks = [int(x) for x in re.findall(r"key_splits=(\d+)", capfd.readouterr().err)]
+    print(f"[split chunk 70 seqs] key splits per launch {ks}", flush=True)
+    assert len(ks) == 2 and min(ks) > 1
+    o_ref, lse_ref = oracle.chunk(q.float().numpy(), kc.float().numpy(), vc.float().numpy(), cu,
+                                  Ns, 512, 2048, THETA, "pa", SCALE)
+    _check(o.float().cpu().numpy(), o_ref, "split chunk 70 seqs")
+    _check(lse.cpu().numpy(), lse_ref, "split chunk 70 seqs lse")
 
 
 @pytest.mark.parametrize("mode", ["fi", "band"])
