@@ -505,18 +505,18 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p, De
 }
 
 // Log-sum-exp merge of the splits. Workgroup = (query head, batch, quarter
-// of the head dims). Every load (the split maxima, row sums and partial rows)
-// is issued up front, so the merge costs one memory round trip: thread t
-// owns float4 d4 = t % 8 of the quarter for splits t / 8 + 32 k, and the
-// split maxima / sums of splits t + 256 k.
+// of the head dims). Thread t owns float4 d4 = t % 8 of the quarter for the
+// splits t / 8 + 32 k: it loads their partial rows, maxima and row sums up
+// front (the first 160 splits; more are read in a loop), so the merge costs
+// one memory round trip plus two barriers: one for the maximum over all
+// splits, one for the sums over the 32 split groups (three lane swaps inside
+// a wave, then four LDS entries).
 constexpr int kDecMaxSplits = 1088;
 constexpr int kCombGroups = 32;  // split groups per workgroup
 constexpr int kCombHold = 5;     // 32 x 5 = 160 splits held in registers
-static_assert(5 * 256 >= kDecMaxSplits, "split maxima are read five per thread");
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p, DecodeSeqs ds) {
-  __shared__ float wgt[kDecMaxSplits];
   __shared__ float red[8];
-  __shared__ float4 part4[kCombGroups][8];
+  __shared__ float4 part4[4][8];  // per-wave sums of the weighted rows
   const int b = blockIdx.y, h = blockIdx.x, dq = blockIdx.z, t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
   const int ns = ds.nsplit[b];
@@ -524,70 +524,64 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p, Dec
   const int d4 = t & 7, grp = t >> 3;
   const int dcol = 32 * dq + 4 * d4;  // first head dim of this thread's float4
   float4 hold[kCombHold];
+  float mi[kCombHold], li[kCombHold];
 #pragma unroll
   for (int k = 0; k < kCombHold; ++k) {
     const int i = grp + kCombGroups * k;
-    const float4 v = *(const float4*)(p.part_acc + (row0 + min(i, ns - 1)) * kHeadDim + dcol);
+    const size_t r = row0 + min(i, ns - 1);
+    const float4 v = *(const float4*)(p.part_acc + r * kHeadDim + dcol);
+    const float m = p.part_m[r], l = p.part_l[r];
     hold[k] = i < ns ? v : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-  // split maxima and row sums of splits t, t + 256, ... (at most kDecMaxSplits)
-  float mi[5], li[5];
-#pragma unroll
-  for (int k = 0; k < 5; ++k) {
-    const int i = t + 256 * k;
-    const int ic = min(i, ns - 1);
-    const float m = p.part_m[row0 + ic], l = p.part_l[row0 + ic];
     mi[k] = i < ns ? m : -INFINITY;
     li[k] = i < ns ? l : 0.f;
   }
   float mloc = fmaxf(fmaxf(fmaxf(mi[0], mi[1]), fmaxf(mi[2], mi[3])), mi[4]);
+  for (int i = grp + kCombGroups * kCombHold; i < ns; i += kCombGroups)
+    mloc = fmaxf(mloc, p.part_m[row0 + i]);
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, o));
+  for (int o = 8; o < 64; o <<= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, o));
   if (lane == 0) red[wave] = mloc;
   __syncthreads();
   const float mt = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const float mbt = (mt == -INFINITY) ? 0.f : mt;
-  float lloc = 0.f;
-#pragma unroll
-  for (int k = 0; k < 5; ++k) {
-    const int i = t + 256 * k;
-    const float w = __builtin_amdgcn_exp2f(mi[k] - mbt);  // 0 for absent splits
-    if (i < ns) wgt[i] = w;
-    lloc += w * li[k];
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) lloc += __shfl_xor(lloc, o);
-  if (lane == 0) red[4 + wave] = lloc;
-  __syncthreads();
-  const float lt = (red[4] + red[5]) + (red[6] + red[7]);
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float lsum = 0.f;
 #pragma unroll
   for (int k = 0; k < kCombHold; ++k) {
-    const int i = grp + kCombGroups * k;
-    const float w = i < ns ? wgt[min(i, ns - 1)] : 0.f;
+    const float w = __builtin_amdgcn_exp2f(mi[k] - mbt);  // 0 for absent splits
     acc.x += w * hold[k].x;
     acc.y += w * hold[k].y;
     acc.z += w * hold[k].z;
     acc.w += w * hold[k].w;
+    lsum += w * li[k];
   }
   for (int i = grp + kCombGroups * kCombHold; i < ns; i += kCombGroups) {
     const float4 v = *(const float4*)(p.part_acc + (row0 + i) * kHeadDim + dcol);
-    const float w = wgt[i];
+    const float w = __builtin_amdgcn_exp2f(p.part_m[row0 + i] - mbt);
     acc.x += w * v.x;
     acc.y += w * v.y;
     acc.z += w * v.z;
     acc.w += w * v.w;
+    lsum += w * p.part_l[row0 + i];
   }
-  part4[grp][d4] = acc;
+  // sums over the split groups: the lanes 8 g + d4 of a wave hold groups
+  // 8 wave + g (every d4 lane carries the same row sum)
+#pragma unroll
+  for (int o = 8; o < 64; o <<= 1) {
+    acc.x += __shfl_xor(acc.x, o);
+    acc.y += __shfl_xor(acc.y, o);
+    acc.z += __shfl_xor(acc.z, o);
+    acc.w += __shfl_xor(acc.w, o);
+    lsum += __shfl_xor(lsum, o);
+  }
+  if (lane < 8) part4[wave][lane] = acc;
+  if (lane == 0) red[4 + wave] = lsum;
   __syncthreads();
   if (t < 8) {
-    float4 a = part4[0][t];
-    for (int g = 1; g < kCombGroups; ++g) {
-      a.x += part4[g][t].x;
-      a.y += part4[g][t].y;
-      a.z += part4[g][t].z;
-      a.w += part4[g][t].w;
-    }
+    const float4 a0 = part4[0][t], a1 = part4[1][t], a2 = part4[2][t], a3 = part4[3][t];
+    const float4 a = make_float4((a0.x + a1.x) + (a2.x + a3.x), (a0.y + a1.y) + (a2.y + a3.y),
+                                 (a0.z + a1.z) + (a2.z + a3.z), (a0.w + a1.w) + (a2.w + a3.w));
+    const float lt = (red[4] + red[5]) + (red[6] + red[7]);
     const float inv = 1.f / lt;
     uint16_t* o = p.o + ((size_t)b * p.Hq + h) * kHeadDim + 32 * dq + 4 * t;
     uint2 w;
