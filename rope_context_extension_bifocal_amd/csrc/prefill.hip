@@ -75,15 +75,18 @@ __device__ __forceinline__ int key_of_acc(int r, int hl) {  // key of acc regist
 // sequence, over its row blocks last (heaviest) first. The workgroups that
 // run at the same time then mostly share one sequence's keys, which the XCD's
 // L2 serves, and the lightest items come last.
+// The lookup is wave-parallel: lane i loads ioff[i + 1], ioff[i] and
+// order[i] (one memory round trip), a ballot counts the sequences that start
+// at or below the rank, and that count selects the entries by lane reads.
+// (A search would chain one load per step at the start of every workgroup.)
 __device__ __forceinline__ void decode_item(const SeqTable& st, int rank, int& b, int& rb) {
-  int lo = 0, hi = st.n;  // the last i with ioff[i] <= rank (that sequence has items)
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (st.ioff[mid] <= rank) lo = mid;
-    else hi = mid;
-  }
-  b = st.order[lo];
-  rb = st.nrb[b] - 1 - (rank - st.ioff[lo]);
+  static_assert(kMaxSeqPerLaunch == 64, "one table entry per lane");
+  const int lane = threadIdx.x & 63;
+  const int next = st.ioff[lane + 1];  // start of sequence lane + 1 in the order
+  const int own = st.ioff[lane], ord = st.order[lane];
+  const int pos = __popcll(__ballot(lane + 1 < st.n && next <= rank));
+  b = __builtin_amdgcn_readlane(ord, pos);
+  rb = st.nrb[b] - 1 - (rank - __builtin_amdgcn_readlane(own, pos));
 }
 
 // ----------------------------------------------------------------- prep
