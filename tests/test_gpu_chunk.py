@@ -358,3 +358,31 @@ def test_chunk_512_at_128k_split_sampled(mode, capfd, monkeypatch):
           f"gap-other-mode {gap_mode:.3e}", flush=True)
     assert err <= 0.05 * gap_plain
     assert err <= 0.25 * gap_mode
+
+
+def test_chunk_workspace_without_partials_runs_unsplit(capfd, monkeypatch):
+    # the partials take 516 bytes per (split, query head, query token) at the
+    # end of the workspace; a workspace short of all 8 splits' partials holds
+    # the base layout but no split, so the call must run unsplit
+    monkeypatch.setenv("BIFOCAL_TRACE", "1")
+    Ns, Lqs = [20000, 9000, 12345], [64, 33, 100]
+    Hq, Hkv, cap = 8, 2, 20000
+    cu = wl.cu_seqlens(Lqs)
+    q, kc, vc = chunk_inputs(Ns, Lqs, Hq, Hkv, cap, "bf16", 116)
+    q, kc, vc = q.cuda(), kc.cuda(), vc.cuda()
+    scale = 1 / math.sqrt(128)
+    full = bfl.chunk_workspace_bytes(len(Ns), cu[-1], sum(Ns), Hq, Hkv)
+    small = full - 8 * Hq * cu[-1] * 516
+    outs = []
+    for nbytes in (full, small):
+        ws = bfl.alloc_workspace(nbytes, "cuda")
+        outs.append(bfl.prefill_chunk(q, kc, vc, cu, Ns, 1024, 4096, THETA, "fi", scale,
+                                      workspace=ws))
+    torch.cuda.synchronize()
+    ks = _key_splits(capfd)
+    print(f"[chunk workspace] key splits with the full / the small workspace: {ks}", flush=True)
+    assert len(ks) == 2 and ks[0] > 1 and ks[1] == 1
+    o_ref, _ = oracle.chunk(q.float().cpu().numpy(), kc.float().cpu().numpy(),
+                            vc.float().cpu().numpy(), cu, Ns, 1024, 4096, THETA, "fi", scale)
+    for o, what in zip(outs, ("split", "unsplit")):
+        _check(o.float().cpu().numpy(), o_ref, f"chunk workspace {what}")
