@@ -190,7 +190,8 @@ int bifocal_prefill_chunk(const void* q, const void* k_cache, const void* v_cach
  *   workspace        : bifocal_chunk_workspace_bytes(..., paged = 1)
  * The keys are gathered once per call into a packed copy in the workspace,
  * so the result is bitwise that of bifocal_prefill_chunk on a contiguous
- * cache holding the same keys.
+ * cache holding the same keys (each call given the workspace size its
+ * bifocal_chunk_workspace_bytes returns, so that both split the same way).
  */
 int bifocal_prefill_chunk_paged(const void* q, const void* k_pages, const void* v_pages, void* o,
                                 float* lse, const int32_t* block_table, const int32_t* cu_q_host,
