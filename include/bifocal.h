@@ -62,8 +62,11 @@ extern "C" {
 #define BF_LONG_FI 0 /* frequency interpolation: phi(p) = p / s */
 #define BF_LONG_PA 1 /* position aliasing:       phi(p) = floor(p / s) */
 #define BF_LONG_SHIFT 4 /* flag, OR-ed into BF_LONG_FI / BF_LONG_PA: band-edge continuity
-                           shift. The far query sits at phi(p) + w0 - phi(w0), so a far pair
-                           at distance exactly w0 sees relative position w0 as the band does
+                           shift. The far query sits at phi(p) + w0 - phi(w0) (keys stay at
+                           phi(j)). A far pair at distance exactly w0 then sees relative
+                           position w0, as the band does one step closer: for FI always,
+                           for PA when s divides w0 or the key is at position 0 (otherwise
+                           floor(i/s) - floor((i-w0)/s) may differ from floor(w0/s) by one)
                            [seventnews.com (FR), fusion paragraph: the correction re-aligns
                            the phases of the two branches]. Off by default. */
 #define BF_LONG_NONE 2 /* band only: far pairs are dropped, i.e. sliding-window attention

@@ -193,9 +193,10 @@ def _s1_inputs(L, D, theta, amp, mstars):
     return q, k, v
 
 
-def _s1_expected(L, D, theta, amp, mstars, w0, s, mode, scale, v):
+def _s1_expected(L, D, theta, amp, mstars, w0, s, mode, scale, v, delta=0.0):
     """Closed form: score(i, j) = scale * a_q * a_k * cos(theta_m* * dpos) with
-    dpos = i - j for local pairs and phi(i) - phi(j) for far pairs."""
+    dpos = i - j for local pairs and phi(i) + delta - phi(j) for far pairs
+    (delta: a constant far-query offset, 0 without the continuity shift)."""
     phi = (lambda p: p / s) if mode == "fi" else (lambda p: np.floor(p / s))
     Hkv = len(mstars)
     o = np.zeros((2 * Hkv, L, D))
@@ -205,7 +206,7 @@ def _s1_expected(L, D, theta, amp, mstars, w0, s, mode, scale, v):
             a_q = amp * (1.0 if hh == 0 else 0.5)
             for i in range(L):
                 j = np.arange(i + 1)
-                dpos = np.where(i - j < w0, i - j, phi(i) - phi(j))
+                dpos = np.where(i - j < w0, i - j, phi(i) + delta - phi(j))
                 sc = scale * a_q * amp * np.cos(th * dpos)
                 w = np.exp(sc - sc.max())
                 o[2 * g + hh, i] = (w[:, None] * v[g, : i + 1]).sum(0) / w.sum()
@@ -233,6 +234,31 @@ def test_structured_input_closed_form(mode):
     off_by_one = _s1_expected(L, D, theta, amp, mstars, w0 + 1, 4, mode, scale, v)
     wrong_s = _s1_expected(L, D, theta, amp, mstars, w0, 3, mode, scale, v)
     for alt in (other, plain, off_by_one, wrong_s):
+        assert np.abs(o - alt).max() > 1e-2
+
+
+@pytest.mark.parametrize("mode", ["fi", "pa"])
+def test_structured_input_closed_form_with_shift(mode):
+    # the continuity shift moves every far query by the constant
+    # delta = w0 - phi(w0): FI w0 (s - 1) / s, PA w0 - floor(w0 / s). With
+    # w0 = 9 and s = 4 these are 6.75 and 7, so the closed form below fails
+    # for a shift computed with the other mode's phi, for no shift and for the
+    # unshifted other mode.
+    L, D, theta, w0, w_pre = 64, 128, 1e4, 9, 16       # s = 4
+    scale = 1 / math.sqrt(D)
+    amp = math.sqrt(8 / scale)
+    mstars = [1, 9]
+    q, k, v = _s1_inputs(L, D, theta, amp, mstars)
+    o, _ = oracle.prefill(q, k, v, [0, L], w0=w0, w_pre=w_pre, theta=theta, mode=mode + "+shift",
+                          scale=scale)
+    delta = {"fi": w0 - w0 / 4, "pa": w0 - w0 // 4}
+    exp_mode = _s1_expected(L, D, theta, amp, mstars, w0, 4, mode, scale, v, delta[mode])
+    np.testing.assert_allclose(o, exp_mode, atol=1e-5, rtol=0)
+    other = "pa" if mode == "fi" else "fi"
+    wrong_delta = _s1_expected(L, D, theta, amp, mstars, w0, 4, mode, scale, v, delta[other])
+    unshifted = _s1_expected(L, D, theta, amp, mstars, w0, 4, mode, scale, v)
+    other_shifted = _s1_expected(L, D, theta, amp, mstars, w0, 4, other, scale, v, delta[other])
+    for alt in (wrong_delta, unshifted, other_shifted):
         assert np.abs(o - alt).max() > 1e-2
 
 
@@ -409,14 +435,17 @@ def test_band_only_decode_is_last_row():
 
 # ---------------------------------------------------------------- band-edge continuity shift
 @pytest.mark.parametrize("mode", ["fi", "pa"])
-def test_shift_makes_the_window_edge_continuous(mode):
+@pytest.mark.parametrize("w0", [24, 25, 26])
+def test_shift_makes_the_window_edge_continuous(mode, w0):
     # row i = w0 has exactly one far pair, j = 0, at distance w0. With the
     # shift its relative position is w0 again (FI: w0/s + w0 - w0/s; PA:
     # floor(w0/s) + w0 - floor(w0/s)), so the row equals plain causal
     # attention on the original-RoPE inputs (library SDPA, fp64); without the
-    # shift it does not.
+    # shift it does not. w0 = 25 and 26 are not multiples of s = 3, so there
+    # the FI and PA offsets differ (16.67 against 17, 17.33 against 18) and a
+    # PA branch that took FI's offset fails.
     rng = np.random.default_rng(51)
-    Hq, Hkv, L, D, w0, w_pre = 2, 1, 60, 128, 24, 20  # s = 3
+    Hq, Hkv, L, D, w_pre = 2, 1, 60, 128, 20  # s = 3
     q = rng.standard_normal((Hq, L, D)).astype(np.float32)
     k = rng.standard_normal((Hkv, L, D)).astype(np.float32)
     v = rng.standard_normal((Hkv, L, D)).astype(np.float32)
@@ -529,11 +558,13 @@ def test_chunk_batch_is_independent_per_sequence():
     np.testing.assert_array_equal(sub, o[:, rows])
 
 
-def test_chunk_shift_makes_the_window_edge_continuous():
+@pytest.mark.parametrize("mode,w0", [("fi", 24), ("pa", 25), ("fi", 26), ("pa", 26)])
+def test_chunk_shift_makes_the_window_edge_continuous(mode, w0):
     # the query at position w0 (the last of N = w0 + 1 keys) with the shift
     # equals plain causal attention (library SDPA); cf. the prefill pin above
+    # (s = s(60) = 3 from s_len, so w0 = 25 and 26 are not multiples of s)
     rng = np.random.default_rng(83)
-    Hq, Hkv, D, w0, w_pre = 2, 1, 128, 24, 20
+    Hq, Hkv, D, w_pre = 2, 1, 128, 20
     N = w0 + 1
     q = rng.standard_normal((Hq, N, D)).astype(np.float32)
     k = rng.standard_normal((Hkv, N, D)).astype(np.float32)
@@ -541,5 +572,27 @@ def test_chunk_shift_makes_the_window_edge_continuous():
     scale = 1 / math.sqrt(D)
     ref = _sdpa_band(q, k, v, N + 1, scale)[:, N - 3:]
     o, _ = oracle.chunk(q[:, N - 3:], _as_cache(k, N, 0.0), _as_cache(v, N, 0.0), [0, 3], [N], w0,
-                        w_pre, 1e4, "fi+shift", scale, s_len=[60])
+                        w_pre, 1e4, mode + "+shift", scale, s_len=[60])
     np.testing.assert_allclose(o, ref, atol=1e-11)
+
+
+# ---------------------------------------------------------------- input S2 separates the modes
+def test_s2_input_separates_the_long_modes():
+    # the input the GPU mode-discrimination tests use: on rows at an aliasing
+    # group's first position the oracle's FI and PA results differ by at least
+    # half of their distance to plain attention, in prefill and in decode, so
+    # a kernel computing the wrong mode fails a 0.05 bar by a factor of 10
+    from structured import s2_inputs
+    L, theta, w_pre, w0, sc = 8192, 1e4, 3000, 256, 1 / math.sqrt(128)
+    q, k, v = (x.float().numpy() for x in s2_inputs(L, theta))
+    rows = np.arange(2049, L, 3)[::40]
+    r = {m: oracle.prefill(q, k, v, [0, L], w0, w_pre, theta, m, sc, rows=rows)[0] for m in ("fi", "pa")}
+    plain = oracle.prefill(q, k, v, [0, L], 10**9, w_pre, theta, "fi", sc, rows=rows)[0]
+    N = L - 1
+    d = {m: oracle.decode(q[:, N - 1][None], k[None, :, :N], v[None, :, :N], [N], w0, w_pre, theta,
+                          m, sc)[0] for m in ("fi", "pa")}
+    dplain = oracle.decode(q[:, N - 1][None], k[None, :, :N], v[None, :, :N], [N], 10**9, w_pre,
+                           theta, "fi", sc)[0]
+    for a, b in (("fi", "pa"), ("pa", "fi")):
+        assert np.linalg.norm(r[a] - r[b]) >= 0.5 * np.linalg.norm(r[a] - plain)
+        assert np.linalg.norm(d[a] - d[b]) >= 0.5 * np.linalg.norm(d[a] - dplain)
