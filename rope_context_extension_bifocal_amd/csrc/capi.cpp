@@ -269,11 +269,23 @@ int run_rows(RowsJob& j) {
   const int Tpad = vt_off[batch];
   const bf::ThetaTable tt = theta_table(bifocal ? j.theta : 10000.0);
   char* wsb = (char*)j.ws;
-  if (forced_launch_failure()) return fail(BF_ERR_HIP, "launch failure forced by BIFOCAL_TEST_FAIL_LAUNCH");
 
+  // Plan every launch group (at most kMaxSeqPerLaunch sequences each) before
+  // the first launch, so that an argument a later group rejects leaves
+  // nothing enqueued and the outputs untouched.
+  struct Group {
+    bf::SeqTable st;
+    bf::PrefillParams pp;
+    bf::PagedKV pk;
+    bool any_far;
+    long long grid;
+  };
+  std::vector<Group> groups;
   for (int b0 = 0; b0 < batch; b0 += bf::kMaxSeqPerLaunch) {
     const int nb = std::min(bf::kMaxSeqPerLaunch, batch - b0);
-    bf::SeqTable st;
+    groups.emplace_back();
+    Group& gr = groups.back();
+    bf::SeqTable& st = gr.st;
     std::memset(&st, 0, sizeof st);
     st.n = nb;
     bool any_far = false;
@@ -289,7 +301,8 @@ int run_rows(RowsJob& j) {
       const long long Lq = j.cu[b0 + i + 1] - j.cu[b0 + i];
       const long long N = j.qpos[b0 + i] + Lq;
       const long long s = bifocal && !band_only ? bifocal_s_of_L(j.slen[b0 + i], j.w_pre) : 1;
-      if (s < 1 || s > (1LL << 30)) return fail(BF_ERR_INVALID_ARG, "s(L) out of range");
+      if (s < 1 || s > (1LL << 30))
+        return fail(BF_ERR_INVALID_ARG, "s(L) of sequence %d is %lld, outside [1, 2^30]", b0 + i, s);
       st.s[i] = (int)s;
       st.qpos[i] = j.qpos[b0 + i];
       // a paged source is gathered into the packed copy, which the tile
@@ -305,26 +318,16 @@ int run_rows(RowsJob& j) {
       visit_sum += (double)st.nrb[i] * (double)((span + bf::kKeyTile - 1) / bf::kKeyTile);
       work[i] = scored_pairs(j.qpos[b0 + i], Lq, band_only ? j.w0 : -1);
     }
+    gr.any_far = any_far;
     // work order: sequences with the most scored pairs first (ties in batch
     // order), each one's row blocks as one run of ranks
     std::iota(st.order, st.order + nb, 0);
     std::stable_sort(st.order, st.order + nb, [&](int a, int b) { return work[a] > work[b]; });
     st.ioff[0] = 0;
     for (int i = 0; i < nb; ++i) st.ioff[i + 1] = st.ioff[i] + st.nrb[st.order[i]];
-    hipError_t e = hipSuccess;
-    bf::PagedKV pk = j.pk;  // the block-table rows of this launch's sequences
-    if (paged) pk.block_table += (size_t)b0 * pk.max_pages;
-    bf::VtParams vp{j.v, wsb + wl.vt_off, pk, j.k_hstride, Tpad, Hkv};
-    e = bf::launch_vt_transpose(dtype, vp, st, j.stream);
-    if (e != hipSuccess) return fail(BF_ERR_HIP, "vt_transpose launch: %s", hipGetErrorString(e));
-    if ((bifocal && any_far && !band_only) || paged) {
-      // band-only or s = 1 sequences get no rotation: the prep only gathers
-      bf::PrepParams pp{j.q, j.k, wsb + wl.q2_off, wsb + wl.k2_off, paged ? wsb + wl.kc_off : nullptr, pk,
-                        j.k_hstride, (int)Tq, (int)Tk, Hq, Hkv, mode, shift ? 1 : 0, j.w0};
-      e = bf::launch_correction_prep(dtype, pp, st, tt, j.stream);
-      if (e != hipSuccess) return fail(BF_ERR_HIP, "correction_prep launch: %s", hipGetErrorString(e));
-    }
-    bf::PrefillParams pp;
+    gr.pk = j.pk;  // the block-table rows of this group's sequences
+    if (paged) gr.pk.block_table += (size_t)b0 * gr.pk.max_pages;
+    bf::PrefillParams& pp = gr.pp;
     pp.q = j.q;
     pp.k = paged ? (const void*)(wsb + wl.kc_off) : j.k;
     pp.q2 = wsb + wl.q2_off;
@@ -351,13 +354,34 @@ int run_rows(RowsJob& j) {
     pp.part_o = pp.nks > 1 ? (float*)(wsb + wl.po_off) : nullptr;
     pp.part_lse = pp.nks > 1 ? (float*)(wsb + prefill_ws_layout(batch, Tq, Tk, Hq, Hkv, dtype, paged, pp.nks).pl_off)
                              : nullptr;
-    const long long grid = wgs * pp.nks;
-    if (grid > 0x7fffffffLL) return fail(BF_ERR_INVALID_ARG, "launch grid too large");
+    gr.grid = wgs * pp.nks;
+    if (gr.grid > 0x7fffffffLL)
+      return fail(BF_ERR_INVALID_ARG, "launch grid of sequences %d..%d too large (%lld workgroups)", b0,
+                  b0 + nb - 1, gr.grid);
+  }
+  if (forced_launch_failure()) return fail(BF_ERR_HIP, "launch failure forced by BIFOCAL_TEST_FAIL_LAUNCH");
+
+  for (size_t gi = 0; gi < groups.size(); ++gi) {
+    const Group& gr = groups[gi];
+    const bf::SeqTable& st = gr.st;
+    const bf::PrefillParams& pp = gr.pp;
+    const int b0 = (int)gi * bf::kMaxSeqPerLaunch, nb = st.n;
+    hipError_t e = hipSuccess;
+    bf::VtParams vp{j.v, wsb + wl.vt_off, gr.pk, j.k_hstride, Tpad, Hkv};
+    e = bf::launch_vt_transpose(dtype, vp, st, j.stream);
+    if (e != hipSuccess) return fail(BF_ERR_HIP, "vt_transpose launch: %s", hipGetErrorString(e));
+    if ((bifocal && gr.any_far && !band_only) || paged) {
+      // band-only or s = 1 sequences get no rotation: the prep only gathers
+      bf::PrepParams prep{j.q, j.k, wsb + wl.q2_off, wsb + wl.k2_off, paged ? wsb + wl.kc_off : nullptr, gr.pk,
+                          j.k_hstride, (int)Tq, (int)Tk, Hq, Hkv, mode, shift ? 1 : 0, j.w0};
+      e = bf::launch_correction_prep(dtype, prep, st, tt, j.stream);
+      if (e != hipSuccess) return fail(BF_ERR_HIP, "correction_prep launch: %s", hipGetErrorString(e));
+    }
     if (trace_on())
       fprintf(stderr, "[bifocal] prefill %s dtype=%d seqs=%d..%d grid=%lld P_wg=%d hpw=%d n_hsub=%d s0=%d qpos0=%d w0=%lld key_splits=%d\n",
-              band_only ? "band-only" : bifocal ? "bifocal" : "plain", dtype, b0, b0 + nb - 1, grid, geo.P_wg, geo.hpw,
+              band_only ? "band-only" : bifocal ? "bifocal" : "plain", dtype, b0, b0 + nb - 1, gr.grid, geo.P_wg, geo.hpw,
               geo.n_hsub, st.s[0], st.qpos[0], j.w0, pp.nks);
-    e = bf::launch_prefill_main(dtype, bifocal && any_far, band_only && any_far, pp, st, (int)grid, j.stream);
+    e = bf::launch_prefill_main(dtype, bifocal && gr.any_far, band_only && gr.any_far, pp, st, (int)gr.grid, j.stream);
     if (e != hipSuccess) return fail(BF_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
     if (pp.nks > 1) {
       e = bf::launch_chunk_combine(pp, st.cu[0], st.cu[nb] - st.cu[0], j.stream);

@@ -267,6 +267,20 @@ def test_chunk_valid_arguments_reach_the_launch(L, monkeypatch):
     assert _chunk(L, cu=[0, 100, 101], sl=[100, 128]) == bfl.BF_ERR_HIP  # whole-sequence chunk
 
 
+def test_chunk_later_launch_group_is_validated_before_any_launch(L, monkeypatch):
+    # 65 sequences run as two launch groups; the last one's s(L) (s_len
+    # 2^31 - 1 at w_pre = 1) is out of range. The call must reject it before
+    # the first group is launched: with the launch hook armed, a call that
+    # reached any launch would return BF_ERR_HIP instead.
+    monkeypatch.setenv("BIFOCAL_TEST_FAIL_LAUNCH", "1")
+    n = 65
+    cu = list(range(0, 2 * n + 1, 2))
+    kw = dict(cu=cu, sl=[10] * n, w_pre=1, cap=16)
+    assert _chunk(L, **kw, s_len=[10] * n) == bfl.BF_ERR_HIP          # valid: reaches the hook
+    assert _chunk(L, **kw, s_len=[10] * (n - 1) + [2**31 - 1]) == bfl.BF_ERR_INVALID_ARG
+    assert b"s(L)" in L.bifocal_last_error()
+
+
 def _chunk_paged(L, **kw):
     a = dict(q=P, kp=P, vp=P, o=P, lse=None, bt=P, cu=[0, 30, 31], sl=[100, 1], s_len=None,
              page=16, maxp=8, npages=20, Hq=4, Hkv=2, D=128, dtype=0, w0=16, w_pre=64, theta=1e4,
