@@ -261,7 +261,15 @@ def test_qwen3_8b_decode(Lc, mode):
                                  mode, 1 / math.sqrt(128))
         gap = np.linalg.norm(o_ref - plain)
         err = np.linalg.norm(og - o_ref)
-        print(f"[decode discrimination] err {err:.3e} gap {gap:.3e}", flush=True)
+        # the other long mode, for the record: on N(0,1) inputs FI and PA
+        # differ by about 2e-4 mean-abs here, too close to the bf16 rounding
+        # of k'' and P for a 0.05 bar; the structured input S2 holds that bar
+        # (tests/test_gpu_modes.py)
+        other, _ = oracle.decode(_f32(q), _f32(kc), _f32(vc), Ns, c["w0"], c["w_pre"], c["theta"],
+                                 "pa" if mode == "fi" else "fi", 1 / math.sqrt(128))
+        gap_other = np.linalg.norm(o_ref - other)
+        print(f"[decode discrimination] err {err:.3e} gap-plain {gap:.3e} gap-other-mode "
+              f"{gap_other:.3e} err/gap-other {err / gap_other:.3f}", flush=True)
         assert err <= 0.05 * gap
 
 
