@@ -227,6 +227,26 @@ int bifocal_decode(const void* q, const void* k_cache, const void* v_cache, void
                    float softmax_scale, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * bifocal_decode without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation). Same arguments, layouts, result (bitwise) and
+ * validation as bifocal_decode, minus workspace / workspace_bytes. The split
+ * partials live in a scratch array the library holds in device memory, 32 MiB
+ * per GPU it runs on, kept until the process ends; a call whose partials
+ * would not fit (batch x n_heads_q x splits x 520 bytes, splits = max(129,
+ * ceil(max N / 4032) + 1)) returns BF_ERR_UNSUPPORTED before any HIP call.
+ * The array is the current device's: `stream` must belong to it. Every call
+ * on one GPU shares that GPU's array, so calls that overlap on one GPU (other
+ * streams, other threads) race; serialise them. The call allocates nothing.
+ */
+int bifocal_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, void* o,
+                           float* lse, const int32_t* seqlens_host, int32_t batch,
+                           int32_t cache_capacity, int32_t n_heads_q, int32_t n_heads_kv,
+                           int32_t head_dim, int32_t dtype, int64_t w0, int64_t w_pre,
+                           double rope_theta, int32_t long_mode, float softmax_scale,
+                           void* stream);
+
+/*
  * bifocal_decode over a PAGED KV cache: the same computation and arguments as
  * bifocal_decode, with the cache split into fixed-size pages.
  *   k_pages, v_pages : [num_pages, n_heads_kv, page_size, head_dim] bf16

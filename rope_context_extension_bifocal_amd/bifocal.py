@@ -28,7 +28,7 @@ EXPORTED = ("bifocal_s_of_L", "bifocal_workspace_bytes", "bifocal_prefill", "bif
             "bifocal_chunk_workspace_bytes", "bifocal_prefill_chunk", "bifocal_prefill_chunk_paged",
             "bifocal_decode_paged", "plain_attention_ref_gpu", "bifocal_rope_prefill", "bifocal_rope_append",
             "bifocal_rope_prefill_paged", "bifocal_rope_append_paged",
-            "bifocal_test_pair_map", "bifocal_last_error")
+            "bifocal_test_pair_map", "bifocal_last_error", "bifocal_decode_noalloc")
 
 _lib = None
 
@@ -67,6 +67,9 @@ def lib():
         L.bifocal_decode.restype = ctypes.c_int
         L.bifocal_decode.argtypes = [p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, i64, i64,
                                      f64, i32, f32, p, sz, p]
+        L.bifocal_decode_noalloc.restype = ctypes.c_int
+        L.bifocal_decode_noalloc.argtypes = [p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, i64,
+                                             i64, f64, i32, f32, p]
         L.bifocal_decode_paged.restype = ctypes.c_int
         L.bifocal_decode_paged.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, i32,
                                            i32, i64, i64, f64, i32, f32, p, sz, p]
@@ -252,6 +255,24 @@ def decode(q, k_cache, v_cache, seqlens, w0, w_pre, rope_theta, long_mode="fi",
                                 float(rope_theta), LONG_MODES[long_mode],
                                 _scale(softmax_scale, D), _ptr(workspace), workspace.numel(),
                                 _stream(stream)))
+    return (o, lse) if return_lse else o
+
+
+def decode_noalloc(q, k_cache, v_cache, seqlens, w0, w_pre, rope_theta, long_mode="fi",
+                   softmax_scale=None, return_lse=False, out=None, lse=None, stream=None):
+    """bifocal_decode without a workspace: the library's own per-GPU scratch
+    holds the split partials (calls that overlap on one GPU race). Pass `out`
+    (and `lse`) to allocate nothing on this side either."""
+    B, Hq, D = q.shape
+    Hkv, cap = k_cache.shape[1], k_cache.shape[2]
+    o = out if out is not None else torch.empty_like(q)
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    sl = _i32_array(seqlens)
+    _check(lib().bifocal_decode_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(lse),
+                                        sl, B, cap, Hq, Hkv, D, _DTYPES[q.dtype], int(w0),
+                                        int(w_pre), float(rope_theta), LONG_MODES[long_mode],
+                                        _scale(softmax_scale, D), _stream(stream)))
     return (o, lse) if return_lse else o
 
 

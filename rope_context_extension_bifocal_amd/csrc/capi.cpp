@@ -28,6 +28,8 @@ hipError_t launch_chunk_combine(const PrefillParams& pp, int tok_begin, int n_to
 hipError_t launch_pair_map(long long L, long long w0, long long s, int mode, int8_t* br,
                            long long* dphi_num, long long* s_out, hipStream_t stream);
 size_t decode_workspace_bytes(int batch, long long max_len, int Hq);
+size_t decode_noalloc_capacity();
+int decode_noalloc_scratch(hipStream_t stream, void** out, std::string& err);
 struct PagedCache {
   const int* block_table;
   int page_size;
@@ -37,7 +39,8 @@ struct PagedCache {
 int run_decode(bool bifocal, const void* q, const void* kc, const void* vc, void* o, float* lse,
                const int32_t* seqlens, int batch, int cap, int Hq, int Hkv, long long w0,
                long long w_pre, double theta, int mode, float scale, void* ws, size_t ws_bytes,
-               hipStream_t stream, std::string& err, long long window, const PagedCache* paged);
+               hipStream_t stream, std::string& err, long long window, const PagedCache* paged,
+               bool validate_only = false);
 int run_rope_prefill(const void* q, const void* k, const void* v, void* q_out, void* k_out,
                      void* k_cache, void* v_cache, int cap, const int32_t* cu, const int32_t* pos0,
                      const PagedKV& pk, int batch, int Hq, int Hkv, int dtype, double theta,
@@ -671,6 +674,41 @@ int bifocal_decode(const void* q, const void* k_cache, const void* v_cache, void
   rc = bf::run_decode(!band_only, q, k_cache, v_cache, o, lse, seqlens_host, batch, cache_capacity,
                       n_heads_q, n_heads_kv, w0, w_pre, rope_theta, long_mode, softmax_scale,
                       workspace, workspace_bytes, (hipStream_t)stream, err, band_only ? w0 : 0, nullptr);
+  if (rc) return fail(rc, "%s", err.c_str());
+  g_err.clear();
+  return BF_OK;
+}
+
+int bifocal_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, void* o,
+                           float* lse, const int32_t* seqlens_host, int32_t batch,
+                           int32_t cache_capacity, int32_t n_heads_q, int32_t n_heads_kv,
+                           int32_t head_dim, int32_t dtype, int64_t w0, int64_t w_pre,
+                           double rope_theta, int32_t long_mode, float softmax_scale,
+                           void* stream) {
+  int rc = check_common(n_heads_q, n_heads_kv, head_dim, dtype);
+  if (rc) return rc;
+  if ((rc = check_bifocal_knobs(w0, w_pre, rope_theta, long_mode))) return rc;
+  if (dtype != BF_DTYPE_BF16) return fail(BF_ERR_UNSUPPORTED, "decode supports bf16 only");
+  const bool band_only = long_mode == BF_LONG_NONE;
+  std::string err;
+  // every argument is checked (no HIP call) before the scratch is looked up
+  rc = bf::run_decode(!band_only, q, k_cache, v_cache, o, lse, seqlens_host, batch, cache_capacity,
+                      n_heads_q, n_heads_kv, w0, w_pre, rope_theta, long_mode, softmax_scale, nullptr, 0,
+                      (hipStream_t)stream, err, band_only ? w0 : 0, nullptr, true);
+  if (rc) return fail(rc, "%s", err.c_str());
+  long long max_len = 0;
+  for (int b = 0; b < batch; ++b) max_len = std::max<long long>(max_len, seqlens_host[b]);
+  const size_t need = bf::decode_workspace_bytes(batch, max_len, n_heads_q);
+  const size_t cap = bf::decode_noalloc_capacity();
+  if (need > cap)
+    return fail(BF_ERR_UNSUPPORTED, "this call needs %zu bytes of decode scratch; the allocation-free "
+                "entry point holds %zu (fewer sequences or query heads per call, or bifocal_decode "
+                "with a workspace)", need, cap);
+  void* ws = nullptr;
+  if ((rc = bf::decode_noalloc_scratch((hipStream_t)stream, &ws, err))) return fail(rc, "%s", err.c_str());
+  rc = bf::run_decode(!band_only, q, k_cache, v_cache, o, lse, seqlens_host, batch, cache_capacity,
+                      n_heads_q, n_heads_kv, w0, w_pre, rope_theta, long_mode, softmax_scale, ws, cap,
+                      (hipStream_t)stream, err, band_only ? w0 : 0, nullptr);
   if (rc) return fail(rc, "%s", err.c_str());
   g_err.clear();
   return BF_OK;

@@ -15,6 +15,7 @@
 // decode_combine_kernel: log-sum-exp merge of the splits of each query head.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
 #include <string>
 
 #include "bifocal.h"
@@ -688,10 +689,72 @@ struct PagedCache {
 static_assert(BF_DEC_MAX_CHUNK / kDecWaves / kDecStep + 1 <= 64,
               "a wave's keys must span at most 64 pages of 16 keys");
 
+// ------------------------------------------------------------------ allocation-free decode
+// Scratch for bifocal_decode_noalloc: the split partials (m, l, acc) live in
+// this file-scope device array instead of a caller workspace. Each GPU the
+// library runs on holds its own copy until the process ends; every call on
+// that GPU shares it, so calls that overlap on one GPU race. The split kernel
+// writes every partial the combine kernel reads, so no clearing is needed.
+// Host code never passes the array's name to a kernel: it uses the device
+// address hipGetSymbolAddress returns for the current device, looked up once
+// per device and kept below.
+constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kScratchMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchMaxDevices];  // per device: the device address of `scratch`
+}  // namespace
+
+size_t decode_noalloc_capacity() { return kNoAllocScratchBytes; }
+
+// Device address of `scratch` on the current device (looked up on the first
+// call per device, with that device current).
+int decode_noalloc_scratch(hipStream_t stream, void** out, std::string& err) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    err = std::string("hipGetDevice: ") + hipGetErrorString(e);
+    return BF_ERR_HIP;
+  }
+  if (stream != nullptr) {  // the scratch used is the current device's
+    hipDevice_t sdev = -1;
+    e = hipStreamGetDevice(stream, &sdev);
+    if (e != hipSuccess) {
+      err = std::string("hipStreamGetDevice: ") + hipGetErrorString(e);
+      return BF_ERR_HIP;
+    }
+    if ((int)sdev != dev) {
+      err = "stream belongs to device " + std::to_string((int)sdev) + ", the current device is " +
+            std::to_string(dev);
+      return BF_ERR_INVALID_ARG;
+    }
+  }
+  if (dev < 0 || dev >= kScratchMaxDevices) {
+    err = "device index " + std::to_string(dev) + " beyond the " + std::to_string(kScratchMaxDevices) +
+          " devices the allocation-free decode tracks";
+    return BF_ERR_UNSUPPORTED;
+  }
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) {
+      err = std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e);
+      return BF_ERR_HIP;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return BF_OK;
+}
+
 int run_decode(bool bifocal, const void* q, const void* kc, const void* vc, void* o, float* lse,
                const int32_t* seqlens, int batch, int cap, int Hq, int Hkv, long long w0,
                long long w_pre, double theta, int mode, float scale, void* ws, size_t ws_bytes,
-               hipStream_t stream, std::string& err, long long window, const PagedCache* paged) {
+               hipStream_t stream, std::string& err, long long window, const PagedCache* paged,
+               bool validate_only) {
   auto bad = [&](int code, const std::string& m) { err = m; return code; };
   if (!q || !kc || !vc || !o || !seqlens) return bad(BF_ERR_INVALID_ARG, "null tensor or seqlens pointer");
   int page_log2 = 0;
@@ -725,6 +788,7 @@ int run_decode(bool bifocal, const void* q, const void* kc, const void* vc, void
     return bad(BF_ERR_UNSUPPORTED, "decode supports at most " + std::to_string(kDecMaxSplits - 1) +
                                        " x " + std::to_string(kDecMaxChunk) + " keys per sequence");
   const DecodeWs wl = decode_ws_layout(batch, max_len, Hq);
+  if (validate_only) return BF_OK;  // every argument but the workspace checked
   if (!ws) return bad(BF_ERR_WORKSPACE, "workspace is null");
   if ((uintptr_t)ws & 255u) return bad(BF_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   if (ws_bytes < wl.total)

@@ -123,6 +123,29 @@ def test_valid_arguments_reach_the_launch(L, monkeypatch):
     assert _decode(L, mode=2, w0=5) == bfl.BF_ERR_HIP
 
 
+def _decode_noalloc(L, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=None, sl=[100], cap=128, Hq=4, Hkv=2, D=128, dtype=0, w0=16,
+             w_pre=64, theta=1e4, mode=1, scale=0.088, stream=None)
+    a.update(kw)
+    sl = (ctypes.c_int32 * len(a["sl"]))(*a["sl"])
+    return L.bifocal_decode_noalloc(a["q"], a["k"], a["v"], a["o"], a["lse"], sl, len(a["sl"]),
+                                    a["cap"], a["Hq"], a["Hkv"], a["D"], a["dtype"], a["w0"],
+                                    a["w_pre"], a["theta"], a["mode"], a["scale"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(sl=[0]), -1), (dict(sl=[129]), -1), (dict(dtype=1), -2),
+    (dict(D=96), -2), (dict(Hq=5, Hkv=2), -1), (dict(w0=-3), -1), (dict(mode=9), -1),
+    (dict(Hq=34, Hkv=2), -2), (dict(mode=2, w0=0), -1), (dict(cap=0), -1),
+    # partials of 64 sequences x 128 query heads x 129 splits do not fit the 32 MiB scratch
+    (dict(sl=[100] * 64, Hq=128, Hkv=8), -2),
+])
+def test_decode_noalloc_validation(L, kw, code):
+    # every rejection happens before any HIP call (no GPU here)
+    assert _decode_noalloc(L, **kw) == code
+    assert len(L.bifocal_last_error()) > 0
+
+
 def test_plain_validation(L):
     cu = (ctypes.c_int32 * 2)(0, 100)
     assert L.plain_attention_ref_gpu(7, P, P, P, P, None, cu, 1, 0, 2, 1, 128, 0, 0.1, P, 1 << 30,
