@@ -359,17 +359,50 @@ int bifocal_rope_append_paged(const void* q_raw, const void* k_raw, const void* 
                               double rope_theta, void* stream);
 
 /*
- * Test hook: runs the kernels' own device-side pair classification and
- * position map for one sequence of length L (L <= 4096).
- *   branch_out : device int8 [L * L], row-major (i, j): 0 masked (j > i),
- *                1 local, 2 far;
- *   phi_num_out: device int64 [L], phi(p) * s for FI (= p) and
- *                floor(p / s) * s for PA, so both are exact integers;
- *   s_out      : device int64 [1], s(L) as the device computes it.
+ * Test hook: the bf16 prefill tile kernel's own pair classification for one
+ * sequence of length L (L <= 4096, query positions 0 .. L - 1, the work items
+ * of GQA groups of 4 query heads: 32 query positions each). For every
+ * (32-row item, 64-key tile) one wave takes the item's far-pass and
+ * local-pass tile ranges and applies both passes' per-element masks to a
+ * tile, exactly as the tile loop does, and reports how each pair it covers
+ * would be scored:
+ *   branch_out : device int8 [L * L], row-major (i, j); 1 = by the local pass
+ *                (original RoPE), 2 = by the far pass (scaled RoPE), 3 = by
+ *                both (never correct), 0 = by neither (j > i, or a pair
+ *                band-only attention drops). Entries the kernel never covers
+ *                (tiles past an item's last key) keep the caller's value.
+ *                With s(L) = 1 the two branches coincide and the kernel
+ *                scores every causal pair locally.
+ *   phi_num_out: device int64 [L], the prep pass's (phi(p) - p) * s: -p (s - 1)
+ *                for FI, (floor(p / s) - p) s for PA, both exact integers
+ *                (unused, may be NULL, for BF_LONG_NONE).
+ * long_mode: BF_LONG_FI, BF_LONG_PA or BF_LONG_NONE (s(L) computed on the
+ * host from w_pre, as for bifocal_prefill).
+ * [ai-feeds.com summary, "关键模块" items 1 and 3: the local window and the
+ *  correction of far keys]
  */
 int bifocal_test_pair_map(int64_t L, int64_t w0, int64_t w_pre, int32_t long_mode,
-                          int8_t* branch_out, int64_t* phi_num_out, int64_t* s_out,
-                          void* stream);
+                          int8_t* branch_out, int64_t* phi_num_out, void* stream);
+
+/*
+ * Test hook: the fp32 (cos, sin) pairs the kernels rotate with, for up to
+ * 128 positions given on the host, written to cs_out (device float
+ * [n_pos][64][2], rotary pair m = theta_m = rope_theta^(-2m/128)):
+ *   which 0: prefill queries at the positions of a sequence of length L
+ *            (the prep pass's angle theta_m (phi(p) - p), plus
+ *            theta_m (w0 - phi(w0)) with BF_LONG_SHIFT);
+ *   which 1: prefill keys (the same without the shift);
+ *   which 2: decode keys of a call with N = L keys, through the split
+ *            kernel's angle addition (per-step base rotation times the
+ *            offset-table rotation, with its incremental divmod tracking);
+ *   which 3: decode queries at position p (a call with N = p + 1 keys).
+ * s = s(L) (s(p + 1) for which 3); long_mode BF_LONG_FI or BF_LONG_PA, with
+ * BF_LONG_SHIFT for the queries' continuity shift.
+ * [ai-feeds.com summary, "关键模块" item 3: the correction rotation]
+ */
+int bifocal_test_angles(int32_t which, const int64_t* positions_host, int32_t n_pos, int64_t L,
+                        int64_t w0, int64_t w_pre, double rope_theta, int32_t long_mode,
+                        float* cs_out, void* stream);
 
 /* Thread-local description of the last error (empty string after success). */
 const char* bifocal_last_error(void);

@@ -28,7 +28,8 @@ EXPORTED = ("bifocal_s_of_L", "bifocal_workspace_bytes", "bifocal_prefill", "bif
             "bifocal_chunk_workspace_bytes", "bifocal_prefill_chunk", "bifocal_prefill_chunk_paged",
             "bifocal_decode_paged", "plain_attention_ref_gpu", "bifocal_rope_prefill", "bifocal_rope_append",
             "bifocal_rope_prefill_paged", "bifocal_rope_append_paged",
-            "bifocal_test_pair_map", "bifocal_last_error", "bifocal_decode_noalloc")
+            "bifocal_test_pair_map", "bifocal_last_error", "bifocal_decode_noalloc",
+            "bifocal_test_angles")
 
 _lib = None
 
@@ -89,7 +90,9 @@ def lib():
         L.bifocal_rope_append.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, f64,
                                           p]
         L.bifocal_test_pair_map.restype = ctypes.c_int
-        L.bifocal_test_pair_map.argtypes = [i64, i64, i64, i32, p, p, p, p]
+        L.bifocal_test_pair_map.argtypes = [i64, i64, i64, i32, p, p, p]
+        L.bifocal_test_angles.restype = ctypes.c_int
+        L.bifocal_test_angles.argtypes = [i32, p, i32, i64, i64, i64, f64, i32, p, p]
         L.bifocal_last_error.restype = ctypes.c_char_p
         L.bifocal_last_error.argtypes = []
         _lib = L
@@ -389,11 +392,26 @@ def rope_append_paged(q_raw, k_raw, v_new, k_pages, v_pages, block_table, seqlen
     return qo
 
 
-def test_pair_map(L, w0, w_pre, long_mode="fi", device="cuda"):
-    """Device pair classification and correction offsets (test hook)."""
-    br = torch.empty((L, L), dtype=torch.int8, device=device)
+def test_pair_map(L, w0, w_pre, long_mode="fi", device="cuda", fill=-1):
+    """The bf16 tile kernel's pair classification (1 local, 2 far, 3 both, 0
+    neither; `fill` where no wave covers the pair) and the prep pass's
+    (phi(p) - p) * s numerators (test hook)."""
+    br = torch.full((L, L), fill, dtype=torch.int8, device=device)
     num = torch.empty((L,), dtype=torch.int64, device=device)
-    s = torch.empty((1,), dtype=torch.int64, device=device)
     _check(lib().bifocal_test_pair_map(int(L), int(w0), int(w_pre), LONG_MODES[long_mode],
-                                       _ptr(br), _ptr(num), _ptr(s), _stream(None)))
-    return br, num, int(s.item())
+                                       _ptr(br), _ptr(num), _stream(None)))
+    torch.cuda.synchronize()
+    return br, num
+
+
+def test_angles(which, positions, L, w0, w_pre, rope_theta, long_mode="fi", device="cuda"):
+    """fp32 (cos, sin) [n, 64, 2] the kernels rotate with at `positions`
+    (which: 0 prefill queries, 1 prefill keys, 2 decode keys of an L-key call,
+    3 decode queries at position p of a (p + 1)-key call) (test hook)."""
+    pos = (ctypes.c_int64 * len(positions))(*[int(x) for x in positions])
+    cs = torch.empty((len(positions), 64, 2), dtype=torch.float32, device=device)
+    _check(lib().bifocal_test_angles(int(which), pos, len(positions), int(L), int(w0), int(w_pre),
+                                     float(rope_theta), LONG_MODES[long_mode], _ptr(cs),
+                                     _stream(None)))
+    torch.cuda.synchronize()
+    return cs

@@ -98,4 +98,17 @@ struct VtParams {
   int Tpad, Hkv;
 };
 
+// Positions whose correction angles a test hook reports (at most kProbeMax).
+constexpr int kProbeMax = 128;
+struct AngleProbe {
+  int n;
+  int mode;   // 0 = FI, 1 = PA
+  int shift;  // band-edge continuity shift (queries)
+  int query;  // prefill: 1 = query angles, 0 = key angles
+  long long w0;
+  long long N;               // decode: keys of the call (s = s(N) for key angles)
+  long long pos[kProbeMax];  // positions
+  long long s[kProbeMax];    // s of each position's call
+};
+
 }  // namespace bf

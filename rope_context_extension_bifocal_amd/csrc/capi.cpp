@@ -26,7 +26,11 @@ hipError_t launch_prefill_main(int dtype, bool bifocal, bool band, const Prefill
 hipError_t launch_chunk_combine(const PrefillParams& pp, int tok_begin, int n_tok,
                                 hipStream_t stream);
 hipError_t launch_pair_map(long long L, long long w0, long long s, int mode, int8_t* br,
-                           long long* dphi_num, long long* s_out, hipStream_t stream);
+                           long long* dphi_num, hipStream_t stream);
+hipError_t launch_prep_angles(const AngleProbe& a, const ThetaTable& tt, float* cs,
+                              hipStream_t stream);
+hipError_t launch_decode_angles(const AngleProbe& a, const ThetaTable& tt, int which, float* cs,
+                                hipStream_t stream);
 size_t decode_workspace_bytes(int batch, long long max_len, int Hq);
 size_t decode_noalloc_capacity();
 int decode_noalloc_scratch(hipStream_t stream, void** out, std::string& err);
@@ -759,17 +763,57 @@ int plain_attention_ref_gpu(int32_t phase, const void* q, const void* k, const v
 }
 
 int bifocal_test_pair_map(int64_t L, int64_t w0, int64_t w_pre, int32_t long_mode,
-                          int8_t* branch_out, int64_t* phi_num_out, int64_t* s_out,
-                          void* stream) {
+                          int8_t* branch_out, int64_t* phi_num_out, void* stream) {
   if (L < 1 || L > 4096) return fail(BF_ERR_INVALID_ARG, "test_pair_map needs 1 <= L <= 4096");
+  if (long_mode & BF_LONG_SHIFT) return fail(BF_ERR_INVALID_ARG, "test_pair_map takes FI, PA or band only");
   int rc = check_bifocal_knobs(w0, w_pre, 10000.0, long_mode);
   if (rc) return rc;
-  if (!branch_out || !phi_num_out || !s_out) return fail(BF_ERR_INVALID_ARG, "null output pointer");
+  if (!branch_out || (!phi_num_out && long_mode != BF_LONG_NONE))
+    return fail(BF_ERR_INVALID_ARG, "null output pointer");
   if (forced_launch_failure()) return fail(BF_ERR_HIP, "launch failure forced by BIFOCAL_TEST_FAIL_LAUNCH");
-  const long long s = bifocal_s_of_L(L, w_pre);
+  const long long s = long_mode == BF_LONG_NONE ? 1 : bifocal_s_of_L(L, w_pre);
   hipError_t e = bf::launch_pair_map(L, w0, s, long_mode, branch_out, (long long*)phi_num_out,
-                                     (long long*)s_out, (hipStream_t)stream);
+                                     (hipStream_t)stream);
   if (e != hipSuccess) return fail(BF_ERR_HIP, "pair_map launch: %s", hipGetErrorString(e));
+  g_err.clear();
+  return BF_OK;
+}
+
+int bifocal_test_angles(int32_t which, const int64_t* positions_host, int32_t n_pos, int64_t L,
+                        int64_t w0, int64_t w_pre, double rope_theta, int32_t long_mode,
+                        float* cs_out, void* stream) {
+  if (which < 0 || which > 3) return fail(BF_ERR_INVALID_ARG, "which must be 0..3 (got %d)", which);
+  if (n_pos < 1 || n_pos > bf::kProbeMax)
+    return fail(BF_ERR_INVALID_ARG, "n_pos must be in [1, %d] (got %d)", bf::kProbeMax, n_pos);
+  if (!positions_host || !cs_out) return fail(BF_ERR_INVALID_ARG, "null pointer");
+  const int base = long_mode & ~BF_LONG_SHIFT;
+  if (base != BF_LONG_FI && base != BF_LONG_PA)
+    return fail(BF_ERR_INVALID_ARG, "long_mode must be FI or PA (optionally with the shift)");
+  int rc = check_bifocal_knobs(w0, w_pre, rope_theta, long_mode);
+  if (rc) return rc;
+  if (L < 1 || L > (1LL << 31)) return fail(BF_ERR_INVALID_ARG, "L must be in [1, 2^31]");
+  bf::AngleProbe a;
+  std::memset(&a, 0, sizeof a);
+  a.n = n_pos;
+  a.mode = base;
+  a.shift = (long_mode & BF_LONG_SHIFT) ? 1 : 0;
+  a.query = which == 0 ? 1 : 0;
+  a.w0 = w0;
+  a.N = L;
+  for (int i = 0; i < n_pos; ++i) {
+    const long long p = positions_host[i];
+    if (p < 0 || (which != 3 && p >= L) || p + 1 > (1LL << 31))
+      return fail(BF_ERR_INVALID_ARG, "position %lld out of range", p);
+    a.pos[i] = p;
+    const long long s = bifocal_s_of_L(which == 3 ? p + 1 : L, w_pre);
+    if (s > (1LL << 30)) return fail(BF_ERR_INVALID_ARG, "s(L) out of range");
+    a.s[i] = s;
+  }
+  if (forced_launch_failure()) return fail(BF_ERR_HIP, "launch failure forced by BIFOCAL_TEST_FAIL_LAUNCH");
+  const bf::ThetaTable tt = theta_table(rope_theta);
+  const hipError_t e = which <= 1 ? bf::launch_prep_angles(a, tt, cs_out, (hipStream_t)stream)
+                                  : bf::launch_decode_angles(a, tt, which, cs_out, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(BF_ERR_HIP, "angle probe launch: %s", hipGetErrorString(e));
   g_err.clear();
   return BF_OK;
 }

@@ -124,6 +124,55 @@ __device__ __forceinline__ uint32_t rot_word(uint32_t x, uint32_t y, float c0, f
   return pack_bf16x2(a0 * c0 - b0 * s0, a1 * c1 - b1 * s1);
 }
 
+// Pieces of the far-key correction angle, shared by the split kernel and the
+// angle test kernel (reading: angle addition over a 16-key step, see below).
+// Base angle of a step starting at key jb, in turns per unit theta_m
+// (multiplied by theta_m / 2pi by the caller): phi(jb) - jb, where
+// q_pa = floor(jb / s) for position aliasing.
+__device__ __forceinline__ double dec_step_base(int mode, long long q_pa, long long jb, long long s,
+                                                double inv_s) {
+  return mode == 1 ? (double)(q_pa - jb) : (double)(-jb * (s - 1)) * inv_s;
+}
+// Offset-table row of key jb + n16 (r_pa = jb mod s): n16 for FI,
+// n16 - floor((r_pa + n16) / s) for PA (a float divide corrected by one either way).
+__device__ __forceinline__ int dec_offset_row(int mode, int r_pa, int n16, int s_i, float inv_s_f) {
+  if (mode != 1) return n16;
+  const int x = r_pa + n16;
+  int qd = (int)((float)x * inv_s_f);
+  if ((qd + 1) * s_i <= x) ++qd;
+  if (qd * s_i > x) --qd;
+  return n16 - qd;
+}
+// Offset-table entry of row idx for pair m: rotation by -theta_m idx kappa,
+// kappa = (s - 1) / s (FI) or 1 (PA).
+__device__ __forceinline__ void dec_offset_cos_sin(double th_m, int idx, double kappa, float& c,
+                                                   float& sn) {
+  turn_cos_sin(-th_m * kInv2Pi * (double)idx * kappa, c, sn);
+}
+// Rotation of a key: the step's base rotation (bc, bs) times the offset (tc, ts).
+__device__ __forceinline__ void dec_compose(float bc, float bs, float tc, float ts, float& c,
+                                            float& sn) {
+  c = bc * tc - bs * ts;
+  sn = bs * tc + bc * ts;
+}
+// (q_pa, r_pa) = divmod(step start, s), advanced by one 16-key step.
+__device__ __forceinline__ void dec_advance(long long& q_pa, int& r_pa, int add16_q, int add16_r,
+                                            int s_i) {
+  q_pa += add16_q;
+  r_pa += add16_r;
+  if (r_pa >= s_i) {
+    r_pa -= s_i;
+    ++q_pa;
+  }
+}
+// Query angle numerator in turns per unit theta_m: (phi(N - 1) - (N - 1)),
+// plus w0 - phi(w0) with the band-edge continuity shift.
+__device__ __forceinline__ double dec_query_base(int mode, int shift, long long N, long long s,
+                                                 long long w0) {
+  const long long qsh = !shift ? 0 : mode == 1 ? (w0 - w0 / s) * s : w0 * (s - 1);
+  return (double)(dcorr_num(N - 1, s, mode) + qsh) / (double)s;
+}
+
 // ------------------------------------------------------------------ kernels
 // Split kernel: workgroup = (batch b, KV head, split of `chunk` keys). Each of
 // the 4 waves streams its own contiguous quarter of the split in 16-key steps,
@@ -283,7 +332,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p, De
     for (int e = tid; e < kDecStep * kPairs; e += 256) {  // pair m = e % 64 = lane
       const int idx = e >> 6;
       float c, sn;
-      turn_cos_sin(-th_lane * kInv2Pi * (double)idx * kappa, c, sn);
+      dec_offset_cos_sin(th_lane, idx, kappa, c, sn);
       sT[idx * kDecTRow + lane] = make_float2(c, sn);
     }
   }
@@ -291,8 +340,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p, De
   if (split_far) {
     // query angle numerator (phi(N - 1) - (N - 1)) s, plus (w0 - phi(w0)) s
     // with the band-edge continuity shift (w0 < N here, so no overflow)
-    const long long qsh = !p.shift ? 0 : p.mode == 1 ? (w0 - w0 / s) * s : w0 * (s - 1);
-    const double qn = (double)(dcorr_num(N - 1, s, p.mode) + qsh) / (double)s;
+    const double qn = dec_query_base(p.mode, p.shift, N, s, w0);
     float c, sn;
     turn_cos_sin(th_lane * kInv2Pi * qn, c, sn);
     for (int e = tid; e < p.G * kPairs; e += 256) {  // pair m = e % 64 = lane
@@ -346,18 +394,11 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p, De
     if (any_far) {
       // base rotation of the step, pair m = lane
       const long long jb = kw0 + jbl;
-      const double qb = p.mode == 1 ? (double)(q_pa - jb) : (double)(-jb * (s - 1)) * inv_s;
+      const double qb = dec_step_base(p.mode, q_pa, jb, s, inv_s);
       float cb, sb;
       turn_cos_sin(th_turn * qb, cb, sb);
       sBw[lane] = make_float2(cb, sb);
-      int idx = n16;
-      if (p.mode == 1) {
-        const int x = r_pa + n16;
-        int qd = (int)((float)x * inv_s_f);
-        if ((qd + 1) * s_i <= x) ++qd;
-        if (qd * s_i > x) --qd;
-        idx = n16 - qd;
-      }
+      const int idx = dec_offset_row(p.mode, r_pa, n16, s_i, inv_s_f);
       if (jbl + n16 < far_l) {
         const float4* bq4 = (const float4*)sBw;
         const float4* tq4 = (const float4*)(sT + idx * kDecTRow);
@@ -371,8 +412,9 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p, De
             // pairs m = 32 t + 8 g4 + 2 w and m + 1
             const float4 bq = bq4[16 * t + 4 * g4 + w];
             const float4 tq = tq4[16 * t + 4 * g4 + w];
-            const float c0 = bq.x * tq.x - bq.y * tq.y, s0 = bq.y * tq.x + bq.x * tq.y;
-            const float c1 = bq.z * tq.z - bq.w * tq.w, s1 = bq.w * tq.z + bq.z * tq.w;
+            float c0, s0, c1, s1;
+            dec_compose(bq.x, bq.y, tq.x, tq.y, c0, s0);
+            dec_compose(bq.z, bq.w, tq.z, tq.w, c1, s1);
             uint32_t yo;
             lo[w] = rot_word(lo[w], hi[w], c0, s0, c1, s1, yo);
             hi[w] = yo;
@@ -380,14 +422,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p, De
         }
       }
     }
-    if (BIFOCAL) {
-      q_pa += add16_q;
-      r_pa += add16_r;
-      if (r_pa >= s_i) {
-        r_pa -= s_i;
-        ++q_pa;
-      }
-    }
+    if (BIFOCAL) dec_advance(q_pa, r_pa, add16_q, add16_r, s_i);
     dbf16x8 qs[4];
     q_operand(any_far, qs);
     df32x4 S = df32x4{};
@@ -592,6 +627,43 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p, Dec
     if (p.lse && t == 0 && dq == 0)
       p.lse[(size_t)b * p.Hq + h] = (mt + __log2f(lt)) * 0.69314718055994530942f;
   }
+}
+
+// ------------------------------------------------------------------ test hook
+// The fp32 cos / sin the split kernel rotates with, for given positions:
+// which = 2: the key at a.pos[n] of a call with s = a.s[n], through the
+//   kernel's own angle addition (a wave whose first key is the multiple of
+//   1024 below the key, the per-step divmod tracking, the step's base
+//   rotation, the offset-table row and the product of the two);
+// which = 3: the query at a.pos[n] (N = pos + 1 keys, s = a.s[n]).
+// Block = position, thread = rotary pair; cs [n][64][2].
+__global__ __launch_bounds__(64) void decode_angle_kernel(AngleProbe a, ThetaTable tt, int which,
+                                                          float* cs) {
+  const int n = blockIdx.x, m = threadIdx.x;
+  const long long pos = a.pos[n], s = a.s[n];
+  const int s_i = (int)s;
+  float c, sn;
+  if (which == 3) {
+    turn_cos_sin(tt.th[m] * kInv2Pi * dec_query_base(a.mode, a.shift, pos + 1, s, a.w0), c, sn);
+  } else {
+    const long long kw0 = (pos / 1024) * 1024, jb = pos & ~15LL;
+    long long q_pa = kw0 / s;
+    int r_pa = (int)(kw0 - q_pa * s);
+    for (long long j = kw0; j < jb; j += kDecStep) dec_advance(q_pa, r_pa, 16 / s_i, 16 % s_i, s_i);
+    float cb, sb, tc, ts;
+    turn_cos_sin(tt.th[m] * kInv2Pi * dec_step_base(a.mode, q_pa, jb, s, 1.0 / (double)s), cb, sb);
+    const int idx = dec_offset_row(a.mode, r_pa, (int)(pos - jb), s_i, 1.f / (float)s_i);
+    dec_offset_cos_sin(tt.th[m], idx, a.mode == 1 ? 1.0 : (double)(s - 1) / (double)s, tc, ts);
+    dec_compose(cb, sb, tc, ts, c, sn);
+  }
+  cs[((size_t)n * kPairs + m) * 2] = c;
+  cs[((size_t)n * kPairs + m) * 2 + 1] = sn;
+}
+
+hipError_t launch_decode_angles(const AngleProbe& a, const ThetaTable& tt, int which, float* cs,
+                                hipStream_t stream) {
+  hipLaunchKernelGGL(decode_angle_kernel, dim3(a.n), dim3(64), 0, stream, a, tt, which, cs);
+  return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ host side

@@ -157,6 +157,23 @@ __device__ __forceinline__ int seq_of_tok(const int* cu, int n, int tok) {
   return lo;
 }
 
+// Correction angle of the prep pass: (phi(pos) - pos) * s as an exact
+// integer, plus for queries with the band-edge continuity shift
+// (w0 - phi(w0)) * s = w0 (s - 1) (FI) or (w0 - floor(w0 / s)) s (PA); the
+// angle theta_m * num / s is formed in fp64 and rounded to fp32 cos / sin.
+__device__ __forceinline__ long long prep_num(long long pos, long long s, int mode, bool query,
+                                              int shift, long long w0) {
+  long long num = corr_num(pos, s, mode);
+  if (query && shift) num += mode == 1 ? (w0 - w0 / s) * s : w0 * (s - 1);
+  return num;
+}
+__device__ __forceinline__ void prep_cos_sin(double th_m, double ratio, float& c, float& sn) {
+  double sd, cd;
+  sincos(th_m * ratio, &sd, &cd);
+  c = (float)cd;
+  sn = (float)sd;
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void correction_prep_kernel(PrepParams p, SeqTable st,
                                                               ThetaTable tt) {
@@ -178,18 +195,10 @@ __global__ __launch_bounds__(256) void correction_prep_kernel(PrepParams p, SeqT
   float c[E], sn[E];
   if (rot) {
     const long long pos = keys ? row : st.qpos[b] + row;
-    long long num = corr_num(pos, s, p.long_mode);
-    // queries with the band-edge continuity shift: (w0 - phi(w0)) * s is the
-    // exact integer w0 (s - 1) (FI) or (w0 - floor(w0 / s)) s (PA)
-    if (!keys && p.shift) num += p.long_mode == 1 ? (p.w0 - p.w0 / s) * s : p.w0 * (s - 1);
+    const long long num = prep_num(pos, s, p.long_mode, !keys, p.shift, p.w0);
     const double ratio = (double)num / (double)s;
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      double sd, cd;
-      sincos(tt.th[m0 + e] * ratio, &sd, &cd);
-      c[e] = (float)cd;
-      sn[e] = (float)sd;
-    }
+    for (int e = 0; e < E; ++e) prep_cos_sin(tt.th[m0 + e], ratio, c[e], sn[e]);
   }
   const int nh = keys ? p.Hkv : p.Hq;
   for (int h = 0; h < nh; ++h) {
@@ -346,6 +355,21 @@ __device__ __forceinline__ Item make_item(const PrefillParams& p, const SeqTable
   const int wg_end = it.qp + min(it.R0 + p.P_wg, it.L);  // keys < wg_end
   it.nkt = (wg_end + kKeyTile - 1) / kKeyTile;
   return it;
+}
+
+// Key-tile ranges of the two passes for a workgroup's query positions
+// R0 .. Rl: the far pass visits tiles [0, far_end) (a far pair needs a key
+// j <= Rl - w0), the local pass [loc_b, nkt) (a local pair needs j > R0 - w0).
+// w0 is the effective window (2^62 when every pair is local).
+template <bool BIFOCAL, bool BAND>
+__device__ __forceinline__ void pass_ranges(long long R0, long long Rl, int nkt, long long w0,
+                                            int& far_end, int& loc_b) {
+  far_end = (BIFOCAL && !BAND && Rl - w0 >= 0) ? min(nkt, (int)((Rl - w0) / kKeyTile) + 1) : 0;
+  loc_b = nkt;
+  if (w0 > 0) {
+    const long long first = R0 - w0 + 1;  // smallest key with a local pair
+    loc_b = first <= 0 ? 0 : (int)min((long long)nkt, first / kKeyTile);
+  }
 }
 
 // Tile needs, for the whole workgroup (query positions R0 .. R0 + P_wg - 1)
@@ -897,15 +921,8 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillParams p, S
   // R0 .. R0 + P_wg - 1
   const long long R0 = (long long)it.qp + it.R0, Rl = R0 + p.P_wg - 1;
   const long long w0 = it.w0;
-  // far pass over tiles [0, far_end) (far pairs exist: keys j <= Rl - w0),
-  // local pass over [loc_b, nkt) (local pairs: keys j > R0 - w0)
-  const int far_end = (BIFOCAL && !BAND && Rl - w0 >= 0)
-                          ? min(it.nkt, (int)((Rl - w0) / kKeyTile) + 1) : 0;
-  int loc_b = it.nkt;
-  if (w0 > 0) {
-    const long long first = R0 - w0 + 1;  // smallest key with a local pair
-    loc_b = first <= 0 ? 0 : (int)min((long long)it.nkt, first / kKeyTile);
-  }
+  int far_end, loc_b;
+  pass_ranges<BIFOCAL, BAND>(R0, Rl, it.nkt, w0, far_end, loc_b);
   // key split: part `split` of the nks takes visits [v0, v1) of the sequence
   // far tiles, then local tiles
   int far_b = 0, far_e = far_end, loc_e = it.nkt;
@@ -1166,19 +1183,59 @@ __global__ __launch_bounds__(256, 1) void prefill_f32_kernel(PrefillParams p, Se
     p.lse[(size_t)it.hq * p.T + it.tok0 + row] = (m_run + __log2f(l_run)) * 0.69314718055994530942f;
 }
 
-// --------------------------------------------------------------- test hook
-__global__ void pair_map_kernel(long long L, long long w0, long long s, int mode, int8_t* br,
-                                long long* dphi_num, long long* s_out) {
-  const long long n = L * L;
-  for (long long e = blockIdx.x * (long long)blockDim.x + threadIdx.x; e < n;
-       e += (long long)gridDim.x * blockDim.x) {
-    const long long i = e / L, j = e % L;
-    br[e] = (j > i) ? 0 : (pair_is_local(i, j, w0) ? 1 : 2);
-  }
+// --------------------------------------------------------------- test hooks
+// The bf16 tile kernel's own classification for one sequence of length L
+// (query positions 0 .. L - 1, GQA groups of 4 heads: 32-row work items):
+// wave (row block rb, key tile kt) takes the pass tile ranges of its item
+// (pass_ranges) and runs mask_tile of both passes on a zero tile, exactly as
+// the tile loop does, and writes for every causal pair it covers
+//   1: scored by the local pass, 2: scored by the far pass,
+//   3: scored by both (an error), 0: scored by neither.
+// Pairs the kernel never visits keep what the caller put there.
+template <bool BAND>
+__global__ __launch_bounds__(64) void pair_map_kernel(long long L, long long w0_eff, int8_t* br) {
+  const int rb = blockIdx.x, kt = blockIdx.y, lane = threadIdx.x;
+  const int li = lane & 31, hl = lane >> 5;
+  const long long R0 = 32LL * rb, Rl = min(R0 + 31, L - 1);
+  const int nkt = (int)((Rl + 1 + kKeyTile - 1) / kKeyTile);
+  if (kt >= nkt) return;
+  int far_end, loc_b;
+  pass_ranges<true, BAND>(R0, R0 + 31, nkt, w0_eff, far_end, loc_b);
+  const WaveRows wr{(int)R0, (int)R0, (int)L, (int)min(w0_eff, (long long)(1 << 30))};
+  f32x16 Sf[2], Sl[2];
+  Sf[0] = Sf[1] = Sl[0] = Sl[1] = f32x16{};
+  mask_tile<true>(Sf, wr, kt * kKeyTile, li, hl);
+  mask_tile<false>(Sl, wr, kt * kKeyTile, li, hl);
+  const long long i = R0 + li;
+  if (i >= L) return;
+#pragma unroll
+  for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const long long j = (long long)kt * kKeyTile + 32 * jb + key_of_acc(r, hl);
+      if (j >= L) continue;
+      const bool far = kt < far_end && Sf[jb][r] != -INFINITY;
+      const bool loc = kt >= loc_b && kt < nkt && Sl[jb][r] != -INFINITY;
+      br[i * L + j] = (int8_t)((far ? 2 : 0) + (loc ? 1 : 0));
+    }
+}
+
+// The prep pass's (phi(p) - p) * s numerators for p < L.
+__global__ void phi_num_kernel(long long L, long long s, int mode, long long* dphi_num) {
   for (long long pidx = blockIdx.x * (long long)blockDim.x + threadIdx.x; pidx < L;
        pidx += (long long)gridDim.x * blockDim.x)
-    dphi_num[pidx] = corr_num(pidx, s, mode);
-  if (blockIdx.x == 0 && threadIdx.x == 0) *s_out = s;
+    dphi_num[pidx] = prep_num(pidx, s, mode, false, 0, 0);
+}
+
+// The prep pass's fp32 cos / sin of the correction angle for given positions:
+// block = position, thread = rotary pair; cs [n][64][2].
+__global__ __launch_bounds__(64) void prep_angle_kernel(AngleProbe a, ThetaTable tt, float* cs) {
+  const int n = blockIdx.x, m = threadIdx.x;
+  const long long num = prep_num(a.pos[n], a.s[n], a.mode, a.query != 0, a.shift, a.w0);
+  float c, sn;
+  prep_cos_sin(tt.th[m], (double)num / (double)a.s[n], c, sn);
+  cs[((size_t)n * kPairs + m) * 2] = c;
+  cs[((size_t)n * kPairs + m) * 2 + 1] = sn;
 }
 
 // --------------------------------------------------------------- launchers
@@ -1280,9 +1337,22 @@ hipError_t launch_prefill_main(int dtype, bool bifocal, bool band, const Prefill
 }
 
 hipError_t launch_pair_map(long long L, long long w0, long long s, int mode, int8_t* br,
-                           long long* dphi_num, long long* s_out, hipStream_t stream) {
-  hipLaunchKernelGGL(pair_map_kernel, dim3(64), dim3(256), 0, stream, L, w0, s, mode, br,
-                     dphi_num, s_out);
+                           long long* dphi_num, hipStream_t stream) {
+  // the tile kernel treats every pair as local when s = 1 (both branches coincide)
+  const bool band = mode == 2;
+  const long long w0_eff = (band || s > 1) ? w0 : (1LL << 62);
+  const dim3 grid((unsigned)((L + 31) / 32), (unsigned)((L + kKeyTile - 1) / kKeyTile));
+  if (band) hipLaunchKernelGGL(pair_map_kernel<true>, grid, dim3(64), 0, stream, L, w0_eff, br);
+  else hipLaunchKernelGGL(pair_map_kernel<false>, grid, dim3(64), 0, stream, L, w0_eff, br);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || band) return e;
+  hipLaunchKernelGGL(phi_num_kernel, dim3(16), dim3(256), 0, stream, L, s, mode, dphi_num);
+  return hipGetLastError();
+}
+
+hipError_t launch_prep_angles(const AngleProbe& a, const ThetaTable& tt, float* cs,
+                              hipStream_t stream) {
+  hipLaunchKernelGGL(prep_angle_kernel, dim3(a.n), dim3(64), 0, stream, a, tt, cs);
   return hipGetLastError();
 }
 

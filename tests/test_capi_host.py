@@ -157,9 +157,17 @@ def test_plain_validation(L):
 
 
 def test_pair_map_validation(L):
-    assert L.bifocal_test_pair_map(5000, 4, 8, 0, P, P, P, None) == -1
-    assert L.bifocal_test_pair_map(64, -1, 8, 0, P, P, P, None) == -1
-    assert L.bifocal_test_pair_map(64, 4, 8, 0, None, P, P, None) == -1
+    assert L.bifocal_test_pair_map(5000, 4, 8, 0, P, P, None) == -1
+    assert L.bifocal_test_pair_map(64, -1, 8, 0, P, P, None) == -1
+    assert L.bifocal_test_pair_map(64, 4, 8, 0, None, P, None) == -1
+    assert L.bifocal_test_pair_map(64, 4, 8, 4, P, P, None) == -1      # shift flag not taken
+    assert L.bifocal_test_pair_map(64, 4, 8, 0, P, None, None) == -1   # FI needs phi_num_out
+    pos = (ctypes.c_int64 * 3)(0, 5, 99)
+    assert L.bifocal_test_angles(4, pos, 3, 100, 4, 8, 1e4, 0, P, None) == -1     # bad which
+    assert L.bifocal_test_angles(0, pos, 129, 100, 4, 8, 1e4, 0, P, None) == -1   # too many
+    assert L.bifocal_test_angles(0, pos, 3, 99, 4, 8, 1e4, 0, P, None) == -1      # 99 >= L
+    assert L.bifocal_test_angles(0, pos, 3, 100, 4, 8, 1e4, 2, P, None) == -1     # band mode
+    assert L.bifocal_test_angles(3, pos, 3, 1, 4, 8, 1e4, 5, None, None) == -1    # null output
 
 
 def _rope_prefill(L, **kw):

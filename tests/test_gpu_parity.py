@@ -72,23 +72,81 @@ def _prefill_case(lens, Hq, Hkv, dtype, w0, w_pre, theta, mode, seed, rows_per_s
 # ---------------------------------------------------------------- integer work
 @pytest.mark.parametrize("L,w0,w_pre,mode", [
     (1, 0, 1, "fi"), (200, 17, 64, "fi"), (200, 17, 64, "pa"), (300, 0, 7, "pa"),
-    (129, 200, 16, "fi"), (1000, 64, 333, "pa"), (4096, 256, 1024, "pa")])
+    (129, 200, 16, "fi"), (1000, 64, 333, "pa"), (4096, 256, 1024, "pa"), (700, 100, 1000, "fi"),
+    (1000, 64, 333, "band"), (777, 1, 5, "band"), (500, 600, 5, "band")])
 def test_pair_map_bit_exact(L, w0, w_pre, mode):
-    br, num, s = bfl.test_pair_map(L, w0, w_pre, mode)
-    assert s == oracle.s_of_L(L, w_pre)
-    br = br.cpu().numpy()
+    # the bf16 tile kernel's own pass ranges and per-element masks: every
+    # causal pair is scored by exactly one pass, the one the definition names
+    # (local iff i - j < w0; with s(L) = 1 every pair is local since the two
+    # branches coincide; band-only drops the far pairs); no pair above the
+    # diagonal is scored
+    br, num = bfl.test_pair_map(L, w0, w_pre, mode)
+    br = br.cpu().numpy().astype(np.int64)
+    s = oracle.s_of_L(L, w_pre)
     i, j = np.meshgrid(np.arange(L), np.arange(L), indexing="ij")
-    sub = [(a, b) for a, b in zip(np.random.default_rng(L).integers(0, L, 2000),
-                                  np.random.default_rng(L + 1).integers(0, L, 2000))]
-    sub += [(a, b) for a in range(min(L, 40)) for b in range(min(L, 40))]
-    for a, b in sub:
-        assert br[a, b] == oracle.pair_branch(a, b, w0)
-    # closed form counts of the band
-    assert int((br == 1).sum()) == sum(min(x + 1, w0) for x in range(L))
-    assert int((br == 0).sum()) == L * (L - 1) // 2
-    num = num.cpu().numpy()
-    for p in list(range(min(L, 300))) + [L - 1]:
-        assert num[p] == round((oracle.phi(p, s, mode) - p) * s)
+    causal = j <= i
+    local = (i - j) < w0
+    if mode == "band":
+        want = np.where(local, 1, 0)
+    elif s == 1:
+        want = np.ones_like(br)
+    else:
+        want = np.where(local, 1, 2)
+    assert np.array_equal(br[causal], want[causal])
+    above = br[~causal]
+    assert np.all((above == 0) | (above == -1))  # masked, or a tile no wave covers
+    # the oracle's own rule on a sample, and the closed-form band count
+    for a, b in zip(np.random.default_rng(L).integers(0, L, 2000),
+                    np.random.default_rng(L + 1).integers(0, L, 2000)):
+        if b <= a and (s > 1 or mode == "band"):
+            ob = oracle.pair_branch(a, b, w0)
+            assert br[a, b] == (ob if mode != "band" or ob == 1 else 0)
+    if s > 1 or mode == "band":
+        assert int((br == 1).sum()) == sum(min(x + 1, w0) for x in range(L))
+    if mode != "band":
+        num = num.cpu().numpy()
+        for p in list(range(min(L, 300))) + [L - 1]:
+            assert num[p] == round((oracle.phi(p, s, mode) - p) * s)
+
+
+@pytest.mark.parametrize("mode", ["fi", "pa", "fi+shift", "pa+shift"])
+def test_correction_angles_against_closed_form(mode):
+    # The fp32 (cos, sin) the kernels rotate with, against the exact angle
+    # theta_m (phi(p) - p) (+ theta_m (w0 - phi(w0)) for shifted queries) in
+    # fp64, at positions up to 2^20. Prefill (fp64 angle and sincos, rounded
+    # once to fp32): within one fp32 ulp of 1 (1.2e-7). Decode (a base
+    # rotation from an fp64 reduction plus the hardware sin / cos of the fp32
+    # fraction, times a tabulated offset rotation of the same kind): each
+    # factor is within 2^-26 turn of reduction error plus 1.8e-7 of the
+    # hardware sin / cos, and the product adds about two ulp: bar 8e-7.
+    base = mode[:2]
+    shift = mode.endswith("+shift")
+    theta = 1e6
+    th = theta ** (-2.0 * np.arange(64) / 128)
+    cases = [(1048576, 4096, 32768), (131073, 4096, 32768), (8192, 256, 3000), (3000, 100, 7)]
+    worst = {}
+    for L, w0, w_pre in cases:
+        rng = np.random.default_rng(L)
+        edge = [0, 1, 15, 16, 17, 1023, 1024, 1025, L - 1, L - 2, L // 2]
+        pos = np.unique(np.clip(np.concatenate([edge, rng.integers(0, L, 117)]), 0, L - 1))[:128]
+        for which in (0, 1, 2, 3):
+            if shift and which in (1, 2):
+                continue  # keys carry no shift
+            cs = bfl.test_angles(which, pos, L, w0, w_pre, theta, mode).cpu().numpy().astype(np.float64)
+            ref = np.empty_like(cs)
+            for n, p in enumerate(pos):
+                s = oracle.s_of_L(int(p) + 1 if which == 3 else L, w_pre)
+                d = oracle.phi(int(p), s, base) - int(p)
+                if shift and which in (0, 3):
+                    d += w0 - oracle.phi(w0, s, base)
+                ang = th * d
+                ref[n, :, 0], ref[n, :, 1] = np.cos(ang), np.sin(ang)
+            err = float(np.abs(cs - ref).max())
+            worst[which] = max(worst.get(which, 0.0), err)
+            bar = 1.2e-7 if which <= 1 else 8e-7
+            assert err <= bar, (L, which, err)
+    print(f"[angles {mode}] max |fp32 - exact| by probe (0 prefill q, 1 prefill k, 2 decode k, "
+          f"3 decode q): {worst}", flush=True)
 
 
 # ---------------------------------------------------------------- prefill, fp32
