@@ -138,30 +138,99 @@ def time_calls(fn, n, stream):
     return start.elapsed_time(end) / n
 
 
-def cpu_baseline(q, k, v, L, cfg, budget_s=15.0):
-    """The fp64 oracle as it stands, on a seeded sample of query rows of the
-    same prefill workload (all heads), timed on the host cores. The sample
-    grows until one run takes at least a third of the budget."""
+def _oracle_sampled(q, k, v, cu, cfg, mode, target_s, seed, what):
+    """The oracle on seeded samples of query rows (all heads) of a packed
+    prefill workload. A small sample and a large one (grown until a run takes
+    at least target_s) separate the oracle's fixed key / value setup (rotating
+    every key up to the sampled rows) from its cost per causal pair; the
+    value is the pair rate, and the full workload's time is extrapolated as
+    setup + pairs x cost per pair."""
     import oracle
 
     kf, vf = k.float().numpy(), v.float().numpy()
-    rng = np.random.default_rng(7)
-    n_rows = 4
-    while True:
-        rows = np.sort(rng.choice(L, size=n_rows, replace=False)).astype(np.int64)
+    cu_a = np.asarray(cu)
+    T, D = cu[-1], q.shape[-1]
+    rng = np.random.default_rng(seed)
+
+    last = cu_a[1:] - 1  # every sample holds each sequence's last row: the same key setup
+
+    def run(n):
+        rows = np.unique(np.concatenate([last, rng.choice(T, size=min(n, T), replace=False)]))
+        rows = rows.astype(np.int64)
         q_rows = q[:, torch.from_numpy(rows)].float().numpy()
         t0 = time.perf_counter()
-        oracle.prefill(q_rows, kf, vf, [0, L], cfg["w0"], cfg["w_pre"], cfg["theta"], "fi",
-                       1 / math.sqrt(q.shape[-1]), rows=rows, gathered=True)
+        oracle.prefill(q_rows, kf, vf, cu, cfg["w0"], cfg["w_pre"], cfg["theta"], mode,
+                       1 / math.sqrt(D), rows=rows, gathered=True)
         dt = time.perf_counter() - t0
-        if dt >= budget_s / 3 or n_rows >= 4096:
+        seq = np.searchsorted(cu_a, rows, side="right") - 1
+        return rows, int(q.shape[0] * (rows - cu_a[seq] + 1).sum()), dt
+
+    _, pairs_a, t_a = run(16)
+    n = 48
+    while True:
+        rows, pairs_b, t_b = run(n)
+        if t_b >= target_s or n >= 4096:
             break
-        n_rows = int(min(4096, n_rows * max(2.0, budget_s / max(dt, 1e-3))))
-    pairs = int(q.shape[0] * (rows + 1).sum())
-    return {"value": round(4.0 * q.shape[-1] * pairs / dt / 1e12, 6), "unit": "TFLOP/s",
-            "cores": oracle.threads(), "kind": "oracle", "seconds": round(dt, 2),
-            "sample": f"{len(rows)} seeded query rows x {q.shape[0]} heads of the 128K FI "
-                      f"prefill workload ({pairs} causal pairs; key/value setup included)"}
+        n = int(min(4096, n * max(2.0, 1.2 * target_s / max(t_b, 1e-3))))
+    per_pair = max((t_b - t_a) / max(pairs_b - pairs_a, 1), 1e-15)
+    setup = max(t_a - per_pair * pairs_a, 0.0)
+    full_pairs = q.shape[0] * sum((cu[i + 1] - cu[i]) * (cu[i + 1] - cu[i] + 1) / 2
+                                  for i in range(len(cu) - 1))
+    return {"mode": "sampled rows, extrapolated", "value": round(4.0 * D / per_pair / 1e12, 6),
+            "unit": "TFLOP/s", "seconds": round(t_a + t_b, 2), "setup_seconds": round(setup, 2),
+            "extrapolated_full_seconds": round(setup + per_pair * full_pairs, 1),
+            "sample": f"{len(rows)} seeded query rows x {q.shape[0]} heads of {what} ({pairs_b} "
+                      f"causal pairs), after a smaller run with the same last rows that separates the key setup"}
+
+
+def cpu_baseline(q3, k3, v3, budget_s=15.0):
+    """The fp64 oracle as it stands, timed on the host cores, per workload:
+    the tiny fp32 prefill and the three decode caches in full, the 32K, 128K
+    and ragged prefills on seeded row samples (time extrapolated to the whole
+    workload). The headline value is the 128K FI prefill's."""
+    import oracle
+
+    per = {}
+    c3 = wl.CONFIGS["qwen3_8b_prefill_128k"]
+    L3 = c3["lens"][0]
+    per["qwen3_8b_prefill_128k"] = _oracle_sampled(q3, k3, v3, [0, L3], c3, "fi", budget_s * 0.35, 7,
+                                                   "the 128K FI prefill")
+    c2 = wl.CONFIGS["qwen3_1p7b_prefill_32k_s1"]
+    q2, k2, v2 = wl.prefill_inputs(c2["Hq"], c2["Hkv"], c2["lens"][0], c2["D"], "bf16", c2["seed"])
+    per["qwen3_1p7b_prefill_32k_s1"] = _oracle_sampled(q2, k2, v2, [0, c2["lens"][0]], c2, "fi",
+                                                       budget_s * 0.2, 8, "the 32K s = 1 prefill")
+    del q2, k2, v2
+    c5 = wl.CONFIGS["qwen3_4b_ragged_prefill"]
+    lens5 = wl.ragged_lengths(c5["n_seqs"], c5["len_lo"], c5["len_hi"], c5["seed"])
+    cu5 = wl.cu_seqlens(lens5)
+    q5, k5, v5 = wl.prefill_inputs(c5["Hq"], c5["Hkv"], cu5[-1], c5["D"], "bf16", c5["seed"])
+    per["qwen3_4b_ragged_prefill"] = _oracle_sampled(q5, k5, v5, cu5, c5, "fi", budget_s * 0.2, 9,
+                                                     "the ragged 8-sequence prefill")
+    del q5, k5, v5
+    c1 = wl.CONFIGS["tiny_fp32_s2"]
+    L1 = c1["lens"][0]
+    q1, k1, v1 = (x.numpy() for x in wl.prefill_inputs(c1["Hq"], c1["Hkv"], L1, c1["D"], "fp32",
+                                                       c1["seed"]))
+    t0 = time.perf_counter()
+    oracle.prefill(q1, k1, v1, [0, L1], c1["w0"], c1["w_pre"], c1["theta"], "fi",
+                   1 / math.sqrt(c1["D"]))
+    dt = time.perf_counter() - t0
+    per["tiny_fp32_s2"] = {"mode": "full", "value": round(4.0 * 128 * c1["Hq"] * L1 * (L1 + 1) / 2 / dt / 1e12, 6),
+                           "unit": "TFLOP/s", "seconds": round(dt, 3)}
+    cd = wl.CONFIGS["qwen3_8b_decode"]
+    for i, Lc in enumerate(cd["cache_lens"]):
+        N = Lc + 1
+        qd, kc, vc = (x.float().numpy() for x in wl.decode_inputs(1, cd["Hq"], cd["Hkv"], N, 128,
+                                                                  "bf16", cd["seed"] + i))
+        t0 = time.perf_counter()
+        oracle.decode(qd, kc, vc, [N], cd["w0"], cd["w_pre"], cd["theta"], "fi", 1 / math.sqrt(128))
+        dt = time.perf_counter() - t0
+        per[f"qwen3_8b_decode_{N}"] = {"mode": "full", "value": round(2.0 * N * cd["Hkv"] * 128 * 2 / dt / 1e9, 3),
+                                       "unit": "GB/s", "seconds": round(dt, 3)}
+    head = per["qwen3_8b_prefill_128k"]
+    return {"value": head["value"], "unit": "TFLOP/s", "cores": oracle.threads(), "kind": "oracle",
+            "seconds": round(sum(r["seconds"] for r in per.values()), 2),
+            "sample": head["sample"], "per_config": per}
 
 
 def main():
@@ -407,6 +476,31 @@ def main():
     ragged_flops = 4.0 * D * rcfg["Hq"] * sum(x * (x + 1) / 2 for x in rlens)
     del rq, rk, rv, ro, rws
 
+    log("32K s = 1 prefill (Qwen3-1.7B shapes) and the tiny fp32 workload")
+    c2 = wl.CONFIGS["qwen3_1p7b_prefill_32k_s1"]
+    L2 = c2["lens"][0]
+    q2, k2, v2 = (x.cuda() for x in wl.prefill_inputs(c2["Hq"], c2["Hkv"], L2, D, "bf16", c2["seed"]))
+    o2 = torch.empty_like(q2)
+    ws2 = bfl.alloc_workspace(bfl.workspace_bytes(bfl.BF_PHASE_PREFILL, 1, L2, c2["Hq"], c2["Hkv"]),
+                              "cuda")
+    f2 = lambda: bfl.prefill(q2, k2, v2, [0, L2], c2["w0"], c2["w_pre"], c2["theta"], "fi", scale,
+                             out=o2, workspace=ws2)
+    p2 = lambda: bfl.plain_prefill(q2, k2, v2, [0, L2], scale, out=o2, workspace=ws2)
+    f2()
+    p2()
+    t2 = time_calls(f2, 10, stream)
+    t2p = time_calls(p2, 10, stream)
+    flops2 = 4.0 * D * c2["Hq"] * L2 * (L2 + 1) / 2
+    del q2, k2, v2, o2, ws2
+    c1 = wl.CONFIGS["tiny_fp32_s2"]
+    L1 = c1["lens"][0]
+    q1, k1, v1 = (x.cuda() for x in wl.prefill_inputs(c1["Hq"], c1["Hkv"], L1, D, "fp32", c1["seed"]))
+    f1 = lambda: bfl.prefill(q1, k1, v1, [0, L1], c1["w0"], c1["w_pre"], c1["theta"], "fi", scale)
+    f1()
+    t1 = time_calls(f1, 20, stream)
+    flops1 = 4.0 * D * c1["Hq"] * L1 * (L1 + 1) / 2
+    del q1, k1, v1
+
     log("batched prefill: 64 x 2048 and 16 x 8192 prompts")
     batched_pre = {}
     for nb, lb in ((64, 2048), (16, 8192)):
@@ -540,6 +634,12 @@ def main():
                       "decode_gbs": round(band_dec_bytes / (band_dec_ms * 1e-3) / 1e9, 1)},
         "ragged_prefill": {"lengths": rlens, "ms": round(ragged_ms, 3),
                            "tflops": round(ragged_flops / (ragged_ms * 1e-3) / 1e12, 2)},
+        "prefill_32k_s1": {"workload": "qwen3_1p7b_prefill_32k_s1 (16/8 heads, s = 1)",
+                           "ms": round(t2, 3), "tflops": round(flops2 / (t2 * 1e-3) / 1e12, 2),
+                           "plain_ms": round(t2p, 3),
+                           "overhead_vs_plain": round(t2 / t2p - 1, 4)},
+        "tiny_fp32_s2": {"ms": round(t1, 4), "tflops": round(flops1 / (t1 * 1e-3) / 1e12, 3),
+                         "note": "parity workload (fp32 MFMA 32x32x2), not a throughput target"},
         "batched_prefill": batched_pre,
         "chunk_prefill_at_128k": chunk,
         "rope_prefill_ms": round(rope_ms, 4),
@@ -562,8 +662,8 @@ def main():
                           "traffic": traffic_for("rope_kernel")},
     }
     if not args.no_cpu_baseline:
-        log("timing the CPU oracle on a row sample")
-        result["cpu_baseline"] = cpu_baseline(q, k, v, L, cfg)
+        log("timing the CPU oracle per workload")
+        result["cpu_baseline"] = cpu_baseline(q, k, v)
     print(json.dumps(result), flush=True)
 
 
