@@ -20,8 +20,11 @@ _lib = None
 def _load():
     global _lib
     if _lib is None:
-        build(force=False)
-        lib = ctypes.CDLL(LIB)
+        path = os.environ.get("ORACLE_LIB")  # e.g. the AddressSanitizer build
+        if not path:
+            build(force=False)
+            path = LIB
+        lib = ctypes.CDLL(path)
         i64, i32, f64 = ctypes.c_int64, ctypes.c_int32, ctypes.c_double
         p = ctypes.c_void_p
         lib.oracle_s_of_L.restype = i64

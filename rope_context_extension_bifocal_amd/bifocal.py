@@ -13,7 +13,9 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libbifocal.so")
+# BIFOCAL_LIB selects another build of the same library (e.g. the
+# AddressSanitizer build of the host code for CPU-side test runs)
+LIB_PATH = os.environ.get("BIFOCAL_LIB") or os.path.join(_PKG, "libbifocal.so")
 
 BF_OK, BF_ERR_INVALID_ARG, BF_ERR_UNSUPPORTED, BF_ERR_WORKSPACE, BF_ERR_HIP = 0, -1, -2, -3, -4
 BF_DTYPE_BF16, BF_DTYPE_FP32 = 0, 1
