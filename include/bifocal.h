@@ -89,6 +89,13 @@ int64_t bifocal_s_of_L(int64_t L, int64_t w_pre);
  *   PREFILL: `tokens` = total packed tokens T = cu_seqlens[batch].
  *   DECODE:  `tokens` = the largest seqlens[b] of the call.
  * The same figure covers both the bifocal and the plain call of a phase.
+ * PREFILL holds V^T (padded per sequence to 64 keys), the corrected queries
+ * q'' and the corrected keys k'' in the input dtype: about
+ * (Hq + 2 Hkv) x T x head_dim elements, 1.5 GiB for a 131072-token bf16
+ * prefill with 32 query / 8 KV heads (k'' and q'' are formed once per call
+ * instead of on every re-read of a key tile). DECODE holds the split
+ * partials: batch x Hq x S x 520 bytes, S = max(129, ceil(tokens / 4032) + 1),
+ * 2.1 MB for one 131073-key sequence with 32 query heads.
  * Returns 0 for invalid arguments.
  */
 size_t bifocal_workspace_bytes(int32_t phase, int32_t batch, int64_t tokens, int32_t n_heads_q,
