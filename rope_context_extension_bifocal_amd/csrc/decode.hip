@@ -155,11 +155,12 @@ __device__ __forceinline__ void dec_compose(float bc, float bs, float tc, float 
   c = bc * tc - bs * ts;
   sn = bs * tc + bc * ts;
 }
-// (q_pa, r_pa) = divmod(step start, s), advanced by one 16-key step.
-__device__ __forceinline__ void dec_advance(long long& q_pa, int& r_pa, int add16_q, int add16_r,
+// (q_pa, r_pa) = divmod(step start, s), advanced by add_q s + add_r keys
+// (0 <= add_r < s).
+__device__ __forceinline__ void dec_advance(long long& q_pa, int& r_pa, int add_q, int add_r,
                                             int s_i) {
-  q_pa += add16_q;
-  r_pa += add16_r;
+  q_pa += add_q;
+  r_pa += add_r;
   if (r_pa >= s_i) {
     r_pa -= s_i;
     ++q_pa;
@@ -174,10 +175,14 @@ __device__ __forceinline__ double dec_query_base(int mode, int shift, long long 
 }
 
 // ------------------------------------------------------------------ kernels
-// Split kernel: workgroup = (batch b, KV head, split of `chunk` keys). Each of
-// the 4 waves streams its own contiguous quarter of the split in 16-key steps,
-// independently of the other waves. Both K and V go straight from HBM into
-// registers, already in the MFMA operand layouts (no LDS staging):
+// Split kernel: workgroup = (batch b, KV head, split of `chunk` keys). The 4
+// waves take the split's 16-key steps in turn (step st of wave w is the
+// split's step 4 st + w), each with its own softmax state, so the workgroup
+// reads one contiguous stream of K and one of V; otherwise the waves run
+// independently. (Each wave streaming its own quarter of the split made four
+// times as many streams and read about 3 % slower.) Both K and V go straight
+// from HBM into registers, already in the MFMA operand layouts (no LDS
+// staging):
 //   - K: lane (key n16, group g4) holds head-dim chunks 4 t + g4 (t = 0..3) of
 //     its key, the A operand of MFMA 16x16x32 for S^T = K Q^T. Both halves
 //     (m, m + 64) of every rotary pair sit in the same lane, so the correction
@@ -204,6 +209,7 @@ constexpr int kDecStep = 16;  // keys per wave step
 constexpr int kDecRing = 3;   // register slots per wave (two steps in flight)
 constexpr int kDecTRow = 66;  // padded float2 row of the offset table (conflict-free reads)
 constexpr float kDecRescaleLog2 = 8.f;
+constexpr int kDecPageRegs = 4;  // page-number registers per lane: 256 pages per split
 
 // LDS layout (bytes). Prologue / loop: Q' and Q'' [2][16][128] bf16, offset
 // table [16][66] float2, per-wave base rows [4][64] float2. After the loop the
@@ -241,35 +247,40 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p, De
   const int chunk = ds.chunk[b];
   const long long k_begin = ds.kstart[b] + (long long)sp * chunk;
   const long long k_end = min(N, k_begin + chunk);
-  const int per = chunk / kDecWaves;  // multiple of 16
-  const long long kw0 = k_begin + (long long)wave * per;
-  const long long kw1 = min(k_end, kw0 + per);
-  const int ns = kw1 > kw0 ? (int)((kw1 - kw0 + kDecStep - 1) / kDecStep) : 0;
+  const long long kw0 = k_begin, kw1 = k_end;
+  const int tsteps = kw1 > kw0 ? (int)((kw1 - kw0 + kDecStep - 1) / kDecStep) : 0;
+  const int ns = tsteps > wave ? (tsteps - wave + kDecWaves - 1) / kDecWaves : 0;  // this wave's steps
   const bool split_far = BIFOCAL && k_begin < far_lim;
 
-  // wave-local key indexing: key kw0 + jl, jl in [0, nl); byte offsets fit 32 bits
+  // split-local key indexing: key kw0 + jl, jl in [0, nl); step st of this
+  // wave starts at jl = 16 (4 st + wave); byte offsets fit 32 bits
   const int nl = ns > 0 ? (int)(kw1 - kw0) : 0;
-  const int far_l = (int)max(-1LL, min(far_lim - kw0, (long long)(per + kDecStep)));
+  auto jl_of = [&](int st) { return (st * kDecWaves + wave) * kDecStep; };
+  const int far_l = (int)max(-1LL, min(far_lim - kw0, (long long)(chunk + kDecStep)));
   // keys below kmin (the band-only window start, rounded down to kstart) are masked
-  const int lo_l = (int)max(0LL, min((long long)ds.kmin[b] - kw0, (long long)(per + kDecStep)));
+  const int lo_l = (int)max(0LL, min((long long)ds.kmin[b] - kw0, (long long)(chunk + kDecStep)));
   const char* kwb;
   const char* vwb;
-  int first_page = 0, pg = 0;
+  int first_page = 0, pg[kDecPageRegs] = {};
   if constexpr (!PAGED) {
     const uint16_t* kbase = p.kc + ((size_t)b * p.Hkv + kvh) * (size_t)p.cap * kHeadDim;
     const uint16_t* vbase = p.vc + ((size_t)b * p.Hkv + kvh) * (size_t)p.cap * kHeadDim;
     kwb = dscalar_ptr(kbase + (size_t)(ns > 0 ? kw0 : 0) * kHeadDim);
     vwb = dscalar_ptr(vbase + (size_t)(ns > 0 ? kw0 : 0) * kHeadDim);
   } else {
-    // the pages this wave's keys live in, one per lane (a wave spans at most
-    // per / 16 + 1 <= 64 pages), read once; each step picks its page by lane
+    // the pages the split's keys live in, page i of the split in lane i % 64
+    // of register i / 64 (a split spans at most 4032 / 16 + 1 = 253 pages),
+    // read once; each step picks its page by register and lane
     kwb = dscalar_ptr(p.kc);
     vwb = dscalar_ptr(p.vc);
     if (ns > 0) {
       first_page = (int)(kw0 >> p.page_log2);
       const int last_page = (int)((kw1 - 1) >> p.page_log2);
-      if (first_page + lane <= last_page)
-        pg = min(max(p.block_table[(size_t)b * p.max_pages + first_page + lane], 0), p.num_pages - 1);
+#pragma unroll
+      for (int g = 0; g < kDecPageRegs; ++g)
+        if (first_page + 64 * g + lane <= last_page)
+          pg[g] = min(max(p.block_table[(size_t)b * p.max_pages + first_page + 64 * g + lane], 0),
+                      p.num_pages - 1);
     }
   }
   const uint32_t v_lane = (uint32_t)(g4 * 4 * 256 + n16 * 16);  // key 4 g4, chunk n16
@@ -280,13 +291,19 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p, De
   // Keys are addressed from kb / vb: the wave's first key (contiguous cache)
   // or the first key of the step's page block (paged cache, rel0 = 0).
   auto issue = [&](int st, int r) {
-    const int j0 = st * kDecStep;
+    const int j0 = jl_of(st);
     const char* kb = kwb;
     const char* vb = vwb;
     int rel0 = j0;
     if constexpr (PAGED) {
       const long long key = kw0 + j0;  // a step never crosses a page (16 | page size)
-      const int page = __builtin_amdgcn_readlane(pg, (int)(key >> p.page_log2) - first_page);
+      const int pi = (int)(key >> p.page_log2) - first_page;  // wave-uniform, < 64 kDecPageRegs
+      int page = __builtin_amdgcn_readlane(pg[0], pi & 63);
+#pragma unroll
+      for (int g = 1; g < kDecPageRegs; ++g) {
+        const int pgg = __builtin_amdgcn_readlane(pg[g], pi & 63);
+        page = (pi >> 6) == g ? pgg : page;
+      }
       const size_t row = (((size_t)page * p.Hkv + kvh) << p.page_log2) +
                          (size_t)(key & ((1LL << p.page_log2) - 1));
       kb = dscalar_ptr((const char*)p.kc + row * (kHeadDim * 2));
@@ -364,14 +381,16 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p, De
   const double inv_s = 1.0 / (double)s;
   const float inv_s_f = 1.f / (float)s_i;
   const double th_turn = th_lane * kInv2Pi;  // this lane's pair m = lane
-  // (q_pa, r_pa) = divmod(step start, s), advanced by 16 keys per step
+  // (q_pa, r_pa) = divmod(step start, s), advanced by 64 keys per step of this wave
   long long q_pa = 0;
   int r_pa = 0;
   if (BIFOCAL) {
-    q_pa = kw0 / s;
-    r_pa = (int)(kw0 - q_pa * s);
+    const long long k0 = kw0 + (long long)wave * kDecStep;  // this wave's first step
+    q_pa = k0 / s;
+    r_pa = (int)(k0 - q_pa * s);
   }
-  const int add16_q = 16 / s_i, add16_r = 16 % s_i;
+  constexpr int kAdv = kDecStep * kDecWaves;  // keys from one of this wave's steps to the next
+  const int adv_q = kAdv / s_i, adv_r = kAdv % s_i;
 
   float m_used = -INFINITY, l_part = 0.f;
   df32x4 oacc[8];
@@ -379,7 +398,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p, De
   for (int db = 0; db < 8; ++db) oacc[db] = df32x4{};
 
   auto process = [&](int st, int r) {
-    const int jbl = st * kDecStep;  // wave-local first key of the step
+    const int jbl = jl_of(st);  // split-local first key of the step
     const bool any_far = BIFOCAL && jbl < far_l;
     const bool any_loc = !BIFOCAL || jbl + kDecStep - 1 >= far_l;
     uint4* kr = kreg[r];  // rotated in place
@@ -422,7 +441,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p, De
         }
       }
     }
-    if (BIFOCAL) dec_advance(q_pa, r_pa, add16_q, add16_r, s_i);
+    if (BIFOCAL) dec_advance(q_pa, r_pa, adv_q, adv_r, s_i);
     dbf16x8 qs[4];
     q_operand(any_far, qs);
     df32x4 S = df32x4{};
@@ -632,9 +651,10 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p, Dec
 // ------------------------------------------------------------------ test hook
 // The fp32 cos / sin the split kernel rotates with, for given positions:
 // which = 2: the key at a.pos[n] of a call with s = a.s[n], through the
-//   kernel's own angle addition (a wave whose first key is the multiple of
-//   1024 below the key, the per-step divmod tracking, the step's base
-//   rotation, the offset-table row and the product of the two);
+//   kernel's own angle addition (a split whose first key is the multiple of
+//   1024 below the key, the divmod tracking of the wave that takes the key's
+//   step, the step's base rotation, the offset-table row and the product of
+//   the two);
 // which = 3: the query at a.pos[n] (N = pos + 1 keys, s = a.s[n]).
 // Block = position, thread = rotary pair; cs [n][64][2].
 __global__ __launch_bounds__(64) void decode_angle_kernel(AngleProbe a, ThetaTable tt, int which,
@@ -647,9 +667,11 @@ __global__ __launch_bounds__(64) void decode_angle_kernel(AngleProbe a, ThetaTab
     turn_cos_sin(tt.th[m] * kInv2Pi * dec_query_base(a.mode, a.shift, pos + 1, s, a.w0), c, sn);
   } else {
     const long long kw0 = (pos / 1024) * 1024, jb = pos & ~15LL;
-    long long q_pa = kw0 / s;
-    int r_pa = (int)(kw0 - q_pa * s);
-    for (long long j = kw0; j < jb; j += kDecStep) dec_advance(q_pa, r_pa, 16 / s_i, 16 % s_i, s_i);
+    const long long k0 = kw0 + (jb - kw0) / kDecStep % kDecWaves * kDecStep;  // the wave's first step
+    long long q_pa = k0 / s;
+    int r_pa = (int)(k0 - q_pa * s);
+    constexpr int kAdv = kDecStep * kDecWaves;
+    for (long long j = k0; j < jb; j += kAdv) dec_advance(q_pa, r_pa, kAdv / s_i, kAdv % s_i, s_i);
     float cb, sb, tc, ts;
     turn_cos_sin(tt.th[m] * kInv2Pi * dec_step_base(a.mode, q_pa, jb, s, 1.0 / (double)s), cb, sb);
     const int idx = dec_offset_row(a.mode, r_pa, (int)(pos - jb), s_i, 1.f / (float)s_i);
@@ -690,6 +712,8 @@ constexpr long long kDecMaxTargetSplits = 128;
 constexpr long long kDecMinChunk = 256;  // fewer keys per split cost more than they save
 constexpr long long kDecWgCost = 256;    // fixed cost of a split workgroup, in keys
 static_assert(kDecMaxChunk % kDecBlock == 0, "chunk must be a multiple of 64 keys");
+static_assert(kDecMaxChunk / 16 + 1 <= 64 * kDecPageRegs,
+              "a split's pages of 16 keys must fit the kernel's page-number registers");
 
 static long long decode_target_splits(int batch, int Hkv) {
   return (long long)batch * Hkv;  // (sequence, KV head) groups sharing the launch

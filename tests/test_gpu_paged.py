@@ -98,8 +98,8 @@ def test_paged_validation():
 
 def test_paged_longest_wave_span():
     # 64 sequences x 8 KV heads of 16128 keys make the split rule choose
-    # 4032-key chunks: each wave's 1008 keys span 63 pages of 16, close to the
-    # 64 page numbers a wave holds in its lanes
+    # 4032-key chunks: each split's keys span 252 pages of 16, close to the
+    # 256 page numbers a wave holds (four registers of 64 lanes)
     B, Hq, Hkv, N, page = 64, 8, 8, 16128, 16
     q, kc, vc = wl.decode_inputs(B, Hq, Hkv, N, 128, "bf16", 103)
     q, kc, vc = q.cuda(), kc.cuda(), vc.cuda()
