@@ -17,6 +17,7 @@
 
 #include <mutex>
 #include <string>
+#include <type_traits>
 
 #include "bifocal.h"
 #include "bf_common.h"
@@ -191,7 +192,9 @@ __device__ __forceinline__ double dec_query_base(int mode, int shift, long long 
 //     4 g4 + q (q = 0..3); each quarter-wave reads whole 256-byte rows. P V
 //     uses the head-dim order d = 8 row + block, so these four registers feed
 //     the 8 MFMA 16x16x16 of the step after byte permutes only;
-//   - loads run two steps ahead of compute (three register slots).
+//   - three register slots: a step's K is reloaded with the step three
+//     ahead as soon as QK^T has read it, its V after P V, so two to three
+//     steps are in flight.
 // The G query heads of the KV group are the MFMA columns (columns >= G are
 // zero queries whose results are dropped).
 //
@@ -206,7 +209,7 @@ __device__ __forceinline__ double dec_query_base(int mode, int shift, long long 
 // the two (cos / sin addition formulas).
 constexpr int kDecWaves = 4;
 constexpr int kDecStep = 16;  // keys per wave step
-constexpr int kDecRing = 3;   // register slots per wave (two steps in flight)
+constexpr int kDecRing = 3;   // register slots per wave
 constexpr int kDecTRow = 66;  // padded float2 row of the offset table (conflict-free reads)
 constexpr float kDecRescaleLog2 = 8.f;
 constexpr int kDecPageRegs = 4;  // page-number registers per lane: 256 pages per split
@@ -283,14 +286,14 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p, De
                       p.num_pages - 1);
     }
   }
-  const uint32_t v_lane = (uint32_t)(g4 * 4 * 256 + n16 * 16);  // key 4 g4, chunk n16
-  const uint32_t k_lane = (uint32_t)(n16 * 256 + g4 * 16);      // key n16, chunk g4
   uint4 kreg[kDecRing][4], vreg[kDecRing][4];
   // issue the loads of step st into register slot r, K first (needed first);
   // rows past the wave's last key re-read that key (their scores are masked).
   // Keys are addressed from kb / vb: the wave's first key (contiguous cache)
   // or the first key of the step's page block (paged cache, rel0 = 0).
-  auto issue = [&](int st, int r) {
+  // (KV = 0: K, 1: V)
+  auto issue_half = [&](int st, int r, auto kv) {
+    constexpr int KV = decltype(kv)::value;
     const int j0 = jl_of(st);
     const char* kb = kwb;
     const char* vb = vwb;
@@ -310,16 +313,13 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p, De
       vb = dscalar_ptr((const char*)p.vc + row * (kHeadDim * 2));
       rel0 = 0;
     }
-    if (j0 + kDecStep <= nl) {
-      const uint32_t base = (uint32_t)rel0 * (kHeadDim * 2);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) kreg[r][t] = kvload16<NT>(kb, base + k_lane + t * 64);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) vreg[r][q] = kvload16<NT>(vb, base + v_lane + q * 256);
-    } else {
+    // rows are clamped to the last key (a no-op except in the split's last
+    // step), without a branch, so that every step issues the same loads
+    if constexpr (KV == 0) {
       const uint32_t kk = (uint32_t)(min(j0 + n16, nl - 1) - j0 + rel0);
 #pragma unroll
       for (int t = 0; t < 4; ++t) kreg[r][t] = kvload16<NT>(kb, kk * (kHeadDim * 2) + (4 * t + g4) * 16);
+    } else {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const uint32_t kv = (uint32_t)(min(j0 + 4 * g4 + q, nl - 1) - j0 + rel0);
@@ -327,9 +327,15 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p, De
       }
     }
   };
+  using KHalf = std::integral_constant<int, 0>;
+  using VHalf = std::integral_constant<int, 1>;
+  auto issue = [&](int st, int r) {
+    issue_half(st, r, KHalf{});
+    issue_half(st, r, VHalf{});
+  };
 
   // the query row and this lane's theta (every loop below over pairs has
-  // m = lane) are loaded first, then the first two steps' K / V loads go out
+  // m = lane) are loaded first, then the first three steps' K / V loads go out
   // before the prologue that needs them
   const double th_lane = BIFOCAL ? tt.th[lane] : 0.0;
   {
@@ -338,6 +344,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p, De
     if (qi < p.G) v0 = gload16((const char*)p.q, (uint32_t)((((size_t)b * p.Hq + kvh * p.G + qi) * kHeadDim + c * 8) * 2));
     if (ns > 0) issue(0, 0);
     if (ns > 1) issue(1, 1);
+    if (ns > 2) issue(2, 2);
     sQ[qi * 16 + c] = v0;
     sQ[kDecMaxG * 16 + qi * 16 + c] = v0;
   }
@@ -397,7 +404,12 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p, De
 #pragma unroll
   for (int db = 0; db < 8; ++db) oacc[db] = df32x4{};
 
-  auto process = [&](int st, int r) {
+  // process step st from register slot r; REFILL 1: then load step st + 3
+  // into the same slot (K as soon as QK^T has read it, V after P V),
+  // REFILL 2: the same if step st + 3 exists
+  auto process = [&](int st, int r, auto refill) {
+    constexpr int REFILL = decltype(refill)::value;
+    const bool more = REFILL == 1 || (REFILL == 2 && st + kDecRing < ns);
     const int jbl = jl_of(st);  // split-local first key of the step
     const bool any_far = BIFOCAL && jbl < far_l;
     const bool any_loc = !BIFOCAL || jbl + kDecStep - 1 >= far_l;
@@ -448,6 +460,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p, De
 #pragma unroll
     for (int t = 0; t < 4; ++t)
       S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(dbf16x8, kr[t]), qs[t], S, 0, 0, 0);
+    if (REFILL != 0 && more) issue_half(st + kDecRing, r, KHalf{});
     if (any_far && any_loc) {
 #pragma unroll
       for (int q = 0; q < 4; ++q)
@@ -497,26 +510,24 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p, De
       oacc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
           __builtin_bit_cast(ds16x4, make_uint2(x01, x23)), pb, oacc[db], 0, 0, 0);
     }
+    if (REFILL != 0 && more) issue_half(st + kDecRing, r, VHalf{});
   };
 
-  // steady state: every step issues the step two ahead (no branches, so the
-  // compiler's load-counter waits stay exact); the last steps drain
+  // steady state: every step refills its own slot with the step three ahead
+  // (no branches, so the compiler's load-counter waits stay exact); the last
+  // steps drain
+  using Refill = std::integral_constant<int, 1>;
+  using RefillIfAny = std::integral_constant<int, 2>;
   int st = 0;
-  for (; st + 5 <= ns; st += kDecRing) {
-    issue(st + 2, 2);
-    process(st, 0);
-    issue(st + 3, 0);
-    process(st + 1, 1);
-    issue(st + 4, 1);
-    process(st + 2, 2);
+  for (; st + 2 * kDecRing <= ns; st += kDecRing) {
+    process(st, 0, Refill{});
+    process(st + 1, 1, Refill{});
+    process(st + 2, 2, Refill{});
   }
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
+  for (int u = 0; u < 2 * kDecRing - 1; ++u) {
     const int cur = st + u;
-    if (cur < ns) {
-      if (cur + 2 < ns) issue(cur + 2, (u + 2) % kDecRing);
-      process(cur, u % kDecRing);
-    }
+    if (cur < ns) process(cur, u % kDecRing, RefillIfAny{});
   }
 
   // ---- merge the 4 waves, write the split's partial
