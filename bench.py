@@ -400,8 +400,21 @@ def main():
     paged_ms = time_calls(pfn, 50, stream)
     del kpg, vpg
 
+    def stored_us(qx, kx, vx, n, ws_x, calls=100):
+        """Decode with a far-key store (bifocal_decode_stored) once the store
+        holds the far keys: the steady state of a decode loop at one s."""
+        store = bfl.DecodeStore(kx)
+        fn = lambda: bfl.decode_stored(qx, kx, vx, store, [n], dcfg["w0"], dcfg["w_pre"],
+                                       dcfg["theta"], "fi", scale, workspace=ws_x)
+        for _ in range(10):
+            fn()
+        t = time_calls(fn, calls, stream)
+        del store
+        return t * 1e3
+
     MALL = 256 * 1024 * 1024
     dec_cold_us = cold_us(qdc, kc, vc, N, ws_d, max(2, math.ceil(2 * MALL / kv_bytes)))
+    dec_stored_us = stored_us(qdc, kc, vc, N, ws_d)
     small = {}
     for Lc in dcfg["cache_lens"][:2]:
         n = Lc + 1
@@ -417,7 +430,9 @@ def main():
         t_p = time_calls(pfn, 100, stream)
         nbytes = 2.0 * n * Hkv * D * 2
         t_c = cold_us(qs, ks, vs, n, ws_s, max(2, math.ceil(2 * MALL / nbytes))) * 1e-3
+        t_s = stored_us(qs, ks, vs, n, ws_s) * 1e-3
         small[str(n)] = {"bifocal_us": round(t_b * 1e3, 2), "plain_us": round(t_p * 1e3, 2),
+                         "stored_us": round(t_s * 1e3, 2),
                          "bifocal_gbs": round(nbytes / (t_b * 1e-3) / 1e9, 1),
                          "bifocal_cold_us": round(t_c * 1e3, 2),
                          "bifocal_cold_gbs": round(nbytes / (t_c * 1e-3) / 1e9, 1)}
@@ -626,6 +641,9 @@ def main():
         "decode_cold_gbs": round(kv_bytes / (dec_cold_us * 1e-6) / 1e9, 1),
         "plain_decode_us": round(plain_dec_ms * 1e3, 2),
         "decode_overhead_vs_plain": round(dec_many_ms / plain_dec_ms - 1, 4),
+        "decode_stored_us": round(dec_stored_us, 2),
+        "decode_stored_gbs": round(kv_bytes / (dec_stored_us * 1e-6) / 1e9, 1),
+        "decode_stored_overhead_vs_plain": round(dec_stored_us / (plain_dec_ms * 1e3) - 1, 4),
         "decode_small": small,
         "decode_batched_cold": batched,
         "band_only": {"prefill_ms": round(band_ms, 3),

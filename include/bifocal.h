@@ -234,6 +234,40 @@ int bifocal_decode(const void* q, const void* k_cache, const void* v_cache, void
                    float softmax_scale, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * bifocal_decode with a caller-kept store of corrected far keys, so that a
+ * decode step rotates only the keys that became far since the store was
+ * filled. The correction of key j, R(theta_m (phi(j) - j)), depends on j and
+ * s alone, and s = s(N_b) stays the same over w_pre steps, so k'' of a far
+ * key can be kept between steps [ai-feeds.com summary, "关键模块" item 3: the
+ * correction rotation of cached keys; item 2: s from the length].
+ *   k2_store         : [batch, n_heads_kv, cache_capacity, head_dim] bf16,
+ *                      device, caller-owned, the layout of k_cache
+ *   store_keys_host  : host int32 [batch], in/out: keys 0 .. P_b - 1 of
+ *                      sequence b in k2_store hold k'' for s = store_s_host[b]
+ *   store_s_host     : host int32 [batch], in/out (start both at 0)
+ * Other arguments as bifocal_decode, long_mode FI or PA (with or without
+ * BF_LONG_SHIFT); band-only (BF_LONG_NONE) returns BF_ERR_UNSUPPORTED.
+ * If store_s_host[b] != s(N_b) the store of sequence b is treated as empty.
+ * Far keys below min(P_b, N_b - w0), rounded down to a multiple of 16, are
+ * read from k2_store; every other far key is rotated from k_cache and its k''
+ * written to k2_store. When the call has been queued it sets
+ * store_keys_host[b] = max(0, N_b - w0) (0 when s = 1) and store_s_host[b] =
+ * s(N_b): the store as the stream leaves the call. The result is bitwise that
+ * of bifocal_decode (the stored k'' are the values it forms on the fly). The
+ * store belongs to one cache, long_mode and rope_theta: after rewriting cache
+ * positions below P_b (a rollback), lower store_keys_host[b] to the first
+ * rewritten position; after changing the mode or rope_theta, set it to 0.
+ * Validation errors leave outputs and both host arrays untouched.
+ */
+int bifocal_decode_stored(const void* q, const void* k_cache, const void* v_cache, void* k2_store,
+                          void* o, float* lse, const int32_t* seqlens_host, int32_t* store_keys_host,
+                          int32_t* store_s_host, int32_t batch, int32_t cache_capacity,
+                          int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim, int32_t dtype,
+                          int64_t w0, int64_t w_pre, double rope_theta, int32_t long_mode,
+                          float softmax_scale, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/*
  * bifocal_decode without a workspace, for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops, harnesses
  * that forbid allocation). Same arguments, layouts, result (bitwise) and

@@ -31,7 +31,7 @@ EXPORTED = ("bifocal_s_of_L", "bifocal_workspace_bytes", "bifocal_prefill", "bif
             "bifocal_decode_paged", "plain_attention_ref_gpu", "bifocal_rope_prefill", "bifocal_rope_append",
             "bifocal_rope_prefill_paged", "bifocal_rope_append_paged",
             "bifocal_test_pair_map", "bifocal_last_error", "bifocal_decode_noalloc",
-            "bifocal_test_angles")
+            "bifocal_test_angles", "bifocal_decode_stored")
 
 _lib = None
 
@@ -70,6 +70,9 @@ def lib():
         L.bifocal_decode.restype = ctypes.c_int
         L.bifocal_decode.argtypes = [p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, i64, i64,
                                      f64, i32, f32, p, sz, p]
+        L.bifocal_decode_stored.restype = ctypes.c_int
+        L.bifocal_decode_stored.argtypes = [p, p, p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32,
+                                            i64, i64, f64, i32, f32, p, sz, p]
         L.bifocal_decode_noalloc.restype = ctypes.c_int
         L.bifocal_decode_noalloc.argtypes = [p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, i64,
                                              i64, f64, i32, f32, p]
@@ -260,6 +263,46 @@ def decode(q, k_cache, v_cache, seqlens, w0, w_pre, rope_theta, long_mode="fi",
                                 float(rope_theta), LONG_MODES[long_mode],
                                 _scale(softmax_scale, D), _ptr(workspace), workspace.numel(),
                                 _stream(stream)))
+    return (o, lse) if return_lse else o
+
+
+class DecodeStore:
+    """Caller-kept state of decode_stored for one contiguous cache [B,Hkv,cap,D]:
+    the far-key store k2 (same shape, bf16) and, per sequence, how many keys
+    it holds (keys) and for which s (s). The library updates keys and s."""
+
+    def __init__(self, k_cache):
+        self.k2 = torch.empty_like(k_cache)
+        B = k_cache.shape[0]
+        self.keys = (ctypes.c_int32 * B)()
+        self.s = (ctypes.c_int32 * B)()
+
+    def reset(self, b=None, keys=0):
+        """Forget stored keys from `keys` on (all sequences, or sequence b),
+        e.g. after rewriting cache positions from `keys` on."""
+        for i in (range(len(self.keys)) if b is None else [b]):
+            self.keys[i] = min(self.keys[i], int(keys))
+
+
+def decode_stored(q, k_cache, v_cache, store, seqlens, w0, w_pre, rope_theta, long_mode="fi",
+                  softmax_scale=None, return_lse=False, out=None, lse=None, workspace=None,
+                  stream=None):
+    """bifocal_decode reading the k'' of far keys from a DecodeStore and
+    adding the ones it forms; bitwise the result of decode()."""
+    B, Hq, D = q.shape
+    Hkv, cap = k_cache.shape[1], k_cache.shape[2]
+    o = out if out is not None else torch.empty_like(q)
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = alloc_workspace(workspace_bytes(BF_PHASE_DECODE, B, max(seqlens), Hq, Hkv, D,
+                                                    q.dtype), q.device)
+    sl = _i32_array(seqlens)
+    _check(lib().bifocal_decode_stored(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(store.k2), _ptr(o),
+                                       _ptr(lse), sl, store.keys, store.s, B, cap, Hq, Hkv, D,
+                                       _DTYPES[q.dtype], int(w0), int(w_pre), float(rope_theta),
+                                       LONG_MODES[long_mode], _scale(softmax_scale, D),
+                                       _ptr(workspace), workspace.numel(), _stream(stream)))
     return (o, lse) if return_lse else o
 
 

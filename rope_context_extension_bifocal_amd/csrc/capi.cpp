@@ -40,11 +40,16 @@ struct PagedCache {
   int max_pages;
   int num_pages;
 };
+struct DecodeStore {
+  void* k2;
+  int32_t* keys;
+  int32_t* s;
+};
 int run_decode(bool bifocal, const void* q, const void* kc, const void* vc, void* o, float* lse,
                const int32_t* seqlens, int batch, int cap, int Hq, int Hkv, long long w0,
                long long w_pre, double theta, int mode, float scale, void* ws, size_t ws_bytes,
                hipStream_t stream, std::string& err, long long window, const PagedCache* paged,
-               bool validate_only = false);
+               bool validate_only = false, const DecodeStore* store = nullptr);
 int run_rope_prefill(const void* q, const void* k, const void* v, void* q_out, void* k_out,
                      void* k_cache, void* v_cache, int cap, const int32_t* cu, const int32_t* pos0,
                      const PagedKV& pk, int batch, int Hq, int Hkv, int dtype, double theta,
@@ -713,6 +718,29 @@ int bifocal_decode_noalloc(const void* q, const void* k_cache, const void* v_cac
   rc = bf::run_decode(!band_only, q, k_cache, v_cache, o, lse, seqlens_host, batch, cache_capacity,
                       n_heads_q, n_heads_kv, w0, w_pre, rope_theta, long_mode, softmax_scale, ws, cap,
                       (hipStream_t)stream, err, band_only ? w0 : 0, nullptr);
+  if (rc) return fail(rc, "%s", err.c_str());
+  g_err.clear();
+  return BF_OK;
+}
+
+int bifocal_decode_stored(const void* q, const void* k_cache, const void* v_cache, void* k2_store,
+                          void* o, float* lse, const int32_t* seqlens_host, int32_t* store_keys_host,
+                          int32_t* store_s_host, int32_t batch, int32_t cache_capacity,
+                          int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim, int32_t dtype,
+                          int64_t w0, int64_t w_pre, double rope_theta, int32_t long_mode,
+                          float softmax_scale, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  int rc = check_common(n_heads_q, n_heads_kv, head_dim, dtype);
+  if (rc) return rc;
+  if ((rc = check_bifocal_knobs(w0, w_pre, rope_theta, long_mode))) return rc;
+  if (dtype != BF_DTYPE_BF16) return fail(BF_ERR_UNSUPPORTED, "decode supports bf16 only");
+  if (long_mode == BF_LONG_NONE)
+    return fail(BF_ERR_UNSUPPORTED, "band-only decode has no far keys to store (use bifocal_decode)");
+  const bf::DecodeStore st{k2_store, store_keys_host, store_s_host};
+  std::string err;
+  rc = bf::run_decode(true, q, k_cache, v_cache, o, lse, seqlens_host, batch, cache_capacity,
+                      n_heads_q, n_heads_kv, w0, w_pre, rope_theta, long_mode, softmax_scale,
+                      workspace, workspace_bytes, (hipStream_t)stream, err, 0, nullptr, false, &st);
   if (rc) return fail(rc, "%s", err.c_str());
   g_err.clear();
   return BF_OK;

@@ -15,6 +15,7 @@
 // decode_combine_kernel: log-sum-exp merge of the splits of each query head.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <mutex>
 #include <string>
 #include <type_traits>
@@ -37,6 +38,7 @@ struct DecodeParams {
   const uint16_t* q;    // [B][Hq][D]
   const uint16_t* kc;   // [B][Hkv][cap][D], or pages [num_pages][Hkv][page][D]
   const uint16_t* vc;   // same layout as kc
+  uint16_t* k2;         // far-key store (contiguous cache only): k'' of each far key, layout of kc
   const int* block_table;  // paged cache: [B][max_pages] page of each page-sized key block
   float* part_m;        // [B][Hq][S]  running max (log2 domain, scaled)
   float* part_l;        // [B][Hq][S]
@@ -62,6 +64,7 @@ struct DecodeSeqs {
   int chunk[kMaxSeqPerLaunch];   // keys per split (multiple of 64)
   int kstart[kMaxSeqPerLaunch];  // first key read, a multiple of 16 (steps never cross a page)
   int kmin[kMaxSeqPerLaunch];    // first key that counts: 0, or N - w0 for band-only attention
+  int stored[kMaxSeqPerLaunch];  // far-key store: keys 0 .. stored - 1 hold k'' (a multiple of 16)
 };
 
 __device__ __forceinline__ float dbf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
@@ -231,9 +234,14 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <bool BIFOCAL, bool PAGED, bool NT>
+// STORE (bifocal, contiguous cache): the far keys below ds.stored[b] are read
+// as k'' from p.k2 and used as loaded; every other far key is rotated as
+// usual and its k'' written to p.k2, so after the call p.k2 holds k'' of all
+// far keys (a later call with the same s reads them back).
+template <bool BIFOCAL, bool PAGED, bool NT, bool STORE = false>
 __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p, DecodeSeqs ds,
                                                               ThetaTable tt) {
+  static_assert(!STORE || (BIFOCAL && !PAGED), "the far-key store serves the bifocal contiguous cache");
   __shared__ uint4 smem[kDecLds / 16];
   uint4* sQ = smem + kDecLdsQ / 16;
 
@@ -264,12 +272,16 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p, De
   const int lo_l = (int)max(0LL, min((long long)ds.kmin[b] - kw0, (long long)(chunk + kDecStep)));
   const char* kwb;
   const char* vwb;
+  char* k2wb = nullptr;  // far-key store at the split's first key (STORE)
+  // steps with jl + 16 <= st_l read k'' from the store (STORE)
+  const int st_l = STORE ? (int)max(0LL, min((long long)ds.stored[b] - kw0, (long long)(chunk + kDecStep))) : 0;
   int first_page = 0, pg[kDecPageRegs] = {};
   if constexpr (!PAGED) {
-    const uint16_t* kbase = p.kc + ((size_t)b * p.Hkv + kvh) * (size_t)p.cap * kHeadDim;
-    const uint16_t* vbase = p.vc + ((size_t)b * p.Hkv + kvh) * (size_t)p.cap * kHeadDim;
-    kwb = dscalar_ptr(kbase + (size_t)(ns > 0 ? kw0 : 0) * kHeadDim);
-    vwb = dscalar_ptr(vbase + (size_t)(ns > 0 ? kw0 : 0) * kHeadDim);
+    const size_t hoff = ((size_t)b * p.Hkv + kvh) * (size_t)p.cap * kHeadDim;
+    const size_t koff = (size_t)(ns > 0 ? kw0 : 0) * kHeadDim;
+    kwb = dscalar_ptr(p.kc + hoff + koff);
+    vwb = dscalar_ptr(p.vc + hoff + koff);
+    if constexpr (STORE) k2wb = (char*)dscalar_ptr(p.k2 + hoff + koff);
   } else {
     // the pages the split's keys live in, page i of the split in lane i % 64
     // of register i / 64 (a split spans at most 4032 / 16 + 1 = 253 pages),
@@ -295,7 +307,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p, De
   auto issue_half = [&](int st, int r, auto kv) {
     constexpr int KV = decltype(kv)::value;
     const int j0 = jl_of(st);
-    const char* kb = kwb;
+    const char* kb = (STORE && j0 + kDecStep <= st_l) ? (const char*)k2wb : kwb;
     const char* vb = vwb;
     int rel0 = j0;
     if constexpr (PAGED) {
@@ -350,7 +362,10 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p, De
   }
   float2* sT = (float2*)((char*)smem + kDecLdsT);
   float2* sBw = (float2*)((char*)smem + kDecLdsB) + wave * kPairs;
-  if (split_far) {
+  // the offset table serves the far keys this split rotates (with a store:
+  // those at or above its stored count)
+  const bool rotates = split_far && (!STORE || min(k_end, far_lim) - kw0 > (long long)st_l);
+  if (rotates) {
     // offset table: row idx, pair m = rotation by -theta_m * idx * kappa
     const double kappa = p.mode == 1 ? 1.0 : (double)(s - 1) / (double)s;
     for (int e = tid; e < kDecStep * kPairs; e += 256) {  // pair m = e % 64 = lane
@@ -422,7 +437,8 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p, De
       for (int t = 0; t < 4; ++t)
         Sl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(dbf16x8, kr[t]), ql[t], Sl, 0, 0, 0);
     }
-    if (any_far) {
+    const bool stored = STORE && jbl + kDecStep <= st_l;  // k'' read from the store
+    if (any_far && !stored) {
       // base rotation of the step, pair m = lane
       const long long jb = kw0 + jbl;
       const double qb = dec_step_base(p.mode, q_pa, jb, s, inv_s);
@@ -449,6 +465,15 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p, De
             uint32_t yo;
             lo[w] = rot_word(lo[w], hi[w], c0, s0, c1, s1, yo);
             hi[w] = yo;
+          }
+        }
+        if constexpr (STORE) {  // this lane's key is far: keep its k'' (rows as loaded)
+          if (jbl + n16 < nl) {
+            const uint32_t row = (uint32_t)(jbl + n16) * (kHeadDim * 2);
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+              *(__attribute__((address_space(1))) du32x4*)(k2wb + row + (4 * t + g4) * 16) =
+                  __builtin_bit_cast(du32x4, kr[t]);
           }
         }
       }
@@ -793,8 +818,15 @@ struct PagedCache {
   int max_pages;           // row length of block_table
   int num_pages;           // pages in the pool
 };
-static_assert(BF_DEC_MAX_CHUNK / kDecWaves / kDecStep + 1 <= 64,
-              "a wave's keys must span at most 64 pages of 16 keys");
+
+// A caller-kept far-key store (bifocal_decode_stored): k2 has the layout of
+// the contiguous cache; keys 0 .. keys[b] - 1 of sequence b hold k'' for
+// s = s[b]. Both host arrays are updated when the launch has been queued.
+struct DecodeStore {
+  void* k2;
+  int32_t* keys;
+  int32_t* s;
+};
 
 // ------------------------------------------------------------------ allocation-free decode
 // Scratch for bifocal_decode_noalloc: the split partials (m, l, acc) live in
@@ -861,9 +893,20 @@ int run_decode(bool bifocal, const void* q, const void* kc, const void* vc, void
                const int32_t* seqlens, int batch, int cap, int Hq, int Hkv, long long w0,
                long long w_pre, double theta, int mode, float scale, void* ws, size_t ws_bytes,
                hipStream_t stream, std::string& err, long long window, const PagedCache* paged,
-               bool validate_only) {
+               bool validate_only, const DecodeStore* store) {
   auto bad = [&](int code, const std::string& m) { err = m; return code; };
   if (!q || !kc || !vc || !o || !seqlens) return bad(BF_ERR_INVALID_ARG, "null tensor or seqlens pointer");
+  if (store) {
+    if (paged || !bifocal || window > 0)
+      return bad(BF_ERR_UNSUPPORTED, "the far-key store serves FI / PA decode over a contiguous cache");
+    if (!store->k2 || ((uintptr_t)store->k2 & 15u))
+      return bad(BF_ERR_INVALID_ARG, "k2_store must be a non-null 16-byte aligned device pointer");
+    if (!store->keys || !store->s) return bad(BF_ERR_INVALID_ARG, "null store_keys or store_s pointer");
+    for (int b = 0; b < batch; ++b)
+      if (store->keys[b] < 0 || store->s[b] < 0)
+        return bad(BF_ERR_INVALID_ARG, "store_keys[" + std::to_string(b) + "] and store_s[" +
+                                           std::to_string(b) + "] must be >= 0");
+  }
   int page_log2 = 0;
   if (paged) {
     if (!paged->block_table || ((uintptr_t)paged->block_table & 3u))
@@ -943,6 +986,12 @@ int run_decode(bool bifocal, const void* q, const void* kc, const void* vc, void
       ds.chunk[i] = decode_chunk(N - k0, target);
       ds.nsplit[i] = decode_splits(N - k0, target);
       if (ds.nsplit[i] > max_split) max_split = ds.nsplit[i];
+      // far keys are 0 .. N - w0 - 1 (none when s = 1); the store's k'' count
+      // only when it was made with this s, rounded down to whole 16-key steps
+      const long long far_n = ds.s[i] > 1 && N > w0 ? N - w0 : 0;
+      ds.stored[i] = 0;
+      if (store && store->s[b0 + i] == ds.s[i])
+        ds.stored[i] = (int)(std::min<long long>(store->keys[b0 + i], far_n) & ~15LL);
       kv_bytes += (N - k0) * Hkv * kHeadDim * 2 * 2;
     }
     dp.q = (const uint16_t*)q + (size_t)b0 * Hq * kHeadDim;
@@ -950,6 +999,7 @@ int run_decode(bool bifocal, const void* q, const void* kc, const void* vc, void
     // the block table from the launch's first sequence on
     dp.kc = (const uint16_t*)kc + (paged ? 0 : (size_t)b0 * Hkv * cap * kHeadDim);
     dp.vc = (const uint16_t*)vc + (paged ? 0 : (size_t)b0 * Hkv * cap * kHeadDim);
+    dp.k2 = store ? (uint16_t*)store->k2 + (size_t)b0 * Hkv * cap * kHeadDim : nullptr;
     if (paged) dp.block_table = paged->block_table + (size_t)b0 * paged->max_pages;
     dp.o = (uint16_t*)o + (size_t)b0 * Hq * kHeadDim;
     dp.lse = lse ? lse + (size_t)b0 * Hq : nullptr;
@@ -963,7 +1013,8 @@ int run_decode(bool bifocal, const void* q, const void* kc, const void* vc, void
     // non-temporal K / V loads unless the launch reads little enough that
     // its cache could stay resident in the 256 MB MALL between calls
     const bool nt = kv_bytes >= kDecStreamBytes;
-    auto kern = bifocal ? (paged ? (nt ? decode_split_kernel<true, true, true> : decode_split_kernel<true, true, false>)
+    auto kern = store ? (nt ? decode_split_kernel<true, false, true, true> : decode_split_kernel<true, false, false, true>)
+              : bifocal ? (paged ? (nt ? decode_split_kernel<true, true, true> : decode_split_kernel<true, true, false>)
                                  : (nt ? decode_split_kernel<true, false, true> : decode_split_kernel<true, false, false>))
                         : (paged ? (nt ? decode_split_kernel<false, true, true> : decode_split_kernel<false, true, false>)
                                  : (nt ? decode_split_kernel<false, false, true> : decode_split_kernel<false, false, false>));
@@ -973,6 +1024,12 @@ int run_decode(bool bifocal, const void* q, const void* kc, const void* vc, void
     hipLaunchKernelGGL(decode_combine_kernel, dim3(Hq, nb, kHeadDim / 32), dim3(256), 0, stream, dp, ds);
     e = hipGetLastError();
     if (e != hipSuccess) return bad(BF_ERR_HIP, std::string("decode combine launch: ") + hipGetErrorString(e));
+    if (store)  // the store as the stream leaves this launch: k'' of every far key for s
+      for (int i = 0; i < nb; ++i) {
+        const long long N = ds.N[i];
+        store->keys[b0 + i] = ds.s[i] > 1 && N > w0 ? (int32_t)(N - w0) : 0;
+        store->s[b0 + i] = ds.s[i];
+      }
   }
   return BF_OK;
 }

@@ -146,6 +146,37 @@ def test_decode_noalloc_validation(L, kw, code):
     assert len(L.bifocal_last_error()) > 0
 
 
+def _decode_stored(L, keys, svals, **kw):
+    a = dict(q=P, k=P, v=P, k2=P, o=P, lse=None, sl=[100], cap=128, Hq=4, Hkv=2, D=128, dtype=0,
+             w0=16, w_pre=64, theta=1e4, mode=0, scale=0.088, ws=P, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    sl = (ctypes.c_int32 * len(a["sl"]))(*a["sl"])
+    return L.bifocal_decode_stored(a["q"], a["k"], a["v"], a["k2"], a["o"], a["lse"], sl, keys, svals,
+                                   len(a["sl"]), a["cap"], a["Hq"], a["Hkv"], a["D"], a["dtype"],
+                                   a["w0"], a["w_pre"], a["theta"], a["mode"], a["scale"], a["ws"],
+                                   a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,keys,code", [
+    (dict(k2=None), 0, -1), (dict(k2=ctypes.c_void_p(0x100008)), 0, -1), (dict(), -5, -1), (dict(mode=2), 0, -2),
+    (dict(dtype=1), 0, -2), (dict(sl=[129]), 0, -1), (dict(mode=9), 0, -1), (dict(q=None), 0, -1),
+])
+def test_decode_stored_validation(L, kw, keys, code):
+    # rejected before any HIP call; the caller's store counters stay as they were
+    k = (ctypes.c_int32 * len(kw.get("sl", [100])))(*([keys] * len(kw.get("sl", [100]))))
+    sv = (ctypes.c_int32 * len(kw.get("sl", [100])))(*([7] * len(kw.get("sl", [100]))))
+    before = (list(k), list(sv))
+    assert _decode_stored(L, k, sv, **kw) == code
+    assert len(L.bifocal_last_error()) > 0
+    assert (list(k), list(sv)) == before
+
+
+def test_decode_stored_null_counters(L):
+    k = (ctypes.c_int32 * 1)(0)
+    assert _decode_stored(L, None, k) == -1
+    assert _decode_stored(L, k, None) == -1
+
+
 def test_plain_validation(L):
     cu = (ctypes.c_int32 * 2)(0, 100)
     assert L.plain_attention_ref_gpu(7, P, P, P, P, None, cu, 1, 0, 2, 1, 128, 0, 0.1, P, 1 << 30,
