@@ -23,7 +23,8 @@
  * Conventions for every entry point:
  *   - Tensors are caller-owned DEVICE memory and must stay valid until the
  *     work enqueued on `stream` completes. Host arrays (cu_seqlens_host,
- *     seqlens_host) are read before the call returns.
+ *     seqlens_host, ...) are read, and the far-key store's counters
+ *     (store_keys_host, store_s_host) written, before the call returns.
  *   - All work is enqueued on `stream` (a hipStream_t, NULL = default
  *     stream). The library never synchronises and keeps no state between
  *     calls except a thread-local error string.
@@ -266,6 +267,24 @@ int bifocal_decode_stored(const void* q, const void* k_cache, const void* v_cach
                           int64_t w0, int64_t w_pre, double rope_theta, int32_t long_mode,
                           float softmax_scale, void* workspace, size_t workspace_bytes,
                           void* stream);
+
+/*
+ * bifocal_decode_stored over a PAGED KV cache: the arguments of
+ * bifocal_decode_paged plus the store of bifocal_decode_stored, which is a
+ * page pool of its own with the shape of k_pages, addressed through the same
+ * block_table ([num_pages, n_heads_kv, page_size, head_dim] bf16, device,
+ * caller-owned). Result bitwise that of bifocal_decode_paged (and of
+ * bifocal_decode_stored on a contiguous cache holding the same keys).
+ */
+int bifocal_decode_stored_paged(const void* q, const void* k_pages, const void* v_pages,
+                                void* k2_pages, void* o, float* lse, const int32_t* block_table,
+                                const int32_t* seqlens_host, int32_t* store_keys_host,
+                                int32_t* store_s_host, int32_t batch, int32_t page_size,
+                                int32_t max_pages_per_seq, int32_t num_pages, int32_t n_heads_q,
+                                int32_t n_heads_kv, int32_t head_dim, int32_t dtype, int64_t w0,
+                                int64_t w_pre, double rope_theta, int32_t long_mode,
+                                float softmax_scale, void* workspace, size_t workspace_bytes,
+                                void* stream);
 
 /*
  * bifocal_decode without a workspace, for callers that cannot allocate

@@ -31,7 +31,7 @@ EXPORTED = ("bifocal_s_of_L", "bifocal_workspace_bytes", "bifocal_prefill", "bif
             "bifocal_decode_paged", "plain_attention_ref_gpu", "bifocal_rope_prefill", "bifocal_rope_append",
             "bifocal_rope_prefill_paged", "bifocal_rope_append_paged",
             "bifocal_test_pair_map", "bifocal_last_error", "bifocal_decode_noalloc",
-            "bifocal_test_angles", "bifocal_decode_stored")
+            "bifocal_test_angles", "bifocal_decode_stored", "bifocal_decode_stored_paged")
 
 _lib = None
 
@@ -73,6 +73,10 @@ def lib():
         L.bifocal_decode_stored.restype = ctypes.c_int
         L.bifocal_decode_stored.argtypes = [p, p, p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32,
                                             i64, i64, f64, i32, f32, p, sz, p]
+        L.bifocal_decode_stored_paged.restype = ctypes.c_int
+        L.bifocal_decode_stored_paged.argtypes = [p, p, p, p, p, p, p, p, p, p, i32, i32, i32, i32,
+                                                  i32, i32, i32, i32, i64, i64, f64, i32, f32, p,
+                                                  sz, p]
         L.bifocal_decode_noalloc.restype = ctypes.c_int
         L.bifocal_decode_noalloc.argtypes = [p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, i64,
                                              i64, f64, i32, f32, p]
@@ -267,13 +271,14 @@ def decode(q, k_cache, v_cache, seqlens, w0, w_pre, rope_theta, long_mode="fi",
 
 
 class DecodeStore:
-    """Caller-kept state of decode_stored for one contiguous cache [B,Hkv,cap,D]:
-    the far-key store k2 (same shape, bf16) and, per sequence, how many keys
-    it holds (keys) and for which s (s). The library updates keys and s."""
+    """Caller-kept state of decode_stored for one cache: the far-key store k2
+    (the cache's shape: [B,Hkv,cap,D], or a page pool [pages,Hkv,page,D] with
+    `batch` given) and, per sequence, how many keys it holds (keys) and for
+    which s (s). The library updates keys and s."""
 
-    def __init__(self, k_cache):
+    def __init__(self, k_cache, batch=None):
         self.k2 = torch.empty_like(k_cache)
-        B = k_cache.shape[0]
+        B = k_cache.shape[0] if batch is None else int(batch)  # a page pool needs `batch`
         self.keys = (ctypes.c_int32 * B)()
         self.s = (ctypes.c_int32 * B)()
 
@@ -303,6 +308,28 @@ def decode_stored(q, k_cache, v_cache, store, seqlens, w0, w_pre, rope_theta, lo
                                        _DTYPES[q.dtype], int(w0), int(w_pre), float(rope_theta),
                                        LONG_MODES[long_mode], _scale(softmax_scale, D),
                                        _ptr(workspace), workspace.numel(), _stream(stream)))
+    return (o, lse) if return_lse else o
+
+
+def decode_stored_paged(q, k_pages, v_pages, block_table, store, seqlens, w0, w_pre, rope_theta,
+                        long_mode="fi", softmax_scale=None, return_lse=False, out=None, lse=None,
+                        workspace=None, stream=None):
+    """decode_stored over a paged cache; `store` is a DecodeStore made from
+    k_pages (its k2 is a page pool under the same block table)."""
+    B, Hq, D = q.shape
+    num_pages, Hkv, page = k_pages.shape[0], k_pages.shape[1], k_pages.shape[2]
+    o = out if out is not None else torch.empty_like(q)
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = alloc_workspace(workspace_bytes(BF_PHASE_DECODE, B, max(seqlens), Hq, Hkv, D,
+                                                    q.dtype), q.device)
+    sl = _i32_array(seqlens)
+    _check(lib().bifocal_decode_stored_paged(
+        _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(store.k2), _ptr(o), _ptr(lse), _ptr(block_table),
+        sl, store.keys, store.s, B, page, block_table.shape[1], num_pages, Hq, Hkv, D,
+        _DTYPES[q.dtype], int(w0), int(w_pre), float(rope_theta), LONG_MODES[long_mode],
+        _scale(softmax_scale, D), _ptr(workspace), workspace.numel(), _stream(stream)))
     return (o, lse) if return_lse else o
 
 

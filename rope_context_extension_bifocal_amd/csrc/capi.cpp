@@ -746,6 +746,32 @@ int bifocal_decode_stored(const void* q, const void* k_cache, const void* v_cach
   return BF_OK;
 }
 
+int bifocal_decode_stored_paged(const void* q, const void* k_pages, const void* v_pages,
+                                void* k2_pages, void* o, float* lse, const int32_t* block_table,
+                                const int32_t* seqlens_host, int32_t* store_keys_host,
+                                int32_t* store_s_host, int32_t batch, int32_t page_size,
+                                int32_t max_pages_per_seq, int32_t num_pages, int32_t n_heads_q,
+                                int32_t n_heads_kv, int32_t head_dim, int32_t dtype, int64_t w0,
+                                int64_t w_pre, double rope_theta, int32_t long_mode,
+                                float softmax_scale, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  int rc = check_common(n_heads_q, n_heads_kv, head_dim, dtype);
+  if (rc) return rc;
+  if ((rc = check_bifocal_knobs(w0, w_pre, rope_theta, long_mode))) return rc;
+  if (dtype != BF_DTYPE_BF16) return fail(BF_ERR_UNSUPPORTED, "decode supports bf16 only");
+  if (long_mode == BF_LONG_NONE)
+    return fail(BF_ERR_UNSUPPORTED, "band-only decode has no far keys to store (use bifocal_decode_paged)");
+  const bf::PagedCache pc{block_table, page_size, max_pages_per_seq, num_pages};
+  const bf::DecodeStore st{k2_pages, store_keys_host, store_s_host};
+  std::string err;
+  rc = bf::run_decode(true, q, k_pages, v_pages, o, lse, seqlens_host, batch, 1, n_heads_q,
+                      n_heads_kv, w0, w_pre, rope_theta, long_mode, softmax_scale, workspace,
+                      workspace_bytes, (hipStream_t)stream, err, 0, &pc, false, &st);
+  if (rc) return fail(rc, "%s", err.c_str());
+  g_err.clear();
+  return BF_OK;
+}
+
 int bifocal_decode_paged(const void* q, const void* k_pages, const void* v_pages, void* o,
                          float* lse, const int32_t* block_table, const int32_t* seqlens_host,
                          int32_t batch, int32_t page_size, int32_t max_pages_per_seq,

@@ -234,14 +234,15 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// STORE (bifocal, contiguous cache): the far keys below ds.stored[b] are read
-// as k'' from p.k2 and used as loaded; every other far key is rotated as
-// usual and its k'' written to p.k2, so after the call p.k2 holds k'' of all
-// far keys (a later call with the same s reads them back).
+// STORE (bifocal): the far keys below ds.stored[b] are read as k'' from p.k2
+// (the layout of p.kc: a contiguous cache, or a page pool under the same
+// block table) and used as loaded; every other far key is rotated as usual
+// and its k'' written to p.k2, so after the call p.k2 holds k'' of all far
+// keys (a later call with the same s reads them back).
 template <bool BIFOCAL, bool PAGED, bool NT, bool STORE = false>
 __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p, DecodeSeqs ds,
                                                               ThetaTable tt) {
-  static_assert(!STORE || (BIFOCAL && !PAGED), "the far-key store serves the bifocal contiguous cache");
+  static_assert(!STORE || BIFOCAL, "the far-key store serves the bifocal decode");
   __shared__ uint4 smem[kDecLds / 16];
   uint4* sQ = smem + kDecLdsQ / 16;
 
@@ -288,6 +289,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p, De
     // read once; each step picks its page by register and lane
     kwb = dscalar_ptr(p.kc);
     vwb = dscalar_ptr(p.vc);
+    if constexpr (STORE) k2wb = (char*)dscalar_ptr(p.k2);
     if (ns > 0) {
       first_page = (int)(kw0 >> p.page_log2);
       const int last_page = (int)((kw1 - 1) >> p.page_log2);
@@ -304,6 +306,19 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p, De
   // Keys are addressed from kb / vb: the wave's first key (contiguous cache)
   // or the first key of the step's page block (paged cache, rel0 = 0).
   // (KV = 0: K, 1: V)
+  // paged cache: the pool row of the first key of the step at split-local key j0
+  // (a step never crosses a page: 16 | page size)
+  auto page_row = [&](int j0) -> size_t {
+    const long long key = kw0 + j0;
+    const int pi = (int)(key >> p.page_log2) - first_page;  // wave-uniform, < 64 kDecPageRegs
+    int page = __builtin_amdgcn_readlane(pg[0], pi & 63);
+#pragma unroll
+    for (int g = 1; g < kDecPageRegs; ++g) {
+      const int pgg = __builtin_amdgcn_readlane(pg[g], pi & 63);
+      page = (pi >> 6) == g ? pgg : page;
+    }
+    return (((size_t)page * p.Hkv + kvh) << p.page_log2) + (size_t)(key & ((1LL << p.page_log2) - 1));
+  };
   auto issue_half = [&](int st, int r, auto kv) {
     constexpr int KV = decltype(kv)::value;
     const int j0 = jl_of(st);
@@ -311,18 +326,9 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p, De
     const char* vb = vwb;
     int rel0 = j0;
     if constexpr (PAGED) {
-      const long long key = kw0 + j0;  // a step never crosses a page (16 | page size)
-      const int pi = (int)(key >> p.page_log2) - first_page;  // wave-uniform, < 64 kDecPageRegs
-      int page = __builtin_amdgcn_readlane(pg[0], pi & 63);
-#pragma unroll
-      for (int g = 1; g < kDecPageRegs; ++g) {
-        const int pgg = __builtin_amdgcn_readlane(pg[g], pi & 63);
-        page = (pi >> 6) == g ? pgg : page;
-      }
-      const size_t row = (((size_t)page * p.Hkv + kvh) << p.page_log2) +
-                         (size_t)(key & ((1LL << p.page_log2) - 1));
-      kb = dscalar_ptr((const char*)p.kc + row * (kHeadDim * 2));
-      vb = dscalar_ptr((const char*)p.vc + row * (kHeadDim * 2));
+      const size_t row = page_row(j0);
+      kb = dscalar_ptr(kb + row * (kHeadDim * 2));
+      vb = dscalar_ptr(vb + row * (kHeadDim * 2));
       rel0 = 0;
     }
     // rows are clamped to the last key (a no-op except in the split's last
@@ -469,10 +475,11 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p, De
         }
         if constexpr (STORE) {  // this lane's key is far: keep its k'' (rows as loaded)
           if (jbl + n16 < nl) {
-            const uint32_t row = (uint32_t)(jbl + n16) * (kHeadDim * 2);
+            char* wb = PAGED ? k2wb + page_row(jbl) * (kHeadDim * 2) : k2wb;
+            const uint32_t row = (uint32_t)(PAGED ? n16 : jbl + n16) * (kHeadDim * 2);
 #pragma unroll
             for (int t = 0; t < 4; ++t)
-              *(__attribute__((address_space(1))) du32x4*)(k2wb + row + (4 * t + g4) * 16) =
+              *(__attribute__((address_space(1))) du32x4*)(wb + row + (4 * t + g4) * 16) =
                   __builtin_bit_cast(du32x4, kr[t]);
           }
         }
@@ -897,8 +904,8 @@ int run_decode(bool bifocal, const void* q, const void* kc, const void* vc, void
   auto bad = [&](int code, const std::string& m) { err = m; return code; };
   if (!q || !kc || !vc || !o || !seqlens) return bad(BF_ERR_INVALID_ARG, "null tensor or seqlens pointer");
   if (store) {
-    if (paged || !bifocal || window > 0)
-      return bad(BF_ERR_UNSUPPORTED, "the far-key store serves FI / PA decode over a contiguous cache");
+    if (!bifocal || window > 0)
+      return bad(BF_ERR_UNSUPPORTED, "the far-key store serves FI / PA decode");
     if (!store->k2 || ((uintptr_t)store->k2 & 15u))
       return bad(BF_ERR_INVALID_ARG, "k2_store must be a non-null 16-byte aligned device pointer");
     if (!store->keys || !store->s) return bad(BF_ERR_INVALID_ARG, "null store_keys or store_s pointer");
@@ -999,7 +1006,7 @@ int run_decode(bool bifocal, const void* q, const void* kc, const void* vc, void
     // the block table from the launch's first sequence on
     dp.kc = (const uint16_t*)kc + (paged ? 0 : (size_t)b0 * Hkv * cap * kHeadDim);
     dp.vc = (const uint16_t*)vc + (paged ? 0 : (size_t)b0 * Hkv * cap * kHeadDim);
-    dp.k2 = store ? (uint16_t*)store->k2 + (size_t)b0 * Hkv * cap * kHeadDim : nullptr;
+    dp.k2 = store ? (uint16_t*)store->k2 + (paged ? 0 : (size_t)b0 * Hkv * cap * kHeadDim) : nullptr;
     if (paged) dp.block_table = paged->block_table + (size_t)b0 * paged->max_pages;
     dp.o = (uint16_t*)o + (size_t)b0 * Hq * kHeadDim;
     dp.lse = lse ? lse + (size_t)b0 * Hq : nullptr;
@@ -1013,7 +1020,8 @@ int run_decode(bool bifocal, const void* q, const void* kc, const void* vc, void
     // non-temporal K / V loads unless the launch reads little enough that
     // its cache could stay resident in the 256 MB MALL between calls
     const bool nt = kv_bytes >= kDecStreamBytes;
-    auto kern = store ? (nt ? decode_split_kernel<true, false, true, true> : decode_split_kernel<true, false, false, true>)
+    auto kern = store ? (paged ? (nt ? decode_split_kernel<true, true, true, true> : decode_split_kernel<true, true, false, true>)
+                               : (nt ? decode_split_kernel<true, false, true, true> : decode_split_kernel<true, false, false, true>))
               : bifocal ? (paged ? (nt ? decode_split_kernel<true, true, true> : decode_split_kernel<true, true, false>)
                                  : (nt ? decode_split_kernel<true, false, true> : decode_split_kernel<true, false, false>))
                         : (paged ? (nt ? decode_split_kernel<false, true, true> : decode_split_kernel<false, true, false>)

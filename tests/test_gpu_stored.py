@@ -97,3 +97,29 @@ def test_stored_128k():
     torch.cuda.synchronize()
     assert torch.equal(a, ref) and torch.equal(b, ref)
     assert store.keys[0] == N - 4096 and store.s[0] == 5
+
+
+@pytest.mark.parametrize("page", [16, 64])
+def test_stored_paged_equals_contiguous(page):
+    # the same two-sequence walk over a shuffled page pool: bitwise the
+    # contiguous stored decode and the stateless paged decode at every step
+    B, Hq, Hkv, cap, w0, w_pre, theta = 2, 32, 8, 2304, 256, 1024, 1e4
+    q, kc, vc = (x.cuda() for x in wl.decode_inputs(B, Hq, Hkv, cap, 128, "bf16", 74))
+    per = cap // page
+    perm = torch.randperm(B * per, generator=torch.Generator().manual_seed(75)).cuda()
+    kp = torch.empty((B * per, Hkv, page, 128), dtype=torch.bfloat16, device="cuda")
+    vp = torch.empty_like(kp)
+    kp[perm] = kc.view(B, Hkv, per, page, 128).permute(0, 2, 1, 3, 4).reshape(B * per, Hkv, page, 128)
+    vp[perm] = vc.view(B, Hkv, per, page, 128).permute(0, 2, 1, 3, 4).reshape(B * per, Hkv, page, 128)
+    table = perm.to(torch.int32).view(B, per)
+    sc, sp = bfl.DecodeStore(kc), bfl.DecodeStore(kp, batch=B)
+    sp.k2.fill_(float("nan"))
+    for n in [2030, 2031, 2048, 2049, 2050, 2100]:
+        lens = [n, n - 21]
+        ref = bfl.decode_paged(q, kp, vp, table, lens, w0, w_pre, theta, "pa+shift", SCALE)
+        got_c = bfl.decode_stored(q, kc, vc, sc, lens, w0, w_pre, theta, "pa+shift", SCALE)
+        got_p = bfl.decode_stored_paged(q, kp, vp, table, sp, lens, w0, w_pre, theta, "pa+shift",
+                                        SCALE)
+        torch.cuda.synchronize()
+        assert torch.equal(got_p, ref) and torch.equal(got_c, ref), n
+        assert list(sp.keys) == list(sc.keys) and list(sp.s) == list(sc.s)
