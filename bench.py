@@ -361,9 +361,10 @@ def main():
     for _ in range(10):
         plain_decode()
     plain_dec_ms = time_calls(plain_decode, 50, stream)
-    def cold_us(qx, kx, vx, n, ws_x, copies, calls=200):
+    def cold_us(qx, kx, vx, n, ws_x, copies, calls=200, plain=False):
         """Decode over `copies` distinct cache copies in turn (together more
-        than twice the 256 MB MALL), so no call finds its cache resident."""
+        than twice the 256 MB MALL), so no call finds its cache resident
+        (plain: the library's plain attention the same way)."""
         kcs = [kx] + [kx.clone() for _ in range(copies - 1)]
         vcs = [vx] + [vx.clone() for _ in range(copies - 1)]
         it = [0]
@@ -371,8 +372,11 @@ def main():
         def fn():
             i = it[0] % copies
             it[0] += 1
-            bfl.decode(qx, kcs[i], vcs[i], [n], dcfg["w0"], dcfg["w_pre"], dcfg["theta"], "fi",
-                       scale, workspace=ws_x)
+            if plain:
+                bfl.plain_decode(qx, kcs[i], vcs[i], [n], scale, workspace=ws_x)
+            else:
+                bfl.decode(qx, kcs[i], vcs[i], [n], dcfg["w0"], dcfg["w_pre"], dcfg["theta"], "fi",
+                           scale, workspace=ws_x)
 
         for _ in range(20):
             fn()
@@ -414,6 +418,7 @@ def main():
 
     MALL = 256 * 1024 * 1024
     dec_cold_us = cold_us(qdc, kc, vc, N, ws_d, max(2, math.ceil(2 * MALL / kv_bytes)))
+    plain_cold_us = cold_us(qdc, kc, vc, N, ws_d, max(2, math.ceil(2 * MALL / kv_bytes)), plain=True)
     dec_stored_us = stored_us(qdc, kc, vc, N, ws_d)
     small = {}
     for Lc in dcfg["cache_lens"][:2]:
@@ -430,11 +435,13 @@ def main():
         t_p = time_calls(pfn, 100, stream)
         nbytes = 2.0 * n * Hkv * D * 2
         t_c = cold_us(qs, ks, vs, n, ws_s, max(2, math.ceil(2 * MALL / nbytes))) * 1e-3
+        t_pc = cold_us(qs, ks, vs, n, ws_s, max(2, math.ceil(2 * MALL / nbytes)), plain=True) * 1e-3
         t_s = stored_us(qs, ks, vs, n, ws_s) * 1e-3
         small[str(n)] = {"bifocal_us": round(t_b * 1e3, 2), "plain_us": round(t_p * 1e3, 2),
                          "stored_us": round(t_s * 1e3, 2),
                          "bifocal_gbs": round(nbytes / (t_b * 1e-3) / 1e9, 1),
                          "bifocal_cold_us": round(t_c * 1e3, 2),
+                         "plain_cold_us": round(t_pc * 1e3, 2),
                          "bifocal_cold_gbs": round(nbytes / (t_c * 1e-3) / 1e9, 1)}
         del qs, ks, vs
 
@@ -639,6 +646,8 @@ def main():
         "decode_cold_us": round(dec_cold_us, 2),
         "decode_paged16_us": round(paged_ms * 1e3, 2),
         "decode_cold_gbs": round(kv_bytes / (dec_cold_us * 1e-6) / 1e9, 1),
+        "plain_decode_cold_us": round(plain_cold_us, 2),
+        "decode_cold_overhead_vs_plain": round(dec_cold_us / plain_cold_us - 1, 4),
         "plain_decode_us": round(plain_dec_ms * 1e3, 2),
         "decode_overhead_vs_plain": round(dec_many_ms / plain_dec_ms - 1, 4),
         "decode_stored_us": round(dec_stored_us, 2),
