@@ -123,3 +123,21 @@ def test_stored_paged_equals_contiguous(page):
         torch.cuda.synchronize()
         assert torch.equal(got_p, ref) and torch.equal(got_c, ref), n
         assert list(sp.keys) == list(sc.keys) and list(sp.s) == list(sc.s)
+
+
+def test_stored_batch_of_70():
+    # more sequences than one launch takes (64): the counters of every group
+    # are kept; lengths spread over s = 1 .. 3
+    B, Hq, Hkv, cap, w0, w_pre, theta = 70, 8, 2, 2560, 128, 1024, 1e4
+    q, kc, vc = (x.cuda() for x in wl.decode_inputs(B, Hq, Hkv, cap, 128, "bf16", 76))
+    lens = [100 + 35 * b for b in range(B)]
+    store = bfl.DecodeStore(kc)
+    for step in range(3):
+        cur = [n + step for n in lens]
+        ref = bfl.decode(q, kc, vc, cur, w0, w_pre, theta, "fi", SCALE)
+        got = bfl.decode_stored(q, kc, vc, store, cur, w0, w_pre, theta, "fi", SCALE)
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref), step
+        for b, n in enumerate(cur):
+            s = bfl.s_of_L(n, w_pre)
+            assert store.s[b] == s and store.keys[b] == (n - w0 if s > 1 and n > w0 else 0)
