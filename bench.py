@@ -12,8 +12,9 @@ Prints one JSON line. `value` is the prefill effective TFLOP/s: algorithmic
 flops 4 * D * Hq * L (L + 1) / 2 (one score and one PV product per causal
 pair) over the measured prefill time. Extra fields report the decode
 bandwidth, position aliasing, the library's plain causal attention on the
-same shapes (overhead reference), chunks of the last 4096 / 16384 queries
-against the 128K cache (contiguous, and 4096 over 16-key pages), roofline
+same shapes (overhead reference), chunks of the last 512 / 4096 / 16384
+queries against the 128K cache (contiguous, with a chunk store that holds
+k'' and V^T of the keys before the chunk, and 4096 over 16-key pages), roofline
 fractions against MI355X peaks
 (bf16 dense MFMA 2.5 PFLOP/s, HBM 8 TB/s) and the fp64 CPU oracle timed on a
 bounded row sample of the prefill workload.
@@ -543,6 +544,7 @@ def main():
     log("chunked prefill: the last 512 / 4096 / 16384 queries against the 128K cache")
     kcc, vcc = kd.unsqueeze(0), vd.unsqueeze(0)  # [1, Hkv, L, D]: the cache layout, cap = L
     chunk = {}
+    cstore = bfl.ChunkStore(kcc)
     for lq in (512, 4096, 16384):
         qch = qd[:, L - lq:].contiguous()
         och = torch.empty_like(qch)
@@ -553,6 +555,19 @@ def main():
         c_ms = time_calls(cfn, 5, stream)
         c_flops = 4.0 * D * Hq * (lq * L - lq * (lq - 1) / 2)  # positions L - lq .. L - 1
         chunk[str(lq)] = {"ms": round(c_ms, 3), "tflops": round(c_flops / (c_ms * 1e-3) / 1e12, 2)}
+        # with a chunk store holding the cache up to the chunk: each call forms
+        # k'' and V^T of the chunk's own keys only (as a chunk-by-chunk prompt does)
+        wss = bfl.alloc_workspace(bfl.chunk_workspace_bytes(1, lq, lq, Hq, Hkv), "cuda")
+
+        def sfn():
+            cstore.reset(keys=L - lq)
+            bfl.prefill_chunk_stored(qch, kcc, vcc, cstore, [0, lq], [L], cfg["w0"], cfg["w_pre"],
+                                     cfg["theta"], "fi", scale, out=och, workspace=wss)
+        sfn()
+        s_ms = time_calls(sfn, 5, stream)
+        chunk[f"{lq}_stored"] = {"ms": round(s_ms, 3),
+                                 "tflops": round(c_flops / (s_ms * 1e-3) / 1e12, 2)}
+        del wss
         if lq == 4096:  # the same chunk over a shuffled pool of 16-key pages
             npg = L // 16
             perm = torch.randperm(npg, generator=torch.Generator().manual_seed(17)).cuda()
@@ -580,6 +595,7 @@ def main():
             chunk["4096_band"] = {"ms": round(b_ms, 3),
                                   "tflops": round(b_flops / (b_ms * 1e-3) / 1e12, 2)}
         del qch, och, wsc
+    del cstore
 
     log("raw-input pre-step")
     qr, kr = qd.clone(), kd.clone()

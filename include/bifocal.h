@@ -214,6 +214,58 @@ int bifocal_prefill_chunk_paged(const void* q, const void* k_pages, const void* 
                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Bytes of the store of bifocal_prefill_chunk_stored for `batch` sequences
+ * of a cache with cache_capacity keys and n_heads_kv KV heads (k'' and V^T of
+ * every cache position, padded to 64 keys). Returns 0 for invalid arguments
+ * and when 64 sequences x n_heads_kv x cache_capacity (rounded up to 64)
+ * exceed 2^31 - 1 key rows.
+ */
+size_t bifocal_chunk_store_bytes(int32_t batch, int32_t cache_capacity, int32_t n_heads_kv,
+                                 int32_t head_dim, int32_t dtype);
+
+/*
+ * bifocal_prefill_chunk with a caller-kept store of the per-key operands the
+ * call would otherwise rebuild for the whole cache: k''_j = R(theta_m (phi(j)
+ * - j)) k'_j, which depends only on j and s, and V^T. A call then forms them
+ * only for the keys appended since the store was filled, so successive
+ * chunks of one long prompt (s fixed by s_len) cost what their new keys
+ * cost [mufans.github.io wiki, Jet-Long Dynamic RoPE, "可执行建议": pairing
+ * the method with prompt caching; ai-feeds.com summary, "关键模块" item 3:
+ * the correction rotation of cached keys; item 2: s from the length].
+ *   store            : device, caller-owned, 256-byte aligned, at least
+ *                      bifocal_chunk_store_bytes(batch, cache_capacity, ...)
+ *                      bytes; its contents are the library's (opaque)
+ *   store_bytes      : its size
+ *   store_keys_host  : host int32 [batch], in/out: the store holds keys
+ *                      0 .. P_b - 1 of sequence b for s = store_s_host[b]
+ *   store_s_host     : host int32 [batch], in/out (start both at 0)
+ *   workspace        : bifocal_chunk_workspace_bytes(batch, Tq, Tq, ..., 0)
+ *                      suffices (q'' and the key-split partials only); the
+ *                      split count follows the workspace as for
+ *                      bifocal_prefill_chunk
+ * Other arguments as bifocal_prefill_chunk on a contiguous cache, long_mode
+ * FI or PA with or without BF_LONG_SHIFT; band-only (BF_LONG_NONE) returns
+ * BF_ERR_UNSUPPORTED. If store_s_host[b] != s(s_len_b) (s(N_b) without
+ * s_len) the store of sequence b counts as empty. The call forms k'' of keys
+ * min(P_b, N_b) .. N_b - 1 and V^T from that key's 64-key tile on; after it
+ * has been queued, store_keys_host[b] = N_b and store_s_host[b] = s. The
+ * result is bitwise that of bifocal_prefill_chunk given a workspace of the
+ * same size. The store belongs to one cache, long_mode and rope_theta: after
+ * rewriting cache positions below P_b, lower store_keys_host[b] to the first
+ * rewritten position; after changing the mode or rope_theta, set it to 0.
+ * Validation errors leave outputs, store and both host arrays untouched.
+ */
+int bifocal_prefill_chunk_stored(const void* q, const void* k_cache, const void* v_cache,
+                                 void* store, size_t store_bytes, void* o, float* lse,
+                                 const int32_t* cu_q_host, const int32_t* seqlens_host,
+                                 const int32_t* s_len_host, int32_t* store_keys_host,
+                                 int32_t* store_s_host, int32_t batch, int32_t cache_capacity,
+                                 int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim,
+                                 int32_t dtype, int64_t w0, int64_t w_pre, double rope_theta,
+                                 int32_t long_mode, float softmax_scale, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/*
  * Single-token bifocal decode over a KV cache (bf16 only).
  *   q, o             : [batch, n_heads_q, head_dim] bf16
  *   k_cache, v_cache : [batch, n_heads_kv, cache_capacity, head_dim] bf16,

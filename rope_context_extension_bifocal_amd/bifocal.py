@@ -31,7 +31,8 @@ EXPORTED = ("bifocal_s_of_L", "bifocal_workspace_bytes", "bifocal_prefill", "bif
             "bifocal_decode_paged", "plain_attention_ref_gpu", "bifocal_rope_prefill", "bifocal_rope_append",
             "bifocal_rope_prefill_paged", "bifocal_rope_append_paged",
             "bifocal_test_pair_map", "bifocal_last_error", "bifocal_decode_noalloc",
-            "bifocal_test_angles", "bifocal_decode_stored", "bifocal_decode_stored_paged")
+            "bifocal_test_angles", "bifocal_decode_stored", "bifocal_decode_stored_paged",
+            "bifocal_chunk_store_bytes", "bifocal_prefill_chunk_stored")
 
 _lib = None
 
@@ -64,6 +65,12 @@ def lib():
         L.bifocal_prefill_chunk_paged.restype = ctypes.c_int
         L.bifocal_prefill_chunk_paged.argtypes = [p, p, p, p, p, p, p, p, p, i32, i32, i32, i32, i32,
                                                   i32, i32, i32, i64, i64, f64, i32, f32, p, sz, p]
+        L.bifocal_chunk_store_bytes.restype = sz
+        L.bifocal_chunk_store_bytes.argtypes = [i32, i32, i32, i32, i32]
+        L.bifocal_prefill_chunk_stored.restype = ctypes.c_int
+        L.bifocal_prefill_chunk_stored.argtypes = [p, p, p, p, sz, p, p, p, p, p, p, p, i32, i32,
+                                                   i32, i32, i32, i32, i64, i64, f64, i32, f32, p,
+                                                   sz, p]
         L.bifocal_prefill_chunk.restype = ctypes.c_int
         L.bifocal_prefill_chunk.argtypes = [p, p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32,
                                             i64, i64, f64, i32, f32, p, sz, p]
@@ -199,6 +206,59 @@ def prefill_chunk(q, k_cache, v_cache, cu_q, seqlens, w0, w_pre, rope_theta, lon
                                        int(w_pre), float(rope_theta), LONG_MODES[long_mode],
                                        _scale(softmax_scale, D), _ptr(workspace),
                                        workspace.numel(), _stream(stream)))
+    return (o, lse) if return_lse else o
+
+
+def chunk_store_bytes(batch, cache_capacity, n_heads_kv, head_dim=128, dtype=torch.bfloat16):
+    return lib().bifocal_chunk_store_bytes(batch, cache_capacity, n_heads_kv, head_dim,
+                                           _DTYPES[dtype])
+
+
+class ChunkStore:
+    """Caller-kept state of prefill_chunk_stored for one cache [B,Hkv,cap,D]:
+    an opaque device buffer holding k'' and V^T of the cache positions and,
+    per sequence, how many keys it holds (keys) and for which s (s). The
+    library updates keys and s."""
+
+    def __init__(self, k_cache):
+        B, Hkv, cap, D = k_cache.shape
+        n = chunk_store_bytes(B, cap, Hkv, D, k_cache.dtype)
+        if n == 0:
+            raise ValueError("no chunk store for a cache of shape %s" % (tuple(k_cache.shape),))
+        self.buf = torch.empty(n, dtype=torch.uint8, device=k_cache.device)
+        self.keys = (ctypes.c_int32 * B)()
+        self.s = (ctypes.c_int32 * B)()
+
+    def reset(self, b=None, keys=0):
+        """Forget stored keys from `keys` on (all sequences, or sequence b),
+        e.g. after rewriting cache positions from `keys` on."""
+        for i in (range(len(self.keys)) if b is None else [b]):
+            self.keys[i] = min(self.keys[i], int(keys))
+
+
+def prefill_chunk_stored(q, k_cache, v_cache, store, cu_q, seqlens, w0, w_pre, rope_theta,
+                         long_mode="fi", softmax_scale=None, s_len=None, return_lse=False,
+                         out=None, lse=None, workspace=None, stream=None):
+    """prefill_chunk with a ChunkStore: k'' and V^T are formed only for the
+    keys the store does not hold yet. Bitwise prefill_chunk when both run with
+    their default workspaces (the same key splits); the default here holds
+    q'' and the split partials only."""
+    Hq, Tq, D = q.shape
+    Hkv, cap = k_cache.shape[1], k_cache.shape[2]
+    B = len(cu_q) - 1
+    o = out if out is not None else torch.empty_like(q)
+    if return_lse and lse is None:
+        lse = torch.empty((Hq, Tq), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = alloc_workspace(chunk_workspace_bytes(B, Tq, Tq, Hq, Hkv, D, q.dtype), q.device)
+    cu = _i32_array(cu_q)
+    sl = _i32_array(seqlens)
+    sls = _i32_array(s_len) if s_len is not None else None
+    _check(lib().bifocal_prefill_chunk_stored(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(store.buf), store.buf.numel(), _ptr(o),
+        _ptr(lse), cu, sl, sls, store.keys, store.s, B, cap, Hq, Hkv, D, _DTYPES[q.dtype], int(w0),
+        int(w_pre), float(rope_theta), LONG_MODES[long_mode], _scale(softmax_scale, D),
+        _ptr(workspace), workspace.numel(), _stream(stream)))
     return (o, lse) if return_lse else o
 
 

@@ -55,6 +55,8 @@ struct PrefillParams {
   float scale_log2; // softmax_scale * log2(e)
   long long k_hstride;  // K rows between KV heads
   long long k_rows;     // rows of the whole K tensor (range limit of the loads)
+  long long k2_rows;    // rows of the k'' tensor (range limit): Hkv * Tk, or a store's
+  long long vt_rows;    // head-dim rows x 64 keys of V^T (range limit): Hkv * Tpad, or a store's
   int T, Tk, Tpad;
   int Hq, Hkv, G;
   int hpw;          // query heads per workgroup
@@ -80,7 +82,7 @@ struct PrepParams {
   const void* q;  // [Hq][T][D]
   const void* k;  // rows h * k_hstride + kbase[b] + j, or pages (pk)
   void* q2;       // [Hq][T][D]
-  void* k2;       // [Hkv][Tk][D]
+  void* k2;       // [Hkv][Tk][D], or with k2_cap > 0 a store [n][Hkv][k2_cap][D]
   void* kcopy;    // [Hkv][Tk][D] packed copy of the keys (paged source only), else null
   PagedKV pk;
   long long k_hstride;
@@ -88,15 +90,26 @@ struct PrepParams {
   int long_mode;  // 0 = FI, 1 = PA
   int shift;      // 1: queries get the band-edge continuity shift w0 - phi(w0)
   long long w0;
+  // k2_cap > 0: k'' of key j of sequence b (of the launch) goes to row
+  // (b * Hkv + h) * k2_cap + j of the store, and the packed key axis (kcu)
+  // holds only keys kfirst[b] .. N_b - 1; k2_cap = 0: the packed layout, kfirst 0
+  int k2_cap;
+  int kfirst[kMaxSeqPerLaunch];
 };
 
 struct VtParams {
   const void* v;  // rows h * k_hstride + kbase[b] + j (the layout of K), or pages (pk)
-  void* vt;       // [Hkv][D][Tpad]
+  void* vt;       // [Hkv][D][Tpad], or with store_tiles > 0 a store [n][Hkv][store_tiles][D][64]
   PagedKV pk;
   long long k_hstride;
   int Tpad, Hkv;
+  int store_tiles;  // > 0: tile t of sequence b (of the launch), KV head h, goes to store
+                    // tile (b * Hkv + h) * store_tiles + t
 };
+
+// Kernel arguments stay within 4 KiB.
+static_assert(sizeof(PrepParams) + sizeof(SeqTable) + sizeof(ThetaTable) <= 4096, "prep arguments");
+static_assert(sizeof(PrefillParams) + sizeof(SeqTable) <= 4096, "prefill arguments");
 
 // Positions whose correction angles a test hook reports (at most kProbeMax).
 constexpr int kProbeMax = 128;

@@ -223,6 +223,14 @@ struct RowsJob {
   size_t ws_bytes = 0;
   hipStream_t stream = nullptr;
   int split_cap = 1;  // key splits allowed (chunk launches; the workspace may cap it further)
+  // caller-kept store of k'' and V^T (chunk launches over a contiguous cache),
+  // or null: k'' at rows (b * Hkv + h) * store_cap64 + j, V^T from byte
+  // store_vt_off in tiles (b * Hkv + h) * store_cap64 / 64 + t; the call forms
+  // them for keys kfirst[b] .. N_b - 1 only (V^T from kfirst[b]'s tile on)
+  char* store = nullptr;
+  long long store_cap64 = 0;
+  size_t store_vt_off = 0;
+  std::vector<int> kfirst;
 };
 
 // Validation of the arguments both paths share; tensors checked by the caller.
@@ -261,7 +269,9 @@ int run_rows(RowsJob& j) {
   }
   Tk = kcu[batch];
   const bool paged = j.pk.block_table != nullptr;
-  const PrefillWs wl = prefill_ws_layout(batch, Tq, Tk, Hq, Hkv, dtype, paged);
+  const bool stored = j.store != nullptr;
+  const long long Tk_ws = stored ? 0 : Tk;  // a store holds k'' and V^T: none in the workspace
+  const PrefillWs wl = prefill_ws_layout(batch, Tq, Tk_ws, Hq, Hkv, dtype, paged);
   if (!j.ws) return fail(BF_ERR_WORKSPACE, "workspace is null");
   if ((uintptr_t)j.ws & 255u) return fail(BF_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   const bool shift = bifocal && (j.mode & BF_LONG_SHIFT);
@@ -273,7 +283,7 @@ int run_rows(RowsJob& j) {
   // key splits the workspace has room for (partials after the base layout)
   int split_cap = dtype == BF_DTYPE_BF16 ? std::max(1, std::min(j.split_cap, bf::kMaxKeySplits)) : 1;
   while (split_cap > 1 &&
-         prefill_ws_layout(batch, Tq, Tk, Hq, Hkv, dtype, paged, split_cap).total > j.ws_bytes)
+         prefill_ws_layout(batch, Tq, Tk_ws, Hq, Hkv, dtype, paged, split_cap).total > j.ws_bytes)
     --split_cap;
 
   const int G = Hq / Hkv;
@@ -364,8 +374,20 @@ int run_rows(RowsJob& j) {
     const long long wgs = (long long)Hkv * geo.n_hsub * total_items;
     pp.nks = split_cap > 1 ? pick_key_splits(wgs, visit_sum / total_items, split_cap) : 1;
     pp.part_o = pp.nks > 1 ? (float*)(wsb + wl.po_off) : nullptr;
-    pp.part_lse = pp.nks > 1 ? (float*)(wsb + prefill_ws_layout(batch, Tq, Tk, Hq, Hkv, dtype, paged, pp.nks).pl_off)
+    pp.part_lse = pp.nks > 1 ? (float*)(wsb + prefill_ws_layout(batch, Tq, Tk_ws, Hq, Hkv, dtype, paged, pp.nks).pl_off)
                              : nullptr;
+    pp.k2_rows = (long long)Hkv * Tk;
+    pp.vt_rows = (long long)Hkv * Tpad;
+    if (stored) {
+      // this group's sequences in the store: k'' and V^T of (i, h) at
+      // rows / columns (i * Hkv + h) * cap64 from the group's first sequence
+      const size_t seq_bytes = (size_t)Hkv * j.store_cap64 * bf::kHeadDim * elem_size(dtype);
+      pp.k2 = j.store + (size_t)b0 * seq_bytes;
+      pp.vt = j.store + j.store_vt_off + (size_t)b0 * seq_bytes;
+      pp.Tk = (int)j.store_cap64;
+      pp.Tpad = (int)j.store_cap64;
+      pp.k2_rows = pp.vt_rows = (long long)nb * Hkv * j.store_cap64;
+    }
     gr.grid = wgs * pp.nks;
     if (gr.grid > 0x7fffffffLL)
       return fail(BF_ERR_INVALID_ARG, "launch grid of sequences %d..%d too large (%lld workgroups)", b0,
@@ -379,21 +401,60 @@ int run_rows(RowsJob& j) {
     const bf::PrefillParams& pp = gr.pp;
     const int b0 = (int)gi * bf::kMaxSeqPerLaunch, nb = st.n;
     hipError_t e = hipSuccess;
-    bf::VtParams vp{j.v, wsb + wl.vt_off, gr.pk, j.k_hstride, Tpad, Hkv};
-    e = bf::launch_vt_transpose(dtype, vp, st, j.stream);
-    if (e != hipSuccess) return fail(BF_ERR_HIP, "vt_transpose launch: %s", hipGetErrorString(e));
-    if ((bifocal && gr.any_far && !band_only) || paged) {
-      // band-only or s = 1 sequences get no rotation: the prep only gathers
-      bf::PrepParams prep{j.q, j.k, wsb + wl.q2_off, wsb + wl.k2_off, paged ? wsb + wl.kc_off : nullptr, gr.pk,
-                          j.k_hstride, (int)Tq, (int)Tk, Hq, Hkv, mode, shift ? 1 : 0, j.w0};
-      e = bf::launch_correction_prep(dtype, prep, st, tt, j.stream);
+    if (!stored) {
+      bf::VtParams vp{j.v, wsb + wl.vt_off, gr.pk, j.k_hstride, Tpad, Hkv, 0};
+      e = bf::launch_vt_transpose(dtype, vp, st, j.stream);
+      if (e != hipSuccess) return fail(BF_ERR_HIP, "vt_transpose launch: %s", hipGetErrorString(e));
+      if ((bifocal && gr.any_far && !band_only) || paged) {
+        // band-only or s = 1 sequences get no rotation: the prep only gathers
+        bf::PrepParams prep{j.q, j.k, wsb + wl.q2_off, wsb + wl.k2_off, paged ? wsb + wl.kc_off : nullptr, gr.pk,
+                            j.k_hstride, (int)Tq, (int)Tk, Hq, Hkv, mode, shift ? 1 : 0, j.w0, 0, {}};
+        e = bf::launch_correction_prep(dtype, prep, st, tt, j.stream);
+        if (e != hipSuccess) return fail(BF_ERR_HIP, "correction_prep launch: %s", hipGetErrorString(e));
+      }
+    } else {
+      // V^T of the tiles from each sequence's first new key on (the tile of
+      // kfirst is redone whole: its keys past the old length were zero)
+      bf::SeqTable sv = st;
+      sv.vt_off[0] = 0;
+      for (int i = 0; i < nb; ++i) {
+        const int N = st.kcu[i + 1] - st.kcu[i];
+        sv.vt_t0[i] = j.kfirst[b0 + i] / bf::kKeyTile;
+        sv.vt_off[i + 1] = sv.vt_off[i] + ((N + bf::kKeyTile - 1) / bf::kKeyTile - sv.vt_t0[i]) * bf::kKeyTile;
+      }
+      if (sv.vt_off[nb] > 0) {
+        bf::VtParams vp{j.v, const_cast<void*>(pp.vt), gr.pk, j.k_hstride, 0, Hkv,
+                        (int)(j.store_cap64 / bf::kKeyTile)};
+        e = bf::launch_vt_transpose(dtype, vp, sv, j.stream);
+        if (e != hipSuccess) return fail(BF_ERR_HIP, "vt_transpose launch: %s", hipGetErrorString(e));
+      }
+      // q'' of the chunk and k'' of keys kfirst .. N - 1 into the store, for
+      // every sequence with s > 1 (also one whose keys are all local yet:
+      // the store then holds its far keys for later calls)
+      bf::SeqTable sp = st;
+      sp.kcu[0] = 0;
+      for (int i = 0; i < nb; ++i)
+        sp.kcu[i + 1] = sp.kcu[i] + (st.kcu[i + 1] - st.kcu[i]) - j.kfirst[b0 + i];
+      bf::PrepParams prep{j.q, j.k, wsb + wl.q2_off, const_cast<void*>(pp.k2), nullptr, gr.pk, j.k_hstride,
+                          (int)Tq, 0, Hq, Hkv, mode, shift ? 1 : 0, j.w0, (int)j.store_cap64, {}};
+      for (int i = 0; i < nb; ++i) prep.kfirst[i] = j.kfirst[b0 + i];
+      e = bf::launch_correction_prep(dtype, prep, sp, tt, j.stream);
       if (e != hipSuccess) return fail(BF_ERR_HIP, "correction_prep launch: %s", hipGetErrorString(e));
+    }
+    // a store: the main kernel finds k'' and V^T of sequence i at
+    // (i * Hkv + h) * cap64 rows and columns of the group's part of it
+    bf::SeqTable sm;
+    if (stored) {
+      sm = st;
+      for (int i = 0; i <= nb; ++i) sm.kcu[i] = sm.vt_off[i] = (int)(i * Hkv * j.store_cap64);
+      for (int i = 0; i < nb; ++i) sm.vt_t0[i] = 0;
     }
     if (trace_on())
       fprintf(stderr, "[bifocal] prefill %s dtype=%d seqs=%d..%d grid=%lld P_wg=%d hpw=%d n_hsub=%d s0=%d qpos0=%d w0=%lld key_splits=%d\n",
               band_only ? "band-only" : bifocal ? "bifocal" : "plain", dtype, b0, b0 + nb - 1, gr.grid, geo.P_wg, geo.hpw,
               geo.n_hsub, st.s[0], st.qpos[0], j.w0, pp.nks);
-    e = bf::launch_prefill_main(dtype, bifocal && gr.any_far, band_only && gr.any_far, pp, st, (int)gr.grid, j.stream);
+    e = bf::launch_prefill_main(dtype, bifocal && gr.any_far, band_only && gr.any_far, pp, stored ? sm : st,
+                                (int)gr.grid, j.stream);
     if (e != hipSuccess) return fail(BF_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
     if (pp.nks > 1) {
       e = bf::launch_chunk_combine(pp, st.cu[0], st.cu[nb] - st.cu[0], j.stream);
@@ -464,14 +525,35 @@ int run_prefill(bool bifocal, const void* q, const void* k, const void* v, void*
 }
 
 
+// The caller-kept k'' / V^T store of bifocal_prefill_chunk_stored: `bytes`
+// of device memory and two host arrays of per-sequence state.
+struct ChunkStore {
+  void* buf;
+  size_t bytes;
+  int32_t* keys;  // in/out: keys 0 .. keys[b] - 1 of sequence b are held ...
+  int32_t* s;     // ... for s = s[b]
+};
+
+// Bytes of a chunk store: k'' [batch][Hkv][cap64][D], then (256-aligned) V^T
+// [batch][Hkv][cap64 / 64][D][64], cap64 = cap rounded up to 64. 0 when a
+// launch group's offsets (64 sequences x Hkv x cap64) would not fit an int.
+size_t chunk_store_bytes(int batch, long long cap, int Hkv, int dtype) {
+  if (batch < 1 || cap < 1 || Hkv < 1) return 0;
+  const long long cap64 = (cap + bf::kKeyTile - 1) / bf::kKeyTile * bf::kKeyTile;
+  if ((long long)std::min(batch, bf::kMaxSeqPerLaunch) * Hkv * cap64 > 0x7fffffffLL) return 0;
+  const size_t region = align256((size_t)batch * Hkv * cap64 * bf::kHeadDim * elem_size(dtype));
+  return 2 * region;
+}
+
 // Chunk of queries against a KV cache [B][Hkv][cap][D] (bifocal_prefill_chunk)
 // or a paged cache (bifocal_prefill_chunk_paged: pages != null, cap = the
-// most keys a sequence's pages hold).
+// most keys a sequence's pages hold); with `store`, k'' and V^T are kept
+// between calls (bifocal_prefill_chunk_stored, contiguous caches only).
 int run_chunk(const void* q, const void* kc, const void* vc, void* o, float* lse,
               const int32_t* cu_q, const int32_t* seqlens, const int32_t* s_len, int batch,
               int cap, int Hq, int Hkv, int head_dim, int dtype, long long w0, long long w_pre,
               double theta, int mode, float scale, void* ws, size_t ws_bytes, hipStream_t stream,
-              const ChunkPages* pages = nullptr) {
+              const ChunkPages* pages = nullptr, const ChunkStore* store = nullptr) {
   if (!q || !kc || !vc || !o || !cu_q || !seqlens)
     return fail(BF_ERR_INVALID_ARG, "null tensor, cu_q or seqlens pointer");
   int rc = check_rows_common(true, batch, Hq, Hkv, head_dim, dtype, w0, w_pre, theta, mode, scale);
@@ -500,6 +582,23 @@ int run_chunk(const void* q, const void* kc, const void* vc, void* o, float* lse
   if (!aligned16(q) || !aligned16(kc) || !aligned16(vc) || !aligned16(o))
     return fail(BF_ERR_INVALID_ARG, "q, k_cache, v_cache and o must be 16-byte aligned");
   if (lse && ((uintptr_t)lse & 3u)) return fail(BF_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  size_t store_need = 0;
+  if (store) {
+    if ((mode & ~BF_LONG_SHIFT) == BF_LONG_NONE)
+      return fail(BF_ERR_UNSUPPORTED, "band-only attention (long_mode NONE) has no k'' to store");
+    if (!store->buf || ((uintptr_t)store->buf & 255u))
+      return fail(BF_ERR_INVALID_ARG, "store must be a non-null 256-byte aligned device pointer");
+    if (!store->keys || !store->s)
+      return fail(BF_ERR_INVALID_ARG, "store_keys_host and store_s_host must be non-null");
+    store_need = chunk_store_bytes(batch, cap, Hkv, dtype);
+    if (store_need == 0)
+      return fail(BF_ERR_UNSUPPORTED, "store of 64 sequences x %d KV heads x %d keys exceeds 2^31 rows", Hkv, cap);
+    if (store->bytes < store_need)
+      return fail(BF_ERR_WORKSPACE, "store too small: %zu bytes given, %zu needed", store->bytes, store_need);
+    for (int b = 0; b < batch; ++b)
+      if (store->keys[b] < 0)
+        return fail(BF_ERR_INVALID_ARG, "store_keys_host[%d] = %d is negative", b, store->keys[b]);
+  }
   RowsJob j;
   j.bifocal = true;
   j.q = q; j.k = kc; j.v = vc; j.o = o; j.lse = lse;
@@ -519,7 +618,25 @@ int run_chunk(const void* q, const void* kc, const void* vc, void* o, float* lse
   j.w0 = w0; j.w_pre = w_pre; j.theta = theta; j.mode = mode; j.scale = scale;
   j.ws = ws; j.ws_bytes = ws_bytes; j.stream = stream;
   j.split_cap = chunk_split_cap(j.cu[batch], Hq, Hkv, dtype);
-  return run_rows(j);
+  std::vector<int> s_of(batch, 1);
+  if (store) {
+    j.store = (char*)store->buf;
+    j.store_cap64 = (cap + bf::kKeyTile - 1) / bf::kKeyTile * bf::kKeyTile;
+    j.store_vt_off = store_need / 2;
+    j.kfirst.resize(batch);
+    for (int b = 0; b < batch; ++b) {
+      // an s outside [1, 2^30] is rejected by run_rows before any launch
+      s_of[b] = (int)std::min<long long>(bifocal_s_of_L(j.slen[b], w_pre), 1LL << 30);
+      j.kfirst[b] = store->s[b] == s_of[b] ? std::min(store->keys[b], seqlens[b]) : 0;
+    }
+  }
+  rc = run_rows(j);
+  if (rc == BF_OK && store)
+    for (int b = 0; b < batch; ++b) {
+      store->keys[b] = seqlens[b];
+      store->s[b] = s_of[b];
+    }
+  return rc;
 }
 
 int rope_prefill_impl(const void* q_raw, const void* k_raw, const void* v, void* q_out,
@@ -666,6 +783,28 @@ int bifocal_prefill_chunk_paged(const void* q, const void* k_pages, const void* 
   return run_chunk(q, k_pages, v_pages, o, lse, cu_q_host, seqlens_host, s_len_host, batch, 1,
                    n_heads_q, n_heads_kv, head_dim, dtype, w0, w_pre, rope_theta, long_mode,
                    softmax_scale, workspace, workspace_bytes, (hipStream_t)stream, &pg);
+}
+
+size_t bifocal_chunk_store_bytes(int32_t batch, int32_t cache_capacity, int32_t n_heads_kv,
+                                 int32_t head_dim, int32_t dtype) {
+  if (head_dim != bf::kHeadDim || (dtype != BF_DTYPE_BF16 && dtype != BF_DTYPE_FP32)) return 0;
+  return chunk_store_bytes(batch, cache_capacity, n_heads_kv, dtype);
+}
+
+int bifocal_prefill_chunk_stored(const void* q, const void* k_cache, const void* v_cache,
+                                 void* store, size_t store_bytes, void* o, float* lse,
+                                 const int32_t* cu_q_host, const int32_t* seqlens_host,
+                                 const int32_t* s_len_host, int32_t* store_keys_host,
+                                 int32_t* store_s_host, int32_t batch, int32_t cache_capacity,
+                                 int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim,
+                                 int32_t dtype, int64_t w0, int64_t w_pre, double rope_theta,
+                                 int32_t long_mode, float softmax_scale, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  const ChunkStore cs{store, store_bytes, store_keys_host, store_s_host};
+  return run_chunk(q, k_cache, v_cache, o, lse, cu_q_host, seqlens_host, s_len_host, batch,
+                   cache_capacity, n_heads_q, n_heads_kv, head_dim, dtype, w0, w_pre, rope_theta,
+                   long_mode, softmax_scale, workspace, workspace_bytes, (hipStream_t)stream,
+                   nullptr, &cs);
 }
 
 int bifocal_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,

@@ -190,7 +190,7 @@ __global__ __launch_bounds__(256) void correction_prep_kernel(PrepParams p, SeqT
   const bool rot = s > 1;         // s = 1: no far branch for this sequence
   const bool copy = keys && p.kcopy != nullptr;  // paged keys: gather the packed copy
   if (!rot && !copy) return;
-  const long long row = tok - cu[b];
+  const long long row = tok - cu[b] + (keys ? p.kfirst[b] : 0);
   if (keys && row < (long long)st.vt_t0[b] * kKeyTile) return;  // key no window reaches
   float c[E], sn[E];
   if (rot) {
@@ -206,7 +206,8 @@ __global__ __launch_bounds__(256) void correction_prep_kernel(PrepParams p, SeqT
     T* dst;
     if (keys) {
       src = (const T*)p.k + kv_row(p.pk, st, p.k_hstride, p.Hkv, b, h, row) * kHeadDim;
-      dst = (T*)p.k2 + ((size_t)h * p.Tk + tok) * kHeadDim;
+      dst = (T*)p.k2 + (p.k2_cap > 0 ? ((size_t)b * p.Hkv + h) * p.k2_cap + row
+                                     : (size_t)h * p.Tk + tok) * kHeadDim;
     } else {
       src = (const T*)p.q + ((size_t)h * p.T + tok) * kHeadDim;
       dst = (T*)p.q2 + ((size_t)h * p.T + tok) * kHeadDim;
@@ -245,6 +246,13 @@ __device__ __forceinline__ int seq_of_vt(const SeqTable& st, int c) {
   return lo;
 }
 
+// Destination tile of padded column c (key p0 of sequence b, KV head h): the
+// packed axis, or the store's tile of (b, h, p0 / 64).
+__device__ __forceinline__ size_t vt_tile_index(const VtParams& p, int b, int h, int c, int p0) {
+  return p.store_tiles > 0 ? ((size_t)b * p.Hkv + h) * p.store_tiles + p0 / kKeyTile
+                           : (size_t)h * (p.Tpad / kKeyTile) + c / kKeyTile;
+}
+
 // fp32 V^T: one 256-thread workgroup per (64-key tile, KV head), through LDS.
 __global__ __launch_bounds__(256) void vt_transpose_f32_kernel(VtParams p, SeqTable st) {
   __shared__ float tile[kKeyTile][kHeadDim + 1];
@@ -266,7 +274,7 @@ __global__ __launch_bounds__(256) void vt_transpose_f32_kernel(VtParams p, SeqTa
     tile[r][d] = vr >= 0 ? v[(size_t)vr * kHeadDim + d] : 0.f;
   }
   __syncthreads();
-  float* vt = (float*)p.vt + ((size_t)h * (p.Tpad / kKeyTile) + c / kKeyTile) * (kHeadDim * kKeyTile);
+  float* vt = (float*)p.vt + vt_tile_index(p, b, h, c, p0) * (kHeadDim * kKeyTile);
   for (int e = threadIdx.x; e < kKeyTile * kHeadDim; e += 256) {
     const int d = e / kKeyTile, r = e % kKeyTile;
     vt[d * kKeyTile + r] = tile[r][d];
@@ -304,8 +312,7 @@ __global__ __launch_bounds__(128) void vt_transpose_bf16_kernel(VtParams p, SeqT
     in[k][2] = x.z;
     in[k][3] = x.w;
   }
-  uint16_t* vt = (uint16_t*)p.vt +
-                 ((size_t)h * (p.Tpad / kKeyTile) + c / kKeyTile) * (kHeadDim * kKeyTile);
+  uint16_t* vt = (uint16_t*)p.vt + vt_tile_index(p, b, h, c, p0) * (kHeadDim * kKeyTile);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {  // head dim 8 db + i: keys 8 kb .. 8 kb + 7, two per word
     uint32_t w[4];
@@ -909,8 +916,8 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillParams p, S
 
   // ends of the K, K'' and V^T tensors (range limit of the staging loads)
   const char* k_end = (const char*)p.k + (size_t)p.k_rows * kHeadDim * 2;
-  const char* k2_end = (const char*)p.k2 + (size_t)p.Hkv * p.Tk * kHeadDim * 2;
-  const char* vt_end = (const char*)p.vt + (size_t)p.Hkv * p.Tpad * kHeadDim * 2;
+  const char* k2_end = (const char*)p.k2 + (size_t)p.k2_rows * kHeadDim * 2;
+  const char* vt_end = (const char*)p.vt + (size_t)p.vt_rows * kHeadDim * 2;
 
   RowState rs{-INFINITY, 0.f, 1.f, false};
   f32x16 oacc[4];

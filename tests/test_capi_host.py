@@ -343,6 +343,65 @@ def test_chunk_later_launch_group_is_validated_before_any_launch(L, monkeypatch)
     assert b"s(L)" in L.bifocal_last_error()
 
 
+def _chunk_stored(L, keys, svals, **kw):
+    a = dict(q=P, kc=P, vc=P, store=ctypes.c_void_p(0x200000), store_bytes=1 << 30, o=P, lse=None,
+             cu=[0, 30, 31], sl=[100, 1], s_len=None, cap=128, Hq=4, Hkv=2, D=128, dtype=0, w0=16,
+             w_pre=64, theta=1e4, mode=0, scale=0.088, ws=P, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    cu = (ctypes.c_int32 * len(a["cu"]))(*a["cu"])
+    sl = (ctypes.c_int32 * len(a["sl"]))(*a["sl"])
+    sls = (ctypes.c_int32 * len(a["s_len"]))(*a["s_len"]) if a["s_len"] is not None else None
+    return L.bifocal_prefill_chunk_stored(a["q"], a["kc"], a["vc"], a["store"], a["store_bytes"],
+                                          a["o"], a["lse"], cu, sl, sls, keys, svals,
+                                          len(a["cu"]) - 1, a["cap"], a["Hq"], a["Hkv"], a["D"],
+                                          a["dtype"], a["w0"], a["w_pre"], a["theta"], a["mode"],
+                                          a["scale"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+def test_chunk_store_bytes(L):
+    # k'' and V^T of every cache position, the capacity padded to 64 keys
+    assert bfl.chunk_store_bytes(1, 131072, 8) == 2 * 8 * 131072 * 128 * 2
+    assert bfl.chunk_store_bytes(2, 100, 1) == 2 * 2 * 128 * 128 * 2
+    assert bfl.chunk_store_bytes(3, 65, 2, dtype=bfl.torch.float32) == 2 * 3 * 2 * 128 * 128 * 4
+    assert L.bifocal_chunk_store_bytes(1, 100, 1, 64, 0) == 0       # head_dim 64
+    assert L.bifocal_chunk_store_bytes(0, 100, 1, 128, 0) == 0      # no sequences
+    assert L.bifocal_chunk_store_bytes(1, 100, 1, 128, 5) == 0      # bad dtype
+    # 64 sequences x 32 heads x 2^20 keys: launch-group offsets past 2^31
+    assert L.bifocal_chunk_store_bytes(64, 1 << 20, 32, 128, 0) == 0
+
+
+@pytest.mark.parametrize("kw,keys,code", [
+    (dict(store=None), 0, -1), (dict(store=ctypes.c_void_p(0x200080)), 0, -1),
+    (dict(store_bytes=1000), 0, -3), (dict(), -5, -1), (dict(mode=2), 0, -2), (dict(mode=6), 0, -1),
+    (dict(sl=[129, 1]), 0, -1), (dict(q=None), 0, -1), (dict(ws_bytes=1000), 0, -3),
+    (dict(D=64), 0, -2), (dict(mode=9), 0, -1),
+])
+def test_chunk_stored_validation(L, kw, keys, code):
+    # rejected before any HIP call; the caller's store counters stay as they were
+    k = (ctypes.c_int32 * 2)(keys, 3)
+    sv = (ctypes.c_int32 * 2)(7, 7)
+    before = (list(k), list(sv))
+    assert _chunk_stored(L, k, sv, **kw) == code
+    assert len(L.bifocal_last_error()) > 0
+    assert (list(k), list(sv)) == before
+
+
+def test_chunk_stored_null_counters(L):
+    k = (ctypes.c_int32 * 2)(0, 0)
+    assert _chunk_stored(L, None, k) == -1
+    assert _chunk_stored(L, k, None) == -1
+
+
+def test_chunk_stored_failed_launch_keeps_counters(L, monkeypatch):
+    # valid arguments reach the launches; a launch failure leaves the counters
+    monkeypatch.setenv("BIFOCAL_TEST_FAIL_LAUNCH", "1")
+    k = (ctypes.c_int32 * 2)(40, 0)
+    sv = (ctypes.c_int32 * 2)(2, 0)
+    assert _chunk_stored(L, k, sv) == bfl.BF_ERR_HIP
+    assert _chunk_stored(L, k, sv, dtype=1, mode=5, s_len=[1000, 1]) == bfl.BF_ERR_HIP
+    assert list(k) == [40, 0] and list(sv) == [2, 0]
+
+
 def _chunk_paged(L, **kw):
     a = dict(q=P, kp=P, vp=P, o=P, lse=None, bt=P, cu=[0, 30, 31], sl=[100, 1], s_len=None,
              page=16, maxp=8, npages=20, Hq=4, Hkv=2, D=128, dtype=0, w0=16, w_pre=64, theta=1e4,
