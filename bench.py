@@ -429,15 +429,21 @@ def main():
         fn = lambda: bfl.decode(qs, ks, vs, [n], dcfg["w0"], dcfg["w_pre"], dcfg["theta"], "fi",
                                 scale, workspace=ws_s)
         pfn = lambda: bfl.plain_decode(qs, ks, vs, [n], scale, workspace=ws_s)
+        # with a far-key store, timed in the same warm state as the other two
+        store_s = bfl.DecodeStore(ks)
+        sfn = lambda: bfl.decode_stored(qs, ks, vs, store_s, [n], dcfg["w0"], dcfg["w_pre"],
+                                        dcfg["theta"], "fi", scale, workspace=ws_s)
         for _ in range(10):
             fn()
             pfn()
+            sfn()
         t_b = time_calls(fn, 100, stream)
         t_p = time_calls(pfn, 100, stream)
+        t_s = time_calls(sfn, 100, stream)
+        del store_s
         nbytes = 2.0 * n * Hkv * D * 2
         t_c = cold_us(qs, ks, vs, n, ws_s, max(2, math.ceil(2 * MALL / nbytes))) * 1e-3
         t_pc = cold_us(qs, ks, vs, n, ws_s, max(2, math.ceil(2 * MALL / nbytes)), plain=True) * 1e-3
-        t_s = stored_us(qs, ks, vs, n, ws_s) * 1e-3
         small[str(n)] = {"bifocal_us": round(t_b * 1e3, 2), "plain_us": round(t_p * 1e3, 2),
                          "stored_us": round(t_s * 1e3, 2),
                          "bifocal_gbs": round(nbytes / (t_b * 1e-3) / 1e9, 1),
