@@ -13,8 +13,9 @@ flops 4 * D * Hq * L (L + 1) / 2 (one score and one PV product per causal
 pair) over the measured prefill time. Extra fields report the decode
 bandwidth, position aliasing, the library's plain causal attention on the
 same shapes (overhead reference), chunks of the last 512 / 4096 / 16384
-queries against the 128K cache (contiguous, with a chunk store that holds
-k'' and V^T of the keys before the chunk, and 4096 over 16-key pages), roofline
+queries against the 128K cache (contiguous and, for 512 / 4096, over 16-key
+pages; each also with a chunk store that holds k'' and V^T of the keys
+before the chunk), roofline
 fractions against MI355X peaks
 (bf16 dense MFMA 2.5 PFLOP/s, HBM 8 TB/s) and the fp64 CPU oracle timed on a
 bounded row sample of the prefill workload.
@@ -551,6 +552,15 @@ def main():
     kcc, vcc = kd.unsqueeze(0), vd.unsqueeze(0)  # [1, Hkv, L, D]: the cache layout, cap = L
     chunk = {}
     cstore = bfl.ChunkStore(kcc)
+    # the same cache as a shuffled pool of 16-key pages
+    npg = L // 16
+    perm = torch.randperm(npg, generator=torch.Generator().manual_seed(17)).cuda()
+    kpg = torch.empty((npg, Hkv, 16, D), dtype=torch.bfloat16, device="cuda")
+    vpg = torch.empty_like(kpg)
+    kpg[perm] = kd.view(Hkv, npg, 16, D).permute(1, 0, 2, 3)
+    vpg[perm] = vd.view(Hkv, npg, 16, D).permute(1, 0, 2, 3)
+    tbl = perm.to(torch.int32).view(1, npg)
+    pstore = bfl.ChunkStore(kpg, batch=1, max_pages_per_seq=npg)
     for lq in (512, 4096, 16384):
         qch = qd[:, L - lq:].contiguous()
         och = torch.empty_like(qch)
@@ -574,23 +584,27 @@ def main():
         chunk[f"{lq}_stored"] = {"ms": round(s_ms, 3),
                                  "tflops": round(c_flops / (s_ms * 1e-3) / 1e12, 2)}
         del wss
-        if lq == 4096:  # the same chunk over a shuffled pool of 16-key pages
-            npg = L // 16
-            perm = torch.randperm(npg, generator=torch.Generator().manual_seed(17)).cuda()
-            kpg = torch.empty((npg, Hkv, 16, D), dtype=torch.bfloat16, device="cuda")
-            vpg = torch.empty_like(kpg)
-            kpg[perm] = kd.view(Hkv, npg, 16, D).permute(1, 0, 2, 3)
-            vpg[perm] = vd.view(Hkv, npg, 16, D).permute(1, 0, 2, 3)
-            tbl = perm.to(torch.int32).view(1, npg)
+        if lq <= 4096:  # the same chunk over the page pool, stateless and with a store
             wsp = bfl.alloc_workspace(bfl.chunk_workspace_bytes(1, lq, L, Hq, Hkv, paged=True), "cuda")
             pfn = lambda: bfl.prefill_chunk_paged(qch, kpg, vpg, tbl, [0, lq], [L], cfg["w0"],
                                                   cfg["w_pre"], cfg["theta"], "fi", scale, out=och,
                                                   workspace=wsp)
             pfn()
             p_ms = time_calls(pfn, 5, stream)
-            chunk["4096_paged16"] = {"ms": round(p_ms, 3),
-                                     "tflops": round(c_flops / (p_ms * 1e-3) / 1e12, 2)}
-            del kpg, vpg, tbl, wsp
+            chunk[f"{lq}_paged16"] = {"ms": round(p_ms, 3),
+                                      "tflops": round(c_flops / (p_ms * 1e-3) / 1e12, 2)}
+
+            def psfn():
+                pstore.reset(keys=L - lq)
+                bfl.prefill_chunk_stored_paged(qch, kpg, vpg, tbl, pstore, [0, lq], [L], cfg["w0"],
+                                               cfg["w_pre"], cfg["theta"], "fi", scale, out=och,
+                                               workspace=wsp)
+            psfn()
+            ps_ms = time_calls(psfn, 5, stream)
+            chunk[f"{lq}_paged16_stored"] = {"ms": round(ps_ms, 3),
+                                             "tflops": round(c_flops / (ps_ms * 1e-3) / 1e12, 2)}
+            del wsp
+        if lq == 4096:
             # band-only (a sliding-window layer): the same chunk sees only its
             # window; its work is the pairs with i - j < w0
             bfn = lambda: bfl.prefill_chunk(qch, kcc, vcc, [0, lq], [L], cfg["w0"], cfg["w_pre"],
@@ -601,7 +615,7 @@ def main():
             chunk["4096_band"] = {"ms": round(b_ms, 3),
                                   "tflops": round(b_flops / (b_ms * 1e-3) / 1e12, 2)}
         del qch, och, wsc
-    del cstore
+    del cstore, pstore, kpg, vpg, tbl
 
     log("raw-input pre-step")
     qr, kr = qd.clone(), kd.clone()

@@ -215,7 +215,8 @@ int bifocal_prefill_chunk_paged(const void* q, const void* k_pages, const void* 
 
 /*
  * Bytes of the store of bifocal_prefill_chunk_stored for `batch` sequences
- * of a cache with cache_capacity keys and n_heads_kv KV heads (k'' and V^T of
+ * of a cache with cache_capacity keys (max_pages_per_seq * page_size for the
+ * paged form) and n_heads_kv KV heads (k'' and V^T of
  * every cache position, padded to 64 keys). Returns 0 for invalid arguments
  * and when 64 sequences x n_heads_kv x cache_capacity (rounded up to 64)
  * exceed 2^31 - 1 key rows.
@@ -264,6 +265,33 @@ int bifocal_prefill_chunk_stored(const void* q, const void* k_cache, const void*
                                  int32_t dtype, int64_t w0, int64_t w_pre, double rope_theta,
                                  int32_t long_mode, float softmax_scale, void* workspace,
                                  size_t workspace_bytes, void* stream);
+
+/*
+ * bifocal_prefill_chunk_stored over a PAGED KV cache: the arguments of
+ * bifocal_prefill_chunk_paged plus the store and host arrays of
+ * bifocal_prefill_chunk_stored. The store is sized by
+ * bifocal_chunk_store_bytes(batch, max_pages_per_seq * page_size, ...) and
+ * indexed by sequence and position (not by page). The call still gathers
+ * into the workspace's packed copy the keys its local pass reads: from the
+ * window start of the chunk's first query on (64-aligned; every key when s
+ * = 1), plus any key without a stored k''.
+ *   workspace        : bifocal_chunk_workspace_bytes(..., paged = 1), as for
+ *                      bifocal_prefill_chunk_paged
+ * The result is bitwise that of bifocal_prefill_chunk_paged given a workspace
+ * of the same size (and of bifocal_prefill_chunk_stored on a contiguous cache
+ * holding the same keys). Validation errors leave outputs, store and both
+ * host arrays untouched.
+ */
+int bifocal_prefill_chunk_stored_paged(const void* q, const void* k_pages, const void* v_pages,
+                                       void* store, size_t store_bytes, void* o, float* lse,
+                                       const int32_t* block_table, const int32_t* cu_q_host,
+                                       const int32_t* seqlens_host, const int32_t* s_len_host,
+                                       int32_t* store_keys_host, int32_t* store_s_host,
+                                       int32_t batch, int32_t page_size, int32_t max_pages_per_seq,
+                                       int32_t num_pages, int32_t n_heads_q, int32_t n_heads_kv,
+                                       int32_t head_dim, int32_t dtype, int64_t w0, int64_t w_pre,
+                                       double rope_theta, int32_t long_mode, float softmax_scale,
+                                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Single-token bifocal decode over a KV cache (bf16 only).

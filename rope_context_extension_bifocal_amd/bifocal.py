@@ -32,7 +32,8 @@ EXPORTED = ("bifocal_s_of_L", "bifocal_workspace_bytes", "bifocal_prefill", "bif
             "bifocal_rope_prefill_paged", "bifocal_rope_append_paged",
             "bifocal_test_pair_map", "bifocal_last_error", "bifocal_decode_noalloc",
             "bifocal_test_angles", "bifocal_decode_stored", "bifocal_decode_stored_paged",
-            "bifocal_chunk_store_bytes", "bifocal_prefill_chunk_stored")
+            "bifocal_chunk_store_bytes", "bifocal_prefill_chunk_stored",
+            "bifocal_prefill_chunk_stored_paged")
 
 _lib = None
 
@@ -71,6 +72,10 @@ def lib():
         L.bifocal_prefill_chunk_stored.argtypes = [p, p, p, p, sz, p, p, p, p, p, p, p, i32, i32,
                                                    i32, i32, i32, i32, i64, i64, f64, i32, f32, p,
                                                    sz, p]
+        L.bifocal_prefill_chunk_stored_paged.restype = ctypes.c_int
+        L.bifocal_prefill_chunk_stored_paged.argtypes = [p, p, p, p, sz, p, p, p, p, p, p, p, p, i32,
+                                                         i32, i32, i32, i32, i32, i32, i32, i64, i64,
+                                                         f64, i32, f32, p, sz, p]
         L.bifocal_prefill_chunk.restype = ctypes.c_int
         L.bifocal_prefill_chunk.argtypes = [p, p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32,
                                             i64, i64, f64, i32, f32, p, sz, p]
@@ -215,13 +220,18 @@ def chunk_store_bytes(batch, cache_capacity, n_heads_kv, head_dim=128, dtype=tor
 
 
 class ChunkStore:
-    """Caller-kept state of prefill_chunk_stored for one cache [B,Hkv,cap,D]:
-    an opaque device buffer holding k'' and V^T of the cache positions and,
-    per sequence, how many keys it holds (keys) and for which s (s). The
-    library updates keys and s."""
+    """Caller-kept state of prefill_chunk_stored for one cache [B,Hkv,cap,D]
+    (or, for prefill_chunk_stored_paged, a page pool [pages,Hkv,page,D] with
+    `batch` and `max_pages_per_seq` given): an opaque device buffer holding
+    k'' and V^T of the cache positions and, per sequence, how many keys it
+    holds (keys) and for which s (s). The library updates keys and s."""
 
-    def __init__(self, k_cache):
-        B, Hkv, cap, D = k_cache.shape
+    def __init__(self, k_cache, batch=None, max_pages_per_seq=None):
+        if batch is None:
+            B, Hkv, cap, D = k_cache.shape
+        else:  # a page pool: capacity = pages per sequence x page size
+            B, Hkv, D = int(batch), k_cache.shape[1], k_cache.shape[3]
+            cap = int(max_pages_per_seq) * k_cache.shape[2]
         n = chunk_store_bytes(B, cap, Hkv, D, k_cache.dtype)
         if n == 0:
             raise ValueError("no chunk store for a cache of shape %s" % (tuple(k_cache.shape),))
@@ -259,6 +269,34 @@ def prefill_chunk_stored(q, k_cache, v_cache, store, cu_q, seqlens, w0, w_pre, r
         _ptr(lse), cu, sl, sls, store.keys, store.s, B, cap, Hq, Hkv, D, _DTYPES[q.dtype], int(w0),
         int(w_pre), float(rope_theta), LONG_MODES[long_mode], _scale(softmax_scale, D),
         _ptr(workspace), workspace.numel(), _stream(stream)))
+    return (o, lse) if return_lse else o
+
+
+def prefill_chunk_stored_paged(q, k_pages, v_pages, block_table, store, cu_q, seqlens, w0, w_pre,
+                               rope_theta, long_mode="fi", softmax_scale=None, s_len=None,
+                               return_lse=False, out=None, lse=None, workspace=None, stream=None):
+    """prefill_chunk_paged with a ChunkStore (made with batch and
+    max_pages_per_seq); bitwise prefill_chunk_paged with the same workspace
+    size (both defaults are the same)."""
+    Hq, Tq, D = q.shape
+    Hkv, page = k_pages.shape[1], k_pages.shape[2]
+    num_pages = k_pages.shape[0]
+    B = len(cu_q) - 1
+    maxp = block_table.shape[1]
+    o = out if out is not None else torch.empty_like(q)
+    if return_lse and lse is None:
+        lse = torch.empty((Hq, Tq), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = alloc_workspace(chunk_workspace_bytes(B, Tq, sum(int(n) for n in seqlens), Hq,
+                                                          Hkv, D, q.dtype, paged=True), q.device)
+    cu = _i32_array(cu_q)
+    sl = _i32_array(seqlens)
+    sls = _i32_array(s_len) if s_len is not None else None
+    _check(lib().bifocal_prefill_chunk_stored_paged(
+        _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(store.buf), store.buf.numel(), _ptr(o),
+        _ptr(lse), _ptr(block_table), cu, sl, sls, store.keys, store.s, B, page, maxp, num_pages, Hq,
+        Hkv, D, _DTYPES[q.dtype], int(w0), int(w_pre), float(rope_theta), LONG_MODES[long_mode],
+        _scale(softmax_scale, D), _ptr(workspace), workspace.numel(), _stream(stream)))
     return (o, lse) if return_lse else o
 
 

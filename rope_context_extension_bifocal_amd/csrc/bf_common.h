@@ -91,10 +91,13 @@ struct PrepParams {
   int shift;      // 1: queries get the band-edge continuity shift w0 - phi(w0)
   long long w0;
   // k2_cap > 0: k'' of key j of sequence b (of the launch) goes to row
-  // (b * Hkv + h) * k2_cap + j of the store, and the packed key axis (kcu)
-  // holds only keys kfirst[b] .. N_b - 1; k2_cap = 0: the packed layout, kfirst 0
+  // (b * Hkv + h) * k2_cap + j of the store, the packed key axis (kcu) holds
+  // only keys kfirst[b] .. N_b - 1 (all of them copied when kcopy is set), and
+  // only keys from krot[b] on are rotated (the store holds the ones below);
+  // k2_cap = 0: the packed layout, kfirst 0
   int k2_cap;
   int kfirst[kMaxSeqPerLaunch];
+  int krot[kMaxSeqPerLaunch];
 };
 
 struct VtParams {

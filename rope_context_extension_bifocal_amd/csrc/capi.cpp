@@ -117,10 +117,10 @@ struct PrefillWs {
 
 // Workspace of Tq packed queries against Tk keys (a one-shot prefill has
 // Tk = Tq = T): V^T padded per sequence, q'', k'', for a paged key source the
-// packed copy of the keys (base ends here), and for `splits` > 1 key splits
-// their partial O (fp32) and log2-sum-exp.
+// packed copy of the keys (Tk_copy of them, by default Tk; base ends here),
+// and for `splits` > 1 key splits their partial O (fp32) and log2-sum-exp.
 PrefillWs prefill_ws_layout(int batch, long long Tq, long long Tk, int Hq, int Hkv, int dtype,
-                            bool paged = false, int splits = 1) {
+                            bool paged = false, int splits = 1, long long Tk_copy = -1) {
   const size_t es = elem_size(dtype);
   const size_t tpad_bound = (size_t)Tk + 63u * (size_t)batch;
   PrefillWs w;
@@ -128,7 +128,8 @@ PrefillWs prefill_ws_layout(int batch, long long Tq, long long Tk, int Hq, int H
   w.q2_off = align256((size_t)Hkv * bf::kHeadDim * tpad_bound * es);
   w.k2_off = w.q2_off + align256((size_t)Hq * (size_t)Tq * bf::kHeadDim * es);
   w.kc_off = w.k2_off + align256((size_t)Hkv * (size_t)Tk * bf::kHeadDim * es);
-  w.base = w.kc_off + (paged ? align256((size_t)Hkv * (size_t)Tk * bf::kHeadDim * es) : 0);
+  if (Tk_copy < 0) Tk_copy = Tk;
+  w.base = w.kc_off + (paged ? align256((size_t)Hkv * (size_t)Tk_copy * bf::kHeadDim * es) : 0);
   const size_t rows = splits > 1 ? (size_t)splits * Hq * (size_t)Tq : 0;
   w.po_off = w.base;
   w.pl_off = w.po_off + align256(rows * bf::kHeadDim * sizeof(float));
@@ -271,7 +272,23 @@ int run_rows(RowsJob& j) {
   const bool paged = j.pk.block_table != nullptr;
   const bool stored = j.store != nullptr;
   const long long Tk_ws = stored ? 0 : Tk;  // a store holds k'' and V^T: none in the workspace
-  const PrefillWs wl = prefill_ws_layout(batch, Tq, Tk_ws, Hq, Hkv, dtype, paged);
+  // with a store, the prep's key axis of sequence b holds keys ax0[b] ..
+  // N_b - 1 (at acu[b] ..): those without a stored k'' and, for a paged
+  // source, also every key the local pass reads (from the window start of
+  // the chunk's first query on), which go to the packed copy
+  std::vector<int> ax0(batch, 0), acu(batch + 1, 0);
+  if (stored) {
+    for (int b = 0; b < batch; ++b) {
+      const long long N = kcu[b + 1] - kcu[b];
+      const long long s = std::max<long long>(1, bifocal_s_of_L(j.slen[b], j.w_pre));
+      const long long win = s > 1 ? std::max(0LL, (long long)j.qpos[b] - j.w0 + 1) : 0;
+      const long long kc0 = win / bf::kKeyTile * bf::kKeyTile;
+      ax0[b] = (int)(paged ? std::min<long long>(j.kfirst[b], kc0) : j.kfirst[b]);
+      acu[b + 1] = acu[b] + (int)(N - ax0[b]);
+    }
+  }
+  const long long Tk_copy = stored ? acu[batch] : Tk;  // rows of the packed copy (paged)
+  const PrefillWs wl = prefill_ws_layout(batch, Tq, Tk_ws, Hq, Hkv, dtype, paged, 1, Tk_copy);
   if (!j.ws) return fail(BF_ERR_WORKSPACE, "workspace is null");
   if ((uintptr_t)j.ws & 255u) return fail(BF_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   const bool shift = bifocal && (j.mode & BF_LONG_SHIFT);
@@ -283,7 +300,7 @@ int run_rows(RowsJob& j) {
   // key splits the workspace has room for (partials after the base layout)
   int split_cap = dtype == BF_DTYPE_BF16 ? std::max(1, std::min(j.split_cap, bf::kMaxKeySplits)) : 1;
   while (split_cap > 1 &&
-         prefill_ws_layout(batch, Tq, Tk_ws, Hq, Hkv, dtype, paged, split_cap).total > j.ws_bytes)
+         prefill_ws_layout(batch, Tq, Tk_ws, Hq, Hkv, dtype, paged, split_cap, Tk_copy).total > j.ws_bytes)
     --split_cap;
 
   const int G = Hq / Hkv;
@@ -328,8 +345,8 @@ int run_rows(RowsJob& j) {
       st.s[i] = (int)s;
       st.qpos[i] = j.qpos[b0 + i];
       // a paged source is gathered into the packed copy, which the tile
-      // kernel then reads like packed keys
-      st.kbase[i] = paged ? kcu[b0 + i] : j.kbase[b0 + i];
+      // kernel then reads like packed keys (with a store, from key ax0 on)
+      st.kbase[i] = paged ? (stored ? (long long)acu[b0 + i] - ax0[b0 + i] : kcu[b0 + i]) : j.kbase[b0 + i];
       // far pairs to score (bifocal) or to drop (band only): the last query
       // (position N - 1) reaches back past the window
       if ((s > 1 || band_only) && j.w0 < N) any_far = true;
@@ -359,8 +376,8 @@ int run_rows(RowsJob& j) {
     pp.lse = j.lse;
     pp.w0 = j.w0;
     pp.scale_log2 = j.scale * 1.4426950408889634f;
-    pp.k_hstride = paged ? Tk : j.k_hstride;
-    pp.k_rows = paged ? (long long)Hkv * Tk : j.k_rows;
+    pp.k_hstride = paged ? Tk_copy : j.k_hstride;
+    pp.k_rows = paged ? (long long)Hkv * Tk_copy : j.k_rows;
     pp.T = (int)Tq;
     pp.Tk = (int)Tk;
     pp.Tpad = Tpad;
@@ -374,7 +391,8 @@ int run_rows(RowsJob& j) {
     const long long wgs = (long long)Hkv * geo.n_hsub * total_items;
     pp.nks = split_cap > 1 ? pick_key_splits(wgs, visit_sum / total_items, split_cap) : 1;
     pp.part_o = pp.nks > 1 ? (float*)(wsb + wl.po_off) : nullptr;
-    pp.part_lse = pp.nks > 1 ? (float*)(wsb + prefill_ws_layout(batch, Tq, Tk_ws, Hq, Hkv, dtype, paged, pp.nks).pl_off)
+    pp.part_lse = pp.nks > 1 ? (float*)(wsb + prefill_ws_layout(batch, Tq, Tk_ws, Hq, Hkv, dtype, paged, pp.nks,
+                                                                  Tk_copy).pl_off)
                              : nullptr;
     pp.k2_rows = (long long)Hkv * Tk;
     pp.vt_rows = (long long)Hkv * Tpad;
@@ -408,7 +426,7 @@ int run_rows(RowsJob& j) {
       if ((bifocal && gr.any_far && !band_only) || paged) {
         // band-only or s = 1 sequences get no rotation: the prep only gathers
         bf::PrepParams prep{j.q, j.k, wsb + wl.q2_off, wsb + wl.k2_off, paged ? wsb + wl.kc_off : nullptr, gr.pk,
-                            j.k_hstride, (int)Tq, (int)Tk, Hq, Hkv, mode, shift ? 1 : 0, j.w0, 0, {}};
+                            j.k_hstride, (int)Tq, (int)Tk, Hq, Hkv, mode, shift ? 1 : 0, j.w0, 0, {}, {}};
         e = bf::launch_correction_prep(dtype, prep, st, tt, j.stream);
         if (e != hipSuccess) return fail(BF_ERR_HIP, "correction_prep launch: %s", hipGetErrorString(e));
       }
@@ -430,14 +448,17 @@ int run_rows(RowsJob& j) {
       }
       // q'' of the chunk and k'' of keys kfirst .. N - 1 into the store, for
       // every sequence with s > 1 (also one whose keys are all local yet:
-      // the store then holds its far keys for later calls)
+      // the store then holds its far keys for later calls); a paged source
+      // also gathers keys ax0 .. N - 1 into the packed copy
       bf::SeqTable sp = st;
-      sp.kcu[0] = 0;
-      for (int i = 0; i < nb; ++i)
-        sp.kcu[i + 1] = sp.kcu[i] + (st.kcu[i + 1] - st.kcu[i]) - j.kfirst[b0 + i];
-      bf::PrepParams prep{j.q, j.k, wsb + wl.q2_off, const_cast<void*>(pp.k2), nullptr, gr.pk, j.k_hstride,
-                          (int)Tq, 0, Hq, Hkv, mode, shift ? 1 : 0, j.w0, (int)j.store_cap64, {}};
-      for (int i = 0; i < nb; ++i) prep.kfirst[i] = j.kfirst[b0 + i];
+      for (int i = 0; i <= nb; ++i) sp.kcu[i] = acu[b0 + i];
+      bf::PrepParams prep{j.q, j.k, wsb + wl.q2_off, const_cast<void*>(pp.k2), paged ? wsb + wl.kc_off : nullptr,
+                          gr.pk, j.k_hstride, (int)Tq, (int)Tk_copy, Hq, Hkv, mode, shift ? 1 : 0, j.w0,
+                          (int)j.store_cap64, {}, {}};
+      for (int i = 0; i < nb; ++i) {
+        prep.kfirst[i] = ax0[b0 + i];
+        prep.krot[i] = j.kfirst[b0 + i];
+      }
       e = bf::launch_correction_prep(dtype, prep, sp, tt, j.stream);
       if (e != hipSuccess) return fail(BF_ERR_HIP, "correction_prep launch: %s", hipGetErrorString(e));
     }
@@ -548,7 +569,7 @@ size_t chunk_store_bytes(int batch, long long cap, int Hkv, int dtype) {
 // Chunk of queries against a KV cache [B][Hkv][cap][D] (bifocal_prefill_chunk)
 // or a paged cache (bifocal_prefill_chunk_paged: pages != null, cap = the
 // most keys a sequence's pages hold); with `store`, k'' and V^T are kept
-// between calls (bifocal_prefill_chunk_stored, contiguous caches only).
+// between calls (bifocal_prefill_chunk_stored and its paged form).
 int run_chunk(const void* q, const void* kc, const void* vc, void* o, float* lse,
               const int32_t* cu_q, const int32_t* seqlens, const int32_t* s_len, int batch,
               int cap, int Hq, int Hkv, int head_dim, int dtype, long long w0, long long w_pre,
@@ -783,6 +804,23 @@ int bifocal_prefill_chunk_paged(const void* q, const void* k_pages, const void* 
   return run_chunk(q, k_pages, v_pages, o, lse, cu_q_host, seqlens_host, s_len_host, batch, 1,
                    n_heads_q, n_heads_kv, head_dim, dtype, w0, w_pre, rope_theta, long_mode,
                    softmax_scale, workspace, workspace_bytes, (hipStream_t)stream, &pg);
+}
+
+int bifocal_prefill_chunk_stored_paged(const void* q, const void* k_pages, const void* v_pages,
+                                       void* store, size_t store_bytes, void* o, float* lse,
+                                       const int32_t* block_table, const int32_t* cu_q_host,
+                                       const int32_t* seqlens_host, const int32_t* s_len_host,
+                                       int32_t* store_keys_host, int32_t* store_s_host,
+                                       int32_t batch, int32_t page_size, int32_t max_pages_per_seq,
+                                       int32_t num_pages, int32_t n_heads_q, int32_t n_heads_kv,
+                                       int32_t head_dim, int32_t dtype, int64_t w0, int64_t w_pre,
+                                       double rope_theta, int32_t long_mode, float softmax_scale,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+  const ChunkPages pg{block_table, page_size, max_pages_per_seq, num_pages};
+  const ChunkStore cs{store, store_bytes, store_keys_host, store_s_host};
+  return run_chunk(q, k_pages, v_pages, o, lse, cu_q_host, seqlens_host, s_len_host, batch, 1,
+                   n_heads_q, n_heads_kv, head_dim, dtype, w0, w_pre, rope_theta, long_mode,
+                   softmax_scale, workspace, workspace_bytes, (hipStream_t)stream, &pg, &cs);
 }
 
 size_t bifocal_chunk_store_bytes(int32_t batch, int32_t cache_capacity, int32_t n_heads_kv,

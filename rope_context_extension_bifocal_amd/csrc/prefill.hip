@@ -187,10 +187,12 @@ __global__ __launch_bounds__(256) void correction_prep_kernel(PrepParams p, SeqT
   if (tok >= cu[st.n]) return;
   const int b = seq_of_tok(cu, st.n, tok);
   const int s = st.s[b];
-  const bool rot = s > 1;         // s = 1: no far branch for this sequence
+  const long long row = tok - cu[b] + (keys ? p.kfirst[b] : 0);
+  // s = 1: no far branch for this sequence; a store already holds the k'' of
+  // its keys below krot
+  const bool rot = s > 1 && !(keys && p.k2_cap > 0 && row < p.krot[b]);
   const bool copy = keys && p.kcopy != nullptr;  // paged keys: gather the packed copy
   if (!rot && !copy) return;
-  const long long row = tok - cu[b] + (keys ? p.kfirst[b] : 0);
   if (keys && row < (long long)st.vt_t0[b] * kKeyTile) return;  // key no window reaches
   float c[E], sn[E];
   if (rot) {

@@ -402,6 +402,47 @@ def test_chunk_stored_failed_launch_keeps_counters(L, monkeypatch):
     assert list(k) == [40, 0] and list(sv) == [2, 0]
 
 
+def _chunk_stored_paged(L, keys, svals, **kw):
+    a = dict(q=P, kp=P, vp=P, store=ctypes.c_void_p(0x200000), store_bytes=1 << 30, o=P, lse=None,
+             bt=P, cu=[0, 30, 31], sl=[100, 1], s_len=None, page=16, maxp=8, npages=20, Hq=4,
+             Hkv=2, D=128, dtype=0, w0=16, w_pre=64, theta=1e4, mode=0, scale=0.088, ws=P,
+             ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    cu = (ctypes.c_int32 * len(a["cu"]))(*a["cu"])
+    sl = (ctypes.c_int32 * len(a["sl"]))(*a["sl"])
+    sls = (ctypes.c_int32 * len(a["s_len"]))(*a["s_len"]) if a["s_len"] is not None else None
+    return L.bifocal_prefill_chunk_stored_paged(
+        a["q"], a["kp"], a["vp"], a["store"], a["store_bytes"], a["o"], a["lse"], a["bt"], cu, sl,
+        sls, keys, svals, len(a["cu"]) - 1, a["page"], a["maxp"], a["npages"], a["Hq"], a["Hkv"],
+        a["D"], a["dtype"], a["w0"], a["w_pre"], a["theta"], a["mode"], a["scale"], a["ws"],
+        a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,keys,code", [
+    (dict(store=None), 0, -1), (dict(store_bytes=1000), 0, -3), (dict(), -5, -1),
+    (dict(mode=2), 0, -2), (dict(bt=None), 0, -1), (dict(page=24), 0, -1),
+    (dict(sl=[129, 1]), 0, -1), (dict(ws_bytes=10), 0, -3),
+    # the store must cover max_pages x page_size = 128 keys per sequence
+    (dict(store_bytes=2 * 2 * 2 * 64 * 128 * 2), 0, -3),
+])
+def test_chunk_stored_paged_validation(L, kw, keys, code):
+    k = (ctypes.c_int32 * 2)(keys, 3)
+    sv = (ctypes.c_int32 * 2)(7, 7)
+    before = (list(k), list(sv))
+    assert _chunk_stored_paged(L, k, sv, **kw) == code
+    assert len(L.bifocal_last_error()) > 0
+    assert (list(k), list(sv)) == before
+
+
+def test_chunk_stored_paged_reaches_the_launch(L, monkeypatch):
+    monkeypatch.setenv("BIFOCAL_TEST_FAIL_LAUNCH", "1")
+    k = (ctypes.c_int32 * 2)(64, 0)
+    sv = (ctypes.c_int32 * 2)(2, 0)
+    assert _chunk_stored_paged(L, k, sv) == bfl.BF_ERR_HIP
+    assert _chunk_stored_paged(L, k, sv, dtype=1, mode=5, page=1, maxp=128, npages=300) == bfl.BF_ERR_HIP
+    assert list(k) == [64, 0] and list(sv) == [2, 0]
+
+
 def _chunk_paged(L, **kw):
     a = dict(q=P, kp=P, vp=P, o=P, lse=None, bt=P, cu=[0, 30, 31], sl=[100, 1], s_len=None,
              page=16, maxp=8, npages=20, Hq=4, Hkv=2, D=128, dtype=0, w0=16, w_pre=64, theta=1e4,

@@ -162,3 +162,103 @@ def test_stored_chunk_512_at_128k():
     torch.cuda.synchronize()
     assert torch.equal(got, ref) and torch.equal(lgot, lref)
     assert store.keys[0] == N and store.s[0] == 4
+
+
+def _paginate(kc, vc, page, seed, spare=3):
+    """Shuffled page pool [B * per + spare, Hkv, page, D] of the caches (the
+    spare pages hold NaN) and its block table [B, per]."""
+    B, Hkv, cap, D = kc.shape
+    per = cap // page
+    n = B * per + spare
+    perm = torch.randperm(n, generator=torch.Generator().manual_seed(seed))[:B * per].cuda()
+    kp = torch.full((n, Hkv, page, D), float("nan"), dtype=kc.dtype, device="cuda")
+    vp = torch.full_like(kp, float("nan"))
+    kp[perm] = kc.view(B, Hkv, per, page, D).permute(0, 2, 1, 3, 4).reshape(B * per, Hkv, page, D)
+    vp[perm] = vc.view(B, Hkv, per, page, D).permute(0, 2, 1, 3, 4).reshape(B * per, Hkv, page, D)
+    return kp, vp, perm.to(torch.int32).view(B, per)
+
+
+@pytest.mark.parametrize("page", [1, 16, 64, 256])
+def test_stored_paged_chunks_equal_paged_chunk(page):
+    # the two-prompt walk over a shuffled page pool: every call bitwise the
+    # stateless paged call and the contiguous stored call on the same keys
+    Hq, Hkv, w0, w_pre = 8, 2, 300, 700
+    kc, vc = _caches(2, Hkv, 3072, torch.bfloat16, 140)
+    kp, vp, table = _paginate(kc, vc, page, 141)
+    sp = bfl.ChunkStore(kp, batch=2, max_pages_per_seq=table.shape[1])
+    sc = bfl.ChunkStore(kc)
+    sp.buf.fill_(255)
+    sc.buf.fill_(255)
+    chunks = [[200, 197, 1000, 1, 700, 802], [100, 900, 64, 700, 36, 700]]
+    ends = [0, 0]
+    args = (w0, w_pre, THETA, "pa+shift", SCALE)
+    for i in range(len(chunks[0])):
+        Lqs = [c[i] for c in chunks]
+        ends = [e + n for e, n in zip(ends, Lqs)]
+        q = _queries(Hq, Lqs, torch.bfloat16, 142 + i)
+        cu = wl.cu_seqlens(Lqs)
+        ref, lref = bfl.prefill_chunk_paged(q, kp, vp, table, cu, ends, *args, s_len=[2900, 2500],
+                                            return_lse=True)
+        got, lgot = bfl.prefill_chunk_stored_paged(q, kp, vp, table, sp, cu, ends, *args,
+                                                   s_len=[2900, 2500], return_lse=True)
+        gc, lgc = bfl.prefill_chunk_stored(q, kc, vc, sc, cu, ends, *args, s_len=[2900, 2500],
+                                           return_lse=True)
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref) and torch.equal(lgot, lref), (page, i)
+        assert torch.equal(gc, ref) and torch.equal(lgc, lref), (page, i)
+        assert list(sp.keys) == ends and list(sp.s) == list(sc.s)
+
+
+def test_stored_paged_chunk_s_change_and_rollback():
+    # s = s(N) changes as the prompt grows (each change empties the store and
+    # the call rotates and gathers from key 0), then a rollback over rewritten
+    # pages; 16-key pages
+    Hq, Hkv, w0, w_pre = 16, 4, 256, 512
+    kc, vc = _caches(1, Hkv, 2400, torch.bfloat16, 143)
+    kp, vp, table = _paginate(kc, vc, 16, 144)
+    st = bfl.ChunkStore(kp, batch=1, max_pages_per_seq=table.shape[1])
+    st.buf.fill_(255)
+    n = 0
+    for i, lq in enumerate([300, 200, 13, 500, 511, 1, 300]):
+        n += lq
+        q = _queries(Hq, [lq], torch.bfloat16, 145 + i)
+        ref = bfl.prefill_chunk_paged(q, kp, vp, table, [0, lq], [n], w0, w_pre, THETA, "fi", SCALE)
+        got = bfl.prefill_chunk_stored_paged(q, kp, vp, table, st, [0, lq], [n], w0, w_pre, THETA,
+                                             "fi", SCALE)
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref), n
+        assert st.keys[0] == n and st.s[0] == bfl.s_of_L(n, w_pre)
+    # rewrite the pages from position 1696 on, cut the store back, redo
+    g = torch.Generator().manual_seed(146)
+    pages = table[0, 1696 // 16:].long()
+    kp[pages] = torch.randn(len(pages), Hkv, 16, 128, generator=g).to(torch.bfloat16).cuda()
+    vp[pages] = torch.randn(len(pages), Hkv, 16, 128, generator=g).to(torch.bfloat16).cuda()
+    st.reset(keys=1696)
+    q = _queries(Hq, [200], torch.bfloat16, 147)
+    ref = bfl.prefill_chunk_paged(q, kp, vp, table, [0, 200], [1900], w0, w_pre, THETA, "fi", SCALE)
+    got = bfl.prefill_chunk_stored_paged(q, kp, vp, table, st, [0, 200], [1900], w0, w_pre, THETA,
+                                         "fi", SCALE)
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref)
+
+
+def test_stored_paged_chunk_512_at_128k():
+    # the last 512 queries of the 131072-key Qwen3-8B-shaped cache over 16-key
+    # pages, after a call that filled the store up to 130560
+    c = wl.CONFIGS["qwen3_8b_prefill_128k"]
+    N, Lq, Hq, Hkv = c["lens"][0], 512, c["Hq"], c["Hkv"]
+    kc, vc = _caches(1, Hkv, N, torch.bfloat16, 148)
+    kp, vp, table = _paginate(kc, vc, 16, 149, spare=0)
+    del kc, vc
+    st = bfl.ChunkStore(kp, batch=1, max_pages_per_seq=table.shape[1])
+    st.buf.fill_(255)
+    args = (c["w0"], c["w_pre"], c["theta"], "pa", SCALE)
+    q0 = _queries(Hq, [Lq], torch.bfloat16, 150)
+    bfl.prefill_chunk_stored_paged(q0, kp, vp, table, st, [0, Lq], [N - Lq], *args, s_len=[N])
+    q = _queries(Hq, [Lq], torch.bfloat16, 151)
+    ref, lref = bfl.prefill_chunk_paged(q, kp, vp, table, [0, Lq], [N], *args, s_len=[N],
+                                        return_lse=True)
+    got, lgot = bfl.prefill_chunk_stored_paged(q, kp, vp, table, st, [0, Lq], [N], *args,
+                                               s_len=[N], return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref) and torch.equal(lgot, lref)
