@@ -69,6 +69,13 @@ struct PrefillParams {
   int nks;
   float* part_o;
   float* part_lse;
+  // null: workgroup w runs work item w. Otherwise 8 counters, zeroed before
+  // the launch, and fewer workgroups than items: each workgroup claims the
+  // next item of its XCD's queue (the items whose id is the XCD's index mod
+  // 8, in id order) and, once that queue is empty, of the other queues, until
+  // all n_items are taken
+  int* item_ctr;
+  int n_items;
 };
 
 // A paged K / V source: pages [num_pages][Hkv][page][D], key j of sequence

@@ -112,11 +112,12 @@ PrefillGeom prefill_geom(int dtype, int G) {
 }
 
 struct PrefillWs {
-  size_t vt_off, q2_off, k2_off, kc_off, base, po_off, pl_off, total;
+  size_t ctr_off, vt_off, q2_off, k2_off, kc_off, base, po_off, pl_off, total;
 };
 
 // Workspace of Tq packed queries against Tk keys (a one-shot prefill has
-// Tk = Tq = T): V^T padded per sequence, q'', k'', for a paged key source the
+// Tk = Tq = T): 256 bytes of work-item counters, V^T padded per sequence,
+// q'', k'', for a paged key source the
 // packed copy of the keys (Tk_copy of them, by default Tk; base ends here),
 // and for `splits` > 1 key splits their partial O (fp32) and log2-sum-exp.
 PrefillWs prefill_ws_layout(int batch, long long Tq, long long Tk, int Hq, int Hkv, int dtype,
@@ -124,8 +125,9 @@ PrefillWs prefill_ws_layout(int batch, long long Tq, long long Tk, int Hq, int H
   const size_t es = elem_size(dtype);
   const size_t tpad_bound = (size_t)Tk + 63u * (size_t)batch;
   PrefillWs w;
-  w.vt_off = 0;
-  w.q2_off = align256((size_t)Hkv * bf::kHeadDim * tpad_bound * es);
+  w.ctr_off = 0;
+  w.vt_off = 256;
+  w.q2_off = w.vt_off + align256((size_t)Hkv * bf::kHeadDim * tpad_bound * es);
   w.k2_off = w.q2_off + align256((size_t)Hq * (size_t)Tq * bf::kHeadDim * es);
   w.kc_off = w.k2_off + align256((size_t)Hkv * (size_t)Tk * bf::kHeadDim * es);
   if (Tk_copy < 0) Tk_copy = Tk;
@@ -407,9 +409,19 @@ int run_rows(RowsJob& j) {
       pp.k2_rows = pp.vt_rows = (long long)nb * Hkv * j.store_cap64;
     }
     gr.grid = wgs * pp.nks;
+    // a bf16 launch of two rounds of workgroups or more runs on persistent
+    // workgroups that claim their work items from per-XCD queues (see
+    // claim_item): the XCDs run at slightly different speeds, and a static
+    // split leaves the faster ones idle for up to a few percent of a long
+    // launch; short items also skip the workgroup turnover. Same box, bitwise
+    // the same output: 128K 120.4 against 121.7-123.3 ms, 64 x 2048 prompts
+    // 2.49-2.50 against 2.52-2.53 ms, 16 x 8192 7.96-7.98 against 8.06-8.13 ms.
+    pp.item_ctr = dtype == BF_DTYPE_BF16 && gr.grid >= 2 * kPrefillSlots ? (int*)(wsb + wl.ctr_off) : nullptr;
     if (gr.grid > 0x7fffffffLL)
       return fail(BF_ERR_INVALID_ARG, "launch grid of sequences %d..%d too large (%lld workgroups)", b0,
                   b0 + nb - 1, gr.grid);
+    pp.n_items = (int)gr.grid;
+    if (pp.item_ctr) gr.grid = kPrefillSlots;  // persistent workgroups, two per CU
   }
   if (forced_launch_failure()) return fail(BF_ERR_HIP, "launch failure forced by BIFOCAL_TEST_FAIL_LAUNCH");
 

@@ -338,9 +338,8 @@ struct Item {
 
 template <bool BIFOCAL, bool BAND>
 __device__ __forceinline__ Item make_item(const PrefillParams& p, const SeqTable& st, int wave,
-                                          int wave_rows) {
+                                          int wave_rows, int id) {
   Item it;
-  const int id = blockIdx.x;
   it.kvh = id % p.Hkv;
   const int r1 = id / p.Hkv;
   const int hsub = r1 % p.n_hsub;
@@ -364,6 +363,26 @@ __device__ __forceinline__ Item make_item(const PrefillParams& p, const SeqTable
   const int wg_end = it.qp + min(it.R0 + p.P_wg, it.L);  // keys < wg_end
   it.nkt = (wg_end + kKeyTile - 1) / kKeyTile;
   return it;
+}
+
+// Next work item of a persistent workgroup (PrefillParams::item_ctr): queue r
+// holds the item ids r, r + 8, r + 16, ... below n, in that order, which
+// with the KV head in the low bits of the id is one KV head's work, heaviest
+// first. A workgroup takes the next id of its own XCD's queue, so each XCD's
+// L2 still serves one KV head, and once that queue is empty the next id of
+// the following queues: XCDs that run faster take over the last items of
+// slower ones instead of idling. A failed claim means that queue is empty
+// for good; -1 when every queue is.
+__device__ __forceinline__ int claim_item(int* ctr, int n) {
+  const int xcc = (int)__builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 7;  // XCC_ID
+  for (int i = 0; i < 8; ++i) {
+    const int r = (xcc + i) & 7;
+    const int len = (n - r + 7) >> 3;
+    if (len <= 0) continue;
+    const int k = atomicAdd(ctr + r, 1);
+    if (k < len) return r + 8 * k;
+  }
+  return -1;
 }
 
 // Key-tile ranges of the two passes for a workgroup's query positions
@@ -896,15 +915,17 @@ __device__ __forceinline__ void run_pass(const uint16_t* qsrc, const uint16_t* k
   }
 }
 
+// One work item of the bf16 kernel (lanes whose query row is past the
+// sequence return early from the epilogue only, after the last barrier).
 template <bool BIFOCAL, bool BAND>
-__global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillParams p, SeqTable st) {
-  extern __shared__ uint4 smem[];
+__device__ __forceinline__ void prefill_bf16_item(const PrefillParams& p, const SeqTable& st, int id,
+                                                  uint4* smem) {
   uint4* sK = smem;                  // kRing slots
   uint4* sV = smem + kRing * kSlot;  // kRing slots
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar) index
   const int li = lane & 31, hl = lane >> 5;
-  const Item it = make_item<BIFOCAL, BAND>(p, st, wave, kWaveRowsBf16);
+  const Item it = make_item<BIFOCAL, BAND>(p, st, wave, kWaveRowsBf16, id);
   const WaveRows wr{it.r0, it.qp + it.r0, it.L, (int)min(it.w0, (long long)(1 << 30))};
 
   const uint16_t* qg = (const uint16_t*)p.q + ((size_t)it.hq * p.T + it.tok0) * kHeadDim;
@@ -992,6 +1013,26 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillParams p, S
     p.lse[(size_t)it.hq * p.T + it.tok0 + row] = (rs.m_used + __log2f(l)) * 0.69314718055994530942f;
 }
 
+// Workgroup w runs work item w, or, with claim counters, workgroups loop
+// over the items they claim until every queue is empty (see claim_item).
+template <bool BIFOCAL, bool BAND>
+__global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillParams p, SeqTable st) {
+  extern __shared__ uint4 smem[];
+  __shared__ int s_item;
+  int id = blockIdx.x;
+  for (;;) {
+    if (p.item_ctr) {
+      __syncthreads();  // every wave has read the previous item's id
+      if (threadIdx.x == 0) s_item = claim_item(p.item_ctr, p.n_items);
+      __syncthreads();
+      id = __builtin_amdgcn_readfirstlane(s_item);
+      if (id < 0) return;
+    }
+    prefill_bf16_item<BIFOCAL, BAND>(p, st, id, smem);
+    if (!p.item_ctr) return;
+  }
+}
+
 // --------------------------------------------------------------- fp32
 // Same loop with fp32 operands on MFMA 32x32x2 f32: one 32-row query block per
 // wave; k-step t contracts head dims t (lanes 0-31) and 64 + t (lanes 32-63).
@@ -1025,7 +1066,7 @@ __global__ __launch_bounds__(256, 1) void prefill_f32_kernel(PrefillParams p, Se
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 31, hl = lane >> 5;
-  const Item it = make_item<BIFOCAL, BAND>(p, st, wave, kWaveRowsF32);
+  const Item it = make_item<BIFOCAL, BAND>(p, st, wave, kWaveRowsF32, blockIdx.x);
   const long long w0 = it.w0;
 
   const float* qg = (const float*)p.q + ((size_t)it.hq * p.T + it.tok0) * kHeadDim;
@@ -1331,8 +1372,17 @@ static hipError_t launch_with_lds(K kernel, int grid, int threads, size_t lds, h
   return hipGetLastError();
 }
 
+__global__ __launch_bounds__(64) void zero_item_ctr_kernel(int* ctr) {
+  if (threadIdx.x < 8) ctr[threadIdx.x] = 0;
+}
+
 hipError_t launch_prefill_main(int dtype, bool bifocal, bool band, const PrefillParams& pp,
                                const SeqTable& st, int grid, hipStream_t stream) {
+  if (pp.item_ctr) {  // the claim counters start at zero (a fill kernel, not a memset)
+    hipLaunchKernelGGL(zero_item_ctr_kernel, dim3(1), dim3(64), 0, stream, pp.item_ctr);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (dtype == 0) {
     const int th = 64 * kBf16Waves;
     const size_t lds = 2 * kRing * kSlot * sizeof(uint4);
