@@ -23,8 +23,9 @@
  * Conventions for every entry point:
  *   - Tensors are caller-owned DEVICE memory and must stay valid until the
  *     work enqueued on `stream` completes. Host arrays (cu_seqlens_host,
- *     seqlens_host, ...) are read, and the far-key store's counters
- *     (store_keys_host, store_s_host) written, before the call returns.
+ *     seqlens_host, ...) are read, and the counters of the far-key and
+ *     chunk stores (store_keys_host, store_s_host) written, before the call
+ *     returns.
  *   - All work is enqueued on `stream` (a hipStream_t, NULL = default
  *     stream). The library never synchronises and keeps no state between
  *     calls except a thread-local error string.
@@ -90,8 +91,10 @@ int64_t bifocal_s_of_L(int64_t L, int64_t w_pre);
  *   PREFILL: `tokens` = total packed tokens T = cu_seqlens[batch].
  *   DECODE:  `tokens` = the largest seqlens[b] of the call.
  * The same figure covers both the bifocal and the plain call of a phase.
- * PREFILL holds V^T (padded per sequence to 64 keys), the corrected queries
- * q'' and the corrected keys k'' in the input dtype: about
+ * PREFILL holds 256 bytes of work-item counters (launches of 1024 or more
+ * work items run persistent workgroups that claim their items), V^T (padded
+ * per sequence to 64 keys), the corrected queries q'' and the corrected keys
+ * k'' in the input dtype: about
  * (Hq + 2 Hkv) x T x head_dim elements, 1.5 GiB for a 131072-token bf16
  * prefill with 32 query / 8 KV heads (k'' and q'' are formed once per call
  * instead of on every re-read of a key tile). DECODE holds the split
