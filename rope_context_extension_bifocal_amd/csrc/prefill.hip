@@ -977,8 +977,8 @@ __device__ __forceinline__ void prefill_bf16_item(const PrefillParams& p, const 
   // epilogue: normalise, store O (bf16) and lse, or a key split's partial
   const int row = it.r0 + li;
   const float l = rs.l_part + __shfl_xor(rs.l_part, 32);
-  if (row >= it.L) return;
   if (p.nks > 1) {
+    if (row >= it.L) return;
     // a split may hold no key of a row: O = 0 and lse = -inf then weigh
     // nothing in the merge
     const size_t prow = ((size_t)it.split * p.Hq + it.hq) * p.T + it.tok0 + row;
@@ -995,21 +995,30 @@ __device__ __forceinline__ void prefill_bf16_item(const PrefillParams& p, const 
     if (hl == 0) p.part_lse[prow] = l > 0.f ? rs.m_used + __log2f(l) : -INFINITY;
     return;
   }
-  uint16_t* og = (uint16_t*)p.o + ((size_t)it.hq * p.T + it.tok0) * kHeadDim;
-  const float inv = 1.f / l;
+  // the wave's 32 rows are one 8 KiB block of O: they go through the K ring
+  // (no longer read after the last QK^T) and out as row-contiguous 16-byte
+  // stores; in LDS, 16-byte chunk c of row r sits at chunk c ^ (r % 16)
+  char* lds = (char*)sK + wave * 8192;
+  const float inv = row < it.L ? 1.f / l : 0.f;
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const int d = 32 * db + 8 * g + 4 * hl;
       uint2 w;
       w.x = (uint32_t)f32_to_bf16(oacc[db][4 * g + 0] * inv) |
             ((uint32_t)f32_to_bf16(oacc[db][4 * g + 1] * inv) << 16);
       w.y = (uint32_t)f32_to_bf16(oacc[db][4 * g + 2] * inv) |
             ((uint32_t)f32_to_bf16(oacc[db][4 * g + 3] * inv) << 16);
-      *(uint2*)(og + (size_t)row * kHeadDim + d) = w;
+      *(uint2*)(lds + li * 256 + (((4 * db + g) ^ (li & 15)) << 4) + (hl << 3)) = w;
     }
-  if (p.lse && hl == 0)
+  uint16_t* og = (uint16_t*)p.o + ((size_t)it.hq * p.T + it.tok0 + it.r0) * kHeadDim;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int rr = 4 * i + (lane >> 4), cc = lane & 15;
+    const uint4 v = *(const uint4*)(lds + rr * 256 + ((cc ^ (rr & 15)) << 4));
+    if (it.r0 + rr < it.L) *(uint4*)(og + (size_t)rr * kHeadDim + cc * 8) = v;
+  }
+  if (p.lse && hl == 0 && row < it.L)
     p.lse[(size_t)it.hq * p.T + it.tok0 + row] = (rs.m_used + __log2f(l)) * 0.69314718055994530942f;
 }
 
