@@ -262,3 +262,25 @@ def test_stored_paged_chunk_512_at_128k():
                                                s_len=[N], return_lse=True)
     torch.cuda.synchronize()
     assert torch.equal(got, ref) and torch.equal(lgot, lref)
+
+
+def test_stored_paged_chunks_fp32():
+    # fp32 over 16-key pages: the fp32 kernel reads k' of the packed copy only
+    # for tiles with a local pair, which start at or above the copy's first key
+    Hq, Hkv, w0, w_pre = 4, 1, 128, 256
+    kc, vc = _caches(2, Hkv, 1152, torch.float32, 152)
+    kp, vp, table = _paginate(kc, vc, 16, 153)
+    st = bfl.ChunkStore(kp, batch=2, max_pages_per_seq=table.shape[1])
+    st.buf.fill_(255)
+    ends = [0, 0]
+    for i, Lqs in enumerate([[300, 64], [5, 700], [400, 1], [64, 300]]):
+        ends = [e + n for e, n in zip(ends, Lqs)]
+        q = _queries(Hq, Lqs, torch.float32, 154 + i)
+        cu = wl.cu_seqlens(Lqs)
+        args = (w0, w_pre, THETA, "pa+shift", SCALE)
+        ref, lref = bfl.prefill_chunk_paged(q, kp, vp, table, cu, ends, *args, s_len=[1100, 1100],
+                                            return_lse=True)
+        got, lgot = bfl.prefill_chunk_stored_paged(q, kp, vp, table, st, cu, ends, *args,
+                                                   s_len=[1100, 1100], return_lse=True)
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref) and torch.equal(lgot, lref), i
