@@ -284,3 +284,26 @@ def test_stored_paged_chunks_fp32():
                                                    s_len=[1100, 1100], return_lse=True)
         torch.cuda.synchronize()
         assert torch.equal(got, ref) and torch.equal(lgot, lref), i
+
+
+def test_stored_paged_chunks_batch_of_70():
+    # 70 sequences over a shuffled 16-key page pool: two launch groups, each
+    # with its rows of the block table, its part of the store and of the key axis
+    B, Hq, Hkv, w0, w_pre = 70, 8, 2, 128, 512
+    kc, vc = _caches(B, Hkv, 1600, torch.bfloat16, 170)
+    kp, vp, table = _paginate(kc, vc, 16, 171)
+    st = bfl.ChunkStore(kp, batch=B, max_pages_per_seq=table.shape[1])
+    st.buf.fill_(255)
+    chunks = [[40 + 3 * b, 200 + (7 * b) % 300, 1 + b % 5] for b in range(B)]
+    ends = [0] * B
+    for i in range(3):
+        Lqs = [c[i] for c in chunks]
+        ends = [e + n for e, n in zip(ends, Lqs)]
+        q = _queries(Hq, Lqs, torch.bfloat16, 172 + i)
+        cu = wl.cu_seqlens(Lqs)
+        args = (w0, w_pre, THETA, "fi", SCALE)
+        ref = bfl.prefill_chunk_paged(q, kp, vp, table, cu, ends, *args, s_len=[1600] * B)
+        got = bfl.prefill_chunk_stored_paged(q, kp, vp, table, st, cu, ends, *args, s_len=[1600] * B)
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref), i
+        assert list(st.keys) == ends
